@@ -1,0 +1,432 @@
+"""Pins of the float64 oracle against facts fixed by the mathematics and the
+pages, independent of the oracle's own code path (CPU only).
+
+* central finite differences of L = <dy, y> + <dS_T, S_T> (the toy shape of
+  mlx-lm PR #1217, Correctness section, plus a B=2 variant);
+* a hand-worked T=2 example in exact rationals (tests/golden);
+* closed forms for T=1 (any S0) and T=2 (S0 = 0), expanded by hand;
+* the delta-rule invariant: beta=1, |k|=1 gives S_t k_t = v_t;
+* the identity case g=1, beta=0;
+* joint linearity in (v, S0) and in (dy, dS_T);
+* the adjoint identity <grad, direction> = directional derivative;
+* batch-row independence (unsloth-zoo PR #776: rows past the first);
+* the GQA map h // (Hv/Hk) equals numpy.repeat of q, k over value heads
+  (mlx issue #4614 repro, recurrence helper);
+* and a mutation check: plausible mistakes planted in a copy of the oracle
+  must each fail at least one of these pins.
+"""
+import json
+import os
+import types
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle.gdr_oracle as O
+from gated_delta_rule_recurrence_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0")
+
+
+def _loss(orc, p, q, k, v, g, beta, S0):
+    y, ST = orc.forward(q, k, v, g, beta, S0)
+    L = float((y * p.dy).sum())
+    if p.dST is not None:
+        L += float((ST * p.dST).sum())
+    return L
+
+
+def fd_grads(orc, p, h=1e-6):
+    args = [p.q, p.k, p.v, p.g, p.beta,
+            p.S0 if p.S0 is not None else np.zeros((p.B, p.Hv, p.Dv, p.Dk))]
+    out = []
+    for i, x in enumerate(args):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a1 = list(args)
+            a2 = list(args)
+            xp = x.copy()
+            xp[idx] += h
+            xm = x.copy()
+            xm[idx] -= h
+            a1[i] = xp
+            a2[i] = xm
+            fd[idx] = (_loss(orc, p, *a1) - _loss(orc, p, *a2)) / (2 * h)
+        out.append(fd)
+    return out
+
+
+def complex_step_grads(orc, p, h=1e-30):
+    """dL/dx_i = Im L(x + i h e_i) / h: no subtractive cancellation, so the
+    derivative is exact to rounding even where it is tiny (strong decay)."""
+    args = [p.q, p.k, p.v, p.g, p.beta,
+            p.S0 if p.S0 is not None else np.zeros((p.B, p.Hv, p.Dv, p.Dk))]
+    out = []
+    for i, x in enumerate(args):
+        d = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = [np.asarray(z, dtype=np.complex128) for z in args]
+            a[i][idx] += 1j * h
+            y, ST = orc.forward(*a)
+            L = (y * p.dy).sum()
+            if p.dST is not None:
+                L += (ST * p.dST).sum()
+            d[idx] = L.imag / h
+        out.append(d)
+    return out
+
+
+def check_fd(orc, p, tol=1e-6):
+    grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
+    fds = fd_grads(orc, p)
+    for name, gr, fd in zip(NAMES, grads, fds):
+        err = O.rel_l2(gr, fd)
+        assert err <= tol, f"{name}: rel L2 vs central FD = {err:.3e}"
+
+
+# --------------------------------------------------------------------------
+# finite differences
+
+
+@pytest.mark.parametrize("with_dST", [False, True])
+def test_fd_toy(with_dST):
+    check_fd(O, inputs.toy(seed=1, with_dST=with_dST))
+
+
+def test_fd_batch2_gqa():
+    p = inputs.draw(2, 3, 1, 3, 4, 3, seed=7, S0_std=0.3, dST_std=1.0)
+    check_fd(O, p)
+
+
+@pytest.mark.parametrize("decay", ["strong", "weak"])
+def test_complex_step(decay):
+    """Every gradient, dg and the tiny dS0 under strong decay included, to
+    1e-12 relative."""
+    p = inputs.draw(1, 5, 1, 2, 4, 4, seed=3, decay=decay, S0_std=0.5,
+                    dST_std=1.0)
+    grads = O.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
+    for name, gr, cs in zip(NAMES, grads, complex_step_grads(O, p)):
+        err = O.rel_l2(gr, cs)
+        assert err <= 1e-12, f"{name}: rel L2 vs complex step = {err:.3e}"
+
+
+# --------------------------------------------------------------------------
+# hand-worked example
+
+
+def _frac_array(x):
+    return np.vectorize(lambda s: float(Fraction(s)))(np.array(x, dtype=object)).astype(np.float64)
+
+
+def _worked_example(orc=O):
+    with open(os.path.join(GOLDEN, "worked_T2_D2.json")) as f:
+        fx = json.load(f)
+    i = {k: _frac_array(v) for k, v in fx["inputs"].items()}
+    e = {k: _frac_array(v) for k, v in fx["expected"].items()}
+    q = i["q"].reshape(1, 2, 1, 2)
+    k = i["k"].reshape(1, 2, 1, 2)
+    v = i["v"].reshape(1, 2, 1, 2)
+    g = i["g"].reshape(1, 2, 1)
+    beta = i["beta"].reshape(1, 2, 1)
+    dy = i["dy"].reshape(1, 2, 1, 2)
+    y, ST = orc.forward(q, k, v, g, beta)
+    grads = orc.backward(q, k, v, g, beta, dy)
+    got = dict(zip(NAMES, grads), y=y, S_T=ST)
+    for name, want in e.items():
+        np.testing.assert_allclose(got[name].ravel(), want.ravel(), rtol=0,
+                                   atol=1e-14, err_msg=name)
+
+
+def test_worked_example_exact():
+    _worked_example()
+
+
+# --------------------------------------------------------------------------
+# closed forms
+
+
+def _rand_T1(seed):
+    rng = np.random.default_rng(seed)
+    Dk, Dv = 5, 3
+    q = rng.standard_normal(Dk)
+    k = rng.standard_normal(Dk)
+    v = rng.standard_normal(Dv)
+    g = float(rng.uniform(0.2, 0.9))
+    b = float(rng.uniform(0.1, 0.9))
+    S0 = rng.standard_normal((Dv, Dk))
+    dy = rng.standard_normal(Dv)
+    return q, k, v, g, b, S0, dy
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_closed_form_T1(seed, orc=O):
+    q, k, v, g, b, S0, dy = _rand_T1(seed)
+    kq = k @ q
+    S0k = S0 @ k
+    # y = g S0 q - g b (S0 k)(k.q) + b (k.q) v ;  L = dy . y
+    y_cf = g * (S0 @ q) - g * b * S0k * kq + b * kq * v
+    S1_cf = g * S0 - g * b * np.outer(S0k, k) + b * np.outer(v, k)
+    dq_cf = g * (S0.T @ dy) - g * b * (dy @ S0k) * k + b * (dy @ v) * k
+    dk_cf = (-g * b * kq * (S0.T @ dy) - g * b * (dy @ S0k) * q
+             + b * (dy @ v) * q)
+    dv_cf = b * kq * dy
+    db_cf = -g * (dy @ S0k) * kq + (dy @ v) * kq
+    dg_cf = dy @ (S0 @ q) - b * (dy @ S0k) * kq
+    dS0_cf = g * np.outer(dy, q) - g * b * kq * np.outer(dy, k)
+    sh = lambda a, *s: np.asarray(a, dtype=np.float64).reshape(*s)
+    args = (sh(q, 1, 1, 1, 5), sh(k, 1, 1, 1, 5), sh(v, 1, 1, 1, 3),
+            sh(g, 1, 1, 1), sh(b, 1, 1, 1))
+    y, S1 = orc.forward(*args, S0=S0[None, None])
+    np.testing.assert_allclose(y.ravel(), y_cf, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S1[0, 0], S1_cf, rtol=1e-12, atol=1e-12)
+    dq, dk, dv, dg, db, dS0 = orc.backward(*args, dy=sh(dy, 1, 1, 1, 3),
+                                           S0=S0[None, None])
+    for got, want in ((dq, dq_cf), (dk, dk_cf), (dv, dv_cf), (dg, dg_cf),
+                      (db, db_cf), (dS0, dS0_cf)):
+        np.testing.assert_allclose(np.ravel(got), np.ravel(want), rtol=1e-12,
+                                   atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_closed_form_T2(seed, orc=O):
+    rng = np.random.default_rng(100 + seed)
+    D = 4
+    q1, q2, k1, k2 = (rng.standard_normal(D) for _ in range(4))
+    v1, v2 = rng.standard_normal(3), rng.standard_normal(3)
+    g1, g2 = rng.uniform(0.3, 0.9, 2)
+    b1, b2 = rng.uniform(0.1, 0.9, 2)
+    dy1, dy2 = rng.standard_normal(3), rng.standard_normal(3)
+    q = np.stack([q1, q2]).reshape(1, 2, 1, D)
+    k = np.stack([k1, k2]).reshape(1, 2, 1, D)
+    v = np.stack([v1, v2]).reshape(1, 2, 1, 3)
+    g = np.array([g1, g2]).reshape(1, 2, 1)
+    beta = np.array([b1, b2]).reshape(1, 2, 1)
+    dy = np.stack([dy1, dy2]).reshape(1, 2, 1, 3)
+    y, _ = orc.forward(q, k, v, g, beta)
+    y1 = b1 * (k1 @ q1) * v1
+    y2 = (g2 * b1 * ((k1 @ q2) - b2 * (k2 @ q2) * (k1 @ k2)) * v1
+          + b2 * (k2 @ q2) * v2)
+    np.testing.assert_allclose(y[0, 0, 0], y1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(y[0, 1, 0], y2, rtol=1e-12, atol=1e-13)
+    _, _, _, dg, _, _ = orc.backward(q, k, v, g, beta, dy)
+    dg2 = b1 * (v1 @ dy2) * ((k1 @ q2) - b2 * (k1 @ k2) * (k2 @ q2))
+    assert dg[0, 0, 0] == 0.0
+    np.testing.assert_allclose(dg[0, 1, 0], dg2, rtol=1e-12, atol=1e-13)
+
+
+def test_closed_form_T1_zero_state_grads(orc=O):
+    """T=1, S0=0: dq = b(v.dy)k, dk = b(v.dy)q, dv = b(k.q)dy,
+    dbeta = (k.q)(v.dy), dg = 0."""
+    rng = np.random.default_rng(5)
+    q, k = rng.standard_normal(6), rng.standard_normal(6)
+    v, dy = rng.standard_normal(4), rng.standard_normal(4)
+    g, b = 0.7, 0.4
+    sh = lambda a, *s: np.asarray(a, dtype=np.float64).reshape(*s)
+    dq, dk, dv, dg, db, _ = orc.backward(sh(q, 1, 1, 1, 6), sh(k, 1, 1, 1, 6),
+                                         sh(v, 1, 1, 1, 4), sh(g, 1, 1, 1),
+                                         sh(b, 1, 1, 1), sh(dy, 1, 1, 1, 4))
+    np.testing.assert_allclose(dq.ravel(), b * (v @ dy) * k, rtol=1e-13)
+    np.testing.assert_allclose(dk.ravel(), b * (v @ dy) * q, rtol=1e-13)
+    np.testing.assert_allclose(dv.ravel(), b * (k @ q) * dy, rtol=1e-13)
+    np.testing.assert_allclose(db.ravel(), [(k @ q) * (v @ dy)], rtol=1e-13)
+    assert dg.ravel()[0] == 0.0
+
+
+# --------------------------------------------------------------------------
+# invariants and special cases
+
+
+def test_delta_rule_invariant(orc=O):
+    """beta = 1 and |k| = 1: after each step S_t k_t = v_t exactly."""
+    p = inputs.draw(2, 9, 2, 4, 6, 5, seed=11, normalised=True, S0_std=1.0)
+    beta = np.ones_like(p.beta)
+    p.k = p.k / np.linalg.norm(p.k, axis=-1, keepdims=True)  # unit in float64
+    _, _, states = orc.forward(p.q, p.k, p.v, p.g, beta, p.S0, keep_states=True)
+    kv = np.arange(p.Hv) // (p.Hv // p.Hk)
+    for t in range(p.T):
+        Sk = np.einsum("bhij,bhj->bhi", states[t + 1], p.k[:, t, kv])
+        np.testing.assert_allclose(Sk, p.v[:, t], rtol=1e-12, atol=1e-12)
+
+
+def test_identity_case(orc=O):
+    """g = 1, beta = 0: S stays S0, y_t = S0 q_t; with
+    G_t = dS_T + sum_{s>=t} dy_s q_s^T: dq_t = S0^T dy_t, dk = dv = 0,
+    dbeta_t = (v_t - S0 k_t) . (G_t k_t), dg_t = <G_t, S0>, dS0 = G_0."""
+    p = inputs.draw(1, 6, 1, 1, 5, 4, seed=2, S0_std=1.0, dST_std=1.0)
+    g = np.ones_like(p.g)
+    beta = np.zeros_like(p.beta)
+    y, ST = orc.forward(p.q, p.k, p.v, g, beta, p.S0)
+    S0 = p.S0[0, 0]
+    np.testing.assert_array_equal(ST[0, 0], S0)
+    for t in range(p.T):
+        np.testing.assert_allclose(y[0, t, 0], S0 @ p.q[0, t, 0], rtol=1e-13)
+    dq, dk, dv, dg, db, dS0 = orc.backward(p.q, p.k, p.v, g, beta, p.dy, p.S0,
+                                           p.dST)
+    assert not dk.any() and not dv.any()
+    G = p.dST[0, 0].copy()
+    for t in range(p.T - 1, -1, -1):
+        G = G + np.outer(p.dy[0, t, 0], p.q[0, t, 0])
+        np.testing.assert_allclose(dq[0, t, 0], S0.T @ p.dy[0, t, 0], rtol=1e-12)
+        e = p.v[0, t, 0] - S0 @ p.k[0, t, 0]
+        np.testing.assert_allclose(db[0, t, 0], e @ (G @ p.k[0, t, 0]), rtol=1e-12)
+        np.testing.assert_allclose(dg[0, t, 0], np.sum(G * S0), rtol=1e-12)
+    np.testing.assert_allclose(dS0[0, 0], G, rtol=1e-12)
+
+
+def test_linearity_in_v_and_S0(orc=O):
+    p1 = inputs.draw(1, 7, 2, 4, 5, 3, seed=21, S0_std=1.0)
+    p2 = inputs.draw(1, 7, 2, 4, 5, 3, seed=22, S0_std=1.0)
+    a, b = 0.7, -1.3
+    y1, S1 = orc.forward(p1.q, p1.k, p1.v, p1.g, p1.beta, p1.S0)
+    y2, S2 = orc.forward(p1.q, p1.k, p2.v, p1.g, p1.beta, p2.S0)
+    y3, S3 = orc.forward(p1.q, p1.k, a * p1.v + b * p2.v, p1.g, p1.beta,
+                         a * p1.S0 + b * p2.S0)
+    np.testing.assert_allclose(y3, a * y1 + b * y2, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(S3, a * S1 + b * S2, rtol=1e-11, atol=1e-12)
+
+
+def test_linearity_in_cotangents(orc=O):
+    p = inputs.draw(1, 6, 1, 2, 4, 3, seed=31, S0_std=1.0, dST_std=1.0)
+    rng = np.random.default_rng(32)
+    dy2 = rng.standard_normal(p.dy.shape)
+    dST2 = rng.standard_normal(p.dST.shape)
+    g1 = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
+    g2 = orc.backward(p.q, p.k, p.v, p.g, p.beta, dy2, p.S0, dST2)
+    g3 = orc.backward(p.q, p.k, p.v, p.g, p.beta, 2 * p.dy - dy2, p.S0,
+                      2 * p.dST - dST2)
+    for a, b, c in zip(g1, g2, g3):
+        np.testing.assert_allclose(c, 2 * a - b, rtol=1e-10, atol=1e-11)
+
+
+def test_adjoint_identity(orc=O):
+    """<grad, D> equals the central directional derivative of L along D."""
+    p = inputs.draw(1, 12, 2, 4, 8, 6, seed=41, S0_std=0.5, dST_std=1.0,
+                    normalised=True)
+    rng = np.random.default_rng(42)
+    args = [p.q, p.k, p.v, p.g, p.beta, p.S0]
+    dirs = [rng.standard_normal(a.shape) for a in args]
+    grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
+    lhs = sum(float((gr * d).sum()) for gr, d in zip(grads, dirs))
+    h = 1e-6
+    ap = [a + h * d for a, d in zip(args, dirs)]
+    am = [a - h * d for a, d in zip(args, dirs)]
+    rhs = (_loss(orc, p, *ap) - _loss(orc, p, *am)) / (2 * h)
+    assert abs(lhs - rhs) <= 1e-7 * max(1.0, abs(rhs))
+
+
+def test_batch_rows_independent(orc=O):
+    p = inputs.draw(3, 8, 2, 4, 6, 5, seed=51, S0_std=0.3, dST_std=1.0)
+    y, ST = orc.forward(p.q, p.k, p.v, p.g, p.beta, p.S0)
+    grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
+    for b in range(p.B):
+        s = slice(b, b + 1)
+        yb, STb = orc.forward(p.q[s], p.k[s], p.v[s], p.g[s], p.beta[s], p.S0[s])
+        gb = orc.backward(p.q[s], p.k[s], p.v[s], p.g[s], p.beta[s], p.dy[s],
+                          p.S0[s], p.dST[s])
+        np.testing.assert_array_equal(y[s], yb)
+        np.testing.assert_array_equal(ST[s], STb)
+        for a, c in zip(grads, gb):
+            np.testing.assert_array_equal(a[s], c)
+
+
+def test_gqa_is_repeat(orc=O):
+    """Hk < Hv equals the Hk = Hv call on numpy.repeat-expanded q, k, with the
+    expanded dq, dk summed over each group (value head h reads kv head
+    h // (Hv/Hk), not h % Hk)."""
+    p = inputs.draw(1, 6, 2, 6, 5, 4, seed=61, S0_std=0.3)
+    rep = p.Hv // p.Hk
+    qe = np.repeat(p.q, rep, axis=2)
+    ke = np.repeat(p.k, rep, axis=2)
+    y, ST = orc.forward(p.q, p.k, p.v, p.g, p.beta, p.S0)
+    ye, STe = orc.forward(qe, ke, p.v, p.g, p.beta, p.S0)
+    np.testing.assert_allclose(y, ye, rtol=1e-13, atol=1e-14)
+    g1 = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0)
+    ge = orc.backward(qe, ke, p.v, p.g, p.beta, p.dy, p.S0)
+    sumg = lambda a: a.reshape(a.shape[0], a.shape[1], p.Hk, rep, -1).sum(3)
+    np.testing.assert_allclose(g1[0], sumg(ge[0]), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g1[1], sumg(ge[1]), rtol=1e-12, atol=1e-13)
+    for a, b in zip(g1[2:], ge[2:]):
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-13)
+
+
+def test_head_map_errors():
+    with pytest.raises(ValueError):
+        O.head_map(3, 4)
+    assert list(O.head_map(2, 6)) == [0, 0, 0, 1, 1, 1]
+
+
+def test_rel_l2_metric():
+    assert O.rel_l2([3.0, 4.0], [3.0, 4.0]) == 0.0
+    assert O.rel_l2([0.0], [0.0]) == 0.0
+    assert abs(O.rel_l2([1.0, 1.0], [1.0, 0.0]) - 1.0) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# mutation check: each planted mistake must fail some pin
+
+
+MUTANTS = {
+    "readout_uses_k": ('y[:, t] = np.einsum("bhij,bhj->bhi", S, qt)',
+                       'y[:, t] = np.einsum("bhij,bhj->bhi", S, kt)'),
+    "dropped_beta": ("d = beta[:, t, :, None] * e", "d = e"),
+    "no_decay_before_read": (
+        "S = g[:, t, :, None, None] * S           # decay\n"
+        "        u = np.einsum(\"bhij,bhj->bhi\", S, kt)    # S k_t on the decayed state",
+        "u = np.einsum(\"bhij,bhj->bhi\", S, kt)\n"
+        "        S = g[:, t, :, None, None] * S"),
+    "dg_on_new_state": ('dg[:, t] = np.einsum("bhij,bhij->bh", dA, S_prev)',
+                        'dg[:, t] = np.einsum("bhij,bhij->bh", dA, S_cur)'),
+    "sign_of_du": ("de_u = -bt * dd", "de_u = bt * dd"),
+    "no_decay_of_G": ("G = gt * dA", "G = dA"),
+    "dk_missing_g": ('dk_h[:, t] += np.einsum("bhij,bhi->bhj", A, de_u)',
+                     'dk_h[:, t] += np.einsum("bhij,bhi->bhj", S_prev, de_u)'),
+    "tile_head_map": ("return np.arange(Hv) // (Hv // Hk)",
+                      "return np.arange(Hv) % Hk"),
+    "dq_wrong_group": ("dq[:, :, h // rep] += dq_h[:, :, h]",
+                       "dq[:, :, h % Hk] += dq_h[:, :, h]"),
+    "dbeta_uses_v": ('dbeta[:, t] = np.einsum("bhi,bhi->bh", e, dd)',
+                     'dbeta[:, t] = np.einsum("bhi,bhi->bh", v[:, t], dd)'),
+}
+
+
+def _mutant(name):
+    src_path = O.__file__
+    with open(src_path) as f:
+        src = f.read()
+    old, new = MUTANTS[name]
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("oracle_mutant_" + name)
+    exec(compile(src.replace(old, new), src_path, "exec"), mod.__dict__)
+    return mod
+
+
+def _pins(orc):
+    """Run the pins against `orc`; return the names of those that fail."""
+    failed = []
+    checks = {
+        "fd_toy": lambda: check_fd(orc, inputs.toy(seed=1, with_dST=True)),
+        "fd_gqa": lambda: check_fd(orc, inputs.draw(1, 3, 1, 2, 3, 2, seed=7,
+                                                    S0_std=0.3, dST_std=1.0)),
+        "worked": lambda: _worked_example(orc),
+        "T1": lambda: test_closed_form_T1(0, orc),
+        "T2": lambda: test_closed_form_T2(0, orc),
+        "gqa_repeat": lambda: test_gqa_is_repeat(orc),
+        "identity": lambda: test_identity_case(orc),
+    }
+    for name, fn in checks.items():
+        try:
+            fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def test_pins_pass_on_oracle():
+    assert _pins(O) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    assert _pins(_mutant(name)), f"no pin caught mutant {name}"
