@@ -1,0 +1,172 @@
+#!/usr/bin/env python3
+"""Forward+backward throughput of the gated delta rule on one MI355X.
+
+Workload: the Qwen3.5-9B linear_attn shape of mlx-lm PR #1217 (Performance
+table): B=1, Hk=16, Hv=64, Dk=192, Dv=128, T=2048, bf16 q/k/v/g/beta/dy,
+fp32 state, weak decay, normalised q/k, S0=0 (synthetic, seeded).  A step is
+one gdr_forward (with save) plus one gdr_backward over that batch; inputs and
+every output/scratch buffer are resident in HBM before timing starts.
+
+Prints one JSON line (see README of the bench contract in the design doc).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_VECTOR_PEAK_TF = 157.3    # MI355X FP32 vector, TFLOP/s
+FLOPS_FWD = 7                  # per state element per step (S k, S q, decay+rank-1)
+FLOPS_BWD = 15                 # per state element per step (reverse sweep)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--T", type=int, default=2048)
+    ap.add_argument("--B", type=int, default=1)
+    ap.add_argument("--chunk", type=int, default=64)
+    ap.add_argument("--dtype", default="bf16", choices=("bf16", "f32"))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-T", type=int, default=2048)
+    return ap.parse_args()
+
+
+def cpu_baseline(T, seed, dtype):
+    """Time the float64 oracle (as it stands) on one kv group of the same
+    workload: 4 of the 64 value heads, full T, forward + backward."""
+    from threadpoolctl import threadpool_limits
+    import oracle.gdr_oracle as O
+    from gated_delta_rule_recurrence_amd import inputs
+    p = inputs.qwen35_9b(T, seed=seed, dtype=dtype)
+    rep = p.Hv // p.Hk
+    sl = lambda a: a[:, :, 0:rep]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        O.forward(p.q[:, :, 0:1], p.k[:, :, 0:1], sl(p.v), sl(p.g), sl(p.beta))
+        O.backward(p.q[:, :, 0:1], p.k[:, :, 0:1], sl(p.v), sl(p.g), sl(p.beta),
+                   sl(p.dy))
+        dt = time.perf_counter() - t0
+    frac = rep / p.Hv
+    return {"value": p.B * T * frac / dt, "unit": "tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"kv group 0 (value heads 0-{rep - 1} of {p.Hv}), B=1, T={T}, "
+                      f"fwd+bwd in {dt:.2f} s on 1 thread; tokens scaled by {rep}/{p.Hv}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the path "
+              "shards by (batch row, kv head) with no communication, see DESIGN.md",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib, inputs, ops
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    _lib.load()  # fail loudly if the HIP library is missing
+
+    p = inputs.qwen35_9b(args.T, seed=args.seed, dtype=args.dtype, B=args.B)
+    dt = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    q, k, v, g, beta, dy = (t(getattr(p, n)) for n in ("q", "k", "v", "g", "beta", "dy"))
+    B, T, Hk, Hv, Dk, Dv = p.B, p.T, p.Hk, p.Hv, p.Dk, p.Dv
+
+    # every buffer allocated up front
+    shape = ops.shape_of(q, v, args.chunk, dt)
+    ckpt = torch.empty(_lib.checkpoint_bytes(shape), dtype=torch.uint8, device=dev)
+    ws = torch.empty(_lib.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(v)
+    S_T = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+            torch.empty_like(g), torch.empty_like(beta),
+            torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev))
+    saved = ops.Saved(ckpt, args.chunk)
+    stream = torch.cuda.current_stream(dev)
+
+    def fwd():
+        ops.gdr_forward(q, k, v, g, beta, None, chunk=args.chunk, y=y, S_T=S_T,
+                        ckpt=ckpt)
+
+    def bwd():
+        ops.gdr_backward(q, k, g, beta, saved, dy, None, workspace=ws, out=outs)
+
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, events on the library's stream around each call
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        fwd()
+        ev[i][1].record(stream)
+        bwd()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    ms = wall * 1e3 / args.steps
+    tokens = B * T
+    value = tokens / (ms / 1e3)
+
+    elems = B * T * Hv * Dv * Dk  # state-element steps
+    fwd_flops = FLOPS_FWD * elems
+    fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    all_tf = (FLOPS_FWD + FLOPS_BWD) * elems / (ms * 1e-3) / 1e12
+
+    ckpt_mb = ckpt.numel() / 1e6
+    ws_mb = ws.numel() / 1e6
+    rec = {
+        "metric": "fwd+bwd tokens/s, Qwen3.5-9B gated-delta shape T=2048",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"Qwen3.5-9B linear_attn gated delta rule fwd+bwd, "
+                               f"B={B} T={T} Hk={Hk} Hv={Hv} Dk={Dk} Dv={Dv}, "
+                               f"{args.dtype} inputs, fp32 state, chunk={args.chunk}",
+                   "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "alu", "kernel": "fwd_sweep_kernel",
+                     "achieved": fwd_tf, "peak": FP32_VECTOR_PEAK_TF,
+                     "unit": "TFLOP/s", "frac": fwd_tf / FP32_VECTOR_PEAK_TF,
+                     "traffic": None},
+        "breakdown": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+                      "useful_tflops_whole_step": all_tf,
+                      "frac_whole_step_vs_fp32_vector_peak": all_tf / FP32_VECTOR_PEAK_TF,
+                      "checkpoint_MB": ckpt_mb, "workspace_MB": ws_mb},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(min(args.cpu_sample_T, T), args.seed, args.dtype)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

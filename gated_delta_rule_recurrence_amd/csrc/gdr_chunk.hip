@@ -1,0 +1,451 @@
+// Chunk-parallel part of the gated delta rule VJP on gfx950: dq, dk, dg, dbeta.
+//
+// The two sweeps leave, per chunk of n <= 64 steps (t0 .. t0+n-1, local index
+// t = 0..n-1) and per value head:
+//   S0 = the state before the chunk (forward checkpoint),
+//   H1 = dL/dS after the chunk (reverse-sweep checkpoint),
+//   e_t, c_t (per row): the forward residual and G_t k_t,
+// and with delta_t = beta_t e_t, dv_t = beta_t c_t every state inside the
+// chunk is an explicit sum of these pieces (unrolling the two recurrences):
+//   S_t = Gam(start,t] S0 + sum_{r<=t} Gam(r,t] delta_r k_r^T
+//   H_t = Gam(t,end] H1 + sum_{s>t} Gam(t,s] (dy_s q_s^T - dv_s k_s^T)
+// where Gam(a,b] is the product of g over the steps a+1..b, always formed as a
+// running product (no ratio of cumulative decays and no division by g, which
+// is what keeps dg accurate under strong decay, cf. mlx issue #4614).
+// Substituting into the per-step VJP (dq_t = S_t^T dy_t,
+// dk_t = G_t^T delta_t - g_t S_{t-1}^T dv_t, dg_t = <dA_t, S_{t-1}>,
+// dbeta_t = e_t . c_t) turns every sum over Dv into a contraction over the
+// chunk:
+//   P1 = S0^T DY, P2' = S0^T C, P3' = H1^T E          [Dk x n]
+//   Phi'[t][r] = dy_t . e_r,  Psi'[t][r] = c_t . e_r  [n x n]
+//   QK[s][r] = q_s . k_r,     KK[s][r] = k_s . k_r    [n x n]
+// followed by O(n^2) work per head and [Dk x n] x [n x n] products.
+//
+// Mapping: one workgroup of 512 threads per (batch row, kv head, chunk); it
+// loops over the Hv/Hk value heads of the kv head in ascending order and
+// accumulates dq, dk in registers, so the GQA sum has a fixed order and needs
+// no atomics.  Thread (jt, tt) owns the output columns j = jt + 32m (m < J)
+// and local steps t = tt + 16u (u < 4).
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+constexpr int kThreads = 512;
+constexpr int kN = 64;   // max chunk length
+constexpr int kIB = 16;  // Dv rows staged per block
+constexpr int kNP = kN + 1;  // padded row stride of the [kN][kN] LDS matrices
+
+template <int J>
+struct CL {  // LDS layout, offsets in floats
+  static constexpr int DKP = 32 * J;
+  static constexpr int STAGE_A = 2 * kIB * DKP + 3 * kIB * kNP; // S, H, dy/e/c
+  static constexpr int STAGE_QK = 2 * kN * kNP;                 // q, k j-blocks
+  static constexpr int STAGE_F = 2 * kIB * DKP;                 // final k, q
+  static constexpr int GRAM = 2 * kN * kNP;                     // Phi', Psi'
+  static constexpr int A_SZ0 = STAGE_A > STAGE_QK ? STAGE_A : STAGE_QK;
+  static constexpr int A_SZ = A_SZ0 > GRAM ? A_SZ0 : GRAM;
+  static constexpr int A = 0;
+  static constexpr int QK = A + A_SZ;        // [kN][kNP]
+  static constexpr int KK = QK + kN * kNP;   // [kN][kNP]
+  static constexpr int GM = KK + kN * kNP;   // Gam(r,t] for r <= t
+  static constexpr int MZ = GM + kN * kNP;   // M, then the dg terms
+  static constexpr int RED = MZ + kN * kNP;  // [2][32][kNP]
+  static constexpr int VEC = RED + 2 * 32 * kNP;
+  static constexpr int V_G = VEC, V_B = VEC + kN, V_PRE = VEC + 2 * kN,
+                       V_PREX = VEC + 3 * kN, V_SUF = VEC + 4 * kN,
+                       V_CHI = VEC + 5 * kN, V_PSI = VEC + 6 * kN,
+                       V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;
+  static constexpr int SIZE = V_SCR + 64;
+};
+
+template <typename TIn, int J>
+__global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
+  using L = CL<J>;
+  extern __shared__ __align__(16) float sm[];
+
+  const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ g = static_cast<const TIn*>(a.g);
+  const TIn* __restrict__ beta = static_cast<const TIn*>(a.beta);
+  const TIn* __restrict__ dy = static_cast<const TIn*>(a.dy);
+
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
+  const int jc = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int rep = Hv / Hk;
+  const int t0 = jc * a.L;
+  const int n = min(a.L, T - t0);
+  const int tid = threadIdx.x;
+  const int jt = tid & 31, tt = tid >> 5;
+  const int64_t mat = (int64_t)Dv * Dk;
+
+  auto qk_index = [&](int t, int j) -> int64_t {
+    return ((int64_t)(b * (int64_t)T + t0 + t) * Hk + hk) * Dk + j;
+  };
+
+  // ---- QK and KK for the kv head (shared by all its value heads) ----------
+  float qk8[8], kk8[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) qk8[w] = kk8[w] = 0.f;
+  for (int j0 = 0; j0 < Dk; j0 += 64) {
+    float* sq = sm + L::A;
+    float* sk = sm + L::A + kN * kNP;
+    for (int idx = tid; idx < kN * 64; idx += kThreads) {
+      const int s = idx >> 6, jj = idx & 63, j = j0 + jj;
+      const bool ok = s < n && j < Dk;
+      sq[s * kNP + jj] = ok ? ld(q, qk_index(s, j)) : 0.f;
+      sk[s * kNP + jj] = ok ? ld(k, qk_index(s, j)) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int w = 0; w < 8; ++w) {
+      const int e = tid + kThreads * w;
+      const int s = e >> 6, r = e & 63;
+      float aq = qk8[w], ak = kk8[w];
+#pragma unroll 4
+      for (int jj = 0; jj < 64; ++jj) {
+        const float kr = sk[r * kNP + jj];
+        aq = fmaf(sq[s * kNP + jj], kr, aq);
+        ak = fmaf(sk[s * kNP + jj], kr, ak);
+      }
+      qk8[w] = aq;
+      kk8[w] = ak;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int e = tid + kThreads * w;
+    const int x = (e >> 6) * kNP + (e & 63);
+    sm[L::QK + x] = qk8[w];
+    sm[L::KK + x] = kk8[w];
+  }
+
+  // running sums over the value heads
+  float wq[8], w1[8], w2[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) wq[w] = w1[w] = w2[w] = 0.f;
+  float dQ[J][4], dK[J][4];
+#pragma unroll
+  for (int m = 0; m < J; ++m)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dQ[m][u] = dK[m][u] = 0.f;
+
+  for (int hh = 0; hh < rep; ++hh) {
+    const int h = hk * rep + hh;
+    const int64_t bh = (int64_t)b * Hv + h;
+    const float* __restrict__ S0 = a.Sck + (bh * a.nch + jc) * mat;
+    const float* __restrict__ H1 = a.Hck + (bh * a.nch + jc) * mat;
+    auto row_index = [&](int t, int i) -> int64_t {
+      return ((int64_t)(b * (int64_t)T + t0 + t) * Hv + h) * Dv + i;
+    };
+
+    // ---- contractions over Dv --------------------------------------------
+    float P1[J][4], P2[J][4], P3[J][4];
+    float phi[4][2], psi[4][2];
+    float hs = 0.f;
+#pragma unroll
+    for (int m = 0; m < J; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) P1[m][u] = P2[m][u] = P3[m][u] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) phi[u][0] = phi[u][1] = psi[u][0] = psi[u][1] = 0.f;
+
+    float* sS = sm + L::A;
+    float* sH = sS + kIB * L::DKP;
+    float* sY = sH + kIB * L::DKP;  // [kIB][kNP] dy
+    float* sE = sY + kIB * kNP;     // [kIB][kNP] e
+    float* sC = sE + kIB * kNP;     // [kIB][kNP] c
+    for (int i0 = 0; i0 < Dv; i0 += kIB) {
+      for (int idx = tid; idx < kIB * L::DKP; idx += kThreads) {
+        const int ii = idx / L::DKP, j = idx % L::DKP, i = i0 + ii;
+        const bool ok = i < Dv && j < Dk;
+        sS[idx] = ok ? S0[(int64_t)i * Dk + j] : 0.f;
+        sH[idx] = ok ? H1[(int64_t)i * Dk + j] : 0.f;
+      }
+      for (int idx = tid; idx < kIB * kN; idx += kThreads) {
+        const int ii = idx % kIB, t = idx / kIB, i = i0 + ii;  // rows fastest
+        const bool ok = i < Dv && t < n;
+        sY[ii * kNP + t] = ok ? ld(dy, row_index(t, i)) : 0.f;
+        sE[ii * kNP + t] = ok ? a.E[row_index(t, i)] : 0.f;
+        sC[ii * kNP + t] = ok ? a.C[row_index(t, i)] : 0.f;
+      }
+      __syncthreads();
+#pragma unroll 1
+      for (int ii = 0; ii < kIB; ++ii) {
+        float sj[J], hj[J], yu[4], cu[4], eu[4], ew[2];
+#pragma unroll
+        for (int m = 0; m < J; ++m) {
+          sj[m] = sS[ii * L::DKP + jt + 32 * m];
+          hj[m] = sH[ii * L::DKP + jt + 32 * m];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          yu[u] = sY[ii * kNP + tt + 16 * u];
+          cu[u] = sC[ii * kNP + tt + 16 * u];
+          eu[u] = sE[ii * kNP + tt + 16 * u];
+        }
+        ew[0] = sE[ii * kNP + 2 * jt];
+        ew[1] = sE[ii * kNP + 2 * jt + 1];
+#pragma unroll
+        for (int m = 0; m < J; ++m)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            P1[m][u] = fmaf(sj[m], yu[u], P1[m][u]);
+            P2[m][u] = fmaf(sj[m], cu[u], P2[m][u]);
+            P3[m][u] = fmaf(hj[m], eu[u], P3[m][u]);
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int w = 0; w < 2; ++w) {
+            phi[u][w] = fmaf(yu[u], ew[w], phi[u][w]);
+            psi[u][w] = fmaf(cu[u], ew[w], psi[u][w]);
+          }
+        if (tt == 0) {
+#pragma unroll
+          for (int m = 0; m < J; ++m) hs = fmaf(sj[m], hj[m], hs);
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- per-head O(n^2) stage -------------------------------------------
+    float* sPhi = sm + L::A;        // Phi'[t][r]
+    float* sPsi = sm + L::A + kN * kNP;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        sPhi[(tt + 16 * u) * kNP + 2 * jt + w] = phi[u][w];
+        sPsi[(tt + 16 * u) * kNP + 2 * jt + w] = psi[u][w];
+      }
+    if (tt == 0) sm[L::RED + jt] = hs;  // <H1, S0> partials (32 of them)
+    if (tid < kN) {
+      const bool ok = tid < n;
+      sm[L::V_G + tid] = ok ? ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
+      sm[L::V_B + tid] = ok ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float phi0 = 0.f;
+      for (int w = 0; w < 32; ++w) phi0 += sm[L::RED + w];
+      sm[L::V_SCR] = phi0;
+      float acc = 1.f;
+      for (int t = 0; t < n; ++t) {
+        sm[L::V_PREX + t] = acc;
+        acc *= sm[L::V_G + t];
+        sm[L::V_PRE + t] = acc;
+      }
+      acc = 1.f;
+      for (int t = n - 1; t >= 0; --t) {
+        sm[L::V_SUF + t] = acc;
+        acc *= sm[L::V_G + t];
+      }
+    }
+    if (tid < kN) {  // row r = tid of Gam(r, t]
+      const int r = tid;
+      float acc = 1.f;
+      for (int t = 0; t < kN; ++t) {
+        float val = 0.f;
+        if (t == r) {
+          val = 1.f;
+        } else if (t > r && t < n) {
+          acc *= sm[L::V_G + t];
+          val = acc;
+        }
+        sm[L::GM + r * kNP + t] = val;
+      }
+    }
+    __syncthreads();
+    if (tid < n)
+      st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h,
+         sPsi[tid * kNP + tid]);
+
+    // running weight matrices and M
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int e = tid + kThreads * w;
+      const int s = e >> 6, t = e & 63;  // entry (s, t)
+      if (s < n && t < n) {
+        const float bs = sm[L::V_B + s], bt = sm[L::V_B + t];
+        const float phi_st = sPhi[s * kNP + t], phi_ts = sPhi[t * kNP + s];
+        const float psi_st = sPsi[s * kNP + t], psi_ts = sPsi[t * kNP + s];
+        const float gam_st = sm[L::GM + s * kNP + t];  // Gam(s,t], s <= t
+        const float gam_ts = sm[L::GM + t * kNP + s];  // Gam(t,s], t <= s
+        // Wq[s][t] = Gam(s,t] beta_s Phi'[t][s]            (s <= t)
+        if (s <= t) wq[w] = fmaf(gam_st * bs, phi_ts, wq[w]);
+        // W1[s][t] = Gam(t,s] beta_t Phi'[s][t]            (s >= t)
+        if (s >= t) w1[w] = fmaf(gam_ts * bt, phi_st, w1[w]);
+        // W2[s][t] = Gam(t,s] Psi[s][t] (s > t), Gam(s,t] Psi[t][s] (s < t)
+        if (s > t) w2[w] = fmaf(gam_ts * (bs * bt), psi_st, w2[w]);
+        if (s < t) w2[w] = fmaf(gam_st * (bs * bt), psi_ts, w2[w]);
+        // M[s][r=t] = Phi[s][r] QK[s][r] - Psi[s][r] KK[s][r]
+        const int x = s * kNP + t;
+        sm[L::MZ + x] = (bt * phi_st) * sm[L::QK + x] - ((bs * bt) * psi_st) * sm[L::KK + x];
+      }
+    }
+
+    // chi, psi partials and the P terms of dq, dk
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tt + 16 * u;
+      float cp = 0.f, pp = 0.f;
+      if (t < n) {
+        const float bt = sm[L::V_B + t];
+        const float pre = sm[L::V_PRE + t], suf = sm[L::V_SUF + t];
+#pragma unroll
+        for (int m = 0; m < J; ++m) {
+          const int j = jt + 32 * m;
+          float qv = 0.f, kv = 0.f;
+          if (j < Dk) {
+            qv = ld(q, qk_index(t, j));
+            kv = ld(k, qk_index(t, j));
+          }
+          const float p2 = bt * P2[m][u], p3 = bt * P3[m][u];
+          cp = fmaf(P1[m][u], qv, cp);
+          cp = fmaf(-p2, kv, cp);
+          pp = fmaf(p3, kv, pp);
+          dQ[m][u] = fmaf(pre, P1[m][u], dQ[m][u]);
+          dK[m][u] = fmaf(suf, p3, dK[m][u]);
+          dK[m][u] = fmaf(-pre, p2, dK[m][u]);
+        }
+      }
+      sm[L::RED + jt * kNP + t] = cp;
+      sm[L::RED + 32 * kNP + jt * kNP + t] = pp;
+    }
+    __syncthreads();
+    if (tid < n) {
+      float cs = 0.f, ps = 0.f;
+      for (int w = 0; w < 32; ++w) {
+        cs += sm[L::RED + w * kNP + tid];
+        ps += sm[L::RED + 32 * kNP + w * kNP + tid];
+      }
+      sm[L::V_CHI + tid] = cs;
+      sm[L::V_PSI + tid] = ps;
+    }
+    __syncthreads();
+    if (tid == kThreads - 1 && n > 0) {
+      // A_t = sum_{s>=t} Gam(t,s] chi_s + Gam(t,end] phi0
+      float acc = sm[L::V_CHI + n - 1] + sm[L::V_SCR];
+      sm[L::V_A + n - 1] = acc;
+      for (int t = n - 1; t > 0; --t) {
+        acc = fmaf(sm[L::V_G + t], acc, sm[L::V_CHI + t - 1]);
+        sm[L::V_A + t - 1] = acc;
+      }
+    }
+    if (tid < n) {
+      // B_t[r] = sum_{s>=t} Gam(t,s] M[s][r] + Gam(t,end] psi_r, for t > r;
+      // store Gam(r,t-1] B_t[r] in place of M[t][r].
+      const int r = tid;
+      float bacc = 0.f;
+      for (int t = n - 1; t > r; --t) {
+        const float mtr = sm[L::MZ + t * kNP + r];
+        bacc = (t == n - 1) ? mtr + sm[L::V_PSI + r]
+                            : fmaf(sm[L::V_G + t + 1], bacc, mtr);
+        sm[L::MZ + t * kNP + r] = sm[L::GM + r * kNP + t - 1] * bacc;
+      }
+    }
+    __syncthreads();
+    if (tid < n) {
+      const int t = tid;
+      float dg = sm[L::V_PREX + t] * sm[L::V_A + t];
+      for (int r = 0; r < t; ++r) dg += sm[L::MZ + t * kNP + r];
+      st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h, dg);
+    }
+    __syncthreads();
+  }
+
+  // ---- dq += K Wq;  dk += Q W1 - K W2 -------------------------------------
+  float* sWq = sm + L::QK;
+  float* sW1 = sm + L::KK;
+  float* sW2 = sm + L::GM;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int e = tid + kThreads * w;
+    const int x = (e >> 6) * kNP + (e & 63);
+    sWq[x] = wq[w];
+    sW1[x] = w1[w];
+    sW2[x] = w2[w];
+  }
+  float* sKf = sm + L::A;
+  float* sQf = sm + L::A + kIB * L::DKP;
+  for (int s0 = 0; s0 < n; s0 += kIB) {
+    for (int idx = tid; idx < kIB * L::DKP; idx += kThreads) {
+      const int ss = idx / L::DKP, j = idx % L::DKP, s = s0 + ss;
+      const bool ok = s < n && j < Dk;
+      sKf[idx] = ok ? ld(k, qk_index(s, j)) : 0.f;
+      sQf[idx] = ok ? ld(q, qk_index(s, j)) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int ss = 0; ss < kIB; ++ss) {
+      const int s = s0 + ss;
+      float kv[J], qv[J], a_q[4], a_1[4], a_2[4];
+#pragma unroll
+      for (int m = 0; m < J; ++m) {
+        kv[m] = sKf[ss * L::DKP + jt + 32 * m];
+        qv[m] = sQf[ss * L::DKP + jt + 32 * m];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a_q[u] = sWq[s * kNP + tt + 16 * u];
+        a_1[u] = sW1[s * kNP + tt + 16 * u];
+        a_2[u] = sW2[s * kNP + tt + 16 * u];
+      }
+#pragma unroll
+      for (int m = 0; m < J; ++m)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dQ[m][u] = fmaf(kv[m], a_q[u], dQ[m][u]);
+          dK[m][u] = fmaf(qv[m], a_1[u], dK[m][u]);
+          dK[m][u] = fmaf(-kv[m], a_2[u], dK[m][u]);
+        }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int m = 0; m < J; ++m)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = jt + 32 * m, t = tt + 16 * u;
+      if (j < Dk && t < n) {
+        st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[m][u]);
+        st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[m][u]);
+      }
+    }
+}
+
+template <typename TIn, int J>
+hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
+  const size_t lds = sizeof(float) * CL<J>::SIZE;
+  auto kern = chunk_kernel<TIn, J>;
+  // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
+  // launch error below.
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(lds));
+  dim3 grid(a.nch, a.Hk, a.B);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t chunk_dispatch(const ChunkArgs& a, hipStream_t s) {
+  const int J = (a.Dk + 31) / 32;
+  if (J <= 1) return chunk_launch<TIn, 1>(a, s);
+  if (J <= 2) return chunk_launch<TIn, 2>(a, s);
+  if (J <= 4) return chunk_launch<TIn, 4>(a, s);
+  if (J <= 6) return chunk_launch<TIn, 6>(a, s);
+  if (J <= 8) return chunk_launch<TIn, 8>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? chunk_dispatch<gdr::bf16>(a, s) : chunk_dispatch<float>(a, s);
+}
+
+}  // namespace gdr

@@ -1,0 +1,61 @@
+// Internal launch interface between the C ABI (gdr_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// Forward sweep: state recurrence with save.
+struct FwdSweepArgs {
+  int B, T, Hk, Hv, Dk, Dv, L, nch;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const float* S0;  // may be null (zeros)
+  void* y;
+  float* ST;   // may be null
+  float* Sck;  // [B][Hv][nch][Dv][Dk] or null (inference)
+  float* E;    // [B][T][Hv][Dv] or null (inference)
+};
+
+// Reverse sweep of the state gradient.
+struct BwdSweepArgs {
+  int B, T, Hk, Hv, Dk, Dv, L, nch;
+  const void* q;
+  const void* k;
+  const void* g;
+  const void* beta;
+  const void* dy;
+  const float* dST;  // may be null (zeros)
+  void* dv;
+  float* dS0;  // may be null
+  float* Hck;  // [B][Hv][nch][Dv][Dk]: slot j = dL/dS after chunk j
+  float* C;    // [B][T][Hv][Dv]: G_t k_t
+};
+
+// Chunk-parallel contraction: dq, dk, dg, dbeta.
+struct ChunkArgs {
+  int B, T, Hk, Hv, Dk, Dv, L, nch;
+  const void* q;
+  const void* k;
+  const void* g;
+  const void* beta;
+  const void* dy;
+  const float* Sck;
+  const float* E;
+  const float* Hck;
+  const float* C;
+  void* dq;
+  void* dk;
+  void* dg;
+  void* dbeta;
+};
+
+hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace gdr

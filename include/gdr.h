@@ -1,0 +1,121 @@
+/*
+ * gdr.h - C ABI of the MI355X (gfx950) gated delta rule library (libgdr.so).
+ *
+ * The operation (mlx issue #4614 "mx.fast.gated_delta_update VJP: wrong
+ * gradient w.r.t. g", recurrence statement under the accuracy table, and the
+ * repro script's recurrence helper): for every batch row b and value head h,
+ * reading kv head h / (Hv/Hk), with a state S[Dv][Dk] (fp32):
+ *
+ *     S <- g_t * S;   S <- S + outer(beta_t * (v_t - S k_t), k_t);   y_t = S q_t
+ *
+ * gdr_forward runs it and saves what the VJP needs (forward-with-save, mlx-lm
+ * PR #1217 "Add Metal VJP kernel for gated_delta_update", section "What this
+ * PR adds"); gdr_backward returns the gradients of q, k, v, g, beta and the
+ * initial state from a deterministic reverse sweep (no atomics; fixed
+ * reduction order, so repeated calls are bitwise identical on one GPU).
+ *
+ * Layouts (all dense, row-major, last index fastest, no strides):
+ *   q, k, dq, dk      [B][T][Hk][Dk]      element type = shape.dtype
+ *   v, y, dv, dy      [B][T][Hv][Dv]      element type = shape.dtype
+ *   g, beta, dg, dbeta[B][T][Hv]          element type = shape.dtype
+ *   S0, S_T, dS_T, dS0[B][Hv][Dv][Dk]     always fp32
+ *   g is the decay itself (not its log); dg is dL/dg.
+ *
+ * Ownership: every buffer is allocated and freed by the caller; all data
+ * pointers are device pointers.  The library allocates nothing, keeps no
+ * state between calls and is reentrant.  Work is enqueued on `stream`
+ * (hipStream_t, NULL = the default stream) without any host synchronisation;
+ * results are ready when the stream reaches that point.
+ *
+ * Errors: every function returns GDR_OK (0) or a negative gdr_status.  All
+ * argument checks happen on the host before anything is enqueued, so a
+ * rejected call has no effect.  Nothing crosses the ABI as an exception.
+ * gdr_strerror() maps a status to a static string.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GDR_OK = 0,
+  GDR_ERR_NULL_ARG = -1,        /* a required pointer is NULL                  */
+  GDR_ERR_BAD_SHAPE = -2,       /* B or T < 0, or Hk, Hv, Dk, Dv < 1            */
+  GDR_ERR_HEAD_RATIO = -3,      /* Hv is not a multiple of Hk                   */
+  GDR_ERR_UNSUPPORTED_DIM = -4, /* Dk or Dv > 256, or B or Hv > 65535           */
+  GDR_ERR_BAD_CHUNK = -5,       /* chunk outside [1, 64]                        */
+  GDR_ERR_BAD_DTYPE = -6,       /* dtype is not GDR_F32 or GDR_BF16             */
+  GDR_ERR_OVERFLOW = -7,        /* a byte size does not fit in 63 bits          */
+  GDR_ERR_WORKSPACE = -8,       /* workspace smaller than the size query says  */
+  GDR_ERR_ALIGNMENT = -9,       /* a pointer is not 16-byte aligned             */
+  GDR_ERR_HIP = -10             /* the HIP runtime rejected a launch            */
+} gdr_status;
+
+typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* Problem description.  chunk = C, the checkpoint interval: the forward saves
+ * the state every C steps and the backward processes time in chunks of C
+ * steps (the "fixed-size chunks" of the pages' chunked VJP).  The last chunk
+ * may be shorter.  Results do not depend on C beyond fp32 rounding. */
+typedef struct {
+  int64_t B, T, Hk, Hv, Dk, Dv;
+  int64_t chunk;
+  int32_t dtype; /* gdr_dtype: element type of q,k,v,g,beta,y,dy and grads */
+} gdr_shape;
+
+/* Number of chunks, ceil(T / chunk) (0 when T == 0). */
+int gdr_num_chunks(const gdr_shape* shape, int64_t* out);
+
+/* Bytes of the forward save buffer `ckpt`:
+ *   state checkpoints  S_{jC} for j = 0..nchunks-1   [B][Hv][nchunks][Dv][Dk] fp32
+ *   per-step residual  e_t = v_t - g_t S_{t-1} k_t    [B][T][Hv][Dv]           fp32
+ * each region starting on a 256-byte boundary. */
+int gdr_checkpoint_bytes(const gdr_shape* shape, size_t* out);
+
+/* Bytes of the scratch buffer gdr_backward needs: the state-gradient
+ * checkpoints (one per chunk) and the per-step G_t k_t vectors, fp32. */
+int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out);
+
+/* Forward pass.
+ *   in : q, k, v, g, beta (shape.dtype); S0 (fp32, NULL means zeros)
+ *   out: y (shape.dtype); S_T (fp32, NULL means not written);
+ *        ckpt (gdr_checkpoint_bytes bytes, NULL means inference: nothing is
+ *        saved and gdr_backward cannot follow).
+ * `stream` is a hipStream_t passed as void*. */
+int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
+                const void* v, const void* g, const void* beta,
+                const float* S0, void* y, float* S_T, void* ckpt,
+                void* stream);
+
+/* Backward pass (VJP of gdr_forward for L = <dy, y> + <dS_T, S_T>).
+ *   in : q, k, g, beta, dy (shape.dtype) - the same q, k, g, beta given to
+ *        gdr_forward; ckpt as written by that gdr_forward call;
+ *        dS_T (fp32, NULL means zeros).
+ *   out: dq, dk (summed over the Hv/Hk value heads of each kv head, in
+ *        ascending head order), dv, dg, dbeta (shape.dtype);
+ *        dS0 (fp32, NULL means not written).
+ *   workspace: at least gdr_backward_workspace_bytes bytes of device memory,
+ *        contents ignored on entry and undefined on exit.
+ * v is not needed: the forward saved the residual e_t in ckpt. */
+int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
+                 const void* g, const void* beta, const void* ckpt,
+                 const void* dy, const float* dS_T, void* dq, void* dk,
+                 void* dv, void* dg, void* dbeta, float* dS0,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static, human-readable text for a gdr_status value. */
+const char* gdr_strerror(int status);
+
+/* Library version as "major.minor.patch". */
+const char* gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

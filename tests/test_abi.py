@@ -1,0 +1,154 @@
+"""CPU tests of the C ABI: libgdr.so loads, exports every function that
+include/gdr.h declares, and rejects bad arguments on the host before any HIP
+call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_recurrence_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not _lib.LIB_PATH.exists():
+        from gated_delta_rule_recurrence_amd import build
+        build.build(verbose=False)
+    return _lib.load()
+
+
+def declared_functions():
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(gdr_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ("gdr_forward", "gdr_backward", "gdr_checkpoint_bytes",
+              "gdr_backward_workspace_bytes", "gdr_num_chunks", "gdr_strerror",
+              "gdr_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", str(_lib.LIB_PATH)],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(gdr_\w+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, f"not exported: {missing}"
+    for n in declared_functions():
+        assert getattr(lib, n) is not None
+
+
+def test_binding_covers_header():
+    assert set(declared_functions()) == set(_lib._SIGNATURES)
+
+
+def test_version_and_strerror(lib):
+    assert re.fullmatch(r"\d+\.\d+\.\d+", lib.gdr_version().decode())
+    for code in range(0, -11, -1):
+        assert "unknown" not in _lib.strerror(code)
+    assert "unknown" in _lib.strerror(-999)
+
+
+def S(B=1, T=4, Hk=2, Hv=4, Dk=8, Dv=8, chunk=2, dtype=_lib.GDR_F32):
+    return _lib.make_shape(B, T, Hk, Hv, Dk, Dv, chunk, dtype)
+
+
+@pytest.mark.parametrize("shape,code", [
+    (S(B=-1), -2), (S(T=-1), -2), (S(Hk=0), -2), (S(Hv=0), -2), (S(Dk=0), -2),
+    (S(Dv=0), -2), (S(Hk=3, Hv=4), -3), (S(Dk=257), -4), (S(Dv=300), -4),
+    (S(B=70000), -4), (S(chunk=0), -5), (S(chunk=65), -5), (S(dtype=2), -6),
+    (S(dtype=-1), -6), (S(T=2**40), -7),
+])
+def test_shape_errors(lib, shape, code):
+    out = ctypes.c_size_t()
+    assert lib.gdr_checkpoint_bytes(ctypes.byref(shape), ctypes.byref(out)) == code
+    assert lib.gdr_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)) == code
+    assert _lib.forward_raw(shape, *([0] * 10)) == code
+
+
+def test_null_shape(lib):
+    out = ctypes.c_size_t()
+    assert lib.gdr_checkpoint_bytes(None, ctypes.byref(out)) == -1
+    assert lib.gdr_forward(None, *([None] * 10)) == -1
+    assert lib.gdr_backward(None, *([None] * 14), 0, None) == -1
+
+
+def test_null_out_pointer(lib):
+    sh = S()
+    assert lib.gdr_checkpoint_bytes(ctypes.byref(sh), None) == -1
+    assert lib.gdr_num_chunks(ctypes.byref(sh), None) == -1
+
+
+def _round256(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,T,Hk,Hv,Dk,Dv,C", [
+    (1, 4, 2, 4, 8, 8, 2), (1, 2048, 16, 64, 192, 128, 64),
+    (4, 8192, 16, 64, 192, 128, 64), (2, 5, 1, 3, 7, 5, 64), (1, 0, 1, 1, 4, 4, 8),
+])
+def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
+    sh = S(B, T, Hk, Hv, Dk, Dv, C)
+    nch = (T + C - 1) // C
+    assert _lib.num_chunks(sh) == nch
+    states = nch * B * Hv * Dv * Dk * 4
+    rows = B * T * Hv * Dv * 4
+    assert _lib.checkpoint_bytes(sh) == _round256(states) + rows
+    assert _lib.backward_workspace_bytes(sh) == _round256(states) + rows
+
+
+FAKE = 1 << 20  # a 16-byte aligned address; never dereferenced in these tests
+
+
+def test_forward_null_required_pointer(lib):
+    sh = S()
+    for i in range(5):  # q, k, v, g, beta
+        ptrs = [FAKE] * 10
+        ptrs[i] = 0
+        assert _lib.forward_raw(sh, *ptrs) == -1
+    ptrs = [FAKE] * 10
+    ptrs[6] = 0  # y
+    assert _lib.forward_raw(sh, *ptrs) == -1
+
+
+def test_forward_misaligned_pointer(lib):
+    sh = S()
+    for i in range(9):
+        ptrs = [FAKE] * 10
+        ptrs[i] = FAKE + 4
+        assert _lib.forward_raw(sh, *ptrs) == -9
+
+
+def test_backward_errors(lib):
+    sh = S()
+    ws = _lib.backward_workspace_bytes(sh)
+    args = [FAKE] * 14
+    assert _lib.backward_raw(sh, *args, ws - 1, 0) == -8
+    for i in (0, 1, 2, 3, 4, 5, 7, 8, 9, 10, 11, 13):
+        a = list(args)
+        a[i] = 0
+        assert _lib.backward_raw(sh, *a, ws, 0) == -1
+    a = list(args)
+    a[6] = FAKE + 8  # dS_T misaligned
+    assert _lib.backward_raw(sh, *a, ws, 0) == -9
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # B = 0: nothing to compute, nothing is launched, all pointers may be NULL
+    sh = S(B=0)
+    assert _lib.forward_raw(sh, *([0] * 10)) == 0
+    assert _lib.backward_raw(sh, *([0] * 14), 0, 0) == 0
+    # T = 0 and no state output requested: also nothing to launch
+    sh = S(T=0)
+    assert _lib.forward_raw(sh, *([0] * 10)) == 0
+    assert _lib.backward_raw(sh, *([0] * 14), 0, 0) == 0

@@ -1,0 +1,221 @@
+"""GPU parity of the HIP path (through the C ABI) against the float64
+oracle, element by element on the same seeded inputs.
+
+Bars: relative L2 <= 1e-5 on every output for fp32 inputs, <= 1e-2 for bf16
+inputs against the oracle fed the same bf16-rounded inputs (the rel() metric
+of mlx issue #4614).  Sizes span several tiles and ragged tails; the
+Qwen3.5-9B shape at T=2048 (the benchmark's workload and launch
+configuration) and the long-context shape are checked on sampled (batch row,
+kv group) slices that the oracle computes on their own.
+"""
+import numpy as np
+import pytest
+
+from gated_delta_rule_recurrence_amd import inputs
+from parity import TOL, compare, device_inputs, log, run_gpu, run_oracle, slice_group
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------- config 1
+@pytest.mark.parametrize("with_dST", [False, True])
+@pytest.mark.parametrize("chunk", [1, 2, 3, 64])
+def test_toy(cuda, with_dST, chunk):
+    p = inputs.toy(seed=0, with_dST=with_dST)
+    log(f"toy dST={with_dST} C={chunk}")
+    compare(run_gpu(p, cuda, chunk), run_oracle(p), TOL["f32"], "toy")
+
+
+# ---------------------------------------------------------------- config 2
+@pytest.mark.parametrize("B", [1, 2, 4, 8])
+def test_batch_rows(cuda, B):
+    p = inputs.batch_rows(B)
+    log(f"batch B={B}")
+    gpu = run_gpu(p, cuda, 16)
+    ref = run_oracle(p)
+    compare(gpu, ref, TOL["f32"], f"B={B}")
+    for b in range(1, B):  # rows past the first (unsloth-zoo PR #776)
+        sl = {n: (a[b:b + 1]) for n, a in gpu.items()}
+        rf = {n: (a[b:b + 1]) for n, a in ref.items()}
+        compare(sl, rf, TOL["f32"], f"B={B} row {b}")
+
+
+def test_batch_rows_bitwise_independent(cuda):
+    p8 = inputs.batch_rows(8)
+    g8 = run_gpu(p8, cuda, 64)
+    for b in (0, 3, 7):
+        p1 = inputs.batch_rows(8)
+        for n in ("q", "k", "v", "g", "beta", "dy"):
+            setattr(p1, n, getattr(p8, n)[b:b + 1].copy())
+        p1.B = 1
+        g1 = run_gpu(p1, cuda, 64)
+        for n in g1:
+            np.testing.assert_array_equal(g8[n][b:b + 1], g1[n], err_msg=f"row {b} {n}")
+
+
+# ---------------------------------------------------------------- config 3
+@pytest.mark.parametrize("heads", [(16, 48), (16, 16), (4, 12)])
+@pytest.mark.parametrize("normalised", [False, True])
+def test_strong_decay(cuda, heads, normalised):
+    p = inputs.strong_decay(*heads, normalised=normalised)
+    log(f"strong decay Hk/Hv={heads} normalised={normalised} "
+        f"mean log g={p.meta['mean_log_g']:.2f}")
+    compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["f32"], "strong")
+
+
+def test_strong_decay_short_chunks(cuda):
+    p = inputs.strong_decay(4, 12)
+    compare(run_gpu(p, cuda, 7), run_oracle(p), TOL["f32"], "strong C=7")
+
+
+# ---------------------------------------------------------------- config 4
+def test_qwen_bf16_T256_full(cuda):
+    p = inputs.qwen35_9b(256)
+    log("qwen35-9b bf16 T=256 full oracle")
+    compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["bf16"], "qwen T=256")
+
+
+def test_qwen_f32_T256_sampled(cuda):
+    p = inputs.qwen35_9b(256, dtype="f32")
+    gpu = run_gpu(p, cuda, 64)
+    for hk in (0, 15):
+        compare(slice_group(gpu, p, 0, hk), run_oracle(p, 0, hk), TOL["f32"],
+                f"qwen f32 T=256 kv{hk}")
+
+
+def test_qwen_bf16_T2048_sampled(cuda):
+    """The benchmark workload, in the benchmark's launch configuration."""
+    p = inputs.qwen35_9b(2048)
+    log("qwen35-9b bf16 T=2048 sampled groups")
+    gpu = run_gpu(p, cuda, 64)
+    for hk in (0, 9):
+        compare(slice_group(gpu, p, 0, hk), run_oracle(p, 0, hk), TOL["bf16"],
+                f"qwen T=2048 kv{hk}")
+
+
+# ---------------------------------------------------------------- config 5
+def test_long_context_sampled(cuda):
+    p = inputs.long_context()
+    log("long context B=4 T=8192 sampled group")
+    gpu = run_gpu(p, cuda, 64)
+    compare(slice_group(gpu, p, 3, 5), run_oracle(p, 3, 5), TOL["bf16"],
+            "long b3 kv5")
+
+
+# ---------------------------------------------------------------- properties
+def test_deterministic(cuda):
+    p = inputs.strong_decay(4, 12)
+    d = device_inputs(p, cuda)
+    a = run_gpu(p, cuda, 64, d)
+    b = run_gpu(p, cuda, 64, d)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+
+
+def test_chunk_invariance(cuda):
+    p = inputs.draw(2, 150, 2, 6, 64, 64, seed=5, normalised=True, S0_std=0.1,
+                    dST_std=1.0)
+    ref = run_gpu(p, cuda, 64)
+    for C in (1, 7, 50):
+        got = run_gpu(p, cuda, C)
+        compare(got, ref, 2e-6, f"C={C} vs C=64")
+
+
+def test_gqa_matches_repeat_expanded(cuda):
+    p = inputs.draw(1, 40, 2, 6, 32, 16, seed=9, normalised=True, S0_std=0.2)
+    rep = p.Hv // p.Hk
+    pe = inputs.draw(1, 40, 2, 6, 32, 16, seed=9, normalised=True, S0_std=0.2)
+    pe.q = np.repeat(p.q, rep, axis=2)
+    pe.k = np.repeat(p.k, rep, axis=2)
+    pe.Hk = p.Hv
+    a = run_gpu(p, cuda, 16)
+    e = run_gpu(pe, cuda, 16)
+    grp = lambda x: x.reshape(1, p.T, p.Hk, rep, -1).sum(3)
+    e["dq"], e["dk"] = grp(e["dq"]), grp(e["dk"])
+    compare(a, e, 1e-6, "gqa vs repeat")
+
+
+def test_segment_chaining(cuda):
+    """Two calls chained through S_T -> S0 and dS0 -> dS_T equal one call."""
+    import torch
+    from gated_delta_rule_recurrence_amd import ops
+    p = inputs.draw(1, 90, 2, 4, 48, 40, seed=13, normalised=True, S0_std=0.1,
+                    dST_std=1.0)
+    d = device_inputs(p, cuda)
+    y, ST, sv = ops.gdr_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"], chunk=16)
+    full = ops.gdr_backward(d["q"], d["k"], d["g"], d["beta"], sv, d["dy"], d["dST"])
+    cut = 37
+    A = {n: d[n][:, :cut].contiguous() for n in ("q", "k", "v", "g", "beta", "dy")}
+    Bn = {n: d[n][:, cut:].contiguous() for n in ("q", "k", "v", "g", "beta", "dy")}
+    y1, S1, sv1 = ops.gdr_forward(A["q"], A["k"], A["v"], A["g"], A["beta"], d["S0"], chunk=16)
+    y2, S2, sv2 = ops.gdr_forward(Bn["q"], Bn["k"], Bn["v"], Bn["g"], Bn["beta"], S1, chunk=16)
+    g2 = ops.gdr_backward(Bn["q"], Bn["k"], Bn["g"], Bn["beta"], sv2, Bn["dy"], d["dST"])
+    g1 = ops.gdr_backward(A["q"], A["k"], A["g"], A["beta"], sv1, A["dy"], g2[5])
+    torch.cuda.synchronize()
+    np_ = lambda t: t.double().cpu().numpy()
+    one = dict(y=y, S_T=ST, dq=full[0], dk=full[1], dv=full[2], dg=full[3],
+               dbeta=full[4], dS0=full[5])
+    two = dict(y=torch.cat([y1, y2], 1), S_T=S2, dq=torch.cat([g1[0], g2[0]], 1),
+               dk=torch.cat([g1[1], g2[1]], 1), dv=torch.cat([g1[2], g2[2]], 1),
+               dg=torch.cat([g1[3], g2[3]], 1), dbeta=torch.cat([g1[4], g2[4]], 1),
+               dS0=g1[5])
+    compare({k: np_(v) for k, v in two.items()}, {k: np_(v) for k, v in one.items()},
+            2e-6, "chained")
+
+
+@pytest.mark.parametrize("dims", [(5, 3), (36, 20), (100, 70), (256, 256), (130, 256)])
+def test_ragged_and_max_dims(cuda, dims):
+    Dk, Dv = dims
+    p = inputs.draw(1, 45, 1, 2, Dk, Dv, seed=17, normalised=True, S0_std=0.2,
+                    dST_std=1.0)
+    log(f"dims Dk={Dk} Dv={Dv}")
+    compare(run_gpu(p, cuda, 16), run_oracle(p), TOL["f32"], f"Dk={Dk} Dv={Dv}")
+
+
+def test_bf16_small(cuda):
+    p = inputs.draw(2, 70, 2, 4, 64, 32, seed=19, normalised=True, S0_std=0.1,
+                    dST_std=1.0, dtype="bf16")
+    compare(run_gpu(p, cuda, 32), run_oracle(p), TOL["bf16"], "bf16 small")
+
+
+def test_T1_and_empty(cuda):
+    import torch
+    from gated_delta_rule_recurrence_amd import ops
+    p = inputs.draw(1, 1, 1, 2, 8, 8, seed=23, S0_std=0.5, dST_std=1.0)
+    compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["f32"], "T=1")
+    # T = 0: S_T = S0 and dS0 = dS_T
+    p0 = inputs.draw(1, 0, 1, 2, 8, 8, seed=23, S0_std=0.5, dST_std=1.0)
+    d = device_inputs(p0, cuda)
+    y, ST, sv = ops.gdr_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"])
+    grads = ops.gdr_backward(d["q"], d["k"], d["g"], d["beta"], sv, d["dy"], d["dST"])
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(ST, d["S0"])
+    assert torch.equal(grads[5], d["dST"])
+
+
+def test_checkpoints_hold_states(cuda):
+    """The saved state checkpoints are S_{jC} of the recurrence."""
+    import oracle.gdr_oracle as O
+    p = inputs.draw(1, 20, 1, 2, 16, 8, seed=29, normalised=True, S0_std=0.3)
+    res = run_gpu(p, cuda, 6, want_saved=True)
+    ck = res["_saved"].ckpt[: 4 * 4 * 2 * 8 * 16].view(dtype=__import__("torch").float32)
+    ck = ck.reshape(1, 2, 4, 8, 16).double().cpu().numpy()
+    _, _, states = O.forward(p.q, p.k, p.v, p.g, p.beta, p.S0, keep_states=True)
+    for j in range(4):
+        assert O.rel_l2(ck[:, :, j], states[6 * j]) <= 1e-6
+
+
+def test_autograd_function(cuda):
+    import torch
+    from gated_delta_rule_recurrence_amd import ops
+    p = inputs.draw(1, 33, 2, 4, 32, 16, seed=31, normalised=True, S0_std=0.1)
+    d = device_inputs(p, cuda)
+    leaves = [d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "S0")]
+    y, ST = ops.gated_delta_rule(*leaves, chunk=8)
+    (y * d["dy"]).sum().backward()
+    ref = run_oracle(p)
+    import oracle.gdr_oracle as O
+    for leaf, name in zip(leaves, ("dq", "dk", "dv", "dg", "dbeta", "dS0")):
+        err = O.rel_l2(leaf.grad.double().cpu().numpy(), ref[name])
+        assert err <= 1e-5, (name, err)
