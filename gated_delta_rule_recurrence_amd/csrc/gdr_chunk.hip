@@ -91,11 +91,28 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
   for (int j0 = 0; j0 < Dk; j0 += 64) {
     float* sq = sm + L::A;
     float* sk = sm + L::A + kN * kNP;
-    for (int idx = tid; idx < kN * 64; idx += kThreads) {
-      const int s = idx >> 6, jj = idx & 63, j = j0 + jj;
-      const bool ok = s < n && j < Dk;
-      sq[s * kNP + jj] = ok ? ld(q, qk_index(s, j)) : 0.f;
-      sk[s * kNP + jj] = ok ? ld(k, qk_index(s, j)) : 0.f;
+    {
+      constexpr int U = (kN * 64) / kThreads;
+      TIn rq[U], rk[U];
+      uint32_t okm = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = tid + kThreads * u;
+        const int s = idx >> 6, j = j0 + (idx & 63);
+        const bool ok = s < n && j < Dk;
+        const int64_t o = ok ? qk_index(s, j) : 0;
+        rq[u] = q[o];
+        rk[u] = k[o];
+        okm |= (uint32_t)ok << u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = tid + kThreads * u;
+        const int s = idx >> 6, jj = idx & 63;
+        const bool ok = (okm >> u) & 1;
+        sq[s * kNP + jj] = ok ? to_f32(rq[u]) : 0.f;
+        sk[s * kNP + jj] = ok ? to_f32(rk[u]) : 0.f;
+      }
     }
     __syncthreads();
 #pragma unroll 1
@@ -157,21 +174,65 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
     float* sY = sH + kIB * L::DKP;  // [kIB][kNP] dy
     float* sE = sY + kIB * kNP;     // [kIB][kNP] e
     float* sC = sE + kIB * kNP;     // [kIB][kNP] c
-    for (int i0 = 0; i0 < Dv; i0 += kIB) {
-      for (int idx = tid; idx < kIB * L::DKP; idx += kThreads) {
-        const int ii = idx / L::DKP, j = idx % L::DKP, i = i0 + ii;
+    const TIn* __restrict__ dyh = dy + row_index(0, 0);
+    const float* __restrict__ Eh = a.E + row_index(0, 0);
+    const float* __restrict__ Ch = a.C + row_index(0, 0);
+    const int64_t tstride = (int64_t)Hv * Dv;
+    // One Dv block of S0, H1 (kIB x DKP) and of dy, e, c (n x kIB), fetched
+    // into registers with unconditional loads from clamped offsets.
+    constexpr int US = (kIB * L::DKP) / kThreads;  // = J
+    constexpr int UX = (kIB * kN) / kThreads;      // = 2
+    static_assert(US * kThreads == kIB * L::DKP && UX * kThreads == kIB * kN, "tiling");
+    float fs[US], fh[US], fe[UX], fc[UX];
+    TIn fy[UX];
+    uint32_t fok = 0;
+    auto fetch = [&](int i0) {
+      fok = 0;
+#pragma unroll
+      for (int u = 0; u < US; ++u) {
+        const int idx = tid + kThreads * u;
+        const int ii = idx / L::DKP, j = idx - ii * L::DKP, i = i0 + ii;
         const bool ok = i < Dv && j < Dk;
-        sS[idx] = ok ? S0[(int64_t)i * Dk + j] : 0.f;
-        sH[idx] = ok ? H1[(int64_t)i * Dk + j] : 0.f;
+        const int64_t o = ok ? (int64_t)i * Dk + j : 0;
+        fs[u] = S0[o];
+        fh[u] = H1[o];
+        fok |= (uint32_t)ok << u;
       }
-      for (int idx = tid; idx < kIB * kN; idx += kThreads) {
+#pragma unroll
+      for (int u = 0; u < UX; ++u) {
+        const int idx = tid + kThreads * u;
         const int ii = idx % kIB, t = idx / kIB, i = i0 + ii;  // rows fastest
         const bool ok = i < Dv && t < n;
-        sY[ii * kNP + t] = ok ? ld(dy, row_index(t, i)) : 0.f;
-        sE[ii * kNP + t] = ok ? a.E[row_index(t, i)] : 0.f;
-        sC[ii * kNP + t] = ok ? a.C[row_index(t, i)] : 0.f;
+        const int64_t o = ok ? t * tstride + i : 0;
+        fy[u] = dyh[o];
+        fe[u] = Eh[o];
+        fc[u] = Ch[o];
+        fok |= (uint32_t)ok << (16 + u);
       }
-      __syncthreads();
+    };
+    auto deposit = [&]() {
+#pragma unroll
+      for (int u = 0; u < US; ++u) {
+        const int idx = tid + kThreads * u;
+        const bool ok = (fok >> u) & 1;
+        sS[idx] = ok ? fs[u] : 0.f;
+        sH[idx] = ok ? fh[u] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < UX; ++u) {
+        const int idx = tid + kThreads * u;
+        const int ii = idx % kIB, t = idx / kIB;
+        const bool ok = (fok >> (16 + u)) & 1;
+        sY[ii * kNP + t] = ok ? to_f32(fy[u]) : 0.f;
+        sE[ii * kNP + t] = ok ? fe[u] : 0.f;
+        sC[ii * kNP + t] = ok ? fc[u] : 0.f;
+      }
+    };
+    fetch(0);
+    deposit();
+    __syncthreads();
+    for (int i0 = 0; i0 < Dv; i0 += kIB) {
+      if (i0 + kIB < Dv) fetch(i0 + kIB);
 #pragma unroll 1
       for (int ii = 0; ii < kIB; ++ii) {
         float sj[J], hj[J], yu[4], cu[4], eu[4], ew[2];
@@ -209,6 +270,10 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
         }
       }
       __syncthreads();
+      if (i0 + kIB < Dv) {
+        deposit();
+        __syncthreads();
+      }
     }
 
     // ---- per-head O(n^2) stage -------------------------------------------
@@ -372,11 +437,27 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
   float* sKf = sm + L::A;
   float* sQf = sm + L::A + kIB * L::DKP;
   for (int s0 = 0; s0 < n; s0 += kIB) {
-    for (int idx = tid; idx < kIB * L::DKP; idx += kThreads) {
-      const int ss = idx / L::DKP, j = idx % L::DKP, s = s0 + ss;
-      const bool ok = s < n && j < Dk;
-      sKf[idx] = ok ? ld(k, qk_index(s, j)) : 0.f;
-      sQf[idx] = ok ? ld(q, qk_index(s, j)) : 0.f;
+    {
+      constexpr int U = (kIB * L::DKP) / kThreads;
+      TIn rk[U], rq[U];
+      uint32_t okm = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = tid + kThreads * u;
+        const int ss = idx / L::DKP, j = idx - ss * L::DKP, s = s0 + ss;
+        const bool ok = s < n && j < Dk;
+        const int64_t o = ok ? qk_index(s, j) : 0;
+        rk[u] = k[o];
+        rq[u] = q[o];
+        okm |= (uint32_t)ok << u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = tid + kThreads * u;
+        const bool ok = (okm >> u) & 1;
+        sKf[idx] = ok ? to_f32(rk[u]) : 0.f;
+        sQf[idx] = ok ? to_f32(rq[u]) : 0.f;
+      }
     }
     __syncthreads();
 #pragma unroll 1

@@ -26,14 +26,12 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 // float -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
 template <>
 __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
-  uint32_t u = __float_as_uint(x);
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t quiet = (u >> 16) | 0x0040u;
+  const bool nan = (u & 0x7fffffffu) > 0x7f800000u;
   bf16 r;
-  if ((u & 0x7fffffffu) > 0x7f800000u) {
-    r.bits = static_cast<uint16_t>((u >> 16) | 0x0040u);
-  } else {
-    u += 0x7fffu + ((u >> 16) & 1u);
-    r.bits = static_cast<uint16_t>(u >> 16);
-  }
+  r.bits = static_cast<uint16_t>(nan ? quiet : rounded);
   return r;
 }
 

@@ -46,58 +46,69 @@ struct SweepLayout {
 };
 
 // Fetch one block of kStage steps (steps blk*kStage ...) into registers.
-// x is the per-row tensor [B][T][Hv][Dv] (v or dy).
+// x is the per-row tensor [B][T][Hv][Dv] (v or dy).  The loads are
+// unconditional and branch-free: an element outside the tensor is read from
+// offset 0 of the same tensor and masked to zero later, in stage_store, so
+// no load has to complete before the current block is consumed.
 template <typename TIn, int NC, int R, int N>
 __device__ __forceinline__ void stage_fetch(
-    float (&reg)[N], int blk, int T, int Hk, int Hv, int Dk,
+    TIn (&raw)[N], uint64_t& okmask, int blk, int T, int Hk, int Hv, int Dk,
     int Dv, int b, int h, int hk, int rowbase, const TIn* __restrict__ k,
     const TIn* __restrict__ q, const TIn* __restrict__ x,
     const TIn* __restrict__ g, const TIn* __restrict__ beta) {
   using Lo = SweepLayout<NC, R>;
-  static_assert(N == Lo::PF, "prefetch register count");
+  static_assert(N == Lo::PF && N <= 64, "prefetch register count");
   const int tid = threadIdx.x;
+  const int64_t bt0 = (int64_t)b * T + (int64_t)blk * kStage;  // (b, first t)
+  uint64_t mask = 0;
 #pragma unroll
-  for (int u = 0; u < Lo::PF; ++u) {
+  for (int u = 0; u < N; ++u) {
     const int idx = tid + kThreads * u;
-    float val = 0.f;
-    if (idx < Lo::Q_OFF) {
-      const int s = idx / Lo::DKP, col = idx % Lo::DKP;
-      const int t = blk * kStage + s;
-      if (t < T && col < Dk)
-        val = ld(k, ((int64_t)(b * (int64_t)T + t) * Hk + hk) * Dk + col);
-    } else if (idx < Lo::X_OFF) {
-      const int j = idx - Lo::Q_OFF;
-      const int s = j / Lo::DKP, col = j % Lo::DKP;
-      const int t = blk * kStage + s;
-      if (t < T && col < Dk)
-        val = ld(q, ((int64_t)(b * (int64_t)T + t) * Hk + hk) * Dk + col);
-    } else if (idx < Lo::G_OFF) {
-      const int j = idx - Lo::X_OFF;
-      const int s = j / Lo::RW, r = j % Lo::RW;
-      const int t = blk * kStage + s;
-      const int row = rowbase + r;
-      if (t < T && row < Dv)
-        val = ld(x, ((int64_t)(b * (int64_t)T + t) * Hv + h) * Dv + row);
-    } else if (idx < Lo::B_OFF) {
-      const int t = blk * kStage + (idx - Lo::G_OFF);
-      if (t < T) val = ld(g, (int64_t)(b * (int64_t)T + t) * Hv + h);
-    } else if (idx < Lo::SIZE) {
-      const int t = blk * kStage + (idx - Lo::B_OFF);
-      if (t < T) val = ld(beta, (int64_t)(b * (int64_t)T + t) * Hv + h);
+    // decode the slot without branches
+    const bool in_k = idx < Lo::Q_OFF;
+    const bool in_q = !in_k && idx < Lo::X_OFF;
+    const bool in_x = !in_k && !in_q && idx < Lo::G_OFF;
+    const bool in_g = idx >= Lo::G_OFF && idx < Lo::B_OFF;
+    const bool in_b = idx >= Lo::B_OFF && idx < Lo::SIZE;
+    const int jk = in_k ? idx : idx - Lo::Q_OFF;  // offset inside the k or q block
+    const int sk = jk / Lo::DKP, col = jk - sk * Lo::DKP;
+    const int jx = idx - Lo::X_OFF;
+    const int sx = jx / Lo::RW, r = jx - sx * Lo::RW;
+    const int sg = in_g ? idx - Lo::G_OFF : idx - Lo::B_OFF;
+    const int s = (in_k || in_q) ? sk : (in_x ? sx : sg);
+    const bool t_ok = (int64_t)blk * kStage + s < T;
+    bool ok;
+    int64_t off;
+    const TIn* base;
+    if (in_k || in_q) {
+      ok = t_ok && col < Dk;
+      off = ((bt0 + s) * Hk + hk) * Dk + col;
+      base = in_k ? k : q;
+    } else if (in_x) {
+      ok = t_ok && rowbase + r < Dv;
+      off = ((bt0 + s) * Hv + h) * Dv + rowbase + r;
+      base = x;
+    } else {
+      ok = t_ok && (in_g || in_b);
+      off = (bt0 + s) * Hv + h;
+      base = in_g ? g : beta;
     }
-    reg[u] = val;
+    raw[u] = base[ok ? off : 0];
+    mask |= (uint64_t)ok << u;
   }
+  okmask = mask;
 }
 
-template <int NC, int R, int N>
+template <typename TIn, int NC, int R, int N>
 __device__ __forceinline__ void stage_store(float* __restrict__ buf,
-                                            const float (&reg)[N]) {
+                                            const TIn (&raw)[N],
+                                            uint64_t okmask) {
   using Lo = SweepLayout<NC, R>;
   static_assert(N == Lo::PF, "prefetch register count");
 #pragma unroll
-  for (int u = 0; u < Lo::PF; ++u) {
+  for (int u = 0; u < N; ++u) {
     const int idx = threadIdx.x + kThreads * u;
-    if (idx < Lo::SIZE) buf[idx] = reg[u];
+    if (idx < Lo::SIZE) buf[idx] = ((okmask >> u) & 1) ? to_f32(raw[u]) : 0.f;
   }
 }
 
@@ -182,11 +193,12 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   tile_load<NC, R>(S, a.S0 ? a.S0 + bh * mat : nullptr, row0, p, Dk, Dv);
 
   const int nblk = (T + kStage - 1) / kStage;
-  float pre[Lo::PF];
+  TIn pre[Lo::PF];
+  uint64_t pre_ok = 0;
   if (nblk > 0) {
-    stage_fetch<TIn, NC, R>(pre, 0, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q,
+    stage_fetch<TIn, NC, R>(pre, pre_ok, 0, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q,
                             v, g, beta);
-    stage_store<NC, R>(lds[0], pre);
+    stage_store<TIn, NC, R>(lds[0], pre, pre_ok);
   }
   __syncthreads();
 
@@ -196,10 +208,12 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   const int my_row = row0 + p;  // row written by lanes p < R
   const bool writer = (p < R) && (my_row < Dv);
 
+  int to_ckpt = 0;  // steps until the next checkpoint (t % L == 0)
+  int ckpt_slot = 0;
   for (int blk = 0; blk < nblk; ++blk) {
     const float* __restrict__ cur = lds[blk & 1];
     if (blk + 1 < nblk)
-      stage_fetch<TIn, NC, R>(pre, blk + 1, T, Hk, Hv, Dk, Dv, b, h, hk,
+      stage_fetch<TIn, NC, R>(pre, pre_ok, blk + 1, T, Hk, Hv, Dk, Dv, b, h, hk,
                               rowbase, k, q, v, g, beta);
     const int tbase = blk * kStage;
     const int nsteps = min(kStage, T - tbase);
@@ -208,9 +222,14 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
       float kk[NC], qq[NC];
       lds_cols<NC>(kk, cur + Lo::K_OFF + s * Lo::DKP, p);
       lds_cols<NC>(qq, cur + Lo::Q_OFF + s * Lo::DKP, p);
-      if (a.Sck != nullptr && (t % a.L) == 0)
-        tile_store<NC, R>(S, a.Sck + (bh * a.nch + t / a.L) * mat, row0, p,
-                          Dk, Dv);
+      if (to_ckpt == 0) {
+        if (a.Sck != nullptr)
+          tile_store<NC, R>(S, a.Sck + (bh * a.nch + ckpt_slot) * mat, row0, p,
+                            Dk, Dv);
+        ++ckpt_slot;
+        to_ckpt = a.L;
+      }
+      --to_ckpt;
       // dots on the state before step t: S k_t (for the update) and
       // S q_{t-1} (= y_{t-1}, the read-out of the previous step)
       float pk[R], pq[R];
@@ -242,11 +261,11 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) S[r][c] = fmaf(gt, S[r][c], d[r] * kk[c]);
+        for (int c = 0; c < NC; ++c) S[r][c] = fmaf(d[r], kk[c], gt * S[r][c]);
 #pragma unroll
       for (int c = 0; c < NC; ++c) qprev[c] = qq[c];
     }
-    if (blk + 1 < nblk) stage_store<NC, R>(lds[(blk + 1) & 1], pre);
+    if (blk + 1 < nblk) stage_store<TIn, NC, R>(lds[(blk + 1) & 1], pre, pre_ok);
     __syncthreads();
   }
 
@@ -297,21 +316,25 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
                       Dv);
 
   const int nblk = (T + kStage - 1) / kStage;
-  float pre[Lo::PF];
+  TIn pre[Lo::PF];
+  uint64_t pre_ok = 0;
   if (nblk > 0) {
-    stage_fetch<TIn, NC, R>(pre, nblk - 1, T, Hk, Hv, Dk, Dv, b, h, hk,
+    stage_fetch<TIn, NC, R>(pre, pre_ok, nblk - 1, T, Hk, Hv, Dk, Dv, b, h, hk,
                             rowbase, k, q, dy, g, beta);
-    stage_store<NC, R>(lds[(nblk - 1) & 1], pre);
+    stage_store<TIn, NC, R>(lds[(nblk - 1) & 1], pre, pre_ok);
   }
   __syncthreads();
 
   const int my_row = row0 + p;
   const bool writer = (p < R) && (my_row < Dv);
 
+  // H after step t is saved when t % L == 0 and t > 0, in slot t / L - 1
+  int last_chunk = (T - 1) / (a.L > 0 ? a.L : 1);
+  int to_ckpt = T - 1 - last_chunk * a.L;  // steps until t % L == 0
   for (int blk = nblk - 1; blk >= 0; --blk) {
     const float* __restrict__ cur = lds[blk & 1];
     if (blk > 0)
-      stage_fetch<TIn, NC, R>(pre, blk - 1, T, Hk, Hv, Dk, Dv, b, h, hk,
+      stage_fetch<TIn, NC, R>(pre, pre_ok, blk - 1, T, Hk, Hv, Dk, Dv, b, h, hk,
                               rowbase, k, q, dy, g, beta);
     const int tbase = blk * kStage;
     const int nsteps = min(kStage, T - tbase);
@@ -347,11 +370,16 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
 #pragma unroll
         for (int j = 0; j < NC; ++j)
           H[r][j] = gt * fmaf(-dvr[r], kk[j], H[r][j]);
-      if (t > 0 && (t % a.L) == 0)
-        tile_store<NC, R>(H, a.Hck + (bh * a.nch + t / a.L - 1) * mat, row0,
-                          p, Dk, Dv);
+      if (to_ckpt == 0) {
+        if (t > 0)
+          tile_store<NC, R>(H, a.Hck + (bh * a.nch + last_chunk - 1) * mat,
+                            row0, p, Dk, Dv);
+        --last_chunk;
+        to_ckpt = a.L;
+      }
+      --to_ckpt;
     }
-    if (blk > 0) stage_store<NC, R>(lds[(blk - 1) & 1], pre);
+    if (blk > 0) stage_store<TIn, NC, R>(lds[(blk - 1) & 1], pre, pre_ok);
     __syncthreads();
   }
   if (a.dS0 != nullptr) tile_store<NC, R>(H, a.dS0 + bh * mat, row0, p, Dk, Dv);
