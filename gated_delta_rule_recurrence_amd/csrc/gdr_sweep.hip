@@ -8,10 +8,9 @@
 //
 // Reverse sweep: the state-gradient recurrence of the VJP, swept backwards in
 // time.  With H = dL/dS after step t (dS_T at t = T):
-//     G = H + outer(dy_t, q_t);   c_t = G k_t;   dv_t = beta_t c_t;
-//     H <- g_t (G - outer(dv_t, k_t))
-// It writes dv, c_t, dS0 and H at every chunk boundary.  Only multiplications
-// by g occur, never a division.
+//     G = H + outer(dy_t, q_t);   c_t = G k_t = H k_t + dy_t (q_t . k_t);
+//     dv_t = beta_t c_t;          H <- g_t (G - outer(dv_t, k_t))
+// It writes dv, c_t, dS0 and H at every chunk boundary.
 //
 // Mapping.  A workgroup of 256 threads owns 16 R consecutive rows of the
 // [Dv x Dk] state of one (batch row, value head): 16 row groups of R rows, one
@@ -21,16 +20,33 @@
 // the state never leaves the chip between checkpoints.  Rows are independent
 // in both recurrences (they couple only through the outputs), which is what
 // lets a head be split over several workgroups.  k, q, v / dy, g and beta are
-// staged into LDS 16 steps at a time, double-buffered, the next block being
-// fetched into registers while the current one is consumed.
+// staged into LDS 16 steps at a time with 16-byte loads, double-buffered: the
+// next block is fetched into registers while the current one is consumed.
+// Inside a block the step loop is unrolled by two over two operand register
+// sets, so the LDS operands of step t+1 are read while step t computes.
+//
+// Decay is applied lazily: the state is kept as S = sigma * St with a scalar
+// sigma shared by the workgroup (every row of one head sees the same g_t).
+// A step multiplies sigma by g_t and adds (d / sigma) k^T to St, one FMA per
+// element instead of a multiply and an FMA.  When sigma falls below 2^-60 it
+// is folded back into St (St *= sigma, sigma = 1), so sigma never underflows,
+// 1/sigma <= 2^60, and the decay never has to be divided out: sigma is only a
+// running product of g.  Contribution s reaches step t through the same t - s
+// roundings as in the direct form.  The reverse sweep keeps H = tau * Ht the
+// same way.
 #include "gdr_device.h"
 #include "gdr_internal.h"
+
+#ifndef GDR_SWEEP_R
+#define GDR_SWEEP_R 2
+#endif
 
 namespace gdr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStage = 16;  // time steps per LDS block
+constexpr int kStage = 16;            // time steps per LDS block
+constexpr float kRescale = 0x1p-60f;  // fold the lazy decay below this
 
 template <int NC, int R>
 struct SweepLayout {
@@ -41,76 +57,149 @@ struct SweepLayout {
   static constexpr int X_OFF = 2 * kStage * DKP;  // v (forward) or dy (reverse)
   static constexpr int G_OFF = X_OFF + kStage * RW;
   static constexpr int B_OFF = G_OFF + kStage;
-  static constexpr int SIZE = B_OFF + kStage;
-  static constexpr int PF = (SIZE + kThreads - 1) / kThreads;
+  static constexpr int QK_OFF = B_OFF + kStage;   // q_t . k_t (reverse sweep)
+  static constexpr int BUF = QK_OFF + kStage;     // one LDS buffer, floats
 };
 
-// Fetch one block of kStage steps (steps blk*kStage ...) into registers.
-// x is the per-row tensor [B][T][Hv][Dv] (v or dy).  The loads are
-// unconditional and branch-free: an element outside the tensor is read from
-// offset 0 of the same tensor and masked to zero later, in stage_store, so
-// no load has to complete before the current block is consumed.
-template <typename TIn, int NC, int R, int N>
-__device__ __forceinline__ void stage_fetch(
-    TIn (&raw)[N], uint64_t& okmask, int blk, int T, int Hk, int Hv, int Dk,
-    int Dv, int b, int h, int hk, int rowbase, const TIn* __restrict__ k,
-    const TIn* __restrict__ q, const TIn* __restrict__ x,
-    const TIn* __restrict__ g, const TIn* __restrict__ beta) {
-  using Lo = SweepLayout<NC, R>;
-  static_assert(N == Lo::PF && N <= 64, "prefetch register count");
-  const int tid = threadIdx.x;
-  const int64_t bt0 = (int64_t)b * T + (int64_t)blk * kStage;  // (b, first t)
-  uint64_t mask = 0;
+// 16-byte vector of raw input elements.
+struct alignas(16) Raw16 {
+  uint32_t w[4];
+};
+
+template <typename TIn>
+__device__ __forceinline__ void unpack(const Raw16& r, float* out);
+
+template <>
+__device__ __forceinline__ void unpack<float>(const Raw16& r, float* out) {
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const int idx = tid + kThreads * u;
-    // decode the slot without branches
-    const bool in_k = idx < Lo::Q_OFF;
-    const bool in_q = !in_k && idx < Lo::X_OFF;
-    const bool in_x = !in_k && !in_q && idx < Lo::G_OFF;
-    const bool in_g = idx >= Lo::G_OFF && idx < Lo::B_OFF;
-    const bool in_b = idx >= Lo::B_OFF && idx < Lo::SIZE;
-    const int jk = in_k ? idx : idx - Lo::Q_OFF;  // offset inside the k or q block
-    const int sk = jk / Lo::DKP, col = jk - sk * Lo::DKP;
-    const int jx = idx - Lo::X_OFF;
-    const int sx = jx / Lo::RW, r = jx - sx * Lo::RW;
-    const int sg = in_g ? idx - Lo::G_OFF : idx - Lo::B_OFF;
-    const int s = (in_k || in_q) ? sk : (in_x ? sx : sg);
-    const bool t_ok = (int64_t)blk * kStage + s < T;
-    bool ok;
-    int64_t off;
-    const TIn* base;
-    if (in_k || in_q) {
-      ok = t_ok && col < Dk;
-      off = ((bt0 + s) * Hk + hk) * Dk + col;
-      base = in_k ? k : q;
-    } else if (in_x) {
-      ok = t_ok && rowbase + r < Dv;
-      off = ((bt0 + s) * Hv + h) * Dv + rowbase + r;
-      base = x;
-    } else {
-      ok = t_ok && (in_g || in_b);
-      off = (bt0 + s) * Hv + h;
-      base = in_g ? g : beta;
-    }
-    raw[u] = base[ok ? off : 0];
-    mask |= (uint64_t)ok << u;
-  }
-  okmask = mask;
+  for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r.w[i]);
 }
 
-template <typename TIn, int NC, int R, int N>
-__device__ __forceinline__ void stage_store(float* __restrict__ buf,
-                                            const TIn (&raw)[N],
-                                            uint64_t okmask) {
-  using Lo = SweepLayout<NC, R>;
-  static_assert(N == Lo::PF, "prefetch register count");
+template <>
+__device__ __forceinline__ void unpack<bf16>(const Raw16& r, float* out) {
 #pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const int idx = threadIdx.x + kThreads * u;
-    if (idx < Lo::SIZE) buf[idx] = ((okmask >> u) & 1) ? to_f32(raw[u]) : 0.f;
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = __uint_as_float(r.w[i] << 16);
+    out[2 * i + 1] = __uint_as_float(r.w[i] & 0xffff0000u);
   }
 }
+
+// Global -> register -> LDS staging of one block of kStage steps.
+// VEC: k/q rows and v/dy rows are read as 16-byte vectors (needs Dk and Dv to
+// be multiples of the vector width; the base pointers are 16-byte aligned by
+// the ABI).  Otherwise element by element.  Loads are unconditional and
+// branch-free (an out-of-range slot reads offset 0 of the same tensor and is
+// zeroed on the way into LDS), so no load has to complete before the block in
+// flight is consumed.
+template <typename TIn, int NC, int R, bool VEC>
+struct Stager {
+  using Lo = SweepLayout<NC, R>;
+  static constexpr int VW = VEC ? 16 / (int)sizeof(TIn) : 1;  // elements/slot
+  static constexpr int NKV = kStage * Lo::DKP / VW;  // slots in a k block
+  static constexpr int NXV = kStage * Lo::RW / VW;   // slots in an x block
+  static constexpr int SK = (NKV + kThreads - 1) / kThreads;
+  static constexpr int SX = (NXV + kThreads - 1) / kThreads;
+  static_assert(Lo::DKP % VW == 0 && Lo::RW % VW == 0, "vector width");
+  static_assert(2 * SK + SX + 1 <= 64, "ok mask bits");
+  using Slot = typename std::conditional<VEC, Raw16, TIn>::type;
+
+  Slot kr[SK], qr[SK], xr[SX];
+  TIn gb;  // g (threads 0..15) or beta (threads 16..31) of one step
+  uint64_t ok;
+
+  __device__ __forceinline__ void fetch(int blk, int T, int Hk, int Hv,
+                                        int Dk, int Dv, int b, int h, int hk,
+                                        int rowbase, const TIn* __restrict__ k,
+                                        const TIn* __restrict__ q,
+                                        const TIn* __restrict__ x,
+                                        const TIn* __restrict__ g,
+                                        const TIn* __restrict__ beta) {
+    const int tid = threadIdx.x;
+    const int t0 = blk * kStage;
+    uint64_t m = 0;
+#pragma unroll
+    for (int u = 0; u < SK; ++u) {
+      const int vi = tid + kThreads * u;
+      const int s = vi / (Lo::DKP / VW);
+      const int c = (vi - s * (Lo::DKP / VW)) * VW;
+      const bool good = vi < NKV && t0 + s < T && c < Dk;
+      const int64_t off =
+          good ? (((int64_t)b * T + t0 + s) * Hk + hk) * Dk + c : 0;
+      kr[u] = *reinterpret_cast<const Slot*>(k + off);
+      qr[u] = *reinterpret_cast<const Slot*>(q + off);
+      m |= (uint64_t)good << u;
+    }
+#pragma unroll
+    for (int u = 0; u < SX; ++u) {
+      const int vi = tid + kThreads * u;
+      const int s = vi / (Lo::RW / VW);
+      const int r = (vi - s * (Lo::RW / VW)) * VW;
+      const bool good = vi < NXV && t0 + s < T && rowbase + r < Dv;
+      const int64_t off =
+          good ? (((int64_t)b * T + t0 + s) * Hv + h) * Dv + rowbase + r : 0;
+      xr[u] = *reinterpret_cast<const Slot*>(x + off);
+      m |= (uint64_t)good << (SK + u);
+    }
+    {
+      const int s = tid & 15;
+      const bool good = tid < 32 && t0 + s < T;
+      const int64_t off = good ? ((int64_t)b * T + t0 + s) * Hv + h : 0;
+      gb = (tid < 16 ? g : beta)[off];
+      m |= (uint64_t)good << (SK + SX);
+    }
+    ok = m;
+  }
+
+  __device__ __forceinline__ void store(float* __restrict__ buf) const {
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int u = 0; u < SK; ++u) {
+      const int vi = tid + kThreads * u;
+      if (vi < NKV) {
+        const bool good = (ok >> u) & 1;
+        const int s = vi / (Lo::DKP / VW);
+        const int c = (vi - s * (Lo::DKP / VW)) * VW;
+        write(buf + Lo::K_OFF + s * Lo::DKP + c, kr[u], good);
+        write(buf + Lo::Q_OFF + s * Lo::DKP + c, qr[u], good);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < SX; ++u) {
+      const int vi = tid + kThreads * u;
+      if (vi < NXV) {
+        const bool good = (ok >> (SK + u)) & 1;
+        const int s = vi / (Lo::RW / VW);
+        const int r = (vi - s * (Lo::RW / VW)) * VW;
+        write(buf + Lo::X_OFF + s * Lo::RW + r, xr[u], good);
+      }
+    }
+    if (tid < 32) {
+      const bool good = (ok >> (SK + SX)) & 1;
+      buf[(tid < 16 ? Lo::G_OFF : Lo::B_OFF) + (tid & 15)] =
+          good ? to_f32(gb) : 0.f;
+    }
+  }
+
+ private:
+  __device__ __forceinline__ static void write(float* dst, const Raw16& r,
+                                               bool good) {
+    float v[VW];
+    unpack<TIn>(r, v);
+#pragma unroll
+    for (int i = 0; i < VW; i += 4) {
+      float4 f;
+      f.x = good ? v[i] : 0.f;
+      f.y = good ? v[i + 1] : 0.f;
+      f.z = good ? v[i + 2] : 0.f;
+      f.w = good ? v[i + 3] : 0.f;
+      *reinterpret_cast<float4*>(dst + i) = f;
+    }
+  }
+  __device__ __forceinline__ static void write(float* dst, const TIn& r,
+                                               bool good) {
+    *dst = good ? to_f32(r) : 0.f;
+  }
+};
 
 // Select element `i` of a small register array without dynamic indexing.
 template <int N>
@@ -122,7 +211,7 @@ __device__ __forceinline__ float pick(const float (&a)[N], int i) {
   return r;
 }
 
-// Load/store this lane's part of rows [row0, row0+R) of a [Dv][Dk] matrix.
+// Load this lane's part of rows [row0, row0+R) of a [Dv][Dk] matrix.
 template <int NC, int R>
 __device__ __forceinline__ void tile_load(float (&S)[R][NC],
                                           const float* __restrict__ M, int row0,
@@ -139,18 +228,35 @@ __device__ __forceinline__ void tile_load(float (&S)[R][NC],
     }
 }
 
+// Store scale * (this lane's part of rows [row0, row0+R)).
 template <int NC, int R>
-__device__ __forceinline__ void tile_store(const float (&S)[R][NC],
+__device__ __forceinline__ void tile_store(const float (&S)[R][NC], float scale,
                                            float* __restrict__ M, int row0,
                                            int p, int Dk, int Dv) {
+  float v[R][NC];
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int col = 4 * p + 64 * (c / 4) + (c % 4);
-      const int row = row0 + r;
-      if (row < Dv && col < Dk) M[(int64_t)row * Dk + col] = S[r][c];
+    for (int c = 0; c < NC; ++c) v[r][c] = scale * S[r][c];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = row0 + r;
+    if (row >= Dv) continue;
+#pragma unroll
+    for (int m = 0; m < NC / 4; ++m) {
+      const int col = 4 * p + 64 * m;
+      float* dst = M + (int64_t)row * Dk + col;
+      if (col + 3 < Dk && (Dk & 3) == 0) {
+        *reinterpret_cast<float4*>(dst) =
+            make_float4(v[r][4 * m], v[r][4 * m + 1], v[r][4 * m + 2],
+                        v[r][4 * m + 3]);
+      } else {
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+          if (col + x < Dk) dst[x] = v[r][4 * m + x];
+      }
     }
+  }
 }
 
 template <int NC>
@@ -166,10 +272,33 @@ __device__ __forceinline__ void lds_cols(float (&out)[NC],
   }
 }
 
-template <typename TIn, int NC, int R>
+// Operands of one time step, read from an LDS block.
+template <int NC, int R>
+struct StepOps {
+  float k[NC], q[NC], x[R], g, beta, qk;
+};
+
+template <int NC, int R, bool WITH_QK>
+__device__ __forceinline__ void load_ops(StepOps<NC, R>& o,
+                                         const float* __restrict__ buf, int s,
+                                         int p, int rg) {
+  using Lo = SweepLayout<NC, R>;
+  lds_cols<NC>(o.k, buf + Lo::K_OFF + s * Lo::DKP, p);
+  lds_cols<NC>(o.q, buf + Lo::Q_OFF + s * Lo::DKP, p);
+#pragma unroll
+  for (int r = 0; r < R; ++r) o.x[r] = buf[Lo::X_OFF + s * Lo::RW + rg * R + r];
+  o.g = buf[Lo::G_OFF + s];
+  o.beta = buf[Lo::B_OFF + s];
+  o.qk = WITH_QK ? buf[Lo::QK_OFF + s] : 0.f;
+}
+
+// FAST: L is a multiple of kStage (checkpoints fall on block starts) and the
+// vectorised staging applies.
+template <typename TIn, int NC, int R, bool FAST>
 __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   using Lo = SweepLayout<NC, R>;
-  __shared__ __align__(16) float lds[2][Lo::SIZE];
+  using St_ = Stager<TIn, NC, R, FAST>;
+  __shared__ __align__(16) float lds[2][Lo::BUF];
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -189,106 +318,146 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   const int64_t bh = (int64_t)b * Hv + h;
   const int64_t mat = (int64_t)Dv * Dk;
 
-  float S[R][NC];
-  tile_load<NC, R>(S, a.S0 ? a.S0 + bh * mat : nullptr, row0, p, Dk, Dv);
+  // S = sig * St
+  float St[R][NC];
+  float sig = 1.f;
+  tile_load<NC, R>(St, a.S0 ? a.S0 + bh * mat : nullptr, row0, p, Dk, Dv);
 
   const int nblk = (T + kStage - 1) / kStage;
-  TIn pre[Lo::PF];
-  uint64_t pre_ok = 0;
+  St_ stg;
   if (nblk > 0) {
-    stage_fetch<TIn, NC, R>(pre, pre_ok, 0, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q,
-                            v, g, beta);
-    stage_store<TIn, NC, R>(lds[0], pre, pre_ok);
+    stg.fetch(0, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, v, g, beta);
+    stg.store(lds[0]);
   }
   __syncthreads();
 
-  float qprev[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) qprev[c] = 0.f;
   const int my_row = row0 + p;  // row written by lanes p < R
   const bool writer = (p < R) && (my_row < Dv);
-
-  int to_ckpt = 0;  // steps until the next checkpoint (t % L == 0)
+  const int64_t out0 = ((int64_t)b * T * Hv + h) * Dv + my_row;  // (b,0,h,row)
+  const int64_t tstep = (int64_t)Hv * Dv;
+  float* __restrict__ E = a.E;
+  float* __restrict__ Sck = a.Sck;
+  int to_ckpt = 0;  // generic path: steps until the next checkpoint
   int ckpt_slot = 0;
-  for (int blk = 0; blk < nblk; ++blk) {
-    const float* __restrict__ cur = lds[blk & 1];
-    if (blk + 1 < nblk)
-      stage_fetch<TIn, NC, R>(pre, pre_ok, blk + 1, T, Hk, Hv, Dk, Dv, b, h, hk,
-                              rowbase, k, q, v, g, beta);
-    const int tbase = blk * kStage;
-    const int nsteps = min(kStage, T - tbase);
-    for (int s = 0; s < nsteps; ++s) {
-      const int t = tbase + s;
-      float kk[NC], qq[NC];
-      lds_cols<NC>(kk, cur + Lo::K_OFF + s * Lo::DKP, p);
-      lds_cols<NC>(qq, cur + Lo::Q_OFF + s * Lo::DKP, p);
+
+  // One forward step t with operands `cur`; `oth` holds the operands of the
+  // previous step (its q is q_{t-1}, for the read-out y_{t-1}) and, once the
+  // dots have consumed it, is refilled with the operands of step s + 1.
+  auto step = [&](const StepOps<NC, R>& cur, StepOps<NC, R>& oth,
+                  const float* __restrict__ buf, int t, int s_next) {
+    if (!FAST) {
       if (to_ckpt == 0) {
-        if (a.Sck != nullptr)
-          tile_store<NC, R>(S, a.Sck + (bh * a.nch + ckpt_slot) * mat, row0, p,
-                            Dk, Dv);
+        if (Sck != nullptr)
+          tile_store<NC, R>(St, sig, Sck + (bh * a.nch + ckpt_slot) * mat,
+                            row0, p, Dk, Dv);
         ++ckpt_slot;
         to_ckpt = a.L;
       }
       --to_ckpt;
-      // dots on the state before step t: S k_t (for the update) and
-      // S q_{t-1} (= y_{t-1}, the read-out of the previous step)
-      float pk[R], pq[R];
+    }
+    // dots on the state before step t: St k_t (for the update) and
+    // St q_{t-1} (the read-out y_{t-1} of the previous step)
+    float pk[R], pq[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float ak = 0.f, aq = 0.f;
+    for (int r = 0; r < R; ++r) {
+      float ak0 = 0.f, ak1 = 0.f, aq0 = 0.f, aq1 = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          ak = fmaf(S[r][c], kk[c], ak);
-          aq = fmaf(S[r][c], qprev[c], aq);
-        }
-        pk[r] = rowsum16(ak);
-        pq[r] = rowsum16(aq);
+      for (int c = 0; c < NC; c += 2) {
+        ak0 = fmaf(St[r][c], cur.k[c], ak0);
+        aq0 = fmaf(St[r][c], oth.q[c], aq0);
+        ak1 = fmaf(St[r][c + 1], cur.k[c + 1], ak1);
+        aq1 = fmaf(St[r][c + 1], oth.q[c + 1], aq1);
       }
-      if (t > 0 && writer)
-        st(y, ((int64_t)(b * (int64_t)T + t - 1) * Hv + h) * Dv + my_row,
-           pick<R>(pq, p));
-      const float gt = cur[Lo::G_OFF + s];
-      const float bt = cur[Lo::B_OFF + s];
-      float d[R], e[R];
+      pk[r] = ak0 + ak1;
+      pq[r] = aq0 + aq1;
+    }
+    load_ops<NC, R, false>(oth, buf, s_next, p, rg);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        e[r] = cur[Lo::X_OFF + s * Lo::RW + rg * R + r] - gt * pk[r];
-        d[r] = bt * e[r];
-      }
-      if (a.E != nullptr && writer)
-        a.E[((int64_t)(b * (int64_t)T + t) * Hv + h) * Dv + my_row] =
-            pick<R>(e, p);
+    for (int r = 0; r < R; ++r) {
+      pk[r] = rowsum16(pk[r]);
+      pq[r] = rowsum16(pq[r]);
+    }
+    // u_t = (g_t S) k_t,  e_t = v_t - u_t,  d_t = beta_t e_t
+    const float gs = cur.g * sig;
+    float d[R], e[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      e[r] = cur.x[r] - gs * pk[r];
+      d[r] = cur.beta * e[r];
+    }
+    if (writer) {
+      if (t > 0) st(y, out0 + (t - 1) * tstep, sig * pick<R>(pq, p));
+      if (E != nullptr) E[out0 + t * tstep] = pick<R>(e, p);
+    }
+    // S_t = g_t S + d k^T  ==  sig' (St + (d / sig') k^T) with sig' = g_t sig
+    const bool fold = gs < kRescale;
+    const float sig_new = fold ? 1.f : gs;
+    const float inv = __builtin_amdgcn_rcpf(sig_new);
+    if (fold) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int c = 0; c < NC; ++c) S[r][c] = fmaf(d[r], kk[c], gt * S[r][c]);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) qprev[c] = qq[c];
+        for (int c = 0; c < NC; ++c) St[r][c] *= gs;
     }
-    if (blk + 1 < nblk) stage_store<TIn, NC, R>(lds[(blk + 1) & 1], pre, pre_ok);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float coef = d[r] * inv;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) St[r][c] = fmaf(coef, cur.k[c], St[r][c]);
+    }
+    sig = sig_new;
+  };
+
+  // A and B alternate as the operand sets of consecutive steps.  The refill
+  // index is clamped to the block's last step, so after a block both sets, and
+  // in particular B, hold that step's q: q_{t-1} for the next block's first
+  // step and for the final read-out.  B.q is zero before the first step.
+  StepOps<NC, R> A, B;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) B.q[c] = 0.f;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const float* __restrict__ cur = lds[blk & 1];
+    if (blk + 1 < nblk)
+      stg.fetch(blk + 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, v, g,
+                beta);
+    const int tbase = blk * kStage;
+    const int nsteps = min(kStage, T - tbase);
+    if (FAST && Sck != nullptr && (tbase % a.L) == 0)
+      tile_store<NC, R>(St, sig, Sck + (bh * a.nch + tbase / a.L) * mat, row0,
+                        p, Dk, Dv);
+    load_ops<NC, R, false>(A, cur, 0, p, rg);
+    const int slast = nsteps - 1;
+    int s = 0;
+    for (; s + 1 < nsteps; s += 2) {
+      step(A, B, cur, tbase + s, s + 1);
+      step(B, A, cur, tbase + s + 1, min(s + 2, slast));
+    }
+    if (s < nsteps) step(A, B, cur, tbase + s, slast);
+    if (blk + 1 < nblk) stg.store(lds[(blk + 1) & 1]);
     __syncthreads();
   }
 
   if (T > 0) {
+    const float* qlast = B.q;
     float pq[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float aq = 0.f;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) aq = fmaf(S[r][c], qprev[c], aq);
+      for (int c = 0; c < NC; ++c) aq = fmaf(St[r][c], qlast[c], aq);
       pq[r] = rowsum16(aq);
     }
-    if (writer)
-      st(y, ((int64_t)(b * (int64_t)T + T - 1) * Hv + h) * Dv + my_row,
-         pick<R>(pq, p));
+    if (writer) st(y, out0 + (int64_t)(T - 1) * tstep, sig * pick<R>(pq, p));
   }
-  if (a.ST != nullptr) tile_store<NC, R>(S, a.ST + bh * mat, row0, p, Dk, Dv);
+  if (a.ST != nullptr)
+    tile_store<NC, R>(St, sig, a.ST + bh * mat, row0, p, Dk, Dv);
 }
 
-template <typename TIn, int NC, int R>
+template <typename TIn, int NC, int R, bool FAST>
 __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
   using Lo = SweepLayout<NC, R>;
-  __shared__ __align__(16) float lds[2][Lo::SIZE];
+  using St_ = Stager<TIn, NC, R, FAST>;
+  __shared__ __align__(16) float lds[2][Lo::BUF];
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -308,124 +477,189 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
   const int64_t bh = (int64_t)b * Hv + h;
   const int64_t mat = (int64_t)Dv * Dk;
 
-  float H[R][NC];
-  tile_load<NC, R>(H, a.dST ? a.dST + bh * mat : nullptr, row0, p, Dk, Dv);
+  // H (dL/dS after the step being processed) = tau * Ht
+  float Ht[R][NC];
+  float tau = 1.f;
+  tile_load<NC, R>(Ht, a.dST ? a.dST + bh * mat : nullptr, row0, p, Dk, Dv);
   // slot nch-1 holds dL/dS_T for the last chunk
   if (a.nch > 0)
-    tile_store<NC, R>(H, a.Hck + (bh * a.nch + a.nch - 1) * mat, row0, p, Dk,
-                      Dv);
+    tile_store<NC, R>(Ht, 1.f, a.Hck + (bh * a.nch + a.nch - 1) * mat, row0,
+                      p, Dk, Dv);
 
   const int nblk = (T + kStage - 1) / kStage;
-  TIn pre[Lo::PF];
-  uint64_t pre_ok = 0;
+  St_ stg;
   if (nblk > 0) {
-    stage_fetch<TIn, NC, R>(pre, pre_ok, nblk - 1, T, Hk, Hv, Dk, Dv, b, h, hk,
-                            rowbase, k, q, dy, g, beta);
-    stage_store<TIn, NC, R>(lds[(nblk - 1) & 1], pre, pre_ok);
+    stg.fetch(nblk - 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, dy, g,
+              beta);
+    stg.store(lds[(nblk - 1) & 1]);
   }
   __syncthreads();
 
   const int my_row = row0 + p;
   const bool writer = (p < R) && (my_row < Dv);
+  const int64_t out0 = ((int64_t)b * T * Hv + h) * Dv + my_row;
+  const int64_t tstep = (int64_t)Hv * Dv;
+  float* __restrict__ C = a.C;
+  float* __restrict__ Hck = a.Hck;
 
-  // H after step t is saved when t % L == 0 and t > 0, in slot t / L - 1
+  // generic path: H after step t is saved when t % L == 0 and t > 0, in slot
+  // t / L - 1
   int last_chunk = (T - 1) / (a.L > 0 ? a.L : 1);
   int to_ckpt = T - 1 - last_chunk * a.L;  // steps until t % L == 0
-  for (int blk = nblk - 1; blk >= 0; --blk) {
-    const float* __restrict__ cur = lds[blk & 1];
-    if (blk > 0)
-      stage_fetch<TIn, NC, R>(pre, pre_ok, blk - 1, T, Hk, Hv, Dk, Dv, b, h, hk,
-                              rowbase, k, q, dy, g, beta);
-    const int tbase = blk * kStage;
-    const int nsteps = min(kStage, T - tbase);
-    for (int s = nsteps - 1; s >= 0; --s) {
-      const int t = tbase + s;
-      float kk[NC], qq[NC];
-      lds_cols<NC>(kk, cur + Lo::K_OFF + s * Lo::DKP, p);
-      lds_cols<NC>(qq, cur + Lo::Q_OFF + s * Lo::DKP, p);
-      const float gt = cur[Lo::G_OFF + s];
-      const float bt = cur[Lo::B_OFF + s];
-      float c[R];
+
+  auto step = [&](const StepOps<NC, R>& op, StepOps<NC, R>& oth,
+                  const float* __restrict__ buf, int t, int s_next) {
+    load_ops<NC, R, true>(oth, buf, s_next, p, rg);
+    // c_t = G k_t = tau (Ht k_t) + dy_t (q_t . k_t)
+    float c[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float dyr = cur[Lo::X_OFF + s * Lo::RW + rg * R + r];
-        float acc = 0.f;
+    for (int r = 0; r < R; ++r) {
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-        for (int j = 0; j < NC; ++j) {
-          H[r][j] = fmaf(dyr, qq[j], H[r][j]);  // G = H + dy q^T
-          acc = fmaf(H[r][j], kk[j], acc);
-        }
-        c[r] = rowsum16(acc);
+      for (int j = 0; j < NC; j += 2) {
+        a0 = fmaf(Ht[r][j], op.k[j], a0);
+        a1 = fmaf(Ht[r][j + 1], op.k[j + 1], a1);
       }
-      float dvr[R];
+      c[r] = fmaf(tau, rowsum16(a0 + a1), op.x[r] * op.qk);
+    }
+    float dvr[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) dvr[r] = bt * c[r];
-      if (writer) {
-        const int64_t o = ((int64_t)(b * (int64_t)T + t) * Hv + h) * Dv + my_row;
-        a.C[o] = pick<R>(c, p);
-        st(dv, o, pick<R>(dvr, p));
-      }
+    for (int r = 0; r < R; ++r) dvr[r] = op.beta * c[r];
+    if (writer) {
+      const int64_t o = out0 + t * tstep;
+      C[o] = pick<R>(c, p);
+      st(dv, o, pick<R>(dvr, p));
+    }
+    // H_t = g_t (tau Ht + dy q^T - dv k^T) = tau' (Ht + (dy q^T - dv k^T)/tau)
+    const float inv = __builtin_amdgcn_rcpf(tau);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float cy = op.x[r] * inv, cv = -dvr[r] * inv;
+#pragma unroll
+      for (int j = 0; j < NC; ++j)
+        Ht[r][j] = fmaf(cv, op.k[j], fmaf(cy, op.q[j], Ht[r][j]));
+    }
+    const float gt = op.g * tau;
+    const bool fold = gt < kRescale;
+    if (fold) {
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int j = 0; j < NC; ++j)
-          H[r][j] = gt * fmaf(-dvr[r], kk[j], H[r][j]);
+        for (int j = 0; j < NC; ++j) Ht[r][j] *= gt;
+    }
+    tau = fold ? 1.f : gt;
+    if (!FAST) {
       if (to_ckpt == 0) {
         if (t > 0)
-          tile_store<NC, R>(H, a.Hck + (bh * a.nch + last_chunk - 1) * mat,
+          tile_store<NC, R>(Ht, tau, Hck + (bh * a.nch + last_chunk - 1) * mat,
                             row0, p, Dk, Dv);
         --last_chunk;
         to_ckpt = a.L;
       }
       --to_ckpt;
     }
-    if (blk > 0) stage_store<TIn, NC, R>(lds[(blk - 1) & 1], pre, pre_ok);
+  };
+
+  for (int blk = nblk - 1; blk >= 0; --blk) {
+    float* __restrict__ cur = lds[blk & 1];
+    // q_t . k_t of this block: row group rg handles step rg
+    {
+      float kq[NC], qv[NC];
+      lds_cols<NC>(kq, cur + Lo::K_OFF + rg * Lo::DKP, p);
+      lds_cols<NC>(qv, cur + Lo::Q_OFF + rg * Lo::DKP, p);
+      float z = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) z = fmaf(kq[c], qv[c], z);
+      z = rowsum16(z);
+      if (p == 0) cur[Lo::QK_OFF + rg] = z;
+    }
+    __syncthreads();
+    if (blk > 0)
+      stg.fetch(blk - 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, dy, g,
+                beta);
+    const int tbase = blk * kStage;
+    const int nsteps = min(kStage, T - tbase);
+    StepOps<NC, R> A, B;
+    load_ops<NC, R, true>(A, cur, nsteps - 1, p, rg);
+    int s = nsteps - 1;
+    for (; s >= 1; s -= 2) {
+      step(A, B, cur, tbase + s, s - 1);
+      step(B, A, cur, tbase + s - 1, max(s - 2, 0));
+    }
+    if (s == 0) step(A, B, cur, tbase, 0);
+    if (FAST && tbase > 0 && (tbase % a.L) == 0)
+      tile_store<NC, R>(Ht, tau, Hck + (bh * a.nch + tbase / a.L - 1) * mat,
+                        row0, p, Dk, Dv);
+    if (blk > 0) stg.store(lds[(blk - 1) & 1]);
     __syncthreads();
   }
-  if (a.dS0 != nullptr) tile_store<NC, R>(H, a.dS0 + bh * mat, row0, p, Dk, Dv);
+  if (a.dS0 != nullptr)
+    tile_store<NC, R>(Ht, tau, a.dS0 + bh * mat, row0, p, Dk, Dv);
 }
 
-template <typename TIn, int NC, int R>
+template <typename TIn, int NC, int R, bool FAST>
 hipError_t fwd_launch(const FwdSweepArgs& a, hipStream_t s) {
   using Lo = SweepLayout<NC, R>;
   dim3 grid((a.Dv + Lo::RW - 1) / Lo::RW, a.Hv, a.B);
-  hipLaunchKernelGGL((fwd_sweep_kernel<TIn, NC, R>), grid, dim3(kThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((fwd_sweep_kernel<TIn, NC, R, FAST>), grid,
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-template <typename TIn, int NC, int R>
+template <typename TIn, int NC, int R, bool FAST>
 hipError_t bwd_launch(const BwdSweepArgs& a, hipStream_t s) {
   using Lo = SweepLayout<NC, R>;
   dim3 grid((a.Dv + Lo::RW - 1) / Lo::RW, a.Hv, a.B);
-  hipLaunchKernelGGL((bwd_sweep_kernel<TIn, NC, R>), grid, dim3(kThreads), 0,
-                     s, a);
+  hipLaunchKernelGGL((bwd_sweep_kernel<TIn, NC, R, FAST>), grid,
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // Columns per lane: the smallest multiple of 4 with 16 * NC >= Dk.
 int pick_nc(int Dk) { return 4 * ((Dk + 63) / 64); }
 
+constexpr int kR = GDR_SWEEP_R;
+
+// The vectorised, block-aligned-checkpoint kernels need 16-byte rows of k, q
+// and v / dy, and L a multiple of the staging block.
 template <typename TIn>
-hipError_t fwd_dispatch(const FwdSweepArgs& a, hipStream_t s) {
+bool fast_ok(int Dk, int Dv, int L) {
+  const int vw = 16 / (int)sizeof(TIn);
+  return Dk % vw == 0 && Dv % vw == 0 && (16 * kR) % vw == 0 && L % kStage == 0;
+}
+
+template <typename TIn, bool FAST>
+hipError_t fwd_dispatch2(const FwdSweepArgs& a, hipStream_t s) {
   switch (pick_nc(a.Dk)) {
-    case 4: return fwd_launch<TIn, 4, 2>(a, s);
-    case 8: return fwd_launch<TIn, 8, 2>(a, s);
-    case 12: return fwd_launch<TIn, 12, 2>(a, s);
-    case 16: return fwd_launch<TIn, 16, 2>(a, s);
+    case 4: return fwd_launch<TIn, 4, kR, FAST>(a, s);
+    case 8: return fwd_launch<TIn, 8, kR, FAST>(a, s);
+    case 12: return fwd_launch<TIn, 12, kR, FAST>(a, s);
+    case 16: return fwd_launch<TIn, 16, kR, FAST>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename TIn, bool FAST>
+hipError_t bwd_dispatch2(const BwdSweepArgs& a, hipStream_t s) {
+  switch (pick_nc(a.Dk)) {
+    case 4: return bwd_launch<TIn, 4, kR, FAST>(a, s);
+    case 8: return bwd_launch<TIn, 8, kR, FAST>(a, s);
+    case 12: return bwd_launch<TIn, 12, kR, FAST>(a, s);
+    case 16: return bwd_launch<TIn, 16, kR, FAST>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename TIn>
+hipError_t fwd_dispatch(const FwdSweepArgs& a, hipStream_t s) {
+  return fast_ok<TIn>(a.Dk, a.Dv, a.L) ? fwd_dispatch2<TIn, true>(a, s)
+                                       : fwd_dispatch2<TIn, false>(a, s);
+}
+
+template <typename TIn>
 hipError_t bwd_dispatch(const BwdSweepArgs& a, hipStream_t s) {
-  switch (pick_nc(a.Dk)) {
-    case 4: return bwd_launch<TIn, 4, 2>(a, s);
-    case 8: return bwd_launch<TIn, 8, 2>(a, s);
-    case 12: return bwd_launch<TIn, 12, 2>(a, s);
-    case 16: return bwd_launch<TIn, 16, 2>(a, s);
-  }
-  return hipErrorInvalidValue;
+  return fast_ok<TIn>(a.Dk, a.Dv, a.L) ? bwd_dispatch2<TIn, true>(a, s)
+                                       : bwd_dispatch2<TIn, false>(a, s);
 }
 
 }  // namespace
