@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/gdr.h"
 #include "gdr_internal.h"
 
@@ -243,3 +245,34 @@ const char* gdr_strerror(int status) {
 const char* gdr_version(void) { return "0.1.0"; }
 
 }  // extern "C"
+
+namespace gdr {
+
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s) {
+  const int cu = device_cu_count();
+  return bf16 ? launch_fwd_sweep_bf16(a, cu, s) : launch_fwd_sweep_f32(a, cu, s);
+}
+
+hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s) {
+  const int cu = device_cu_count();
+  return bf16 ? launch_bwd_sweep_bf16(a, cu, s) : launch_bwd_sweep_f32(a, cu, s);
+}
+
+}  // namespace gdr

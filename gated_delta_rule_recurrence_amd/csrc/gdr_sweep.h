@@ -34,15 +34,15 @@
 // running product of g.  Contribution s reaches step t through the same t - s
 // roundings as in the direct form.  The reverse sweep keeps H = tau * Ht the
 // same way.
+#pragma once
+
+#include <type_traits>
+
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
-#ifndef GDR_SWEEP_R
-#define GDR_SWEEP_R 2
-#endif
-
 namespace gdr {
-namespace {
+namespace sweep {
 
 constexpr int kThreads = 256;
 constexpr int kStage = 16;            // time steps per LDS block
@@ -616,60 +616,69 @@ hipError_t bwd_launch(const BwdSweepArgs& a, hipStream_t s) {
 }
 
 // Columns per lane: the smallest multiple of 4 with 16 * NC >= Dk.
-int pick_nc(int Dk) { return 4 * ((Dk + 63) / 64); }
-
-constexpr int kR = GDR_SWEEP_R;
+inline int pick_nc(int Dk) { return 4 * ((Dk + 63) / 64); }
 
 // The vectorised, block-aligned-checkpoint kernels need 16-byte rows of k, q
 // and v / dy, and L a multiple of the staging block.
 template <typename TIn>
 bool fast_ok(int Dk, int Dv, int L) {
   const int vw = 16 / (int)sizeof(TIn);
-  return Dk % vw == 0 && Dv % vw == 0 && (16 * kR) % vw == 0 && L % kStage == 0;
+  return Dk % vw == 0 && Dv % vw == 0 && L % kStage == 0;
 }
 
-template <typename TIn, bool FAST>
-hipError_t fwd_dispatch2(const FwdSweepArgs& a, hipStream_t s) {
+// Rows per lane R: one workgroup owns 16 R rows of a head, one wave per
+// SIMD per workgroup.  Pick the largest R that still gives two workgroups
+// per CU (so two waves share each SIMD and hide each other's dependency
+// stalls, with every workgroup resident in one round); fall back to R = 1.
+inline int pick_r(int B, int Hv, int Dv, int num_cu) {
+  for (int R = 4; R >= 2; R /= 2) {
+    const long wgs = (long)B * Hv * ((Dv + 16 * R - 1) / (16 * R));
+    if (wgs >= 2L * num_cu) return R;
+  }
+  return 1;
+}
+
+template <typename TIn, bool FAST, int R>
+hipError_t fwd_dispatch_nc(const FwdSweepArgs& a, hipStream_t s) {
   switch (pick_nc(a.Dk)) {
-    case 4: return fwd_launch<TIn, 4, kR, FAST>(a, s);
-    case 8: return fwd_launch<TIn, 8, kR, FAST>(a, s);
-    case 12: return fwd_launch<TIn, 12, kR, FAST>(a, s);
-    case 16: return fwd_launch<TIn, 16, kR, FAST>(a, s);
+    case 4: return fwd_launch<TIn, 4, R, FAST>(a, s);
+    case 8: return fwd_launch<TIn, 8, R, FAST>(a, s);
+    case 12: return fwd_launch<TIn, 12, R, FAST>(a, s);
+    case 16: return fwd_launch<TIn, 16, R, FAST>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
-template <typename TIn, bool FAST>
-hipError_t bwd_dispatch2(const BwdSweepArgs& a, hipStream_t s) {
+template <typename TIn, bool FAST, int R>
+hipError_t bwd_dispatch_nc(const BwdSweepArgs& a, hipStream_t s) {
   switch (pick_nc(a.Dk)) {
-    case 4: return bwd_launch<TIn, 4, kR, FAST>(a, s);
-    case 8: return bwd_launch<TIn, 8, kR, FAST>(a, s);
-    case 12: return bwd_launch<TIn, 12, kR, FAST>(a, s);
-    case 16: return bwd_launch<TIn, 16, kR, FAST>(a, s);
+    case 4: return bwd_launch<TIn, 4, R, FAST>(a, s);
+    case 8: return bwd_launch<TIn, 8, R, FAST>(a, s);
+    case 12: return bwd_launch<TIn, 12, R, FAST>(a, s);
+    case 16: return bwd_launch<TIn, 16, R, FAST>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename TIn>
-hipError_t fwd_dispatch(const FwdSweepArgs& a, hipStream_t s) {
-  return fast_ok<TIn>(a.Dk, a.Dv, a.L) ? fwd_dispatch2<TIn, true>(a, s)
-                                       : fwd_dispatch2<TIn, false>(a, s);
+hipError_t fwd_dispatch(const FwdSweepArgs& a, int num_cu, hipStream_t s) {
+  if (!fast_ok<TIn>(a.Dk, a.Dv, a.L)) return fwd_dispatch_nc<TIn, false, 1>(a, s);
+  switch (pick_r(a.B, a.Hv, a.Dv, num_cu)) {
+    case 4: return fwd_dispatch_nc<TIn, true, 4>(a, s);
+    case 2: return fwd_dispatch_nc<TIn, true, 2>(a, s);
+    default: return fwd_dispatch_nc<TIn, true, 1>(a, s);
+  }
 }
 
 template <typename TIn>
-hipError_t bwd_dispatch(const BwdSweepArgs& a, hipStream_t s) {
-  return fast_ok<TIn>(a.Dk, a.Dv, a.L) ? bwd_dispatch2<TIn, true>(a, s)
-                                       : bwd_dispatch2<TIn, false>(a, s);
+hipError_t bwd_dispatch(const BwdSweepArgs& a, int num_cu, hipStream_t s) {
+  if (!fast_ok<TIn>(a.Dk, a.Dv, a.L)) return bwd_dispatch_nc<TIn, false, 1>(a, s);
+  switch (pick_r(a.B, a.Hv, a.Dv, num_cu)) {
+    case 4: return bwd_dispatch_nc<TIn, true, 4>(a, s);
+    case 2: return bwd_dispatch_nc<TIn, true, 2>(a, s);
+    default: return bwd_dispatch_nc<TIn, true, 1>(a, s);
+  }
 }
 
-}  // namespace
-
-hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s) {
-  return bf16 ? fwd_dispatch<gdr::bf16>(a, s) : fwd_dispatch<float>(a, s);
-}
-
-hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s) {
-  return bf16 ? bwd_dispatch<gdr::bf16>(a, s) : bwd_dispatch<float>(a, s);
-}
-
+}  // namespace sweep
 }  // namespace gdr

@@ -93,6 +93,15 @@ def test_qwen_bf16_T2048_sampled(cuda):
                 f"qwen T=2048 kv{hk}")
 
 
+def test_qwen_bf16_B2_sampled(cuda):
+    """B=2 selects two rows per lane in the sweeps (B=1 one, B=4 four)."""
+    p = inputs.qwen35_9b(96, B=2)
+    gpu = run_gpu(p, cuda, 32)
+    for b, hk in ((0, 3), (1, 12)):
+        compare(slice_group(gpu, p, b, hk), run_oracle(p, b, hk), TOL["bf16"],
+                f"qwen B=2 b{b} kv{hk}")
+
+
 # ---------------------------------------------------------------- config 5
 def test_long_context_sampled(cuda):
     p = inputs.long_context()
