@@ -19,50 +19,78 @@
 //   P1 = S0^T DY, P2' = S0^T C, P3' = H1^T E          [Dk x n]
 //   Phi'[t][r] = dy_t . e_r,  Psi'[t][r] = c_t . e_r  [n x n]
 //   QK[s][r] = q_s . k_r,     KK[s][r] = k_s . k_r    [n x n]
-// followed by O(n^2) work per head and [Dk x n] x [n x n] products.
+// followed by O(n^2) work per head and the products dq += K Wq,
+// dk += Q W1 - K W2 with [n x n] weight matrices summed over the heads.
 //
-// Mapping: one workgroup of 512 threads per (batch row, kv head, chunk); it
-// loops over the Hv/Hk value heads of the kv head in ascending order and
-// accumulates dq, dk in registers, so the GQA sum has a fixed order and needs
-// no atomics.  Thread (jt, tt) owns the output columns j = jt + 32m (m < J)
-// and local steps t = tt + 16u (u < 4).
+// Mapping: one workgroup of 512 threads (8 waves) per (batch row, kv head,
+// chunk).  It loops over the Hv/Hk value heads of the kv head in ascending
+// order and accumulates dq, dk in registers, so the GQA sum has a fixed order
+// and needs no atomics.  The contractions over Dv and the final products run
+// on fp32 MFMA (v_mfma_f32_16x16x4_f32): the [Dk x n] plane is cut into
+// 16 x 16 tiles (jt, tt) handed to the waves in jt-major order, each tile
+// holding P1, P2', P3', dq and dk in the MFMA accumulator layout (lane l,
+// register v: row 16 jt + 4 (l / 16) + v, column 16 tt + l % 16).  MFMA
+// operands are staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a
+// fragment (lane l <-> m = l % 16, k = l / 16) is 64 consecutive floats.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
 namespace gdr {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kN = 64;   // max chunk length
-constexpr int kIB = 16;  // Dv rows staged per block
-constexpr int kNP = kN + 1;  // padded row stride of the [kN][kN] LDS matrices
+typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int J>
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kN = 64;       // max chunk length
+constexpr int kNP = kN + 1;  // padded row stride of [kN][kN] LDS matrices
+constexpr int kKB = 8;       // Dv rows per staged block (2 MFMA k-steps)
+
+__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int JT>
 struct CL {  // LDS layout, offsets in floats
-  static constexpr int DKP = 32 * J;
-  static constexpr int STAGE_A = 2 * kIB * DKP + 3 * kIB * kNP; // S, H, dy/e/c
-  static constexpr int STAGE_QK = 2 * kN * kNP;                 // q, k j-blocks
-  static constexpr int STAGE_F = 2 * kIB * DKP;                 // final k, q
-  static constexpr int GRAM = 2 * kN * kNP;                     // Phi', Psi'
-  static constexpr int A_SZ0 = STAGE_A > STAGE_QK ? STAGE_A : STAGE_QK;
-  static constexpr int A_SZ = A_SZ0 > GRAM ? A_SZ0 : GRAM;
-  static constexpr int A = 0;
-  static constexpr int QK = A + A_SZ;        // [kN][kNP]
-  static constexpr int KK = QK + kN * kNP;   // [kN][kNP]
-  static constexpr int GM = KK + kN * kNP;   // Gam(r,t] for r <= t
-  static constexpr int MZ = GM + kN * kNP;   // M, then the dg terms
-  static constexpr int RED = MZ + kN * kNP;  // [2][32][kNP]
-  static constexpr int VEC = RED + 2 * 32 * kNP;
+  static constexpr int DKP = 16 * JT;
+  static constexpr int G = 4 * JT;  // j-groups of 4 rows (chi/psi partials)
+  // Phase A stage: S0, H1 [kKB/4][DKP][4]; DY, C, E [kKB/4][kN][4]
+  static constexpr int ST_S = 0, ST_H = kKB * DKP, ST_Y = 2 * kKB * DKP,
+                       ST_C = ST_Y + kKB * kN, ST_E = ST_C + kKB * kN;
+  static constexpr int STAGE = ST_E + kKB * kN;
+  // per-head O(n^2) arrays.  Phi'/Psi' alias the stage (written after the
+  // last Gram block); the chi/psi partials alias Gam/M (consumed before
+  // those are formed).
+  static constexpr int PHI = 0, PSI = PHI + kN * kNP, GM = PSI + kN * kNP,
+                       MZ = GM + kN * kNP, VEC = MZ + kN * kNP;
+  static constexpr int RED = GM;
+  static_assert(2 * G * kNP <= 2 * kN * kNP, "chi/psi partials fit Gam/M");
+  static_assert(STAGE <= GM, "stage stays clear of the chi/psi partials");
   static constexpr int V_G = VEC, V_B = VEC + kN, V_PRE = VEC + 2 * kN,
                        V_PREX = VEC + 3 * kN, V_SUF = VEC + 4 * kN,
                        V_CHI = VEC + 5 * kN, V_PSI = VEC + 6 * kN,
-                       V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;
-  static constexpr int SIZE = V_SCR + 64;
+                       V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;  // 512 floats
+  static constexpr int HEAD = V_SCR + kThreads;
+  // final products: K, Q blocks [kKB/4][DKP][4]
+  static constexpr int FK = 0, FQ = FK + kKB * DKP;
+  static constexpr int FINAL = FQ + kKB * DKP;
+  // QK/KK staging: q, k [kN][kNP] j-blocks of 64
+  static constexpr int QKST = 2 * kN * kNP;
+  static constexpr int A_SZ0 = STAGE > HEAD ? STAGE : HEAD;
+  static constexpr int A_SZ1 = A_SZ0 > FINAL ? A_SZ0 : FINAL;
+  static constexpr int A_SZ = A_SZ1 > QKST ? A_SZ1 : QKST;
+  // persistent per workgroup: QK, KK and the head sums W1, -W2, Wq [kN][kNP]
+  static constexpr int QK = A_SZ, KK = QK + kN * kNP, W1 = KK + kN * kNP,
+                       W2 = W1 + kN * kNP, WQ = W2 + kN * kNP;
+  static constexpr int SIZE = WQ + kN * kNP;
 };
 
-template <typename TIn, int J>
+template <typename TIn, int JT>
 __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
-  using L = CL<J>;
+  using L = CL<JT>;
+  constexpr int DKP = L::DKP;
+  constexpr int NPAIR = 4 * JT;                      // (jt, tt) tiles
+  constexpr int NPW = (NPAIR + kWaves - 1) / kWaves;  // tiles per wave
   extern __shared__ __align__(16) float sm[];
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
@@ -77,21 +105,34 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
   const int t0 = jc * a.L;
   const int n = min(a.L, T - t0);
   const int tid = threadIdx.x;
-  const int jt = tid & 31, tt = tid >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int l = tid & 63;
+  const int lr = l & 15, lq = l >> 4;
   const int64_t mat = (int64_t)Dv * Dk;
 
   auto qk_index = [&](int t, int j) -> int64_t {
     return ((int64_t)(b * (int64_t)T + t0 + t) * Hk + hk) * Dk + j;
   };
 
-  // ---- QK and KK for the kv head (shared by all its value heads) ----------
-  float qk8[8], kk8[8];
+  // tiles of this wave
+  int pj[NPW], pt[NPW];
+  bool pv[NPW];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) qk8[w] = kk8[w] = 0.f;
-  for (int j0 = 0; j0 < Dk; j0 += 64) {
-    float* sq = sm + L::A;
-    float* sk = sm + L::A + kN * kNP;
-    {
+  for (int u = 0; u < NPW; ++u) {
+    const int pi = w * NPW + u;
+    pv[u] = (NPAIR % kWaves == 0) || pi < NPAIR;  // constant when tiles divide evenly
+    pj[u] = pv[u] ? (pi >> 2) : 0;
+    pt[u] = pi & 3;
+  }
+
+  // ---- QK and KK for the kv head (shared by all its value heads) ----------
+  {
+    float qk8[8], kk8[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) qk8[x] = kk8[x] = 0.f;
+    float* sq = sm;
+    float* sk = sm + kN * kNP;
+    for (int j0 = 0; j0 < Dk; j0 += 64) {
       constexpr int U = (kN * 64) / kThreads;
       TIn rq[U], rk[U];
       uint32_t okm = 0;
@@ -113,190 +154,58 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
         sq[s * kNP + jj] = ok ? to_f32(rq[u]) : 0.f;
         sk[s * kNP + jj] = ok ? to_f32(rk[u]) : 0.f;
       }
-    }
-    __syncthreads();
+      __syncthreads();
 #pragma unroll 1
-    for (int w = 0; w < 8; ++w) {
-      const int e = tid + kThreads * w;
-      const int s = e >> 6, r = e & 63;
-      float aq = qk8[w], ak = kk8[w];
+      for (int x = 0; x < 8; ++x) {
+        const int e = tid + kThreads * x;
+        const int s = e >> 6, r = e & 63;
+        float aq = qk8[x], ak = kk8[x];
 #pragma unroll 4
-      for (int jj = 0; jj < 64; ++jj) {
-        const float kr = sk[r * kNP + jj];
-        aq = fmaf(sq[s * kNP + jj], kr, aq);
-        ak = fmaf(sk[s * kNP + jj], kr, ak);
+        for (int jj = 0; jj < 64; ++jj) {
+          const float kr = sk[r * kNP + jj];
+          aq = fmaf(sq[s * kNP + jj], kr, aq);
+          ak = fmaf(sk[s * kNP + jj], kr, ak);
+        }
+        qk8[x] = aq;
+        kk8[x] = ak;
       }
-      qk8[w] = aq;
-      kk8[w] = ak;
+      __syncthreads();
     }
-    __syncthreads();
-  }
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const int e = tid + kThreads * w;
-    const int x = (e >> 6) * kNP + (e & 63);
-    sm[L::QK + x] = qk8[w];
-    sm[L::KK + x] = kk8[w];
+    for (int x = 0; x < 8; ++x) {
+      const int e = tid + kThreads * x;
+      const int o = (e >> 6) * kNP + (e & 63);
+      sm[L::QK + o] = qk8[x];
+      sm[L::KK + o] = kk8[x];
+      sm[L::W1 + o] = 0.f;  // running sums over the value heads
+      sm[L::W2 + o] = 0.f;
+      sm[L::WQ + o] = 0.f;
+    }
   }
 
-  // running sums over the value heads
-  float wq[8], w1[8], w2[8];
+  f4 dQ[NPW], dK[NPW];
 #pragma unroll
-  for (int w = 0; w < 8; ++w) wq[w] = w1[w] = w2[w] = 0.f;
-  float dQ[J][4], dK[J][4];
-#pragma unroll
-  for (int m = 0; m < J; ++m)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dQ[m][u] = dK[m][u] = 0.f;
+  for (int u = 0; u < NPW; ++u) dQ[u] = dK[u] = f4{0.f, 0.f, 0.f, 0.f};
 
   for (int hh = 0; hh < rep; ++hh) {
     const int h = hk * rep + hh;
     const int64_t bh = (int64_t)b * Hv + h;
     const float* __restrict__ S0 = a.Sck + (bh * a.nch + jc) * mat;
     const float* __restrict__ H1 = a.Hck + (bh * a.nch + jc) * mat;
-    auto row_index = [&](int t, int i) -> int64_t {
-      return ((int64_t)(b * (int64_t)T + t0 + t) * Hv + h) * Dv + i;
-    };
-
-    // ---- contractions over Dv --------------------------------------------
-    float P1[J][4], P2[J][4], P3[J][4];
-    float phi[4][2], psi[4][2];
-    float hs = 0.f;
-#pragma unroll
-    for (int m = 0; m < J; ++m)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) P1[m][u] = P2[m][u] = P3[m][u] = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) phi[u][0] = phi[u][1] = psi[u][0] = psi[u][1] = 0.f;
-
-    float* sS = sm + L::A;
-    float* sH = sS + kIB * L::DKP;
-    float* sY = sH + kIB * L::DKP;  // [kIB][kNP] dy
-    float* sE = sY + kIB * kNP;     // [kIB][kNP] e
-    float* sC = sE + kIB * kNP;     // [kIB][kNP] c
-    const TIn* __restrict__ dyh = dy + row_index(0, 0);
-    const float* __restrict__ Eh = a.E + row_index(0, 0);
-    const float* __restrict__ Ch = a.C + row_index(0, 0);
+    const int64_t rowbase = ((int64_t)b * T + t0) * Hv * Dv + (int64_t)h * Dv;
     const int64_t tstride = (int64_t)Hv * Dv;
-    // One Dv block of S0, H1 (kIB x DKP) and of dy, e, c (n x kIB), fetched
-    // into registers with unconditional loads from clamped offsets.
-    constexpr int US = (kIB * L::DKP) / kThreads;  // = J
-    constexpr int UX = (kIB * kN) / kThreads;      // = 2
-    static_assert(US * kThreads == kIB * L::DKP && UX * kThreads == kIB * kN, "tiling");
-    float fs[US], fh[US], fe[UX], fc[UX];
-    TIn fy[UX];
-    uint32_t fok = 0;
-    auto fetch = [&](int i0) {
-      fok = 0;
-#pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ii = idx / L::DKP, j = idx - ii * L::DKP, i = i0 + ii;
-        const bool ok = i < Dv && j < Dk;
-        const int64_t o = ok ? (int64_t)i * Dk + j : 0;
-        fs[u] = S0[o];
-        fh[u] = H1[o];
-        fok |= (uint32_t)ok << u;
-      }
-#pragma unroll
-      for (int u = 0; u < UX; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ii = idx % kIB, t = idx / kIB, i = i0 + ii;  // rows fastest
-        const bool ok = i < Dv && t < n;
-        const int64_t o = ok ? t * tstride + i : 0;
-        fy[u] = dyh[o];
-        fe[u] = Eh[o];
-        fc[u] = Ch[o];
-        fok |= (uint32_t)ok << (16 + u);
-      }
-    };
-    auto deposit = [&]() {
-#pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const int idx = tid + kThreads * u;
-        const bool ok = (fok >> u) & 1;
-        sS[idx] = ok ? fs[u] : 0.f;
-        sH[idx] = ok ? fh[u] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < UX; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ii = idx % kIB, t = idx / kIB;
-        const bool ok = (fok >> (16 + u)) & 1;
-        sY[ii * kNP + t] = ok ? to_f32(fy[u]) : 0.f;
-        sE[ii * kNP + t] = ok ? fe[u] : 0.f;
-        sC[ii * kNP + t] = ok ? fc[u] : 0.f;
-      }
-    };
-    fetch(0);
-    deposit();
-    __syncthreads();
-    for (int i0 = 0; i0 < Dv; i0 += kIB) {
-      if (i0 + kIB < Dv) fetch(i0 + kIB);
-#pragma unroll 1
-      for (int ii = 0; ii < kIB; ++ii) {
-        float sj[J], hj[J], yu[4], cu[4], eu[4], ew[2];
-#pragma unroll
-        for (int m = 0; m < J; ++m) {
-          sj[m] = sS[ii * L::DKP + jt + 32 * m];
-          hj[m] = sH[ii * L::DKP + jt + 32 * m];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          yu[u] = sY[ii * kNP + tt + 16 * u];
-          cu[u] = sC[ii * kNP + tt + 16 * u];
-          eu[u] = sE[ii * kNP + tt + 16 * u];
-        }
-        ew[0] = sE[ii * kNP + 2 * jt];
-        ew[1] = sE[ii * kNP + 2 * jt + 1];
-#pragma unroll
-        for (int m = 0; m < J; ++m)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            P1[m][u] = fmaf(sj[m], yu[u], P1[m][u]);
-            P2[m][u] = fmaf(sj[m], cu[u], P2[m][u]);
-            P3[m][u] = fmaf(hj[m], eu[u], P3[m][u]);
-          }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int w = 0; w < 2; ++w) {
-            phi[u][w] = fmaf(yu[u], ew[w], phi[u][w]);
-            psi[u][w] = fmaf(cu[u], ew[w], psi[u][w]);
-          }
-        if (tt == 0) {
-#pragma unroll
-          for (int m = 0; m < J; ++m) hs = fmaf(sj[m], hj[m], hs);
-        }
-      }
-      __syncthreads();
-      if (i0 + kIB < Dv) {
-        deposit();
-        __syncthreads();
-      }
-    }
+    const TIn* __restrict__ dyh = dy + rowbase;
+    const float* __restrict__ Eh = a.E + rowbase;
+    const float* __restrict__ Ch = a.C + rowbase;
 
-    // ---- per-head O(n^2) stage -------------------------------------------
-    float* sPhi = sm + L::A;        // Phi'[t][r]
-    float* sPsi = sm + L::A + kN * kNP;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int w = 0; w < 2; ++w) {
-        sPhi[(tt + 16 * u) * kNP + 2 * jt + w] = phi[u][w];
-        sPsi[(tt + 16 * u) * kNP + 2 * jt + w] = psi[u][w];
-      }
-    if (tt == 0) sm[L::RED + jt] = hs;  // <H1, S0> partials (32 of them)
+    // per-head vectors: g, beta and the running decay products
     if (tid < kN) {
       const bool ok = tid < n;
       sm[L::V_G + tid] = ok ? ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
       sm[L::V_B + tid] = ok ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
     }
     __syncthreads();
-    if (tid == 0) {
-      float phi0 = 0.f;
-      for (int w = 0; w < 32; ++w) phi0 += sm[L::RED + w];
-      sm[L::V_SCR] = phi0;
+    if (tid == kThreads - 1) {
       float acc = 1.f;
       for (int t = 0; t < n; ++t) {
         sm[L::V_PREX + t] = acc;
@@ -309,8 +218,199 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
         acc *= sm[L::V_G + t];
       }
     }
-    if (tid < kN) {  // row r = tid of Gam(r, t]
-      const int r = tid;
+
+    // Dv blocks (kKB rows) of S0, H1 and of dy, e, c are fetched into
+    // registers with unconditional loads from clamped offsets and deposited
+    // k-interleaved in the stage.
+    constexpr int US = (kKB * DKP + kThreads - 1) / kThreads;  // S0, H1 / thread
+    constexpr int UX = (kKB * kN) / kThreads;                  // dy, e, c / thread
+    float fs[US], fh[US], fe[UX], fc[UX];
+    TIn fy[UX];
+    uint32_t fok = 0;
+    float hs = 0.f;  // partial <H1, S0>
+    auto fetch_x = [&](int i0) {
+#pragma unroll
+      for (int u = 0; u < UX; ++u) {
+        const int idx = tid + kThreads * u;
+        const int ii = idx % kKB, t = idx / kKB, i = i0 + ii;  // rows fastest
+        const bool ok = i < Dv && t < n;
+        const int64_t o = ok ? t * tstride + i : 0;
+        fy[u] = dyh[o];
+        fe[u] = Eh[o];
+        fc[u] = Ch[o];
+        fok = (fok & ~(1u << (16 + u))) | ((uint32_t)ok << (16 + u));
+      }
+    };
+    auto fetch_s = [&](int i0) {
+#pragma unroll
+      for (int u = 0; u < US; ++u) {
+        const int idx = tid + kThreads * u;
+        const int ii = idx / DKP, j = idx - ii * DKP, i = i0 + ii;
+        const bool ok = idx < kKB * DKP && i < Dv && j < Dk;
+        const int64_t o = ok ? (int64_t)i * Dk + j : 0;
+        fs[u] = S0[o];
+        fh[u] = H1[o];
+        fok = (fok & ~(1u << u)) | ((uint32_t)ok << u);
+      }
+    };
+    auto deposit_x = [&]() {
+#pragma unroll
+      for (int u = 0; u < UX; ++u) {
+        const int idx = tid + kThreads * u;
+        const int ii = idx % kKB, t = idx / kKB;
+        const bool ok = (fok >> (16 + u)) & 1;
+        const int o = ((ii >> 2) * kN + t) * 4 + (ii & 3);
+        sm[L::ST_Y + o] = ok ? to_f32(fy[u]) : 0.f;
+        sm[L::ST_E + o] = ok ? fe[u] : 0.f;
+        sm[L::ST_C + o] = ok ? fc[u] : 0.f;
+      }
+    };
+    auto deposit_s = [&]() {  // also accumulates <H1, S0>
+#pragma unroll
+      for (int u = 0; u < US; ++u) {
+        const int idx = tid + kThreads * u;
+        if (idx < kKB * DKP) {
+          const int ii = idx / DKP, j = idx - ii * DKP;
+          const bool ok = (fok >> u) & 1;
+          const float sv = ok ? fs[u] : 0.f, hv = ok ? fh[u] : 0.f;
+          const int o = ((ii >> 2) * DKP + j) * 4 + (ii & 3);
+          sm[L::ST_S + o] = sv;
+          sm[L::ST_H + o] = hv;
+          hs = fmaf(sv, hv, hs);
+        }
+      }
+    };
+
+    // ---- P1 = S0^T DY, P2' = S0^T C, P3' = H1^T E  (MFMA over Dv) ---------
+    f4 P1[NPW], P2[NPW], P3[NPW];
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) P1[u] = P2[u] = P3[u] = f4{0.f, 0.f, 0.f, 0.f};
+    fetch_s(0);
+    fetch_x(0);
+    deposit_s();
+    deposit_x();
+    __syncthreads();
+    for (int i0 = 0; i0 < Dv; i0 += kKB) {
+      const bool more = i0 + kKB < Dv;
+      if (more) {
+        fetch_s(i0 + kKB);
+        fetch_x(i0 + kKB);
+      }
+#pragma unroll 1
+      for (int ks = 0; ks < kKB / 4; ++ks) {
+#pragma unroll
+        for (int u = 0; u < NPW; ++u) {
+          if (!pv[u]) continue;
+          const int ja = ((ks * DKP + pj[u] * 16 + lr) << 2) + lq;
+          const int tb = ((ks * kN + pt[u] * 16 + lr) << 2) + lq;
+          const float as = sm[L::ST_S + ja], ah = sm[L::ST_H + ja];
+          const float by = sm[L::ST_Y + tb], bc = sm[L::ST_C + tb],
+                      be = sm[L::ST_E + tb];
+          P1[u] = mfma(as, by, P1[u]);
+          P2[u] = mfma(as, bc, P2[u]);
+          P3[u] = mfma(ah, be, P3[u]);
+        }
+      }
+      __syncthreads();
+      if (more) {
+        deposit_s();
+        deposit_x();
+        __syncthreads();
+      }
+    }
+
+    // chi, psi partials and the P terms of dq, dk (accumulator layout)
+#pragma unroll
+    for (int u = 0; u < NPW; ++u) {
+      if (!pv[u]) continue;
+      const int t = pt[u] * 16 + lr;
+      const int gidx = pj[u] * 4 + lq;
+      float cp = 0.f, pp = 0.f;
+      if (t < n) {
+        const float bt = sm[L::V_B + t];
+        const float pre = sm[L::V_PRE + t], suf = sm[L::V_SUF + t];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int j = pj[u] * 16 + 4 * lq + v;
+          float qv = 0.f, kv = 0.f;
+          if (j < Dk) {
+            qv = ld(q, qk_index(t, j));
+            kv = ld(k, qk_index(t, j));
+          }
+          const float p2 = bt * P2[u][v], p3 = bt * P3[u][v];
+          cp = fmaf(P1[u][v], qv, cp);
+          cp = fmaf(-p2, kv, cp);
+          pp = fmaf(p3, kv, pp);
+          dQ[u][v] = fmaf(pre, P1[u][v], dQ[u][v]);
+          dK[u][v] = fmaf(suf, p3, dK[u][v]);
+          dK[u][v] = fmaf(-pre, p2, dK[u][v]);
+        }
+      }
+      sm[L::RED + gidx * kNP + t] = cp;
+      sm[L::RED + L::G * kNP + gidx * kNP + t] = pp;
+    }
+    __syncthreads();
+    if (tid < n) {
+      float cs = 0.f, ps = 0.f;
+      for (int x = 0; x < L::G; ++x) {
+        cs += sm[L::RED + x * kNP + tid];
+        ps += sm[L::RED + L::G * kNP + x * kNP + tid];
+      }
+      sm[L::V_CHI + tid] = cs;
+      sm[L::V_PSI + tid] = ps;
+    }
+
+    // ---- Phi' = DY E^T, Psi' = C E^T  (MFMA over Dv) ----------------------
+    f4 GR[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) GR[u] = f4{0.f, 0.f, 0.f, 0.f};
+    fetch_x(0);
+    deposit_x();
+    __syncthreads();
+    for (int i0 = 0; i0 < Dv; i0 += kKB) {
+      const bool more = i0 + kKB < Dv;
+      if (more) fetch_x(i0 + kKB);
+#pragma unroll 1
+      for (int ks = 0; ks < kKB / 4; ++ks) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int gi = w * 4 + u;  // Gram tile: kind, (ta, tb)
+          const int ta = (gi >> 2) & 3, tb = gi & 3;
+          const float av = sm[((gi >> 4) ? L::ST_C : L::ST_Y) +
+                              (((ks * kN + ta * 16 + lr) << 2) + lq)];
+          const float bv = sm[L::ST_E + (((ks * kN + tb * 16 + lr) << 2) + lq)];
+          GR[u] = mfma(av, bv, GR[u]);
+        }
+      }
+      __syncthreads();
+      if (more) {
+        deposit_x();
+        __syncthreads();
+      }
+    }
+
+    // ---- per-head O(n^2) stage -------------------------------------------
+    float* sPhi = sm + L::PHI;  // Phi'[t][r]
+    float* sPsi = sm + L::PSI;  // Psi'[t][r]
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int gi = w * 4 + u;
+      const int ta = (gi >> 2) & 3, tb = gi & 3;
+      float* dst = (gi >> 4) ? sPsi : sPhi;
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        dst[(ta * 16 + 4 * lq + v) * kNP + tb * 16 + lr] = GR[u][v];
+    }
+    sm[L::V_SCR + tid] = hs;
+    __syncthreads();
+    if (tid < 64) {  // <H1, S0>: 8 partials per thread, fixed order
+      float x = 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x += sm[L::V_SCR + tid * 8 + u];
+      sm[L::V_SCR + tid * 8] = x;
+    }
+    if (tid >= 64 && tid < 64 + kN) {  // row r of Gam(r, t]
+      const int r = tid - 64;
       float acc = 1.f;
       for (int t = 0; t < kN; ++t) {
         float val = 0.f;
@@ -324,14 +424,19 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
+    if (tid == 0) {
+      float x = 0.f;
+      for (int u = 0; u < 64; ++u) x += sm[L::V_SCR + u * 8];
+      sm[L::V_SCR + 1] = x;  // phi0 = <H1, S0>
+    }
     if (tid < n)
       st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h,
          sPsi[tid * kNP + tid]);
 
     // running weight matrices and M
-#pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int e = tid + kThreads * w;
+#pragma unroll 1
+    for (int x = 0; x < 8; ++x) {
+      const int e = tid + kThreads * x;
       const int s = e >> 6, t = e & 63;  // entry (s, t)
       if (s < n && t < n) {
         const float bs = sm[L::V_B + s], bt = sm[L::V_B + t];
@@ -339,61 +444,24 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
         const float psi_st = sPsi[s * kNP + t], psi_ts = sPsi[t * kNP + s];
         const float gam_st = sm[L::GM + s * kNP + t];  // Gam(s,t], s <= t
         const float gam_ts = sm[L::GM + t * kNP + s];  // Gam(t,s], t <= s
+        const int o = s * kNP + t;
         // Wq[s][t] = Gam(s,t] beta_s Phi'[t][s]            (s <= t)
-        if (s <= t) wq[w] = fmaf(gam_st * bs, phi_ts, wq[w]);
+        if (s <= t) sm[L::WQ + o] = fmaf(gam_st * bs, phi_ts, sm[L::WQ + o]);
         // W1[s][t] = Gam(t,s] beta_t Phi'[s][t]            (s >= t)
-        if (s >= t) w1[w] = fmaf(gam_ts * bt, phi_st, w1[w]);
-        // W2[s][t] = Gam(t,s] Psi[s][t] (s > t), Gam(s,t] Psi[t][s] (s < t)
-        if (s > t) w2[w] = fmaf(gam_ts * (bs * bt), psi_st, w2[w]);
-        if (s < t) w2[w] = fmaf(gam_st * (bs * bt), psi_ts, w2[w]);
+        if (s >= t) sm[L::W1 + o] = fmaf(gam_ts * bt, phi_st, sm[L::W1 + o]);
+        // -W2[s][t]: W2 = Gam(t,s] Psi[s][t] (s > t), Gam(s,t] Psi[t][s] (s < t)
+        if (s > t) sm[L::W2 + o] = fmaf(-gam_ts * (bs * bt), psi_st, sm[L::W2 + o]);
+        if (s < t) sm[L::W2 + o] = fmaf(-gam_st * (bs * bt), psi_ts, sm[L::W2 + o]);
         // M[s][r=t] = Phi[s][r] QK[s][r] - Psi[s][r] KK[s][r]
-        const int x = s * kNP + t;
-        sm[L::MZ + x] = (bt * phi_st) * sm[L::QK + x] - ((bs * bt) * psi_st) * sm[L::KK + x];
+        sm[L::MZ + o] = (bt * phi_st) * sm[L::QK + o] -
+                        ((bs * bt) * psi_st) * sm[L::KK + o];
       }
     }
 
-    // chi, psi partials and the P terms of dq, dk
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = tt + 16 * u;
-      float cp = 0.f, pp = 0.f;
-      if (t < n) {
-        const float bt = sm[L::V_B + t];
-        const float pre = sm[L::V_PRE + t], suf = sm[L::V_SUF + t];
-#pragma unroll
-        for (int m = 0; m < J; ++m) {
-          const int j = jt + 32 * m;
-          float qv = 0.f, kv = 0.f;
-          if (j < Dk) {
-            qv = ld(q, qk_index(t, j));
-            kv = ld(k, qk_index(t, j));
-          }
-          const float p2 = bt * P2[m][u], p3 = bt * P3[m][u];
-          cp = fmaf(P1[m][u], qv, cp);
-          cp = fmaf(-p2, kv, cp);
-          pp = fmaf(p3, kv, pp);
-          dQ[m][u] = fmaf(pre, P1[m][u], dQ[m][u]);
-          dK[m][u] = fmaf(suf, p3, dK[m][u]);
-          dK[m][u] = fmaf(-pre, p2, dK[m][u]);
-        }
-      }
-      sm[L::RED + jt * kNP + t] = cp;
-      sm[L::RED + 32 * kNP + jt * kNP + t] = pp;
-    }
-    __syncthreads();
-    if (tid < n) {
-      float cs = 0.f, ps = 0.f;
-      for (int w = 0; w < 32; ++w) {
-        cs += sm[L::RED + w * kNP + tid];
-        ps += sm[L::RED + 32 * kNP + w * kNP + tid];
-      }
-      sm[L::V_CHI + tid] = cs;
-      sm[L::V_PSI + tid] = ps;
-    }
     __syncthreads();
     if (tid == kThreads - 1 && n > 0) {
       // A_t = sum_{s>=t} Gam(t,s] chi_s + Gam(t,end] phi0
-      float acc = sm[L::V_CHI + n - 1] + sm[L::V_SCR];
+      float acc = sm[L::V_CHI + n - 1] + sm[L::V_SCR + 1];
       sm[L::V_A + n - 1] = acc;
       for (int t = n - 1; t > 0; --t) {
         acc = fmaf(sm[L::V_G + t], acc, sm[L::V_CHI + t - 1]);
@@ -415,37 +483,24 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
     if (tid < n) {
       const int t = tid;
-      float dg = sm[L::V_PREX + t] * sm[L::V_A + t];
-      for (int r = 0; r < t; ++r) dg += sm[L::MZ + t * kNP + r];
-      st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h, dg);
+      float dgv = sm[L::V_PREX + t] * sm[L::V_A + t];
+      for (int r = 0; r < t; ++r) dgv += sm[L::MZ + t * kNP + r];
+      st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h, dgv);
     }
     __syncthreads();
   }
 
-  // ---- dq += K Wq;  dk += Q W1 - K W2 -------------------------------------
-  float* sWq = sm + L::QK;
-  float* sW1 = sm + L::KK;
-  float* sW2 = sm + L::GM;
-#pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const int e = tid + kThreads * w;
-    const int x = (e >> 6) * kNP + (e & 63);
-    sWq[x] = wq[w];
-    sW1[x] = w1[w];
-    sW2[x] = w2[w];
-  }
-  float* sKf = sm + L::A;
-  float* sQf = sm + L::A + kIB * L::DKP;
-  for (int s0 = 0; s0 < n; s0 += kIB) {
+  // ---- dq += K Wq;  dk += Q W1 - K W2 (MFMA over the chunk steps) --------
+  for (int s0 = 0; s0 < n; s0 += kKB) {
     {
-      constexpr int U = (kIB * L::DKP) / kThreads;
+      constexpr int U = (kKB * DKP + kThreads - 1) / kThreads;
       TIn rk[U], rq[U];
       uint32_t okm = 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int idx = tid + kThreads * u;
-        const int ss = idx / L::DKP, j = idx - ss * L::DKP, s = s0 + ss;
-        const bool ok = s < n && j < Dk;
+        const int ss = idx / DKP, j = idx - ss * DKP, s = s0 + ss;
+        const bool ok = idx < kKB * DKP && s < n && j < Dk;
         const int64_t o = ok ? qk_index(s, j) : 0;
         rk[u] = k[o];
         rq[u] = q[o];
@@ -454,54 +509,52 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int idx = tid + kThreads * u;
-        const bool ok = (okm >> u) & 1;
-        sKf[idx] = ok ? to_f32(rk[u]) : 0.f;
-        sQf[idx] = ok ? to_f32(rq[u]) : 0.f;
+        if (idx < kKB * DKP) {
+          const int ss = idx / DKP, j = idx - ss * DKP;
+          const bool ok = (okm >> u) & 1;
+          const int o = ((ss >> 2) * DKP + j) * 4 + (ss & 3);
+          sm[L::FK + o] = ok ? to_f32(rk[u]) : 0.f;
+          sm[L::FQ + o] = ok ? to_f32(rq[u]) : 0.f;
+        }
       }
     }
     __syncthreads();
 #pragma unroll 1
-    for (int ss = 0; ss < kIB; ++ss) {
-      const int s = s0 + ss;
-      float kv[J], qv[J], a_q[4], a_1[4], a_2[4];
+    for (int ks = 0; ks < kKB / 4; ++ks) {
+      const int srow = s0 + 4 * ks + lq;  // k index of this lane's B element
 #pragma unroll
-      for (int m = 0; m < J; ++m) {
-        kv[m] = sKf[ss * L::DKP + jt + 32 * m];
-        qv[m] = sQf[ss * L::DKP + jt + 32 * m];
+      for (int u = 0; u < NPW; ++u) {
+        if (!pv[u]) continue;
+        const int ja = ((ks * DKP + pj[u] * 16 + lr) << 2) + lq;
+        const float ak = sm[L::FK + ja], aq = sm[L::FQ + ja];
+        const int wb = srow * kNP + pt[u] * 16 + lr;
+        dQ[u] = mfma(ak, sm[L::WQ + wb], dQ[u]);
+        dK[u] = mfma(aq, sm[L::W1 + wb], dK[u]);
+        dK[u] = mfma(ak, sm[L::W2 + wb], dK[u]);
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a_q[u] = sWq[s * kNP + tt + 16 * u];
-        a_1[u] = sW1[s * kNP + tt + 16 * u];
-        a_2[u] = sW2[s * kNP + tt + 16 * u];
-      }
-#pragma unroll
-      for (int m = 0; m < J; ++m)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          dQ[m][u] = fmaf(kv[m], a_q[u], dQ[m][u]);
-          dK[m][u] = fmaf(qv[m], a_1[u], dK[m][u]);
-          dK[m][u] = fmaf(-kv[m], a_2[u], dK[m][u]);
-        }
     }
     __syncthreads();
   }
 #pragma unroll
-  for (int m = 0; m < J; ++m)
+  for (int u = 0; u < NPW; ++u) {
+    if (!pv[u]) continue;
+    const int t = pt[u] * 16 + lr;
+    if (t >= n) continue;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = jt + 32 * m, t = tt + 16 * u;
-      if (j < Dk && t < n) {
-        st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[m][u]);
-        st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[m][u]);
+    for (int v = 0; v < 4; ++v) {
+      const int j = pj[u] * 16 + 4 * lq + v;
+      if (j < Dk) {
+        st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[u][v]);
+        st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[u][v]);
       }
     }
+  }
 }
 
-template <typename TIn, int J>
+template <typename TIn, int JT>
 hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
-  const size_t lds = sizeof(float) * CL<J>::SIZE;
-  auto kern = chunk_kernel<TIn, J>;
+  const size_t lds = sizeof(float) * CL<JT>::SIZE;
+  auto kern = chunk_kernel<TIn, JT>;
   // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -514,12 +567,13 @@ hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
 
 template <typename TIn>
 hipError_t chunk_dispatch(const ChunkArgs& a, hipStream_t s) {
-  const int J = (a.Dk + 31) / 32;
-  if (J <= 1) return chunk_launch<TIn, 1>(a, s);
-  if (J <= 2) return chunk_launch<TIn, 2>(a, s);
-  if (J <= 4) return chunk_launch<TIn, 4>(a, s);
-  if (J <= 6) return chunk_launch<TIn, 6>(a, s);
-  if (J <= 8) return chunk_launch<TIn, 8>(a, s);
+  const int jt = (a.Dk + 15) / 16;
+  if (jt <= 1) return chunk_launch<TIn, 1>(a, s);
+  if (jt <= 2) return chunk_launch<TIn, 2>(a, s);
+  if (jt <= 4) return chunk_launch<TIn, 4>(a, s);
+  if (jt <= 8) return chunk_launch<TIn, 8>(a, s);
+  if (jt <= 12) return chunk_launch<TIn, 12>(a, s);
+  if (jt <= 16) return chunk_launch<TIn, 16>(a, s);
   return hipErrorInvalidValue;
 }
 
