@@ -28,6 +28,24 @@ FP32_VECTOR_PEAK_TF = 157.3    # MI355X FP32 vector, TFLOP/s
 FLOPS_FWD = 7                  # per state element per step (S k, S q, decay+rank-1)
 FLOPS_BWD = 15                 # per state element per step (reverse sweep)
 
+# HBM bytes per launch of the forward sweep at the default workload, from
+# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy
+# calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).  They describe the
+# kernel built from sources with this digest and are not reported otherwise.
+FWD_TRAFFIC = {"sources_sha256_16": "422d2acc362bfe43",
+               "read_bytes": 342.5e6, "write_bytes": 308.3e6}
+FWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_sweep.h",
+               "gdr_sweep_fwd_bf16.hip")
+
+
+def fwd_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FWD_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_recurrence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -41,29 +59,58 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-T", type=int, default=2048)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (read + write), "
+                         "the reference for scaling HBM byte counters, and exit")
     return ap.parse_args()
 
 
-def cpu_baseline(T, seed, dtype):
-    """Time the float64 oracle (as it stands) on one kv group of the same
-    workload: 4 of the 64 value heads, full T, forward + backward."""
+def copy_calibration(mib):
+    """One warm-up and one measured dispatch of a plain contiguous fp32 copy
+    (mib MiB read, mib MiB written): the HBM byte counters of the second
+    dispatch, divided into its known size, give the counter scale factor."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read": n * 4, "bytes_written": n * 4,
+                                           "dispatches": 2}}), flush=True)
+
+
+def cpu_baseline(T, seed, dtype, budget_s=25.0):
+    """Time the float64 oracle (as it stands, one BLAS thread) on the same
+    workload, one (batch row, kv group) at a time: forward + backward of the
+    group's value heads over the full T.  Groups run until all are done or
+    the time budget is spent; tokens are scaled by the share of groups run."""
     from threadpoolctl import threadpool_limits
     import oracle.gdr_oracle as O
     from gated_delta_rule_recurrence_amd import inputs
     p = inputs.qwen35_9b(T, seed=seed, dtype=dtype)
     rep = p.Hv // p.Hk
-    sl = lambda a: a[:, :, 0:rep]
+    groups = [(b, hk) for b in range(p.B) for hk in range(p.Hk)]
+    done = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        O.forward(p.q[:, :, 0:1], p.k[:, :, 0:1], sl(p.v), sl(p.g), sl(p.beta))
-        O.backward(p.q[:, :, 0:1], p.k[:, :, 0:1], sl(p.v), sl(p.g), sl(p.beta),
-                   sl(p.dy))
+        for b, hk in groups:
+            bs, ks, vs = slice(b, b + 1), slice(hk, hk + 1), slice(hk * rep, (hk + 1) * rep)
+            O.forward(p.q[bs, :, ks], p.k[bs, :, ks], p.v[bs, :, vs], p.g[bs, :, vs],
+                      p.beta[bs, :, vs])
+            O.backward(p.q[bs, :, ks], p.k[bs, :, ks], p.v[bs, :, vs], p.g[bs, :, vs],
+                       p.beta[bs, :, vs], p.dy[bs, :, vs])
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
         dt = time.perf_counter() - t0
-    frac = rep / p.Hv
+    frac = done / len(groups)
     return {"value": p.B * T * frac / dt, "unit": "tokens/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"kv group 0 (value heads 0-{rep - 1} of {p.Hv}), B=1, T={T}, "
-                      f"fwd+bwd in {dt:.2f} s on 1 thread; tokens scaled by {rep}/{p.Hv}"}
+            "sample": f"{done} of {len(groups)} (batch row, kv group) units of the same "
+                      f"workload (B={p.B}, T={T}, {rep} value heads each), forward + "
+                      f"backward in {dt:.1f} s on 1 thread; tokens scaled by "
+                      f"{done}/{len(groups)}"}
 
 
 def main():
@@ -73,6 +120,9 @@ def main():
               "shards by (batch row, kv head) with no communication, see DESIGN.md",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     import torch
     from gated_delta_rule_recurrence_amd import _lib, inputs, ops
 
@@ -134,6 +184,17 @@ def main():
     fwd_flops = FLOPS_FWD * elems
     fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
     all_tf = (FLOPS_FWD + FLOPS_BWD) * elems / (ms * 1e-3) / 1e12
+    # algorithmic HBM bytes of one forward launch: q, k, v, g, beta read once,
+    # y, the residual rows e, the chunk checkpoints and S_T written once
+    esz = 2 if args.dtype == "bf16" else 4
+    nch = -(-T // args.chunk)
+    fwd_bytes = (B * T * (2 * Hk * Dk + Hv * Dv + 2 * Hv) * esz        # inputs
+                 + B * T * Hv * Dv * (esz + 4)                          # y, e
+                 + B * Hv * (nch + 1) * Dv * Dk * 4)                    # ckpt, S_T
+    traffic = None
+    default_workload = (args.T, args.B, args.chunk, args.dtype) == (2048, 1, 64, "bf16")
+    if default_workload and fwd_sources_digest() == FWD_TRAFFIC["sources_sha256_16"]:
+        traffic = FWD_TRAFFIC["read_bytes"] + FWD_TRAFFIC["write_bytes"]
 
     ckpt_mb = ckpt.numel() / 1e6
     ws_mb = ws.numel() / 1e6
@@ -157,7 +218,11 @@ def main():
         "roofline": {"bound": "alu", "kernel": "fwd_sweep_kernel",
                      "achieved": fwd_tf, "peak": FP32_VECTOR_PEAK_TF,
                      "unit": "TFLOP/s", "frac": fwd_tf / FP32_VECTOR_PEAK_TF,
-                     "traffic": None},
+                     "traffic": traffic,
+                     "flops_per_launch": fwd_flops,
+                     "algorithmic_bytes_per_launch": fwd_bytes,
+                     "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "avg_launch_ms": fwd_ms},
         "breakdown": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                       "useful_tflops_whole_step": all_tf,
                       "frac_whole_step_vs_fp32_vector_peak": all_tf / FP32_VECTOR_PEAK_TF,
