@@ -50,7 +50,7 @@ template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL,
-                                         0xF, 0xF, false));
+                                         0xF, 0xF, true));
 }
 
 constexpr int kDppQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: lane ^ 1
@@ -61,12 +61,18 @@ constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within 16
 // Sum over the 16 lanes of a DPP row; every lane of the row receives the
 // same bits (each stage adds two operands that are swapped between the two
 // partner lanes, and IEEE addition is commutative).
+// The last stage is written as one v_add_f32_dpp (the compiler keeps a
+// separate v_mov_dpp for row_mirror); the s_nop covers the two wait states
+// gfx9 requires between a VALU write and a DPP read of the same VGPR.
 __device__ __forceinline__ float rowsum16(float x) {
   x += dpp<kDppQuadSwap1>(x);
   x += dpp<kDppQuadSwap2>(x);
   x += dpp<kDppHalfMirror>(x);
-  x += dpp<kDppMirror>(x);
-  return x;
+  float r;
+  asm("s_nop 1\n\tv_add_f32_dpp %0, %1, %1 row_mirror row_mask:0xf bank_mask:0xf"
+      : "=v"(r)
+      : "v"(x));
+  return r;
 }
 
 }  // namespace gdr

@@ -211,6 +211,44 @@ __device__ __forceinline__ float pick(const float (&a)[N], int i) {
   return r;
 }
 
+// Store v[0..R) to the R consecutive elements o .. o+R-1 of p (R consecutive
+// state rows of one step of a [.., Dv] tensor).  One vector store when all R
+// rows exist and the address is R-element aligned, else element by element.
+template <typename T, int R>
+__device__ __forceinline__ void st_rows(T* __restrict__ p, int64_t o,
+                                        const float (&v)[R], int nvalid,
+                                        bool aligned) {
+  if (nvalid >= R && aligned) {
+    if constexpr (std::is_same<T, float>::value) {
+      if constexpr (R == 1) {
+        p[o] = v[0];
+      } else if constexpr (R == 2) {
+        *reinterpret_cast<float2*>(p + o) = make_float2(v[0], v[1]);
+      } else {
+        static_assert(R == 4, "rows per lane");
+        *reinterpret_cast<float4*>(p + o) = make_float4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+      uint32_t w[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) w[r] = from_f32<T>(v[r]).bits;
+      if constexpr (R == 1) {
+        p[o] = from_f32<T>(v[0]);
+      } else if constexpr (R == 2) {
+        *reinterpret_cast<uint32_t*>(p + o) = w[0] | (w[1] << 16);
+      } else {
+        static_assert(R == 4, "rows per lane");
+        *reinterpret_cast<uint2*>(p + o) =
+            make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nvalid) st(p, o + r, v[r]);
+  }
+}
+
 // Load this lane's part of rows [row0, row0+R) of a [Dv][Dk] matrix.
 template <int NC, int R>
 __device__ __forceinline__ void tile_load(float (&S)[R][NC],
@@ -299,6 +337,9 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   using Lo = SweepLayout<NC, R>;
   using St_ = Stager<TIn, NC, R, FAST>;
   __shared__ __align__(16) float lds[2][Lo::BUF];
+  // Fully unrolled 16-step blocks where the registers allow it (R <= 2 keeps
+  // two waves per SIMD; at R = 4 the unrolled block would drop to one).
+  constexpr bool kUnroll = FAST && R <= 2;
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -334,17 +375,30 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   const int my_row = row0 + p;  // row written by lanes p < R
   const bool writer = (p < R) && (my_row < Dv);
   const int64_t out0 = ((int64_t)b * T * Hv + h) * Dv + my_row;  // (b,0,h,row)
+  const int64_t rows0 = ((int64_t)b * T * Hv + h) * Dv + row0;   // (b,0,h,row0)
   const int64_t tstep = (int64_t)Hv * Dv;
+  const int nrow = Dv - row0;  // rows of this row group that exist (if < R)
+  const bool rows_aligned = (Dv % R) == 0;
   float* __restrict__ E = a.E;
   float* __restrict__ Sck = a.Sck;
   int to_ckpt = 0;  // generic path: steps until the next checkpoint
   int ckpt_slot = 0;
 
-  // One forward step t with operands `cur`; `oth` holds the operands of the
-  // previous step (its q is q_{t-1}, for the read-out y_{t-1}) and, once the
-  // dots have consumed it, is refilled with the operands of step s + 1.
+  // Per-step outputs are captured, not stored: after the dots of block step
+  // s, lane p == s keeps y_{tbase+s-1} and e_{tbase+s} of its R rows (every
+  // lane of a DPP row holds the same sums), and the block's outputs leave in
+  // one store per lane at the end of the block.
+  float ycap[R], ecap[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) ycap[r] = ecap[r] = 0.f;
+
+  // One forward step (block step s) with operands `cur`; `oth` holds the
+  // operands of the previous step (its q is q_{t-1}, for the read-out
+  // y_{t-1}) and, once the dots have consumed it, is refilled with the
+  // operands of block step s_next.
   auto step = [&](const StepOps<NC, R>& cur, StepOps<NC, R>& oth,
-                  const float* __restrict__ buf, int t, int s_next) {
+                  const float* __restrict__ buf, int s, int s_next)
+                  __attribute__((always_inline)) {
     if (!FAST) {
       if (to_ckpt == 0) {
         if (Sck != nullptr)
@@ -385,9 +439,11 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
       e[r] = cur.x[r] - gs * pk[r];
       d[r] = cur.beta * e[r];
     }
-    if (writer) {
-      if (t > 0) st(y, out0 + (t - 1) * tstep, sig * pick<R>(pq, p));
-      if (E != nullptr) E[out0 + t * tstep] = pick<R>(e, p);
+    const bool mine = p == s;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      ycap[r] = mine ? sig * pq[r] : ycap[r];
+      ecap[r] = mine ? e[r] : ecap[r];
     }
     // S_t = g_t S + d k^T  ==  sig' (St + (d / sig') k^T) with sig' = g_t sig
     const bool fold = gs < kRescale;
@@ -415,27 +471,49 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   StepOps<NC, R> A, B;
 #pragma unroll
   for (int c = 0; c < NC; ++c) B.q[c] = 0.f;
-  for (int blk = 0; blk < nblk; ++blk) {
+  // One staged block.  FULL blocks (16 steps, unrolled) and the others
+  // (a short last block, or every block when unrolling is off) are separate
+  // instantiations, so the main loop carries no code for the short case.
+  auto run_block = [&](int blk, auto full) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full)::value;
     const float* __restrict__ cur = lds[blk & 1];
     if (blk + 1 < nblk)
       stg.fetch(blk + 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, v, g,
                 beta);
     const int tbase = blk * kStage;
-    const int nsteps = min(kStage, T - tbase);
+    const int nsteps = FULL ? kStage : min(kStage, T - tbase);
     if (FAST && Sck != nullptr && (tbase % a.L) == 0)
       tile_store<NC, R>(St, sig, Sck + (bh * a.nch + tbase / a.L) * mat, row0,
                         p, Dk, Dv);
     load_ops<NC, R, false>(A, cur, 0, p, rg);
-    const int slast = nsteps - 1;
-    int s = 0;
-    for (; s + 1 < nsteps; s += 2) {
-      step(A, B, cur, tbase + s, s + 1);
-      step(B, A, cur, tbase + s + 1, min(s + 2, slast));
+    if constexpr (FULL) {
+      // every LDS offset is a compile-time constant
+#pragma unroll
+      for (int s = 0; s < kStage; s += 2) {
+        step(A, B, cur, s, s + 1);
+        step(B, A, cur, s + 1, s + 2 < kStage ? s + 2 : kStage - 1);
+      }
+    } else {
+      const int slast = nsteps - 1;
+      int s = 0;
+      for (; s + 1 < nsteps; s += 2) {
+        step(A, B, cur, s, s + 1);
+        step(B, A, cur, s + 1, min(s + 2, slast));
+      }
+      if (s < nsteps) step(A, B, cur, s, slast);
     }
-    if (s < nsteps) step(A, B, cur, tbase + s, slast);
+    if (p < nsteps) {
+      const int64_t o = rows0 + (int64_t)(tbase + p) * tstep;
+      if (E != nullptr) st_rows<float, R>(E, o, ecap, nrow, rows_aligned);
+      if (tbase + p > 0) st_rows<TIn, R>(y, o - tstep, ycap, nrow, rows_aligned);
+    }
     if (blk + 1 < nblk) stg.store(lds[(blk + 1) & 1]);
     __syncthreads();
-  }
+  };
+  const int nfull = kUnroll ? T / kStage : 0;
+  int blk = 0;
+  for (; blk < nfull; ++blk) run_block(blk, std::true_type{});
+  for (; blk < nblk; ++blk) run_block(blk, std::false_type{});
 
   if (T > 0) {
     const float* qlast = B.q;
@@ -458,6 +536,9 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
   using Lo = SweepLayout<NC, R>;
   using St_ = Stager<TIn, NC, R, FAST>;
   __shared__ __align__(16) float lds[2][Lo::BUF];
+  // Fully unrolled 16-step blocks where the registers allow it (R <= 2 keeps
+  // two waves per SIMD; at R = 4 the unrolled block would drop to one).
+  constexpr bool kUnroll = FAST && R <= 2;
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -495,10 +576,10 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
   }
   __syncthreads();
 
-  const int my_row = row0 + p;
-  const bool writer = (p < R) && (my_row < Dv);
-  const int64_t out0 = ((int64_t)b * T * Hv + h) * Dv + my_row;
+  const int64_t rows0 = ((int64_t)b * T * Hv + h) * Dv + row0;  // (b,0,h,row0)
   const int64_t tstep = (int64_t)Hv * Dv;
+  const int nrow = Dv - row0;
+  const bool rows_aligned = (Dv % R) == 0;
   float* __restrict__ C = a.C;
   float* __restrict__ Hck = a.Hck;
 
@@ -507,8 +588,15 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
   int last_chunk = (T - 1) / (a.L > 0 ? a.L : 1);
   int to_ckpt = T - 1 - last_chunk * a.L;  // steps until t % L == 0
 
+  // c_t and dv_t of block step s are captured by lane p == s and stored at
+  // the end of the block (as in the forward sweep).
+  float ccap[R], dvcap[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) ccap[r] = dvcap[r] = 0.f;
+
   auto step = [&](const StepOps<NC, R>& op, StepOps<NC, R>& oth,
-                  const float* __restrict__ buf, int t, int s_next) {
+                  const float* __restrict__ buf, int t, int s, int s_next)
+                  __attribute__((always_inline)) {
     load_ops<NC, R, true>(oth, buf, s_next, p, rg);
     // c_t = G k_t = tau (Ht k_t) + dy_t (q_t . k_t)
     float c[R];
@@ -525,10 +613,11 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
     float dvr[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) dvr[r] = op.beta * c[r];
-    if (writer) {
-      const int64_t o = out0 + t * tstep;
-      C[o] = pick<R>(c, p);
-      st(dv, o, pick<R>(dvr, p));
+    const bool mine = p == s;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      ccap[r] = mine ? c[r] : ccap[r];
+      dvcap[r] = mine ? dvr[r] : dvcap[r];
     }
     // H_t = g_t (tau Ht + dy q^T - dv k^T) = tau' (Ht + (dy q^T - dv k^T)/tau)
     const float inv = __builtin_amdgcn_rcpf(tau);
@@ -560,7 +649,10 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
     }
   };
 
-  for (int blk = nblk - 1; blk >= 0; --blk) {
+  // Blocks run last to first; only the last block of the sequence can be
+  // short, and it is the first one processed.
+  auto run_block = [&](int blk, auto full) __attribute__((always_inline)) {
+    constexpr bool FULL = decltype(full)::value;
     float* __restrict__ cur = lds[blk & 1];
     // q_t . k_t of this block: row group rg handles step rg
     {
@@ -578,20 +670,40 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
       stg.fetch(blk - 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, dy, g,
                 beta);
     const int tbase = blk * kStage;
-    const int nsteps = min(kStage, T - tbase);
+    const int nsteps = FULL ? kStage : min(kStage, T - tbase);
     StepOps<NC, R> A, B;
     load_ops<NC, R, true>(A, cur, nsteps - 1, p, rg);
-    int s = nsteps - 1;
-    for (; s >= 1; s -= 2) {
-      step(A, B, cur, tbase + s, s - 1);
-      step(B, A, cur, tbase + s - 1, max(s - 2, 0));
+    if constexpr (FULL) {
+#pragma unroll
+      for (int s = kStage - 1; s >= 1; s -= 2) {
+        step(A, B, cur, tbase + s, s, s - 1);
+        step(B, A, cur, tbase + s - 1, s - 1, s - 2 > 0 ? s - 2 : 0);
+      }
+    } else {
+      int s = nsteps - 1;
+      for (; s >= 1; s -= 2) {
+        step(A, B, cur, tbase + s, s, s - 1);
+        step(B, A, cur, tbase + s - 1, s - 1, max(s - 2, 0));
+      }
+      if (s == 0) step(A, B, cur, tbase, 0, 0);
     }
-    if (s == 0) step(A, B, cur, tbase, 0);
+    if (p < nsteps) {
+      const int64_t o = rows0 + (int64_t)(tbase + p) * tstep;
+      st_rows<float, R>(C, o, ccap, nrow, rows_aligned);
+      st_rows<TIn, R>(dv, o, dvcap, nrow, rows_aligned);
+    }
     if (FAST && tbase > 0 && (tbase % a.L) == 0)
       tile_store<NC, R>(Ht, tau, Hck + (bh * a.nch + tbase / a.L - 1) * mat,
                         row0, p, Dk, Dv);
     if (blk > 0) stg.store(lds[(blk - 1) & 1]);
     __syncthreads();
+  };
+  int blk = nblk - 1;
+  if (!kUnroll) {
+    for (; blk >= 0; --blk) run_block(blk, std::false_type{});
+  } else {
+    if (blk >= 0 && T % kStage != 0) run_block(blk--, std::false_type{});
+    for (; blk >= 0; --blk) run_block(blk, std::true_type{});
   }
   if (a.dS0 != nullptr)
     tile_store<NC, R>(Ht, tau, a.dS0 + bh * mat, row0, p, Dk, Dv);

@@ -181,6 +181,18 @@ def test_ragged_and_max_dims(cuda, dims):
     compare(run_gpu(p, cuda, 16), run_oracle(p), TOL["f32"], f"Dk={Dk} Dv={Dv}")
 
 
+@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_rows_per_lane_variants(cuda, B, dtype):
+    """Wide heads (Hv=64, Dv=256) give the sweeps enough workgroups to hold 2
+    (B=1) or 4 (B=2) state rows per lane on a 256-CU device; T=45 leaves a
+    short last staging block after two full ones."""
+    p = inputs.draw(B, 45, 16, 64, 16, 256, seed=37, normalised=True, S0_std=0.2,
+                    dST_std=1.0, dtype=dtype)
+    log(f"rows/lane B={B} {dtype}")
+    compare(run_gpu(p, cuda, 16), run_oracle(p), TOL[dtype], f"wide B={B} {dtype}")
+
+
 def test_bf16_small(cuda):
     p = inputs.draw(2, 70, 2, 4, 64, 32, seed=19, normalised=True, S0_std=0.1,
                     dST_std=1.0, dtype="bf16")
