@@ -22,16 +22,21 @@
 // followed by O(n^2) work per head and the products dq += K Wq,
 // dk += Q W1 - K W2 with [n x n] weight matrices summed over the heads.
 //
-// Mapping: one workgroup of 512 threads (8 waves) per (batch row, kv head,
-// chunk).  It loops over the Hv/Hk value heads of the kv head in ascending
-// order and accumulates dq, dk in registers, so the GQA sum has a fixed order
-// and needs no atomics.  The contractions over Dv and the final products run
-// on fp32 MFMA (v_mfma_f32_16x16x4_f32): the [Dk x n] plane is cut into
-// 16 x 16 tiles (jt, tt) handed to the waves in jt-major order, each tile
-// holding P1, P2', P3', dq and dk in the MFMA accumulator layout (lane l,
-// register v: row 16 jt + 4 (l / 16) + v, column 16 tt + l % 16).  MFMA
-// operands are staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a
-// fragment (lane l <-> m = l % 16, k = l / 16) is 64 consecutive floats.
+// Mapping: one workgroup of 256 threads (4 waves, one per SIMD, so each wave
+// may hold 512 registers) per (batch row, kv head, chunk).  It loops over the
+// Hv/Hk value heads of the kv head in ascending order and accumulates dq, dk
+// in registers, so the GQA sum has a fixed order and needs no atomics.  Wave
+// w owns the chunk steps 16w .. 16w+15: the [Dk x 16] slices of P1, P2', P3',
+// dq, dk (all Dk tiles) and the rows 16w.. of Phi', Psi', QK, KK.  Every
+// contraction runs on fp32 MFMA (v_mfma_f32_16x16x4_f32) with the
+// accumulator layout "lane l, register v: row 16 i + 4 (l / 16) + v, column
+// 16 j + l % 16" of a 16 x 16 tile (i, j).  The Dv contractions P and the Gram
+// matrices share one pass over Dv: the dy/c fragments of a wave are at once
+// the B operands of P and the A operands of Phi', Psi'.  MFMA operands are
+// staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a fragment (lane
+// l <-> m = l % 16, k = l / 16) is 64 consecutive floats, 16 Dv rows per
+// block, with the next block fetched into registers while the current one is
+// multiplied.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -40,11 +45,11 @@ namespace {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / 64;
+constexpr int kThreads = 256;
 constexpr int kN = 64;       // max chunk length
 constexpr int kNP = kN + 1;  // padded row stride of [kN][kN] LDS matrices
-constexpr int kKB = 8;       // Dv rows per staged block (2 MFMA k-steps)
+constexpr int kKB = 32;      // Dv rows per staged block of the Dv pass
+constexpr int kSB = 16;      // chunk steps per staged block of the final products
 
 __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -53,44 +58,136 @@ __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
 template <int JT>
 struct CL {  // LDS layout, offsets in floats
   static constexpr int DKP = 16 * JT;
-  static constexpr int G = 4 * JT;  // j-groups of 4 rows (chi/psi partials)
-  // Phase A stage: S0, H1 [kKB/4][DKP][4]; DY, C, E [kKB/4][kN][4]
-  static constexpr int ST_S = 0, ST_H = kKB * DKP, ST_Y = 2 * kKB * DKP,
+  // The Dv pass covers JPW column tiles of Dk at a time (NJP passes), which
+  // bounds the live P1, P2', P3' accumulators to 3 JPW tiles per wave.
+  static constexpr int JPW = JT < 4 ? JT : 4;
+  static constexpr int NJP = JT / JPW;
+  static constexpr int PC = 16 * JPW;  // Dk columns of one pass
+  // Dv block stage: S0, H1 row-major [kKB][PCP] (rows padded so that the
+  // four rows of an MFMA fragment fall in disjoint banks); DY, C, E
+  // k-interleaved [kKB/4][kN][4]
+  static constexpr int PCP = PC == 16 ? 48 : PC + 16;
+  static constexpr int ST_S = 0, ST_H = kKB * PCP, ST_Y = 2 * kKB * PCP,
                        ST_C = ST_Y + kKB * kN, ST_E = ST_C + kKB * kN;
   static constexpr int STAGE = ST_E + kKB * kN;
-  // per-head O(n^2) arrays.  Phi'/Psi' alias the stage (written after the
-  // last Gram block); the chi/psi partials alias Gam/M (consumed before
-  // those are formed).
+  // per-head O(n^2) arrays, after the Dv pass (alias the stage)
   static constexpr int PHI = 0, PSI = PHI + kN * kNP, GM = PSI + kN * kNP,
-                       MZ = GM + kN * kNP, VEC = MZ + kN * kNP;
-  static constexpr int RED = GM;
-  static_assert(2 * G * kNP <= 2 * kN * kNP, "chi/psi partials fit Gam/M");
-  static_assert(STAGE <= GM, "stage stays clear of the chi/psi partials");
+                       MZ = GM + kN * kNP;
+  static constexpr int HEAD = MZ + kN * kNP;
+  // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns)
+  static constexpr int QS = 0, KS = 64 * kN, QKST = 2 * 64 * kN;
+  // k, q stage of the final products: [kSB/4][DKP][4] each
+  static constexpr int FK = 0, FQ = kSB * DKP, FINAL = 2 * kSB * DKP;
+  static constexpr int A_SZ0 = STAGE > HEAD ? STAGE : HEAD;
+  static constexpr int A_SZ1 = A_SZ0 > QKST ? A_SZ0 : QKST;
+  static constexpr int A_SZ = A_SZ1 > FINAL ? A_SZ1 : FINAL;
+  // per-head vectors
+  static constexpr int VEC = A_SZ;
   static constexpr int V_G = VEC, V_B = VEC + kN, V_PRE = VEC + 2 * kN,
                        V_PREX = VEC + 3 * kN, V_SUF = VEC + 4 * kN,
                        V_CHI = VEC + 5 * kN, V_PSI = VEC + 6 * kN,
-                       V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;  // 512 floats
-  static constexpr int HEAD = V_SCR + kThreads;
-  // final products: K, Q blocks [kKB/4][DKP][4]
-  static constexpr int FK = 0, FQ = FK + kKB * DKP;
-  static constexpr int FINAL = FQ + kKB * DKP;
-  // QK/KK staging: q, k [kN][kNP] j-blocks of 64
-  static constexpr int QKST = 2 * kN * kNP;
-  static constexpr int A_SZ0 = STAGE > HEAD ? STAGE : HEAD;
-  static constexpr int A_SZ1 = A_SZ0 > FINAL ? A_SZ0 : FINAL;
-  static constexpr int A_SZ = A_SZ1 > QKST ? A_SZ1 : QKST;
+                       V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;  // kThreads
   // persistent per workgroup: QK, KK and the head sums W1, -W2, Wq [kN][kNP]
-  static constexpr int QK = A_SZ, KK = QK + kN * kNP, W1 = KK + kN * kNP,
-                       W2 = W1 + kN * kNP, WQ = W2 + kN * kNP;
+  static constexpr int QK = V_SCR + kThreads, KK = QK + kN * kNP,
+                       W1 = KK + kN * kNP, W2 = W1 + kN * kNP,
+                       WQ = W2 + kN * kNP;
   static constexpr int SIZE = WQ + kN * kNP;
+  static_assert(SIZE * 4 <= 160 * 1024, "LDS budget of one workgroup");
+  static_assert(JT % JPW == 0, "whole passes");
 };
 
-template <typename TIn, int JT>
-__global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
+// Four consecutive elements p[o .. o+3] as fp32; elements at or beyond `lim`
+// (and all four when !ok) read as 0.  VEC: o is a multiple of 4 and the
+// four are either all below lim or all at/above it, so one vector load does.
+template <bool VEC, typename T>
+__device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
+                                  int lim) {
+  f4 r = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (VEC) {
+    if constexpr (sizeof(T) == 4) {
+      const float4 x = *reinterpret_cast<const float4*>(p + (ok ? o : 0));
+      r = f4{x.x, x.y, x.z, x.w};
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p + (ok ? o : 0));
+      r = f4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+             __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u)};
+    }
+    if (!ok) r = f4{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const bool good = ok && x < lim;
+      const T v = p[good ? o + x : 0];  // never an address past the row
+      r[x] = good ? to_f32(v) : 0.f;
+    }
+  }
+  return r;
+}
+
+// Four consecutive elements p[o .. o+3] held as the raw loaded bits, so that
+// issuing the load does not wait for it: the validity mask depends on the
+// indices only, and zeroing and bf16 widening happen in get(), where the
+// block is consumed.  VEC as in ld4.
+template <typename T, bool VEC>
+struct Quad;
+
+template <>
+struct Quad<float, true> {
+  float4 v;
+  __device__ __forceinline__ void load(const float* __restrict__ p, int64_t o, bool ok, int) {
+    v = *reinterpret_cast<const float4*>(p + (ok ? o : 0));
+  }
+  __device__ __forceinline__ static uint32_t mask(bool ok, int) { return ok ? 15u : 0u; }
+  __device__ __forceinline__ f4 get(uint32_t m) const {
+    return m ? f4{v.x, v.y, v.z, v.w} : f4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+template <>
+struct Quad<bf16, true> {
+  uint2 v;
+  __device__ __forceinline__ void load(const bf16* __restrict__ p, int64_t o, bool ok, int) {
+    v = *reinterpret_cast<const uint2*>(p + (ok ? o : 0));
+  }
+  __device__ __forceinline__ static uint32_t mask(bool ok, int) { return ok ? 15u : 0u; }
+  __device__ __forceinline__ f4 get(uint32_t m) const {
+    const f4 r = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+    return m ? r : f4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+template <typename T>
+struct Quad<T, false> {
+  T v[4];
+  __device__ __forceinline__ void load(const T* __restrict__ p, int64_t o, bool ok, int lim) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) v[x] = p[(ok && x < lim) ? o + x : 0];
+  }
+  __device__ __forceinline__ static uint32_t mask(bool ok, int lim) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) m |= (uint32_t)(ok && x < lim) << x;
+    return m;
+  }
+  __device__ __forceinline__ f4 get(uint32_t m) const {
+    f4 r;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) r[x] = ((m >> x) & 1) ? to_f32(v[x]) : 0.f;
+    return r;
+  }
+};
+
+template <typename TIn, int JT, bool VEC>
+__global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   using L = CL<JT>;
   constexpr int DKP = L::DKP;
-  constexpr int NPAIR = 4 * JT;                      // (jt, tt) tiles
-  constexpr int NPW = (NPAIR + kWaves - 1) / kWaves;  // tiles per wave
+  constexpr int JPW = L::JPW, NJP = L::NJP, PC = L::PC;
+  constexpr int PCP = L::PCP;
+  constexpr int NSQ = kKB * PC / 4;  // 4-column quads of a pass's S0 slice
+  constexpr int SQT = (NSQ + kThreads - 1) / kThreads;  // per thread
+  constexpr int NFB = (kSB / 4) * (DKP / 4);  // 4x4 blocks of a k, q step block
+  static_assert(SQT <= 4 && NFB <= kThreads, "staging shares per thread");
   extern __shared__ __align__(16) float sm[];
 
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
@@ -108,95 +205,155 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l = tid & 63;
   const int lr = l & 15, lq = l >> 4;
+  const int tw = 16 * w;  // first chunk step of this wave's tiles
   const int64_t mat = (int64_t)Dv * Dk;
 
-  auto qk_index = [&](int t, int j) -> int64_t {
+  auto qk_index = [&](int t, int j) __attribute__((always_inline)) -> int64_t {
     return ((int64_t)(b * (int64_t)T + t0 + t) * Hk + hk) * Dk + j;
   };
 
-  // tiles of this wave
-  int pj[NPW], pt[NPW];
-  bool pv[NPW];
-#pragma unroll
-  for (int u = 0; u < NPW; ++u) {
-    const int pi = w * NPW + u;
-    pv[u] = (NPAIR % kWaves == 0) || pi < NPAIR;  // constant when tiles divide evenly
-    pj[u] = pv[u] ? (pi >> 2) : 0;
-    pt[u] = pi & 3;
-  }
-
   // ---- QK and KK for the kv head (shared by all its value heads) ----------
   {
-    float qk8[8], kk8[8];
+    f4 acc[8];  // QK tiles (w, 0..3), KK tiles (w, 0..3)
 #pragma unroll
-    for (int x = 0; x < 8; ++x) qk8[x] = kk8[x] = 0.f;
-    float* sq = sm;
-    float* sk = sm + kN * kNP;
+    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < Dk; j0 += 64) {
-      constexpr int U = (kN * 64) / kThreads;
-      TIn rq[U], rk[U];
-      uint32_t okm = 0;
+      // 64 steps x 64 columns of q and k: 4 quads of 4 columns per thread
+      f4 rq[4], rk[4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = tid + kThreads * u;
-        const int s = idx >> 6, j = j0 + (idx & 63);
+      for (int u = 0; u < 4; ++u) {
+        const int qi = tid + kThreads * u;
+        const int s = qi >> 4, j = j0 + 4 * (qi & 15);
         const bool ok = s < n && j < Dk;
-        const int64_t o = ok ? qk_index(s, j) : 0;
-        rq[u] = q[o];
-        rk[u] = k[o];
-        okm |= (uint32_t)ok << u;
+        rq[u] = ld4<VEC>(q, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
+        rk[u] = ld4<VEC>(k, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = tid + kThreads * u;
-        const int s = idx >> 6, jj = idx & 63;
-        const bool ok = (okm >> u) & 1;
-        sq[s * kNP + jj] = ok ? to_f32(rq[u]) : 0.f;
-        sk[s * kNP + jj] = ok ? to_f32(rk[u]) : 0.f;
+      for (int u = 0; u < 4; ++u) {
+        const int qi = tid + kThreads * u;
+        const int s = qi >> 4, jq = qi & 15;
+        *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq[u];
+        *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk[u];
       }
       __syncthreads();
-#pragma unroll 1
-      for (int x = 0; x < 8; ++x) {
-        const int e = tid + kThreads * x;
-        const int s = e >> 6, r = e & 63;
-        float aq = qk8[x], ak = kk8[x];
-#pragma unroll 4
-        for (int jj = 0; jj < 64; ++jj) {
-          const float kr = sk[r * kNP + jj];
-          aq = fmaf(sq[s * kNP + jj], kr, aq);
-          ak = fmaf(sk[s * kNP + jj], kr, ak);
+#pragma unroll 2
+      for (int ks = 0; ks < 16; ++ks) {
+        const int fw = ((ks * kN + tw + lr) << 2) + lq;
+        const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
+          acc[tb] = mfma(aq, bk, acc[tb]);
+          acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
         }
-        qk8[x] = aq;
-        kk8[x] = ak;
       }
       __syncthreads();
     }
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sm[L::QK + o] = acc[tb][v];
+        sm[L::KK + o] = acc[4 + tb][v];
+      }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
       const int e = tid + kThreads * x;
       const int o = (e >> 6) * kNP + (e & 63);
-      sm[L::QK + o] = qk8[x];
-      sm[L::KK + o] = kk8[x];
-      sm[L::W1 + o] = 0.f;  // running sums over the value heads
+      sm[L::W1 + o] = 0.f;
       sm[L::W2 + o] = 0.f;
       sm[L::WQ + o] = 0.f;
     }
   }
 
-  f4 dQ[NPW], dK[NPW];
+  f4 dQ[JT], dK[JT];
 #pragma unroll
-  for (int u = 0; u < NPW; ++u) dQ[u] = dK[u] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < JT; ++u) dQ[u] = dK[u] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // staging roles: thread tid moves the quads tid + 256 u (row qd / (PC/4),
+  // columns 4 (qd % (PC/4))..) of a pass's S0 and H1 slices, and two quads
+  // (step ts, rows 4 iq.. and 4 iq + 16..) of dy, e and c.
+  const int ts = tid >> 2, iq = tid & 3;
+  // final products: thread tid < NFB moves the 4x4 block (steps 4 fb..,
+  // columns 4 fj..) of k and q
+  const int fb = tid / (DKP / 4), fj = tid % (DKP / 4);
+  const bool f_role = tid < NFB;
+
+  // ---- the block stream of the Dv passes ---------------------------------
+  // Blocks are numbered over the whole workgroup, gb = (hh NJP + jp) nbk +
+  // blk, with nbk (blocks per pass) rounded up to even; a block past Dv reads
+  // as zeros.  Two register slots carry blocks gb and gb + 1 while block gb -
+  // 1 is multiplied out of LDS, so every load has two MFMA phases to land,
+  // and the first blocks of the next pass or value head are in flight while
+  // the current one finishes.
+  const int nbk = (((Dv + kKB - 1) / kKB) + 1) & ~1;
+  const int nblk_all = rep * NJP * nbk;
+  const int64_t tstride = (int64_t)Hv * Dv;
+  struct Slot {
+    Quad<float, VEC> s[SQT], h[SQT], e[2], c[2];
+    Quad<TIn, VEC> y[2];
+    uint32_t ms;  // validity: 4 bits per S0/H1 quad, then 4 per dy/e/c quad
+  };
+  Slot RA, RB;
+  float hs = 0.f;  // partial <H1, S0> of the current value head
+  auto fetch = [&](Slot& R, int gbi) __attribute__((always_inline)) {
+    const int hb = gbi / (NJP * nbk);
+    const int rem = gbi - hb * (NJP * nbk);
+    const int jp = rem / nbk;
+    const int i0 = (rem - jp * nbk) * kKB;
+    const int64_t bh = (int64_t)b * Hv + hk * rep + hb;
+    const float* __restrict__ S0 = a.Sck + (bh * a.nch + jc) * mat;
+    const float* __restrict__ H1 = a.Hck + (bh * a.nch + jc) * mat;
+    const int64_t rowbase = ((int64_t)b * T + t0) * tstride + (bh - (int64_t)b * Hv) * Dv;
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < SQT; ++u) {
+      const int qd = tid + kThreads * u;
+      const int i = i0 + qd / (PC / 4), j = PC * jp + 4 * (qd % (PC / 4));
+      const bool ok = qd < NSQ && i < Dv && j < Dk;
+      const int64_t o = (int64_t)i * Dk + j;
+      R.s[u].load(S0, o, ok, Dk - j);
+      R.h[u].load(H1, o, ok, Dk - j);
+      m |= Quad<float, VEC>::mask(ok, Dk - j) << (4 * u);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = i0 + 4 * iq + 16 * u;
+      const bool ok = ts < n && i < Dv;
+      const int64_t o = rowbase + ts * tstride + i;
+      R.y[u].load(dy, o, ok, Dv - i);
+      R.e[u].load(a.E, o, ok, Dv - i);
+      R.c[u].load(a.C, o, ok, Dv - i);
+      m |= Quad<float, VEC>::mask(ok, Dv - i) << (16 + 4 * u);
+    }
+    R.ms = m;
+  };
+  auto deposit = [&](const Slot& R) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < SQT; ++u) {
+      const int qd = tid + kThreads * u;
+      if (qd < NSQ) {
+        const uint32_t mu = (R.ms >> (4 * u)) & 15u;
+        const int o = (qd / (PC / 4)) * PCP + 4 * (qd % (PC / 4));
+        *reinterpret_cast<f4*>(sm + L::ST_S + o) = R.s[u].get(mu);
+        *reinterpret_cast<f4*>(sm + L::ST_H + o) = R.h[u].get(mu);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t mu = (R.ms >> (16 + 4 * u)) & 15u;
+      const int o = ((iq + 4 * u) * kN + ts) << 2;
+      *reinterpret_cast<f4*>(sm + L::ST_Y + o) = R.y[u].get(mu);
+      *reinterpret_cast<f4*>(sm + L::ST_E + o) = R.e[u].get(mu);
+      *reinterpret_cast<f4*>(sm + L::ST_C + o) = R.c[u].get(mu);
+    }
+  };
+  fetch(RA, 0);
+  fetch(RB, 1);
 
   for (int hh = 0; hh < rep; ++hh) {
     const int h = hk * rep + hh;
-    const int64_t bh = (int64_t)b * Hv + h;
-    const float* __restrict__ S0 = a.Sck + (bh * a.nch + jc) * mat;
-    const float* __restrict__ H1 = a.Hck + (bh * a.nch + jc) * mat;
-    const int64_t rowbase = ((int64_t)b * T + t0) * Hv * Dv + (int64_t)h * Dv;
-    const int64_t tstride = (int64_t)Hv * Dv;
-    const TIn* __restrict__ dyh = dy + rowbase;
-    const float* __restrict__ Eh = a.E + rowbase;
-    const float* __restrict__ Ch = a.C + rowbase;
 
     // per-head vectors: g, beta and the running decay products
     if (tid < kN) {
@@ -219,191 +376,127 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
       }
     }
 
-    // Dv blocks (kKB rows) of S0, H1 and of dy, e, c are fetched into
-    // registers with unconditional loads from clamped offsets and deposited
-    // k-interleaved in the stage.
-    constexpr int US = (kKB * DKP + kThreads - 1) / kThreads;  // S0, H1 / thread
-    constexpr int UX = (kKB * kN) / kThreads;                  // dy, e, c / thread
-    float fs[US], fh[US], fe[UX], fc[UX];
-    TIn fy[UX];
-    uint32_t fok = 0;
-    float hs = 0.f;  // partial <H1, S0>
-    auto fetch_x = [&](int i0) {
+    // ---- passes over Dv: P1, P2', P3' (JPW column tiles per pass) and, in
+    // the first pass, Phi', Psi' (MFMA) --------------------------------------
+    hs = 0.f;
+    float cp = 0.f, pp = 0.f;  // partial chi, psi of step tw + lr
+    const int tl = tw + lr;    // the step this lane accumulates
+    f4 GR[8];
 #pragma unroll
-      for (int u = 0; u < UX; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ii = idx % kKB, t = idx / kKB, i = i0 + ii;  // rows fastest
-        const bool ok = i < Dv && t < n;
-        const int64_t o = ok ? t * tstride + i : 0;
-        fy[u] = dyh[o];
-        fe[u] = Eh[o];
-        fc[u] = Ch[o];
-        fok = (fok & ~(1u << (16 + u))) | ((uint32_t)ok << (16 + u));
-      }
-    };
-    auto fetch_s = [&](int i0) {
+    for (int u = 0; u < 8; ++u) GR[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ii = idx / DKP, j = idx - ii * DKP, i = i0 + ii;
-        const bool ok = idx < kKB * DKP && i < Dv && j < Dk;
-        const int64_t o = ok ? (int64_t)i * Dk + j : 0;
-        fs[u] = S0[o];
-        fh[u] = H1[o];
-        fok = (fok & ~(1u << u)) | ((uint32_t)ok << u);
-      }
-    };
-    auto deposit_x = [&]() {
+    for (int jp = 0; jp < NJP; ++jp) {
+      f4 P1[JPW], P2[JPW], P3[JPW];
 #pragma unroll
-      for (int u = 0; u < UX; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ii = idx % kKB, t = idx / kKB;
-        const bool ok = (fok >> (16 + u)) & 1;
-        const int o = ((ii >> 2) * kN + t) * 4 + (ii & 3);
-        sm[L::ST_Y + o] = ok ? to_f32(fy[u]) : 0.f;
-        sm[L::ST_E + o] = ok ? fe[u] : 0.f;
-        sm[L::ST_C + o] = ok ? fc[u] : 0.f;
-      }
-    };
-    auto deposit_s = [&]() {  // also accumulates <H1, S0>
+      for (int u = 0; u < JPW; ++u) P1[u] = P2[u] = P3[u] = f4{0.f, 0.f, 0.f, 0.f};
+      auto multiply = [&]() __attribute__((always_inline)) {
+#pragma unroll 2
+        for (int ks = 0; ks < kKB / 4; ++ks) {
+          const int fw = ((ks * kN + tw + lr) << 2) + lq;
+          const float by = sm[L::ST_Y + fw], bc = sm[L::ST_C + fw],
+                      bw = sm[L::ST_E + fw];
 #pragma unroll
-      for (int u = 0; u < US; ++u) {
-        const int idx = tid + kThreads * u;
-        if (idx < kKB * DKP) {
-          const int ii = idx / DKP, j = idx - ii * DKP;
-          const bool ok = (fok >> u) & 1;
-          const float sv = ok ? fs[u] : 0.f, hv = ok ? fh[u] : 0.f;
-          const int o = ((ii >> 2) * DKP + j) * 4 + (ii & 3);
-          sm[L::ST_S + o] = sv;
-          sm[L::ST_H + o] = hv;
-          hs = fmaf(sv, hv, hs);
-        }
-      }
-    };
-
-    // ---- P1 = S0^T DY, P2' = S0^T C, P3' = H1^T E  (MFMA over Dv) ---------
-    f4 P1[NPW], P2[NPW], P3[NPW];
-#pragma unroll
-    for (int u = 0; u < NPW; ++u) P1[u] = P2[u] = P3[u] = f4{0.f, 0.f, 0.f, 0.f};
-    fetch_s(0);
-    fetch_x(0);
-    deposit_s();
-    deposit_x();
-    __syncthreads();
-    for (int i0 = 0; i0 < Dv; i0 += kKB) {
-      const bool more = i0 + kKB < Dv;
-      if (more) {
-        fetch_s(i0 + kKB);
-        fetch_x(i0 + kKB);
-      }
-#pragma unroll 1
-      for (int ks = 0; ks < kKB / 4; ++ks) {
-#pragma unroll
-        for (int u = 0; u < NPW; ++u) {
-          if (!pv[u]) continue;
-          const int ja = ((ks * DKP + pj[u] * 16 + lr) << 2) + lq;
-          const int tb = ((ks * kN + pt[u] * 16 + lr) << 2) + lq;
-          const float as = sm[L::ST_S + ja], ah = sm[L::ST_H + ja];
-          const float by = sm[L::ST_Y + tb], bc = sm[L::ST_C + tb],
-                      be = sm[L::ST_E + tb];
-          P1[u] = mfma(as, by, P1[u]);
-          P2[u] = mfma(as, bc, P2[u]);
-          P3[u] = mfma(ah, be, P3[u]);
-        }
-      }
-      __syncthreads();
-      if (more) {
-        deposit_s();
-        deposit_x();
-        __syncthreads();
-      }
-    }
-
-    // chi, psi partials and the P terms of dq, dk (accumulator layout)
-#pragma unroll
-    for (int u = 0; u < NPW; ++u) {
-      if (!pv[u]) continue;
-      const int t = pt[u] * 16 + lr;
-      const int gidx = pj[u] * 4 + lq;
-      float cp = 0.f, pp = 0.f;
-      if (t < n) {
-        const float bt = sm[L::V_B + t];
-        const float pre = sm[L::V_PRE + t], suf = sm[L::V_SUF + t];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = pj[u] * 16 + 4 * lq + v;
-          float qv = 0.f, kv = 0.f;
-          if (j < Dk) {
-            qv = ld(q, qk_index(t, j));
-            kv = ld(k, qk_index(t, j));
+          for (int jt = 0; jt < JPW; ++jt) {
+            const int fa = (4 * ks + lq) * PCP + 16 * jt + lr;
+            const float as = sm[L::ST_S + fa], ah = sm[L::ST_H + fa];
+            P1[jt] = mfma(as, by, P1[jt]);
+            P2[jt] = mfma(as, bc, P2[jt]);
+            P3[jt] = mfma(ah, bw, P3[jt]);
+            // the fragments of one wave cover the slice once: <H1, S0>
+            if (w == 0) hs = fmaf(as, ah, hs);
           }
-          const float p2 = bt * P2[u][v], p3 = bt * P3[u][v];
-          cp = fmaf(P1[u][v], qv, cp);
-          cp = fmaf(-p2, kv, cp);
-          pp = fmaf(p3, kv, pp);
-          dQ[u][v] = fmaf(pre, P1[u][v], dQ[u][v]);
-          dK[u][v] = fmaf(suf, p3, dK[u][v]);
-          dK[u][v] = fmaf(-pre, p2, dK[u][v]);
-        }
-      }
-      sm[L::RED + gidx * kNP + t] = cp;
-      sm[L::RED + L::G * kNP + gidx * kNP + t] = pp;
-    }
-    __syncthreads();
-    if (tid < n) {
-      float cs = 0.f, ps = 0.f;
-      for (int x = 0; x < L::G; ++x) {
-        cs += sm[L::RED + x * kNP + tid];
-        ps += sm[L::RED + L::G * kNP + x * kNP + tid];
-      }
-      sm[L::V_CHI + tid] = cs;
-      sm[L::V_PSI + tid] = ps;
-    }
-
-    // ---- Phi' = DY E^T, Psi' = C E^T  (MFMA over Dv) ----------------------
-    f4 GR[4];
+          if (jp == 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) GR[u] = f4{0.f, 0.f, 0.f, 0.f};
-    fetch_x(0);
-    deposit_x();
-    __syncthreads();
-    for (int i0 = 0; i0 < Dv; i0 += kKB) {
-      const bool more = i0 + kKB < Dv;
-      if (more) fetch_x(i0 + kKB);
-#pragma unroll 1
-      for (int ks = 0; ks < kKB / 4; ++ks) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int gi = w * 4 + u;  // Gram tile: kind, (ta, tb)
-          const int ta = (gi >> 2) & 3, tb = gi & 3;
-          const float av = sm[((gi >> 4) ? L::ST_C : L::ST_Y) +
-                              (((ks * kN + ta * 16 + lr) << 2) + lq)];
-          const float bv = sm[L::ST_E + (((ks * kN + tb * 16 + lr) << 2) + lq)];
-          GR[u] = mfma(av, bv, GR[u]);
+            for (int tb = 0; tb < 4; ++tb) {
+              const float be = sm[L::ST_E + ((ks * kN + 16 * tb + lr) << 2) + lq];
+              GR[tb] = mfma(by, be, GR[tb]);
+              GR[4 + tb] = mfma(bc, be, GR[4 + tb]);
+            }
+          }
         }
+      };
+      // q, k of this lane's step for the pass's chi/psi, loaded before the
+      // pass's block loads so that waiting for them never waits for those
+      Quad<TIn, VEC> qq[JPW], kq[JPW];
+      uint32_t qkm = 0;
+#pragma unroll
+      for (int jt = 0; jt < JPW; ++jt) {
+        const int j = 16 * (JPW * jp + jt) + 4 * lq;
+        const bool ok = tl < n && j < Dk;
+        const int64_t o = qk_index(ok ? tl : 0, ok ? j : 0);
+        qq[jt].load(q, o, ok, Dk - j);
+        kq[jt].load(k, o, ok, Dk - j);
+        qkm |= Quad<TIn, VEC>::mask(ok, Dk - j) << (4 * jt);
       }
-      __syncthreads();
-      if (more) {
-        deposit_x();
+      const int gbase = (hh * NJP + jp) * nbk;
+      // nbk >= 2: a do-while keeps the loads in flight identical on every
+      // path out of the loop (the waits for qq/kq then skip the ring's loads)
+      int blk = 0;
+      do {
+        const int gb = gbase + blk;
+        __syncthreads();  // the stage is no longer read
+        deposit(RA);
         __syncthreads();
+        // unconditional (clamped) refills: every path has the same loads in
+        // flight, so the wait before a deposit covers only that slot
+        fetch(RA, min(gb + 2, nblk_all - 1));
+        multiply();
+        __syncthreads();
+        deposit(RB);
+        __syncthreads();
+        fetch(RB, min(gb + 3, nblk_all - 1));
+        multiply();
+        blk += 2;
+      } while (blk < nbk);
+
+      // chi, psi and the P terms of dq, dk (accumulator layout: the lane
+      // holds step tl and the rows 16 (JPW jp + jt) + 4 lq + v)
+      if (tl < n) {
+        const float bt = sm[L::V_B + tl];
+        const float pre = sm[L::V_PRE + tl], suf = sm[L::V_SUF + tl];
+#pragma unroll
+        for (int jt = 0; jt < JPW; ++jt) {
+          const int J = JPW * jp + jt;
+          const f4 qv = qq[jt].get((qkm >> (4 * jt)) & 15u);
+          const f4 kv = kq[jt].get((qkm >> (4 * jt)) & 15u);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float p2 = bt * P2[jt][v], p3 = bt * P3[jt][v];
+            cp = fmaf(P1[jt][v], qv[v], cp);
+            cp = fmaf(-p2, kv[v], cp);
+            pp = fmaf(p3, kv[v], pp);
+            dQ[J][v] = fmaf(pre, P1[jt][v], dQ[J][v]);
+            dK[J][v] = fmaf(suf, p3, dK[J][v]);
+            dK[J][v] = fmaf(-pre, p2, dK[J][v]);
+          }
+        }
       }
     }
+    // the four lanes of a step (lq = 0..3) hold disjoint row sets
+    cp += __shfl_xor(cp, 16);
+    cp += __shfl_xor(cp, 32);
+    pp += __shfl_xor(pp, 16);
+    pp += __shfl_xor(pp, 32);
+    if (lq == 0) {
+      sm[L::V_CHI + tl] = tl < n ? cp : 0.f;
+      sm[L::V_PSI + tl] = tl < n ? pp : 0.f;
+    }
+    __syncthreads();  // the stage is free: the O(n^2) arrays alias it
 
     // ---- per-head O(n^2) stage -------------------------------------------
     float* sPhi = sm + L::PHI;  // Phi'[t][r]
     float* sPsi = sm + L::PSI;  // Psi'[t][r]
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int gi = w * 4 + u;
-      const int ta = (gi >> 2) & 3, tb = gi & 3;
-      float* dst = (gi >> 4) ? sPsi : sPhi;
+    for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        dst[(ta * 16 + 4 * lq + v) * kNP + tb * 16 + lr] = GR[u][v];
-    }
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sPhi[o] = GR[tb][v];
+        sPsi[o] = GR[4 + tb][v];
+      }
     sm[L::V_SCR + tid] = hs;
     __syncthreads();
-    if (tid < 64) {  // <H1, S0>: 8 partials per thread, fixed order
+    if (tid < 32) {  // <H1, S0>: 8 partials per thread, fixed order
       float x = 0.f;
 #pragma unroll
       for (int u = 0; u < 8; ++u) x += sm[L::V_SCR + tid * 8 + u];
@@ -426,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
     if (tid == 0) {
       float x = 0.f;
-      for (int u = 0; u < 64; ++u) x += sm[L::V_SCR + u * 8];
+      for (int u = 0; u < 32; ++u) x += sm[L::V_SCR + u * 8];
       sm[L::V_SCR + 1] = x;  // phi0 = <H1, S0>
     }
     if (tid < n)
@@ -434,8 +527,8 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
          sPsi[tid * kNP + tid]);
 
     // running weight matrices and M
-#pragma unroll 1
-    for (int x = 0; x < 8; ++x) {
+#pragma unroll 2
+    for (int x = 0; x < 16; ++x) {
       const int e = tid + kThreads * x;
       const int s = e >> 6, t = e & 63;  // entry (s, t)
       if (s < n && t < n) {
@@ -491,70 +584,62 @@ __global__ __launch_bounds__(kThreads) void chunk_kernel(ChunkArgs a) {
   }
 
   // ---- dq += K Wq;  dk += Q W1 - K W2 (MFMA over the chunk steps) --------
-  for (int s0 = 0; s0 < n; s0 += kKB) {
-    {
-      constexpr int U = (kKB * DKP + kThreads - 1) / kThreads;
-      TIn rk[U], rq[U];
-      uint32_t okm = 0;
+  for (int s0 = 0; s0 < n; s0 += kSB) {
+    if (f_role) {
+      f4 rk[4], rq[4];
+      const int j = 4 * fj;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = tid + kThreads * u;
-        const int ss = idx / DKP, j = idx - ss * DKP, s = s0 + ss;
-        const bool ok = idx < kKB * DKP && s < n && j < Dk;
-        const int64_t o = ok ? qk_index(s, j) : 0;
-        rk[u] = k[o];
-        rq[u] = q[o];
-        okm |= (uint32_t)ok << u;
+      for (int x = 0; x < 4; ++x) {
+        const int s = s0 + 4 * fb + x;
+        const bool ok = s < n && j < Dk;
+        rk[x] = ld4<VEC>(k, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
+        rq[x] = ld4<VEC>(q, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = tid + kThreads * u;
-        if (idx < kKB * DKP) {
-          const int ss = idx / DKP, j = idx - ss * DKP;
-          const bool ok = (okm >> u) & 1;
-          const int o = ((ss >> 2) * DKP + j) * 4 + (ss & 3);
-          sm[L::FK + o] = ok ? to_f32(rk[u]) : 0.f;
-          sm[L::FQ + o] = ok ? to_f32(rq[u]) : 0.f;
-        }
+      for (int y = 0; y < 4; ++y) {
+        const int o = ((fb * DKP + 4 * fj + y) << 2);
+        *reinterpret_cast<f4*>(sm + L::FK + o) = f4{rk[0][y], rk[1][y], rk[2][y], rk[3][y]};
+        *reinterpret_cast<f4*>(sm + L::FQ + o) = f4{rq[0][y], rq[1][y], rq[2][y], rq[3][y]};
       }
     }
     __syncthreads();
-#pragma unroll 1
-    for (int ks = 0; ks < kKB / 4; ++ks) {
-      const int srow = s0 + 4 * ks + lq;  // k index of this lane's B element
+#pragma unroll 2
+    for (int ks = 0; ks < kSB / 4; ++ks) {
+      const int wb = (s0 + 4 * ks + lq) * kNP + tw + lr;  // B: rows s, columns t
+      const float wq = sm[L::WQ + wb], w1 = sm[L::W1 + wb], w2 = sm[L::W2 + wb];
 #pragma unroll
-      for (int u = 0; u < NPW; ++u) {
-        if (!pv[u]) continue;
-        const int ja = ((ks * DKP + pj[u] * 16 + lr) << 2) + lq;
-        const float ak = sm[L::FK + ja], aq = sm[L::FQ + ja];
-        const int wb = srow * kNP + pt[u] * 16 + lr;
-        dQ[u] = mfma(ak, sm[L::WQ + wb], dQ[u]);
-        dK[u] = mfma(aq, sm[L::W1 + wb], dK[u]);
-        dK[u] = mfma(ak, sm[L::W2 + wb], dK[u]);
+      for (int jt = 0; jt < JT; ++jt) {
+        const int fa = ((ks * DKP + 16 * jt + lr) << 2) + lq;
+        const float ak = sm[L::FK + fa], aq = sm[L::FQ + fa];
+        dQ[jt] = mfma(ak, wq, dQ[jt]);
+        dK[jt] = mfma(aq, w1, dK[jt]);
+        dK[jt] = mfma(ak, w2, dK[jt]);
       }
     }
     __syncthreads();
   }
+  {
+    const int t = tw + lr;
+    if (t < n) {
 #pragma unroll
-  for (int u = 0; u < NPW; ++u) {
-    if (!pv[u]) continue;
-    const int t = pt[u] * 16 + lr;
-    if (t >= n) continue;
+      for (int jt = 0; jt < JT; ++jt) {
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = pj[u] * 16 + 4 * lq + v;
-      if (j < Dk) {
-        st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[u][v]);
-        st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[u][v]);
+        for (int v = 0; v < 4; ++v) {
+          const int j = 16 * jt + 4 * lq + v;
+          if (j < Dk) {
+            st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[jt][v]);
+            st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[jt][v]);
+          }
+        }
       }
     }
   }
 }
 
-template <typename TIn, int JT>
+template <typename TIn, int JT, bool VEC>
 hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
   const size_t lds = sizeof(float) * CL<JT>::SIZE;
-  auto kern = chunk_kernel<TIn, JT>;
+  auto kern = chunk_kernel<TIn, JT, VEC>;
   // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -565,16 +650,24 @@ hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename TIn, bool VEC>
+hipError_t chunk_dispatch_jt(const ChunkArgs& a, hipStream_t s) {
+  const int jt = (a.Dk + 15) / 16;
+  if (jt <= 1) return chunk_launch<TIn, 1, VEC>(a, s);
+  if (jt <= 2) return chunk_launch<TIn, 2, VEC>(a, s);
+  if (jt <= 4) return chunk_launch<TIn, 4, VEC>(a, s);
+  if (jt <= 8) return chunk_launch<TIn, 8, VEC>(a, s);
+  if (jt <= 12) return chunk_launch<TIn, 12, VEC>(a, s);
+  if (jt <= 16) return chunk_launch<TIn, 16, VEC>(a, s);
+  return hipErrorInvalidValue;
+}
+
+// Vector staging needs every 4-element group of a k/q row (Dk) and of a
+// dy/e/c row (Dv) to start on a 4-element boundary.
 template <typename TIn>
 hipError_t chunk_dispatch(const ChunkArgs& a, hipStream_t s) {
-  const int jt = (a.Dk + 15) / 16;
-  if (jt <= 1) return chunk_launch<TIn, 1>(a, s);
-  if (jt <= 2) return chunk_launch<TIn, 2>(a, s);
-  if (jt <= 4) return chunk_launch<TIn, 4>(a, s);
-  if (jt <= 8) return chunk_launch<TIn, 8>(a, s);
-  if (jt <= 12) return chunk_launch<TIn, 12>(a, s);
-  if (jt <= 16) return chunk_launch<TIn, 16>(a, s);
-  return hipErrorInvalidValue;
+  if (a.Dk % 4 == 0 && a.Dv % 4 == 0) return chunk_dispatch_jt<TIn, true>(a, s);
+  return chunk_dispatch_jt<TIn, false>(a, s);
 }
 
 }  // namespace
