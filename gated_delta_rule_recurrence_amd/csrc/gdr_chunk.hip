@@ -55,6 +55,28 @@ __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// DPP move with 1.0 in the lanes that get no source (the product identity).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or1(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.f),
+                                         __builtin_bit_cast(int, x), CTRL, ROWS,
+                                         0xF, false));
+}
+
+// Inclusive product over lanes 0..l of a wave: a Hillis-Steele scan with
+// row_shr inside each 16-lane row, then row_bcast:15 and row_bcast:31 across
+// rows.  Only products of the inputs are formed (no division).
+__device__ __forceinline__ float wave_prefix_product(float x) {
+  x *= dpp_or1<0x111, 0xF>(x);  // row_shr:1
+  x *= dpp_or1<0x112, 0xF>(x);  // row_shr:2
+  x *= dpp_or1<0x114, 0xF>(x);  // row_shr:4
+  x *= dpp_or1<0x118, 0xF>(x);  // row_shr:8
+  x *= dpp_or1<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
+  x *= dpp_or1<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 template <int JT>
 struct CL {  // LDS layout, offsets in floats
   static constexpr int DKP = 16 * JT;
@@ -362,18 +384,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       sm[L::V_B + tid] = ok ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
     }
     __syncthreads();
-    if (tid == kThreads - 1) {
-      float acc = 1.f;
-      for (int t = 0; t < n; ++t) {
-        sm[L::V_PREX + t] = acc;
-        acc *= sm[L::V_G + t];
-        sm[L::V_PRE + t] = acc;
-      }
-      acc = 1.f;
-      for (int t = n - 1; t >= 0; --t) {
-        sm[L::V_SUF + t] = acc;
-        acc *= sm[L::V_G + t];
-      }
+    if (w == 3) {  // decay products along the chunk, one step per lane
+      // pre[t] = Gam(start, t], prex[t] = Gam(start, t-1], suf[t] = Gam(t, end]
+      const float gi = l < n ? sm[L::V_G + l] : 1.f;
+      const float ge = (l >= 1 && l <= n) ? sm[L::V_G + l - 1] : 1.f;
+      const float gs = (l >= 1 && l < n) ? sm[L::V_G + n - l] : 1.f;  // lane l <-> t = n-1-l
+      sm[L::V_PRE + l] = wave_prefix_product(gi);
+      sm[L::V_PREX + l] = wave_prefix_product(ge);
+      const float sf = wave_prefix_product(gs);
+      if (l < n) sm[L::V_SUF + n - 1 - l] = sf;
     }
 
     // ---- passes over Dv: P1, P2', P3' (JPW column tiles per pass) and, in
@@ -502,18 +521,13 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       for (int u = 0; u < 8; ++u) x += sm[L::V_SCR + tid * 8 + u];
       sm[L::V_SCR + tid * 8] = x;
     }
-    if (tid >= 64 && tid < 64 + kN) {  // row r of Gam(r, t]
-      const int r = tid - 64;
-      float acc = 1.f;
-      for (int t = 0; t < kN; ++t) {
-        float val = 0.f;
-        if (t == r) {
-          val = 1.f;
-        } else if (t > r && t < n) {
-          acc *= sm[L::V_G + t];
-          val = acc;
-        }
-        sm[L::GM + r * kNP + t] = val;
+    {  // rows r = 16 w .. 16 w + 15 of Gam(r, t] (lane l <-> t = l)
+      const float gl = l < n ? sm[L::V_G + l] : 1.f;
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int r = tw + i;
+        const float y = wave_prefix_product(l > r ? gl : 1.f);
+        sm[L::GM + r * kNP + l] = l == r ? 1.f : ((l > r && l < n) ? y : 0.f);
       }
     }
     __syncthreads();
@@ -548,37 +562,52 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         // M[s][r=t] = Phi[s][r] QK[s][r] - Psi[s][r] KK[s][r]
         sm[L::MZ + o] = (bt * phi_st) * sm[L::QK + o] -
                         ((bs * bt) * psi_st) * sm[L::KK + o];
+      } else {
+        sm[L::MZ + s * kNP + t] = 0.f;  // M is multiplied over all 64 rows
       }
     }
 
     __syncthreads();
-    if (tid == kThreads - 1 && n > 0) {
-      // A_t = sum_{s>=t} Gam(t,s] chi_s + Gam(t,end] phi0
-      float acc = sm[L::V_CHI + n - 1] + sm[L::V_SCR + 1];
-      sm[L::V_A + n - 1] = acc;
-      for (int t = n - 1; t > 0; --t) {
-        acc = fmaf(sm[L::V_G + t], acc, sm[L::V_CHI + t - 1]);
-        sm[L::V_A + t - 1] = acc;
+    // dg.  With A_t = sum_{s>=t} Gam(t,s] chi_s + Gam(t,end] phi0 and
+    // B_t[r] = sum_{s>=t} Gam(t,s] M[s][r] + Gam(t,end] psi_r:
+    //   dg_t = prex[t] A_t + sum_{r<t} Gam(r,t-1] B_t[r].
+    // Gam(t,s] for s >= t is row t of GM (0 below the diagonal), so the sums
+    // over s are the product GM [M | chi] (MFMA; chi rides in column 0 of a
+    // fifth tile), and the sum over r is a 16-lane row reduction.
+    {
+      f4 Bt[5];
+#pragma unroll
+      for (int u = 0; u < 5; ++u) Bt[u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int ks = 0; ks < 16; ++ks) {
+        const int sk = 4 * ks + lq;
+        const float ga = sm[L::GM + (tw + lr) * kNP + sk];  // A[t][s]
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          Bt[tb] = mfma(ga, sm[L::MZ + sk * kNP + 16 * tb + lr], Bt[tb]);
+        const float cb = lr == 0 ? sm[L::V_CHI + sk] : 0.f;
+        Bt[4] = mfma(ga, cb, Bt[4]);
       }
-    }
-    if (tid < n) {
-      // B_t[r] = sum_{s>=t} Gam(t,s] M[s][r] + Gam(t,end] psi_r, for t > r;
-      // store Gam(r,t-1] B_t[r] in place of M[t][r].
-      const int r = tid;
-      float bacc = 0.f;
-      for (int t = n - 1; t > r; --t) {
-        const float mtr = sm[L::MZ + t * kNP + r];
-        bacc = (t == n - 1) ? mtr + sm[L::V_PSI + r]
-                            : fmaf(sm[L::V_G + t + 1], bacc, mtr);
-        sm[L::MZ + t * kNP + r] = sm[L::GM + r * kNP + t - 1] * bacc;
+      const float phi0 = sm[L::V_SCR + 1];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = tw + 4 * lq + v;
+        const float gend = n > 0 ? sm[L::GM + t * kNP + n - 1] : 0.f;  // Gam(t,end]
+        float acc = 0.f;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const int r = 16 * tb + lr;
+          const float bv = fmaf(gend, sm[L::V_PSI + r], Bt[tb][v]);
+          const float gr = r < t ? sm[L::GM + r * kNP + t - 1] : 0.f;  // Gam(r,t-1]
+          acc = fmaf(gr, bv, acc);
+        }
+        acc = rowsum16(acc);
+        if (lr == 0 && t < n) {
+          const float At = fmaf(gend, phi0, Bt[4][v]);
+          st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h,
+             fmaf(sm[L::V_PREX + t], At, acc));
+        }
       }
-    }
-    __syncthreads();
-    if (tid < n) {
-      const int t = tid;
-      float dgv = sm[L::V_PREX + t] * sm[L::V_A + t];
-      for (int r = 0; r < t; ++r) dgv += sm[L::MZ + t * kNP + r];
-      st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h, dgv);
     }
     __syncthreads();
   }
