@@ -408,30 +408,54 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       f4 P1[JPW], P2[JPW], P3[JPW];
 #pragma unroll
       for (int u = 0; u < JPW; ++u) P1[u] = P2[u] = P3[u] = f4{0.f, 0.f, 0.f, 0.f};
+      // One staged block: kKB / 4 MFMA k-steps.  The operands of k-step
+      // ks + 1 are read from LDS while the MFMAs of k-step ks issue.
       auto multiply = [&]() __attribute__((always_inline)) {
-#pragma unroll 2
-        for (int ks = 0; ks < kKB / 4; ++ks) {
+        constexpr int KS = kKB / 4;
+        const bool gram = jp == 0;  // Phi', Psi' ride along in the first pass
+        float by[2], bc[2], bw[2], be[2][4], as[2][JPW], ah[2][JPW];
+        auto rd = [&](int ks, int x) __attribute__((always_inline)) {
           const int fw = ((ks * kN + tw + lr) << 2) + lq;
-          const float by = sm[L::ST_Y + fw], bc = sm[L::ST_C + fw],
-                      bw = sm[L::ST_E + fw];
+          by[x] = sm[L::ST_Y + fw];
+          bc[x] = sm[L::ST_C + fw];
+          bw[x] = sm[L::ST_E + fw];
+          if (gram) {
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+              be[x][tb] = sm[L::ST_E + ((ks * kN + 16 * tb + lr) << 2) + lq];
+          }
 #pragma unroll
           for (int jt = 0; jt < JPW; ++jt) {
             const int fa = (4 * ks + lq) * PCP + 16 * jt + lr;
-            const float as = sm[L::ST_S + fa], ah = sm[L::ST_H + fa];
-            P1[jt] = mfma(as, by, P1[jt]);
-            P2[jt] = mfma(as, bc, P2[jt]);
-            P3[jt] = mfma(ah, bw, P3[jt]);
-            // the fragments of one wave cover the slice once: <H1, S0>
-            if (w == 0) hs = fmaf(as, ah, hs);
+            as[x][jt] = sm[L::ST_S + fa];
+            ah[x][jt] = sm[L::ST_H + fa];
           }
-          if (jp == 0) {
+        };
+        auto mm = [&](int x) __attribute__((always_inline)) {
+#pragma unroll
+          for (int jt = 0; jt < JPW; ++jt) {
+            P1[jt] = mfma(as[x][jt], by[x], P1[jt]);
+            P2[jt] = mfma(as[x][jt], bc[x], P2[jt]);
+            P3[jt] = mfma(ah[x][jt], bw[x], P3[jt]);
+            // the fragments of one wave cover the slice once: <H1, S0>
+            if (w == 0) hs = fmaf(as[x][jt], ah[x][jt], hs);
+          }
+          if (gram) {
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
-              const float be = sm[L::ST_E + ((ks * kN + 16 * tb + lr) << 2) + lq];
-              GR[tb] = mfma(by, be, GR[tb]);
-              GR[4 + tb] = mfma(bc, be, GR[4 + tb]);
+              GR[tb] = mfma(by[x], be[x][tb], GR[tb]);
+              GR[4 + tb] = mfma(bc[x], be[x][tb], GR[4 + tb]);
             }
           }
+        };
+        static_assert(KS % 2 == 0, "k-steps in pairs");
+        rd(0, 0);
+#pragma unroll 1
+        for (int ks = 0; ks < KS; ks += 2) {
+          rd(ks + 1, 1);
+          mm(0);
+          if (ks + 2 < KS) rd(ks + 2, 0);
+          mm(1);
         }
       };
       // q, k of this lane's step for the pass's chi/psi, loaded before the
