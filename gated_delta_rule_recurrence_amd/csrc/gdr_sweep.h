@@ -106,6 +106,7 @@ struct Stager {
   Slot kr[SK], qr[SK], xr[SX];
   TIn gb;  // g (threads 0..15) or beta (threads 16..31) of one step
   uint64_t ok;
+  bool full;  // every slot of the block is in range (no zero fill needed)
 
   __device__ __forceinline__ void fetch(int blk, int T, int Hk, int Hv,
                                         int Dk, int Dv, int b, int h, int hk,
@@ -148,15 +149,25 @@ struct Stager {
       m |= (uint64_t)good << (SK + SX);
     }
     ok = m;
+    full = t0 + kStage <= T && Dk == Lo::DKP && rowbase + Lo::RW <= Dv;
   }
 
   __device__ __forceinline__ void store(float* __restrict__ buf) const {
+    if (full)
+      store_impl<false>(buf);
+    else
+      store_impl<true>(buf);
+  }
+
+ private:
+  template <bool CHECK>
+  __device__ __forceinline__ void store_impl(float* __restrict__ buf) const {
     const int tid = threadIdx.x;
 #pragma unroll
     for (int u = 0; u < SK; ++u) {
       const int vi = tid + kThreads * u;
       if (vi < NKV) {
-        const bool good = (ok >> u) & 1;
+        const bool good = !CHECK || ((ok >> u) & 1);
         const int s = vi / (Lo::DKP / VW);
         const int c = (vi - s * (Lo::DKP / VW)) * VW;
         write(buf + Lo::K_OFF + s * Lo::DKP + c, kr[u], good);
@@ -167,20 +178,19 @@ struct Stager {
     for (int u = 0; u < SX; ++u) {
       const int vi = tid + kThreads * u;
       if (vi < NXV) {
-        const bool good = (ok >> (SK + u)) & 1;
+        const bool good = !CHECK || ((ok >> (SK + u)) & 1);
         const int s = vi / (Lo::RW / VW);
         const int r = (vi - s * (Lo::RW / VW)) * VW;
         write(buf + Lo::X_OFF + s * Lo::RW + r, xr[u], good);
       }
     }
     if (tid < 32) {
-      const bool good = (ok >> (SK + SX)) & 1;
+      const bool good = !CHECK || ((ok >> (SK + SX)) & 1);
       buf[(tid < 16 ? Lo::G_OFF : Lo::B_OFF) + (tid & 15)] =
           good ? to_f32(gb) : 0.f;
     }
   }
 
- private:
   __device__ __forceinline__ static void write(float* dst, const Raw16& r,
                                                bool good) {
     float v[VW];
@@ -414,16 +424,14 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
     float pk[R], pq[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float ak0 = 0.f, ak1 = 0.f, aq0 = 0.f, aq1 = 0.f;
+      float ak = St[r][0] * cur.k[0], aq = St[r][0] * oth.q[0];
 #pragma unroll
-      for (int c = 0; c < NC; c += 2) {
-        ak0 = fmaf(St[r][c], cur.k[c], ak0);
-        aq0 = fmaf(St[r][c], oth.q[c], aq0);
-        ak1 = fmaf(St[r][c + 1], cur.k[c + 1], ak1);
-        aq1 = fmaf(St[r][c + 1], oth.q[c + 1], aq1);
+      for (int c = 1; c < NC; ++c) {
+        ak = fmaf(St[r][c], cur.k[c], ak);
+        aq = fmaf(St[r][c], oth.q[c], aq);
       }
-      pk[r] = ak0 + ak1;
-      pq[r] = aq0 + aq1;
+      pk[r] = ak;
+      pq[r] = aq;
     }
     load_ops<NC, R, false>(oth, buf, s_next, p, rg);
 #pragma unroll
@@ -602,13 +610,10 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
     float c[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float a0 = 0.f, a1 = 0.f;
+      float a0 = Ht[r][0] * op.k[0];
 #pragma unroll
-      for (int j = 0; j < NC; j += 2) {
-        a0 = fmaf(Ht[r][j], op.k[j], a0);
-        a1 = fmaf(Ht[r][j + 1], op.k[j + 1], a1);
-      }
-      c[r] = fmaf(tau, rowsum16(a0 + a1), op.x[r] * op.qk);
+      for (int j = 1; j < NC; ++j) a0 = fmaf(Ht[r][j], op.k[j], a0);
+      c[r] = fmaf(tau, rowsum16(a0), op.x[r] * op.qk);
     }
     float dvr[R];
 #pragma unroll
