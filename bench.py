@@ -32,8 +32,8 @@ FLOPS_BWD = 15                 # per state element per step (reverse sweep)
 # rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy
 # calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).  They describe the
 # kernel built from sources with this digest and are not reported otherwise.
-FWD_TRAFFIC = {"sources_sha256_16": "422d2acc362bfe43",
-               "read_bytes": 342.5e6, "write_bytes": 308.3e6}
+FWD_TRAFFIC = {"sources_sha256_16": "2cc936bfdea4eed4",
+               "read_bytes": 343.1e6, "write_bytes": 308.3e6}
 FWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_sweep.h",
                "gdr_sweep_fwd_bf16.hip")
 
