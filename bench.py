@@ -142,6 +142,8 @@ def main():
     shape = ops.shape_of(q, v, args.chunk, dt)
     ckpt = torch.empty(_lib.checkpoint_bytes(shape), dtype=torch.uint8, device=dev)
     ws = torch.empty(_lib.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+    fws = torch.empty(max(_lib.forward_workspace_bytes(shape), 1), dtype=torch.uint8,
+                      device=dev)
     y = torch.empty_like(v)
     S_T = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
     outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
@@ -152,7 +154,7 @@ def main():
 
     def fwd():
         ops.gdr_forward(q, k, v, g, beta, None, chunk=args.chunk, y=y, S_T=S_T,
-                        ckpt=ckpt)
+                        ckpt=ckpt, workspace=fws)
 
     def bwd():
         ops.gdr_backward(q, k, g, beta, saved, dy, None, workspace=ws, out=outs)

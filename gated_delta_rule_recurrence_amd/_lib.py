@@ -37,7 +37,9 @@ _SIGNATURES = {
     "gdr_num_chunks": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_int64)]),
     "gdr_checkpoint_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
     "gdr_backward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
-    "gdr_forward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 10),
+    "gdr_forward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
+    "gdr_forward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 10
+                    + [ctypes.c_size_t, _vp]),
     "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 14
                      + [ctypes.c_size_t, _vp]),
     "gdr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -100,6 +102,13 @@ def checkpoint_bytes(shape: GdrShape) -> int:
     return out.value
 
 
+def forward_workspace_bytes(shape: GdrShape) -> int:
+    out = ctypes.c_size_t()
+    check(load().gdr_forward_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)),
+          "gdr_forward_workspace_bytes")
+    return out.value
+
+
 def backward_workspace_bytes(shape: GdrShape) -> int:
     out = ctypes.c_size_t()
     check(load().gdr_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)),
@@ -107,10 +116,13 @@ def backward_workspace_bytes(shape: GdrShape) -> int:
     return out.value
 
 
-def forward_raw(shape, q, k, v, g, beta, S0, y, S_T, ckpt, stream) -> int:
+def forward_raw(shape, q, k, v, g, beta, S0, y, S_T, ckpt, workspace,
+                workspace_bytes, stream) -> int:
     """gdr_forward with integer device addresses (0 = NULL); returns the status."""
-    return load().gdr_forward(ctypes.byref(shape), *(_vp(x or None) for x in
-                              (q, k, v, g, beta, S0, y, S_T, ckpt, stream)))
+    ptrs = [_vp(x or None) for x in (q, k, v, g, beta, S0, y, S_T, ckpt, workspace)]
+    return load().gdr_forward(ctypes.byref(shape), *ptrs,
+                              ctypes.c_size_t(int(workspace_bytes)),
+                              _vp(stream or None))
 
 
 def backward_raw(shape, q, k, g, beta, ckpt, dy, dS_T, dq, dk, dv, dg, dbeta,

@@ -30,8 +30,9 @@ struct Sizes {
   int64_t state;     // elements of one [B][Hv][Dv][Dk] tensor
   int64_t ckpt;      // elements of [B][Hv][nch][Dv][Dk]
   int64_t rows;      // elements of one [B][T][Hv][Dv] tensor
-  int64_t ckpt_bytes, ws_bytes;
+  int64_t ckpt_bytes, ws_bytes, fws_bytes;
   int64_t e_off, c_off;  // byte offsets of the per-step vectors
+  int64_t p_off;         // byte offset of the backward prep records (or 0)
 };
 
 int check_shape(const gdr_shape* s, Sizes* z) {
@@ -62,6 +63,19 @@ int check_shape(const gdr_shape* s, Sizes* z) {
   if (r.e_off > kMaxIndex - b2) return GDR_ERR_OVERFLOW;
   r.ckpt_bytes = r.e_off + b2;
   r.ws_bytes = r.c_off + b2;
+  r.fws_bytes = 0;
+  r.p_off = 0;
+  if (gdr::chunked_sweep_ok(s->Hk, s->Hv, s->Dk, s->Dv, s->chunk, s->T)) {
+    // the chunked sweeps' prep records: the forward's whole workspace, and
+    // a region after the backward's per-step vectors
+    int64_t f;
+    if (!mul_ok(gdr::chunked_prep_floats(1, 1, r.nch), bh, &f) ||
+        !mul_ok(f, 4, &r.fws_bytes))
+      return GDR_ERR_OVERFLOW;
+    r.p_off = round_up256(r.ws_bytes);
+    if (r.p_off > kMaxIndex - r.fws_bytes) return GDR_ERR_OVERFLOW;
+    r.ws_bytes = r.p_off + r.fws_bytes;
+  }
   // element counts must also index as int64 inside the kernels
   int64_t qk;
   if (!mul_ok(s->B, s->T, &qk) || !mul_ok(qk, s->Hk, &qk) ||
@@ -97,6 +111,15 @@ int gdr_checkpoint_bytes(const gdr_shape* shape, size_t* out) {
   return GDR_OK;
 }
 
+int gdr_forward_workspace_bytes(const gdr_shape* shape, size_t* out) {
+  Sizes z;
+  const int st = check_shape(shape, &z);
+  if (st != GDR_OK) return st;
+  if (out == nullptr) return GDR_ERR_NULL_ARG;
+  *out = static_cast<size_t>(z.fws_bytes);
+  return GDR_OK;
+}
+
 int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out) {
   Sizes z;
   const int st = check_shape(shape, &z);
@@ -109,7 +132,7 @@ int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out) {
 int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
                 const void* v, const void* g, const void* beta,
                 const float* S0, void* y, float* S_T, void* ckpt,
-                void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream) {
   Sizes z;
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
@@ -117,9 +140,12 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
   const bool has_state = shape->B > 0;
   if (has_tokens && (!q || !k || !v || !g || !beta || !y))
     return GDR_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, g, beta, S0, y, S_T, ckpt};
+  const void* ptrs[] = {q, k, v, g, beta, S0, y, S_T, ckpt, workspace};
   for (const void* p : ptrs)
     if (p != nullptr && !aligned16(p)) return GDR_ERR_ALIGNMENT;
+  if (has_tokens && z.fws_bytes > 0 &&
+      (workspace == nullptr || workspace_bytes < static_cast<size_t>(z.fws_bytes)))
+    return GDR_ERR_WORKSPACE;
   if (!has_state) return GDR_OK;
 
   gdr::FwdSweepArgs a{};
@@ -144,8 +170,17 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
     a.E = reinterpret_cast<float*>(static_cast<char*>(ckpt) + z.e_off);
   }
   if (!has_tokens && S_T == nullptr) return GDR_OK;
-  const hipError_t err = gdr::launch_fwd_sweep(
-      a, shape->dtype == GDR_BF16, static_cast<hipStream_t>(stream));
+  const bool bf16 = shape->dtype == GDR_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (has_tokens && z.fws_bytes > 0) {
+    gdr::FwdChunkedArgs c{};
+    c.s = a;
+    c.prep = static_cast<float*>(workspace);
+    err = gdr::launch_fwd_chunked(c, bf16, s);
+  } else {
+    err = gdr::launch_fwd_sweep(a, bf16, s);
+  }
   return err == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
@@ -194,7 +229,15 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
     b.Hck = static_cast<float*>(workspace);
     b.C = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.c_off);
   }
-  hipError_t err = gdr::launch_bwd_sweep(b, bf16, s);
+  hipError_t err;
+  if (has_tokens && z.p_off > 0) {
+    gdr::BwdChunkedArgs c{};
+    c.s = b;
+    c.prep = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.p_off);
+    err = gdr::launch_bwd_chunked(c, bf16, s);
+  } else {
+    err = gdr::launch_bwd_sweep(b, bf16, s);
+  }
   if (err != hipSuccess) return GDR_ERR_HIP;
   if (!has_tokens) return GDR_OK;
 
@@ -235,14 +278,14 @@ const char* gdr_strerror(int status) {
     case GDR_ERR_BAD_CHUNK: return "chunk must be in [1, 64]";
     case GDR_ERR_BAD_DTYPE: return "dtype must be GDR_F32 or GDR_BF16";
     case GDR_ERR_OVERFLOW: return "a tensor size overflows 64-bit indexing";
-    case GDR_ERR_WORKSPACE: return "workspace is smaller than gdr_backward_workspace_bytes";
+    case GDR_ERR_WORKSPACE: return "workspace is smaller than the size query returns";
     case GDR_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case GDR_ERR_HIP: return "the HIP runtime rejected a kernel launch";
   }
   return "unknown gdr status";
 }
 
-const char* gdr_version(void) { return "0.1.0"; }
+const char* gdr_version(void) { return "0.2.0"; }
 
 }  // extern "C"
 

@@ -43,39 +43,11 @@
 namespace gdr {
 namespace {
 
-typedef float f4 __attribute__((ext_vector_type(4)));
-
 constexpr int kThreads = 256;
 constexpr int kN = 64;       // max chunk length
 constexpr int kNP = kN + 1;  // padded row stride of [kN][kN] LDS matrices
 constexpr int kKB = 32;      // Dv rows per staged block of the Dv pass
 constexpr int kSB = 16;      // chunk steps per staged block of the final products
-
-__device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-// DPP move with 1.0 in the lanes that get no source (the product identity).
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_or1(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, 1.f),
-                                         __builtin_bit_cast(int, x), CTRL, ROWS,
-                                         0xF, false));
-}
-
-// Inclusive product over lanes 0..l of a wave: a Hillis-Steele scan with
-// row_shr inside each 16-lane row, then row_bcast:15 and row_bcast:31 across
-// rows.  Only products of the inputs are formed (no division).
-__device__ __forceinline__ float wave_prefix_product(float x) {
-  x *= dpp_or1<0x111, 0xF>(x);  // row_shr:1
-  x *= dpp_or1<0x112, 0xF>(x);  // row_shr:2
-  x *= dpp_or1<0x114, 0xF>(x);  // row_shr:4
-  x *= dpp_or1<0x118, 0xF>(x);  // row_shr:8
-  x *= dpp_or1<0x142, 0xA>(x);  // row_bcast:15 into rows 1 and 3
-  x *= dpp_or1<0x143, 0xC>(x);  // row_bcast:31 into rows 2 and 3
-  return x;
-}
 
 template <int JT>
 struct CL {  // LDS layout, offsets in floats
@@ -145,60 +117,6 @@ __device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
   }
   return r;
 }
-
-// Four consecutive elements p[o .. o+3] held as the raw loaded bits, so that
-// issuing the load does not wait for it: the validity mask depends on the
-// indices only, and zeroing and bf16 widening happen in get(), where the
-// block is consumed.  VEC as in ld4.
-template <typename T, bool VEC>
-struct Quad;
-
-template <>
-struct Quad<float, true> {
-  float4 v;
-  __device__ __forceinline__ void load(const float* __restrict__ p, int64_t o, bool ok, int) {
-    v = *reinterpret_cast<const float4*>(p + (ok ? o : 0));
-  }
-  __device__ __forceinline__ static uint32_t mask(bool ok, int) { return ok ? 15u : 0u; }
-  __device__ __forceinline__ f4 get(uint32_t m) const {
-    return m ? f4{v.x, v.y, v.z, v.w} : f4{0.f, 0.f, 0.f, 0.f};
-  }
-};
-
-template <>
-struct Quad<bf16, true> {
-  uint2 v;
-  __device__ __forceinline__ void load(const bf16* __restrict__ p, int64_t o, bool ok, int) {
-    v = *reinterpret_cast<const uint2*>(p + (ok ? o : 0));
-  }
-  __device__ __forceinline__ static uint32_t mask(bool ok, int) { return ok ? 15u : 0u; }
-  __device__ __forceinline__ f4 get(uint32_t m) const {
-    const f4 r = {__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-    return m ? r : f4{0.f, 0.f, 0.f, 0.f};
-  }
-};
-
-template <typename T>
-struct Quad<T, false> {
-  T v[4];
-  __device__ __forceinline__ void load(const T* __restrict__ p, int64_t o, bool ok, int lim) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) v[x] = p[(ok && x < lim) ? o + x : 0];
-  }
-  __device__ __forceinline__ static uint32_t mask(bool ok, int lim) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) m |= (uint32_t)(ok && x < lim) << x;
-    return m;
-  }
-  __device__ __forceinline__ f4 get(uint32_t m) const {
-    f4 r;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) r[x] = ((m >> x) & 1) ? to_f32(v[x]) : 0.f;
-    return r;
-  }
-};
 
 template <typename TIn, int JT, bool VEC>
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {

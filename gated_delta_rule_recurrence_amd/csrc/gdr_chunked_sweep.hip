@@ -1,0 +1,834 @@
+// Chunked sweeps of the gated delta rule on gfx950 (fp32 MFMA): the forward
+// state recurrence and the reverse recurrence of its state gradient.
+//
+// Notation: a chunk has n <= 64 steps, local t = 0..n-1, and Gam(a,b] is the
+// product of g over the steps a+1..b.  It is always formed as a running
+// product and never by division.  Unrolling the recurrence of mlx issue #4614
+// (the recurrence statement under the accuracy table) over one chunk gives:
+//
+// Forward, with S0 the state before the chunk:
+//   e_t   = v_t - Gam(-1,t] S0 k_t - sum_{r<t} Gam(r,t] (k_t . k_r) beta_r e_r
+//   y_t   = Gam(-1,t] S0 q_t + sum_{r<=t} Gam(r,t] (q_t . k_r) beta_r e_r
+//   S_end = Gam(-1,n-1] S0 + sum_r beta_r Gam(r,n-1] e_r k_r^T
+// For the rows of one value head, with E = [e_t] and U = V - diag(gam) K S0^T:
+//   (I + A) E = U,            A[t][r] = Gam(r,t] (k_t . k_r) beta_r  (r < t)
+//   Y = diag(gam) Q S0^T + M E,  M[t][r] = Gam(r,t] (q_t . k_r) beta_r (r <= t)
+//   S_end = gend S0 + E^T diag(ks) K,  gam_t = Gam(-1,t], ks_r = beta_r Gam(r,n-1].
+//
+// Reverse, with H the gradient of the loss with respect to the state after
+// step t.  The per-step form is
+//   G_t = H_t + dy_t q_t^T,  c_t = G_t k_t,  H_{t-1} = g_t (G_t - beta_t c_t k_t^T).
+// With Hend the gradient after the chunk:
+//   c_t = Gam(t,n-1] Hend k_t + sum_{s>=t} Gam(t,s] (q_s . k_t) dy_s
+//         - sum_{s>t} Gam(t,s] beta_s (k_s . k_t) c_s
+//   H_start = Gam(-1,n-1] Hend + sum_s Gam(-1,s] (dy_s q_s^T - beta_s c_s k_s^T)
+// For C = [c_t]:
+//   (I + Bm) C = diag(suf) K Hend^T + Mq DY,
+//     Bm[t][s] = Gam(t,s] beta_s (k_s . k_t)  (s > t),
+//     Mq[t][s] = Gam(t,s] (q_s . k_t)  (s >= t),
+//     suf_t = Gam(t,n-1],
+//   H_start = pre_{n-1} Hend + DY^T diag(pre) Q - C^T diag(beta pre) K,  pre_s = Gam(-1,s].
+//
+// A prep kernel forms, once per (batch row, value head, chunk), the two
+// Gram matrices and Gam, and from them:
+//   * forward: T = (I + A)^-1 (column-wise forward substitution) and M;
+//   * reverse: Tb = (I + Bm)^-1 (column-wise back substitution) and Mq.
+// Each substitution forms the same sums as the sequential recurrence.  The
+// sweep kernels then run a value head's chunks in order (reverse order for
+// the gradient), 32 state rows per workgroup.  Rows are independent.  Every
+// product runs on fp32 MFMA.
+//
+// Outputs match the sequential sweeps:
+//   * forward: y, S_T, the state checkpoint at every chunk start, and the
+//     residuals e_t;
+//   * reverse: dv, c_t, the gradient at every chunk end, and dS0.
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+namespace {
+
+constexpr int kThreads = 256;    // prep workgroup
+constexpr int kSwThreads = 512;  // sweep workgroup: eight waves, two per SIMD
+constexpr int kN = 64;
+constexpr int kNP = kN + 1;
+constexpr int kDS = 32;       // state rows per sweep workgroup
+constexpr int kUBS = 36;      // row stride of the [kN][kDS] step-by-row stages
+constexpr int kMaxJT = 12;    // Dk <= 192 (LDS of the sweep kernels)
+
+// The products over the steps of a chunk (E = T U, Y = M E, C = Tb U,
+// U += Mq DY and the state updates) use step rstep(ks, lq) as the k index
+// of MFMA k-step ks in lane quarter lq.  That step is
+// 16 (ks / 4) + 4 lq + ks % 4, which keeps the LDS reads of those products
+// free of bank conflicts.
+__device__ __forceinline__ int rstep(int ks, int lq) {
+  return 16 * (ks >> 2) + 4 * lq + (ks & 3);
+}
+
+// Prep record layouts (floats; the stride is kChunkPrepStride).
+// Forward record:
+constexpr int kPrT = 0, kPrM = 4096, kPrGam = 8192, kPrKs = 8256, kPrGend = 8320;
+// Reverse record:
+constexpr int kPbT = 0, kPbM = 4096, kPbSuf = 8192, kPbPre = 8256, kPbBeta = 8320;
+static_assert(kPbBeta + kN <= kChunkPrepStride, "record");
+
+// Element (t, r) of a [64][64] matrix in MFMA A-fragment order: k-step
+// 16 (t / 16) + ks with rstep(ks, lq) = r, lane (t % 16) + 16 lq.
+__device__ __forceinline__ int frag_index(int t, int r) {
+  return ((t >> 4) * 16 + 4 * (r >> 4) + (r & 3)) * 64 + (t & 15) + 16 * ((r >> 2) & 3);
+}
+
+// ---------------------------------------------------------------- prep ----
+// grid (nch, Hk, B); wave w handles value heads w, w + 4, ... of the kv head.
+struct PL {
+  static constexpr int QS = 0, KS = 64 * kN;          // q, k stage [16][kN][4]
+  static constexpr int GW = 0;                         // 4 x [kN][kNP] (alias)
+  static constexpr int VB = 4 * kN * kNP;              // 4 x beta[kN]
+  static constexpr int VS = VB + 4 * kN;               // 4 x suf[kN]
+  static constexpr int QK = VS + 4 * kN, KK = QK + kN * kNP;
+  static constexpr int SIZE = KK + kN * kNP;
+  static_assert(2 * 64 * kN <= VB, "stage fits the per-wave arrays");
+  static_assert(SIZE * 4 <= 160 * 1024, "LDS");
+};
+
+template <typename TIn, bool BWD>
+__global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
+                                                           float* __restrict__ prep) {
+  using L = PL;
+  extern __shared__ __align__(16) float sm[];
+  const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ g = static_cast<const TIn*>(a.g);
+  const TIn* __restrict__ beta = static_cast<const TIn*>(a.beta);
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk;
+  const int jc = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+  const int rep = Hv / Hk;
+  const int t0 = jc * a.L;
+  const int n = min(a.L, T - t0);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  const int tw = 16 * w;
+
+  // ---- QK[t][r] = q_t . k_r, KK[t][r] = k_t . k_r (MFMA over Dk) ----------
+  {
+    f4 acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < Dk; j0 += 64) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qi = tid + kThreads * u;
+        const int s = qi >> 4, jq = qi & 15, j = j0 + 4 * jq;
+        f4 rq, rk;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const bool ok = s < n && j + x < Dk;
+          const int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j + x : 0;
+          rq[x] = ok ? ld(q, o) : 0.f;
+          rk[x] = ok ? ld(k, o) : 0.f;
+        }
+        *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq;
+        *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk;
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int ks = 0; ks < 16; ++ks) {
+        const int fw = ((ks * kN + tw + lr) << 2) + lq;
+        const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
+          acc[tb] = mfma(aq, bk, acc[tb]);
+          acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sm[L::QK + o] = acc[tb][v];
+        sm[L::KK + o] = acc[4 + tb][v];
+      }
+    __syncthreads();
+  }
+
+  // ---- per value head (one wave each; no barriers below) ------------------
+  float* G = sm + L::GW + w * kN * kNP;  // Gam(r,t] above the diagonal
+  float* vb = sm + L::VB + w * kN;
+  float* vs = sm + L::VS + w * kN;
+  for (int hh = w; hh < rep; hh += 4) {
+    const int h = hk * rep + hh;
+    float* __restrict__ rec = prep + (((int64_t)b * Hv + h) * a.nch + jc) * kChunkPrepStride;
+    // every index stays inside the tensors, also where the value is unused
+    const int64_t gi = ((int64_t)b * T + t0 + (l < n ? l : 0)) * Hv + h;
+    const float gl = l < n ? ld(g, gi) : 1.f;
+    const float bl = l < n ? ld(beta, gi) : 0.f;
+    vb[l] = bl;
+    // rows of Gam(r,t] (lane l <-> t = l)
+    for (int r = 0; r < kN; ++r) {
+      const float y = wave_prefix_product(l > r ? gl : 1.f);
+      G[r * kNP + l] = l == r ? 1.f : (l > r ? y : 0.f);
+    }
+    const float pre = wave_prefix_product(gl);  // Gam(-1, l]
+    {  // suf[t] = Gam(t, n-1]: lane l <-> t = n-1-l
+      const bool sok = l >= 1 && l < n;
+      const float gs = sok ? ld(g, ((int64_t)b * T + t0 + (sok ? n - l : 0)) * Hv + h) : 1.f;
+      const float sf = wave_prefix_product(gs);
+      if (l < n) vs[n - 1 - l] = sf;
+    }
+    float x[kN];
+    if constexpr (!BWD) {
+      // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
+      for (int t = 1; t < kN; ++t)
+        if (l < t) G[t * kNP + l] = G[l * kNP + t] * sm[L::KK + t * kNP + l] * bl;
+      // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
+#pragma unroll 1
+      for (int wt = 0; wt < 4; ++wt)
+#pragma unroll 4
+        for (int ks = 0; ks < 16; ++ks) {
+          const int t = 16 * wt + lr, s = rstep(ks, lq);
+          const float m = s <= t ? G[s * kNP + t] * sm[L::QK + t * kNP + s] * vb[s] : 0.f;
+          rec[kPrM + (wt * 16 + ks) * 64 + l] = m;
+        }
+      // T = (I + A)^-1, column l by forward substitution:
+      //   x_t = [t == l] - sum_{r<t} A[t][r] x_r
+#pragma unroll
+      for (int t = 0; t < kN; ++t) {
+        float acc = t == l ? 1.f : 0.f;
+#pragma unroll
+        for (int r = 0; r < t; ++r) acc = fmaf(-G[t * kNP + r], x[r], acc);
+        x[t] = acc;
+      }
+#pragma unroll
+      for (int t = 0; t < kN; ++t) rec[kPrT + frag_index(t, l)] = x[t];
+      rec[kPrGam + l] = pre;
+      rec[kPrKs + l] = l < n ? bl * vs[l] : 0.f;
+      if (l == n - 1) rec[kPrGend] = pre;
+    } else {
+      // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
+#pragma unroll 1
+      for (int wt = 0; wt < 4; ++wt)
+#pragma unroll 4
+        for (int ks = 0; ks < 16; ++ks) {
+          const int t = 16 * wt + lr, s = rstep(ks, lq);
+          const float m = s >= t ? G[t * kNP + s] * sm[L::QK + s * kNP + t] : 0.f;
+          rec[kPbM + (wt * 16 + ks) * 64 + l] = m;
+        }
+      // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, kept transposed below the
+      // diagonal: G[s][t] (lane l <-> t)
+      for (int s = 1; s < kN; ++s)
+        if (l < s) G[s * kNP + l] = G[l * kNP + s] * sm[L::KK + s * kNP + l] * vb[s];
+      // Tb = (I + Bm)^-1, column l by back substitution:
+      //   x_t = [t == l] - sum_{r>t} Bm[t][r] x_r
+#pragma unroll
+      for (int t = kN - 1; t >= 0; --t) {
+        float acc = t == l ? 1.f : 0.f;
+#pragma unroll
+        for (int r = t + 1; r < kN; ++r) acc = fmaf(-G[r * kNP + t], x[r], acc);
+        x[t] = acc;
+      }
+#pragma unroll
+      for (int t = 0; t < kN; ++t) rec[kPbT + frag_index(t, l)] = x[t];
+      rec[kPbSuf + l] = l < n ? vs[l] : 0.f;
+      rec[kPbPre + l] = pre;
+      rec[kPbBeta + l] = bl;
+    }
+  }
+}
+
+// --------------------------------------------------------------- sweeps ---
+// grid (ceil(Dv / 32), Hv, B): state rows i0 .. i0 + 31 of one value head,
+// eight waves (two per SIMD).  In a chunk, wave w owns one 16 x 16 tile
+// (steps 16 (w % 4) .., rows 16 (w / 4) ..) of the step-by-row products, and
+// the state tiles (rows 16 (w % 2) .., Dk columns 16 (JW (w / 2) + nj) ..)
+// of the state update.
+
+// The k, q rows of a chunk: fetched into registers a chunk ahead (raw bits,
+// masked where deposited), then deposited into the natural-layout LDS stages
+// [kN][KLD] with zero padding columns.
+template <typename TIn, int JT, bool VEC>
+struct KQPrefetch {
+  static constexpr int DKP = 16 * JT, KLD = DKP + 4;
+  static constexpr int NQT = kN * DKP / 4;  // 4-column quads of one chunk
+  static constexpr int NQ = NQT / kSwThreads;
+  static_assert(NQT % kSwThreads == 0 && 4 * NQ <= 32, "quads per thread");
+  uint32_t pm = 0;
+  Quad<TIn, VEC> pk[NQ], pq[NQ];
+  int tid;
+
+  // quad u of this thread: step qt(u), columns qj(u) .. qj(u) + 3 (recomputed
+  // where used rather than held in registers)
+  __device__ __forceinline__ int qt(int u) const { return (tid + kSwThreads * u) / (DKP / 4); }
+  __device__ __forceinline__ int qj(int u) const {
+    return 4 * ((tid + kSwThreads * u) % (DKP / 4));
+  }
+  __device__ __forceinline__ void init(int t) { tid = t; }
+  // rows t0 .. t0 + n - 1; base = element (t0, kv head, 0); kst = row stride
+  __device__ __forceinline__ void fetch(const TIn* __restrict__ k, const TIn* __restrict__ q,
+                                        int64_t base, int n, int kst, int Dk) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int t = qt(u), j = qj(u);
+      const bool ok = j < Dk && t < n;
+      const int o = ok ? t * kst + j : 0;
+      pk[u].load(k + base, o, ok, Dk - j);
+      pq[u].load(q + base, o, ok, Dk - j);
+      m |= Quad<TIn, VEC>::mask(ok, Dk - j) << (4 * u);
+    }
+    pm = m;
+  }
+  __device__ __forceinline__ void deposit(float* kl, float* ql) const {
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const uint32_t mu = (pm >> (4 * u)) & 15u;
+      const int o = qt(u) * KLD + qj(u);
+      *reinterpret_cast<f4*>(kl + o) = pk[u].get(mu);
+      *reinterpret_cast<f4*>(ql + o) = pq[u].get(mu);
+    }
+  }
+};
+
+template <int JT>
+struct SL {
+  static constexpr int DKP = 16 * JT;
+  static constexpr int KLD = DKP + 4;
+  static constexpr int KL = 0, QL = kN * KLD;   // k, q stages [kN][KLD]
+  static constexpr int SK = 2 * kN * KLD;       // state k-interleaved [DKP/4][kDS][4]
+  static constexpr int B0 = SK + kDS * DKP;     // three [kN][kUBS] stages
+  static constexpr int B1 = B0 + kN * kUBS;
+  static constexpr int B2 = B1 + kN * kUBS;
+  static constexpr int SIZE = B2 + kN * kUBS;
+  static_assert(SIZE * 4 <= 160 * 1024, "LDS");
+};
+
+// P[16 steps of tile tw][16 rows of slice 16 nt] = [K or Q rows] State^T:
+// k-steps over Dk in groups of G, the LDS operands of a group read while
+// the products of the previous group issue (two register slots; the
+// scheduling barriers keep that order).  NACC accumulators per product
+// alternate over the groups.
+template <int DKP, int KLD, int G, int NM, int NACC>
+__device__ __forceinline__ void state_products(const float* const (&ap)[NM], const float* sp,
+                                               f4 (&acc)[NM][NACC]) {
+  constexpr int NG = DKP / 4 / G;
+  static_assert(NG % NACC == 0, "groups per accumulator");
+  float av[2][NM][G], bs[2][G];
+  auto rd = [&](int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < G; ++x) {
+#pragma unroll
+      for (int m = 0; m < NM; ++m) av[g & 1][m][x] = ap[m][4 * (G * g + x)];
+      bs[g & 1][x] = sp[(G * g + x) * kDS * 4];
+    }
+  };
+  rd(0);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    if (g + 1 < NG) rd(g + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < G; ++x)
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        acc[m][g % NACC] = mfma(av[g & 1][m][x], bs[g & 1][x], acc[m][g % NACC]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Sacc[nj] += sum over the 64 steps of A[i][t] B[t][j] for the state tiles
+// of a wave: A[i][t] = ab[t kUBS + i] (a [kN][kUBS] stage, i = 16 mt + lr),
+// B[t][j] = bb[t KLD + j] (a [kN][KLD] stage, j = 16 (jg + nj) + lr).
+// Steps rstep(ks, lq) in groups of four, read a group ahead.
+template <int JW, int KLD>
+__device__ __forceinline__ void update_products(const float* ab, const float* bb, int lq,
+                                                f4 (&Sacc)[JW]) {
+  const float* ep = ab + 4 * lq * kUBS;
+  const float* kb = bb + 4 * lq * KLD;
+  float ae[2][4], bk[2][4][JW];
+  auto rd = [&](int g) __attribute__((always_inline)) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      ae[g & 1][x] = ep[(16 * g + x) * kUBS];
+#pragma unroll
+      for (int nj = 0; nj < JW; ++nj) bk[g & 1][x][nj] = kb[(16 * g + x) * KLD + 16 * nj];
+    }
+  };
+  rd(0);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    if (g + 1 < 4) rd(g + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int nj = 0; nj < JW; ++nj) Sacc[nj] = mfma(ae[g & 1][x], bk[g & 1][x][nj], Sacc[nj]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// The state tiles of a wave (tile nj, register u <-> row 16 mt + 4 lq + u,
+// column 16 (jg + nj) + lr) into the k-interleaved LDS copy [DKP/4][kDS][4]:
+// element (i, j) at ((j / 4) kDS + i) 4 + j % 4.
+template <int JW>
+__device__ __forceinline__ void tiles_to_lds(float* sk, const f4 (&acc)[JW], int mt, int jg,
+                                             int lq, int lr) {
+  float* p = sk + ((4 * jg + (lr >> 2)) * kDS + 16 * mt + 4 * lq) * 4 + (lr & 3);
+#pragma unroll
+  for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[(4 * nj * kDS + u) * 4] = acc[nj][u];
+}
+
+// The slice in the LDS copy to rows i0 .. i0 + 31 of a [Dv][Dk] matrix in
+// HBM, a 4-column group per thread and pass (one 16-byte store where Dk % 4
+// == 0); rows vary fastest across the lanes, which keeps the LDS reads
+// conflict-free.
+template <int JT, bool VEC>
+__device__ __forceinline__ void lds_to_matrix(const float* sk, float* __restrict__ dst, int i0,
+                                              int Dv, int Dk, int tid) {
+  constexpr int NQ4 = kDS * 4 * JT;  // 4-column groups of the slice
+  static_assert(NQ4 % kSwThreads == 0, "passes");
+#pragma unroll
+  for (int x = 0; x < NQ4 / kSwThreads; ++x) {
+    const int e = tid + kSwThreads * x;
+    const int i = e % kDS, j = 4 * (e / kDS);
+    if (i0 + i >= Dv || j >= Dk) continue;
+    const f4 val = *reinterpret_cast<const f4*>(sk + (e / kDS * kDS + i) * 4);
+    float* o = dst + (int64_t)(i0 + i) * Dk + j;
+    if (VEC) {
+      *reinterpret_cast<f4*>(o) = val;
+    } else {
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        if (j + y < Dk) o[y] = val[y];
+    }
+  }
+}
+
+// ------------------------------------------------------- forward sweep ----
+template <typename TIn, int JT, bool VEC>
+__global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedArgs A) {
+  using L = SL<JT>;
+  constexpr int DKP = L::DKP, KLD = L::KLD;
+  constexpr int JW = JT / 4;  // Dk tiles per wave in the state update
+  static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
+  constexpr int UB = L::B0, EB = L::B1, ES = L::B2;  // U, E, diag(ks) E
+  extern __shared__ __align__(16) float sm[];
+  const FwdSweepArgs& a = A.s;
+  const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ v = static_cast<const TIn*>(a.v);
+  TIn* __restrict__ y = static_cast<TIn*>(a.y);
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
+  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  const int tb = w & 3, nt = w >> 2;         // step-by-row tile
+  const int mt = w & 1, jg = JW * (w >> 1);  // state update tiles
+  const int tw = 16 * tb;
+  const int64_t bh = (int64_t)b * Hv + h;
+  const int64_t mat = (int64_t)Dv * Dk;
+  // step strides of k, q and of v, y (the host bounds 64 steps of either to
+  // fit an int)
+  const int kst = Hk * Dk, vst = Hv * Dv;
+  auto kq_base = [&](int c) { return ((int64_t)b * T + c * a.L) * kst + (int64_t)hk * Dk; };
+
+  KQPrefetch<TIn, JT, VEC> kq;
+  kq.init(tid);
+
+  // state tiles in the accumulator layout of the update: tile nj, register u
+  // <-> row i = 16 mt + 4 lq + u, column j = 16 (jg + nj) + lr
+  f4 Sacc[JW];
+#pragma unroll
+  for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+      const bool ok = a.S0 != nullptr && i0 + i < Dv && j < Dk;
+      Sacc[nj][u] = ok ? a.S0[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
+    }
+  tiles_to_lds<JW>(sm + L::SK, Sacc, mt, jg, lq, lr);
+  kq.fetch(k, q, kq_base(0), min(a.L, T), kst, Dk);
+
+  // v, y of this wave's tile: step tw + 4 lq + u, row i0 + 16 nt + lr
+  for (int c = 0; c < a.nch; ++c) {
+    // lane indices re-derived in each chunk from an opaque copy of the
+    // thread id: the compiler then recomputes the cheap per-lane addresses
+    // instead of holding dozens of them in registers across the loop
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    kq.tid = tl;
+    const int l = tl & 63, lr = l & 15, lq = l >> 4;
+    const int ti = 16 * nt + lr;
+    const bool iok = i0 + ti < Dv;
+    const int t0 = c * a.L;
+    const int n = min(a.L, T - t0);
+    const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
+    const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
+    kq.deposit(sm + L::KL, sm + L::QL);
+    // this chunk's operands, issued before the next chunk's k, q so that
+    // waiting for them never waits for those; held as loaded, masked at use
+    float tf[16], mf[16], gam[4], ksc[4];
+    TIn vr[4];
+    uint32_t vm = 0;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) tf[ks] = rec[kPrT + (tb * 16 + ks) * 64 + l];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      gam[u] = rec[kPrGam + tw + 4 * lq + u];
+      ksc[u] = rec[kPrKs + tw + 4 * lq + u];
+    }
+    const float gend = rec[kPrGend];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      const bool ok = iok && t < n;
+      vr[u] = v[vbase + (ok ? t * vst + ti : 0)];
+      vm |= (uint32_t)ok << u;
+    }
+    {  // unconditional (a branch around loads makes every later wait a full one)
+      const int cn = min(c + 1, a.nch - 1);
+      kq.fetch(k, q, kq_base(cn), min(a.L, T - cn * a.L), kst, Dk);
+    }
+    __syncthreads();
+    // checkpoint S_{c C}: the state before this chunk, from its LDS copy
+    if (a.Sck != nullptr)
+      lds_to_matrix<JT, VEC>(sm + L::SK, a.Sck + (bh * a.nch + c) * mat, i0, Dv, Dk, tid);
+
+    // X = [K; Q] S0^T on this wave's tile
+    f4 X[2][1];
+    X[0][0] = X[1][0] = f4{0.f, 0.f, 0.f, 0.f};
+    {
+      // (fp32 k, q prefetch registers leave room for groups of two)
+      constexpr int G = sizeof(TIn) == 2 && VEC ? 4 : 2;
+      const float* const ap[2] = {sm + L::KL + (tw + lr) * KLD + lq,
+                                  sm + L::QL + (tw + lr) * KLD + lq};
+      state_products<DKP, KLD, G, 2, 1>(ap, sm + L::SK + ((16 * nt + lr) << 2) + lq, X);
+    }
+    // M is first used after two more barriers; loading it here keeps its
+    // registers free during the state products
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) mf[ks] = rec[kPrM + (tb * 16 + ks) * 64 + l];
+    // U = V - diag(gam) X_K
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float vu = ((vm >> u) & 1) ? to_f32(vr[u]) : 0.f;
+      sm[UB + (tw + 4 * lq + u) * kUBS + ti] = vu - gam[u] * X[0][0][u];
+    }
+    __syncthreads();
+
+    // E = T U
+    f4 E = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[UB + rstep(ks, lq) * kUBS + ti], E);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      sm[EB + t * kUBS + ti] = E[u];
+      sm[ES + t * kUBS + ti] = ksc[u] * E[u];
+      if (a.E != nullptr && iok && t < n) a.E[vbase + t * vst + ti] = E[u];
+    }
+    __syncthreads();
+
+    // Y = diag(gam) X_Q + M E
+    {
+      f4 Yv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Yv[u] = gam[u] * X[1][0][u];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) Yv = mfma(mf[ks], sm[EB + rstep(ks, lq) * kUBS + ti], Yv);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        if (iok && t < n) st(y, vbase + t * vst + ti, Yv[u]);
+      }
+    }
+
+    // S_end = gend S0 + E^T diag(ks) K
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj) Sacc[nj] *= gend;
+    update_products<JW, KLD>(sm + ES + 16 * mt + lr, sm + L::KL + 16 * jg + lr, lq, Sacc);
+    __syncthreads();  // stage reads done before it is rewritten
+    tiles_to_lds<JW>(sm + L::SK, Sacc, mt, jg, lq, lr);
+  }
+  if (a.ST != nullptr) {
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        if (i0 + i < Dv && j < Dk) a.ST[bh * mat + (int64_t)(i0 + i) * Dk + j] = Sacc[nj][u];
+      }
+  }
+}
+
+// ------------------------------------------------------- reverse sweep ----
+template <typename TIn, int JT, bool VEC>
+__global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_kernel(BwdChunkedArgs A) {
+  using L = SL<JT>;
+  constexpr int DKP = L::DKP, KLD = L::KLD;
+  constexpr int JW = JT / 4;
+  static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
+  // dy, then -diag(beta pre) C (dy is dead once U is formed); U; diag(pre) dy
+  constexpr int DB = L::B0, UB = L::B1, DP = L::B2;
+  extern __shared__ __align__(16) float sm[];
+  const BwdSweepArgs& a = A.s;
+  const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
+  const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
+  const TIn* __restrict__ dy = static_cast<const TIn*>(a.dy);
+  TIn* __restrict__ dv = static_cast<TIn*>(a.dv);
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
+  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  const int tb = w & 3, nt = w >> 2;
+  const int mt = w & 1, jg = JW * (w >> 1);
+  const int tw = 16 * tb;
+  const int64_t bh = (int64_t)b * Hv + h;
+  const int64_t mat = (int64_t)Dv * Dk;
+  const int kst = Hk * Dk, vst = Hv * Dv;
+  auto kq_base = [&](int c) { return ((int64_t)b * T + c * a.L) * kst + (int64_t)hk * Dk; };
+  auto v_base = [&](int c) { return ((int64_t)b * T + c * a.L) * vst + (int64_t)h * Dv + i0; };
+
+  KQPrefetch<TIn, JT, VEC> kq;
+  kq.init(tid);
+  // dy of this wave's tile (step tw + 4 lq + u, row i0 + ti), a chunk ahead
+  TIn dr[4];
+  uint32_t dm = 0;
+  auto fetch_dy = [&](int c, int lq, int ti, bool iok) __attribute__((always_inline)) {
+    const int n = min(a.L, T - c * a.L);
+    const int64_t base = v_base(c);
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      const bool ok = iok && t < n;
+      dr[u] = dy[base + (ok ? t * vst + ti : 0)];
+      m |= (uint32_t)ok << u;
+    }
+    dm = m;
+  };
+
+  // gradient tiles, same layout as the forward state tiles
+  f4 Hacc[JW];
+#pragma unroll
+  for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+      const bool ok = a.dST != nullptr && i0 + i < Dv && j < Dk;
+      Hacc[nj][u] = ok ? a.dST[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
+    }
+  const int cl = a.nch - 1;
+  tiles_to_lds<JW>(sm + L::SK, Hacc, mt, jg, lq, lr);
+  kq.fetch(k, q, kq_base(cl), min(a.L, T - cl * a.L), kst, Dk);
+  fetch_dy(cl, lq, 16 * nt + lr, i0 + 16 * nt + lr < Dv);
+
+  for (int c = cl; c >= 0; --c) {
+    // lane indices re-derived in each chunk from an opaque copy of the
+    // thread id: the compiler then recomputes the cheap per-lane addresses
+    // instead of holding dozens of them in registers across the loop
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    kq.tid = tl;
+    const int l = tl & 63, lr = l & 15, lq = l >> 4;
+    const int ti = 16 * nt + lr;
+    const bool iok = i0 + ti < Dv;
+    const int t0 = c * a.L;
+    const int n = min(a.L, T - t0);
+    const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
+    const int64_t vbase = v_base(c);
+    kq.deposit(sm + L::KL, sm + L::QL);
+    float dyv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      dyv[u] = ((dm >> u) & 1) ? to_f32(dr[u]) : 0.f;
+      sm[DB + (tw + 4 * lq + u) * kUBS + ti] = dyv[u];
+    }
+    float tf[16], mf[16], suf[4], pre[4], bet[4];
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      tf[ks] = rec[kPbT + (tb * 16 + ks) * 64 + l];
+      mf[ks] = rec[kPbM + (tb * 16 + ks) * 64 + l];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      suf[u] = rec[kPbSuf + tw + 4 * lq + u];
+      pre[u] = rec[kPbPre + tw + 4 * lq + u];
+      bet[u] = rec[kPbBeta + tw + 4 * lq + u];
+    }
+    const float pend = rec[kPbPre + n - 1];
+    {
+      const int cn = max(c - 1, 0);
+      kq.fetch(k, q, kq_base(cn), min(a.L, T - cn * a.L), kst, Dk);
+      fetch_dy(cn, lq, ti, iok);
+    }
+    __syncthreads();
+    // slot c: the gradient after this chunk (dS_T for the last), from its LDS copy
+    lds_to_matrix<JT, VEC>(sm + L::SK, a.Hck + (bh * a.nch + c) * mat, i0, Dv, Dk, tid);
+
+    // X = K Hend^T on this wave's tile (two accumulators over the k-steps)
+    f4 X[1][2];
+    X[0][0] = X[0][1] = f4{0.f, 0.f, 0.f, 0.f};
+    {
+      constexpr int G = sizeof(TIn) == 2 && VEC ? 4 : 2;
+      const float* const ap[1] = {sm + L::KL + (tw + lr) * KLD + lq};
+      state_products<DKP, KLD, G, 1, 2>(ap, sm + L::SK + ((16 * nt + lr) << 2) + lq, X);
+    }
+    // U = diag(suf) X + Mq DY; the stage of diag(pre) DY for the update
+    {
+      f4 U;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) U[u] = suf[u] * (X[0][0][u] + X[0][1][u]);
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) U = mfma(mf[ks], sm[DB + rstep(ks, lq) * kUBS + ti], U);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        sm[UB + t * kUBS + ti] = U[u];
+        sm[DP + t * kUBS + ti] = pre[u] * dyv[u];
+      }
+    }
+    __syncthreads();
+
+    // C = Tb U; dv = diag(beta) C; the stage of -diag(beta pre) C
+    {
+      f4 Cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) Cv = mfma(tf[ks], sm[UB + rstep(ks, lq) * kUBS + ti], Cv);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        sm[DB + t * kUBS + ti] = -(bet[u] * pre[u]) * Cv[u];
+        if (iok && t < n) {
+          a.C[vbase + t * vst + ti] = Cv[u];
+          st(dv, vbase + t * vst + ti, bet[u] * Cv[u]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // H_start = pre_{n-1} Hend + DY^T diag(pre) Q - C^T diag(beta pre) K
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj) Hacc[nj] *= pend;
+    update_products<JW, KLD>(sm + DP + 16 * mt + lr, sm + L::QL + 16 * jg + lr, lq, Hacc);
+    update_products<JW, KLD>(sm + DB + 16 * mt + lr, sm + L::KL + 16 * jg + lr, lq, Hacc);
+    __syncthreads();  // stage reads done before it is rewritten
+    tiles_to_lds<JW>(sm + L::SK, Hacc, mt, jg, lq, lr);
+  }
+  if (a.dS0 != nullptr) {
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        if (i0 + i < Dv && j < Dk) a.dS0[bh * mat + (int64_t)(i0 + i) * Dk + j] = Hacc[nj][u];
+      }
+  }
+}
+
+// ------------------------------------------------------------ launches ----
+template <typename Kern, typename... Args>
+hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
+                  const Args&... args) {
+  (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+  hipLaunchKernelGGL(kern, grid, dim3(threads), lds, s, args...);
+  return hipGetLastError();
+}
+
+template <typename TIn, bool BWD>
+hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep, hipStream_t s) {
+  return launch(prep_kernel<TIn, BWD>, dim3(sh.nch, sh.Hk, sh.B), kThreads,
+                sizeof(float) * PL::SIZE, s, sh, prep);
+}
+
+template <typename TIn, bool BWD, typename Args>
+hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_t s) {
+  const dim3 grid((Dv + kDS - 1) / kDS, Hv, B);
+  const int jt = (Dk + 15) / 16;
+  const bool vec = Dk % 4 == 0;  // 4-element groups of a row start on a 4-element boundary
+  auto go = [&](auto jtc, auto vc) {
+    constexpr int JT = decltype(jtc)::value;
+    constexpr bool V = decltype(vc)::value;
+    const size_t lds = sizeof(float) * SL<JT>::SIZE;
+    if constexpr (BWD)
+      return launch(bwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
+    else
+      return launch(fwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
+  };
+  using I4 = std::integral_constant<int, 4>;
+  using I8 = std::integral_constant<int, 8>;
+  using I12 = std::integral_constant<int, 12>;
+  if (jt > kMaxJT) return hipErrorInvalidValue;
+  if (vec) {
+    if (jt <= 4) return go(I4{}, std::true_type{});
+    if (jt <= 8) return go(I8{}, std::true_type{});
+    return go(I12{}, std::true_type{});
+  }
+  if (jt <= 4) return go(I4{}, std::false_type{});
+  if (jt <= 8) return go(I8{}, std::false_type{});
+  return go(I12{}, std::false_type{});
+}
+
+template <typename Args>
+ChunkedSweepShape shape_of(const Args& a) {
+  ChunkedSweepShape sh{};
+  sh.B = a.B;
+  sh.T = a.T;
+  sh.Hk = a.Hk;
+  sh.Hv = a.Hv;
+  sh.Dk = a.Dk;
+  sh.L = a.L;
+  sh.nch = a.nch;
+  sh.q = a.q;
+  sh.k = a.k;
+  sh.g = a.g;
+  sh.beta = a.beta;
+  return sh;
+}
+
+template <typename TIn>
+hipError_t fwd_go(const FwdChunkedArgs& A, hipStream_t s) {
+  const hipError_t e = launch_prep<TIn, false>(shape_of(A.s), A.prep, s);
+  if (e != hipSuccess) return e;
+  return launch_sweep<TIn, false>(A, A.s.Dk, A.s.Dv, A.s.Hv, A.s.B, s);
+}
+
+template <typename TIn>
+hipError_t bwd_go(const BwdChunkedArgs& A, hipStream_t s) {
+  const hipError_t e = launch_prep<TIn, true>(shape_of(A.s), A.prep, s);
+  if (e != hipSuccess) return e;
+  return launch_sweep<TIn, true>(A, A.s.Dk, A.s.Dv, A.s.Hv, A.s.B, s);
+}
+
+}  // namespace
+
+bool chunked_sweep_ok(int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L, int64_t T) {
+  // the sweep kernels index 64 steps of k, q, v, y with int offsets
+  const int64_t lim = int64_t(1) << 31;
+  return Dk <= 16 * kMaxJT && L >= 16 && L <= kN && T >= L && kN * Hk * Dk < lim &&
+         kN * Hv * Dv < lim;
+}
+
+int64_t chunked_prep_floats(int64_t B, int64_t Hv, int64_t nch) {
+  return B * Hv * nch * kChunkPrepStride;
+}
+
+hipError_t launch_fwd_chunked(const FwdChunkedArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? fwd_go<gdr::bf16>(a, s) : fwd_go<float>(a, s);
+}
+
+hipError_t launch_bwd_chunked(const BwdChunkedArgs& a, bool bf16, hipStream_t s) {
+  return bf16 ? bwd_go<gdr::bf16>(a, s) : bwd_go<float>(a, s);
+}
+
+}  // namespace gdr

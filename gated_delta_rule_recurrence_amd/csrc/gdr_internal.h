@@ -54,6 +54,37 @@ struct ChunkArgs {
   void* dbeta;
 };
 
+// Chunked sweeps (per-chunk matrices on MFMA): the sequential sweeps'
+// arguments plus the per-(batch row, value head, chunk) records written by a
+// prep kernel.
+struct FwdChunkedArgs {
+  FwdSweepArgs s;
+  float* prep;  // [B][Hv][nch][kChunkPrepStride]
+};
+struct BwdChunkedArgs {
+  BwdSweepArgs s;
+  float* prep;  // [B][Hv][nch][kChunkPrepStride]
+};
+// What the prep kernels read.
+struct ChunkedSweepShape {
+  int B, T, Hk, Hv, Dk, L, nch;
+  const void* q;
+  const void* k;
+  const void* g;
+  const void* beta;
+};
+
+// Floats per prep record: two [64][64] matrices in MFMA A-fragment order
+// and three per-step vectors of 64.
+constexpr int kChunkPrepStride = 2 * 64 * 64 + 3 * 64;
+
+// Whether the chunked sweeps take this shape, and the floats of their prep
+// records.
+bool chunked_sweep_ok(int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L, int64_t T);
+int64_t chunked_prep_floats(int64_t B, int64_t Hv, int64_t nch);
+hipError_t launch_fwd_chunked(const FwdChunkedArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_bwd_chunked(const BwdChunkedArgs& a, bool bf16, hipStream_t s);
+
 hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s);
 

@@ -57,11 +57,11 @@ def _stream(device) -> int:
 
 
 def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
-                out_state=True, y=None, S_T=None, ckpt=None):
+                out_state=True, y=None, S_T=None, ckpt=None, workspace=None):
     """Forward pass.  Returns (y, S_T or None, Saved or None).
 
     q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g, beta [B,T,Hv]; S0 [B,Hv,Dv,Dk] fp32
-    or None.  Output buffers may be passed in to avoid allocation.
+    or None.  Output and scratch buffers may be passed in to avoid allocation.
     """
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -91,9 +91,15 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
         if ckpt.numel() * ckpt.element_size() < nbytes:
             raise ValueError("ckpt buffer too small")
         saved = Saved(ckpt, chunk)
+    wbytes = _lib.forward_workspace_bytes(shape)
+    if wbytes > 0 and workspace is None:
+        workspace = torch.empty((wbytes,), dtype=torch.uint8, device=dev)
+    if wbytes > 0 and workspace.numel() * workspace.element_size() < wbytes:
+        raise ValueError("forward workspace too small")
     st = _lib.forward_raw(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                           _ptr(S0), _ptr(y), _ptr(S_T),
-                          _ptr(saved.ckpt) if saved else 0, _stream(dev))
+                          _ptr(saved.ckpt) if saved else 0,
+                          _ptr(workspace) if wbytes > 0 else 0, wbytes, _stream(dev))
     _lib.check(st, "gdr_forward")
     return y, S_T, saved
 

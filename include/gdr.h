@@ -81,16 +81,29 @@ int gdr_checkpoint_bytes(const gdr_shape* shape, size_t* out);
  * checkpoints (one per chunk) and the per-step G_t k_t vectors, fp32. */
 int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out);
 
+/* Bytes of the scratch buffer gdr_forward needs.  Shapes with Dk <= 192,
+ * chunk >= 16 and T >= chunk take the chunked forward (the products inside a
+ * chunk on matrix cores), which keeps two 64 x 64 fp32 matrices and three
+ * vectors per (batch row, value head, chunk) here; every other shape takes
+ * the sequential sweep and needs 0 bytes. */
+int gdr_forward_workspace_bytes(const gdr_shape* shape, size_t* out);
+
 /* Forward pass.
  *   in : q, k, v, g, beta (shape.dtype); S0 (fp32, NULL means zeros)
  *   out: y (shape.dtype); S_T (fp32, NULL means not written);
  *        ckpt (gdr_checkpoint_bytes bytes, NULL means inference: nothing is
  *        saved and gdr_backward cannot follow).
+ *   workspace: at least gdr_forward_workspace_bytes bytes of device memory
+ *        (may be NULL when that is 0), contents ignored on entry and undefined
+ *        on exit; GDR_ERR_WORKSPACE if smaller.
+ * Both algorithms compute the recurrence of mlx issue #4614 (recurrence
+ * statement under the accuracy table) and write the same outputs; they
+ * differ in rounding order only.
  * `stream` is a hipStream_t passed as void*. */
 int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
                 const void* v, const void* g, const void* beta,
                 const float* S0, void* y, float* S_T, void* ckpt,
-                void* stream);
+                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward pass (VJP of gdr_forward for L = <dy, y> + <dS_T, S_T>).
  *   in : q, k, g, beta, dy (shape.dtype) - the same q, k, g, beta given to

@@ -33,8 +33,8 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ("gdr_forward", "gdr_backward", "gdr_checkpoint_bytes",
-              "gdr_backward_workspace_bytes", "gdr_num_chunks", "gdr_strerror",
-              "gdr_version"):
+              "gdr_forward_workspace_bytes", "gdr_backward_workspace_bytes",
+              "gdr_num_chunks", "gdr_strerror", "gdr_version"):
         assert n in names
 
 
@@ -73,13 +73,14 @@ def test_shape_errors(lib, shape, code):
     out = ctypes.c_size_t()
     assert lib.gdr_checkpoint_bytes(ctypes.byref(shape), ctypes.byref(out)) == code
     assert lib.gdr_backward_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)) == code
-    assert _lib.forward_raw(shape, *([0] * 10)) == code
+    assert lib.gdr_forward_workspace_bytes(ctypes.byref(shape), ctypes.byref(out)) == code
+    assert _lib.forward_raw(shape, *([0] * 10), 0, 0) == code
 
 
 def test_null_shape(lib):
     out = ctypes.c_size_t()
     assert lib.gdr_checkpoint_bytes(None, ctypes.byref(out)) == -1
-    assert lib.gdr_forward(None, *([None] * 10)) == -1
+    assert lib.gdr_forward(None, *([None] * 10), 0, None) == -1
     assert lib.gdr_backward(None, *([None] * 14), 0, None) == -1
 
 
@@ -104,7 +105,15 @@ def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
     states = nch * B * Hv * Dv * Dk * 4
     rows = B * T * Hv * Dv * 4
     assert _lib.checkpoint_bytes(sh) == _round256(states) + rows
-    assert _lib.backward_workspace_bytes(sh) == _round256(states) + rows
+    # the chunked sweeps (Dk <= 192, C >= 16, T >= C) keep two 64 x 64
+    # matrices and three 64-vectors per (batch row, value head, chunk): the
+    # whole forward workspace, and a region after the backward's per-step
+    # vectors
+    chunked = Dk <= 192 and C >= 16 and T >= C
+    prep = B * Hv * nch * (2 * 64 * 64 + 3 * 64) * 4 if chunked else 0
+    assert _lib.forward_workspace_bytes(sh) == prep
+    bwd = _round256(states) + rows
+    assert _lib.backward_workspace_bytes(sh) == (_round256(bwd) + prep if chunked else bwd)
 
 
 FAKE = 1 << 20  # a 16-byte aligned address; never dereferenced in these tests
@@ -115,18 +124,30 @@ def test_forward_null_required_pointer(lib):
     for i in range(5):  # q, k, v, g, beta
         ptrs = [FAKE] * 10
         ptrs[i] = 0
-        assert _lib.forward_raw(sh, *ptrs) == -1
+        assert _lib.forward_raw(sh, *ptrs, 0, 0) == -1
     ptrs = [FAKE] * 10
     ptrs[6] = 0  # y
-    assert _lib.forward_raw(sh, *ptrs) == -1
+    assert _lib.forward_raw(sh, *ptrs, 0, 0) == -1
 
 
 def test_forward_misaligned_pointer(lib):
     sh = S()
-    for i in range(9):
+    for i in range(10):  # q .. ckpt, workspace
         ptrs = [FAKE] * 10
         ptrs[i] = FAKE + 4
-        assert _lib.forward_raw(sh, *ptrs) == -9
+        assert _lib.forward_raw(sh, *ptrs, 1 << 30, 0) == -9
+
+
+def test_forward_workspace_errors(lib):
+    sh = S(T=64, Dk=64, Dv=32, chunk=32)  # a shape the chunked forward takes
+    ws = _lib.forward_workspace_bytes(sh)
+    assert ws > 0
+    ptrs = [FAKE] * 10
+    assert _lib.forward_raw(sh, *ptrs, ws - 1, 0) == -8
+    ptrs[9] = 0
+    assert _lib.forward_raw(sh, *ptrs, ws, 0) == -8
+    # the sequential sweep needs none
+    assert _lib.forward_workspace_bytes(S()) == 0
 
 
 def test_backward_errors(lib):
@@ -146,9 +167,9 @@ def test_backward_errors(lib):
 def test_empty_batch_is_a_no_op(lib):
     # B = 0: nothing to compute, nothing is launched, all pointers may be NULL
     sh = S(B=0)
-    assert _lib.forward_raw(sh, *([0] * 10)) == 0
+    assert _lib.forward_raw(sh, *([0] * 10), 0, 0) == 0
     assert _lib.backward_raw(sh, *([0] * 14), 0, 0) == 0
     # T = 0 and no state output requested: also nothing to launch
     sh = S(T=0)
-    assert _lib.forward_raw(sh, *([0] * 10)) == 0
+    assert _lib.forward_raw(sh, *([0] * 10), 0, 0) == 0
     assert _lib.backward_raw(sh, *([0] * 14), 0, 0) == 0
