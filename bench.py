@@ -24,24 +24,25 @@ if ROOT not in sys.path:
 import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-FP32_VECTOR_PEAK_TF = 157.3    # MI355X FP32 vector, TFLOP/s
+FP32_PEAK_TF = 157.3           # MI355X FP32: dense MFMA and (packed) vector, TFLOP/s
 FLOPS_FWD = 7                  # per state element per step (S k, S q, decay+rank-1)
 FLOPS_BWD = 15                 # per state element per step (reverse sweep)
 
-# HBM bytes per launch of the forward sweep at the default workload, from
-# rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled by a plain-copy
-# calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).  They describe the
-# kernel built from sources with this digest and are not reported otherwise.
-FWD_TRAFFIC = {"sources_sha256_16": "2cc936bfdea4eed4",
-               "read_bytes": 343.1e6, "write_bytes": 308.3e6}
-FWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_sweep.h",
-               "gdr_sweep_fwd_bf16.hip")
+# HBM bytes per gdr_backward call at the default workload (the sum over its
+# three kernels), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled
+# by a plain-copy calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).
+# They describe the kernels built from sources with this digest and are not
+# reported otherwise.
+BWD_TRAFFIC = {"sources_sha256_16": "9604a0c70f624ad9",
+               "read_bytes": 1550.0e6, "write_bytes": 404.3e6}
+BWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
+               "gdr_chunk.hip")
 
 
-def fwd_sources_digest():
+def sources_digest(files):
     import hashlib
     h = hashlib.sha256()
-    for f in FWD_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_recurrence_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -183,20 +184,25 @@ def main():
     value = tokens / (ms / 1e3)
 
     elems = B * T * Hv * Dv * Dk  # state-element steps
-    fwd_flops = FLOPS_FWD * elems
+    fwd_flops, bwd_flops = FLOPS_FWD * elems, FLOPS_BWD * elems
     fwd_tf = fwd_flops / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
     all_tf = (FLOPS_FWD + FLOPS_BWD) * elems / (ms * 1e-3) / 1e12
-    # algorithmic HBM bytes of one forward launch: q, k, v, g, beta read once,
-    # y, the residual rows e, the chunk checkpoints and S_T written once
+    # algorithmic HBM bytes, each tensor touched once: the forward reads q, k,
+    # v, g, beta and writes y, the residual rows e (fp32), the chunk
+    # checkpoints and S_T; the backward reads q, k, g, beta, dy, e and the
+    # checkpoints and writes dq, dk, dv, dg, dbeta and dS0
     esz = 2 if args.dtype == "bf16" else 4
     nch = -(-T // args.chunk)
-    fwd_bytes = (B * T * (2 * Hk * Dk + Hv * Dv + 2 * Hv) * esz        # inputs
-                 + B * T * Hv * Dv * (esz + 4)                          # y, e
-                 + B * Hv * (nch + 1) * Dv * Dk * 4)                    # ckpt, S_T
+    tok_in = B * T * (2 * Hk * Dk + Hv * Dv + 2 * Hv) * esz   # q, k, (v | dy), g, beta
+    rows32 = B * T * Hv * Dv * 4
+    state = B * Hv * Dv * Dk * 4
+    fwd_bytes = tok_in + B * T * Hv * Dv * esz + rows32 + (nch + 1) * state
+    bwd_bytes = tok_in + rows32 + nch * state + tok_in + state
     traffic = None
     default_workload = (args.T, args.B, args.chunk, args.dtype) == (2048, 1, 64, "bf16")
-    if default_workload and fwd_sources_digest() == FWD_TRAFFIC["sources_sha256_16"]:
-        traffic = FWD_TRAFFIC["read_bytes"] + FWD_TRAFFIC["write_bytes"]
+    if default_workload and sources_digest(BWD_SOURCES) == BWD_TRAFFIC["sources_sha256_16"]:
+        traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
 
     ckpt_mb = ckpt.numel() / 1e6
     ws_mb = ws.numel() / 1e6
@@ -217,17 +223,25 @@ def main():
                                f"B={B} T={T} Hk={Hk} Hv={Hv} Dk={Dk} Dv={Dv}, "
                                f"{args.dtype} inputs, fp32 state, chunk={args.chunk}",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "alu", "kernel": "fwd_sweep_kernel",
-                     "achieved": fwd_tf, "peak": FP32_VECTOR_PEAK_TF,
-                     "unit": "TFLOP/s", "frac": fwd_tf / FP32_VECTOR_PEAK_TF,
+        # the dominant call: gdr_backward (0.93 of 1.35 ms), timed with HIP
+        # events on the library's stream; its kernels run on fp32 MFMA
+        "roofline": {"bound": "mfma", "kernel": "gdr_backward (prep_kernel<bwd>, "
+                     "bwd_chunked_kernel, chunk_kernel)",
+                     "achieved": bwd_tf, "peak": FP32_PEAK_TF,
+                     "unit": "TFLOP/s", "frac": bwd_tf / FP32_PEAK_TF,
                      "traffic": traffic,
-                     "flops_per_launch": fwd_flops,
-                     "algorithmic_bytes_per_launch": fwd_bytes,
-                     "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "avg_launch_ms": fwd_ms},
+                     "flops_per_launch": bwd_flops,
+                     "algorithmic_bytes_per_launch": bwd_bytes,
+                     "hbm_frac_algorithmic": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "avg_launch_ms": bwd_ms},
+        "forward": {"kernel": "gdr_forward (prep_kernel<fwd>, fwd_chunked_kernel)",
+                    "achieved_tflops": fwd_tf, "frac": fwd_tf / FP32_PEAK_TF,
+                    "flops_per_launch": fwd_flops, "algorithmic_bytes_per_launch": fwd_bytes,
+                    "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "avg_launch_ms": fwd_ms},
         "breakdown": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                       "useful_tflops_whole_step": all_tf,
-                      "frac_whole_step_vs_fp32_vector_peak": all_tf / FP32_VECTOR_PEAK_TF,
+                      "frac_whole_step_vs_fp32_peak": all_tf / FP32_PEAK_TF,
                       "checkpoint_MB": ckpt_mb, "workspace_MB": ws_mb},
     }
     if not args.no_cpu_baseline:

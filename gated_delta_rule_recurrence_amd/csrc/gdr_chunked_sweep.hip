@@ -51,7 +51,8 @@ namespace {
 constexpr int kThreads = 256;    // prep workgroup
 constexpr int kSwThreads = 512;  // sweep workgroup: eight waves, two per SIMD
 constexpr int kN = 64;
-constexpr int kNP = kN + 1;
+constexpr int kNP = kN + 1;   // row stride of the Gram matrices in the prep
+constexpr int kGP = kN + 4;   // row stride of the per-head matrix (16-byte rows)
 constexpr int kDS = 32;       // state rows per sweep workgroup
 constexpr int kUBS = 36;      // row stride of the [kN][kDS] step-by-row stages
 constexpr int kMaxJT = 12;    // Dk <= 192 (LDS of the sweep kernels)
@@ -82,16 +83,16 @@ __device__ __forceinline__ int frag_index(int t, int r) {
 // grid (nch, Hk, B); wave w handles value heads w, w + 4, ... of the kv head.
 struct PL {
   static constexpr int QS = 0, KS = 64 * kN;          // q, k stage [16][kN][4]
-  static constexpr int GW = 0;                         // 4 x [kN][kNP] (alias)
-  static constexpr int VB = 4 * kN * kNP;              // 4 x beta[kN]
-  static constexpr int VS = VB + 4 * kN;               // 4 x suf[kN]
+  static constexpr int GW = 0;                         // 4 x [kN][kGP] (alias)
+  static constexpr int VB = 4 * kN * kGP;              // 4 x beta[kN]
+  static constexpr int VS = VB + 4 * kN;               // 4 x g[kN]
   static constexpr int QK = VS + 4 * kN, KK = QK + kN * kNP;
   static constexpr int SIZE = KK + kN * kNP;
   static_assert(2 * 64 * kN <= VB, "stage fits the per-wave arrays");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
-template <typename TIn, bool BWD>
+template <typename TIn, bool BWD, bool VEC>
 __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
                                                            float* __restrict__ prep) {
   using L = PL;
@@ -110,26 +111,45 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const int tw = 16 * w;
 
+  // g, beta of this wave's first value head, issued before the k, q loads
+  // (index clamped into the tensors; masked where used)
+  auto gb_index = [&](int hh) {
+    return ((int64_t)b * T + t0 + (l < n ? l : 0)) * Hv + hk * rep + hh;
+  };
+  TIn g_raw = g[gb_index(w < rep ? w : 0)], b_raw = beta[gb_index(w < rep ? w : 0)];
+
   // ---- QK[t][r] = q_t . k_r, KK[t][r] = k_t . k_r (MFMA over Dk) ----------
+  // All k, q quads of the chunk (up to 3 blocks of 64 columns) are loaded
+  // up front, unconditionally (clamped indices, masked at the deposit).
   {
+    constexpr int NB = kMaxJT / 4, NU = 4;
+    Quad<TIn, VEC> rq[NB][NU], rk[NB][NU];
+    uint64_t msk = 0;
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int qi = tid + kThreads * u;
+        const int s = qi >> 4, j = 64 * jb + 4 * (qi & 15);
+        const bool ok = s < n && j < Dk;
+        const int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j : 0;
+        rq[jb][u].load(q, o, ok, Dk - j);
+        rk[jb][u].load(k, o, ok, Dk - j);
+        msk |= (uint64_t)Quad<TIn, VEC>::mask(ok, Dk - j) << (4 * (NU * jb + u));
+      }
     f4 acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < Dk; j0 += 64) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+    for (int jb = 0; jb < NB; ++jb) {
+      if (64 * jb >= Dk) break;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
         const int qi = tid + kThreads * u;
-        const int s = qi >> 4, jq = qi & 15, j = j0 + 4 * jq;
-        f4 rq, rk;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const bool ok = s < n && j + x < Dk;
-          const int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j + x : 0;
-          rq[x] = ok ? ld(q, o) : 0.f;
-          rk[x] = ok ? ld(k, o) : 0.f;
-        }
-        *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq;
-        *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk;
+        const int s = qi >> 4, jq = qi & 15;
+        const uint32_t mu = (uint32_t)(msk >> (4 * (NU * jb + u))) & 15u;
+        *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq[jb][u].get(mu);
+        *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk[jb][u].get(mu);
       }
       __syncthreads();
 #pragma unroll 2
@@ -157,56 +177,67 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
   }
 
   // ---- per value head (one wave each; no barriers below) ------------------
-  float* G = sm + L::GW + w * kN * kNP;  // Gam(r,t] above the diagonal
-  float* vb = sm + L::VB + w * kN;
-  float* vs = sm + L::VS + w * kN;
+  float* G = sm + L::GW + w * kN * kGP;  // [kN][kGP] per wave
+  float* vb = sm + L::VB + w * kN;       // beta_t
+  float* vg = sm + L::VS + w * kN;       // g_t
+  const float* QK = sm + L::QK;
+  const float* KK = sm + L::KK;
   for (int hh = w; hh < rep; hh += 4) {
     const int h = hk * rep + hh;
     float* __restrict__ rec = prep + (((int64_t)b * Hv + h) * a.nch + jc) * kChunkPrepStride;
-    // every index stays inside the tensors, also where the value is unused
-    const int64_t gi = ((int64_t)b * T + t0 + (l < n ? l : 0)) * Hv + h;
-    const float gl = l < n ? ld(g, gi) : 1.f;
-    const float bl = l < n ? ld(beta, gi) : 0.f;
+    if (hh != w) {
+      g_raw = g[gb_index(hh)];
+      b_raw = beta[gb_index(hh)];
+    }
+    const float gl = l < n ? to_f32(g_raw) : 1.f;
+    const float bl = l < n ? to_f32(b_raw) : 0.f;
     vb[l] = bl;
-    // rows of Gam(r,t] (lane l <-> t = l)
-    for (int r = 0; r < kN; ++r) {
-      const float y = wave_prefix_product(l > r ? gl : 1.f);
-      G[r * kNP + l] = l == r ? 1.f : (l > r ? y : 0.f);
+    vg[l] = gl;
+    // Gam(r,t] (lane l <-> t = l) as a running product down the rows:
+    // Gam(t-1,t] = g_t, Gam(r,t] = g_{r+1} Gam(r+1,t]; 1 on the diagonal and
+    // 0 below it (rows r > t).  G[r][t] holds it.
+    float p = 1.f;
+#pragma unroll 8
+    for (int r = kN - 1; r >= 0; --r) {
+      const float gr = r + 1 < kN ? vg[r + 1] : 1.f;
+      p = r < l ? p * gr : p;
+      G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
     }
-    const float pre = wave_prefix_product(gl);  // Gam(-1, l]
-    {  // suf[t] = Gam(t, n-1]: lane l <-> t = n-1-l
-      const bool sok = l >= 1 && l < n;
-      const float gs = sok ? ld(g, ((int64_t)b * T + t0 + (sok ? n - l : 0)) * Hv + h) : 1.f;
-      const float sf = wave_prefix_product(gs);
-      if (l < n) vs[n - 1 - l] = sf;
-    }
+    const float pre = vg[0] * p;                      // Gam(-1, l] = g_0 Gam(0, l]
+    const float suf = l < n ? G[l * kGP + n - 1] : 0.f;  // Gam(l, n-1]
     float x[kN];
     if constexpr (!BWD) {
-      // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
-      for (int t = 1; t < kN; ++t)
-        if (l < t) G[t * kNP + l] = G[l * kNP + t] * sm[L::KK + t * kNP + l] * bl;
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
 #pragma unroll 1
       for (int wt = 0; wt < 4; ++wt)
 #pragma unroll 4
         for (int ks = 0; ks < 16; ++ks) {
           const int t = 16 * wt + lr, s = rstep(ks, lq);
-          const float m = s <= t ? G[s * kNP + t] * sm[L::QK + t * kNP + s] * vb[s] : 0.f;
+          const float m = s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
           rec[kPrM + (wt * 16 + ks) * 64 + l] = m;
         }
-      // T = (I + A)^-1, column l by forward substitution:
-      //   x_t = [t == l] - sum_{r<t} A[t][r] x_r
+      // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
+      for (int t = 1; t < kN; ++t)
+        if (l < t) G[t * kGP + l] = G[l * kGP + t] * KK[t * kNP + l] * bl;
+      // T = (I + A)^-1, column l by forward substitution,
+      //   x_t = [t == l] - sum_{r<t} A[t][r] x_r,
+      // row t of A read four columns at a time, four partial sums
 #pragma unroll
       for (int t = 0; t < kN; ++t) {
-        float acc = t == l ? 1.f : 0.f;
+        float acc[4] = {t == l ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < t; ++r) acc = fmaf(-G[t * kNP + r], x[r], acc);
-        x[t] = acc;
+        for (int r4 = 0; r4 < t; r4 += 4) {
+          const f4 a4 = *reinterpret_cast<const f4*>(G + t * kGP + r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r4 + e < t) acc[e] = fmaf(-a4[e], x[r4 + e], acc[e]);
+        }
+        x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
 #pragma unroll
       for (int t = 0; t < kN; ++t) rec[kPrT + frag_index(t, l)] = x[t];
       rec[kPrGam + l] = pre;
-      rec[kPrKs + l] = l < n ? bl * vs[l] : 0.f;
+      rec[kPrKs + l] = bl * suf;
       if (l == n - 1) rec[kPrGend] = pre;
     } else {
       // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
@@ -215,25 +246,30 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
 #pragma unroll 4
         for (int ks = 0; ks < 16; ++ks) {
           const int t = 16 * wt + lr, s = rstep(ks, lq);
-          const float m = s >= t ? G[t * kNP + s] * sm[L::QK + s * kNP + t] : 0.f;
+          const float m = s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
           rec[kPbM + (wt * 16 + ks) * 64 + l] = m;
         }
-      // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, kept transposed below the
-      // diagonal: G[s][t] (lane l <-> t)
-      for (int s = 1; s < kN; ++s)
-        if (l < s) G[s * kNP + l] = G[l * kNP + s] * sm[L::KK + s * kNP + l] * vb[s];
-      // Tb = (I + Bm)^-1, column l by back substitution:
+      // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
+      // diagonal (lane l <-> s)
+      for (int t = 0; t < kN - 1; ++t)
+        if (l > t) G[t * kGP + l] *= bl * KK[l * kNP + t];
+      // Tb = (I + Bm)^-1, column l by back substitution,
       //   x_t = [t == l] - sum_{r>t} Bm[t][r] x_r
 #pragma unroll
       for (int t = kN - 1; t >= 0; --t) {
-        float acc = t == l ? 1.f : 0.f;
+        float acc[4] = {t == l ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = t + 1; r < kN; ++r) acc = fmaf(-G[r * kNP + t], x[r], acc);
-        x[t] = acc;
+        for (int r4 = (t + 1) & ~3; r4 < kN; r4 += 4) {
+          const f4 a4 = *reinterpret_cast<const f4*>(G + t * kGP + r4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r4 + e > t) acc[e] = fmaf(-a4[e], x[r4 + e], acc[e]);
+        }
+        x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
 #pragma unroll
       for (int t = 0; t < kN; ++t) rec[kPbT + frag_index(t, l)] = x[t];
-      rec[kPbSuf + l] = l < n ? vs[l] : 0.f;
+      rec[kPbSuf + l] = suf;
       rec[kPbPre + l] = pre;
       rec[kPbBeta + l] = bl;
     }
@@ -747,8 +783,10 @@ hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
 
 template <typename TIn, bool BWD>
 hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep, hipStream_t s) {
-  return launch(prep_kernel<TIn, BWD>, dim3(sh.nch, sh.Hk, sh.B), kThreads,
-                sizeof(float) * PL::SIZE, s, sh, prep);
+  const dim3 grid(sh.nch, sh.Hk, sh.B);
+  const size_t lds = sizeof(float) * PL::SIZE;
+  if (sh.Dk % 4 == 0) return launch(prep_kernel<TIn, BWD, true>, grid, kThreads, lds, s, sh, prep);
+  return launch(prep_kernel<TIn, BWD, false>, grid, kThreads, lds, s, sh, prep);
 }
 
 template <typename TIn, bool BWD, typename Args>
