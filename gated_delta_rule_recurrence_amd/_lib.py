@@ -14,6 +14,8 @@ LIB_PATH = Path(__file__).resolve().parent / "libgdr.so"
 
 GDR_F32 = 0
 GDR_BF16 = 1
+GDR_DECAY_G = 0
+GDR_DECAY_LOG = 1
 
 # entry points declared in include/gdr.h, with their ctypes signatures
 _c_shape_p = None  # set below
@@ -29,6 +31,7 @@ class GdrShape(ctypes.Structure):
         ("Dv", ctypes.c_int64),
         ("chunk", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
+        ("decay", ctypes.c_int32),
     ]
 
 
@@ -84,9 +87,9 @@ def check(status: int, where: str) -> None:
         raise GdrError(status, where)
 
 
-def make_shape(B, T, Hk, Hv, Dk, Dv, chunk, dtype) -> GdrShape:
+def make_shape(B, T, Hk, Hv, Dk, Dv, chunk, dtype, decay=0) -> GdrShape:
     return GdrShape(int(B), int(T), int(Hk), int(Hv), int(Dk), int(Dv),
-                    int(chunk), int(dtype))
+                    int(chunk), int(dtype), int(decay))
 
 
 def num_chunks(shape: GdrShape) -> int:

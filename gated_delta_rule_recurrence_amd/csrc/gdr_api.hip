@@ -46,6 +46,7 @@ int check_shape(const gdr_shape* s, Sizes* z) {
     return GDR_ERR_UNSUPPORTED_DIM;
   if (s->chunk < 1 || s->chunk > kMaxChunk) return GDR_ERR_BAD_CHUNK;
   if (s->dtype != GDR_F32 && s->dtype != GDR_BF16) return GDR_ERR_BAD_DTYPE;
+  if (s->decay != GDR_DECAY_G && s->decay != GDR_DECAY_LOG) return GDR_ERR_BAD_DECAY;
   if (s->T > INT32_MAX / 2) return GDR_ERR_OVERFLOW;
 
   Sizes r{};
@@ -157,6 +158,7 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
   a.Dv = (int)shape->Dv;
   a.L = (int)shape->chunk;
   a.nch = (int)z.nch;
+  a.log_g = shape->decay == GDR_DECAY_LOG;
   a.q = q;
   a.k = k;
   a.v = v;
@@ -217,6 +219,7 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   b.Dv = (int)shape->Dv;
   b.L = (int)shape->chunk;
   b.nch = (int)z.nch;
+  b.log_g = shape->decay == GDR_DECAY_LOG;
   b.q = q;
   b.k = k;
   b.g = g;
@@ -250,6 +253,7 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   c.Dv = b.Dv;
   c.L = b.L;
   c.nch = b.nch;
+  c.log_g = b.log_g;
   c.q = q;
   c.k = k;
   c.g = g;
@@ -281,11 +285,12 @@ const char* gdr_strerror(int status) {
     case GDR_ERR_WORKSPACE: return "workspace is smaller than the size query returns";
     case GDR_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case GDR_ERR_HIP: return "the HIP runtime rejected a kernel launch";
+    case GDR_ERR_BAD_DECAY: return "decay must be GDR_DECAY_G or GDR_DECAY_LOG";
   }
   return "unknown gdr status";
 }
 
-const char* gdr_version(void) { return "0.2.0"; }
+const char* gdr_version(void) { return "0.3.0"; }
 
 }  // extern "C"
 

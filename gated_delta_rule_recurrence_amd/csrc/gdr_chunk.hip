@@ -298,7 +298,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     // per-head vectors: g, beta and the running decay products
     if (tid < kN) {
       const bool ok = tid < n;
-      sm[L::V_G + tid] = ok ? ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
+      sm[L::V_G + tid] =
+          ok ? decay_of(ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h), a.log_g) : 0.f;
       sm[L::V_B + tid] = ok ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
     }
     __syncthreads();
@@ -546,8 +547,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         acc = rowsum16(acc);
         if (lr == 0 && t < n) {
           const float At = fmaf(gend, phi0, Bt[4][v]);
+          const float dgt = fmaf(sm[L::V_PREX + t], At, acc);
+          // with log-decay input: dL/dlg_t = g_t dL/dg_t
           st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h,
-             fmaf(sm[L::V_PREX + t], At, acc));
+             a.log_g ? sm[L::V_G + t] * dgt : dgt);
         }
       }
     }

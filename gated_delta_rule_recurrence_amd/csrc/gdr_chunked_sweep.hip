@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       g_raw = g[gb_index(hh)];
       b_raw = beta[gb_index(hh)];
     }
-    const float gl = l < n ? to_f32(g_raw) : 1.f;
+    const float gl = l < n ? decay_of(to_f32(g_raw), a.log_g) : 1.f;
     const float bl = l < n ? to_f32(b_raw) : 0.f;
     vb[l] = bl;
     vg[l] = gl;
@@ -827,6 +827,7 @@ ChunkedSweepShape shape_of(const Args& a) {
   sh.Dk = a.Dk;
   sh.L = a.L;
   sh.nch = a.nch;
+  sh.log_g = a.log_g;
   sh.q = a.q;
   sh.k = a.k;
   sh.g = a.g;

@@ -35,6 +35,10 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
   return r;
 }
 
+// The decay g_t from what the g tensor holds: g_t itself, or its log
+// (g_t = exp(lg_t), the fp32 exponential).
+__device__ __forceinline__ float decay_of(float x, bool log_g) { return log_g ? expf(x) : x; }
+
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i) {
   return to_f32(p[i]);

@@ -9,6 +9,7 @@ namespace gdr {
 // Forward sweep: state recurrence with save.
 struct FwdSweepArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
+  int log_g;  // g holds log of the decay
   const void* q;
   const void* k;
   const void* v;
@@ -24,6 +25,7 @@ struct FwdSweepArgs {
 // Reverse sweep of the state gradient.
 struct BwdSweepArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
+  int log_g;  // g holds log of the decay
   const void* q;
   const void* k;
   const void* g;
@@ -39,6 +41,7 @@ struct BwdSweepArgs {
 // Chunk-parallel contraction: dq, dk, dg, dbeta.
 struct ChunkArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
+  int log_g;  // g holds log of the decay; dg is then dL/dlog g
   const void* q;
   const void* k;
   const void* g;
@@ -68,6 +71,7 @@ struct BwdChunkedArgs {
 // What the prep kernels read.
 struct ChunkedSweepShape {
   int B, T, Hk, Hv, Dk, L, nch;
+  int log_g;
   const void* q;
   const void* k;
   const void* g;

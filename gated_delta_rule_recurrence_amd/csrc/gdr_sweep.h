@@ -105,6 +105,7 @@ struct Stager {
 
   Slot kr[SK], qr[SK], xr[SX];
   TIn gb;  // g (threads 0..15) or beta (threads 16..31) of one step
+  bool log_g = false;  // g holds log of the decay
   uint64_t ok;
   bool full;  // every slot of the block is in range (no zero fill needed)
 
@@ -187,7 +188,7 @@ struct Stager {
     if (tid < 32) {
       const bool good = !CHECK || ((ok >> (SK + SX)) & 1);
       buf[(tid < 16 ? Lo::G_OFF : Lo::B_OFF) + (tid & 15)] =
-          good ? to_f32(gb) : 0.f;
+          good ? decay_of(to_f32(gb), tid < 16 && log_g) : 0.f;
     }
   }
 
@@ -376,6 +377,7 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
 
   const int nblk = (T + kStage - 1) / kStage;
   St_ stg;
+  stg.log_g = a.log_g;
   if (nblk > 0) {
     stg.fetch(0, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, v, g, beta);
     stg.store(lds[0]);
@@ -577,6 +579,7 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
 
   const int nblk = (T + kStage - 1) / kStage;
   St_ stg;
+  stg.log_g = a.log_g;
   if (nblk > 0) {
     stg.fetch(nblk - 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, dy, g,
               beta);

@@ -57,6 +57,7 @@ class Problem:
     dST: Optional[np.ndarray] = None
     dtype: str = "f32"  # "f32" or "bf16": the element type handed to the kernels
     meta: Dict[str, object] = field(default_factory=dict)
+    log_decay: bool = False  # g holds log of the decay
 
     def arrays(self):
         return dict(q=self.q, k=self.k, v=self.v, g=self.g, beta=self.beta,
@@ -89,13 +90,14 @@ def _sigmoid(x: np.ndarray) -> np.ndarray:
 
 
 def draw(B, T, Hk, Hv, Dk, Dv, *, seed=0, normalised=False, decay="weak",
-         S0_std=None, dST_std=None, dtype="f32") -> Problem:
+         S0_std=None, dST_std=None, dtype="f32", log_decay=False) -> Problem:
     """Draw one problem.
 
     decay: "weak" (mu=-2), "strong" (mu=+2) or "mix" (value head hv even ->
     weak, odd -> strong).  S0_std / dST_std: None means the tensor is absent
     (zero).  dtype "bf16" rounds every input to bfloat16 (RNE) so that the
-    oracle and the kernels see the same values.
+    oracle and the kernels see the same values.  log_decay: g holds the
+    drawn log g itself (the same draws), for the log-decay input.
     """
     if Hv % Hk:
         raise ValueError("Hv must be a multiple of Hk")
@@ -124,9 +126,11 @@ def draw(B, T, Hk, Hv, Dk, Dv, *, seed=0, normalised=False, decay="weak",
     S0 = None
     if S0_std is not None:
         S0 = rng.normal(0.0, S0_std, (B, Hv, Dv, Dk))
-    p = Problem(B, T, Hk, Hv, Dk, Dv, q, k, v, g, beta, dy, S0, dST, dtype,
+    p = Problem(B, T, Hk, Hv, Dk, Dv, q, k, v, log_g if log_decay else g, beta, dy,
+                S0, dST, dtype,
                 meta=dict(seed=seed, normalised=normalised, decay=decay,
-                          mean_log_g=float(log_g.mean())))
+                          mean_log_g=float(log_g.mean())),
+                log_decay=log_decay)
     if dtype == "bf16":
         for name in ("q", "k", "v", "g", "beta", "dy"):
             setattr(p, name, bf16_round(getattr(p, name)))

@@ -40,16 +40,19 @@ def _check_tensor(name, t, shape, dtype, device):
 
 @dataclass
 class Saved:
-    """What gdr_forward leaves for gdr_backward (opaque fp32 buffer)."""
+    """What gdr_forward leaves for gdr_backward (opaque fp32 buffer), with
+    the settings the backward must repeat."""
 
     ckpt: torch.Tensor
     chunk: int
+    log_decay: bool = False
 
 
-def shape_of(q, v, chunk, dtype) -> _lib.GdrShape:
+def shape_of(q, v, chunk, dtype, log_decay=False) -> _lib.GdrShape:
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
-    return _lib.make_shape(B, T, Hk, Hv, Dk, Dv, chunk, _DTYPES[dtype])
+    decay = _lib.GDR_DECAY_LOG if log_decay else _lib.GDR_DECAY_G
+    return _lib.make_shape(B, T, Hk, Hv, Dk, Dv, chunk, _DTYPES[dtype], decay)
 
 
 def _stream(device) -> int:
@@ -57,11 +60,13 @@ def _stream(device) -> int:
 
 
 def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
-                out_state=True, y=None, S_T=None, ckpt=None, workspace=None):
+                out_state=True, y=None, S_T=None, ckpt=None, workspace=None,
+                log_decay=False):
     """Forward pass.  Returns (y, S_T or None, Saved or None).
 
     q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g, beta [B,T,Hv]; S0 [B,Hv,Dv,Dk] fp32
     or None.  Output and scratch buffers may be passed in to avoid allocation.
+    log_decay: g holds the log of the decay (GDR_DECAY_LOG).
     """
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -75,7 +80,7 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
     _check_tensor("beta", beta, (B, T, Hv), dt, dev)
     if S0 is not None:
         _check_tensor("S0", S0, (B, Hv, Dv, Dk), torch.float32, dev)
-    shape = shape_of(q, v, chunk, dt)
+    shape = shape_of(q, v, chunk, dt, log_decay)
     if y is None:
         y = torch.empty((B, T, Hv, Dv), dtype=dt, device=dev)
     _check_tensor("y", y, (B, T, Hv, Dv), dt, dev)
@@ -90,7 +95,7 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
             ckpt = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         if ckpt.numel() * ckpt.element_size() < nbytes:
             raise ValueError("ckpt buffer too small")
-        saved = Saved(ckpt, chunk)
+        saved = Saved(ckpt, chunk, bool(log_decay))
     wbytes = _lib.forward_workspace_bytes(shape)
     if wbytes > 0 and workspace is None:
         workspace = torch.empty((wbytes,), dtype=torch.uint8, device=dev)
@@ -106,7 +111,9 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
 
 def gdr_backward(q, k, g, beta, saved: Saved, dy, dS_T=None, *, want_dS0=True,
                  workspace=None, out=None):
-    """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dS0 or None)."""
+    """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dS0 or None).
+
+    With a log-decay forward (saved.log_decay), dg is dL/d(log g)."""
     dev, dt = q.device, q.dtype
     B, T, Hk, Dk = q.shape
     Hv, Dv = dy.shape[2], dy.shape[3]
@@ -117,7 +124,7 @@ def gdr_backward(q, k, g, beta, saved: Saved, dy, dS_T=None, *, want_dS0=True,
     _check_tensor("dy", dy, (B, T, Hv, Dv), dt, dev)
     if dS_T is not None:
         _check_tensor("dS_T", dS_T, (B, Hv, Dv, Dk), torch.float32, dev)
-    shape = shape_of(q, dy, saved.chunk, dt)
+    shape = shape_of(q, dy, saved.chunk, dt, saved.log_decay)
     if out is None:
         dq = torch.empty_like(q)
         dk = torch.empty_like(k)
@@ -144,8 +151,9 @@ class GatedDeltaRule(torch.autograd.Function):
     """y, S_T = gated_delta_rule(q, k, v, g, beta, S0) with the library VJP."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, S0, chunk):
-        y, S_T, saved = gdr_forward(q, k, v, g, beta, S0, chunk=chunk)
+    def forward(ctx, q, k, v, g, beta, S0, chunk, log_decay=False):
+        y, S_T, saved = gdr_forward(q, k, v, g, beta, S0, chunk=chunk,
+                                    log_decay=log_decay)
         ctx.saved = saved
         ctx.has_S0 = S0 is not None
         ctx.save_for_backward(q, k, g, beta)
@@ -159,9 +167,10 @@ class GatedDeltaRule(torch.autograd.Function):
         dS_T = None if dS_T is None else dS_T.contiguous()
         dq, dk, dv, dg, dbeta, dS0 = gdr_backward(
             q, k, g, beta, ctx.saved, dy, dS_T, want_dS0=ctx.has_S0)
-        return dq, dk, dv, dg, dbeta, (dS0 if ctx.has_S0 else None), None
+        return dq, dk, dv, dg, dbeta, (dS0 if ctx.has_S0 else None), None, None
 
 
-def gated_delta_rule(q, k, v, g, beta, S0=None, chunk=DEFAULT_CHUNK):
-    """Autograd-enabled forward: returns (y, S_T)."""
-    return GatedDeltaRule.apply(q, k, v, g, beta, S0, chunk)
+def gated_delta_rule(q, k, v, g, beta, S0=None, chunk=DEFAULT_CHUNK, log_decay=False):
+    """Autograd-enabled forward: returns (y, S_T).  With log_decay, g holds
+    the log of the decay and its gradient is dL/d(log g)."""
+    return GatedDeltaRule.apply(q, k, v, g, beta, S0, chunk, log_decay)

@@ -19,7 +19,8 @@
  *   v, y, dv, dy      [B][T][Hv][Dv]      element type = shape.dtype
  *   g, beta, dg, dbeta[B][T][Hv]          element type = shape.dtype
  *   S0, S_T, dS_T, dS0[B][Hv][Dv][Dk]     always fp32
- *   g is the decay itself (not its log); dg is dL/dg.
+ *   g is the decay itself and dg is dL/dg, unless shape.decay is
+ *   GDR_DECAY_LOG (see gdr_decay).
  *
  * Ownership: every buffer is allocated and freed by the caller; all data
  * pointers are device pointers.  The library allocates nothing, keeps no
@@ -53,10 +54,22 @@ typedef enum {
   GDR_ERR_OVERFLOW = -7,        /* a byte size does not fit in 63 bits          */
   GDR_ERR_WORKSPACE = -8,       /* workspace smaller than the size query says  */
   GDR_ERR_ALIGNMENT = -9,       /* a pointer is not 16-byte aligned             */
-  GDR_ERR_HIP = -10             /* the HIP runtime rejected a launch            */
+  GDR_ERR_HIP = -10,            /* the HIP runtime rejected a launch            */
+  GDR_ERR_BAD_DECAY = -11       /* decay is not GDR_DECAY_G or GDR_DECAY_LOG    */
 } gdr_status;
 
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
+
+/* How the g tensor carries the decay (mlx issue #4614, the note under the
+ * accuracy table: models train the decay through its log, e.g. Qwen3.5's
+ * A_log/dt_bias chain; the issue's repro script draws log g and takes
+ * g = exp(log g)).
+ *   GDR_DECAY_G:   g_t is the decay; gdr_backward's dg is dL/dg_t.
+ *   GDR_DECAY_LOG: g holds lg_t = log of the decay; the kernels use
+ *                  g_t = exp(lg_t) (fp32), and gdr_backward's dg is
+ *                  dL/dlg_t = g_t dL/dg_t.  A forward and the backward that
+ *                  uses its save buffer must use the same setting. */
+typedef enum { GDR_DECAY_G = 0, GDR_DECAY_LOG = 1 } gdr_decay;
 
 /* Problem description.  chunk = C, the checkpoint interval: the forward saves
  * the state every C steps and the backward processes time in chunks of C
@@ -66,6 +79,7 @@ typedef struct {
   int64_t B, T, Hk, Hv, Dk, Dv;
   int64_t chunk;
   int32_t dtype; /* gdr_dtype: element type of q,k,v,g,beta,y,dy and grads */
+  int32_t decay; /* gdr_decay: what g holds (0 = the decay itself) */
 } gdr_shape;
 
 /* Number of chunks, ceil(T / chunk) (0 when T == 0). */

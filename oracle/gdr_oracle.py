@@ -36,6 +36,13 @@ backwards from dS_T (zeros when absent), for t = T-1 .. 0:
 dq and dk of the value heads that share a kv head are summed in ascending
 head order.  Float64 throughout; inputs are promoted to float64.
 
+Log-decay input (``log_decay=True``): the g argument holds lg = log of the
+decay, as in the repro script of mlx issue #4614, which draws log g and
+takes g = exp(log g), and as the issue's note on training the decay through
+its log (A_log/dt_bias) requires.  The forward uses g = exp(lg); the
+backward returns dL/dlg = g * dL/dg (chain rule through the exponential) in
+place of dL/dg.
+
 Pins: tests/test_oracle.py checks this module against central finite
 differences, hand-expanded closed forms for T=1 and T=2, the delta-rule
 invariant, the g=1/beta=0 identity case, linearity, the adjoint identity,
@@ -64,14 +71,17 @@ def _f64(x):
     return x.astype(np.result_type(x.dtype, np.float64), copy=False)
 
 
-def forward(q, k, v, g, beta, S0=None, keep_states=False):
+def forward(q, k, v, g, beta, S0=None, keep_states=False, log_decay=False):
     """Run the recurrence.
 
     q, k: [B,T,Hk,Dk]; v: [B,T,Hv,Dv]; g, beta: [B,T,Hv]; S0: [B,Hv,Dv,Dk]
     or None (zeros).  Returns (y [B,T,Hv,Dv], S_T [B,Hv,Dv,Dk]) and, when
     keep_states, also the list of T+1 states S_0 .. S_T (each [B,Hv,Dv,Dk]).
+    With log_decay, g holds log of the decay.
     """
     q, k, v, g, beta, S0 = map(_f64, (q, k, v, g, beta, S0))
+    if log_decay:
+        g = np.exp(g)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     kv = head_map(Hk, Hv)
@@ -95,14 +105,17 @@ def forward(q, k, v, g, beta, S0=None, keep_states=False):
     return y, S
 
 
-def backward(q, k, v, g, beta, dy, S0=None, dST=None):
+def backward(q, k, v, g, beta, dy, S0=None, dST=None, log_decay=False):
     """Gradients of L = <dy, y> + <dST, S_T> with respect to every input.
 
     Returns (dq, dk, dv, dg, dbeta, dS0) with the shapes of (q, k, v, g,
     beta, S0-or-state).  dq/dk are summed over the value heads of each kv
-    head in ascending order.
+    head in ascending order.  With log_decay, g holds log of the decay and
+    the returned dg is the gradient with respect to that log.
     """
     q, k, v, g, beta, dy, S0, dST = map(_f64, (q, k, v, g, beta, dy, S0, dST))
+    if log_decay:
+        g = np.exp(g)
     B, T, Hk, Dk = q.shape
     Hv, Dv = v.shape[2], v.shape[3]
     kv = head_map(Hk, Hv)
@@ -147,6 +160,8 @@ def backward(q, k, v, g, beta, dy, S0=None, dST=None):
     for h in range(Hv):                          # ascending value-head order
         dq[:, :, h // rep] += dq_h[:, :, h]
         dk[:, :, h // rep] += dk_h[:, :, h]
+    if log_decay:
+        dg = g * dg                              # d g / d log g = g
     return dq, dk, dv, dg, dbeta, G
 
 

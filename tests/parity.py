@@ -43,7 +43,7 @@ def run_gpu(p, dev, chunk=64, d=None, want_saved=False):
     from gated_delta_rule_recurrence_amd import ops
     d = d or device_inputs(p, dev)
     y, ST, saved = ops.gdr_forward(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                   d["S0"], chunk=chunk)
+                                   d["S0"], chunk=chunk, log_decay=p.log_decay)
     dq, dk, dv, dg, db, dS0 = ops.gdr_backward(d["q"], d["k"], d["g"], d["beta"],
                                                saved, d["dy"], d["dST"])
     torch.cuda.synchronize()
@@ -66,8 +66,9 @@ def run_oracle(p, b=None, hk=None):
         v, g, beta, dy = v[bs, :, hs], g[bs, :, hs], beta[bs, :, hs], dy[bs, :, hs]
         S0 = None if S0 is None else S0[bs, hs]
         dST = None if dST is None else dST[bs, hs]
-    y, ST = O.forward(q, k, v, g, beta, S0)
-    dq, dk, dv, dg, db, dS0 = O.backward(q, k, v, g, beta, dy, S0, dST)
+    y, ST = O.forward(q, k, v, g, beta, S0, log_decay=p.log_decay)
+    dq, dk, dv, dg, db, dS0 = O.backward(q, k, v, g, beta, dy, S0, dST,
+                                         log_decay=p.log_decay)
     return dict(y=y, S_T=ST, dq=dq, dk=dk, dv=dv, dg=dg, dbeta=db, dS0=dS0)
 
 

@@ -54,20 +54,20 @@ def test_binding_covers_header():
 
 def test_version_and_strerror(lib):
     assert re.fullmatch(r"\d+\.\d+\.\d+", lib.gdr_version().decode())
-    for code in range(0, -11, -1):
+    for code in range(0, -12, -1):
         assert "unknown" not in _lib.strerror(code)
     assert "unknown" in _lib.strerror(-999)
 
 
-def S(B=1, T=4, Hk=2, Hv=4, Dk=8, Dv=8, chunk=2, dtype=_lib.GDR_F32):
-    return _lib.make_shape(B, T, Hk, Hv, Dk, Dv, chunk, dtype)
+def S(B=1, T=4, Hk=2, Hv=4, Dk=8, Dv=8, chunk=2, dtype=_lib.GDR_F32, decay=0):
+    return _lib.make_shape(B, T, Hk, Hv, Dk, Dv, chunk, dtype, decay)
 
 
 @pytest.mark.parametrize("shape,code", [
     (S(B=-1), -2), (S(T=-1), -2), (S(Hk=0), -2), (S(Hv=0), -2), (S(Dk=0), -2),
     (S(Dv=0), -2), (S(Hk=3, Hv=4), -3), (S(Dk=257), -4), (S(Dv=300), -4),
     (S(B=70000), -4), (S(chunk=0), -5), (S(chunk=65), -5), (S(dtype=2), -6),
-    (S(dtype=-1), -6), (S(T=2**40), -7),
+    (S(dtype=-1), -6), (S(T=2**40), -7), (S(decay=2), -11), (S(decay=-1), -11),
 ])
 def test_shape_errors(lib, shape, code):
     out = ctypes.c_size_t()

@@ -63,6 +63,35 @@ def test_strong_decay(cuda, heads, normalised):
     compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["f32"], "strong")
 
 
+# ------------------------------------------------------ log-decay input (f2)
+@pytest.mark.parametrize("chunk", [64, 7])
+def test_log_decay_strong(cuda, chunk):
+    """g given as log g; dg returned as dL/dlog g (chunked path at C=64, the
+    per-step sweeps at C=7)."""
+    p = inputs.draw(1, 128, 4, 12, 128, 128, seed=0, decay="strong", log_decay=True)
+    log(f"log decay strong C={chunk}")
+    compare(run_gpu(p, cuda, chunk), run_oracle(p), TOL["f32"], f"log strong C={chunk}")
+
+
+def test_log_decay_bf16(cuda):
+    p = inputs.draw(2, 70, 2, 4, 64, 32, seed=19, normalised=True, S0_std=0.1,
+                    dST_std=1.0, dtype="bf16", log_decay=True)
+    compare(run_gpu(p, cuda, 32), run_oracle(p), TOL["bf16"], "log bf16")
+
+
+def test_log_decay_matches_plain_path(cuda):
+    """Same problem through both encodings: every output agrees, and the
+    log path's dg is g times the plain path's."""
+    pl = inputs.draw(1, 100, 2, 4, 48, 40, seed=23, normalised=True, S0_std=0.2,
+                     dST_std=1.0, log_decay=True)
+    pg = inputs.draw(1, 100, 2, 4, 48, 40, seed=23, normalised=True, S0_std=0.2,
+                     dST_std=1.0)
+    a = run_gpu(pl, cuda, 32)
+    b = run_gpu(pg, cuda, 32)
+    b["dg"] = b["dg"] * pg.g
+    compare(a, b, 2e-6, "log vs plain")
+
+
 def test_strong_decay_short_chunks(cuda):
     p = inputs.strong_decay(4, 12)
     compare(run_gpu(p, cuda, 7), run_oracle(p), TOL["f32"], "strong C=7")

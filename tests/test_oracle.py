@@ -12,6 +12,9 @@ pages, independent of the oracle's own code path (CPU only).
 * batch-row independence (unsloth-zoo PR #776: rows past the first);
 * the GQA map h // (Hv/Hk) equals numpy.repeat of q, k over value heads
   (mlx issue #4614 repro, recurrence helper);
+* the log-decay input (mlx issue #4614: the repro draws log g and takes
+  g = exp(log g); the note under the accuracy table trains the decay through
+  its log): complex-step derivatives of the loss with respect to log g;
 * and a mutation check: plausible mistakes planted in a copy of the oracle
   must each fail at least one of these pins.
 """
@@ -78,6 +81,33 @@ def complex_step_grads(orc, p, h=1e-30):
     return out
 
 
+def log_decay_grad_cs(orc, p, lg, h=1e-30):
+    """Complex-step dL/dlg for the log-decay forward."""
+    d = np.zeros_like(lg)
+    S0 = p.S0 if p.S0 is not None else np.zeros((p.B, p.Hv, p.Dv, p.Dk))
+    for idx in np.ndindex(lg.shape):
+        a = np.asarray(lg, dtype=np.complex128).copy()
+        a[idx] += 1j * h
+        y, ST = orc.forward(p.q, p.k, p.v, a, p.beta, S0, log_decay=True)
+        L = (y * p.dy).sum()
+        if p.dST is not None:
+            L += (ST * p.dST).sum()
+        d[idx] = L.imag / h
+    return d
+
+
+def check_log_decay(orc, p, tol=1e-12):
+    lg = np.log(p.g)
+    grads = orc.backward(p.q, p.k, p.v, lg, p.beta, p.dy, p.S0, p.dST, log_decay=True)
+    err = O.rel_l2(grads[3], log_decay_grad_cs(orc, p, lg))
+    assert err <= tol, f"d/dlog g: rel L2 vs complex step = {err:.3e}"
+    # every other output of the log-decay path equals the plain path's
+    plain = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
+    for name, a, b in zip(NAMES, grads, plain):
+        if name != "dg":
+            assert O.rel_l2(a, b) <= 1e-13, name
+
+
 def check_fd(orc, p, tol=1e-6):
     grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
     fds = fd_grads(orc, p)
@@ -110,6 +140,14 @@ def test_complex_step(decay):
     for name, gr, cs in zip(NAMES, grads, complex_step_grads(O, p)):
         err = O.rel_l2(gr, cs)
         assert err <= 1e-12, f"{name}: rel L2 vs complex step = {err:.3e}"
+
+
+@pytest.mark.parametrize("decay", ["strong", "weak"])
+def test_log_decay_complex_step(decay):
+    """Log-decay input: the returned gradient is dL/dlog g to 1e-12."""
+    p = inputs.draw(1, 5, 1, 2, 4, 4, seed=11, decay=decay, S0_std=0.5,
+                    dST_std=1.0)
+    check_log_decay(O, p)
 
 
 # --------------------------------------------------------------------------
@@ -388,6 +426,12 @@ MUTANTS = {
                        "dq[:, :, h % Hk] += dq_h[:, :, h]"),
     "dbeta_uses_v": ('dbeta[:, t] = np.einsum("bhi,bhi->bh", e, dd)',
                      'dbeta[:, t] = np.einsum("bhi,bhi->bh", v[:, t], dd)'),
+    "log_dg_without_g": ("dg = g * dg                              # d g / d log g = g",
+                         "dg = dg"),
+    "log_forward_no_exp": ("    if log_decay:\n        g = np.exp(g)\n    B, T, Hk, Dk = q.shape\n"
+                           "    Hv, Dv = v.shape[2], v.shape[3]\n    kv = head_map(Hk, Hv)\n    dt =",
+                           "    B, T, Hk, Dk = q.shape\n"
+                           "    Hv, Dv = v.shape[2], v.shape[3]\n    kv = head_map(Hk, Hv)\n    dt ="),
 }
 
 
@@ -414,6 +458,8 @@ def _pins(orc):
         "T2": lambda: test_closed_form_T2(0, orc),
         "gqa_repeat": lambda: test_gqa_is_repeat(orc),
         "identity": lambda: test_identity_case(orc),
+        "log_decay": lambda: check_log_decay(orc, inputs.draw(1, 3, 1, 2, 3, 2, seed=5,
+                                                              S0_std=0.3, dST_std=1.0)),
     }
     for name, fn in checks.items():
         try:
