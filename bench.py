@@ -63,7 +63,65 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read + write), "
                          "the reference for scaling HBM byte counters, and exit")
+    ap.add_argument("--decode", type=int, default=0, metavar="B",
+                    help="instead of the training step, time single-step inference "
+                         "(T=1, state updated in place, no save buffer) at batch B "
+                         "with the same heads, and exit")
     return ap.parse_args()
+
+
+def decode(args):
+    """Inference decode: T=1 steps with the state in and out of one buffer.
+    The steps are captured in a HIP graph (torch.cuda.CUDAGraph) so that the
+    figure is GPU time, not Python launch overhead; one step streams the
+    fp32 state once (read + write)."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib, inputs, ops
+    dev = torch.device("cuda:0")
+    _lib.load()
+    B, nsteps = args.decode, 16
+    p = inputs.draw(B, nsteps, 16, 64, 192, 128, seed=args.seed, normalised=True,
+                    S0_std=0.05, dtype=args.dtype)
+    dt = torch.bfloat16 if args.dtype == "bf16" else torch.float32
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
+    steps = [{n: t(getattr(p, n)[:, i:i + 1]) for n in ("q", "k", "v", "g", "beta")}
+             for i in range(nsteps)]
+    S = torch.from_numpy(p.S0.astype(np.float32)).to(dev)
+    ys = [torch.empty((B, 1, 64, 128), dtype=dt, device=dev) for _ in range(nsteps)]
+
+    def run():
+        for i, st in enumerate(steps):
+            ops.gdr_forward(st["q"], st["k"], st["v"], st["g"], st["beta"], S, save=False,
+                            y=ys[i], S_T=S)
+
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        run()  # warm-up outside the graph
+    torch.cuda.current_stream(dev).wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * nsteps)
+    esz = 2 if args.dtype == "bf16" else 4
+    nbytes = 2 * B * 64 * 128 * 192 * 4 + B * (2 * 16 * 192 + 2 * 64 * 128 + 2 * 64) * esz
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({"metric": "decode tokens/s (T=1 step, state in place), Qwen3.5-9B heads",
+                      "value": B / (us * 1e-6), "unit": "tokens/s", "batch": B,
+                      "us_per_step": us, "dtype": args.dtype, "data": "synthetic",
+                      "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                                   "algorithmic_bytes_per_step": nbytes}}), flush=True)
 
 
 def copy_calibration(mib):
@@ -123,6 +181,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.decode:
+        decode(args)
         return
     import torch
     from gated_delta_rule_recurrence_amd import _lib, inputs, ops

@@ -175,7 +175,9 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
   const bool bf16 = shape->dtype == GDR_BF16;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (has_tokens && z.fws_bytes > 0) {
+  if (has_tokens && gdr::decode_ok(shape->T)) {
+    err = gdr::launch_decode(a, bf16, s);
+  } else if (has_tokens && z.fws_bytes > 0) {
     gdr::FwdChunkedArgs c{};
     c.s = a;
     c.prep = static_cast<float*>(workspace);

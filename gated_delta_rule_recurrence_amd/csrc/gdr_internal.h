@@ -89,6 +89,10 @@ int64_t chunked_prep_floats(int64_t B, int64_t Hv, int64_t nch);
 hipError_t launch_fwd_chunked(const FwdChunkedArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_chunked(const BwdChunkedArgs& a, bool bf16, hipStream_t s);
 
+// Short-sequence forward (decode): whether it takes T steps, and its launch.
+bool decode_ok(int64_t T);
+hipError_t launch_decode(const FwdSweepArgs& a, bool bf16, hipStream_t s);
+
 hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s);
 

@@ -244,6 +244,77 @@ def test_T1_and_empty(cuda):
     assert torch.equal(grads[5], d["dST"])
 
 
+# ------------------------------------------- short sequences and decode (f3)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_decode_steps(cuda, T, dtype):
+    """T <= 8 takes the decode kernel; forward and backward (from its save
+    buffer) against the oracle, several batch rows, Qwen3.5-9B head dims."""
+    p = inputs.draw(3, T, 2, 4, 192, 128, seed=29, normalised=True, S0_std=0.2,
+                    dST_std=1.0, dtype=dtype)
+    log(f"decode T={T} {dtype}")
+    compare(run_gpu(p, cuda, 64), run_oracle(p), TOL[dtype], f"decode T={T} {dtype}")
+
+
+@pytest.mark.parametrize("dims", [(5, 3), (130, 20), (256, 256), (64, 17)])
+def test_decode_ragged_dims(cuda, dims):
+    Dk, Dv = dims
+    p = inputs.draw(2, 2, 1, 2, Dk, Dv, seed=31, normalised=True, S0_std=0.2,
+                    dST_std=1.0)
+    compare(run_gpu(p, cuda, 1), run_oracle(p), TOL["f32"], f"decode Dk={Dk} Dv={Dv}")
+
+
+def test_decode_in_place_state(cuda):
+    """Inference with the state in and out of one buffer: T single-step calls
+    with S_T = S0 (no save buffer) give the y and final state of one T-step
+    call of the oracle."""
+    import torch
+    import oracle.gdr_oracle as O
+    from gated_delta_rule_recurrence_amd import ops
+    from parity import to_dev
+    T = 6
+    p = inputs.draw(2, T, 2, 4, 192, 128, seed=37, normalised=True, S0_std=0.2,
+                    dtype="bf16")
+    d = device_inputs(p, cuda)
+    S = d["S0"].clone()
+    ys = []
+    for t in range(T):
+        sl = {n: d[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        y, _, saved = ops.gdr_forward(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], S,
+                                      save=False, S_T=S)
+        assert saved is None
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, S_ref = O.forward(p.q, p.k, p.v, p.g, p.beta, p.S0)
+    got = torch.cat(ys, 1).float().cpu().numpy()
+    assert O.rel_l2(got, y_ref) <= TOL["bf16"]
+    assert O.rel_l2(S.cpu().numpy(), S_ref) <= 1e-5
+
+
+def test_prefill_then_decode(cuda):
+    """Prefill (chunked path, no save) then decode steps, state in place."""
+    import torch
+    import oracle.gdr_oracle as O
+    from gated_delta_rule_recurrence_amd import ops
+    T0, T1 = 100, 4
+    p = inputs.draw(1, T0 + T1, 2, 4, 64, 48, seed=41, normalised=True, S0_std=0.1)
+    d = device_inputs(p, cuda)
+    S = d["S0"].clone()
+    pre = {n: d[n][:, :T0].contiguous() for n in ("q", "k", "v", "g", "beta")}
+    y0, _, _ = ops.gdr_forward(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], S,
+                               save=False, S_T=S)
+    ys = [y0]
+    for t in range(T0, T0 + T1):
+        sl = {n: d[n][:, t:t + 1].contiguous() for n in ("q", "k", "v", "g", "beta")}
+        y, _, _ = ops.gdr_forward(sl["q"], sl["k"], sl["v"], sl["g"], sl["beta"], S,
+                                  save=False, S_T=S)
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, S_ref = O.forward(p.q, p.k, p.v, p.g, p.beta, p.S0)
+    assert O.rel_l2(torch.cat(ys, 1).cpu().numpy(), y_ref) <= 1e-5
+    assert O.rel_l2(S.cpu().numpy(), S_ref) <= 1e-5
+
+
 def test_checkpoints_hold_states(cuda):
     """The saved state checkpoints are S_{jC} of the recurrence."""
     import oracle.gdr_oracle as O
