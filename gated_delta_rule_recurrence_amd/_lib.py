@@ -41,9 +41,9 @@ _SIGNATURES = {
     "gdr_checkpoint_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
     "gdr_backward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
     "gdr_forward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
-    "gdr_forward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 10
+    "gdr_forward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 11
                     + [ctypes.c_size_t, _vp]),
-    "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 14
+    "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 15
                      + [ctypes.c_size_t, _vp]),
     "gdr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gdr_version": (ctypes.c_char_p, []),
@@ -120,18 +120,18 @@ def backward_workspace_bytes(shape: GdrShape) -> int:
 
 
 def forward_raw(shape, q, k, v, g, beta, S0, y, S_T, ckpt, workspace,
-                workspace_bytes, stream) -> int:
+                workspace_bytes, stream, mask=0) -> int:
     """gdr_forward with integer device addresses (0 = NULL); returns the status."""
-    ptrs = [_vp(x or None) for x in (q, k, v, g, beta, S0, y, S_T, ckpt, workspace)]
+    ptrs = [_vp(x or None) for x in (q, k, v, g, beta, S0, mask, y, S_T, ckpt, workspace)]
     return load().gdr_forward(ctypes.byref(shape), *ptrs,
                               ctypes.c_size_t(int(workspace_bytes)),
                               _vp(stream or None))
 
 
 def backward_raw(shape, q, k, g, beta, ckpt, dy, dS_T, dq, dk, dv, dg, dbeta,
-                 dS0, workspace, workspace_bytes, stream) -> int:
+                 dS0, workspace, workspace_bytes, stream, mask=0) -> int:
     """gdr_backward with integer device addresses (0 = NULL); returns the status."""
-    ptrs = [_vp(x or None) for x in (q, k, g, beta, ckpt, dy, dS_T, dq, dk, dv,
+    ptrs = [_vp(x or None) for x in (q, k, g, beta, mask, ckpt, dy, dS_T, dq, dk, dv,
                                      dg, dbeta, dS0, workspace)]
     return load().gdr_backward(ctypes.byref(shape), *ptrs,
                                ctypes.c_size_t(int(workspace_bytes)),

@@ -132,8 +132,9 @@ int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out) {
 
 int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
                 const void* v, const void* g, const void* beta,
-                const float* S0, void* y, float* S_T, void* ckpt,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                const float* S0, const uint8_t* mask, void* y, float* S_T,
+                void* ckpt, void* workspace, size_t workspace_bytes,
+                void* stream) {
   Sizes z;
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
@@ -165,6 +166,7 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
   a.g = g;
   a.beta = beta;
   a.S0 = S0;
+  a.mask = mask;
   a.y = y;
   a.ST = S_T;
   if (ckpt != nullptr) {
@@ -189,7 +191,8 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
 }
 
 int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
-                 const void* g, const void* beta, const void* ckpt,
+                 const void* g, const void* beta, const uint8_t* mask,
+                 const void* ckpt,
                  const void* dy, const float* dS_T, void* dq, void* dk,
                  void* dv, void* dg, void* dbeta, float* dS0,
                  void* workspace, size_t workspace_bytes, void* stream) {
@@ -228,6 +231,7 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   b.beta = beta;
   b.dy = dy;
   b.dST = dS_T;
+  b.mask = mask;
   b.dv = dv;
   b.dS0 = dS0;
   if (has_tokens) {
@@ -261,6 +265,7 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   c.g = g;
   c.beta = beta;
   c.dy = dy;
+  c.mask = mask;
   c.Sck = static_cast<const float*>(ckpt);
   c.E = reinterpret_cast<const float*>(static_cast<const char*>(ckpt) +
                                        z.e_off);
@@ -292,7 +297,7 @@ const char* gdr_strerror(int status) {
   return "unknown gdr status";
 }
 
-const char* gdr_version(void) { return "0.3.0"; }
+const char* gdr_version(void) { return "0.4.0"; }
 
 }  // extern "C"
 

@@ -297,10 +297,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
 
     // per-head vectors: g, beta and the running decay products
     if (tid < kN) {
+      // an identity step (mask byte 0) has g = 1, beta = 0
       const bool ok = tid < n;
+      const bool skip = ok && skipped(a.mask, b, T, t0 + tid);
       sm[L::V_G + tid] =
-          ok ? decay_of(ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h), a.log_g) : 0.f;
-      sm[L::V_B + tid] = ok ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
+          !ok ? 0.f
+              : skip ? 1.f
+                     : decay_of(ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h), a.log_g);
+      sm[L::V_B + tid] =
+          ok && !skip ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
     }
     __syncthreads();
     if (w == 3) {  // decay products along the chunk, one step per lane
@@ -479,9 +484,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       for (int u = 0; u < 32; ++u) x += sm[L::V_SCR + u * 8];
       sm[L::V_SCR + 1] = x;  // phi0 = <H1, S0>
     }
-    if (tid < n)
+    if (tid < n)  // g and beta do not enter an identity step
       st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h,
-         sPsi[tid * kNP + tid]);
+         skipped(a.mask, b, T, t0 + tid) ? 0.f : sPsi[tid * kNP + tid]);
 
     // running weight matrices and M
 #pragma unroll 2
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           const float dgt = fmaf(sm[L::V_PREX + t], At, acc);
           // with log-decay input: dL/dlg_t = g_t dL/dg_t
           st(static_cast<TIn*>(a.dg), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h,
-             a.log_g ? sm[L::V_G + t] * dgt : dgt);
+             skipped(a.mask, b, T, t0 + t) ? 0.f : a.log_g ? sm[L::V_G + t] * dgt : dgt);
         }
       }
     }

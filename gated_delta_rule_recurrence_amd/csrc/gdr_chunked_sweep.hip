@@ -189,8 +189,10 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       g_raw = g[gb_index(hh)];
       b_raw = beta[gb_index(hh)];
     }
-    const float gl = l < n ? decay_of(to_f32(g_raw), a.log_g) : 1.f;
-    const float bl = l < n ? to_f32(b_raw) : 0.f;
+    // an identity step (mask byte 0) has g = 1, beta = 0
+    const bool skip = l < n && skipped(a.mask, b, T, t0 + l);
+    const float gl = l < n && !skip ? decay_of(to_f32(g_raw), a.log_g) : 1.f;
+    const float bl = l < n && !skip ? to_f32(b_raw) : 0.f;
     vb[l] = bl;
     vg[l] = gl;
     // Gam(r,t] (lane l <-> t = l) as a running product down the rows:
@@ -828,6 +830,7 @@ ChunkedSweepShape shape_of(const Args& a) {
   sh.L = a.L;
   sh.nch = a.nch;
   sh.log_g = a.log_g;
+  sh.mask = a.mask;
   sh.q = a.q;
   sh.k = a.k;
   sh.g = a.g;

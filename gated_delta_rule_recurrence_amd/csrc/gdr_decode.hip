@@ -97,7 +97,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(FwdSweepArgs a) {
       m |= Quad<TIn, VEC>::mask(ok, Dk - c) << (4 * u);
     }
     const float vi = ld(v, gi * Dv + (rok ? i : 0));
-    const float gt = decay_of(ld(g, gi), a.log_g), bt = ld(beta, gi);
+    // an identity step (mask byte 0) has g = 1, beta = 0
+    const bool skip = skipped(a.mask, b, T, t);
+    const float gt = skip ? 1.f : decay_of(ld(g, gi), a.log_g);
+    const float bt = skip ? 0.f : ld(beta, gi);
     float kk[NC], sk = 0.f, sq = 0.f, kqd = 0.f;
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {

@@ -39,6 +39,22 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
 // (g_t = exp(lg_t), the fp32 exponential).
 __device__ __forceinline__ float decay_of(float x, bool log_g) { return log_g ? expf(x) : x; }
 
+// Whether step t of batch row b is an identity step (mask byte 0).
+__device__ __forceinline__ bool skipped(const uint8_t* mask, int b, int T, int t) {
+  return mask != nullptr && mask[(int64_t)b * T + t] == 0;
+}
+
+// A byte that reads as a valid step: the address a mask load uses when there
+// is no mask (or the step is out of range), so that the load needs no branch.
+__device__ const uint8_t kValidStep = 1;
+
+// The mask byte of step t (1 without a mask or out of range), loaded without
+// a branch around it.
+__device__ __forceinline__ const uint8_t* mask_byte(const uint8_t* mask, int b, int T, int t,
+                                                    bool in_range) {
+  return mask != nullptr && in_range ? mask + (int64_t)b * T + t : &kValidStep;
+}
+
 template <typename T>
 __device__ __forceinline__ float ld(const T* p, int64_t i) {
   return to_f32(p[i]);

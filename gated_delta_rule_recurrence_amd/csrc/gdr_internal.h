@@ -10,6 +10,7 @@ namespace gdr {
 struct FwdSweepArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
   int log_g;  // g holds log of the decay
+  const uint8_t* mask;  // [B][T], 0 = identity step; may be null
   const void* q;
   const void* k;
   const void* v;
@@ -26,6 +27,7 @@ struct FwdSweepArgs {
 struct BwdSweepArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
   int log_g;  // g holds log of the decay
+  const uint8_t* mask;  // [B][T], 0 = identity step; may be null
   const void* q;
   const void* k;
   const void* g;
@@ -42,6 +44,7 @@ struct BwdSweepArgs {
 struct ChunkArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
   int log_g;  // g holds log of the decay; dg is then dL/dlog g
+  const uint8_t* mask;  // [B][T], 0 = identity step; may be null
   const void* q;
   const void* k;
   const void* g;
@@ -72,6 +75,7 @@ struct BwdChunkedArgs {
 struct ChunkedSweepShape {
   int B, T, Hk, Hv, Dk, L, nch;
   int log_g;
+  const uint8_t* mask;
   const void* q;
   const void* k;
   const void* g;

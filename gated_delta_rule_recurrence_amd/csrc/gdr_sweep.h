@@ -105,7 +105,9 @@ struct Stager {
 
   Slot kr[SK], qr[SK], xr[SX];
   TIn gb;  // g (threads 0..15) or beta (threads 16..31) of one step
+  uint8_t mk;  // mask byte of the step (0: an identity step)
   bool log_g = false;  // g holds log of the decay
+  const uint8_t* mask = nullptr;
   uint64_t ok;
   bool full;  // every slot of the block is in range (no zero fill needed)
 
@@ -147,6 +149,7 @@ struct Stager {
       const bool good = tid < 32 && t0 + s < T;
       const int64_t off = good ? ((int64_t)b * T + t0 + s) * Hv + h : 0;
       gb = (tid < 16 ? g : beta)[off];
+      mk = *mask_byte(mask, b, T, t0 + s, good);
       m |= (uint64_t)good << (SK + SX);
     }
     ok = m;
@@ -187,8 +190,9 @@ struct Stager {
     }
     if (tid < 32) {
       const bool good = !CHECK || ((ok >> (SK + SX)) & 1);
-      buf[(tid < 16 ? Lo::G_OFF : Lo::B_OFF) + (tid & 15)] =
-          good ? decay_of(to_f32(gb), tid < 16 && log_g) : 0.f;
+      // an identity step: g = 1, beta = 0
+      const float val = mk == 0 ? (tid < 16 ? 1.f : 0.f) : decay_of(to_f32(gb), tid < 16 && log_g);
+      buf[(tid < 16 ? Lo::G_OFF : Lo::B_OFF) + (tid & 15)] = good ? val : 0.f;
     }
   }
 
@@ -378,6 +382,7 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   const int nblk = (T + kStage - 1) / kStage;
   St_ stg;
   stg.log_g = a.log_g;
+  stg.mask = a.mask;
   if (nblk > 0) {
     stg.fetch(0, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, v, g, beta);
     stg.store(lds[0]);
@@ -580,6 +585,7 @@ __global__ __launch_bounds__(kThreads) void bwd_sweep_kernel(BwdSweepArgs a) {
   const int nblk = (T + kStage - 1) / kStage;
   St_ stg;
   stg.log_g = a.log_g;
+  stg.mask = a.mask;
   if (nblk > 0) {
     stg.fetch(nblk - 1, T, Hk, Hv, Dk, Dv, b, h, hk, rowbase, k, q, dy, g,
               beta);

@@ -58,6 +58,7 @@ class Problem:
     dtype: str = "f32"  # "f32" or "bf16": the element type handed to the kernels
     meta: Dict[str, object] = field(default_factory=dict)
     log_decay: bool = False  # g holds log of the decay
+    mask: Optional[np.ndarray] = None  # [B, T] uint8, 0 = identity step
 
     def arrays(self):
         return dict(q=self.q, k=self.k, v=self.v, g=self.g, beta=self.beta,

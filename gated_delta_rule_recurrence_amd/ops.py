@@ -46,6 +46,7 @@ class Saved:
     ckpt: torch.Tensor
     chunk: int
     log_decay: bool = False
+    mask: Optional[torch.Tensor] = None
 
 
 def shape_of(q, v, chunk, dtype, log_decay=False) -> _lib.GdrShape:
@@ -55,18 +56,29 @@ def shape_of(q, v, chunk, dtype, log_decay=False) -> _lib.GdrShape:
     return _lib.make_shape(B, T, Hk, Hv, Dk, Dv, chunk, _DTYPES[dtype], decay)
 
 
+def _as_mask(mask, B, T, device):
+    if mask is None:
+        return None
+    if mask.dtype == torch.bool:
+        mask = mask.to(torch.uint8)
+    _check_tensor("mask", mask, (B, T), torch.uint8, device)
+    return mask
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
                 out_state=True, y=None, S_T=None, ckpt=None, workspace=None,
-                log_decay=False):
+                log_decay=False, mask=None):
     """Forward pass.  Returns (y, S_T or None, Saved or None).
 
     q, k [B,T,Hk,Dk]; v [B,T,Hv,Dv]; g, beta [B,T,Hv]; S0 [B,Hv,Dv,Dk] fp32
     or None.  Output and scratch buffers may be passed in to avoid allocation.
     log_decay: g holds the log of the decay (GDR_DECAY_LOG).
+    mask: [B,T] torch.uint8 (or bool) or None; a step with mask 0 leaves the
+    state unchanged (an identity step).  S_T may be S0 (in place).
     """
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
@@ -80,6 +92,7 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
     _check_tensor("beta", beta, (B, T, Hv), dt, dev)
     if S0 is not None:
         _check_tensor("S0", S0, (B, Hv, Dv, Dk), torch.float32, dev)
+    mask = _as_mask(mask, B, T, dev)
     shape = shape_of(q, v, chunk, dt, log_decay)
     if y is None:
         y = torch.empty((B, T, Hv, Dv), dtype=dt, device=dev)
@@ -95,7 +108,7 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
             ckpt = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         if ckpt.numel() * ckpt.element_size() < nbytes:
             raise ValueError("ckpt buffer too small")
-        saved = Saved(ckpt, chunk, bool(log_decay))
+        saved = Saved(ckpt, chunk, bool(log_decay), mask)
     wbytes = _lib.forward_workspace_bytes(shape)
     if wbytes > 0 and workspace is None:
         workspace = torch.empty((wbytes,), dtype=torch.uint8, device=dev)
@@ -104,7 +117,8 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
     st = _lib.forward_raw(shape, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                           _ptr(S0), _ptr(y), _ptr(S_T),
                           _ptr(saved.ckpt) if saved else 0,
-                          _ptr(workspace) if wbytes > 0 else 0, wbytes, _stream(dev))
+                          _ptr(workspace) if wbytes > 0 else 0, wbytes, _stream(dev),
+                          mask=_ptr(mask))
     _lib.check(st, "gdr_forward")
     return y, S_T, saved
 
@@ -142,7 +156,7 @@ def gdr_backward(q, k, g, beta, saved: Saved, dy, dS_T=None, *, want_dS0=True,
                            _ptr(saved.ckpt), _ptr(dy), _ptr(dS_T), _ptr(dq),
                            _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dS0),
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _stream(dev))
+                           _stream(dev), mask=_ptr(saved.mask))
     _lib.check(st, "gdr_backward")
     return dq, dk, dv, dg, dbeta, dS0
 
@@ -151,9 +165,9 @@ class GatedDeltaRule(torch.autograd.Function):
     """y, S_T = gated_delta_rule(q, k, v, g, beta, S0) with the library VJP."""
 
     @staticmethod
-    def forward(ctx, q, k, v, g, beta, S0, chunk, log_decay=False):
+    def forward(ctx, q, k, v, g, beta, S0, chunk, log_decay=False, mask=None):
         y, S_T, saved = gdr_forward(q, k, v, g, beta, S0, chunk=chunk,
-                                    log_decay=log_decay)
+                                    log_decay=log_decay, mask=mask)
         ctx.saved = saved
         ctx.has_S0 = S0 is not None
         ctx.save_for_backward(q, k, g, beta)
@@ -167,10 +181,12 @@ class GatedDeltaRule(torch.autograd.Function):
         dS_T = None if dS_T is None else dS_T.contiguous()
         dq, dk, dv, dg, dbeta, dS0 = gdr_backward(
             q, k, g, beta, ctx.saved, dy, dS_T, want_dS0=ctx.has_S0)
-        return dq, dk, dv, dg, dbeta, (dS0 if ctx.has_S0 else None), None, None
+        return dq, dk, dv, dg, dbeta, (dS0 if ctx.has_S0 else None), None, None, None
 
 
-def gated_delta_rule(q, k, v, g, beta, S0=None, chunk=DEFAULT_CHUNK, log_decay=False):
+def gated_delta_rule(q, k, v, g, beta, S0=None, chunk=DEFAULT_CHUNK, log_decay=False,
+                     mask=None):
     """Autograd-enabled forward: returns (y, S_T).  With log_decay, g holds
-    the log of the decay and its gradient is dL/d(log g)."""
-    return GatedDeltaRule.apply(q, k, v, g, beta, S0, chunk, log_decay)
+    the log of the decay and its gradient is dL/d(log g); mask [B,T] marks
+    identity steps with 0."""
+    return GatedDeltaRule.apply(q, k, v, g, beta, S0, chunk, log_decay, mask)

@@ -102,26 +102,41 @@ int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out);
  * the sequential sweep and needs 0 bytes. */
 int gdr_forward_workspace_bytes(const gdr_shape* shape, size_t* out);
 
+/* The step mask (optional, both passes): mask[B][T] uint8, NULL means every
+ * step is valid.  A step whose mask byte is 0 is an identity step: it leaves
+ * the state unchanged (as g_t = 1, beta_t = 0 would), y_t is still the
+ * read-out of the unchanged state, and gdr_backward returns dg_t = dbeta_t =
+ * dv_t = 0 and no k_t gradient from it (dq_t and the read-out stay).  A batch
+ * of sequences of unequal lengths, padded on either side, runs in one call
+ * with it.  The pages name a mask argument of gated_delta_update (mlx-lm PR
+ * #1217, "What this PR adds") but do not define it; this is the reading
+ * taken.  The forward and the backward that uses its save buffer must get the
+ * same mask. */
+
 /* Forward pass.
- *   in : q, k, v, g, beta (shape.dtype); S0 (fp32, NULL means zeros)
+ *   in : q, k, v, g, beta (shape.dtype); S0 (fp32, NULL means zeros);
+ *        mask (see above, NULL means none)
  *   out: y (shape.dtype); S_T (fp32, NULL means not written);
  *        ckpt (gdr_checkpoint_bytes bytes, NULL means inference: nothing is
  *        saved and gdr_backward cannot follow).
  *   workspace: at least gdr_forward_workspace_bytes bytes of device memory
  *        (may be NULL when that is 0), contents ignored on entry and undefined
  *        on exit; GDR_ERR_WORKSPACE if smaller.
- * Both algorithms compute the recurrence of mlx issue #4614 (recurrence
- * statement under the accuracy table) and write the same outputs; they
- * differ in rounding order only.
+ * The algorithms (a per-step form for calls of up to 8 steps and for shapes
+ * outside the chunked range, the chunked form otherwise) compute the
+ * recurrence of mlx issue #4614 (recurrence statement under the accuracy
+ * table) and write the same outputs; they differ in rounding order only.
+ * S_T may be the S0 buffer (the state is then updated in place).
  * `stream` is a hipStream_t passed as void*. */
 int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
                 const void* v, const void* g, const void* beta,
-                const float* S0, void* y, float* S_T, void* ckpt,
-                void* workspace, size_t workspace_bytes, void* stream);
+                const float* S0, const uint8_t* mask, void* y, float* S_T,
+                void* ckpt, void* workspace, size_t workspace_bytes,
+                void* stream);
 
 /* Backward pass (VJP of gdr_forward for L = <dy, y> + <dS_T, S_T>).
- *   in : q, k, g, beta, dy (shape.dtype) - the same q, k, g, beta given to
- *        gdr_forward; ckpt as written by that gdr_forward call;
+ *   in : q, k, g, beta, dy (shape.dtype) - the same q, k, g, beta and mask
+ *        given to gdr_forward; ckpt as written by that gdr_forward call;
  *        dS_T (fp32, NULL means zeros).
  *   out: dq, dk (summed over the Hv/Hk value heads of each kv head, in
  *        ascending head order), dv, dg, dbeta (shape.dtype);
@@ -130,7 +145,8 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
  *        contents ignored on entry and undefined on exit.
  * v is not needed: the forward saved the residual e_t in ckpt. */
 int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
-                 const void* g, const void* beta, const void* ckpt,
+                 const void* g, const void* beta, const uint8_t* mask,
+                 const void* ckpt,
                  const void* dy, const float* dS_T, void* dq, void* dk,
                  void* dv, void* dg, void* dbeta, float* dS0,
                  void* workspace, size_t workspace_bytes, void* stream);

@@ -43,6 +43,13 @@ its log (A_log/dt_bias) requires.  The forward uses g = exp(lg); the
 backward returns dL/dlg = g * dL/dg (chain rule through the exponential) in
 place of dL/dg.
 
+Step mask (``mask``, [B, T], nonzero = valid): the pages name a mask argument
+of gated_delta_update (mlx-lm PR #1217, "What this PR adds") without defining
+it.  The reading taken: a step with mask 0 is an identity step.  The state is
+left as it was (no decay, no update); y_t is still the read-out of that
+state; g_t, beta_t, v_t and k_t do not enter, so their gradients at that step
+are 0, while q_t and dy_t still meet through the read-out.
+
 Pins: tests/test_oracle.py checks this module against central finite
 differences, hand-expanded closed forms for T=1 and T=2, the delta-rule
 invariant, the g=1/beta=0 identity case, linearity, the adjoint identity,
@@ -71,13 +78,14 @@ def _f64(x):
     return x.astype(np.result_type(x.dtype, np.float64), copy=False)
 
 
-def forward(q, k, v, g, beta, S0=None, keep_states=False, log_decay=False):
+def forward(q, k, v, g, beta, S0=None, keep_states=False, log_decay=False, mask=None):
     """Run the recurrence.
 
     q, k: [B,T,Hk,Dk]; v: [B,T,Hv,Dv]; g, beta: [B,T,Hv]; S0: [B,Hv,Dv,Dk]
     or None (zeros).  Returns (y [B,T,Hv,Dv], S_T [B,Hv,Dv,Dk]) and, when
     keep_states, also the list of T+1 states S_0 .. S_T (each [B,Hv,Dv,Dk]).
-    With log_decay, g holds log of the decay.
+    With log_decay, g holds log of the decay.  mask [B,T]: 0 marks an
+    identity step.
     """
     q, k, v, g, beta, S0 = map(_f64, (q, k, v, g, beta, S0))
     if log_decay:
@@ -92,11 +100,15 @@ def forward(q, k, v, g, beta, S0=None, keep_states=False, log_decay=False):
     for t in range(T):
         kt = k[:, t, kv, :]                      # [B,Hv,Dk]
         qt = q[:, t, kv, :]
+        S_before = S
         S = g[:, t, :, None, None] * S           # decay
         u = np.einsum("bhij,bhj->bhi", S, kt)    # S k_t on the decayed state
         e = v[:, t] - u
         d = beta[:, t, :, None] * e
         S = S + d[..., :, None] * kt[..., None, :]
+        if mask is not None:                     # identity steps keep the state
+            keep = np.asarray(mask)[:, t] != 0
+            S = np.where(keep[:, None, None, None], S, S_before)
         y[:, t] = np.einsum("bhij,bhj->bhi", S, qt)
         if keep_states:
             states.append(S.copy())
@@ -105,13 +117,14 @@ def forward(q, k, v, g, beta, S0=None, keep_states=False, log_decay=False):
     return y, S
 
 
-def backward(q, k, v, g, beta, dy, S0=None, dST=None, log_decay=False):
+def backward(q, k, v, g, beta, dy, S0=None, dST=None, log_decay=False, mask=None):
     """Gradients of L = <dy, y> + <dST, S_T> with respect to every input.
 
     Returns (dq, dk, dv, dg, dbeta, dS0) with the shapes of (q, k, v, g,
     beta, S0-or-state).  dq/dk are summed over the value heads of each kv
     head in ascending order.  With log_decay, g holds log of the decay and
-    the returned dg is the gradient with respect to that log.
+    the returned dg is the gradient with respect to that log.  mask: as in
+    forward.
     """
     q, k, v, g, beta, dy, S0, dST = map(_f64, (q, k, v, g, beta, dy, S0, dST))
     if log_decay:
@@ -120,7 +133,8 @@ def backward(q, k, v, g, beta, dy, S0=None, dST=None, log_decay=False):
     Hv, Dv = v.shape[2], v.shape[3]
     kv = head_map(Hk, Hv)
     rep = Hv // Hk
-    _, _, states = forward(q, k, v, g, beta, S0, keep_states=True)
+    _, _, states = forward(q, k, v, g, beta, S0, keep_states=True, mask=mask)
+    keep_all = (np.ones((B, T), bool) if mask is None else np.asarray(mask) != 0)
 
     dq_h = np.zeros((B, T, Hv, Dk))
     dk_h = np.zeros((B, T, Hv, Dk))
@@ -142,6 +156,9 @@ def backward(q, k, v, g, beta, dy, S0=None, dST=None, log_decay=False):
         # y_t = S_t q_t
         G = G + dy[:, t][..., :, None] * qt[..., None, :]
         dq_h[:, t] = np.einsum("bhij,bhi->bhj", S_cur, dy[:, t])
+        keep = keep_all[:, t]
+        if not keep.any():                       # identity step in every row
+            continue
         # S_t = A + outer(d, k)
         c = np.einsum("bhij,bhj->bhi", G, kt)    # G k
         dd = c                                    # dL/dd
@@ -154,7 +171,15 @@ def backward(q, k, v, g, beta, dy, S0=None, dST=None, log_decay=False):
         dA = G + de_u[..., :, None] * kt[..., None, :]
         # A = g S_prev
         dg[:, t] = np.einsum("bhij,bhij->bh", dA, S_prev)
-        G = gt * dA
+        G_prev = gt * dA
+        if not keep.all():                       # identity steps: nothing enters
+            kb = keep[:, None]
+            dk_h[:, t] = np.where(kb[..., None], dk_h[:, t], 0.0)
+            dv[:, t] = np.where(kb[..., None], dv[:, t], 0.0)
+            dbeta[:, t] = np.where(kb, dbeta[:, t], 0.0)
+            dg[:, t] = np.where(kb, dg[:, t], 0.0)
+            G_prev = np.where(kb[..., None, None], G_prev, G)
+        G = G_prev
     dq = np.zeros((B, T, Hk, Dk))
     dk = np.zeros((B, T, Hk, Dk))
     for h in range(Hv):                          # ascending value-head order

@@ -42,8 +42,11 @@ def run_gpu(p, dev, chunk=64, d=None, want_saved=False):
     import torch
     from gated_delta_rule_recurrence_amd import ops
     d = d or device_inputs(p, dev)
+    mask = None
+    if p.mask is not None:
+        mask = torch.from_numpy(np.ascontiguousarray(p.mask, np.uint8)).to(dev)
     y, ST, saved = ops.gdr_forward(d["q"], d["k"], d["v"], d["g"], d["beta"],
-                                   d["S0"], chunk=chunk, log_decay=p.log_decay)
+                                   d["S0"], chunk=chunk, log_decay=p.log_decay, mask=mask)
     dq, dk, dv, dg, db, dS0 = ops.gdr_backward(d["q"], d["k"], d["g"], d["beta"],
                                                saved, d["dy"], d["dST"])
     torch.cuda.synchronize()
@@ -58,6 +61,7 @@ def run_oracle(p, b=None, hk=None):
     """Oracle outputs; optionally only batch row b and kv group hk (the kv
     groups are independent, so a group is computed on its own)."""
     q, k, v, g, beta, dy, S0, dST = p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST
+    mask = p.mask
     if b is not None:
         rep = p.Hv // p.Hk
         hs = slice(hk * rep, (hk + 1) * rep)
@@ -66,9 +70,10 @@ def run_oracle(p, b=None, hk=None):
         v, g, beta, dy = v[bs, :, hs], g[bs, :, hs], beta[bs, :, hs], dy[bs, :, hs]
         S0 = None if S0 is None else S0[bs, hs]
         dST = None if dST is None else dST[bs, hs]
-    y, ST = O.forward(q, k, v, g, beta, S0, log_decay=p.log_decay)
+        mask = None if mask is None else mask[bs]
+    y, ST = O.forward(q, k, v, g, beta, S0, log_decay=p.log_decay, mask=mask)
     dq, dk, dv, dg, db, dS0 = O.backward(q, k, v, g, beta, dy, S0, dST,
-                                         log_decay=p.log_decay)
+                                         log_decay=p.log_decay, mask=mask)
     return dict(y=y, S_T=ST, dq=dq, dk=dk, dv=dv, dg=dg, dbeta=db, dS0=dS0)
 
 

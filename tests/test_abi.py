@@ -80,8 +80,8 @@ def test_shape_errors(lib, shape, code):
 def test_null_shape(lib):
     out = ctypes.c_size_t()
     assert lib.gdr_checkpoint_bytes(None, ctypes.byref(out)) == -1
-    assert lib.gdr_forward(None, *([None] * 10), 0, None) == -1
-    assert lib.gdr_backward(None, *([None] * 14), 0, None) == -1
+    assert lib.gdr_forward(None, *([None] * 11), 0, None) == -1
+    assert lib.gdr_backward(None, *([None] * 15), 0, None) == -1
 
 
 def test_null_out_pointer(lib):

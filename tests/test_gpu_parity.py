@@ -244,6 +244,67 @@ def test_T1_and_empty(cuda):
     assert torch.equal(grads[5], d["dST"])
 
 
+# ------------------------------------------------------- step mask (f4)
+def _with_mask(p, seed, frac=0.3):
+    rng = np.random.default_rng(seed)
+    p.mask = (rng.random((p.B, p.T)) >= frac).astype(np.uint8)
+    p.mask[0, 0] = 0
+    p.mask[-1, -1] = 0
+    return p
+
+
+@pytest.mark.parametrize("chunk", [64, 7])
+def test_mask_strong_decay(cuda, chunk):
+    """Identity steps through the chunked path (C=64) and the per-step sweeps
+    (C=7), strong decay, several batch rows."""
+    p = _with_mask(inputs.draw(2, 150, 2, 6, 64, 64, seed=43, decay="strong",
+                               normalised=True, S0_std=0.2, dST_std=1.0), 1)
+    log(f"mask strong C={chunk}")
+    compare(run_gpu(p, cuda, chunk), run_oracle(p), TOL["f32"], f"mask C={chunk}")
+
+
+def test_mask_decode_and_bf16(cuda):
+    p = _with_mask(inputs.draw(3, 5, 2, 4, 192, 128, seed=47, normalised=True,
+                               S0_std=0.2, dST_std=1.0), 2)
+    compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["f32"], "mask decode")
+    p = _with_mask(inputs.draw(2, 70, 2, 4, 64, 32, seed=53, normalised=True, S0_std=0.1,
+                               dST_std=1.0, dtype="bf16", log_decay=True), 3)
+    compare(run_gpu(p, cuda, 32), run_oracle(p), TOL["bf16"], "mask bf16 log")
+
+
+def test_mask_variable_lengths(cuda):
+    """A batch of sequences of unequal lengths, right- and left-padded in one
+    call, against each sequence run alone (no mask) on the GPU."""
+    import torch
+    from gated_delta_rule_recurrence_amd import ops
+    lens = [90, 41, 64, 17]
+    T = max(lens)
+    p = inputs.draw(len(lens), T, 2, 4, 96, 64, seed=59, normalised=True, S0_std=0.2,
+                    dST_std=1.0)
+    mask = np.zeros((p.B, T), np.uint8)
+    for b, n in enumerate(lens):
+        if b % 2 == 0:
+            mask[b, :n] = 1          # right padding
+        else:
+            mask[b, T - n:] = 1      # left padding
+    p.mask = mask
+    for n_ in ("dy",):
+        getattr(p, n_)[mask == 0] = 0.0  # no cotangent on padding
+    full = run_gpu(p, cuda, 32)
+    for b, n in enumerate(lens):
+        keep = np.flatnonzero(mask[b])
+        one = inputs.draw(1, 1, 2, 4, 96, 64, seed=0)  # shape holder
+        for name in ("q", "k", "v", "g", "beta", "dy"):
+            setattr(one, name, getattr(p, name)[b:b + 1][:, keep].copy())
+        one.T = n
+        one.S0 = p.S0[b:b + 1].copy()
+        one.dST = p.dST[b:b + 1].copy()
+        alone = run_gpu(one, cuda, 32)
+        got = {k_: (v_[b:b + 1] if k_ in ("S_T", "dS0") else v_[b:b + 1][:, keep])
+               for k_, v_ in full.items() if not k_.startswith("_")}
+        compare(got, alone, 2e-6, f"varlen b{b} n={n}")
+
+
 # ------------------------------------------- short sequences and decode (f3)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("T", [1, 3, 8])

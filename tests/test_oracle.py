@@ -15,6 +15,8 @@ pages, independent of the oracle's own code path (CPU only).
 * the log-decay input (mlx issue #4614: the repro draws log g and takes
   g = exp(log g); the note under the accuracy table trains the decay through
   its log): complex-step derivatives of the loss with respect to log g;
+* the step mask (identity steps): complex-step derivatives with a mask, and
+  equality with running each batch row on its valid steps only;
 * and a mutation check: plausible mistakes planted in a copy of the oracle
   must each fail at least one of these pins.
 """
@@ -108,6 +110,73 @@ def check_log_decay(orc, p, tol=1e-12):
             assert O.rel_l2(a, b) <= 1e-13, name
 
 
+def masked_problem(seed, B=3, T=9, Hk=1, Hv=2, Dk=4, Dv=3, decay="weak", frac=0.35):
+    p = inputs.draw(B, T, Hk, Hv, Dk, Dv, seed=seed, decay=decay, S0_std=0.5,
+                    dST_std=1.0)
+    rng = np.random.default_rng(seed + 1000)
+    mask = (rng.random((B, T)) >= frac).astype(np.uint8)
+    mask[0, 0] = 0  # a masked first step
+    mask[-1, -1] = 0  # and a masked last step
+    return p, mask
+
+
+def check_mask_complex_step(orc, p, mask, tol=1e-12, h=1e-30):
+    grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST, mask=mask)
+    args = [p.q, p.k, p.v, p.g, p.beta, p.S0]
+    for i, (name, gr) in enumerate(zip(NAMES, grads)):
+        x = args[i]
+        d = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            a = [np.asarray(z, dtype=np.complex128) for z in args]
+            a[i][idx] += 1j * h
+            y, ST = orc.forward(*a, mask=mask)
+            d[idx] = ((y * p.dy).sum() + (ST * p.dST).sum()).imag / h
+        err = O.rel_l2(gr, d)
+        assert err <= tol, f"{name}: rel L2 vs complex step with mask = {err:.3e}"
+
+
+def check_mask_compaction(orc, p, mask):
+    """Each batch row run on its valid steps alone gives the final state, the
+    outputs at its valid steps and (with dy = 0 on masked steps) the
+    gradients at its valid steps; masked steps read out the carried state and
+    get zero gradients."""
+    dy = p.dy * (mask != 0)[:, :, None, None]
+    y, ST = orc.forward(p.q, p.k, p.v, p.g, p.beta, p.S0, mask=mask)
+    grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, dy, p.S0, p.dST, mask=mask)
+    kv = O.head_map(p.Hk, p.Hv)
+    for b in range(p.B):
+        keep = np.flatnonzero(mask[b])
+        sl = lambda a: a[b:b + 1][:, keep]
+        yc, STc = orc.forward(sl(p.q), sl(p.k), sl(p.v), sl(p.g), sl(p.beta),
+                              p.S0[b:b + 1])
+        np.testing.assert_allclose(ST[b:b + 1], STc, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(y[b:b + 1][:, keep], yc, rtol=1e-12, atol=1e-12)
+        gc = orc.backward(sl(p.q), sl(p.k), sl(p.v), sl(p.g), sl(p.beta), sl(dy),
+                          p.S0[b:b + 1], p.dST[b:b + 1])
+        for name, full, comp in zip(NAMES, grads, gc):
+            if name == "dS0":
+                np.testing.assert_allclose(full[b:b + 1], comp, rtol=1e-12, atol=1e-12)
+            else:
+                np.testing.assert_allclose(full[b:b + 1][:, keep], comp, rtol=1e-12,
+                                           atol=1e-12, err_msg=name)
+        # masked steps: read-out of the carried state, zero gradients
+        S = p.S0[b].copy()
+        for t in range(p.T):
+            if mask[b, t]:
+                _, S = orc.forward(p.q[b:b + 1, :t + 1], p.k[b:b + 1, :t + 1],
+                                   p.v[b:b + 1, :t + 1], p.g[b:b + 1, :t + 1],
+                                   p.beta[b:b + 1, :t + 1], p.S0[b:b + 1],
+                                   mask=mask[b:b + 1, :t + 1])
+                S = S[0]
+            else:
+                want = np.einsum("hij,hj->hi", S, p.q[b, t, kv])
+                np.testing.assert_allclose(y[b, t], want, rtol=1e-12, atol=1e-12)
+                for name, full in zip(NAMES[:5], grads[:5]):
+                    if name in ("dq", "dk"):
+                        continue
+                    assert not np.any(full[b, t]), (name, b, t)
+
+
 def check_fd(orc, p, tol=1e-6):
     grads = orc.backward(p.q, p.k, p.v, p.g, p.beta, p.dy, p.S0, p.dST)
     fds = fd_grads(orc, p)
@@ -148,6 +217,27 @@ def test_log_decay_complex_step(decay):
     p = inputs.draw(1, 5, 1, 2, 4, 4, seed=11, decay=decay, S0_std=0.5,
                     dST_std=1.0)
     check_log_decay(O, p)
+
+
+@pytest.mark.parametrize("decay", ["strong", "weak"])
+def test_mask_complex_step(decay):
+    p, mask = masked_problem(13, decay=decay)
+    check_mask_complex_step(O, p, mask)
+
+
+def test_mask_compaction():
+    p, mask = masked_problem(17, B=4, T=11)
+    check_mask_compaction(O, p, mask)
+
+
+def test_all_masked_is_identity():
+    p, _ = masked_problem(19)
+    mask = np.zeros((p.B, p.T), np.uint8)
+    y, ST = O.forward(p.q, p.k, p.v, p.g, p.beta, p.S0, mask=mask)
+    np.testing.assert_array_equal(ST, p.S0)
+    kv = O.head_map(p.Hk, p.Hv)
+    np.testing.assert_allclose(y, np.einsum("bhij,bthj->bthi", p.S0, p.q[:, :, kv]),
+                               rtol=1e-13, atol=1e-13)
 
 
 # --------------------------------------------------------------------------
@@ -417,7 +507,7 @@ MUTANTS = {
     "dg_on_new_state": ('dg[:, t] = np.einsum("bhij,bhij->bh", dA, S_prev)',
                         'dg[:, t] = np.einsum("bhij,bhij->bh", dA, S_cur)'),
     "sign_of_du": ("de_u = -bt * dd", "de_u = bt * dd"),
-    "no_decay_of_G": ("G = gt * dA", "G = dA"),
+    "no_decay_of_G": ("G_prev = gt * dA", "G_prev = dA"),
     "dk_missing_g": ('dk_h[:, t] += np.einsum("bhij,bhi->bhj", A, de_u)',
                      'dk_h[:, t] += np.einsum("bhij,bhi->bhj", S_prev, de_u)'),
     "tile_head_map": ("return np.arange(Hv) // (Hv // Hk)",
@@ -428,6 +518,8 @@ MUTANTS = {
                      'dbeta[:, t] = np.einsum("bhi,bhi->bh", v[:, t], dd)'),
     "log_dg_without_g": ("dg = g * dg                              # d g / d log g = g",
                          "dg = dg"),
+    "mask_ignored": ("S = np.where(keep[:, None, None, None], S, S_before)", "S = S"),
+    "mask_grads_kept": ("G_prev = np.where(kb[..., None, None], G_prev, G)", "G_prev = G_prev"),
     "log_forward_no_exp": ("    if log_decay:\n        g = np.exp(g)\n    B, T, Hk, Dk = q.shape\n"
                            "    Hv, Dv = v.shape[2], v.shape[3]\n    kv = head_map(Hk, Hv)\n    dt =",
                            "    B, T, Hk, Dk = q.shape\n"
@@ -460,6 +552,7 @@ def _pins(orc):
         "identity": lambda: test_identity_case(orc),
         "log_decay": lambda: check_log_decay(orc, inputs.draw(1, 3, 1, 2, 3, 2, seed=5,
                                                               S0_std=0.3, dST_std=1.0)),
+        "mask": lambda: check_mask_compaction(orc, *masked_problem(3, B=2, T=6)),
     }
     for name, fn in checks.items():
         try:
