@@ -71,12 +71,24 @@ __device__ __forceinline__ int rstep(int ks, int lq) {
 constexpr int kPrT = 0, kPrM = 4096, kPrGam = 8192, kPrKs = 8256, kPrGend = 8320;
 // Reverse record:
 constexpr int kPbT = 0, kPbM = 4096, kPbSuf = 8192, kPbPre = 8256, kPbBeta = 8320;
-static_assert(kPbBeta + kN <= kChunkPrepStride, "record");
+// Both: 64 floats that nothing reads, the target of the sweeps' stores for
+// lanes outside the tensors, so that no store needs a branch around it (a
+// branch makes the compiler's wait counts for later loads conservative).
+constexpr int kPrSink = 8384;
+static_assert(kPbBeta + kN <= kPrSink && kPrSink + 64 <= kChunkPrepStride, "record");
 
 // Element (t, r) of a [64][64] matrix in MFMA A-fragment order: k-step
-// 16 (t / 16) + ks with rstep(ks, lq) = r, lane (t % 16) + 16 lq.
+// 16 (t / 16) + ks with rstep(ks, lq) = r, lane (t % 16) + 16 lq; one
+// k-step of a tile is 64 consecutive floats (one fully coalesced load).
 __device__ __forceinline__ int frag_index(int t, int r) {
   return ((t >> 4) * 16 + 4 * (r >> 4) + (r & 3)) * 64 + (t & 15) + 16 * ((r >> 2) & 3);
+}
+
+// The 16 A operands of a lane's tile tb from a record matrix (frag_index order).
+__device__ __forceinline__ void load_frags(const float* __restrict__ m, int tb, int l,
+                                           float (&f)[16]) {
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) f[ks] = m[(tb * 16 + ks) * 64 + l];
 }
 
 // ---------------------------------------------------------------- prep ----
@@ -216,7 +228,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         for (int ks = 0; ks < 16; ++ks) {
           const int t = 16 * wt + lr, s = rstep(ks, lq);
           const float m = s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
-          rec[kPrM + (wt * 16 + ks) * 64 + l] = m;
+          rec[kPrM + (wt * 16 + ks) * 64 + l] = m;  // = frag_index(t, s)
         }
       // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
       for (int t = 1; t < kN; ++t)
@@ -249,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         for (int ks = 0; ks < 16; ++ks) {
           const int t = 16 * wt + lr, s = rstep(ks, lq);
           const float m = s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
-          rec[kPbM + (wt * 16 + ks) * 64 + l] = m;
+          rec[kPbM + (wt * 16 + ks) * 64 + l] = m;  // = frag_index(t, s)
         }
       // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
       // diagonal (lane l <-> s)
@@ -515,12 +527,12 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
     float tf[16], mf[16], gam[4], ksc[4];
     TIn vr[4];
     uint32_t vm = 0;
+    load_frags(rec + kPrT, tb, l, tf);
+    {
+      const f4 g4 = *reinterpret_cast<const f4*>(rec + kPrGam + tw + 4 * lq);
+      const f4 k4 = *reinterpret_cast<const f4*>(rec + kPrKs + tw + 4 * lq);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) tf[ks] = rec[kPrT + (tb * 16 + ks) * 64 + l];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      gam[u] = rec[kPrGam + tw + 4 * lq + u];
-      ksc[u] = rec[kPrKs + tw + 4 * lq + u];
+      for (int u = 0; u < 4; ++u) gam[u] = g4[u], ksc[u] = k4[u];
     }
     const float gend = rec[kPrGend];
 #pragma unroll
@@ -551,8 +563,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
     }
     // M is first used after two more barriers; loading it here keeps its
     // registers free during the state products
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) mf[ks] = rec[kPrM + (tb * 16 + ks) * 64 + l];
+    load_frags(rec + kPrM, tb, l, mf);
     // U = V - diag(gam) X_K
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -596,6 +607,285 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
     tiles_to_lds<JW>(sm + L::SK, Sacc, mt, jg, lq, lr);
   }
   if (a.ST != nullptr) {
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        if (i0 + i < Dv && j < Dk) a.ST[bh * mat + (int64_t)(i0 + i) * Dk + j] = Sacc[nj][u];
+      }
+  }
+}
+
+// -------------------------------------------- forward sweep, bf16 inputs ----
+// The same sweep for bf16 k, q (Dk a multiple of 8), with the two products
+// that have k or q as an operand on bf16 MFMA (v_mfma_f32_16x16x32_bf16,
+// 16 times the fp32 MFMA rate): [K; Q] S^T and the update E^T diag(ks) K.
+// Their other operand (the state, diag(ks) E) is fp32 and is split exactly
+// into three bf16 pieces (split3), so each product is three bf16 MFMAs whose
+// products are exact and whose sums are fp32: the accuracy of the fp32 path.
+// T U and M E keep fp32 MFMA (both operands are fp32 there).
+//
+// LDS: the state as three bf16 planes [3][kDS][SPS] (row i, column j), k
+// transposed as bf16 [DKP][KTS] (row j, column t), the diag(ks) E pieces
+// transposed [3][kDS][KTS] (row i, column t), and the fp32 U and E stages.
+// Row strides are 16 bytes modulo 256, so the 16-byte operand reads of a
+// quarter-wave (16 rows, one 16-byte column group) hit distinct banks.  The
+// k and q operands of [K; Q] S^T (16 steps x Dk per wave) come straight from
+// HBM as 16-byte fragments, fetched a chunk ahead.
+template <int JT>
+struct SLB {
+  static constexpr int DKP = 16 * JT;
+  static constexpr int KTS = kN + 8;              // bf16 row stride of k^T and E pieces
+  static constexpr int SPS = DKP + 8;             // bf16 row stride of the state planes
+  static constexpr int KT = 0;                    // float offsets below
+  static constexpr int SP = KT + DKP * KTS / 2;
+  static constexpr int EP = SP + 3 * kDS * SPS / 2;
+  static constexpr int UB = EP + 3 * kDS * KTS / 2;
+  static constexpr int EB = UB + kN * kUBS;
+  static constexpr int SIZE = EB + kN * kUBS;
+  // an odd number of 16-byte units per row: 16 consecutive rows at one
+  // column group fall in 16 distinct 16-byte bank groups
+  static_assert((2 * KTS) % 32 == 16 && (2 * SPS) % 32 == 16, "row strides");
+  static_assert(SP % 4 == 0 && EP % 4 == 0 && UB % 4 == 0, "16-byte aligned regions");
+  static_assert(SIZE * 4 <= 160 * 1024, "LDS");
+};
+
+template <int JT, bool SAVE>
+__global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
+  using L = SLB<JT>;
+  constexpr int DKP = L::DKP, KTS = L::KTS, SPS = L::SPS;
+  constexpr int NKS = DKP / 32;  // k-steps of 32 over Dk
+  constexpr int JW = JT / 4;
+  static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
+  extern __shared__ __align__(16) float sm[];
+  uint16_t* const kt = reinterpret_cast<uint16_t*>(sm + L::KT);
+  uint16_t* const sp = reinterpret_cast<uint16_t*>(sm + L::SP);
+  uint16_t* const ep = reinterpret_cast<uint16_t*>(sm + L::EP);
+  const FwdSweepArgs& a = A.s;
+  const bf16* __restrict__ q = static_cast<const bf16*>(a.q);
+  const bf16* __restrict__ k = static_cast<const bf16*>(a.k);
+  const bf16* __restrict__ v = static_cast<const bf16*>(a.v);
+  bf16* __restrict__ y = static_cast<bf16*>(a.y);
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
+  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = w & 3, nt = w >> 2;
+  const int mt = w & 1, jg = JW * (w >> 1);
+  const int tw = 16 * tb;
+  const int64_t bh = (int64_t)b * Hv + h;
+  const int64_t mat = (int64_t)Dv * Dk;
+  const int kst = Hk * Dk, vst = Hv * Dv;
+  auto kq_base = [&](int c) { return ((int64_t)b * T + c * a.L) * kst + (int64_t)hk * Dk; };
+  auto chunk_len = [&](int c) { return min(a.L, T - c * a.L); };
+
+  // k quads of a chunk (for k^T in LDS), a chunk ahead
+  KQPrefetch<bf16, JT, true> kq;
+  kq.init(tid);
+  // this wave's [K; Q] fragments: row tw + l % 16, columns 32 ks + 8 (l / 16)
+  // .. +7 of the chunk, a chunk ahead (raw bits; rows past the chunk and
+  // columns past Dk are zeroed where used)
+  uint4 kf[NKS], qf[NKS];
+  auto fetch_frags = [&](int c, int lr, int lq) __attribute__((always_inline)) {
+    const int64_t base = kq_base(c);
+    const bool rok = tw + lr < chunk_len(c);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int j = 32 * ks + 8 * lq;
+      int o = rok && j < Dk ? (tw + lr) * kst + j : 0;
+      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+      kf[ks] = *reinterpret_cast<const uint4*>(k + base + o);
+      qf[ks] = *reinterpret_cast<const uint4*>(q + base + o);
+    }
+  };
+
+  f4 Sacc[JW];
+  {
+    const int l = tid & 63, lr = l & 15, lq = l >> 4;
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        const bool ok = a.S0 != nullptr && i0 + i < Dv && j < Dk;
+        Sacc[nj][u] = ok ? a.S0[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
+      }
+    kq.fetch(k, q, kq_base(0), chunk_len(0), kst, Dk);
+    fetch_frags(0, lr, lq);
+  }
+  // the state tiles into the three bf16 planes (and checkpoint `slot`, or
+  // the sink when slot < 0; out-of-range lanes store to the sink too)
+  auto put_state = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
+    float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat : nullptr;
+    asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        uint32_t p0, p1, p2;
+        split3(Sacc[nj][u], p0, p1, p2);
+        sp[(0 * kDS + i) * SPS + j] = (uint16_t)p0;
+        sp[(1 * kDS + i) * SPS + j] = (uint16_t)p1;
+        sp[(2 * kDS + i) * SPS + j] = (uint16_t)p2;
+        if (SAVE) {
+          const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
+          *(ok ? ck + (int64_t)(i0 + i) * Dk + j : sink) = Sacc[nj][u];
+        }
+      }
+  };
+  {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink + (tl & 63));
+  }
+
+  for (int c = 0; c < a.nch; ++c) {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    kq.tid = tl;
+    const int l = tl & 63, lr = l & 15, lq = l >> 4;
+    const int ti = 16 * nt + lr;
+    const bool iok = i0 + ti < Dv;
+    const int t0 = c * a.L;
+    const int n = chunk_len(c);
+    const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
+    float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
+    const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
+    // k^T of this chunk from the quads fetched a chunk ago (zero padded)
+#pragma unroll
+    for (int u = 0; u < KQPrefetch<bf16, JT, true>::NQ; ++u) {
+      const uint32_t mu = (kq.pm >> (4 * u)) & 15u;
+      const uint2 raw = kq.pk[u].v;
+      const int t = kq.qt(u), j = kq.qj(u);
+      kt[(j + 0) * KTS + t] = mu ? (uint16_t)(raw.x & 0xffffu) : 0;
+      kt[(j + 1) * KTS + t] = mu ? (uint16_t)(raw.x >> 16) : 0;
+      kt[(j + 2) * KTS + t] = mu ? (uint16_t)(raw.y & 0xffffu) : 0;
+      kt[(j + 3) * KTS + t] = mu ? (uint16_t)(raw.y >> 16) : 0;
+    }
+    // this chunk's fragments, masked
+    uint4 ak[NKS], aq[NKS];
+    {
+      const bool rok = tw + lr < n;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bool ok = rok && 32 * ks + 8 * lq < Dk;
+        const uint4 z = {0u, 0u, 0u, 0u};
+        ak[ks] = ok ? kf[ks] : z;
+        aq[ks] = ok ? qf[ks] : z;
+      }
+    }
+    float tf[16], mf[16], gam[4], ksc[4];
+    bf16 vr[4];
+    uint32_t vm = 0;
+    load_frags(rec + kPrT, tb, l, tf);
+    {
+      const f4 g4 = *reinterpret_cast<const f4*>(rec + kPrGam + tw + 4 * lq);
+      const f4 k4 = *reinterpret_cast<const f4*>(rec + kPrKs + tw + 4 * lq);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gam[u] = g4[u], ksc[u] = k4[u];
+    }
+    const float gend = rec[kPrGend];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      const bool ok = iok && t < n;
+      vr[u] = v[vbase + (ok ? t * vst + ti : 0)];
+      vm |= (uint32_t)ok << u;
+    }
+    {
+      const int cn = min(c + 1, a.nch - 1);
+      kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
+      fetch_frags(cn, lr, lq);
+    }
+    __syncthreads();
+
+    // X = [K; Q] S0^T: three bf16 planes of S, one accumulator per plane
+    f4 XK, XQ;
+    {
+      f4 xk[3], xq[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) xk[p] = xq[p] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const uint4 bs =
+              *reinterpret_cast<const uint4*>(sp + (p * kDS + ti) * SPS + 32 * ks + 8 * lq);
+          xk[p] = mfma_bf16(ak[ks], bs, xk[p]);
+          xq[p] = mfma_bf16(aq[ks], bs, xq[p]);
+        }
+      XK = (xk[0] + xk[1]) + xk[2];
+      XQ = (xq[0] + xq[1]) + xq[2];
+    }
+    load_frags(rec + kPrM, tb, l, mf);
+    // U = V - diag(gam) X_K
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float vu = ((vm >> u) & 1) ? to_f32(vr[u]) : 0.f;
+      sm[L::UB + (tw + 4 * lq + u) * kUBS + ti] = vu - gam[u] * XK[u];
+    }
+    __syncthreads();
+
+    // E = T U; E to the fp32 stage, diag(ks) E as three bf16 planes (row i,
+    // column t)
+    f4 E = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * kUBS + ti], E);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      sm[L::EB + t * kUBS + ti] = E[u];
+      uint32_t p0, p1, p2;
+      split3(ksc[u] * E[u], p0, p1, p2);
+      ep[(0 * kDS + ti) * KTS + t] = (uint16_t)p0;
+      ep[(1 * kDS + ti) * KTS + t] = (uint16_t)p1;
+      ep[(2 * kDS + ti) * KTS + t] = (uint16_t)p2;
+      if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
+    }
+    __syncthreads();
+
+    // Y = diag(gam) X_Q + M E
+    {
+      f4 Yv;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) Yv[u] = gam[u] * XQ[u];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) Yv = mfma(mf[ks], sm[L::EB + rstep(ks, lq) * kUBS + ti], Yv);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        *(iok && t < n ? y + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
+            from_f32<bf16>(Yv[u]);
+      }
+    }
+
+    // S_end = gend S0 + (diag(ks) E)^T K on bf16 MFMA: A = the E planes (row
+    // i = 16 mt + l % 16), B = k^T (row j = 16 (jg + nj) + l % 16)
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj) Sacc[nj] *= gend;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 ae[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        ae[p] = *reinterpret_cast<const uint4*>(ep + (p * kDS + 16 * mt + lr) * KTS + 32 * ks +
+                                                8 * lq);
+#pragma unroll
+      for (int nj = 0; nj < JW; ++nj) {
+        const uint4 bk = *reinterpret_cast<const uint4*>(kt + (16 * (jg + nj) + lr) * KTS +
+                                                         32 * ks + 8 * lq);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) Sacc[nj] = mfma_bf16(ae[p], bk, Sacc[nj]);
+      }
+    }
+    __syncthreads();  // stage reads done before it is rewritten
+    put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink);
+  }
+  if (a.ST != nullptr) {
+    const int l = tid & 63, lr = l & 15, lq = l >> 4;
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj)
 #pragma unroll
@@ -692,14 +982,11 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_kernel(BwdChunkedAr
       sm[DB + (tw + 4 * lq + u) * kUBS + ti] = dyv[u];
     }
     float tf[16], mf[16], suf[4], pre[4], bet[4];
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      tf[ks] = rec[kPbT + (tb * 16 + ks) * 64 + l];
-      mf[ks] = rec[kPbM + (tb * 16 + ks) * 64 + l];
-    }
+    load_frags(rec + kPbT, tb, l, tf);
+    load_frags(rec + kPbM, tb, l, mf);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      suf[u] = rec[kPbSuf + tw + 4 * lq + u];
+      suf[u] = rec[kPbSuf + tw + 4 * lq + u];  // (four consecutive floats each)
       pre[u] = rec[kPbPre + tw + 4 * lq + u];
       bet[u] = rec[kPbBeta + tw + 4 * lq + u];
     }
@@ -800,10 +1087,20 @@ hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_
     constexpr int JT = decltype(jtc)::value;
     constexpr bool V = decltype(vc)::value;
     const size_t lds = sizeof(float) * SL<JT>::SIZE;
-    if constexpr (BWD)
+    if constexpr (BWD) {
       return launch(bwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
-    else
+    } else {
+      // bf16 k, q in 8-element groups: the bf16-product kernel
+      if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
+        if (Dk % 8 == 0) {
+          const size_t lb = sizeof(float) * SLB<JT>::SIZE;
+          // the save buffer holds both the checkpoints and the residuals
+          if (A.s.Sck != nullptr)
+            return launch(fwd_chunked_bf16_kernel<JT, true>, grid, kSwThreads, lb, s, A);
+          return launch(fwd_chunked_bf16_kernel<JT, false>, grid, kSwThreads, lb, s, A);
+        }
       return launch(fwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
+    }
   };
   using I4 = std::integral_constant<int, 4>;
   using I8 = std::integral_constant<int, 8>;

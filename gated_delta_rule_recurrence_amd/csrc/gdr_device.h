@@ -105,6 +105,35 @@ __device__ __forceinline__ f4 mfma(float a, float b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// D = A B + C on one 16x16 tile with k = 32, bf16 operands, fp32 accumulate:
+// lane l supplies A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16]
+// for e = 0..7 (eight bf16 bit patterns, element e in bits 16e..16e+15 of
+// the 128-bit operand); C and D as for mfma().  Products of two bf16 values
+// are exact in fp32.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f4 mfma_bf16(uint4 a, uint4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// bf16 bit pattern of x, round to nearest even (finite x).
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x = hi + mid + lo with three bf16 values (each rounded to nearest even from
+// the remainder; the two remainders are exact in fp32).  The three 8-bit
+// significands cover fp32's 24, so the sum reproduces x (away from the
+// bottom of the exponent range), and products of the pieces with a bf16
+// value are exact: three bf16 MFMAs give an fp32-accurate product.
+__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_bits(x);
+  const float r = x - __uint_as_float(hi << 16);
+  mid = bf16_bits(r);
+  lo = bf16_bits(r - __uint_as_float(mid << 16));
+}
+
 // DPP move with 1.0 in the lanes that get no source (the product identity).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_or1(float x) {

@@ -82,9 +82,10 @@ struct ChunkedSweepShape {
   const void* beta;
 };
 
-// Floats per prep record: two [64][64] matrices in MFMA A-fragment order
-// and three per-step vectors of 64.
-constexpr int kChunkPrepStride = 2 * 64 * 64 + 3 * 64;
+// Floats per prep record: two [64][64] matrices in MFMA A-fragment order,
+// three per-step vectors of 64 and 64 floats that nothing reads (a store
+// target for lanes outside the tensors).
+constexpr int kChunkPrepStride = 2 * 64 * 64 + 4 * 64;
 
 // Whether the chunked sweeps take this shape, and the floats of their prep
 // records.

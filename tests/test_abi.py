@@ -110,7 +110,7 @@ def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
     # whole forward workspace, and a region after the backward's per-step
     # vectors
     chunked = Dk <= 192 and C >= 16 and T >= C
-    prep = B * Hv * nch * (2 * 64 * 64 + 3 * 64) * 4 if chunked else 0
+    prep = B * Hv * nch * (2 * 64 * 64 + 4 * 64) * 4 if chunked else 0
     assert _lib.forward_workspace_bytes(sh) == prep
     bwd = _round256(states) + rows
     assert _lib.backward_workspace_bytes(sh) == (_round256(bwd) + prep if chunked else bwd)
