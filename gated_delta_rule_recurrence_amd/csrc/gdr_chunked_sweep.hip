@@ -77,18 +77,35 @@ constexpr int kPbT = 0, kPbM = 4096, kPbSuf = 8192, kPbPre = 8256, kPbBeta = 832
 constexpr int kPrSink = 8384;
 static_assert(kPbBeta + kN <= kPrSink && kPrSink + 64 <= kChunkPrepStride, "record");
 
-// Element (t, r) of a [64][64] matrix in MFMA A-fragment order: k-step
-// 16 (t / 16) + ks with rstep(ks, lq) = r, lane (t % 16) + 16 lq; one
-// k-step of a tile is 64 consecutive floats (one fully coalesced load).
-__device__ __forceinline__ int frag_index(int t, int r) {
-  return ((t >> 4) * 16 + 4 * (r >> 4) + (r & 3)) * 64 + (t & 15) + 16 * ((r >> 2) & 3);
-}
-
-// The 16 A operands of a lane's tile tb from a record matrix (frag_index order).
+// A [64][64] record matrix in MFMA A-fragment order: the A operand of k-step
+// ks (k index rstep(ks, lq)) of the 16 x 16 tile of rows 16 tb.. sits in
+// lane (t % 16) + 16 lq; each group of four k-steps is one 16-byte block per
+// lane, the 64 lanes' blocks consecutive, so a lane loads its 16 operands
+// with four fully coalesced 16-byte loads.  Block (tb, x) starts at float
+// ((tb * 4 + x) * 64 + lane) * 4.
 __device__ __forceinline__ void load_frags(const float* __restrict__ m, int tb, int l,
                                            float (&f)[16]) {
 #pragma unroll
-  for (int ks = 0; ks < 16; ++ks) f[ks] = m[(tb * 16 + ks) * 64 + l];
+  for (int x = 0; x < 4; ++x) {
+    const f4 v = *reinterpret_cast<const f4*>(m + ((tb * 4 + x) * 64 + l) * 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[4 * x + e] = v[e];
+  }
+}
+
+// Writes a matrix held in LDS (element (t, r) at src[t * ld + r]) to a record
+// in the order above; lane l writes block (tb, x) of itself.
+__device__ __forceinline__ void store_frags(const float* src, int ld, float* __restrict__ m,
+                                            int l) {
+  const int lr = l & 15, lq = l >> 4;
+#pragma unroll 4
+  for (int bx = 0; bx < 16; ++bx) {
+    const int tb = bx >> 2, x = bx & 3, t = 16 * tb + lr;
+    f4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = src[t * ld + rstep(4 * x + e, lq)];
+    *reinterpret_cast<f4*>(m + (bx * 64 + l) * 4) = v;
+  }
 }
 
 // ---------------------------------------------------------------- prep ----
@@ -222,14 +239,17 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     float x[kN];
     if constexpr (!BWD) {
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
-#pragma unroll 1
-      for (int wt = 0; wt < 4; ++wt)
-#pragma unroll 4
-        for (int ks = 0; ks < 16; ++ks) {
-          const int t = 16 * wt + lr, s = rstep(ks, lq);
-          const float m = s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
-          rec[kPrM + (wt * 16 + ks) * 64 + l] = m;  // = frag_index(t, s)
+#pragma unroll 2
+      for (int bx = 0; bx < 16; ++bx) {
+        const int t = 16 * (bx >> 2) + lr;
+        f4 m4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = rstep(4 * (bx & 3) + e, lq);
+          m4[e] = s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
         }
+        *reinterpret_cast<f4*>(rec + kPrM + (bx * 64 + l) * 4) = m4;
+      }
       // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
       for (int t = 1; t < kN; ++t)
         if (l < t) G[t * kGP + l] = G[l * kGP + t] * KK[t * kNP + l] * bl;
@@ -248,21 +268,26 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         }
         x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
+      // T to the record through LDS (G is free now): column l of T is x
 #pragma unroll
-      for (int t = 0; t < kN; ++t) rec[kPrT + frag_index(t, l)] = x[t];
+      for (int t = 0; t < kN; ++t) G[t * kGP + l] = x[t];
+      store_frags(G, kGP, rec + kPrT, l);
       rec[kPrGam + l] = pre;
       rec[kPrKs + l] = bl * suf;
       if (l == n - 1) rec[kPrGend] = pre;
     } else {
       // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
-#pragma unroll 1
-      for (int wt = 0; wt < 4; ++wt)
-#pragma unroll 4
-        for (int ks = 0; ks < 16; ++ks) {
-          const int t = 16 * wt + lr, s = rstep(ks, lq);
-          const float m = s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
-          rec[kPbM + (wt * 16 + ks) * 64 + l] = m;  // = frag_index(t, s)
+#pragma unroll 2
+      for (int bx = 0; bx < 16; ++bx) {
+        const int t = 16 * (bx >> 2) + lr;
+        f4 m4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int s = rstep(4 * (bx & 3) + e, lq);
+          m4[e] = s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
         }
+        *reinterpret_cast<f4*>(rec + kPbM + (bx * 64 + l) * 4) = m4;
+      }
       // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
       // diagonal (lane l <-> s)
       for (int t = 0; t < kN - 1; ++t)
@@ -281,8 +306,10 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         }
         x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
       }
+      // Tb to the record through LDS: column l of Tb is x
 #pragma unroll
-      for (int t = 0; t < kN; ++t) rec[kPbT + frag_index(t, l)] = x[t];
+      for (int t = 0; t < kN; ++t) G[t * kGP + l] = x[t];
+      store_frags(G, kGP, rec + kPbT, l);
       rec[kPbSuf + l] = suf;
       rec[kPbPre + l] = pre;
       rec[kPbBeta + l] = bl;
@@ -300,27 +327,25 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
 // The k, q rows of a chunk: fetched into registers a chunk ahead (raw bits,
 // masked where deposited), then deposited into the natural-layout LDS stages
 // [kN][KLD] with zero padding columns.
-template <typename TIn, int JT, bool VEC>
+template <typename TIn, int JT, bool VEC, int NTH = kSwThreads>
 struct KQPrefetch {
   static constexpr int DKP = 16 * JT, KLD = DKP + 4;
   static constexpr int NQT = kN * DKP / 4;  // 4-column quads of one chunk
-  static constexpr int NQ = NQT / kSwThreads;
-  static_assert(NQT % kSwThreads == 0 && 4 * NQ <= 32, "quads per thread");
-  uint32_t pm = 0;
+  static constexpr int NQ = NQT / NTH;
+  static_assert(NQT % NTH == 0 && 4 * NQ <= 64, "quads per thread");
+  uint64_t pm = 0;
   Quad<TIn, VEC> pk[NQ], pq[NQ];
   int tid;
 
   // quad u of this thread: step qt(u), columns qj(u) .. qj(u) + 3 (recomputed
   // where used rather than held in registers)
-  __device__ __forceinline__ int qt(int u) const { return (tid + kSwThreads * u) / (DKP / 4); }
-  __device__ __forceinline__ int qj(int u) const {
-    return 4 * ((tid + kSwThreads * u) % (DKP / 4));
-  }
+  __device__ __forceinline__ int qt(int u) const { return (tid + NTH * u) / (DKP / 4); }
+  __device__ __forceinline__ int qj(int u) const { return 4 * ((tid + NTH * u) % (DKP / 4)); }
   __device__ __forceinline__ void init(int t) { tid = t; }
   // rows t0 .. t0 + n - 1; base = element (t0, kv head, 0); kst = row stride
   __device__ __forceinline__ void fetch(const TIn* __restrict__ k, const TIn* __restrict__ q,
                                         int64_t base, int n, int kst, int Dk) {
-    uint32_t m = 0;
+    uint64_t m = 0;
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int t = qt(u), j = qj(u);
@@ -328,14 +353,14 @@ struct KQPrefetch {
       const int o = ok ? t * kst + j : 0;
       pk[u].load(k + base, o, ok, Dk - j);
       pq[u].load(q + base, o, ok, Dk - j);
-      m |= Quad<TIn, VEC>::mask(ok, Dk - j) << (4 * u);
+      m |= (uint64_t)Quad<TIn, VEC>::mask(ok, Dk - j) << (4 * u);
     }
     pm = m;
   }
   __device__ __forceinline__ void deposit(float* kl, float* ql) const {
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const uint32_t mu = (pm >> (4 * u)) & 15u;
+      const uint32_t mu = (uint32_t)(pm >> (4 * u)) & 15u;
       const int o = qt(u) * KLD + qj(u);
       *reinterpret_cast<f4*>(kl + o) = pk[u].get(mu);
       *reinterpret_cast<f4*>(ql + o) = pq[u].get(mu);
@@ -633,17 +658,21 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
 // quarter-wave (16 rows, one 16-byte column group) hit distinct banks.  The
 // k and q operands of [K; Q] S^T (16 steps x Dk per wave) come straight from
 // HBM as 16-byte fragments, fetched a chunk ahead.
-template <int JT>
+template <int JT, int RS>
 struct SLB {
   static constexpr int DKP = 16 * JT;
+  static constexpr int UBS = RS + 4;               // row stride of the U, E stages
   static constexpr int KTS = kN + 8;              // bf16 row stride of k^T and E pieces
   static constexpr int SPS = DKP + 8;             // bf16 row stride of the state planes
   static constexpr int KT = 0;                    // float offsets below
   static constexpr int SP = KT + DKP * KTS / 2;
-  static constexpr int EP = SP + 3 * kDS * SPS / 2;
-  static constexpr int UB = EP + 3 * kDS * KTS / 2;
-  static constexpr int EB = UB + kN * kUBS;
-  static constexpr int SIZE = EB + kN * kUBS;
+  static constexpr int EP = SP + 3 * RS * SPS / 2;
+  static constexpr int UB = EP + 3 * RS * KTS / 2;
+  static constexpr int EB = UB + kN * UBS;
+  static constexpr int SIZE = EB + kN * UBS;
+  // the step-permuted reads of U, E hit distinct banks when 4 UBS is 16
+  // modulo 64 (as UBS above)
+  static_assert((4 * UBS) % 64 == 16, "U, E row stride");
   // an odd number of 16-byte units per row: 16 consecutive rows at one
   // column group fall in 16 distinct 16-byte bank groups
   static_assert((2 * KTS) % 32 == 16 && (2 * SPS) % 32 == 16, "row strides");
@@ -651,9 +680,14 @@ struct SLB {
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
-template <int JT, bool SAVE>
-__global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
-  using L = SLB<JT>;
+// RS state rows per workgroup (16 or 32) with 4 RS / 16 waves; at RS = 16 a
+// workgroup needs 64 KB of LDS, so two share a CU and each hides the other's
+// barrier and memory waits.
+template <int JT, int RS, bool SAVE>
+__global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
+  using L = SLB<JT, RS>;
+  constexpr int NTH = RS * 16, NT = RS / 16;  // threads; row tiles
+  constexpr int UBS = L::UBS;
   constexpr int DKP = L::DKP, KTS = L::KTS, SPS = L::SPS;
   constexpr int NKS = DKP / 32;  // k-steps of 32 over Dk
   constexpr int JW = JT / 4;
@@ -668,12 +702,12 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   const bf16* __restrict__ v = static_cast<const bf16*>(a.v);
   bf16* __restrict__ y = static_cast<bf16*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const int i0 = blockIdx.x * RS, h = blockIdx.y, b = blockIdx.z;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tb = w & 3, nt = w >> 2;
-  const int mt = w & 1, jg = JW * (w >> 1);
+  const int mt = w % NT, jg = JW * (w / NT);
   const int tw = 16 * tb;
   const int64_t bh = (int64_t)b * Hv + h;
   const int64_t mat = (int64_t)Dv * Dk;
@@ -682,7 +716,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   auto chunk_len = [&](int c) { return min(a.L, T - c * a.L); };
 
   // k quads of a chunk (for k^T in LDS), a chunk ahead
-  KQPrefetch<bf16, JT, true> kq;
+  KQPrefetch<bf16, JT, true, NTH> kq;
   kq.init(tid);
   // this wave's [K; Q] fragments: row tw + l % 16, columns 32 ks + 8 (l / 16)
   // .. +7 of the chunk, a chunk ahead (raw bits; rows past the chunk and
@@ -727,9 +761,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
         uint32_t p0, p1, p2;
         split3(Sacc[nj][u], p0, p1, p2);
-        sp[(0 * kDS + i) * SPS + j] = (uint16_t)p0;
-        sp[(1 * kDS + i) * SPS + j] = (uint16_t)p1;
-        sp[(2 * kDS + i) * SPS + j] = (uint16_t)p2;
+        sp[(0 * RS + i) * SPS + j] = (uint16_t)p0;
+        sp[(1 * RS + i) * SPS + j] = (uint16_t)p1;
+        sp[(2 * RS + i) * SPS + j] = (uint16_t)p2;
         if (SAVE) {
           const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
           *(ok ? ck + (int64_t)(i0 + i) * Dk + j : sink) = Sacc[nj][u];
@@ -756,8 +790,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
     // k^T of this chunk from the quads fetched a chunk ago (zero padded)
 #pragma unroll
-    for (int u = 0; u < KQPrefetch<bf16, JT, true>::NQ; ++u) {
-      const uint32_t mu = (kq.pm >> (4 * u)) & 15u;
+    for (int u = 0; u < KQPrefetch<bf16, JT, true, NTH>::NQ; ++u) {
+      const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
       const uint2 raw = kq.pk[u].v;
       const int t = kq.qt(u), j = kq.qj(u);
       kt[(j + 0) * KTS + t] = mu ? (uint16_t)(raw.x & 0xffffu) : 0;
@@ -813,7 +847,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
           const uint4 bs =
-              *reinterpret_cast<const uint4*>(sp + (p * kDS + ti) * SPS + 32 * ks + 8 * lq);
+              *reinterpret_cast<const uint4*>(sp + (p * RS + ti) * SPS + 32 * ks + 8 * lq);
           xk[p] = mfma_bf16(ak[ks], bs, xk[p]);
           xq[p] = mfma_bf16(aq[ks], bs, xq[p]);
         }
@@ -825,7 +859,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float vu = ((vm >> u) & 1) ? to_f32(vr[u]) : 0.f;
-      sm[L::UB + (tw + 4 * lq + u) * kUBS + ti] = vu - gam[u] * XK[u];
+      sm[L::UB + (tw + 4 * lq + u) * UBS + ti] = vu - gam[u] * XK[u];
     }
     __syncthreads();
 
@@ -833,16 +867,16 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     // column t)
     f4 E = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * kUBS + ti], E);
+    for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * UBS + ti], E);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = tw + 4 * lq + u;
-      sm[L::EB + t * kUBS + ti] = E[u];
+      sm[L::EB + t * UBS + ti] = E[u];
       uint32_t p0, p1, p2;
       split3(ksc[u] * E[u], p0, p1, p2);
-      ep[(0 * kDS + ti) * KTS + t] = (uint16_t)p0;
-      ep[(1 * kDS + ti) * KTS + t] = (uint16_t)p1;
-      ep[(2 * kDS + ti) * KTS + t] = (uint16_t)p2;
+      ep[(0 * RS + ti) * KTS + t] = (uint16_t)p0;
+      ep[(1 * RS + ti) * KTS + t] = (uint16_t)p1;
+      ep[(2 * RS + ti) * KTS + t] = (uint16_t)p2;
       if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
     }
     __syncthreads();
@@ -853,7 +887,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
       for (int u = 0; u < 4; ++u) Yv[u] = gam[u] * XQ[u];
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) Yv = mfma(mf[ks], sm[L::EB + rstep(ks, lq) * kUBS + ti], Yv);
+      for (int ks = 0; ks < 16; ++ks) Yv = mfma(mf[ks], sm[L::EB + rstep(ks, lq) * UBS + ti], Yv);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
@@ -871,7 +905,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       uint4 ae[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-        ae[p] = *reinterpret_cast<const uint4*>(ep + (p * kDS + 16 * mt + lr) * KTS + 32 * ks +
+        ae[p] = *reinterpret_cast<const uint4*>(ep + (p * RS + 16 * mt + lr) * KTS + 32 * ks +
                                                 8 * lq);
 #pragma unroll
       for (int nj = 0; nj < JW; ++nj) {
@@ -1093,11 +1127,13 @@ hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_
       // bf16 k, q in 8-element groups: the bf16-product kernel
       if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
         if (Dk % 8 == 0) {
-          const size_t lb = sizeof(float) * SLB<JT>::SIZE;
+          constexpr int RS = 32;  // (16 fits two workgroups per CU but measured slower)
+          const dim3 g16((Dv + RS - 1) / RS, Hv, B);
+          const size_t lb = sizeof(float) * SLB<JT, RS>::SIZE;
           // the save buffer holds both the checkpoints and the residuals
           if (A.s.Sck != nullptr)
-            return launch(fwd_chunked_bf16_kernel<JT, true>, grid, kSwThreads, lb, s, A);
-          return launch(fwd_chunked_bf16_kernel<JT, false>, grid, kSwThreads, lb, s, A);
+            return launch(fwd_chunked_bf16_kernel<JT, RS, true>, g16, 16 * RS, lb, s, A);
+          return launch(fwd_chunked_bf16_kernel<JT, RS, false>, g16, 16 * RS, lb, s, A);
         }
       return launch(fwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
     }
