@@ -33,8 +33,8 @@ FLOPS_BWD = 15                 # per state element per step (reverse sweep)
 # by a plain-copy calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).
 # They describe the kernels built from sources with this digest and are not
 # reported otherwise.
-BWD_TRAFFIC = {"sources_sha256_16": "9604a0c70f624ad9",
-               "read_bytes": 1550.0e6, "write_bytes": 404.3e6}
+BWD_TRAFFIC = {"sources_sha256_16": "2d8d11ccde53736d",
+               "read_bytes": 1549.5e6, "write_bytes": 404.8e6}
 BWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
                "gdr_chunk.hip")
 
