@@ -1094,6 +1094,329 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_kernel(BwdChunkedAr
   }
 }
 
+// -------------------------------------------- reverse sweep, bf16 inputs ----
+// The same reverse sweep for bf16 k, q, dy (Dk a multiple of 8), with the
+// products that have k or q as an operand on bf16 MFMA, the fp32 operand
+// split exactly into three bf16 pieces (as in fwd_chunked_bf16_kernel):
+// K H^T, and the update DY^T diag(pre) Q - C^T diag(beta pre) K.  Mq DY and
+// Tb U stay on fp32 MFMA.
+//
+// Operands whose reduction index is the step t or the column j reach the
+// MFMA through transposing LDS reads (lds_read_tr16) from tiles stored as
+// they are produced: k and q row-major [t][j] as loaded, the gradient pieces
+// j-major [j][i] from the accumulator layout (four consecutive rows i per
+// lane).  Both are written in 8-byte blocks whose position inside the row is
+// XOR-swizzled so that the blocks one instruction writes or reads fall on
+// distinct LDS banks.
+template <int JT>
+struct SLR {
+  static constexpr int DKP = 16 * JT;
+  // k, q row stride: an odd multiple of 128 bytes, so rows of opposite
+  // parity use opposite halves of the banks
+  static constexpr int KRS = DKP % 128 == 0 ? DKP + 64 : DKP;
+  static constexpr int KTS = kN + 8;  // bf16 row stride of the step pieces [i][t]
+  static constexpr int KR = 0;        // float offsets below
+  static constexpr int QR = KR + kN * KRS / 2;
+  static constexpr int HT = QR + kN * KRS / 2;         // gradient pieces [3][DKP][kDS]
+  static constexpr int DPP = HT + 3 * DKP * kDS / 2;   // diag(pre) DY pieces [3][kDS][KTS]
+  static constexpr int CPP = DPP + 3 * kDS * KTS / 2;  // -diag(beta pre) C pieces
+  static constexpr int DB = CPP + 3 * kDS * KTS / 2;   // dy fp32 [kN][kUBS]
+  static constexpr int UB = DB + kN * kUBS;            // U fp32 [kN][kUBS]
+  static constexpr int SIZE = UB + kN * kUBS;
+  static_assert((2 * KRS) % 256 == 128, "k, q row stride");
+  static_assert((2 * KTS) % 32 == 16, "step-piece row stride");
+  static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
+  static_assert(QR % 4 == 0 && HT % 4 == 0 && DPP % 4 == 0 && CPP % 4 == 0 && DB % 4 == 0,
+                "alignment");
+  static_assert(SIZE * 4 <= 160 * 1024, "LDS");
+  // 4-element block c of k, q row t is stored at block c ^ kq_swz(t)
+  __device__ static __forceinline__ int kq_swz(int t) {
+    return (((t >> 1) & 1) << 2) | (((t >> 3) & 1) << 3);
+  }
+  // block c (of 8) of gradient-piece row j is stored at block c ^ h_swz(j)
+  __device__ static __forceinline__ int h_swz(int j) { return (j >> 1) & 6; }
+};
+
+template <int JT>
+__global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChunkedArgs A) {
+  using L = SLR<JT>;
+  constexpr int DKP = L::DKP, KRS = L::KRS, KTS = L::KTS;
+  constexpr int NKS = DKP / 32;
+  constexpr int JW = JT / 4;
+  static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
+  extern __shared__ __align__(16) float sm[];
+  uint16_t* const kr = reinterpret_cast<uint16_t*>(sm + L::KR);
+  uint16_t* const qr = reinterpret_cast<uint16_t*>(sm + L::QR);
+  uint16_t* const ht = reinterpret_cast<uint16_t*>(sm + L::HT);
+  uint16_t* const dpp = reinterpret_cast<uint16_t*>(sm + L::DPP);
+  uint16_t* const cpp = reinterpret_cast<uint16_t*>(sm + L::CPP);
+  const BwdSweepArgs& a = A.s;
+  const bf16* __restrict__ q = static_cast<const bf16*>(a.q);
+  const bf16* __restrict__ k = static_cast<const bf16*>(a.k);
+  const bf16* __restrict__ dy = static_cast<const bf16*>(a.dy);
+  bf16* __restrict__ dv = static_cast<bf16*>(a.dv);
+  const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
+  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const int hk = h / (Hv / Hk);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tb = w & 3, nt = w >> 2;
+  const int mt = w & 1, jg = JW * (w >> 1);
+  const int tw = 16 * tb;
+  const int64_t bh = (int64_t)b * Hv + h;
+  const int64_t mat = (int64_t)Dv * Dk;
+  const int kst = Hk * Dk, vst = Hv * Dv;
+  auto kq_base = [&](int c) { return ((int64_t)b * T + c * a.L) * kst + (int64_t)hk * Dk; };
+  auto v_base = [&](int c) { return ((int64_t)b * T + c * a.L) * vst + (int64_t)h * Dv + i0; };
+  auto chunk_len = [&](int c) { return min(a.L, T - c * a.L); };
+
+  KQPrefetch<bf16, JT, true> kq;
+  kq.init(tid);
+  // this wave's K fragments (row tw + l % 16, columns 32 ks + 8 (l / 16)..),
+  // a chunk ahead
+  uint4 kf[NKS];
+  auto fetch_frags = [&](int c, int lr, int lq) __attribute__((always_inline)) {
+    const int64_t base = kq_base(c);
+    const bool rok = tw + lr < chunk_len(c);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int j = 32 * ks + 8 * lq;
+      int o = rok && j < Dk ? (tw + lr) * kst + j : 0;
+      asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
+      kf[ks] = *reinterpret_cast<const uint4*>(k + base + o);
+    }
+  };
+  // dy of this wave's tile (step tw + 4 lq + u, row i0 + ti), a chunk ahead
+  bf16 dr[4];
+  uint32_t dm = 0;
+  auto fetch_dy = [&](int c, int lq, int ti, bool iok) __attribute__((always_inline)) {
+    const int n = chunk_len(c);
+    const int64_t base = v_base(c);
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      const bool ok = iok && t < n;
+      dr[u] = dy[base + (ok ? t * vst + ti : 0)];
+      m |= (uint32_t)ok << u;
+    }
+    dm = m;
+  };
+
+  f4 Hacc[JW];
+  const int cl = a.nch - 1;
+  {
+    const int l = tid & 63, lr = l & 15, lq = l >> 4;
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        const bool ok = a.dST != nullptr && i0 + i < Dv && j < Dk;
+        Hacc[nj][u] = ok ? a.dST[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
+      }
+    kq.fetch(k, q, kq_base(cl), chunk_len(cl), kst, Dk);
+    fetch_frags(cl, lr, lq);
+    fetch_dy(cl, lq, 16 * nt + lr, i0 + 16 * nt + lr < Dv);
+  }
+  // gradient tiles into the three j-major bf16 pieces and into checkpoint
+  // slot `slot` (slot < 0: the sink; out-of-range lanes store to the sink too)
+  auto put_grad = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
+    float* __restrict__ hc = a.Hck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat;
+    asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj) {
+      const int j = 16 * (jg + nj) + lr;
+      uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u;
+        split3(Hacc[nj][u], p0[u], p1[u], p2[u]);
+        const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
+        *(ok ? hc + (int64_t)(i0 + i) * Dk + j : sink) = Hacc[nj][u];
+      }
+      const int o = j * kDS + 4 * ((4 * mt + lq) ^ L::h_swz(j));
+      *reinterpret_cast<uint2*>(ht + 0 * DKP * kDS + o) = pack4(p0);
+      *reinterpret_cast<uint2*>(ht + 1 * DKP * kDS + o) = pack4(p1);
+      *reinterpret_cast<uint2*>(ht + 2 * DKP * kDS + o) = pack4(p2);
+    }
+  };
+  {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    put_grad(cl, tl & 15, (tl & 63) >> 4, A.prep + kPrSink + (tl & 63));
+  }
+
+  for (int c = cl; c >= 0; --c) {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    kq.tid = tl;
+    const int l = tl & 63, lr = l & 15, lq = l >> 4;
+    const int ti = 16 * nt + lr;
+    const bool iok = i0 + ti < Dv;
+    const int n = chunk_len(c);
+    const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
+    float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
+    const int64_t vbase = v_base(c);
+    // k, q of this chunk row-major (zero padded) from the quads fetched a
+    // chunk ago
+#pragma unroll
+    for (int u = 0; u < KQPrefetch<bf16, JT, true>::NQ; ++u) {
+      const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
+      const int t = kq.qt(u), cb = kq.qj(u) >> 2;
+      const int o = t * KRS + 4 * (cb ^ L::kq_swz(t));
+      uint2 rk = kq.pk[u].v, rq = kq.pq[u].v;
+      rk.x = mu ? rk.x : 0u;
+      rk.y = mu ? rk.y : 0u;
+      rq.x = mu ? rq.x : 0u;
+      rq.y = mu ? rq.y : 0u;
+      *reinterpret_cast<uint2*>(kr + o) = rk;
+      *reinterpret_cast<uint2*>(qr + o) = rq;
+    }
+    uint4 ak[NKS];
+    {
+      const bool rok = tw + lr < n;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        // component selects: a select of the whole vector would go through memory
+        const bool ok = rok && 32 * ks + 8 * lq < Dk;
+        ak[ks].x = ok ? kf[ks].x : 0u;
+        ak[ks].y = ok ? kf[ks].y : 0u;
+        ak[ks].z = ok ? kf[ks].z : 0u;
+        ak[ks].w = ok ? kf[ks].w : 0u;
+      }
+    }
+    float dyv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      dyv[u] = ((dm >> u) & 1) ? to_f32(dr[u]) : 0.f;
+      sm[L::DB + (tw + 4 * lq + u) * kUBS + ti] = dyv[u];
+    }
+    float tf[16], mf[16], suf[4], pre[4], bet[4];
+    load_frags(rec + kPbT, tb, l, tf);
+    load_frags(rec + kPbM, tb, l, mf);
+    {
+      const f4 s4 = *reinterpret_cast<const f4*>(rec + kPbSuf + tw + 4 * lq);
+      const f4 p4 = *reinterpret_cast<const f4*>(rec + kPbPre + tw + 4 * lq);
+      const f4 b4 = *reinterpret_cast<const f4*>(rec + kPbBeta + tw + 4 * lq);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) suf[u] = s4[u], pre[u] = p4[u], bet[u] = b4[u];
+    }
+    const float pend = rec[kPbPre + n - 1];
+    {
+      const int cn = max(c - 1, 0);
+      kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
+      fetch_frags(cn, lr, lq);
+      fetch_dy(cn, lq, ti, iok);
+    }
+    __syncthreads();
+
+    // X = K Hend^T: three bf16 pieces of H, one accumulator per piece
+    f4 X;
+    {
+      f4 x3[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) x3[p] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int jl = 32 * ks + 8 * lq + (lr >> 2), jh = jl + 4;
+        const int cb = 4 * nt + (lr & 3);
+        const int ol = jl * kDS + 4 * (cb ^ L::h_swz(jl));
+        const int oh = jh * kDS + 4 * (cb ^ L::h_swz(jh));
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          const uint2 lo = lds_read_tr16(ht + p * DKP * kDS + ol);
+          const uint2 hi = lds_read_tr16(ht + p * DKP * kDS + oh);
+          x3[p] = mfma_bf16(ak[ks], uint4{lo.x, lo.y, hi.x, hi.y}, x3[p]);
+        }
+      }
+      X = (x3[0] + x3[1]) + x3[2];
+    }
+    // U = diag(suf) X + Mq DY; diag(pre) DY as three bf16 pieces [i][t]
+    {
+      f4 U;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) U[u] = suf[u] * X[u];
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) U = mfma(mf[ks], sm[L::DB + rstep(ks, lq) * kUBS + ti], U);
+      uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        sm[L::UB + (tw + 4 * lq + u) * kUBS + ti] = U[u];
+        split3(pre[u] * dyv[u], p0[u], p1[u], p2[u]);
+      }
+      const int o = ti * KTS + tw + 4 * lq;
+      *reinterpret_cast<uint2*>(dpp + 0 * kDS * KTS + o) = pack4(p0);
+      *reinterpret_cast<uint2*>(dpp + 1 * kDS * KTS + o) = pack4(p1);
+      *reinterpret_cast<uint2*>(dpp + 2 * kDS * KTS + o) = pack4(p2);
+    }
+    __syncthreads();
+
+    // C = Tb U; dv = diag(beta) C; -diag(beta pre) C as three bf16 pieces
+    {
+      f4 Cv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) Cv = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * kUBS + ti], Cv);
+      uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        split3(-(bet[u] * pre[u]) * Cv[u], p0[u], p1[u], p2[u]);
+        const bool ok = iok && t < n;
+        *(ok ? a.C + vbase + t * vst + ti : sink) = Cv[u];
+        *(ok ? dv + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
+            from_f32<bf16>(bet[u] * Cv[u]);
+      }
+      const int o = ti * KTS + tw + 4 * lq;
+      *reinterpret_cast<uint2*>(cpp + 0 * kDS * KTS + o) = pack4(p0);
+      *reinterpret_cast<uint2*>(cpp + 1 * kDS * KTS + o) = pack4(p1);
+      *reinterpret_cast<uint2*>(cpp + 2 * kDS * KTS + o) = pack4(p2);
+    }
+    __syncthreads();
+
+    // H_start = pre_{n-1} Hend + (diag(pre) DY)^T Q + (-diag(beta pre) C)^T K
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj) Hacc[nj] *= pend;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      uint4 ad[3], ac[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const int o = (p * kDS + 16 * mt + lr) * KTS + 32 * ks + 8 * lq;
+        ad[p] = *reinterpret_cast<const uint4*>(dpp + o);
+        ac[p] = *reinterpret_cast<const uint4*>(cpp + o);
+      }
+      const int tl0 = 32 * ks + 8 * lq + (lr >> 2), th0 = tl0 + 4;
+#pragma unroll
+      for (int nj = 0; nj < JW; ++nj) {
+        const int cb = 4 * (jg + nj) + (lr & 3);
+        const int ol = tl0 * KRS + 4 * (cb ^ L::kq_swz(tl0));
+        const int oh = th0 * KRS + 4 * (cb ^ L::kq_swz(th0));
+        const uint2 ql = lds_read_tr16(qr + ol), qh = lds_read_tr16(qr + oh);
+        const uint2 kl = lds_read_tr16(kr + ol), kh = lds_read_tr16(kr + oh);
+        const uint4 bq = {ql.x, ql.y, qh.x, qh.y}, bk = {kl.x, kl.y, kh.x, kh.y};
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          Hacc[nj] = mfma_bf16(ad[p], bq, Hacc[nj]);
+          Hacc[nj] = mfma_bf16(ac[p], bk, Hacc[nj]);
+        }
+      }
+    }
+    __syncthreads();  // stage reads done before it is rewritten
+    put_grad(c - 1, lr, lq, sink);
+  }
+  if (a.dS0 != nullptr) {
+    const int l = tid & 63, lr = l & 15, lq = l >> 4;
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
+        if (i0 + i < Dv && j < Dk) a.dS0[bh * mat + (int64_t)(i0 + i) * Dk + j] = Hacc[nj][u];
+      }
+  }
+}
+
 // ------------------------------------------------------------ launches ----
 template <typename Kern, typename... Args>
 hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
@@ -1122,6 +1445,10 @@ hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_
     constexpr bool V = decltype(vc)::value;
     const size_t lds = sizeof(float) * SL<JT>::SIZE;
     if constexpr (BWD) {
+      if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
+        if (Dk % 8 == 0)
+          return launch(bwd_chunked_bf16_kernel<JT>, grid, kSwThreads,
+                        sizeof(float) * SLR<JT>::SIZE, s, A);
       return launch(bwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
     } else {
       // bf16 k, q in 8-element groups: the bf16-product kernel

@@ -134,6 +134,25 @@ __device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uin
   lo = bf16_bits(r - __uint_as_float(mid << 16));
 }
 
+// Four bf16 bit patterns packed as a 64-bit LDS block (element e in bits
+// 16e .. 16e + 15 of the pair).
+__device__ __forceinline__ uint2 pack4(const uint32_t (&x)[4]) {
+  return uint2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
+}
+
+// ds_read_b64_tr_b16: each lane names an 8-byte block of four bf16; inside
+// every group of 16 lanes, lane i receives element i % 4 of the blocks named
+// by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4, in that order.  When
+// lane s of group G names row k0 + 8 G + s / 4, columns n0 + 4 (s % 4) .. +3
+// of a [k][n] tile, lane l receives rows k0 + 8 G + 0..3 of column
+// n0 + l % 16: half of an MFMA 16x16x32 bf16 operand (rows 4..7 from a
+// second read 4 rows further on).
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
+}
+
 // DPP move with 1.0 in the lanes that get no source (the product identity).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_or1(float x) {
