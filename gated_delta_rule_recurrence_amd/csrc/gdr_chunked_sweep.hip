@@ -642,6 +642,70 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
   }
 }
 
+// ------------------------------------------- bf16 operand tiles in LDS ----
+// Operands whose reduction index is the step t or the column j reach the
+// bf16 MFMA through transposing LDS reads (lds_read_tr16) from tiles stored
+// as they are produced: k (and q) row-major [t][j] as loaded, state or
+// gradient pieces j-major [j][i] from the accumulator layout (four
+// consecutive rows i per lane).  Both are written in 8-byte blocks whose
+// place inside the row is XOR-swizzled, so that the blocks one instruction
+// writes or reads fall on distinct banks (64 banks of 4 bytes, a half-wave
+// per cycle).
+//
+// k, q row stride: an odd multiple of 128 bytes, so rows of opposite parity
+// use opposite halves of the banks.
+constexpr int kq_row_stride(int dkp) { return dkp % 128 == 0 ? dkp + 64 : dkp; }
+// 4-element block c of k, q row t is stored at block c ^ kq_swz(t)
+__device__ __forceinline__ int kq_swz(int t) {
+  return (((t >> 1) & 1) << 2) | (((t >> 3) & 1) << 3);
+}
+// block c (of 8) of piece row j (kDS = 32 columns) is stored at block c ^ p_swz(j)
+__device__ __forceinline__ int p_swz(int j) { return (j >> 1) & 6; }
+
+// B operand of a 16x16x32 bf16 MFMA from a swizzled row-major [t][j] tile:
+// rows k0 .. k0 + 31, columns n0 .. n0 + 15 (n0 a multiple of 16)
+template <int KRS>
+__device__ __forceinline__ uint4 kq_operand(const uint16_t* tile, int k0, int n0, int lr, int lq) {
+  const int tl = k0 + 8 * lq + (lr >> 2), th = tl + 4;
+  const int cb = (n0 >> 2) + (lr & 3);
+  const uint2 lo = lds_read_tr16(tile + tl * KRS + 4 * (cb ^ kq_swz(tl)));
+  const uint2 hi = lds_read_tr16(tile + th * KRS + 4 * (cb ^ kq_swz(th)));
+  return uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// B operand from a swizzled j-major piece [j][kDS]: B[j][i] for rows
+// j = k0 .. k0 + 31 and columns i = n0 .. n0 + 15
+__device__ __forceinline__ uint4 piece_operand(const uint16_t* piece, int k0, int n0, int lr,
+                                               int lq) {
+  const int jl = k0 + 8 * lq + (lr >> 2), jh = jl + 4;
+  const int cb = (n0 >> 2) + (lr & 3);
+  const uint2 lo = lds_read_tr16(piece + jl * kDS + 4 * (cb ^ p_swz(jl)));
+  const uint2 hi = lds_read_tr16(piece + jh * kDS + 4 * (cb ^ p_swz(jh)));
+  return uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
+// The row-major k (and q) tile of a chunk from the quads fetched a chunk ago
+// (zero where the mask says so)
+template <int KRS, typename KQ>
+__device__ __forceinline__ void deposit_rows(const KQ& kq, uint16_t* kr, uint16_t* qr) {
+#pragma unroll
+  for (int u = 0; u < KQ::NQ; ++u) {
+    const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
+    const int t = kq.qt(u), cb = kq.qj(u) >> 2;
+    const int o = t * KRS + 4 * (cb ^ kq_swz(t));
+    uint2 rk = kq.pk[u].v;
+    rk.x = mu ? rk.x : 0u;  // component selects (a vector select goes through memory)
+    rk.y = mu ? rk.y : 0u;
+    *reinterpret_cast<uint2*>(kr + o) = rk;
+    if (qr != nullptr) {
+      uint2 rq = kq.pq[u].v;
+      rq.x = mu ? rq.x : 0u;
+      rq.y = mu ? rq.y : 0u;
+      *reinterpret_cast<uint2*>(qr + o) = rq;
+    }
+  }
+}
+
 // -------------------------------------------- forward sweep, bf16 inputs ----
 // The same sweep for bf16 k, q (Dk a multiple of 8), with the two products
 // that have k or q as an operand on bf16 MFMA (v_mfma_f32_16x16x32_bf16,
@@ -651,49 +715,45 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
 // products are exact and whose sums are fp32: the accuracy of the fp32 path.
 // T U and M E keep fp32 MFMA (both operands are fp32 there).
 //
-// LDS: the state as three bf16 planes [3][kDS][SPS] (row i, column j), k
-// transposed as bf16 [DKP][KTS] (row j, column t), the diag(ks) E pieces
-// transposed [3][kDS][KTS] (row i, column t), and the fp32 U and E stages.
-// Row strides are 16 bytes modulo 256, so the 16-byte operand reads of a
-// quarter-wave (16 rows, one 16-byte column group) hit distinct banks.  The
-// k and q operands of [K; Q] S^T (16 steps x Dk per wave) come straight from
-// HBM as 16-byte fragments, fetched a chunk ahead.
-template <int JT, int RS>
+// LDS: k row-major [kN][KRS] and the state pieces j-major [3][DKP][kDS]
+// (both swizzled, read through lds_read_tr16), the diag(ks) E pieces
+// [3][kDS][KTS] (row i, column t: 16-byte operand reads of 16 rows at one
+// column group, the row stride 16 bytes modulo 32, so distinct banks), and
+// the fp32 U and E stages.  The k and q operands of [K; Q] S^T (16 steps x
+// Dk per wave) come straight from HBM as 16-byte fragments, fetched a chunk
+// ahead.
+template <int JT>
 struct SLB {
   static constexpr int DKP = 16 * JT;
-  static constexpr int UBS = RS + 4;               // row stride of the U, E stages
-  static constexpr int KTS = kN + 8;              // bf16 row stride of k^T and E pieces
-  static constexpr int SPS = DKP + 8;             // bf16 row stride of the state planes
-  static constexpr int KT = 0;                    // float offsets below
-  static constexpr int SP = KT + DKP * KTS / 2;
-  static constexpr int EP = SP + 3 * RS * SPS / 2;
-  static constexpr int UB = EP + 3 * RS * KTS / 2;
+  static constexpr int UBS = kDS + 4;              // row stride of the U, E stages
+  static constexpr int KRS = kq_row_stride(DKP);  // bf16 row stride of k
+  static constexpr int KTS = kN + 8;              // bf16 row stride of the E pieces
+  static constexpr int KR = 0;                    // float offsets below
+  static constexpr int SP = KR + kN * KRS / 2;
+  static constexpr int EP = SP + 3 * DKP * kDS / 2;
+  static constexpr int UB = EP + 3 * kDS * KTS / 2;
   static constexpr int EB = UB + kN * UBS;
   static constexpr int SIZE = EB + kN * UBS;
   // the step-permuted reads of U, E hit distinct banks when 4 UBS is 16
   // modulo 64 (as UBS above)
   static_assert((4 * UBS) % 64 == 16, "U, E row stride");
-  // an odd number of 16-byte units per row: 16 consecutive rows at one
-  // column group fall in 16 distinct 16-byte bank groups
-  static_assert((2 * KTS) % 32 == 16 && (2 * SPS) % 32 == 16, "row strides");
+  static_assert((2 * KRS) % 256 == 128 && (2 * KTS) % 32 == 16, "row strides");
+  static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
   static_assert(SP % 4 == 0 && EP % 4 == 0 && UB % 4 == 0, "16-byte aligned regions");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
-// RS state rows per workgroup (16 or 32) with 4 RS / 16 waves; at RS = 16 a
-// workgroup needs 64 KB of LDS, so two share a CU and each hides the other's
-// barrier and memory waits.
-template <int JT, int RS, bool SAVE>
-__global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
-  using L = SLB<JT, RS>;
-  constexpr int NTH = RS * 16, NT = RS / 16;  // threads; row tiles
+// kDS = 32 state rows per workgroup, eight waves
+template <int JT, bool SAVE>
+__global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
+  using L = SLB<JT>;
   constexpr int UBS = L::UBS;
-  constexpr int DKP = L::DKP, KTS = L::KTS, SPS = L::SPS;
+  constexpr int DKP = L::DKP, KRS = L::KRS, KTS = L::KTS;
   constexpr int NKS = DKP / 32;  // k-steps of 32 over Dk
   constexpr int JW = JT / 4;
   static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
   extern __shared__ __align__(16) float sm[];
-  uint16_t* const kt = reinterpret_cast<uint16_t*>(sm + L::KT);
+  uint16_t* const kr = reinterpret_cast<uint16_t*>(sm + L::KR);
   uint16_t* const sp = reinterpret_cast<uint16_t*>(sm + L::SP);
   uint16_t* const ep = reinterpret_cast<uint16_t*>(sm + L::EP);
   const FwdSweepArgs& a = A.s;
@@ -702,12 +762,12 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
   const bf16* __restrict__ v = static_cast<const bf16*>(a.v);
   bf16* __restrict__ y = static_cast<bf16*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int i0 = blockIdx.x * RS, h = blockIdx.y, b = blockIdx.z;
+  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tb = w & 3, nt = w >> 2;
-  const int mt = w % NT, jg = JW * (w / NT);
+  const int mt = w & 1, jg = JW * (w >> 1);
   const int tw = 16 * tb;
   const int64_t bh = (int64_t)b * Hv + h;
   const int64_t mat = (int64_t)Dv * Dk;
@@ -715,8 +775,8 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
   auto kq_base = [&](int c) { return ((int64_t)b * T + c * a.L) * kst + (int64_t)hk * Dk; };
   auto chunk_len = [&](int c) { return min(a.L, T - c * a.L); };
 
-  // k quads of a chunk (for k^T in LDS), a chunk ahead
-  KQPrefetch<bf16, JT, true, NTH> kq;
+  // k quads of a chunk (for the row-major k tile), a chunk ahead
+  KQPrefetch<bf16, JT, true> kq;
   kq.init(tid);
   // this wave's [K; Q] fragments: row tw + l % 16, columns 32 ks + 8 (l / 16)
   // .. +7 of the chunk, a chunk ahead (raw bits; rows past the chunk and
@@ -749,26 +809,30 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
     kq.fetch(k, q, kq_base(0), chunk_len(0), kst, Dk);
     fetch_frags(0, lr, lq);
   }
-  // the state tiles into the three bf16 planes (and checkpoint `slot`, or
-  // the sink when slot < 0; out-of-range lanes store to the sink too)
+  // the state tiles into the three j-major bf16 pieces (and checkpoint
+  // `slot`, or the sink when slot < 0; out-of-range lanes store to the sink
+  // too)
   auto put_state = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
     float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat : nullptr;
     asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
 #pragma unroll
-    for (int nj = 0; nj < JW; ++nj)
+    for (int nj = 0; nj < JW; ++nj) {
+      const int j = 16 * (jg + nj) + lr;
+      uint32_t p0[4], p1[4], p2[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
-        uint32_t p0, p1, p2;
-        split3(Sacc[nj][u], p0, p1, p2);
-        sp[(0 * RS + i) * SPS + j] = (uint16_t)p0;
-        sp[(1 * RS + i) * SPS + j] = (uint16_t)p1;
-        sp[(2 * RS + i) * SPS + j] = (uint16_t)p2;
+        const int i = 16 * mt + 4 * lq + u;
+        split3(Sacc[nj][u], p0[u], p1[u], p2[u]);
         if (SAVE) {
           const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
           *(ok ? ck + (int64_t)(i0 + i) * Dk + j : sink) = Sacc[nj][u];
         }
       }
+      const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
+      *reinterpret_cast<uint2*>(sp + 0 * DKP * kDS + o) = pack4(p0);
+      *reinterpret_cast<uint2*>(sp + 1 * DKP * kDS + o) = pack4(p1);
+      *reinterpret_cast<uint2*>(sp + 2 * DKP * kDS + o) = pack4(p2);
+    }
   };
   {
     int tl = tid;
@@ -788,17 +852,7 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
     float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
     const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
-    // k^T of this chunk from the quads fetched a chunk ago (zero padded)
-#pragma unroll
-    for (int u = 0; u < KQPrefetch<bf16, JT, true, NTH>::NQ; ++u) {
-      const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
-      const uint2 raw = kq.pk[u].v;
-      const int t = kq.qt(u), j = kq.qj(u);
-      kt[(j + 0) * KTS + t] = mu ? (uint16_t)(raw.x & 0xffffu) : 0;
-      kt[(j + 1) * KTS + t] = mu ? (uint16_t)(raw.x >> 16) : 0;
-      kt[(j + 2) * KTS + t] = mu ? (uint16_t)(raw.y & 0xffffu) : 0;
-      kt[(j + 3) * KTS + t] = mu ? (uint16_t)(raw.y >> 16) : 0;
-    }
+    deposit_rows<KRS>(kq, kr, nullptr);
     // this chunk's fragments, masked
     uint4 ak[NKS], aq[NKS];
     {
@@ -806,9 +860,14 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         const bool ok = rok && 32 * ks + 8 * lq < Dk;
-        const uint4 z = {0u, 0u, 0u, 0u};
-        ak[ks] = ok ? kf[ks] : z;
-        aq[ks] = ok ? qf[ks] : z;
+        ak[ks].x = ok ? kf[ks].x : 0u;
+        ak[ks].y = ok ? kf[ks].y : 0u;
+        ak[ks].z = ok ? kf[ks].z : 0u;
+        ak[ks].w = ok ? kf[ks].w : 0u;
+        aq[ks].x = ok ? qf[ks].x : 0u;
+        aq[ks].y = ok ? qf[ks].y : 0u;
+        aq[ks].z = ok ? qf[ks].z : 0u;
+        aq[ks].w = ok ? qf[ks].w : 0u;
       }
     }
     float tf[16], mf[16], gam[4], ksc[4];
@@ -836,7 +895,7 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
     }
     __syncthreads();
 
-    // X = [K; Q] S0^T: three bf16 planes of S, one accumulator per plane
+    // X = [K; Q] S0^T: three bf16 pieces of S, one accumulator per piece
     f4 XK, XQ;
     {
       f4 xk[3], xq[3];
@@ -846,8 +905,7 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-          const uint4 bs =
-              *reinterpret_cast<const uint4*>(sp + (p * RS + ti) * SPS + 32 * ks + 8 * lq);
+          const uint4 bs = piece_operand(sp + p * DKP * kDS, 32 * ks, 16 * nt, lr, lq);
           xk[p] = mfma_bf16(ak[ks], bs, xk[p]);
           xq[p] = mfma_bf16(aq[ks], bs, xq[p]);
         }
@@ -863,21 +921,24 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
     }
     __syncthreads();
 
-    // E = T U; E to the fp32 stage, diag(ks) E as three bf16 planes (row i,
+    // E = T U; E to the fp32 stage, diag(ks) E as three bf16 pieces (row i,
     // column t)
-    f4 E = {0.f, 0.f, 0.f, 0.f};
+    {
+      f4 E = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * UBS + ti], E);
+      for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * UBS + ti], E);
+      uint32_t p0[4], p1[4], p2[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = tw + 4 * lq + u;
-      sm[L::EB + t * UBS + ti] = E[u];
-      uint32_t p0, p1, p2;
-      split3(ksc[u] * E[u], p0, p1, p2);
-      ep[(0 * RS + ti) * KTS + t] = (uint16_t)p0;
-      ep[(1 * RS + ti) * KTS + t] = (uint16_t)p1;
-      ep[(2 * RS + ti) * KTS + t] = (uint16_t)p2;
-      if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        sm[L::EB + t * UBS + ti] = E[u];
+        split3(ksc[u] * E[u], p0[u], p1[u], p2[u]);
+        if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
+      }
+      const int o = ti * KTS + tw + 4 * lq;
+      *reinterpret_cast<uint2*>(ep + 0 * kDS * KTS + o) = pack4(p0);
+      *reinterpret_cast<uint2*>(ep + 1 * kDS * KTS + o) = pack4(p1);
+      *reinterpret_cast<uint2*>(ep + 2 * kDS * KTS + o) = pack4(p2);
     }
     __syncthreads();
 
@@ -896,8 +957,8 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
       }
     }
 
-    // S_end = gend S0 + (diag(ks) E)^T K on bf16 MFMA: A = the E planes (row
-    // i = 16 mt + l % 16), B = k^T (row j = 16 (jg + nj) + l % 16)
+    // S_end = gend S0 + (diag(ks) E)^T K on bf16 MFMA: A = the E pieces (row
+    // i = 16 mt + l % 16), B = k (rows t, columns 16 (jg + nj) ..)
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) Sacc[nj] *= gend;
 #pragma unroll
@@ -905,12 +966,11 @@ __global__ __launch_bounds__(RS * 16, 32 / RS) void fwd_chunked_bf16_kernel(FwdC
       uint4 ae[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-        ae[p] = *reinterpret_cast<const uint4*>(ep + (p * RS + 16 * mt + lr) * KTS + 32 * ks +
+        ae[p] = *reinterpret_cast<const uint4*>(ep + (p * kDS + 16 * mt + lr) * KTS + 32 * ks +
                                                 8 * lq);
 #pragma unroll
       for (int nj = 0; nj < JW; ++nj) {
-        const uint4 bk = *reinterpret_cast<const uint4*>(kt + (16 * (jg + nj) + lr) * KTS +
-                                                         32 * ks + 8 * lq);
+        const uint4 bk = kq_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
 #pragma unroll
         for (int p = 0; p < 3; ++p) Sacc[nj] = mfma_bf16(ae[p], bk, Sacc[nj]);
       }
@@ -1099,23 +1159,15 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_kernel(BwdChunkedAr
 // products that have k or q as an operand on bf16 MFMA, the fp32 operand
 // split exactly into three bf16 pieces (as in fwd_chunked_bf16_kernel):
 // K H^T, and the update DY^T diag(pre) Q - C^T diag(beta pre) K.  Mq DY and
-// Tb U stay on fp32 MFMA.
-//
-// Operands whose reduction index is the step t or the column j reach the
-// MFMA through transposing LDS reads (lds_read_tr16) from tiles stored as
-// they are produced: k and q row-major [t][j] as loaded, the gradient pieces
-// j-major [j][i] from the accumulator layout (four consecutive rows i per
-// lane).  Both are written in 8-byte blocks whose position inside the row is
-// XOR-swizzled so that the blocks one instruction writes or reads fall on
-// distinct LDS banks.
+// Tb U stay on fp32 MFMA.  k, q row-major and the gradient pieces j-major,
+// read through lds_read_tr16 (the tiles above); the diag(pre) DY and
+// -diag(beta pre) C pieces [i][t] as the E pieces of the forward sweep.
 template <int JT>
 struct SLR {
   static constexpr int DKP = 16 * JT;
-  // k, q row stride: an odd multiple of 128 bytes, so rows of opposite
-  // parity use opposite halves of the banks
-  static constexpr int KRS = DKP % 128 == 0 ? DKP + 64 : DKP;
-  static constexpr int KTS = kN + 8;  // bf16 row stride of the step pieces [i][t]
-  static constexpr int KR = 0;        // float offsets below
+  static constexpr int KRS = kq_row_stride(DKP);  // bf16 row stride of k, q
+  static constexpr int KTS = kN + 8;              // bf16 row stride of the step pieces
+  static constexpr int KR = 0;                    // float offsets below
   static constexpr int QR = KR + kN * KRS / 2;
   static constexpr int HT = QR + kN * KRS / 2;         // gradient pieces [3][DKP][kDS]
   static constexpr int DPP = HT + 3 * DKP * kDS / 2;   // diag(pre) DY pieces [3][kDS][KTS]
@@ -1129,12 +1181,6 @@ struct SLR {
   static_assert(QR % 4 == 0 && HT % 4 == 0 && DPP % 4 == 0 && CPP % 4 == 0 && DB % 4 == 0,
                 "alignment");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
-  // 4-element block c of k, q row t is stored at block c ^ kq_swz(t)
-  __device__ static __forceinline__ int kq_swz(int t) {
-    return (((t >> 1) & 1) << 2) | (((t >> 3) & 1) << 3);
-  }
-  // block c (of 8) of gradient-piece row j is stored at block c ^ h_swz(j)
-  __device__ static __forceinline__ int h_swz(int j) { return (j >> 1) & 6; }
 };
 
 template <int JT>
@@ -1235,7 +1281,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
         *(ok ? hc + (int64_t)(i0 + i) * Dk + j : sink) = Hacc[nj][u];
       }
-      const int o = j * kDS + 4 * ((4 * mt + lq) ^ L::h_swz(j));
+      const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
       *reinterpret_cast<uint2*>(ht + 0 * DKP * kDS + o) = pack4(p0);
       *reinterpret_cast<uint2*>(ht + 1 * DKP * kDS + o) = pack4(p1);
       *reinterpret_cast<uint2*>(ht + 2 * DKP * kDS + o) = pack4(p2);
@@ -1258,21 +1304,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
     float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
     const int64_t vbase = v_base(c);
-    // k, q of this chunk row-major (zero padded) from the quads fetched a
-    // chunk ago
-#pragma unroll
-    for (int u = 0; u < KQPrefetch<bf16, JT, true>::NQ; ++u) {
-      const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
-      const int t = kq.qt(u), cb = kq.qj(u) >> 2;
-      const int o = t * KRS + 4 * (cb ^ L::kq_swz(t));
-      uint2 rk = kq.pk[u].v, rq = kq.pq[u].v;
-      rk.x = mu ? rk.x : 0u;
-      rk.y = mu ? rk.y : 0u;
-      rq.x = mu ? rq.x : 0u;
-      rq.y = mu ? rq.y : 0u;
-      *reinterpret_cast<uint2*>(kr + o) = rk;
-      *reinterpret_cast<uint2*>(qr + o) = rq;
-    }
+    deposit_rows<KRS>(kq, kr, qr);
     uint4 ak[NKS];
     {
       const bool rok = tw + lr < n;
@@ -1318,18 +1350,11 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
 #pragma unroll
       for (int p = 0; p < 3; ++p) x3[p] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int jl = 32 * ks + 8 * lq + (lr >> 2), jh = jl + 4;
-        const int cb = 4 * nt + (lr & 3);
-        const int ol = jl * kDS + 4 * (cb ^ L::h_swz(jl));
-        const int oh = jh * kDS + 4 * (cb ^ L::h_swz(jh));
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          const uint2 lo = lds_read_tr16(ht + p * DKP * kDS + ol);
-          const uint2 hi = lds_read_tr16(ht + p * DKP * kDS + oh);
-          x3[p] = mfma_bf16(ak[ks], uint4{lo.x, lo.y, hi.x, hi.y}, x3[p]);
-        }
-      }
+        for (int p = 0; p < 3; ++p)
+          x3[p] = mfma_bf16(ak[ks], piece_operand(ht + p * DKP * kDS, 32 * ks, 16 * nt, lr, lq),
+                            x3[p]);
       X = (x3[0] + x3[1]) + x3[2];
     }
     // U = diag(suf) X + Mq DY; diag(pre) DY as three bf16 pieces [i][t]
@@ -1386,15 +1411,10 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         ad[p] = *reinterpret_cast<const uint4*>(dpp + o);
         ac[p] = *reinterpret_cast<const uint4*>(cpp + o);
       }
-      const int tl0 = 32 * ks + 8 * lq + (lr >> 2), th0 = tl0 + 4;
 #pragma unroll
       for (int nj = 0; nj < JW; ++nj) {
-        const int cb = 4 * (jg + nj) + (lr & 3);
-        const int ol = tl0 * KRS + 4 * (cb ^ L::kq_swz(tl0));
-        const int oh = th0 * KRS + 4 * (cb ^ L::kq_swz(th0));
-        const uint2 ql = lds_read_tr16(qr + ol), qh = lds_read_tr16(qr + oh);
-        const uint2 kl = lds_read_tr16(kr + ol), kh = lds_read_tr16(kr + oh);
-        const uint4 bq = {ql.x, ql.y, qh.x, qh.y}, bk = {kl.x, kl.y, kh.x, kh.y};
+        const uint4 bq = kq_operand<KRS>(qr, 32 * ks, 16 * (jg + nj), lr, lq);
+        const uint4 bk = kq_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
           Hacc[nj] = mfma_bf16(ad[p], bq, Hacc[nj]);
@@ -1454,13 +1474,11 @@ hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_
       // bf16 k, q in 8-element groups: the bf16-product kernel
       if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
         if (Dk % 8 == 0) {
-          constexpr int RS = 32;  // (16 fits two workgroups per CU but measured slower)
-          const dim3 g16((Dv + RS - 1) / RS, Hv, B);
-          const size_t lb = sizeof(float) * SLB<JT, RS>::SIZE;
+          const size_t lb = sizeof(float) * SLB<JT>::SIZE;
           // the save buffer holds both the checkpoints and the residuals
           if (A.s.Sck != nullptr)
-            return launch(fwd_chunked_bf16_kernel<JT, RS, true>, g16, 16 * RS, lb, s, A);
-          return launch(fwd_chunked_bf16_kernel<JT, RS, false>, g16, 16 * RS, lb, s, A);
+            return launch(fwd_chunked_bf16_kernel<JT, true>, grid, kSwThreads, lb, s, A);
+          return launch(fwd_chunked_bf16_kernel<JT, false>, grid, kSwThreads, lb, s, A);
         }
       return launch(fwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
     }
