@@ -108,6 +108,92 @@ __device__ __forceinline__ void store_frags(const float* src, int ld, float* __r
   }
 }
 
+// T = (I + A)^-1 for a unit lower (UPPER: upper) triangular I + A of size
+// 64 whose strict triangle is held in the [64][kGP] LDS matrix G, by one
+// wave, in 16 x 16 blocks:
+//   the diagonal blocks T_ii = (I + A_ii)^-1 by substitution, the four blocks
+//   at once (lane l: block l / 16, column l % 16);
+//   L_ik = -T_ii A_ik for the off-diagonal blocks of the triangle (MFMA);
+//   T_ij = sum_k L_ik T_kj, k from j to i - 1 (UPPER: i + 1 to j), block
+//   row by block row (MFMA), from the block-row equations of (I + A) T = I.
+// T replaces A in G (all of it: the other triangle is zeroed).
+template <bool UPPER>
+__device__ __forceinline__ void invert_unit_triangular(float* G, int l) {
+  const int lr = l & 15, lq = l >> 4;
+  {
+    const int base = 16 * lq, c = lr;
+    float x[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int t = UPPER ? 15 - u : u;
+      float acc[4] = {t == c ? 1.f : 0.f, 0.f, 0.f, 0.f};
+      const float* row = G + (base + t) * kGP + base;
+#pragma unroll
+      for (int r4 = 0; r4 < 16; r4 += 4) {
+        if (UPPER ? r4 + 3 <= t : r4 >= t) continue;
+        const f4 a4 = *reinterpret_cast<const f4*>(row + r4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (UPPER ? r4 + e > t : r4 + e < t) acc[e] = fmaf(-a4[e], x[r4 + e], acc[e]);
+      }
+      x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) G[(base + t) * kGP + base + c] = x[t];
+  }
+  // 16 x 16 block product on fp32 MFMA: A operand block (ra, ca), B operand
+  // block (rb, cb) of G
+  auto prod = [&](int ra, int ca, int rb, int cb, f4 acc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      acc = mfma(G[(16 * ra + lr) * kGP + 16 * ca + 4 * ks + lq],
+                 G[(16 * rb + 4 * ks + lq) * kGP + 16 * cb + lr], acc);
+    return acc;
+  };
+  auto put = [&](int rb, int cb, f4 v) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) G[(16 * rb + 4 * lq + e) * kGP + 16 * cb + lr] = v[e];
+  };
+  // L_ik = -T_ii A_ik in place of A_ik
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (UPPER ? k <= i : k >= i) continue;
+      put(i, k, -prod(i, i, i, k, f4{0.f, 0.f, 0.f, 0.f}));
+    }
+  // T_ij, a block row at a time (its products read L of the same row, so
+  // the row is written once all of it is formed)
+#pragma unroll
+  for (int u = 1; u < 4; ++u) {
+    const int i = UPPER ? 3 - u : u;
+    f4 acc[3];
+#pragma unroll
+    for (int d = 0; d < u; ++d) {
+      const int j = UPPER ? i + 1 + d : d;
+      acc[d] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (UPPER ? (k <= i || k > j) : (k < j || k >= i)) continue;
+        acc[d] = prod(i, k, k, j, acc[d]);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < u; ++d) put(i, UPPER ? i + 1 + d : d, acc[d]);
+  }
+  // the other triangle's off-diagonal blocks
+#pragma unroll
+  for (int x = 0; x < 6; ++x) {
+    const int blk = x * 64 + l;  // (block pair, row, 4-column group)
+    const int pr = blk >> 6, row = (blk >> 2) & 15, cg = blk & 3;
+    // block pairs (0,1) (0,2) (0,3) (1,2) (1,3) (2,3) of the upper triangle
+    const int bi = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+    const int bj = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+    const int r = UPPER ? bj : bi, cb = UPPER ? bi : bj;
+    *reinterpret_cast<f4*>(G + (16 * r + row) * kGP + 16 * cb + 4 * cg) = f4{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
 // ---------------------------------------------------------------- prep ----
 // grid (nch, Hk, B); wave w handles value heads w, w + 4, ... of the kv head.
 struct PL {
@@ -236,7 +322,6 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     }
     const float pre = vg[0] * p;                      // Gam(-1, l] = g_0 Gam(0, l]
     const float suf = l < n ? G[l * kGP + n - 1] : 0.f;  // Gam(l, n-1]
-    float x[kN];
     if constexpr (!BWD) {
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
 #pragma unroll 2
@@ -253,24 +338,8 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
       for (int t = 1; t < kN; ++t)
         if (l < t) G[t * kGP + l] = G[l * kGP + t] * KK[t * kNP + l] * bl;
-      // T = (I + A)^-1, column l by forward substitution,
-      //   x_t = [t == l] - sum_{r<t} A[t][r] x_r,
-      // row t of A read four columns at a time, four partial sums
-#pragma unroll
-      for (int t = 0; t < kN; ++t) {
-        float acc[4] = {t == l ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r4 = 0; r4 < t; r4 += 4) {
-          const f4 a4 = *reinterpret_cast<const f4*>(G + t * kGP + r4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r4 + e < t) acc[e] = fmaf(-a4[e], x[r4 + e], acc[e]);
-        }
-        x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      }
-      // T to the record through LDS (G is free now): column l of T is x
-#pragma unroll
-      for (int t = 0; t < kN; ++t) G[t * kGP + l] = x[t];
+      // T = (I + A)^-1 in place of A
+      invert_unit_triangular<false>(G, l);
       store_frags(G, kGP, rec + kPrT, l);
       rec[kPrGam + l] = pre;
       rec[kPrKs + l] = bl * suf;
@@ -292,23 +361,8 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       // diagonal (lane l <-> s)
       for (int t = 0; t < kN - 1; ++t)
         if (l > t) G[t * kGP + l] *= bl * KK[l * kNP + t];
-      // Tb = (I + Bm)^-1, column l by back substitution,
-      //   x_t = [t == l] - sum_{r>t} Bm[t][r] x_r
-#pragma unroll
-      for (int t = kN - 1; t >= 0; --t) {
-        float acc[4] = {t == l ? 1.f : 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r4 = (t + 1) & ~3; r4 < kN; r4 += 4) {
-          const f4 a4 = *reinterpret_cast<const f4*>(G + t * kGP + r4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (r4 + e > t) acc[e] = fmaf(-a4[e], x[r4 + e], acc[e]);
-        }
-        x[t] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      }
-      // Tb to the record through LDS: column l of Tb is x
-#pragma unroll
-      for (int t = 0; t < kN; ++t) G[t * kGP + l] = x[t];
+      // Tb = (I + Bm)^-1 in place of Bm
+      invert_unit_triangular<true>(G, l);
       store_frags(G, kGP, rec + kPbT, l);
       rec[kPbSuf + l] = suf;
       rec[kPbPre + l] = pre;
