@@ -204,6 +204,12 @@ struct PL {
   static constexpr int QK = VS + 4 * kN, KK = QK + kN * kNP;
   static constexpr int SIZE = KK + kN * kNP;
   static_assert(2 * 64 * kN <= VB, "stage fits the per-wave arrays");
+  // bf16 inputs: q, k row-major bf16 [kN][KGS] (alias the per-wave arrays);
+  // the row stride an odd number of 16-byte units, so the 16-byte operand
+  // reads of 16 rows at one column group hit distinct banks
+  static constexpr int KGS = 16 * kMaxJT + 8;
+  static constexpr int BQ = 0, BK = kN * KGS / 2;
+  static_assert((2 * KGS) % 32 == 16 && 2 * kN * KGS / 2 <= VB, "bf16 stage");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
@@ -234,9 +240,71 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
   TIn g_raw = g[gb_index(w < rep ? w : 0)], b_raw = beta[gb_index(w < rep ? w : 0)];
 
   // ---- QK[t][r] = q_t . k_r, KK[t][r] = k_t . k_r (MFMA over Dk) ----------
-  // All k, q quads of the chunk (up to 3 blocks of 64 columns) are loaded
-  // up front, unconditionally (clamped indices, masked at the deposit).
-  {
+  constexpr bool kBf16 = std::is_same<TIn, bf16>::value && VEC;
+  if (kBf16 && Dk % 8 == 0) {
+    // bf16 k, q: the rows staged as bf16 and multiplied on bf16 MFMA (the
+    // products of two bf16 values are exact in fp32, as in the fp32 path)
+    constexpr int NCH = 2 * kMaxJT;                  // 16-byte chunks per row
+    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
+    uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
+    uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
+    uint4 rq[NL], rk[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int ci = tid + kThreads * u;
+      const int s = ci / NCH, j = 8 * (ci % NCH);
+      const bool ok = ci < kN * NCH && s < n && j < Dk;
+      int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j : 0;
+      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+      rq[u] = *reinterpret_cast<const uint4*>(q + o);
+      rk[u] = *reinterpret_cast<const uint4*>(k + o);
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int ci = tid + kThreads * u;
+      const int s = ci / NCH, j = 8 * (ci % NCH);
+      const bool ok = ci < kN * NCH && s < n && j < Dk;
+      if (ci < kN * NCH) {
+        uint4 xq = rq[u], xk = rk[u];
+        xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
+        xq.y = ok ? xq.y : 0u;
+        xq.z = ok ? xq.z : 0u;
+        xq.w = ok ? xq.w : 0u;
+        xk.x = ok ? xk.x : 0u;
+        xk.y = ok ? xk.y : 0u;
+        xk.z = ok ? xk.z : 0u;
+        xk.w = ok ? xk.w : 0u;
+        *reinterpret_cast<uint4*>(sq + s * L::KGS + j) = xq;
+        *reinterpret_cast<uint4*>(sk + s * L::KGS + j) = xk;
+      }
+    }
+    __syncthreads();
+    f4 acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; 32 * ks < Dk; ++ks) {
+      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
+      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
+      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const uint4 bk =
+            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
+        acc[tb] = mfma_bf16(aq, bk, acc[tb]);
+        acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
+      }
+    }
+    __syncthreads();  // the stage aliases the per-wave arrays
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sm[L::QK + o] = acc[tb][v];
+        sm[L::KK + o] = acc[4 + tb][v];
+      }
+    __syncthreads();
+  } else   {
     constexpr int NB = kMaxJT / 4, NU = 4;
     Quad<TIn, VEC> rq[NB][NU], rk[NB][NU];
     uint64_t msk = 0;
