@@ -64,6 +64,16 @@ struct CL {  // LDS layout, offsets in floats
   static constexpr int ST_S = 0, ST_H = kKB * PCP, ST_Y = 2 * kKB * PCP,
                        ST_C = ST_Y + kKB * kN, ST_E = ST_C + kKB * kN;
   static constexpr int STAGE = ST_E + kKB * kN;
+  // bf16-product stage (bf16 dy, PC = 64): S0, H1 as three bf16 pieces each
+  // [3][kKB][PC] (swizzled tiles, rows i, read through lds_read_tr16); dy
+  // [kN][YS] bf16 and C, E pieces [3][kN][YS] (rows t, columns i; the row
+  // stride of 80 bytes puts the 16-byte reads of 16 rows on distinct banks)
+  static constexpr int YS = kKB + 8;
+  static constexpr int BS_S = 0, BS_H = BS_S + 3 * kKB * PC / 2,
+                       BS_Y = BS_H + 3 * kKB * PC / 2, BS_C = BS_Y + kN * YS / 2,
+                       BS_E = BS_C + 3 * kN * YS / 2;
+  static constexpr int BSTAGE = BS_E + 3 * kN * YS / 2;
+  static_assert((2 * YS) % 32 == 16, "dy, C, E row stride");
   // per-head O(n^2) arrays, after the Dv pass (alias the stage)
   static constexpr int PHI = 0, PSI = PHI + kN * kNP, GM = PSI + kN * kNP,
                        MZ = GM + kN * kNP;
@@ -72,7 +82,8 @@ struct CL {  // LDS layout, offsets in floats
   static constexpr int QS = 0, KS = 64 * kN, QKST = 2 * 64 * kN;
   // k, q stage of the final products: [kSB/4][DKP][4] each
   static constexpr int FK = 0, FQ = kSB * DKP, FINAL = 2 * kSB * DKP;
-  static constexpr int A_SZ0 = STAGE > HEAD ? STAGE : HEAD;
+  static constexpr int A_SZB = STAGE > BSTAGE ? STAGE : BSTAGE;
+  static constexpr int A_SZ0 = A_SZB > HEAD ? A_SZB : HEAD;
   static constexpr int A_SZ1 = A_SZ0 > QKST ? A_SZ0 : QKST;
   static constexpr int A_SZ = A_SZ1 > FINAL ? A_SZ1 : FINAL;
   // per-head vectors
@@ -118,9 +129,15 @@ __device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
   return r;
 }
 
-template <typename TIn, int JT, bool VEC>
+// BFP (bf16 inputs, PC = 64, Dv a multiple of 8): the Dv pass on bf16 MFMA,
+// the fp32 operands (S0, H1, C, E) split exactly into three bf16 pieces;
+// a product with bf16 dy takes the three pieces, a product of two fp32
+// operands the six piece products down to the order of fp32 rounding.
+template <typename TIn, int JT, bool VEC, bool BFP>
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   using L = CL<JT>;
+  static_assert(!BFP || (std::is_same<TIn, bf16>::value && VEC && L::PC == 64),
+                "bf16 products: bf16 inputs in 64-column passes");
   constexpr int DKP = L::DKP;
   constexpr int JPW = L::JPW, NJP = L::NJP, PC = L::PC;
   constexpr int PCP = L::PCP;
@@ -235,9 +252,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     Quad<TIn, VEC> y[2];
     uint32_t ms;  // validity: 4 bits per S0/H1 quad, then 4 per dy/e/c quad
   };
-  Slot RA, RB;
+  struct SlotB {
+    Quad<float, true> s[2], h[2], e[2], c[2];
+    uint4 y;
+    uint32_t ms;  // validity: S0/H1 quads (bits 0, 1), e/c quads (2, 3), dy (4)
+  };
+  using RSlot = typename std::conditional<BFP, SlotB, Slot>::type;
+  RSlot RA, RB;
   float hs = 0.f;  // partial <H1, S0> of the current value head
-  auto fetch = [&](Slot& R, int gbi) __attribute__((always_inline)) {
+  auto fetch = [&](RSlot& R, int gbi) __attribute__((always_inline)) {
     const int hb = gbi / (NJP * nbk);
     const int rem = gbi - hb * (NJP * nbk);
     const int jp = rem / nbk;
@@ -247,6 +270,36 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     const float* __restrict__ H1 = a.Hck + (bh * a.nch + jc) * mat;
     const int64_t rowbase = ((int64_t)b * T + t0) * tstride + (bh - (int64_t)b * Hv) * Dv;
     uint32_t m = 0;
+    if constexpr (BFP) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qd = tid + kThreads * u;  // row qd / 16, columns 4 (qd % 16) ..
+        const int i = i0 + qd / 16, j = 64 * jp + 4 * (qd % 16);
+        const bool ok = i < Dv && j < Dk;
+        const int64_t o = (int64_t)i * Dk + j;
+        R.s[u].load(S0, o, ok, 4);
+        R.h[u].load(H1, o, ok, 4);
+        m |= (uint32_t)ok << u;
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + 4 * iq + 16 * u;
+        const bool ok = ts < n && i < Dv;
+        const int64_t o = rowbase + ts * tstride + i;
+        R.e[u].load(a.E, o, ok, 4);
+        R.c[u].load(a.C, o, ok, 4);
+        m |= (uint32_t)ok << (2 + u);
+      }
+      {
+        const int i = i0 + 8 * iq;
+        const bool ok = ts < n && i < Dv;
+        int64_t o = ok ? rowbase + ts * tstride + i : 0;
+        asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
+        R.y = *reinterpret_cast<const uint4*>(dy + o);
+        m |= (uint32_t)ok << 4;
+      }
+      R.ms = m;
+    } else {
 #pragma unroll
     for (int u = 0; u < SQT; ++u) {
       const int qd = tid + kThreads * u;
@@ -268,8 +321,54 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       m |= Quad<float, VEC>::mask(ok, Dv - i) << (16 + 4 * u);
     }
     R.ms = m;
+    }
   };
-  auto deposit = [&](const Slot& R) __attribute__((always_inline)) {
+  auto deposit = [&](const RSlot& R) __attribute__((always_inline)) {
+    if constexpr (BFP) {
+      uint16_t* const bs = reinterpret_cast<uint16_t*>(sm + L::BS_S);
+      uint16_t* const bh = reinterpret_cast<uint16_t*>(sm + L::BS_H);
+      uint16_t* const by = reinterpret_cast<uint16_t*>(sm + L::BS_Y);
+      uint16_t* const bc = reinterpret_cast<uint16_t*>(sm + L::BS_C);
+      uint16_t* const be = reinterpret_cast<uint16_t*>(sm + L::BS_E);
+      constexpr int SP = kKB * PC, YP = kN * L::YS;  // piece strides (bf16)
+      // three bf16 pieces of four fp32 values, stored as 8-byte blocks
+      auto put3 = [&](uint16_t* dst, int stride, int o, f4 v) __attribute__((always_inline)) {
+        uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split3(v[e], p0[e], p1[e], p2[e]);
+        *reinterpret_cast<uint2*>(dst + o) = pack4(p0);
+        *reinterpret_cast<uint2*>(dst + stride + o) = pack4(p1);
+        *reinterpret_cast<uint2*>(dst + 2 * stride + o) = pack4(p2);
+      };
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qd = tid + kThreads * u;
+        const int r = qd / 16, o = r * PC + 4 * ((qd % 16) ^ tile_swz(r));
+        const uint32_t mu = ((R.ms >> u) & 1u) ? 15u : 0u;
+        const f4 sv = R.s[u].get(mu), hv = R.h[u].get(mu);
+        // every element of the slice passes one thread once: <H1, S0>
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hs = fmaf(sv[e], hv[e], hs);
+        put3(bs, SP, o, sv);
+        put3(bh, SP, o, hv);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint32_t mu = ((R.ms >> (2 + u)) & 1u) ? 15u : 0u;
+        const int o = ts * L::YS + 4 * iq + 16 * u;
+        put3(bc, YP, o, R.c[u].get(mu));
+        put3(be, YP, o, R.e[u].get(mu));
+      }
+      {
+        const bool ok = (R.ms >> 4) & 1u;
+        uint4 yv = R.y;
+        yv.x = ok ? yv.x : 0u;  // component selects (a vector select goes through memory)
+        yv.y = ok ? yv.y : 0u;
+        yv.z = ok ? yv.z : 0u;
+        yv.w = ok ? yv.w : 0u;
+        *reinterpret_cast<uint4*>(by + ts * L::YS + 8 * iq) = yv;
+      }
+    } else {
 #pragma unroll
     for (int u = 0; u < SQT; ++u) {
       const int qd = tid + kThreads * u;
@@ -287,6 +386,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       *reinterpret_cast<f4*>(sm + L::ST_Y + o) = R.y[u].get(mu);
       *reinterpret_cast<f4*>(sm + L::ST_E + o) = R.e[u].get(mu);
       *reinterpret_cast<f4*>(sm + L::ST_C + o) = R.c[u].get(mu);
+    }
     }
   };
   fetch(RA, 0);
@@ -334,7 +434,69 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       for (int u = 0; u < JPW; ++u) P1[u] = P2[u] = P3[u] = f4{0.f, 0.f, 0.f, 0.f};
       // One staged block: kKB / 4 MFMA k-steps.  The operands of k-step
       // ks + 1 are read from LDS while the MFMAs of k-step ks issue.
+      // bf16 products: the block is one k-step of 32 Dv rows
+      auto multiply_bf = [&]() __attribute__((always_inline)) {
+        const uint16_t* const bs = reinterpret_cast<const uint16_t*>(sm + L::BS_S);
+        const uint16_t* const bh = reinterpret_cast<const uint16_t*>(sm + L::BS_H);
+        const uint16_t* const by = reinterpret_cast<const uint16_t*>(sm + L::BS_Y);
+        const uint16_t* const bc = reinterpret_cast<const uint16_t*>(sm + L::BS_C);
+        const uint16_t* const be = reinterpret_cast<const uint16_t*>(sm + L::BS_E);
+        constexpr int SP = kKB * PC, YP = kN * L::YS;
+        // this wave's steps: dy, C, E rows tw + l % 16, Dv rows 8 (l / 16) ..
+        const int ro = (tw + lr) * L::YS + 8 * lq;
+        const uint4 fy = *reinterpret_cast<const uint4*>(by + ro);
+        uint4 fc[3], fe[3];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+          fc[p] = *reinterpret_cast<const uint4*>(bc + p * YP + ro);
+          fe[p] = *reinterpret_cast<const uint4*>(be + p * YP + ro);
+        }
+#pragma unroll
+        for (int jt = 0; jt < JPW; ++jt) {
+          uint4 fs[3], fh[3];
+#pragma unroll
+          for (int p = 0; p < 3; ++p) {
+            fs[p] = tile_operand<PC>(bs + p * SP, 0, 16 * jt, lr, lq);
+            fh[p] = tile_operand<PC>(bh + p * SP, 0, 16 * jt, lr, lq);
+          }
+          // P1 = S0^T DY; P2' = S0^T C; P3' = H1^T E
+#pragma unroll
+          for (int p = 0; p < 3; ++p) P1[jt] = mfma_bf16(fs[p], fy, P1[jt]);
+          P2[jt] = mfma_bf16(fs[0], fc[0], P2[jt]);
+          P2[jt] = mfma_bf16(fs[0], fc[1], P2[jt]);
+          P2[jt] = mfma_bf16(fs[1], fc[0], P2[jt]);
+          P2[jt] = mfma_bf16(fs[0], fc[2], P2[jt]);
+          P2[jt] = mfma_bf16(fs[2], fc[0], P2[jt]);
+          P2[jt] = mfma_bf16(fs[1], fc[1], P2[jt]);
+          P3[jt] = mfma_bf16(fh[0], fe[0], P3[jt]);
+          P3[jt] = mfma_bf16(fh[0], fe[1], P3[jt]);
+          P3[jt] = mfma_bf16(fh[1], fe[0], P3[jt]);
+          P3[jt] = mfma_bf16(fh[0], fe[2], P3[jt]);
+          P3[jt] = mfma_bf16(fh[2], fe[0], P3[jt]);
+          P3[jt] = mfma_bf16(fh[1], fe[1], P3[jt]);
+        }
+        if (jp == 0) {  // Phi'[t][r] = dy_t . e_r, Psi'[t][r] = c_t . e_r
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            const int rr = (16 * tb + lr) * L::YS + 8 * lq;
+            uint4 ge[3];
+#pragma unroll
+            for (int p = 0; p < 3; ++p) ge[p] = *reinterpret_cast<const uint4*>(be + p * YP + rr);
+#pragma unroll
+            for (int p = 0; p < 3; ++p) GR[tb] = mfma_bf16(fy, ge[p], GR[tb]);
+            GR[4 + tb] = mfma_bf16(fc[0], ge[0], GR[4 + tb]);
+            GR[4 + tb] = mfma_bf16(fc[0], ge[1], GR[4 + tb]);
+            GR[4 + tb] = mfma_bf16(fc[1], ge[0], GR[4 + tb]);
+            GR[4 + tb] = mfma_bf16(fc[0], ge[2], GR[4 + tb]);
+            GR[4 + tb] = mfma_bf16(fc[2], ge[0], GR[4 + tb]);
+            GR[4 + tb] = mfma_bf16(fc[1], ge[1], GR[4 + tb]);
+          }
+        }
+      };
       auto multiply = [&]() __attribute__((always_inline)) {
+        if constexpr (BFP) {
+          multiply_bf();
+        } else {
         constexpr int KS = kKB / 4;
         const bool gram = jp == 0;  // Phi', Psi' ride along in the first pass
         float by[2], bc[2], bw[2], be[2][4], as[2][JPW], ah[2][JPW];
@@ -380,6 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           mm(0);
           if (ks + 2 < KS) rd(ks + 2, 0);
           mm(1);
+        }
         }
       };
       // q, k of this lane's step for the pass's chi/psi, loaded before the
@@ -618,7 +781,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
 template <typename TIn, int JT, bool VEC>
 hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
   const size_t lds = sizeof(float) * CL<JT>::SIZE;
-  auto kern = chunk_kernel<TIn, JT, VEC>;
+  auto kern = chunk_kernel<TIn, JT, VEC, false>;
+  if constexpr (std::is_same<TIn, gdr::bf16>::value && VEC && CL<JT>::PC == 64)
+    if (a.Dv % 8 == 0) kern = chunk_kernel<TIn, JT, VEC, true>;
   // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -775,25 +775,11 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
 // per cycle).
 //
 // k, q row stride: an odd multiple of 128 bytes, so rows of opposite parity
-// use opposite halves of the banks.
+// use opposite halves of the banks (the swizzle of tile_swz then spreads a
+// transposing read over all of them).
 constexpr int kq_row_stride(int dkp) { return dkp % 128 == 0 ? dkp + 64 : dkp; }
-// 4-element block c of k, q row t is stored at block c ^ kq_swz(t)
-__device__ __forceinline__ int kq_swz(int t) {
-  return (((t >> 1) & 1) << 2) | (((t >> 3) & 1) << 3);
-}
 // block c (of 8) of piece row j (kDS = 32 columns) is stored at block c ^ p_swz(j)
 __device__ __forceinline__ int p_swz(int j) { return (j >> 1) & 6; }
-
-// B operand of a 16x16x32 bf16 MFMA from a swizzled row-major [t][j] tile:
-// rows k0 .. k0 + 31, columns n0 .. n0 + 15 (n0 a multiple of 16)
-template <int KRS>
-__device__ __forceinline__ uint4 kq_operand(const uint16_t* tile, int k0, int n0, int lr, int lq) {
-  const int tl = k0 + 8 * lq + (lr >> 2), th = tl + 4;
-  const int cb = (n0 >> 2) + (lr & 3);
-  const uint2 lo = lds_read_tr16(tile + tl * KRS + 4 * (cb ^ kq_swz(tl)));
-  const uint2 hi = lds_read_tr16(tile + th * KRS + 4 * (cb ^ kq_swz(th)));
-  return uint4{lo.x, lo.y, hi.x, hi.y};
-}
 
 // B operand from a swizzled j-major piece [j][kDS]: B[j][i] for rows
 // j = k0 .. k0 + 31 and columns i = n0 .. n0 + 15
@@ -814,7 +800,7 @@ __device__ __forceinline__ void deposit_rows(const KQ& kq, uint16_t* kr, uint16_
   for (int u = 0; u < KQ::NQ; ++u) {
     const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
     const int t = kq.qt(u), cb = kq.qj(u) >> 2;
-    const int o = t * KRS + 4 * (cb ^ kq_swz(t));
+    const int o = t * KRS + 4 * (cb ^ tile_swz(t));
     uint2 rk = kq.pk[u].v;
     rk.x = mu ? rk.x : 0u;  // component selects (a vector select goes through memory)
     rk.y = mu ? rk.y : 0u;
@@ -1092,7 +1078,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
                                                 8 * lq);
 #pragma unroll
       for (int nj = 0; nj < JW; ++nj) {
-        const uint4 bk = kq_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
+        const uint4 bk = tile_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
 #pragma unroll
         for (int p = 0; p < 3; ++p) Sacc[nj] = mfma_bf16(ae[p], bk, Sacc[nj]);
       }
@@ -1535,8 +1521,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
 #pragma unroll
       for (int nj = 0; nj < JW; ++nj) {
-        const uint4 bq = kq_operand<KRS>(qr, 32 * ks, 16 * (jg + nj), lr, lq);
-        const uint4 bk = kq_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
+        const uint4 bq = tile_operand<KRS>(qr, 32 * ks, 16 * (jg + nj), lr, lq);
+        const uint4 bk = tile_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
           Hacc[nj] = mfma_bf16(ad[p], bq, Hacc[nj]);

@@ -153,6 +153,32 @@ __device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
 }
 
+// Swizzled bf16 tiles read through lds_read_tr16.  A tile is row-major
+// [k][n] (k the MFMA reduction index), its row stride an odd multiple of 128
+// bytes (rows of opposite parity in opposite halves of the 64 banks), and
+// 4-element (8-byte) block c of row r stored at block c ^ tile_swz(r): the
+// blocks one transposing read touches (rows k0 + 8 G + 0..3 and 4 blocks per
+// row, G over a half-wave) then fall on distinct banks, and so do the
+// 8-byte writes of 16 consecutive blocks of a row.  Rows hold at least 16
+// blocks.
+__device__ __forceinline__ int tile_swz(int r) {
+  return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 3);
+}
+
+// The operand of a 16x16x32 bf16 MFMA whose lane l holds rows k0 + 8 (l / 16)
+// + 0..7 of column n0 + l % 16 of a swizzled tile with row stride RS (n0 a
+// multiple of 16): the B operand of a [k][n] tile, or the A operand of a
+// tile holding A^T.
+template <int RS>
+__device__ __forceinline__ uint4 tile_operand(const uint16_t* tile, int k0, int n0, int lr,
+                                              int lq) {
+  const int tl = k0 + 8 * lq + (lr >> 2), th = tl + 4;
+  const int cb = (n0 >> 2) + (lr & 3);
+  const uint2 lo = lds_read_tr16(tile + tl * RS + 4 * (cb ^ tile_swz(tl)));
+  const uint2 hi = lds_read_tr16(tile + th * RS + 4 * (cb ^ tile_swz(th)));
+  return uint4{lo.x, lo.y, hi.x, hi.y};
+}
+
 // DPP move with 1.0 in the lanes that get no source (the product identity).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_or1(float x) {
