@@ -78,10 +78,22 @@ struct CL {  // LDS layout, offsets in floats
   static constexpr int PHI = 0, PSI = PHI + kN * kNP, GM = PSI + kN * kNP,
                        MZ = GM + kN * kNP;
   static constexpr int HEAD = MZ + kN * kNP;
-  // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns)
-  static constexpr int QS = 0, KS = 64 * kN, QKST = 2 * 64 * kN;
+  // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns); with
+  // bf16 products, q, k rows as bf16 [kN][KGS] (the row stride an odd
+  // number of 16-byte units: the operand reads of 16 rows hit distinct banks)
+  static constexpr int QS = 0, KS = 64 * kN, QKST0 = 2 * 64 * kN;
+  static constexpr int KGS = DKP + 8;
+  static constexpr int BQ = 0, BK = kN * KGS / 2, QKSTB = kN * KGS;
+  static constexpr int QKST = QKST0 > QKSTB ? QKST0 : QKSTB;
   // k, q stage of the final products: [kSB/4][DKP][4] each
   static constexpr int FK = 0, FQ = kSB * DKP, FINAL = 2 * kSB * DKP;
+  // with bf16 products: k, q rows as swizzled bf16 tiles [kN][KFS] (the row
+  // stride an odd multiple of 128 bytes), in the aliased region when they
+  // fit; a weight matrix W[s][t] as three bf16 pieces [3][kN][WS] (rows t),
+  // in the QK, KK region (free after the value heads)
+  static constexpr int KFS = DKP % 128 == 0 ? DKP + 64 : DKP;
+  static constexpr int BFK = 0, BFQ = kN * KFS / 2, BFINAL = kN * KFS;
+  static constexpr int WS = kN + 8;
   static constexpr int A_SZB = STAGE > BSTAGE ? STAGE : BSTAGE;
   static constexpr int A_SZ0 = A_SZB > HEAD ? A_SZB : HEAD;
   static constexpr int A_SZ1 = A_SZ0 > QKST ? A_SZ0 : QKST;
@@ -97,6 +109,8 @@ struct CL {  // LDS layout, offsets in floats
                        W1 = KK + kN * kNP, W2 = W1 + kN * kNP,
                        WQ = W2 + kN * kNP;
   static constexpr int SIZE = WQ + kN * kNP;
+  static constexpr bool BF_FINAL = BFINAL <= A_SZ && DKP % 64 == 0;
+  static_assert(3 * kN * WS / 2 <= 2 * kN * kNP && (2 * WS) % 32 == 16, "W pieces");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS budget of one workgroup");
   static_assert(JT % JPW == 0, "whole passes");
 };
@@ -170,7 +184,78 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   };
 
   // ---- QK and KK for the kv head (shared by all its value heads) ----------
-  {
+  if constexpr (BFP) {
+    // bf16 q, k rows staged as bf16, products on bf16 MFMA (exact products)
+    static_assert((2 * L::KGS) % 32 == 16, "q, k row stride");
+    constexpr int NCH = DKP / 8;  // 16-byte chunks per row
+    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
+    uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
+    uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
+    uint4 rq[NL], rk[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int ci = tid + kThreads * u;
+      const int s = ci / NCH, j = 8 * (ci % NCH);
+      const bool ok = ci < kN * NCH && s < n && j < Dk;
+      int64_t o = ok ? qk_index(s, j) : 0;
+      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+      rq[u] = *reinterpret_cast<const uint4*>(q + o);
+      rk[u] = *reinterpret_cast<const uint4*>(k + o);
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int ci = tid + kThreads * u;
+      const int s = ci / NCH, j = 8 * (ci % NCH);
+      const bool ok = ci < kN * NCH && s < n && j < Dk;
+      if (ci < kN * NCH) {
+        uint4 xq = rq[u], xk = rk[u];
+        xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
+        xq.y = ok ? xq.y : 0u;
+        xq.z = ok ? xq.z : 0u;
+        xq.w = ok ? xq.w : 0u;
+        xk.x = ok ? xk.x : 0u;
+        xk.y = ok ? xk.y : 0u;
+        xk.z = ok ? xk.z : 0u;
+        xk.w = ok ? xk.w : 0u;
+        *reinterpret_cast<uint4*>(sq + s * L::KGS + j) = xq;
+        *reinterpret_cast<uint4*>(sk + s * L::KGS + j) = xk;
+      }
+    }
+    __syncthreads();
+    f4 acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DKP / 32; ++ks) {
+      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
+      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
+      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const uint4 bk =
+            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
+        acc[tb] = mfma_bf16(aq, bk, acc[tb]);
+        acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
+      }
+    }
+    __syncthreads();  // the stage is reused below
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sm[L::QK + o] = acc[tb][v];
+        sm[L::KK + o] = acc[4 + tb][v];
+      }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
+      const int e = tid + kThreads * x;
+      const int o = (e >> 6) * kNP + (e & 63);
+      sm[L::W1 + o] = 0.f;
+      sm[L::W2 + o] = 0.f;
+      sm[L::WQ + o] = 0.f;
+    }
+  } else {
     f4 acc[8];  // QK tiles (w, 0..3), KK tiles (w, 0..3)
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -726,6 +811,84 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   }
 
   // ---- dq += K Wq;  dk += Q W1 - K W2 (MFMA over the chunk steps) --------
+  if constexpr (BFP && L::BF_FINAL) {
+    // k, q (bf16) as swizzled tiles, read as A operands (A[j][s] = k_s[j])
+    // through lds_read_tr16; each W as three bf16 pieces W^T [t][s]
+    constexpr int KFS = L::KFS, WS = L::WS;
+    constexpr int NCH = DKP / 8;
+    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
+    uint16_t* const fk = reinterpret_cast<uint16_t*>(sm + L::BFK);
+    uint16_t* const fq = reinterpret_cast<uint16_t*>(sm + L::BFQ);
+    uint16_t* const wp = reinterpret_cast<uint16_t*>(sm + L::QK);
+    {
+      uint4 rq[NL], rk[NL];
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int ci = tid + kThreads * u;
+        const int s = ci / NCH, j = 8 * (ci % NCH);
+        const bool ok = ci < kN * NCH && s < n && j < Dk;
+        int64_t o = ok ? qk_index(s, j) : 0;
+        asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+        rq[u] = *reinterpret_cast<const uint4*>(q + o);
+        rk[u] = *reinterpret_cast<const uint4*>(k + o);
+      }
+#pragma unroll
+      for (int u = 0; u < NL; ++u) {
+        const int ci = tid + kThreads * u;
+        const int s = ci / NCH, c = ci % NCH;
+        const bool ok = ci < kN * NCH && s < n && 8 * c < Dk;
+        if (ci < kN * NCH) {
+          uint4 xq = rq[u], xk = rk[u];
+          xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
+          xq.y = ok ? xq.y : 0u;
+          xq.z = ok ? xq.z : 0u;
+          xq.w = ok ? xq.w : 0u;
+          xk.x = ok ? xk.x : 0u;
+          xk.y = ok ? xk.y : 0u;
+          xk.z = ok ? xk.z : 0u;
+          xk.w = ok ? xk.w : 0u;
+          // 4-element blocks 2c, 2c + 1 stay adjacent under the swizzle
+          const int o = s * KFS + 4 * ((2 * c) ^ tile_swz(s));
+          *reinterpret_cast<uint4*>(fk + o) = xk;
+          *reinterpret_cast<uint4*>(fq + o) = xq;
+        }
+      }
+    }
+    // acc[jt] += A^T W over the chunk steps, W from the LDS matrix at wo
+    auto wpass = [&](int wo, const uint16_t* at, f4(&acc)[JT]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {  // W[s..s+3][t] -> pieces of row t
+        const int e = tid + kThreads * x;
+        const int t = e & 63, s = 4 * (e >> 6);
+        uint32_t p0[4], p1[4], p2[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) split3(sm[wo + (s + y) * kNP + t], p0[y], p1[y], p2[y]);
+        const int o = t * WS + s;
+        *reinterpret_cast<uint2*>(wp + o) = pack4(p0);
+        *reinterpret_cast<uint2*>(wp + kN * WS + o) = pack4(p1);
+        *reinterpret_cast<uint2*>(wp + 2 * kN * WS + o) = pack4(p2);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 bw[3];
+#pragma unroll
+        for (int pc = 0; pc < 3; ++pc)
+          bw[pc] = *reinterpret_cast<const uint4*>(wp + pc * kN * WS + (tw + lr) * WS + 32 * ks +
+                                                   8 * lq);
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) {
+          const uint4 af = tile_operand<KFS>(at, 32 * ks, 16 * jt, lr, lq);
+#pragma unroll
+          for (int pc = 0; pc < 3; ++pc) acc[jt] = mfma_bf16(af, bw[pc], acc[jt]);
+        }
+      }
+      __syncthreads();  // the pieces are rewritten by the next pass
+    };
+    wpass(L::WQ, fk, dQ);
+    wpass(L::W1, fq, dK);
+    wpass(L::W2, fk, dK);  // W2 holds -W2
+  } else
   for (int s0 = 0; s0 < n; s0 += kSB) {
     if (f_role) {
       f4 rk[4], rq[4];
