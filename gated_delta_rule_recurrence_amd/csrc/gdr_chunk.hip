@@ -418,12 +418,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       constexpr int SP = kKB * PC, YP = kN * L::YS;  // piece strides (bf16)
       // three bf16 pieces of four fp32 values, stored as 8-byte blocks
       auto put3 = [&](uint16_t* dst, int stride, int o, f4 v) __attribute__((always_inline)) {
-        uint32_t p0[4], p1[4], p2[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split3(v[e], p0[e], p1[e], p2[e]);
-        *reinterpret_cast<uint2*>(dst + o) = pack4(p0);
-        *reinterpret_cast<uint2*>(dst + stride + o) = pack4(p1);
-        *reinterpret_cast<uint2*>(dst + 2 * stride + o) = pack4(p2);
+        uint2 p0, p1, p2;
+        split3_quad(v, p0, p1, p2);
+        *reinterpret_cast<uint2*>(dst + o) = p0;
+        *reinterpret_cast<uint2*>(dst + stride + o) = p1;
+        *reinterpret_cast<uint2*>(dst + 2 * stride + o) = p2;
       };
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -860,13 +859,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       for (int x = 0; x < 4; ++x) {  // W[s..s+3][t] -> pieces of row t
         const int e = tid + kThreads * x;
         const int t = e & 63, s = 4 * (e >> 6);
-        uint32_t p0[4], p1[4], p2[4];
+        f4 wv;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) split3(sm[wo + (s + y) * kNP + t], p0[y], p1[y], p2[y]);
+        for (int y = 0; y < 4; ++y) wv[y] = sm[wo + (s + y) * kNP + t];
+        uint2 p0, p1, p2;
+        split3_quad(wv, p0, p1, p2);
         const int o = t * WS + s;
-        *reinterpret_cast<uint2*>(wp + o) = pack4(p0);
-        *reinterpret_cast<uint2*>(wp + kN * WS + o) = pack4(p1);
-        *reinterpret_cast<uint2*>(wp + 2 * kN * WS + o) = pack4(p2);
+        *reinterpret_cast<uint2*>(wp + o) = p0;
+        *reinterpret_cast<uint2*>(wp + kN * WS + o) = p1;
+        *reinterpret_cast<uint2*>(wp + 2 * kN * WS + o) = p2;
       }
       __syncthreads();
 #pragma unroll

@@ -819,7 +819,7 @@ __device__ __forceinline__ void deposit_rows(const KQ& kq, uint16_t* kr, uint16_
 // that have k or q as an operand on bf16 MFMA (v_mfma_f32_16x16x32_bf16,
 // 16 times the fp32 MFMA rate): [K; Q] S^T and the update E^T diag(ks) K.
 // Their other operand (the state, diag(ks) E) is fp32 and is split exactly
-// into three bf16 pieces (split3), so each product is three bf16 MFMAs whose
+// into three bf16 pieces (split3_quad), so each product is three bf16 MFMAs whose
 // products are exact and whose sums are fp32: the accuracy of the fp32 path.
 // T U and M E keep fp32 MFMA (both operands are fp32 there).
 //
@@ -926,20 +926,20 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) {
       const int j = 16 * (jg + nj) + lr;
-      uint32_t p0[4], p1[4], p2[4];
+      uint2 p0, p1, p2;
+      split3_quad(Sacc[nj], p0, p1, p2);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = 16 * mt + 4 * lq + u;
-        split3(Sacc[nj][u], p0[u], p1[u], p2[u]);
         if (SAVE) {
           const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
           *(ok ? ck + (int64_t)(i0 + i) * Dk + j : sink) = Sacc[nj][u];
         }
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
-      *reinterpret_cast<uint2*>(sp + 0 * DKP * kDS + o) = pack4(p0);
-      *reinterpret_cast<uint2*>(sp + 1 * DKP * kDS + o) = pack4(p1);
-      *reinterpret_cast<uint2*>(sp + 2 * DKP * kDS + o) = pack4(p2);
+      *reinterpret_cast<uint2*>(sp + 0 * DKP * kDS + o) = p0;
+      *reinterpret_cast<uint2*>(sp + 1 * DKP * kDS + o) = p1;
+      *reinterpret_cast<uint2*>(sp + 2 * DKP * kDS + o) = p2;
     }
   };
   {
@@ -1035,18 +1035,20 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       f4 E = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * UBS + ti], E);
-      uint32_t p0[4], p1[4], p2[4];
+      f4 ke;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
         sm[L::EB + t * UBS + ti] = E[u];
-        split3(ksc[u] * E[u], p0[u], p1[u], p2[u]);
+        ke[u] = ksc[u] * E[u];
         if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
       }
+      uint2 p0, p1, p2;
+      split3_quad(ke, p0, p1, p2);
       const int o = ti * KTS + tw + 4 * lq;
-      *reinterpret_cast<uint2*>(ep + 0 * kDS * KTS + o) = pack4(p0);
-      *reinterpret_cast<uint2*>(ep + 1 * kDS * KTS + o) = pack4(p1);
-      *reinterpret_cast<uint2*>(ep + 2 * kDS * KTS + o) = pack4(p2);
+      *reinterpret_cast<uint2*>(ep + 0 * kDS * KTS + o) = p0;
+      *reinterpret_cast<uint2*>(ep + 1 * kDS * KTS + o) = p1;
+      *reinterpret_cast<uint2*>(ep + 2 * kDS * KTS + o) = p2;
     }
     __syncthreads();
 
@@ -1381,18 +1383,18 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) {
       const int j = 16 * (jg + nj) + lr;
-      uint32_t p0[4], p1[4], p2[4];
+      uint2 p0, p1, p2;
+      split3_quad(Hacc[nj], p0, p1, p2);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = 16 * mt + 4 * lq + u;
-        split3(Hacc[nj][u], p0[u], p1[u], p2[u]);
         const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
         *(ok ? hc + (int64_t)(i0 + i) * Dk + j : sink) = Hacc[nj][u];
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
-      *reinterpret_cast<uint2*>(ht + 0 * DKP * kDS + o) = pack4(p0);
-      *reinterpret_cast<uint2*>(ht + 1 * DKP * kDS + o) = pack4(p1);
-      *reinterpret_cast<uint2*>(ht + 2 * DKP * kDS + o) = pack4(p2);
+      *reinterpret_cast<uint2*>(ht + 0 * DKP * kDS + o) = p0;
+      *reinterpret_cast<uint2*>(ht + 1 * DKP * kDS + o) = p1;
+      *reinterpret_cast<uint2*>(ht + 2 * DKP * kDS + o) = p2;
     }
   };
   {
@@ -1472,16 +1474,18 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       for (int u = 0; u < 4; ++u) U[u] = suf[u] * X[u];
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) U = mfma(mf[ks], sm[L::DB + rstep(ks, lq) * kUBS + ti], U);
-      uint32_t p0[4], p1[4], p2[4];
+      f4 pd;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         sm[L::UB + (tw + 4 * lq + u) * kUBS + ti] = U[u];
-        split3(pre[u] * dyv[u], p0[u], p1[u], p2[u]);
+        pd[u] = pre[u] * dyv[u];
       }
+      uint2 p0, p1, p2;
+      split3_quad(pd, p0, p1, p2);
       const int o = ti * KTS + tw + 4 * lq;
-      *reinterpret_cast<uint2*>(dpp + 0 * kDS * KTS + o) = pack4(p0);
-      *reinterpret_cast<uint2*>(dpp + 1 * kDS * KTS + o) = pack4(p1);
-      *reinterpret_cast<uint2*>(dpp + 2 * kDS * KTS + o) = pack4(p2);
+      *reinterpret_cast<uint2*>(dpp + 0 * kDS * KTS + o) = p0;
+      *reinterpret_cast<uint2*>(dpp + 1 * kDS * KTS + o) = p1;
+      *reinterpret_cast<uint2*>(dpp + 2 * kDS * KTS + o) = p2;
     }
     __syncthreads();
 
@@ -1490,20 +1494,22 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       f4 Cv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) Cv = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * kUBS + ti], Cv);
-      uint32_t p0[4], p1[4], p2[4];
+      f4 pc;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
-        split3(-(bet[u] * pre[u]) * Cv[u], p0[u], p1[u], p2[u]);
+        pc[u] = -(bet[u] * pre[u]) * Cv[u];
         const bool ok = iok && t < n;
         *(ok ? a.C + vbase + t * vst + ti : sink) = Cv[u];
         *(ok ? dv + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
             from_f32<bf16>(bet[u] * Cv[u]);
       }
+      uint2 p0, p1, p2;
+      split3_quad(pc, p0, p1, p2);
       const int o = ti * KTS + tw + 4 * lq;
-      *reinterpret_cast<uint2*>(cpp + 0 * kDS * KTS + o) = pack4(p0);
-      *reinterpret_cast<uint2*>(cpp + 1 * kDS * KTS + o) = pack4(p1);
-      *reinterpret_cast<uint2*>(cpp + 2 * kDS * KTS + o) = pack4(p2);
+      *reinterpret_cast<uint2*>(cpp + 0 * kDS * KTS + o) = p0;
+      *reinterpret_cast<uint2*>(cpp + 1 * kDS * KTS + o) = p1;
+      *reinterpret_cast<uint2*>(cpp + 2 * kDS * KTS + o) = p2;
     }
     __syncthreads();
 

@@ -116,28 +116,29 @@ __device__ __forceinline__ f4 mfma_bf16(uint4 a, uint4 b, f4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// bf16 bit pattern of x, round to nearest even (finite x).
-__device__ __forceinline__ uint32_t bf16_bits(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Two floats as packed bf16 (element 0 in the low half), each rounded to
+// nearest even by one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// x = hi + mid + lo with three bf16 values (each rounded to nearest even from
-// the remainder; the two remainders are exact in fp32).  The three 8-bit
-// significands cover fp32's 24, so the sum reproduces x (away from the
+// x = hi + mid + lo with three bf16 values, each rounded to nearest even
+// from the remainder (the two remainders are exact in fp32).  The three
+// 8-bit significands cover fp32's 24, so the sum reproduces x (away from the
 // bottom of the exponent range), and products of the pieces with a bf16
-// value are exact: three bf16 MFMAs give an fp32-accurate product.
-__device__ __forceinline__ void split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
-  hi = bf16_bits(x);
-  const float r = x - __uint_as_float(hi << 16);
-  mid = bf16_bits(r);
-  lo = bf16_bits(r - __uint_as_float(mid << 16));
-}
-
-// Four bf16 bit patterns packed as a 64-bit LDS block (element e in bits
-// 16e .. 16e + 15 of the pair).
-__device__ __forceinline__ uint2 pack4(const uint32_t (&x)[4]) {
-  return uint2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
+// value are exact: three bf16 MFMAs give an fp32-accurate product.  Four
+// values at once, as three 8-byte blocks of packed bf16.
+__device__ __forceinline__ void split3_quad(f4 v, uint2& hi, uint2& mid, uint2& lo) {
+  hi = uint2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
+  const f4 r = {v[0] - __uint_as_float(hi.x << 16), v[1] - __uint_as_float(hi.x & 0xffff0000u),
+                v[2] - __uint_as_float(hi.y << 16), v[3] - __uint_as_float(hi.y & 0xffff0000u)};
+  mid = uint2{cvt_pk_bf16(r[0], r[1]), cvt_pk_bf16(r[2], r[3])};
+  lo = uint2{cvt_pk_bf16(r[0] - __uint_as_float(mid.x << 16),
+                         r[1] - __uint_as_float(mid.x & 0xffff0000u)),
+             cvt_pk_bf16(r[2] - __uint_as_float(mid.y << 16),
+                         r[3] - __uint_as_float(mid.y & 0xffff0000u))};
 }
 
 // ds_read_b64_tr_b16: each lane names an 8-byte block of four bf16; inside
