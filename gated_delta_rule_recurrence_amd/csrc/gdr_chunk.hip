@@ -735,30 +735,43 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h,
          skipped(a.mask, b, T, t0 + tid) ? 0.f : sPsi[tid * kNP + tid]);
 
-    // running weight matrices and M
-#pragma unroll 2
-    for (int x = 0; x < 16; ++x) {
-      const int e = tid + kThreads * x;
-      const int s = e >> 6, t = e & 63;  // entry (s, t)
-      if (s < n && t < n) {
-        const float bs = sm[L::V_B + s], bt = sm[L::V_B + t];
-        const float phi_st = sPhi[s * kNP + t], phi_ts = sPhi[t * kNP + s];
-        const float psi_st = sPsi[s * kNP + t], psi_ts = sPsi[t * kNP + s];
-        const float gam_st = sm[L::GM + s * kNP + t];  // Gam(s,t], s <= t
-        const float gam_ts = sm[L::GM + t * kNP + s];  // Gam(t,s], t <= s
-        const int o = s * kNP + t;
+    // running weight matrices and M.  The arrays are disjoint LDS regions:
+    // restrict-qualified pointers let the loads of later entries issue
+    // ahead of the stores of earlier ones.
+    {
+      const float* __restrict__ vB = sm + L::V_B;
+      const float* __restrict__ pPhi = sPhi;
+      const float* __restrict__ pPsi = sPsi;
+      const float* __restrict__ pGM = sm + L::GM;
+      const float* __restrict__ pQK = sm + L::QK;
+      const float* __restrict__ pKK = sm + L::KK;
+      float* __restrict__ pWQ = sm + L::WQ;
+      float* __restrict__ pW1 = sm + L::W1;
+      float* __restrict__ pW2 = sm + L::W2;
+      float* __restrict__ pMZ = sm + L::MZ;
+#pragma unroll 4
+      for (int x = 0; x < 16; ++x) {
+        const int e = tid + kThreads * x;
+        const int s = e >> 6, t = e & 63;  // entry (s, t)
+        const bool in = s < n && t < n;
+        const int o = s * kNP + t, ot = t * kNP + s;
+        const float bs = vB[s], bt = vB[t];
+        const float phi_st = pPhi[o], phi_ts = pPhi[ot];
+        const float psi_st = pPsi[o], psi_ts = pPsi[ot];
+        const float gam_st = pGM[o];   // Gam(s,t], s <= t
+        const float gam_ts = pGM[ot];  // Gam(t,s], t <= s
+        const float wq = pWQ[o], w1 = pW1[o], w2 = pW2[o];
+        const float qk = pQK[o], kk = pKK[o];
         // Wq[s][t] = Gam(s,t] beta_s Phi'[t][s]            (s <= t)
-        if (s <= t) sm[L::WQ + o] = fmaf(gam_st * bs, phi_ts, sm[L::WQ + o]);
+        if (in && s <= t) pWQ[o] = fmaf(gam_st * bs, phi_ts, wq);
         // W1[s][t] = Gam(t,s] beta_t Phi'[s][t]            (s >= t)
-        if (s >= t) sm[L::W1 + o] = fmaf(gam_ts * bt, phi_st, sm[L::W1 + o]);
+        if (in && s >= t) pW1[o] = fmaf(gam_ts * bt, phi_st, w1);
         // -W2[s][t]: W2 = Gam(t,s] Psi[s][t] (s > t), Gam(s,t] Psi[t][s] (s < t)
-        if (s > t) sm[L::W2 + o] = fmaf(-gam_ts * (bs * bt), psi_st, sm[L::W2 + o]);
-        if (s < t) sm[L::W2 + o] = fmaf(-gam_st * (bs * bt), psi_ts, sm[L::W2 + o]);
-        // M[s][r=t] = Phi[s][r] QK[s][r] - Psi[s][r] KK[s][r]
-        sm[L::MZ + o] = (bt * phi_st) * sm[L::QK + o] -
-                        ((bs * bt) * psi_st) * sm[L::KK + o];
-      } else {
-        sm[L::MZ + s * kNP + t] = 0.f;  // M is multiplied over all 64 rows
+        if (in && s != t)
+          pW2[o] = fmaf(-(s > t ? gam_ts : gam_st) * (bs * bt), s > t ? psi_st : psi_ts, w2);
+        // M[s][r=t] = Phi[s][r] QK[s][r] - Psi[s][r] KK[s][r] (0 outside the
+        // chunk: M is multiplied over all 64 rows)
+        pMZ[o] = in ? (bt * phi_st) * qk - ((bs * bt) * psi_st) * kk : 0.f;
       }
     }
 
