@@ -71,11 +71,66 @@ __device__ __forceinline__ int rstep(int ks, int lq) {
 constexpr int kPrT = 0, kPrM = 4096, kPrGam = 8192, kPrKs = 8256, kPrGend = 8320;
 // Reverse record:
 constexpr int kPbT = 0, kPbM = 4096, kPbSuf = 8192, kPbPre = 8256, kPbBeta = 8320;
-// Both: 64 floats that nothing reads, the target of the sweeps' stores for
+// With bf16 inputs (the bf16-product sweeps), the two matrices as three
+// bf16 pieces each in 16x16x32 A-fragment order (pieces_to_record):
+constexpr int kBrT = 0, kBrM = 6144, kBrGam = 12288, kBrKs = 12352, kBrGend = 12416;
+constexpr int kBbT = 0, kBbM = 6144, kBbSuf = 12288, kBbPre = 12352, kBbBeta = 12416;
+// All: 64 floats that nothing reads, the target of the sweeps' stores for
 // lanes outside the tensors, so that no store needs a branch around it (a
 // branch makes the compiler's wait counts for later loads conservative).
-constexpr int kPrSink = 8384;
-static_assert(kPbBeta + kN <= kPrSink && kPrSink + 64 <= kChunkPrepStride, "record");
+constexpr int kPrSink = 12480;
+static_assert(kPbBeta + kN <= kPrSink && kBbBeta + kN <= kPrSink &&
+                  kPrSink + 64 <= kChunkPrepStride, "record");
+
+// A [64][64] matrix, given elementwise, to a record as three bf16 pieces in
+// 16x16x32 A-fragment order: block (tb, ks, piece) holds for lane l the 16
+// bytes of row 16 tb + l % 16, columns 32 ks + 8 (l / 16) .. +7; block b
+// starts at float (b * 64 + l) * 4, the blocks ordered (tb, ks, piece).
+template <typename Elem>
+__device__ __forceinline__ void pieces_to_record(float* __restrict__ dst, int l, Elem elem) {
+  const int lr = l & 15, lq = l >> 4;
+#pragma unroll 2
+  for (int b = 0; b < 8; ++b) {
+    const int t = 16 * (b >> 1) + lr, s0 = 32 * (b & 1) + 8 * lq;
+    f4 x, y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = elem(t, s0 + e), y[e] = elem(t, s0 + 4 + e);
+    uint2 x0, x1, x2, y0, y1, y2;
+    split3_quad(x, x0, x1, x2);
+    split3_quad(y, y0, y1, y2);
+    *reinterpret_cast<uint4*>(dst + ((3 * b + 0) * 64 + l) * 4) = uint4{x0.x, x0.y, y0.x, y0.y};
+    *reinterpret_cast<uint4*>(dst + ((3 * b + 1) * 64 + l) * 4) = uint4{x1.x, x1.y, y1.x, y1.y};
+    *reinterpret_cast<uint4*>(dst + ((3 * b + 2) * 64 + l) * 4) = uint4{x2.x, x2.y, y2.x, y2.y};
+  }
+}
+
+// The pieces of k-steps 0, 1 of step tile tb (lane l), as written above
+__device__ __forceinline__ void pieces_from_record(const float* __restrict__ src, int tb, int l,
+                                                   uint4 (&f)[2][3]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      f[ks][p] = *reinterpret_cast<const uint4*>(src + ((3 * (2 * tb + ks) + p) * 64 + l) * 4);
+}
+
+// acc += A B over the 64 steps with both operands as three bf16 pieces: the
+// six piece products down to the order of fp32 rounding.  a: A pieces per
+// k-step (registers); b(ks, p): B piece p of k-step ks.
+template <typename BFn>
+__device__ __forceinline__ f4 mfma_pieces6(const uint4 (&a)[2][3], BFn b, f4 acc) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const uint4 b0 = b(ks, 0), b1 = b(ks, 1), b2 = b(ks, 2);
+    acc = mfma_bf16(a[ks][0], b0, acc);
+    acc = mfma_bf16(a[ks][0], b1, acc);
+    acc = mfma_bf16(a[ks][1], b0, acc);
+    acc = mfma_bf16(a[ks][0], b2, acc);
+    acc = mfma_bf16(a[ks][2], b0, acc);
+    acc = mfma_bf16(a[ks][1], b1, acc);
+  }
+  return acc;
+}
 
 // A [64][64] record matrix in MFMA A-fragment order: the A operand of k-step
 // ks (k index rstep(ks, lq)) of the 16 x 16 tile of rows 16 tb.. sits in
@@ -390,8 +445,16 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     }
     const float pre = vg[0] * p;                      // Gam(-1, l] = g_0 Gam(0, l]
     const float suf = l < n ? G[l * kGP + n - 1] : 0.f;  // Gam(l, n-1]
+    // bf16 inputs in 8-element groups: the bf16-product sweeps read the
+    // matrices as bf16 pieces
+    const bool pieces = kBf16 && Dk % 8 == 0;
     if constexpr (!BWD) {
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
+      if (pieces) {
+        pieces_to_record(rec + kBrM, l, [&](int t, int s) {
+          return s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
+        });
+      } else
 #pragma unroll 2
       for (int bx = 0; bx < 16; ++bx) {
         const int t = 16 * (bx >> 2) + lr;
@@ -408,12 +471,24 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         if (l < t) G[t * kGP + l] = G[l * kGP + t] * KK[t * kNP + l] * bl;
       // T = (I + A)^-1 in place of A
       invert_unit_triangular<false>(G, l);
-      store_frags(G, kGP, rec + kPrT, l);
-      rec[kPrGam + l] = pre;
-      rec[kPrKs + l] = bl * suf;
-      if (l == n - 1) rec[kPrGend] = pre;
+      if (pieces) {
+        pieces_to_record(rec + kBrT, l, [&](int t, int s) { return G[t * kGP + s]; });
+        rec[kBrGam + l] = pre;
+        rec[kBrKs + l] = bl * suf;
+        if (l == n - 1) rec[kBrGend] = pre;
+      } else {
+        store_frags(G, kGP, rec + kPrT, l);
+        rec[kPrGam + l] = pre;
+        rec[kPrKs + l] = bl * suf;
+        if (l == n - 1) rec[kPrGend] = pre;
+      }
     } else {
       // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
+      if (pieces) {
+        pieces_to_record(rec + kBbM, l, [&](int t, int s) {
+          return s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
+        });
+      } else
 #pragma unroll 2
       for (int bx = 0; bx < 16; ++bx) {
         const int t = 16 * (bx >> 2) + lr;
@@ -431,10 +506,17 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         if (l > t) G[t * kGP + l] *= bl * KK[l * kNP + t];
       // Tb = (I + Bm)^-1 in place of Bm
       invert_unit_triangular<true>(G, l);
-      store_frags(G, kGP, rec + kPbT, l);
-      rec[kPbSuf + l] = suf;
-      rec[kPbPre + l] = pre;
-      rec[kPbBeta + l] = bl;
+      if (pieces) {
+        pieces_to_record(rec + kBbT, l, [&](int t, int s) { return G[t * kGP + s]; });
+        rec[kBbSuf + l] = suf;
+        rec[kBbPre + l] = pre;
+        rec[kBbBeta + l] = bl;
+      } else {
+        store_frags(G, kGP, rec + kPbT, l);
+        rec[kPbSuf + l] = suf;
+        rec[kPbPre + l] = pre;
+        rec[kPbBeta + l] = bl;
+      }
     }
   }
 }
@@ -821,33 +903,31 @@ __device__ __forceinline__ void deposit_rows(const KQ& kq, uint16_t* kr, uint16_
 // Their other operand (the state, diag(ks) E) is fp32 and is split exactly
 // into three bf16 pieces (split3_quad), so each product is three bf16 MFMAs whose
 // products are exact and whose sums are fp32: the accuracy of the fp32 path.
-// T U and M E keep fp32 MFMA (both operands are fp32 there).
+// T U and M E, both operands fp32 (T, M from the prep record as bf16
+// pieces), take the six piece products (mfma_pieces6).
 //
 // LDS: k row-major [kN][KRS] and the state pieces j-major [3][DKP][kDS]
-// (both swizzled, read through lds_read_tr16), the diag(ks) E pieces
-// [3][kDS][KTS] (row i, column t: 16-byte operand reads of 16 rows at one
-// column group, the row stride 16 bytes modulo 32, so distinct banks), and
-// the fp32 U and E stages.  The k and q operands of [K; Q] S^T (16 steps x
-// Dk per wave) come straight from HBM as 16-byte fragments, fetched a chunk
-// ahead.
+// (both swizzled, read through lds_read_tr16), and the U, E and diag(ks) E
+// pieces [3][kDS][KTS] (row i, column t: 16-byte operand reads of 16 rows
+// at one column group, the row stride 16 bytes modulo 32, so distinct
+// banks).  The k and q operands of [K; Q] S^T (16 steps x Dk per wave) come
+// straight from HBM as 16-byte fragments, fetched a chunk ahead.
 template <int JT>
 struct SLB {
   static constexpr int DKP = 16 * JT;
-  static constexpr int UBS = kDS + 4;              // row stride of the U, E stages
   static constexpr int KRS = kq_row_stride(DKP);  // bf16 row stride of k
-  static constexpr int KTS = kN + 8;              // bf16 row stride of the E pieces
+  static constexpr int KTS = kN + 8;              // bf16 row stride of the step pieces
+  static constexpr int PS = kDS * KTS;            // bf16 stride of one step piece
   static constexpr int KR = 0;                    // float offsets below
   static constexpr int SP = KR + kN * KRS / 2;
-  static constexpr int EP = SP + 3 * DKP * kDS / 2;
-  static constexpr int UB = EP + 3 * kDS * KTS / 2;
-  static constexpr int EB = UB + kN * UBS;
-  static constexpr int SIZE = EB + kN * UBS;
-  // the step-permuted reads of U, E hit distinct banks when 4 UBS is 16
-  // modulo 64 (as UBS above)
-  static_assert((4 * UBS) % 64 == 16, "U, E row stride");
+  static constexpr int EP = SP + 3 * DKP * kDS / 2;  // diag(ks) E pieces
+  static constexpr int UP = EP + 3 * PS / 2;          // U pieces
+  static constexpr int EQ = UP + 3 * PS / 2;          // E pieces
+  static constexpr int SIZE = EQ + 3 * PS / 2;
   static_assert((2 * KRS) % 256 == 128 && (2 * KTS) % 32 == 16, "row strides");
   static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
-  static_assert(SP % 4 == 0 && EP % 4 == 0 && UB % 4 == 0, "16-byte aligned regions");
+  static_assert(SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0,
+                "16-byte aligned regions");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
@@ -855,7 +935,7 @@ struct SLB {
 template <int JT, bool SAVE>
 __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
   using L = SLB<JT>;
-  constexpr int UBS = L::UBS;
+  constexpr int PS = L::PS;
   constexpr int DKP = L::DKP, KRS = L::KRS, KTS = L::KTS;
   constexpr int NKS = DKP / 32;  // k-steps of 32 over Dk
   constexpr int JW = JT / 4;
@@ -864,6 +944,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   uint16_t* const kr = reinterpret_cast<uint16_t*>(sm + L::KR);
   uint16_t* const sp = reinterpret_cast<uint16_t*>(sm + L::SP);
   uint16_t* const ep = reinterpret_cast<uint16_t*>(sm + L::EP);
+  uint16_t* const up = reinterpret_cast<uint16_t*>(sm + L::UP);
+  uint16_t* const eq = reinterpret_cast<uint16_t*>(sm + L::EQ);
   const FwdSweepArgs& a = A.s;
   const bf16* __restrict__ q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ k = static_cast<const bf16*>(a.k);
@@ -978,17 +1060,18 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         aq[ks].w = ok ? qf[ks].w : 0u;
       }
     }
-    float tf[16], mf[16], gam[4], ksc[4];
+    uint4 tp[2][3], mp[2][3];  // T, M pieces of this wave's step tile
+    float gam[4], ksc[4];
     bf16 vr[4];
     uint32_t vm = 0;
-    load_frags(rec + kPrT, tb, l, tf);
+    pieces_from_record(rec + kBrT, tb, l, tp);
     {
-      const f4 g4 = *reinterpret_cast<const f4*>(rec + kPrGam + tw + 4 * lq);
-      const f4 k4 = *reinterpret_cast<const f4*>(rec + kPrKs + tw + 4 * lq);
+      const f4 g4 = *reinterpret_cast<const f4*>(rec + kBrGam + tw + 4 * lq);
+      const f4 k4 = *reinterpret_cast<const f4*>(rec + kBrKs + tw + 4 * lq);
 #pragma unroll
       for (int u = 0; u < 4; ++u) gam[u] = g4[u], ksc[u] = k4[u];
     }
-    const float gend = rec[kPrGend];
+    const float gend = rec[kBrGend];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = tw + 4 * lq + u;
@@ -1020,35 +1103,46 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       XK = (xk[0] + xk[1]) + xk[2];
       XQ = (xq[0] + xq[1]) + xq[2];
     }
-    load_frags(rec + kPrM, tb, l, mf);
+    pieces_from_record(rec + kBrM, tb, l, mp);
+    // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
+    const int so = ti * KTS + tw + 4 * lq;
+    auto put_steps = [&](uint16_t* dst, f4 v) __attribute__((always_inline)) {
+      uint2 p0, p1, p2;
+      split3_quad(v, p0, p1, p2);
+      *reinterpret_cast<uint2*>(dst + so) = p0;
+      *reinterpret_cast<uint2*>(dst + PS + so) = p1;
+      *reinterpret_cast<uint2*>(dst + 2 * PS + so) = p2;
+    };
+    // B operand piece p of k-step ks from step pieces: rows t = 32 ks +
+    // 8 (l / 16) .., column ti
+    auto step_piece = [&](const uint16_t* src, int ks, int p) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>(src + p * PS + ti * KTS + 32 * ks + 8 * lq);
+    };
     // U = V - diag(gam) X_K
+    {
+      f4 uv;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float vu = ((vm >> u) & 1) ? to_f32(vr[u]) : 0.f;
-      sm[L::UB + (tw + 4 * lq + u) * UBS + ti] = vu - gam[u] * XK[u];
+      for (int u = 0; u < 4; ++u) {
+        const float vu = ((vm >> u) & 1) ? to_f32(vr[u]) : 0.f;
+        uv[u] = vu - gam[u] * XK[u];
+      }
+      put_steps(up, uv);
     }
     __syncthreads();
 
-    // E = T U; E to the fp32 stage, diag(ks) E as three bf16 pieces (row i,
-    // column t)
+    // E = T U; E and diag(ks) E as three bf16 pieces each (row i, column t)
     {
-      f4 E = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) E = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * UBS + ti], E);
+      const f4 E = mfma_pieces6(
+          tp, [&](int ks, int p) { return step_piece(up, ks, p); }, f4{0.f, 0.f, 0.f, 0.f});
       f4 ke;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
-        sm[L::EB + t * UBS + ti] = E[u];
         ke[u] = ksc[u] * E[u];
         if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
       }
-      uint2 p0, p1, p2;
-      split3_quad(ke, p0, p1, p2);
-      const int o = ti * KTS + tw + 4 * lq;
-      *reinterpret_cast<uint2*>(ep + 0 * kDS * KTS + o) = p0;
-      *reinterpret_cast<uint2*>(ep + 1 * kDS * KTS + o) = p1;
-      *reinterpret_cast<uint2*>(ep + 2 * kDS * KTS + o) = p2;
+      put_steps(eq, E);
+      put_steps(ep, ke);
     }
     __syncthreads();
 
@@ -1057,8 +1151,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       f4 Yv;
 #pragma unroll
       for (int u = 0; u < 4; ++u) Yv[u] = gam[u] * XQ[u];
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) Yv = mfma(mf[ks], sm[L::EB + rstep(ks, lq) * UBS + ti], Yv);
+      Yv = mfma_pieces6(mp, [&](int ks, int p) { return step_piece(eq, ks, p); }, Yv);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
@@ -1076,7 +1169,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       uint4 ae[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p)
-        ae[p] = *reinterpret_cast<const uint4*>(ep + (p * kDS + 16 * mt + lr) * KTS + 32 * ks +
+        ae[p] = *reinterpret_cast<const uint4*>(ep + p * PS + (16 * mt + lr) * KTS + 32 * ks +
                                                 8 * lq);
 #pragma unroll
       for (int nj = 0; nj < JW; ++nj) {
@@ -1268,27 +1361,31 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_kernel(BwdChunkedAr
 // The same reverse sweep for bf16 k, q, dy (Dk a multiple of 8), with the
 // products that have k or q as an operand on bf16 MFMA, the fp32 operand
 // split exactly into three bf16 pieces (as in fwd_chunked_bf16_kernel):
-// K H^T, and the update DY^T diag(pre) Q - C^T diag(beta pre) K.  Mq DY and
-// Tb U stay on fp32 MFMA.  k, q row-major and the gradient pieces j-major,
-// read through lds_read_tr16 (the tiles above); the diag(pre) DY and
-// -diag(beta pre) C pieces [i][t] as the E pieces of the forward sweep.
+// K H^T, and the update DY^T diag(pre) Q - C^T diag(beta pre) K; Mq DY
+// (Mq pieces against bf16 dy) and Tb U (six piece products) from the prep
+// record's bf16 pieces.  k, q row-major and the gradient pieces j-major,
+// read through lds_read_tr16 (the tiles above); dy, U and the diag(pre) DY
+// and -diag(beta pre) C pieces [i][t] as the step pieces of the forward
+// sweep.
 template <int JT>
 struct SLR {
   static constexpr int DKP = 16 * JT;
   static constexpr int KRS = kq_row_stride(DKP);  // bf16 row stride of k, q
   static constexpr int KTS = kN + 8;              // bf16 row stride of the step pieces
+  static constexpr int PS = kDS * KTS;            // bf16 stride of one step piece
   static constexpr int KR = 0;                    // float offsets below
   static constexpr int QR = KR + kN * KRS / 2;
-  static constexpr int HT = QR + kN * KRS / 2;         // gradient pieces [3][DKP][kDS]
-  static constexpr int DPP = HT + 3 * DKP * kDS / 2;   // diag(pre) DY pieces [3][kDS][KTS]
-  static constexpr int CPP = DPP + 3 * kDS * KTS / 2;  // -diag(beta pre) C pieces
-  static constexpr int DB = CPP + 3 * kDS * KTS / 2;   // dy fp32 [kN][kUBS]
-  static constexpr int UB = DB + kN * kUBS;            // U fp32 [kN][kUBS]
-  static constexpr int SIZE = UB + kN * kUBS;
+  static constexpr int HT = QR + kN * KRS / 2;        // gradient pieces [3][DKP][kDS]
+  static constexpr int DPP = HT + 3 * DKP * kDS / 2;  // diag(pre) DY pieces [3][kDS][KTS]
+  static constexpr int CPP = DPP + 3 * PS / 2;        // -diag(beta pre) C pieces
+  static constexpr int DYT = CPP + 3 * PS / 2;        // dy bf16 [kDS][KTS]
+  static constexpr int UP = DYT + PS / 2;             // U pieces [3][kDS][KTS]
+  static constexpr int SIZE = UP + 3 * PS / 2;
   static_assert((2 * KRS) % 256 == 128, "k, q row stride");
   static_assert((2 * KTS) % 32 == 16, "step-piece row stride");
   static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
-  static_assert(QR % 4 == 0 && HT % 4 == 0 && DPP % 4 == 0 && CPP % 4 == 0 && DB % 4 == 0,
+  static_assert(QR % 4 == 0 && HT % 4 == 0 && DPP % 4 == 0 && CPP % 4 == 0 && DYT % 4 == 0 &&
+                    UP % 4 == 0,
                 "alignment");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
@@ -1296,7 +1393,7 @@ struct SLR {
 template <int JT>
 __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChunkedArgs A) {
   using L = SLR<JT>;
-  constexpr int DKP = L::DKP, KRS = L::KRS, KTS = L::KTS;
+  constexpr int DKP = L::DKP, KRS = L::KRS, KTS = L::KTS, PS = L::PS;
   constexpr int NKS = DKP / 32;
   constexpr int JW = JT / 4;
   static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
@@ -1306,6 +1403,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   uint16_t* const ht = reinterpret_cast<uint16_t*>(sm + L::HT);
   uint16_t* const dpp = reinterpret_cast<uint16_t*>(sm + L::DPP);
   uint16_t* const cpp = reinterpret_cast<uint16_t*>(sm + L::CPP);
+  uint16_t* const dyt = reinterpret_cast<uint16_t*>(sm + L::DYT);
+  uint16_t* const up = reinterpret_cast<uint16_t*>(sm + L::UP);
   const BwdSweepArgs& a = A.s;
   const bf16* __restrict__ q = static_cast<const bf16*>(a.q);
   const bf16* __restrict__ k = static_cast<const bf16*>(a.k);
@@ -1428,23 +1527,43 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         ak[ks].w = ok ? kf[ks].w : 0u;
       }
     }
+    // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
+    const int so = ti * KTS + tw + 4 * lq;
+    auto put_steps = [&](uint16_t* dst, f4 v) __attribute__((always_inline)) {
+      uint2 p0, p1, p2;
+      split3_quad(v, p0, p1, p2);
+      *reinterpret_cast<uint2*>(dst + so) = p0;
+      *reinterpret_cast<uint2*>(dst + PS + so) = p1;
+      *reinterpret_cast<uint2*>(dst + 2 * PS + so) = p2;
+    };
+    // B operand piece p of k-step ks from step pieces: rows t = 32 ks +
+    // 8 (l / 16) .., column ti
+    auto step_piece = [&](const uint16_t* src, int ks, int p) __attribute__((always_inline)) {
+      return *reinterpret_cast<const uint4*>(src + p * PS + ti * KTS + 32 * ks + 8 * lq);
+    };
     float dyv[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      dyv[u] = ((dm >> u) & 1) ? to_f32(dr[u]) : 0.f;
-      sm[L::DB + (tw + 4 * lq + u) * kUBS + ti] = dyv[u];
-    }
-    float tf[16], mf[16], suf[4], pre[4], bet[4];
-    load_frags(rec + kPbT, tb, l, tf);
-    load_frags(rec + kPbM, tb, l, mf);
     {
-      const f4 s4 = *reinterpret_cast<const f4*>(rec + kPbSuf + tw + 4 * lq);
-      const f4 p4 = *reinterpret_cast<const f4*>(rec + kPbPre + tw + 4 * lq);
-      const f4 b4 = *reinterpret_cast<const f4*>(rec + kPbBeta + tw + 4 * lq);
+      uint32_t db[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = (dm >> u) & 1;
+        dyv[u] = ok ? to_f32(dr[u]) : 0.f;
+        db[u] = ok ? dr[u].bits : 0u;
+      }
+      *reinterpret_cast<uint2*>(dyt + so) = uint2{db[0] | (db[1] << 16), db[2] | (db[3] << 16)};
+    }
+    uint4 tp[2][3], mp[2][3];  // Tb, Mq pieces of this wave's step tile
+    float suf[4], pre[4], bet[4];
+    pieces_from_record(rec + kBbT, tb, l, tp);
+    pieces_from_record(rec + kBbM, tb, l, mp);
+    {
+      const f4 s4 = *reinterpret_cast<const f4*>(rec + kBbSuf + tw + 4 * lq);
+      const f4 p4 = *reinterpret_cast<const f4*>(rec + kBbPre + tw + 4 * lq);
+      const f4 b4 = *reinterpret_cast<const f4*>(rec + kBbBeta + tw + 4 * lq);
 #pragma unroll
       for (int u = 0; u < 4; ++u) suf[u] = s4[u], pre[u] = p4[u], bet[u] = b4[u];
     }
-    const float pend = rec[kPbPre + n - 1];
+    const float pend = rec[kBbPre + n - 1];
     {
       const int cn = max(c - 1, 0);
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
@@ -1472,28 +1591,25 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       f4 U;
 #pragma unroll
       for (int u = 0; u < 4; ++u) U[u] = suf[u] * X[u];
+      // Mq DY: dy is bf16, so the three Mq pieces give the exact products
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) U = mfma(mf[ks], sm[L::DB + rstep(ks, lq) * kUBS + ti], U);
+      for (int ks = 0; ks < 2; ++ks) {
+        const uint4 bd = step_piece(dyt, ks, 0);
+#pragma unroll
+        for (int p = 0; p < 3; ++p) U = mfma_bf16(mp[ks][p], bd, U);
+      }
+      put_steps(up, U);
       f4 pd;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        sm[L::UB + (tw + 4 * lq + u) * kUBS + ti] = U[u];
-        pd[u] = pre[u] * dyv[u];
-      }
-      uint2 p0, p1, p2;
-      split3_quad(pd, p0, p1, p2);
-      const int o = ti * KTS + tw + 4 * lq;
-      *reinterpret_cast<uint2*>(dpp + 0 * kDS * KTS + o) = p0;
-      *reinterpret_cast<uint2*>(dpp + 1 * kDS * KTS + o) = p1;
-      *reinterpret_cast<uint2*>(dpp + 2 * kDS * KTS + o) = p2;
+      for (int u = 0; u < 4; ++u) pd[u] = pre[u] * dyv[u];
+      put_steps(dpp, pd);
     }
     __syncthreads();
 
     // C = Tb U; dv = diag(beta) C; -diag(beta pre) C as three bf16 pieces
     {
-      f4 Cv = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) Cv = mfma(tf[ks], sm[L::UB + rstep(ks, lq) * kUBS + ti], Cv);
+      const f4 Cv = mfma_pieces6(
+          tp, [&](int ks, int p) { return step_piece(up, ks, p); }, f4{0.f, 0.f, 0.f, 0.f});
       f4 pc;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1504,12 +1620,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         *(ok ? dv + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
             from_f32<bf16>(bet[u] * Cv[u]);
       }
-      uint2 p0, p1, p2;
-      split3_quad(pc, p0, p1, p2);
-      const int o = ti * KTS + tw + 4 * lq;
-      *reinterpret_cast<uint2*>(cpp + 0 * kDS * KTS + o) = p0;
-      *reinterpret_cast<uint2*>(cpp + 1 * kDS * KTS + o) = p1;
-      *reinterpret_cast<uint2*>(cpp + 2 * kDS * KTS + o) = p2;
+      put_steps(cpp, pc);
     }
     __syncthreads();
 

@@ -82,10 +82,11 @@ struct ChunkedSweepShape {
   const void* beta;
 };
 
-// Floats per prep record: two [64][64] matrices in MFMA A-fragment order,
-// three per-step vectors of 64 and 64 floats that nothing reads (a store
-// target for lanes outside the tensors).
-constexpr int kChunkPrepStride = 2 * 64 * 64 + 4 * 64;
+// Floats per prep record: two [64][64] matrices in MFMA A-fragment order
+// (fp32, or three bf16 pieces each: 1.5 times the floats), three per-step
+// vectors of 64 and 64 floats that nothing reads (a store target for lanes
+// outside the tensors).
+constexpr int kChunkPrepStride = 3 * 64 * 64 + 4 * 64;
 
 // Whether the chunked sweeps take this shape, and the floats of their prep
 // records.

@@ -106,11 +106,12 @@ def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
     rows = B * T * Hv * Dv * 4
     assert _lib.checkpoint_bytes(sh) == _round256(states) + rows
     # the chunked sweeps (Dk <= 192, C >= 16, T >= C) keep two 64 x 64
-    # matrices and three 64-vectors per (batch row, value head, chunk): the
+    # matrices (room for three bf16 pieces of each: 3 x 64 x 64 floats) and
+    # three 64-vectors per (batch row, value head, chunk), plus 64 floats: the
     # whole forward workspace, and a region after the backward's per-step
     # vectors
     chunked = Dk <= 192 and C >= 16 and T >= C
-    prep = B * Hv * nch * (2 * 64 * 64 + 4 * 64) * 4 if chunked else 0
+    prep = B * Hv * nch * (3 * 64 * 64 + 4 * 64) * 4 if chunked else 0
     assert _lib.forward_workspace_bytes(sh) == prep
     bwd = _round256(states) + rows
     assert _lib.backward_workspace_bytes(sh) == (_round256(bwd) + prep if chunked else bwd)
