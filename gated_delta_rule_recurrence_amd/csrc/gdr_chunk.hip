@@ -143,7 +143,7 @@ __device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
   return r;
 }
 
-// BFP (bf16 inputs, PC = 64, Dv a multiple of 8): the Dv pass on bf16 MFMA,
+// BFP (bf16 inputs, PC = 64, Dk and Dv multiples of 8): the Dv pass on bf16 MFMA,
 // the fp32 operands (S0, H1, C, E) split exactly into three bf16 pieces;
 // a product with bf16 dy takes the three pieces, a product of two fp32
 // operands the six piece products down to the order of fp32 rounding.
@@ -337,6 +337,12 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     Quad<TIn, VEC> y[2];
     uint32_t ms;  // validity: 4 bits per S0/H1 quad, then 4 per dy/e/c quad
   };
+  // S0, H1, E, C are read once here: non-temporal loads keep them from
+  // displacing the lines the workgroup reads again
+  auto ld_nt = [](const float* p, int64_t o, bool ok) __attribute__((always_inline)) {
+    const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p + (ok ? o : 0)));
+    return float4{x[0], x[1], x[2], x[3]};
+  };
   struct SlotB {
     Quad<float, true> s[2], h[2], e[2], c[2];
     uint4 y;
@@ -362,8 +368,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const int i = i0 + qd / 16, j = 64 * jp + 4 * (qd % 16);
         const bool ok = i < Dv && j < Dk;
         const int64_t o = (int64_t)i * Dk + j;
-        R.s[u].load(S0, o, ok, 4);
-        R.h[u].load(H1, o, ok, 4);
+        R.s[u].v = ld_nt(S0, o, ok);
+        R.h[u].v = ld_nt(H1, o, ok);
         m |= (uint32_t)ok << u;
       }
 #pragma unroll
@@ -371,8 +377,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const int i = i0 + 4 * iq + 16 * u;
         const bool ok = ts < n && i < Dv;
         const int64_t o = rowbase + ts * tstride + i;
-        R.e[u].load(a.E, o, ok, 4);
-        R.c[u].load(a.C, o, ok, 4);
+        R.e[u].v = ld_nt(a.E, o, ok);
+        R.c[u].v = ld_nt(a.C, o, ok);
         m |= (uint32_t)ok << (2 + u);
       }
       {
@@ -959,8 +965,10 @@ template <typename TIn, int JT, bool VEC>
 hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
   const size_t lds = sizeof(float) * CL<JT>::SIZE;
   auto kern = chunk_kernel<TIn, JT, VEC, false>;
+  // bf16 products: dy rows in 8-element blocks, k, q rows in 8-element
+  // groups (the 16-byte loads of the q, k stages)
   if constexpr (std::is_same<TIn, gdr::bf16>::value && VEC && CL<JT>::PC == 64)
-    if (a.Dv % 8 == 0) kern = chunk_kernel<TIn, JT, VEC, true>;
+    if (a.Dv % 8 == 0 && a.Dk % 8 == 0) kern = chunk_kernel<TIn, JT, VEC, true>;
   // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -66,6 +66,13 @@ __device__ __forceinline__ int rstep(int ks, int lq) {
   return 16 * (ks >> 2) + 4 * lq + (ks & 3);
 }
 
+// The bf16-product sweeps (and the bf16-piece prep records they read) take
+// bf16 inputs whose k, q rows come in 8-element groups and whose value rows
+// come in 4-element blocks.
+__host__ __device__ constexpr bool bf16_products(bool bf16_vec, int Dk, int Dv) {
+  return bf16_vec && Dk % 8 == 0 && Dv % 4 == 0;
+}
+
 // Prep record layouts (floats; the stride is kChunkPrepStride).
 // Forward record:
 constexpr int kPrT = 0, kPrM = 4096, kPrGam = 8192, kPrKs = 8256, kPrGend = 8320;
@@ -447,7 +454,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     const float suf = l < n ? G[l * kGP + n - 1] : 0.f;  // Gam(l, n-1]
     // bf16 inputs in 8-element groups: the bf16-product sweeps read the
     // matrices as bf16 pieces
-    const bool pieces = kBf16 && Dk % 8 == 0;
+    const bool pieces = bf16_products(kBf16, Dk, a.Dv);
     if constexpr (!BWD) {
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
       if (pieces) {
@@ -923,10 +930,18 @@ struct SLB {
   static constexpr int EP = SP + 3 * DKP * kDS / 2;  // diag(ks) E pieces
   static constexpr int UP = EP + 3 * PS / 2;          // U pieces
   static constexpr int EQ = UP + 3 * PS / 2;          // E pieces
-  static constexpr int SIZE = EQ + 3 * PS / 2;
+  // output stages, copied out in 16-byte (y: 8-byte) row blocks after a
+  // later barrier: the state checkpoint fp32 [kDS][SKS], E fp32 [kN][OES],
+  // y bf16 [kN][OYS]
+  static constexpr int SKS = DKP + 4, OES = kDS + 4, OYS = kDS + 8;
+  static constexpr int SC = EQ + 3 * PS / 2;
+  static constexpr int OE = SC + kDS * SKS;
+  static constexpr int OY = OE + kN * OES;
+  static constexpr int SIZE = OY + kN * OYS / 2;
   static_assert((2 * KRS) % 256 == 128 && (2 * KTS) % 32 == 16, "row strides");
   static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
-  static_assert(SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0,
+  static_assert(SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0 && SC % 4 == 0 &&
+                    OE % 4 == 0 && OY % 4 == 0 && SKS % 4 == 0 && OES % 4 == 0,
                 "16-byte aligned regions");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
@@ -999,24 +1014,17 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     kq.fetch(k, q, kq_base(0), chunk_len(0), kst, Dk);
     fetch_frags(0, lr, lq);
   }
-  // the state tiles into the three j-major bf16 pieces (and checkpoint
-  // `slot`, or the sink when slot < 0; out-of-range lanes store to the sink
-  // too)
-  auto put_state = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
-    float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat : nullptr;
-    asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
+  // the state tiles into the three j-major bf16 pieces (and, saving, into
+  // the checkpoint stage)
+  auto put_state = [&](int lr, int lq) __attribute__((always_inline)) {
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) {
       const int j = 16 * (jg + nj) + lr;
       uint2 p0, p1, p2;
       split3_quad(Sacc[nj], p0, p1, p2);
+      if (SAVE) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = 16 * mt + 4 * lq + u;
-        if (SAVE) {
-          const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
-          *(ok ? ck + (int64_t)(i0 + i) * Dk + j : sink) = Sacc[nj][u];
-        }
+        for (int u = 0; u < 4; ++u) sm[L::SC + (16 * mt + 4 * lq + u) * L::SKS + j] = Sacc[nj][u];
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
       *reinterpret_cast<uint2*>(sp + 0 * DKP * kDS + o) = p0;
@@ -1027,8 +1035,41 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink + (tl & 63));
+    put_state(tl & 15, (tl & 63) >> 4);
   }
+  // 16-byte blocks of the output stages to the tensors (lanes outside them
+  // store to the sink): the checkpoint stage to slot `slot`, E, y of chunk c
+  auto out_state = [&](int slot, float* sink) __attribute__((always_inline)) {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    float* __restrict__ ck = a.Sck + (bh * a.nch + slot) * mat;
+    constexpr int NB = kDS * (DKP / 4);  // 16-byte blocks of the stage
+#pragma unroll
+    for (int x = 0; x < (NB + kSwThreads - 1) / kSwThreads; ++x) {
+      const int bk = tl + kSwThreads * x;
+      const int r = bk / (DKP / 4), j = 4 * (bk % (DKP / 4));
+      const bool ok = bk < NB && i0 + r < Dv && j < Dk;
+      const f4 v = *reinterpret_cast<const f4*>(sm + L::SC + (bk < NB ? r : 0) * L::SKS + j);
+      // read once, by the reverse pass: streamed past the caches that hold
+      // the k, q and record lines the workgroups share
+      __builtin_nontemporal_store(v, reinterpret_cast<f4*>(ok ? ck + (int64_t)(i0 + r) * Dk + j : sink));
+    }
+  };
+  auto out_rows = [&](int64_t vbase, int n, float* sink) __attribute__((always_inline)) {
+    int tl = tid;
+    asm volatile("" : "+v"(tl));
+    const int t = tl >> 3, c4 = 4 * (tl & 7);  // step t, rows i0 + c4 .. +3
+    const bool ok = t < n && i0 + c4 < Dv;
+    const int64_t o = vbase + (int64_t)t * vst + c4;
+    if (SAVE) {
+      const f4 e = *reinterpret_cast<const f4*>(sm + L::OE + t * L::OES + c4);
+      __builtin_nontemporal_store(e, reinterpret_cast<f4*>(ok ? a.E + o : sink));
+    }
+    const uint2 yv = *reinterpret_cast<const uint2*>(
+        reinterpret_cast<const uint16_t*>(sm + L::OY) + t * L::OYS + c4);
+    *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(y + o) : reinterpret_cast<uint2*>(sink)) =
+        yv;
+  };
 
   for (int c = 0; c < a.nch; ++c) {
     int tl = tid;
@@ -1040,7 +1081,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     const int t0 = c * a.L;
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
-    float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
+    float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
     const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
     deposit_rows<KRS>(kq, kr, nullptr);
     // this chunk's fragments, masked
@@ -1085,6 +1126,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       fetch_frags(cn, lr, lq);
     }
     __syncthreads();
+    // the checkpoint of this chunk's start state, staged by the last put_state
+    if (SAVE) out_state(c, sink16);
 
     // X = [K; Q] S0^T: three bf16 pieces of S, one accumulator per piece
     f4 XK, XQ;
@@ -1139,7 +1182,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
         ke[u] = ksc[u] * E[u];
-        if (SAVE) *(iok && t < n ? a.E + vbase + t * vst + ti : sink) = E[u];
+        if (SAVE) sm[L::OE + t * L::OES + ti] = E[u];
       }
       put_steps(eq, E);
       put_steps(ep, ke);
@@ -1155,8 +1198,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
-        *(iok && t < n ? y + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
-            from_f32<bf16>(Yv[u]);
+        reinterpret_cast<bf16*>(sm + L::OY)[t * L::OYS + ti] = from_f32<bf16>(Yv[u]);
       }
     }
 
@@ -1179,7 +1221,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       }
     }
     __syncthreads();  // stage reads done before it is rewritten
-    put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink);
+    out_rows(vbase, n, sink16);  // E, y of this chunk, staged before the barrier
+    if (c + 1 < a.nch) put_state(lr, lq);
   }
   if (a.ST != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1488,7 +1531,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       for (int u = 0; u < 4; ++u) {
         const int i = 16 * mt + 4 * lq + u;
         const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
-        *(ok ? hc + (int64_t)(i0 + i) * Dk + j : sink) = Hacc[nj][u];
+        // read once, by the chunk-parallel pass: streamed past the caches
+        __builtin_nontemporal_store(Hacc[nj][u], ok ? hc + (int64_t)(i0 + i) * Dk + j : sink);
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
       *reinterpret_cast<uint2*>(ht + 0 * DKP * kDS + o) = p0;
@@ -1616,7 +1660,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         const int t = tw + 4 * lq + u;
         pc[u] = -(bet[u] * pre[u]) * Cv[u];
         const bool ok = iok && t < n;
-        *(ok ? a.C + vbase + t * vst + ti : sink) = Cv[u];
+        __builtin_nontemporal_store(Cv[u], ok ? a.C + vbase + t * vst + ti : sink);
         *(ok ? dv + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
             from_f32<bf16>(bet[u] * Cv[u]);
       }
@@ -1691,14 +1735,15 @@ hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_
     const size_t lds = sizeof(float) * SL<JT>::SIZE;
     if constexpr (BWD) {
       if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
-        if (Dk % 8 == 0)
+        if (bf16_products(true, Dk, Dv))
           return launch(bwd_chunked_bf16_kernel<JT>, grid, kSwThreads,
                         sizeof(float) * SLR<JT>::SIZE, s, A);
       return launch(bwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
     } else {
-      // bf16 k, q in 8-element groups: the bf16-product kernel
+      // bf16 k, q in 8-element groups (and 4-element row blocks of the value
+      // outputs): the bf16-product kernel
       if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
-        if (Dk % 8 == 0) {
+        if (bf16_products(true, Dk, Dv)) {
           const size_t lb = sizeof(float) * SLB<JT>::SIZE;
           // the save buffer holds both the checkpoints and the residuals
           if (A.s.Sck != nullptr)
@@ -1730,6 +1775,7 @@ ChunkedSweepShape shape_of(const Args& a) {
   sh.Hk = a.Hk;
   sh.Hv = a.Hv;
   sh.Dk = a.Dk;
+  sh.Dv = a.Dv;
   sh.L = a.L;
   sh.nch = a.nch;
   sh.log_g = a.log_g;

@@ -73,7 +73,7 @@ struct BwdChunkedArgs {
 };
 // What the prep kernels read.
 struct ChunkedSweepShape {
-  int B, T, Hk, Hv, Dk, L, nch;
+  int B, T, Hk, Hv, Dk, Dv, L, nch;
   int log_g;
   const uint8_t* mask;
   const void* q;

@@ -222,6 +222,21 @@ def test_rows_per_lane_variants(cuda, B, dtype):
     compare(run_gpu(p, cuda, 16), run_oracle(p), TOL[dtype], f"wide B={B} {dtype}")
 
 
+@pytest.mark.parametrize("dims", [(72, 30), (68, 40), (136, 24), (192, 40)])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_bf16_dims(cuda, dims, chunk):
+    """bf16 inputs at the edges of the bf16-product kernels' shape conditions
+    (k rows in 8-element groups, value rows in 4-element blocks, dy rows in
+    8-element blocks for the chunk-parallel part): Dk=72 with Dv=30 and Dk=68
+    take the fp32-operand kernels, Dk=136 pads a 192-column tile, Dv=40 leaves
+    a short last 32-row block; T=70 leaves a short last chunk."""
+    Dk, Dv = dims
+    p = inputs.draw(1, 70, 2, 4, Dk, Dv, seed=23, normalised=True, S0_std=0.2,
+                    dST_std=1.0, dtype="bf16")
+    log(f"bf16 dims Dk={Dk} Dv={Dv} chunk={chunk}")
+    compare(run_gpu(p, cuda, chunk), run_oracle(p), TOL["bf16"], f"bf16 Dk={Dk} Dv={Dv}")
+
+
 def test_bf16_small(cuda):
     p = inputs.draw(2, 70, 2, 4, 64, 32, seed=19, normalised=True, S0_std=0.1,
                     dST_std=1.0, dtype="bf16")
