@@ -337,8 +337,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     Quad<TIn, VEC> y[2];
     uint32_t ms;  // validity: 4 bits per S0/H1 quad, then 4 per dy/e/c quad
   };
-  // S0, H1, E, C are read once here: non-temporal loads keep them from
-  // displacing the lines the workgroup reads again
+  // S0, H1, E, C (and dy) are read once here: non-temporal loads keep them
+  // from displacing the lines the workgroup reads again
   auto ld_nt = [](const float* p, int64_t o, bool ok) __attribute__((always_inline)) {
     const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p + (ok ? o : 0)));
     return float4{x[0], x[1], x[2], x[3]};
@@ -386,7 +386,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const bool ok = ts < n && i < Dv;
         int64_t o = ok ? rowbase + ts * tstride + i : 0;
         asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
-        R.y = *reinterpret_cast<const uint4*>(dy + o);
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 yv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dy + o));
+        R.y = uint4{yv[0], yv[1], yv[2], yv[3]};
         m |= (uint32_t)ok << 4;
       }
       R.ms = m;

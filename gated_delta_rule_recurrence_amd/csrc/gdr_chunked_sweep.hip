@@ -535,6 +535,22 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
 // the state tiles (rows 16 (w % 2) .., Dk columns 16 (JW (w / 2) + nj) ..)
 // of the state update.
 
+// The sweeps' workgroup (row slice, value head, batch row) in an XCD-aware
+// order.  Workgroups go to the 8 XCDs round-robin by linear id; numbering
+// them so that consecutive ids share an XCD puts the row slices of a value
+// head (one prep record) and the value heads of a kv head (one k, q) in one
+// XCD's L2.  Any order is correct; this one only saves cache traffic.
+struct SweepBlock {
+  int x, h, b;
+};
+__device__ __forceinline__ SweepBlock sweep_block() {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int total = nx * ny * gridDim.z;
+  const int lin = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int id = total % 8 == 0 ? (lin % 8) * (total / 8) + lin / 8 : lin;
+  return SweepBlock{id % nx, (id / nx) % ny, id / (nx * ny)};
+}
+
 // The k, q rows of a chunk: fetched into registers a chunk ahead (raw bits,
 // masked where deposited), then deposited into the natural-layout LDS stages
 // [kN][KLD] with zero padding columns.
@@ -710,7 +726,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
   const TIn* __restrict__ v = static_cast<const TIn*>(a.v);
   TIn* __restrict__ y = static_cast<TIn*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const SweepBlock wb = sweep_block();
+  const int i0 = wb.x * kDS, h = wb.h, b = wb.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -967,7 +984,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   const bf16* __restrict__ v = static_cast<const bf16*>(a.v);
   bf16* __restrict__ y = static_cast<bf16*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const SweepBlock wb = sweep_block();
+  const int i0 = wb.x * kDS, h = wb.h, b = wb.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1252,7 +1270,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_kernel(BwdChunkedAr
   const TIn* __restrict__ dy = static_cast<const TIn*>(a.dy);
   TIn* __restrict__ dv = static_cast<TIn*>(a.dv);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const SweepBlock wb = sweep_block();
+  const int i0 = wb.x * kDS, h = wb.h, b = wb.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1454,7 +1473,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   const bf16* __restrict__ dy = static_cast<const bf16*>(a.dy);
   bf16* __restrict__ dv = static_cast<bf16*>(a.dv);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int i0 = blockIdx.x * kDS, h = blockIdx.y, b = blockIdx.z;
+  const SweepBlock wb = sweep_block();
+  const int i0 = wb.x * kDS, h = wb.h, b = wb.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
