@@ -943,22 +943,21 @@ struct SLB {
   static constexpr int KTS = kN + 8;              // bf16 row stride of the step pieces
   static constexpr int PS = kDS * KTS;            // bf16 stride of one step piece
   static constexpr int KR = 0;                    // float offsets below
-  static constexpr int SP = KR + kN * KRS / 2;
+  static constexpr int QR = KR + kN * KRS / 2;
+  static constexpr int SP = QR + kN * KRS / 2;
   static constexpr int EP = SP + 3 * DKP * kDS / 2;  // diag(ks) E pieces
   static constexpr int UP = EP + 3 * PS / 2;          // U pieces
   static constexpr int EQ = UP + 3 * PS / 2;          // E pieces
   // output stages, copied out in 16-byte (y: 8-byte) row blocks after a
-  // later barrier: the state checkpoint fp32 [kDS][SKS], E fp32 [kN][OES],
-  // y bf16 [kN][OYS]
-  static constexpr int SKS = DKP + 4, OES = kDS + 4, OYS = kDS + 8;
-  static constexpr int SC = EQ + 3 * PS / 2;
-  static constexpr int OE = SC + kDS * SKS;
+  // later barrier: E fp32 [kN][OES], y bf16 [kN][OYS]
+  static constexpr int OES = kDS + 4, OYS = kDS + 8;
+  static constexpr int OE = EQ + 3 * PS / 2;
   static constexpr int OY = OE + kN * OES;
   static constexpr int SIZE = OY + kN * OYS / 2;
   static_assert((2 * KRS) % 256 == 128 && (2 * KTS) % 32 == 16, "row strides");
   static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
-  static_assert(SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0 && SC % 4 == 0 &&
-                    OE % 4 == 0 && OY % 4 == 0 && SKS % 4 == 0 && OES % 4 == 0,
+  static_assert(QR % 4 == 0 && SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0 &&
+                    OE % 4 == 0 && OY % 4 == 0 && OES % 4 == 0,
                 "16-byte aligned regions");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
@@ -974,6 +973,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   static_assert(JT % 4 == 0, "four waves of update tiles cover the Dk tiles");
   extern __shared__ __align__(16) float sm[];
   uint16_t* const kr = reinterpret_cast<uint16_t*>(sm + L::KR);
+  uint16_t* const qr = reinterpret_cast<uint16_t*>(sm + L::QR);
   uint16_t* const sp = reinterpret_cast<uint16_t*>(sm + L::SP);
   uint16_t* const ep = reinterpret_cast<uint16_t*>(sm + L::EP);
   uint16_t* const up = reinterpret_cast<uint16_t*>(sm + L::UP);
@@ -1001,23 +1001,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   // k quads of a chunk (for the row-major k tile), a chunk ahead
   KQPrefetch<bf16, JT, true> kq;
   kq.init(tid);
-  // this wave's [K; Q] fragments: row tw + l % 16, columns 32 ks + 8 (l / 16)
-  // .. +7 of the chunk, a chunk ahead (raw bits; rows past the chunk and
-  // columns past Dk are zeroed where used)
-  uint4 kf[NKS], qf[NKS];
-  auto fetch_frags = [&](int c, int lr, int lq) __attribute__((always_inline)) {
-    const int64_t base = kq_base(c);
-    const bool rok = tw + lr < chunk_len(c);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int j = 32 * ks + 8 * lq;
-      int o = rok && j < Dk ? (tw + lr) * kst + j : 0;
-      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
-      kf[ks] = *reinterpret_cast<const uint4*>(k + base + o);
-      qf[ks] = *reinterpret_cast<const uint4*>(q + base + o);
-    }
-  };
-
   f4 Sacc[JW];
   {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1030,11 +1013,13 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         Sacc[nj][u] = ok ? a.S0[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
       }
     kq.fetch(k, q, kq_base(0), chunk_len(0), kst, Dk);
-    fetch_frags(0, lr, lq);
   }
-  // the state tiles into the three j-major bf16 pieces (and, saving, into
-  // the checkpoint stage)
-  auto put_state = [&](int lr, int lq) __attribute__((always_inline)) {
+  // the state tiles into the three j-major bf16 pieces (and checkpoint
+  // `slot`, or the sink when slot < 0; out-of-range lanes store to the sink
+  // too)
+  auto put_state = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
+    float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat : nullptr;
+    asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) {
       const int j = 16 * (jg + nj) + lr;
@@ -1042,7 +1027,13 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       split3_quad(Sacc[nj], p0, p1, p2);
       if (SAVE) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sm[L::SC + (16 * mt + 4 * lq + u) * L::SKS + j] = Sacc[nj][u];
+        for (int u = 0; u < 4; ++u) {
+          const int i = 16 * mt + 4 * lq + u;
+          const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
+          // read once, by the reverse pass: streamed past the caches that
+          // hold the k, q and record lines the workgroups share
+          __builtin_nontemporal_store(Sacc[nj][u], ok ? ck + (int64_t)(i0 + i) * Dk + j : sink);
+        }
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
       *reinterpret_cast<uint2*>(sp + 0 * DKP * kDS + o) = p0;
@@ -1053,26 +1044,10 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_state(tl & 15, (tl & 63) >> 4);
+    put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink + (tl & 63));
   }
-  // 16-byte blocks of the output stages to the tensors (lanes outside them
-  // store to the sink): the checkpoint stage to slot `slot`, E, y of chunk c
-  auto out_state = [&](int slot, float* sink) __attribute__((always_inline)) {
-    int tl = tid;
-    asm volatile("" : "+v"(tl));
-    float* __restrict__ ck = a.Sck + (bh * a.nch + slot) * mat;
-    constexpr int NB = kDS * (DKP / 4);  // 16-byte blocks of the stage
-#pragma unroll
-    for (int x = 0; x < (NB + kSwThreads - 1) / kSwThreads; ++x) {
-      const int bk = tl + kSwThreads * x;
-      const int r = bk / (DKP / 4), j = 4 * (bk % (DKP / 4));
-      const bool ok = bk < NB && i0 + r < Dv && j < Dk;
-      const f4 v = *reinterpret_cast<const f4*>(sm + L::SC + (bk < NB ? r : 0) * L::SKS + j);
-      // read once, by the reverse pass: streamed past the caches that hold
-      // the k, q and record lines the workgroups share
-      __builtin_nontemporal_store(v, reinterpret_cast<f4*>(ok ? ck + (int64_t)(i0 + r) * Dk + j : sink));
-    }
-  };
+  // 16-byte (y: 8-byte) row blocks of the E, y stages of a chunk to the
+  // tensors (lanes outside them store to the sink)
   auto out_rows = [&](int64_t vbase, int n, float* sink) __attribute__((always_inline)) {
     int tl = tid;
     asm volatile("" : "+v"(tl));
@@ -1100,25 +1075,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
     float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
+    float* const sink = sink16 + l;
     const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
-    deposit_rows<KRS>(kq, kr, nullptr);
-    // this chunk's fragments, masked
-    uint4 ak[NKS], aq[NKS];
-    {
-      const bool rok = tw + lr < n;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const bool ok = rok && 32 * ks + 8 * lq < Dk;
-        ak[ks].x = ok ? kf[ks].x : 0u;
-        ak[ks].y = ok ? kf[ks].y : 0u;
-        ak[ks].z = ok ? kf[ks].z : 0u;
-        ak[ks].w = ok ? kf[ks].w : 0u;
-        aq[ks].x = ok ? qf[ks].x : 0u;
-        aq[ks].y = ok ? qf[ks].y : 0u;
-        aq[ks].z = ok ? qf[ks].z : 0u;
-        aq[ks].w = ok ? qf[ks].w : 0u;
-      }
-    }
+    deposit_rows<KRS>(kq, kr, qr);
     uint4 tp[2][3], mp[2][3];  // T, M pieces of this wave's step tile
     float gam[4], ksc[4];
     bf16 vr[4];
@@ -1141,11 +1100,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     {
       const int cn = min(c + 1, a.nch - 1);
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
-      fetch_frags(cn, lr, lq);
     }
     __syncthreads();
-    // the checkpoint of this chunk's start state, staged by the last put_state
-    if (SAVE) out_state(c, sink16);
 
     // X = [K; Q] S0^T: three bf16 pieces of S, one accumulator per piece
     f4 XK, XQ;
@@ -1154,13 +1110,19 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
       for (int p = 0; p < 3; ++p) xk[p] = xq[p] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int ks = 0; ks < NKS; ++ks) {
+        // rows tw + l % 16 of the k, q tiles, columns 32 ks + 8 (l / 16) ..:
+        // 4-element blocks 2c, 2c + 1 stay adjacent under the swizzle
+        const int t = tw + lr, o = t * KRS + 4 * ((2 * (4 * ks + lq)) ^ tile_swz(t));
+        const uint4 ak = *reinterpret_cast<const uint4*>(kr + o);
+        const uint4 aq = *reinterpret_cast<const uint4*>(qr + o);
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
           const uint4 bs = piece_operand(sp + p * DKP * kDS, 32 * ks, 16 * nt, lr, lq);
-          xk[p] = mfma_bf16(ak[ks], bs, xk[p]);
-          xq[p] = mfma_bf16(aq[ks], bs, xq[p]);
+          xk[p] = mfma_bf16(ak, bs, xk[p]);
+          xq[p] = mfma_bf16(aq, bs, xq[p]);
         }
+      }
       XK = (xk[0] + xk[1]) + xk[2];
       XQ = (xq[0] + xq[1]) + xq[2];
     }
@@ -1240,7 +1202,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     }
     __syncthreads();  // stage reads done before it is rewritten
     out_rows(vbase, n, sink16);  // E, y of this chunk, staged before the barrier
-    if (c + 1 < a.nch) put_state(lr, lq);
+    put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink);
   }
   if (a.ST != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1490,20 +1452,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
 
   KQPrefetch<bf16, JT, true> kq;
   kq.init(tid);
-  // this wave's K fragments (row tw + l % 16, columns 32 ks + 8 (l / 16)..),
-  // a chunk ahead
-  uint4 kf[NKS];
-  auto fetch_frags = [&](int c, int lr, int lq) __attribute__((always_inline)) {
-    const int64_t base = kq_base(c);
-    const bool rok = tw + lr < chunk_len(c);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int j = 32 * ks + 8 * lq;
-      int o = rok && j < Dk ? (tw + lr) * kst + j : 0;
-      asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
-      kf[ks] = *reinterpret_cast<const uint4*>(k + base + o);
-    }
-  };
   // dy of this wave's tile (step tw + 4 lq + u, row i0 + ti), a chunk ahead
   bf16 dr[4];
   uint32_t dm = 0;
@@ -1534,7 +1482,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         Hacc[nj][u] = ok ? a.dST[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
       }
     kq.fetch(k, q, kq_base(cl), chunk_len(cl), kst, Dk);
-    fetch_frags(cl, lr, lq);
     fetch_dy(cl, lq, 16 * nt + lr, i0 + 16 * nt + lr < Dv);
   }
   // gradient tiles into the three j-major bf16 pieces and into checkpoint
@@ -1578,19 +1525,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
     const int64_t vbase = v_base(c);
     deposit_rows<KRS>(kq, kr, qr);
-    uint4 ak[NKS];
-    {
-      const bool rok = tw + lr < n;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        // component selects: a select of the whole vector would go through memory
-        const bool ok = rok && 32 * ks + 8 * lq < Dk;
-        ak[ks].x = ok ? kf[ks].x : 0u;
-        ak[ks].y = ok ? kf[ks].y : 0u;
-        ak[ks].z = ok ? kf[ks].z : 0u;
-        ak[ks].w = ok ? kf[ks].w : 0u;
-      }
-    }
     // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
     const int so = ti * KTS + tw + 4 * lq;
     auto put_steps = [&](uint16_t* dst, f4 v) __attribute__((always_inline)) {
@@ -1631,7 +1565,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     {
       const int cn = max(c - 1, 0);
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
-      fetch_frags(cn, lr, lq);
       fetch_dy(cn, lq, ti, iok);
     }
     __syncthreads();
@@ -1643,11 +1576,15 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
 #pragma unroll
       for (int p = 0; p < 3; ++p) x3[p] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+      for (int ks = 0; ks < NKS; ++ks) {
+        // row tw + l % 16 of the k tile, columns 32 ks + 8 (l / 16) ..
+        const int t = tw + lr;
+        const uint4 ak =
+            *reinterpret_cast<const uint4*>(kr + t * KRS + 4 * ((2 * (4 * ks + lq)) ^ tile_swz(t)));
 #pragma unroll
         for (int p = 0; p < 3; ++p)
-          x3[p] = mfma_bf16(ak[ks], piece_operand(ht + p * DKP * kDS, 32 * ks, 16 * nt, lr, lq),
-                            x3[p]);
+          x3[p] = mfma_bf16(ak, piece_operand(ht + p * DKP * kDS, 32 * ks, 16 * nt, lr, lq), x3[p]);
+      }
       X = (x3[0] + x3[1]) + x3[2];
     }
     // U = diag(suf) X + Mq DY; diag(pre) DY as three bf16 pieces [i][t]
