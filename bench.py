@@ -51,8 +51,8 @@ def sources_digest(files):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--T", type=int, default=2048)
     ap.add_argument("--B", type=int, default=1)
     ap.add_argument("--chunk", type=int, default=64)
