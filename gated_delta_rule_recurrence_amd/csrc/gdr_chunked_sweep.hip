@@ -111,23 +111,29 @@ __device__ __forceinline__ void pieces_to_record(float* __restrict__ dst, int l,
   }
 }
 
-// The pieces of k-steps 0, 1 of step tile tb (lane l), as written above
+// The pieces of k-steps 0, 1 of step tile tb (lane l), as written above,
+// except k-step `zero` (wave-uniform; -1: none), a block of zeros that the
+// products skip (the triangular matrices' blocks past the diagonal)
 __device__ __forceinline__ void pieces_from_record(const float* __restrict__ src, int tb, int l,
-                                                   uint4 (&f)[2][3]) {
+                                                   int zero, uint4 (&f)[2][3]) {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
+  for (int ks = 0; ks < 2; ++ks) {
+    if (ks == zero) continue;
 #pragma unroll
     for (int p = 0; p < 3; ++p)
       f[ks][p] = *reinterpret_cast<const uint4*>(src + ((3 * (2 * tb + ks) + p) * 64 + l) * 4);
+  }
 }
 
 // acc += A B over the 64 steps with both operands as three bf16 pieces: the
 // six piece products down to the order of fp32 rounding.  a: A pieces per
-// k-step (registers); b(ks, p): B piece p of k-step ks.
+// k-step (registers); b(ks, p): B piece p of k-step ks; k-step `zero` of A
+// is zero and skipped.
 template <typename BFn>
-__device__ __forceinline__ f4 mfma_pieces6(const uint4 (&a)[2][3], BFn b, f4 acc) {
+__device__ __forceinline__ f4 mfma_pieces6(const uint4 (&a)[2][3], BFn b, int zero, f4 acc) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
+    if (ks == zero) continue;
     const uint4 b0 = b(ks, 0), b1 = b(ks, 1), b2 = b(ks, 2);
     acc = mfma_bf16(a[ks][0], b0, acc);
     acc = mfma_bf16(a[ks][0], b1, acc);
@@ -543,6 +549,12 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
 struct SweepBlock {
   int x, h, b;
 };
+
+// Step tile tb (steps 16 tb ..) and row tile nt of wave w in the bf16-product
+// sweeps: a SIMD's two waves (w, w + 4) take tiles 0 or 1 and 2 or 3, one
+// with a zero k-step in the triangular products and one without, so that
+// the SIMDs carry equal work.
+__device__ __forceinline__ int sweep_tb(int w) { return w < 4 ? w >> 1 : 2 + ((w - 4) >> 1); }
 __device__ __forceinline__ SweepBlock sweep_block() {
   const int nx = gridDim.x, ny = gridDim.y;
   const int total = nx * ny * gridDim.z;
@@ -989,7 +1001,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tb = w & 3, nt = w >> 2;
+  const int tb = sweep_tb(w), nt = w & 1;
+  // T, M are lower triangular: k-step 1 of step tiles 0, 1 is zero
+  const int zk = tb < 2 ? 1 : -1;
   const int mt = w & 1, jg = JW * (w >> 1);
   const int tw = 16 * tb;
   const int64_t bh = (int64_t)b * Hv + h;
@@ -1082,7 +1096,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     float gam[4], ksc[4];
     bf16 vr[4];
     uint32_t vm = 0;
-    pieces_from_record(rec + kBrT, tb, l, tp);
+    pieces_from_record(rec + kBrT, tb, l, zk, tp);
     {
       const f4 g4 = *reinterpret_cast<const f4*>(rec + kBrGam + tw + 4 * lq);
       const f4 k4 = *reinterpret_cast<const f4*>(rec + kBrKs + tw + 4 * lq);
@@ -1126,7 +1140,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       XK = (xk[0] + xk[1]) + xk[2];
       XQ = (xq[0] + xq[1]) + xq[2];
     }
-    pieces_from_record(rec + kBrM, tb, l, mp);
+    pieces_from_record(rec + kBrM, tb, l, zk, mp);
     // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
     const int so = ti * KTS + tw + 4 * lq;
     auto put_steps = [&](uint16_t* dst, f4 v) __attribute__((always_inline)) {
@@ -1156,7 +1170,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     // E = T U; E and diag(ks) E as three bf16 pieces each (row i, column t)
     {
       const f4 E = mfma_pieces6(
-          tp, [&](int ks, int p) { return step_piece(up, ks, p); }, f4{0.f, 0.f, 0.f, 0.f});
+          tp, [&](int ks, int p) { return step_piece(up, ks, p); }, zk, f4{0.f, 0.f, 0.f, 0.f});
       f4 ke;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -1174,7 +1188,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       f4 Yv;
 #pragma unroll
       for (int u = 0; u < 4; ++u) Yv[u] = gam[u] * XQ[u];
-      Yv = mfma_pieces6(mp, [&](int ks, int p) { return step_piece(eq, ks, p); }, Yv);
+      Yv = mfma_pieces6(mp, [&](int ks, int p) { return step_piece(eq, ks, p); }, zk, Yv);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
@@ -1440,7 +1454,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tb = w & 3, nt = w >> 2;
+  const int tb = sweep_tb(w), nt = w & 1;
+  // Tb, Mq are upper triangular: k-step 0 of step tiles 2, 3 is zero
+  const int zk = tb >= 2 ? 0 : -1;
   const int mt = w & 1, jg = JW * (w >> 1);
   const int tw = 16 * tb;
   const int64_t bh = (int64_t)b * Hv + h;
@@ -1552,8 +1568,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     }
     uint4 tp[2][3], mp[2][3];  // Tb, Mq pieces of this wave's step tile
     float suf[4], pre[4], bet[4];
-    pieces_from_record(rec + kBbT, tb, l, tp);
-    pieces_from_record(rec + kBbM, tb, l, mp);
+    pieces_from_record(rec + kBbT, tb, l, zk, tp);
+    pieces_from_record(rec + kBbM, tb, l, zk, mp);
     {
       const f4 s4 = *reinterpret_cast<const f4*>(rec + kBbSuf + tw + 4 * lq);
       const f4 p4 = *reinterpret_cast<const f4*>(rec + kBbPre + tw + 4 * lq);
@@ -1595,6 +1611,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       // Mq DY: dy is bf16, so the three Mq pieces give the exact products
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        if (ks == zk) continue;
         const uint4 bd = step_piece(dyt, ks, 0);
 #pragma unroll
         for (int p = 0; p < 3; ++p) U = mfma_bf16(mp[ks][p], bd, U);
@@ -1610,7 +1627,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     // C = Tb U; dv = diag(beta) C; -diag(beta pre) C as three bf16 pieces
     {
       const f4 Cv = mfma_pieces6(
-          tp, [&](int ks, int p) { return step_piece(up, ks, p); }, f4{0.f, 0.f, 0.f, 0.f});
+          tp, [&](int ks, int p) { return step_piece(up, ks, p); }, zk, f4{0.f, 0.f, 0.f, 0.f});
       f4 pc;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
