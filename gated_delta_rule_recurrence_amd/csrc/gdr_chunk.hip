@@ -337,8 +337,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     Quad<TIn, VEC> y[2];
     uint32_t ms;  // validity: 4 bits per S0/H1 quad, then 4 per dy/e/c quad
   };
-  // S0, H1, E, C (and dy) are read once here: non-temporal loads keep them
-  // from displacing the lines the workgroup reads again
+  // S0, H1 slices are read once (each pass its own columns): non-temporal
+  // loads keep them from displacing the dy, C, E rows that every pass of a
+  // value head reads again
   auto ld_nt = [](const float* p, int64_t o, bool ok) __attribute__((always_inline)) {
     const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p + (ok ? o : 0)));
     return float4{x[0], x[1], x[2], x[3]};
@@ -377,8 +378,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const int i = i0 + 4 * iq + 16 * u;
         const bool ok = ts < n && i < Dv;
         const int64_t o = rowbase + ts * tstride + i;
-        R.e[u].v = ld_nt(a.E, o, ok);
-        R.c[u].v = ld_nt(a.C, o, ok);
+        R.e[u].load(a.E, o, ok, 4);
+        R.c[u].load(a.C, o, ok, 4);
         m |= (uint32_t)ok << (2 + u);
       }
       {
@@ -386,9 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const bool ok = ts < n && i < Dv;
         int64_t o = ok ? rowbase + ts * tstride + i : 0;
         asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
-        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-        const u32x4 yv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dy + o));
-        R.y = uint4{yv[0], yv[1], yv[2], yv[3]};
+        R.y = *reinterpret_cast<const uint4*>(dy + o);
         m |= (uint32_t)ok << 4;
       }
       R.ms = m;
