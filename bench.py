@@ -63,6 +63,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read + write), "
                          "the reference for scaling HBM byte counters, and exit")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="instead of the training step, time fwd+bwd at the long-context "
+                         "shape (B=4, T=8192, Qwen3.5-9B heads, trainable S0) for the "
+                         "chunk sizes 8..64 the library takes, one JSON line each, and exit")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="instead of the training step, time single-step inference "
                          "(T=1, state updated in place, no save buffer) at batch B "
@@ -122,6 +126,74 @@ def decode(args):
                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                                    "algorithmic_bytes_per_step": nbytes}}), flush=True)
+
+
+def chunk_sweep(args):
+    """Long-context training step (B=4, T=8192, Hk=16, Hv=64, Dk=192, Dv=128,
+    S0 ~ N(0, 0.05), decay alternating weak/strong over value heads) for each
+    chunk size C: median fwd and bwd times by HIP events, save-buffer and
+    workspace sizes, algorithmic HBM bytes.  Inputs drawn on the device
+    (inputs.draw_device: the draw() distributions)."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib, inputs, ops
+    dev = torch.device("cuda:0")
+    _lib.load()
+    B, T, Hk, Hv, Dk, Dv = 4, 8192, 16, 64, 192, 128
+    d = inputs.draw_device(B, T, Hk, Hv, Dk, Dv, device=dev, seed=args.seed, decay="mix",
+                           S0_std=0.05, dtype=args.dtype)
+    q, k, v, g, beta, dy, S0 = (d[n] for n in ("q", "k", "v", "g", "beta", "dy", "S0"))
+    esz = 2 if args.dtype == "bf16" else 4
+    for C in (8, 16, 32, 64):  # the library's range: a chunk is one 64-step tile
+        shape = ops.shape_of(q, v, C, q.dtype)
+        ckpt = torch.empty(_lib.checkpoint_bytes(shape), dtype=torch.uint8, device=dev)
+        ws = torch.empty(_lib.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
+        fws = torch.empty(max(_lib.forward_workspace_bytes(shape), 1), dtype=torch.uint8,
+                          device=dev)
+        y = torch.empty_like(v)
+        S_T = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
+                torch.empty_like(g), torch.empty_like(beta), torch.empty_like(S_T))
+        saved = ops.Saved(ckpt, C)
+
+        def fwd():
+            ops.gdr_forward(q, k, v, g, beta, S0, chunk=C, y=y, S_T=S_T, ckpt=ckpt,
+                            workspace=fws)
+
+        def bwd():
+            ops.gdr_backward(q, k, g, beta, saved, dy, None, workspace=ws, out=outs)
+
+        for _ in range(3):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        n = 10
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for i in range(n):
+            ev[i][0].record()
+            fwd()
+            ev[i][1].record()
+            bwd()
+            ev[i][2].record()
+        torch.cuda.synchronize()
+        f = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+        b = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
+        nch = -(-T // C)
+        tok_in = B * T * (2 * Hk * Dk + Hv * Dv + 2 * Hv) * esz
+        rows32 = B * T * Hv * Dv * 4
+        state = B * Hv * Dv * Dk * 4
+        nbytes = (2 * tok_in + B * T * Hv * Dv * esz + 2 * rows32 + (2 * nch + 3) * state
+                  + tok_in)
+        print(json.dumps({"chunk_sweep": {
+            "C": C, "B": B, "T": T, "dtype": args.dtype,
+            "path": "chunked" if _lib.forward_workspace_bytes(shape) > 0 else "sweep",
+            "fwd_ms_median": f, "bwd_ms_median": b, "tokens_per_s": B * T / ((f + b) * 1e-3),
+            "checkpoint_MB": ckpt.numel() / 1e6, "workspace_fwd_MB": fws.numel() / 1e6,
+            "workspace_bwd_MB": ws.numel() / 1e6,
+            "algorithmic_bytes": nbytes,
+            "hbm_frac_algorithmic": nbytes / ((f + b) * 1e-3) / 1e9 / HBM_PEAK_GBS}}),
+            flush=True)
+        del ckpt, ws, fws, y, S_T, outs, saved
+        torch.cuda.empty_cache()
 
 
 def copy_calibration(mib):
@@ -185,6 +257,9 @@ def main():
     if args.decode:
         decode(args)
         return
+    if args.chunk_sweep:
+        chunk_sweep(args)
+        return
     import torch
     from gated_delta_rule_recurrence_amd import _lib, inputs, ops
 
@@ -240,6 +315,23 @@ def main():
     wall = time.perf_counter() - t0
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in ev])
+
+    # the same steps with the caches flushed before each (a 512 MiB write,
+    # outside the timed events, evicts L2 and the 256 MB Infinity Cache)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    nflush = min(args.steps, 20)
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nflush)]
+    for i in range(nflush):
+        flush.zero_()
+        evf[i][0].record(stream)
+        fwd()
+        bwd()
+        evf[i][1].record(stream)
+    torch.cuda.synchronize()
+    flushed_ms = np.array([e[0].elapsed_time(e[1]) for e in evf])
+    del flush
+    peak_mb = torch.cuda.max_memory_allocated(dev) / 1e6
     ms = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms / 1e3)
@@ -300,6 +392,11 @@ def main():
                     "flops_per_launch": fwd_flops, "algorithmic_bytes_per_launch": fwd_bytes,
                     "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "avg_launch_ms": fwd_ms},
+        "timing": {"wall_ms_per_step": ms, "step_ms_median": float(np.median(step_ms)),
+                   "step_ms_min": float(step_ms.min()),
+                   "flushed_step_ms_median": float(np.median(flushed_ms)),
+                   "flushed_step_ms_min": float(flushed_ms.min()), "flushed_steps": nflush},
+        "peak_device_memory_MB": peak_mb,
         "breakdown": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                       "useful_tflops_whole_step": all_tf,
                       "frac_whole_step_vs_fp32_peak": all_tf / FP32_PEAK_TF,

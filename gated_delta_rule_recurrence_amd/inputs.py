@@ -150,6 +150,46 @@ def draw(B, T, Hk, Hv, Dk, Dv, *, seed=0, normalised=False, decay="weak",
     return p
 
 
+def draw_device(B, T, Hk, Hv, Dk, Dv, *, device, seed=0, normalised=True, decay="weak",
+                S0_std=None, dtype="bf16"):
+    """The distributions of draw() sampled directly on a torch device (its
+    own seeded generator, so not the same numbers as draw()): for timing
+    workloads too large to draw on the host in float64.  Returns a dict of
+    device tensors q, k, v, g, beta, dy (in `dtype`) and S0 (fp32 or None).
+    decay "mix": weak on even value heads, strong on odd ones."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    f32 = dict(device=device, dtype=torch.float32, generator=gen)
+
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+
+    q = torch.randn((B, T, Hk, Dk), **f32)
+    k = torch.randn((B, T, Hk, Dk), **f32)
+    if normalised:
+        q = unit(q) * Dk ** -0.5
+        k = unit(k)
+    v = torch.randn((B, T, Hv, Dv), **f32)
+    if decay == "weak":
+        mu = torch.full((Hv,), -2.0, device=device)
+    elif decay == "strong":
+        mu = torch.full((Hv,), 2.0, device=device)
+    elif decay == "mix":
+        mu = torch.where(torch.arange(Hv, device=device) % 2 == 0, -2.0, 2.0)
+    else:
+        raise ValueError(decay)
+    g = torch.exp(-torch.exp(torch.randn((B, T, Hv), **f32) * 0.5 + mu))
+    beta = torch.sigmoid(torch.randn((B, T, Hv), **f32))
+    dy = torch.randn((B, T, Hv, Dv), **f32)
+    S0 = None if S0_std is None else torch.randn((B, Hv, Dv, Dk), **f32) * S0_std
+    out = {n: x.to(dt).contiguous() for n, x in
+           dict(q=q, k=k, v=v, g=g, beta=beta, dy=dy).items()}
+    out["S0"] = S0
+    return out
+
+
 # ---- the five workload recipes -------------------------------------------
 
 def toy(seed=0, with_dST=False) -> Problem:
