@@ -449,14 +449,16 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     // Gam(r,t] (lane l <-> t = l) as a running product down the rows:
     // Gam(t-1,t] = g_t, Gam(r,t] = g_{r+1} Gam(r+1,t]; 1 on the diagonal and
     // 0 below it (rows r > t).  G[r][t] holds it.
+    // (g_{r+1} read from lane r + 1, so the loop holds only LDS stores)
     float p = 1.f;
 #pragma unroll 8
     for (int r = kN - 1; r >= 0; --r) {
-      const float gr = r + 1 < kN ? vg[r + 1] : 1.f;
+      const float gr =
+          r + 1 < kN ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), r + 1)) : 1.f;
       p = r < l ? p * gr : p;
       G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
     }
-    const float pre = vg[0] * p;                      // Gam(-1, l] = g_0 Gam(0, l]
+    const float pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * p;  // Gam(-1, l] = g_0 Gam(0, l]
     const float suf = l < n ? G[l * kGP + n - 1] : 0.f;  // Gam(l, n-1]
     // bf16 inputs in 8-element groups: the bf16-product sweeps read the
     // matrices as bf16 pieces
@@ -479,9 +481,16 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
         }
         *reinterpret_cast<f4*>(rec + kPrM + (bx * 64 + l) * 4) = m4;
       }
-      // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r)
-      for (int t = 1; t < kN; ++t)
-        if (l < t) G[t * kGP + l] = G[l * kGP + t] * KK[t * kNP + l] * bl;
+      // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r):
+      // all of the lane's operands loaded first, then the stores
+      {
+        float av[kN];
+#pragma unroll
+        for (int t = 1; t < kN; ++t) av[t] = G[l * kGP + t] * KK[t * kNP + l] * bl;
+#pragma unroll
+        for (int t = 1; t < kN; ++t)
+          if (l < t) G[t * kGP + l] = av[t];
+      }
       // T = (I + A)^-1 in place of A
       invert_unit_triangular<false>(G, l);
       if (pieces) {
@@ -515,8 +524,14 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       }
       // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
       // diagonal (lane l <-> s)
-      for (int t = 0; t < kN - 1; ++t)
-        if (l > t) G[t * kGP + l] *= bl * KK[l * kNP + t];
+      {
+        float bv[kN];  // the lane's operands first, then the updates
+#pragma unroll
+        for (int t = 0; t < kN - 1; ++t) bv[t] = bl * KK[l * kNP + t] * G[t * kGP + l];
+#pragma unroll
+        for (int t = 0; t < kN - 1; ++t)
+          if (l > t) G[t * kGP + l] = bv[t];
+      }
       // Tb = (I + Bm)^-1 in place of Bm
       invert_unit_triangular<true>(G, l);
       if (pieces) {
