@@ -105,6 +105,7 @@ struct CL {  // LDS layout, offsets in floats
                        V_CHI = VEC + 5 * kN, V_PSI = VEC + 6 * kN,
                        V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;  // kThreads
   // persistent per workgroup: QK, KK and the head sums W1, -W2, Wq [kN][kNP]
+  static_assert(V_SCR % 4 == 0, "16-byte reads of the partials");
   static constexpr int QK = V_SCR + kThreads, KK = QK + kN * kNP,
                        W1 = KK + kN * kNP, W2 = W1 + kN * kNP,
                        WQ = W2 + kN * kNP;
@@ -480,24 +481,29 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     }
     }
   };
+  // g, beta of step tid (threads tid < kN), a value head ahead; an identity
+  // step (mask byte 0) has g = 1, beta = 0
+  const bool gb_ok = tid < n;
+  const bool gb_skip = gb_ok && skipped(a.mask, b, T, t0 + tid);
+  auto gb_index = [&](int hh) {
+    return (int64_t)(b * (int64_t)T + t0 + (gb_ok ? tid : 0)) * Hv + hk * rep + hh;
+  };
+  TIn g_nx = g[gb_index(0)], b_nx = beta[gb_index(0)];
   fetch(RA, 0);
   fetch(RB, 1);
 
   for (int hh = 0; hh < rep; ++hh) {
-    const int h = hk * rep + hh;
-
     // per-head vectors: g, beta and the running decay products
     if (tid < kN) {
-      // an identity step (mask byte 0) has g = 1, beta = 0
-      const bool ok = tid < n;
-      const bool skip = ok && skipped(a.mask, b, T, t0 + tid);
-      sm[L::V_G + tid] =
-          !ok ? 0.f
-              : skip ? 1.f
-                     : decay_of(ld(g, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h), a.log_g);
-      sm[L::V_B + tid] =
-          ok && !skip ? ld(beta, (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h) : 0.f;
+      sm[L::V_G + tid] = !gb_ok ? 0.f : gb_skip ? 1.f : decay_of(to_f32(g_nx), a.log_g);
+      sm[L::V_B + tid] = gb_ok && !gb_skip ? to_f32(b_nx) : 0.f;
     }
+    {
+      const int hn = hh + 1 < rep ? hh + 1 : hh;  // (unconditional: clamped)
+      g_nx = g[gb_index(hn)];
+      b_nx = beta[gb_index(hn)];
+    }
+    const int h = hk * rep + hh;
     __syncthreads();
     if (w == 3) {  // decay products along the chunk, one step per lane
       // pre[t] = Gam(start, t], prex[t] = Gam(start, t-1], suf[t] = Gam(t, end]
@@ -717,12 +723,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       }
     sm[L::V_SCR + tid] = hs;
     __syncthreads();
-    if (tid < 32) {  // <H1, S0>: 8 partials per thread, fixed order
-      float x = 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x += sm[L::V_SCR + tid * 8 + u];
-      sm[L::V_SCR + tid * 8] = x;
-    }
     {  // rows r = 16 w .. 16 w + 15 of Gam(r, t] (lane l <-> t = l)
       const float gl = l < n ? sm[L::V_G + l] : 1.f;
 #pragma unroll 4
@@ -733,10 +733,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       }
     }
     __syncthreads();
-    if (tid == 0) {
-      float x = 0.f;
-      for (int u = 0; u < 32; ++u) x += sm[L::V_SCR + u * 8];
-      sm[L::V_SCR + 1] = x;  // phi0 = <H1, S0>
+    if (w == 0) {  // phi0 = <H1, S0> from the 256 partials, in a fixed order
+      const f4 x4 = *reinterpret_cast<const f4*>(sm + L::V_SCR + 4 * l);
+      const float x = rowsum16((x4[0] + x4[1]) + (x4[2] + x4[3]));
+      const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+      const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+      const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+      const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+      if (l == 0) sm[L::V_SCR + 1] = (r0 + r1) + (r2 + r3);
     }
     if (tid < n)  // g and beta do not enter an identity step
       st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h,
