@@ -1583,7 +1583,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     }
     uint4 tp[2][3], mp[2][3];  // Tb, Mq pieces of this wave's step tile
     float suf[4], pre[4], bet[4];
-    pieces_from_record(rec + kBbT, tb, l, zk, tp);
     pieces_from_record(rec + kBbM, tb, l, zk, mp);
     {
       const f4 s4 = *reinterpret_cast<const f4*>(rec + kBbSuf + tw + 4 * lq);
@@ -1618,6 +1617,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
       X = (x3[0] + x3[1]) + x3[2];
     }
+    pieces_from_record(rec + kBbT, tb, l, zk, tp);  // first used by C = Tb U
     // U = diag(suf) X + Mq DY; diag(pre) DY as three bf16 pieces [i][t]
     {
       f4 U;
