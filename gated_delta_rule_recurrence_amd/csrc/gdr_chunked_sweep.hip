@@ -1055,14 +1055,15 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       uint2 p0, p1, p2;
       split3_quad(Sacc[nj], p0, p1, p2);
       if (SAVE) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = 16 * mt + 4 * lq + u;
-          const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
-          // read once, by the reverse pass: streamed past the caches that
-          // hold the k, q and record lines the workgroups share
-          __builtin_nontemporal_store(Sacc[nj][u], ok ? ck + (int64_t)(i0 + i) * Dk + j : sink);
-        }
+        // after a transpose across each lane quad, lane 4a + b holds row
+        // 16 mt + 4 lq + b, columns 16 (jg + nj) + 4a .. +3: one 16-byte store
+        // (read once, by the reverse pass: streamed past the caches that
+        // hold the k, q and record lines the workgroups share)
+        const f4 rowv = quad_transpose(Sacc[nj], lr);
+        const int i = 16 * mt + 4 * lq + (lr & 3), jq = 16 * (jg + nj) + 4 * (lr >> 2);
+        const bool ok = slot >= 0 && i0 + i < Dv && jq < Dk;
+        __builtin_nontemporal_store(
+            rowv, reinterpret_cast<f4*>(ok ? ck + (int64_t)(i0 + i) * Dk + jq : sink));
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
       *reinterpret_cast<uint2*>(sp + 0 * DKP * kDS + o) = p0;
@@ -1073,7 +1074,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink + (tl & 63));
+    put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
   }
   // 16-byte (y: 8-byte) row blocks of the E, y stages of a chunk to the
   // tensors (lanes outside them store to the sink)
@@ -1104,7 +1105,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
     float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
-    float* const sink = sink16 + l;
     const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
     deposit_rows<KRS>(kq, kr, qr);
     uint4 tp[2][3], mp[2][3];  // T, M pieces of this wave's step tile
@@ -1231,7 +1231,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     }
     __syncthreads();  // stage reads done before it is rewritten
     out_rows(vbase, n, sink16);  // E, y of this chunk, staged before the barrier
-    put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink);
+    put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink16);
   }
   if (a.ST != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1517,7 +1517,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   }
   // gradient tiles into the three j-major bf16 pieces and into checkpoint
   // slot `slot` (slot < 0: the sink; out-of-range lanes store to the sink too)
-  auto put_grad = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
+  auto put_grad = [&](int slot, int lr, int lq, float* sink16) __attribute__((always_inline)) {
     float* __restrict__ hc = a.Hck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat;
     asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
 #pragma unroll
@@ -1525,12 +1525,15 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       const int j = 16 * (jg + nj) + lr;
       uint2 p0, p1, p2;
       split3_quad(Hacc[nj], p0, p1, p2);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = 16 * mt + 4 * lq + u;
-        const bool ok = slot >= 0 && i0 + i < Dv && j < Dk;
-        // read once, by the chunk-parallel pass: streamed past the caches
-        __builtin_nontemporal_store(Hacc[nj][u], ok ? hc + (int64_t)(i0 + i) * Dk + j : sink);
+      {
+        // after a transpose across each lane quad, lane 4a + b holds row
+        // 16 mt + 4 lq + b, columns 16 (jg + nj) + 4a .. +3: one 16-byte store
+        // (read once, by the chunk-parallel pass: streamed past the caches)
+        const f4 rowv = quad_transpose(Hacc[nj], lr);
+        const int i = 16 * mt + 4 * lq + (lr & 3), jq = 16 * (jg + nj) + 4 * (lr >> 2);
+        const bool ok = slot >= 0 && i0 + i < Dv && jq < Dk;
+        __builtin_nontemporal_store(
+            rowv, reinterpret_cast<f4*>(ok ? hc + (int64_t)(i0 + i) * Dk + jq : sink16));
       }
       const int o = j * kDS + 4 * ((4 * mt + lq) ^ p_swz(j));
       *reinterpret_cast<uint2*>(ht + 0 * DKP * kDS + o) = p0;
@@ -1541,7 +1544,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_grad(cl, tl & 15, (tl & 63) >> 4, A.prep + kPrSink + (tl & 63));
+    put_grad(cl, tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
   }
 
   for (int c = cl; c >= 0; --c) {
@@ -1681,7 +1684,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
     }
     __syncthreads();  // stage reads done before it is rewritten
-    put_grad(c - 1, lr, lq, sink);
+    put_grad(c - 1, lr, lq, A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink);
   }
   if (a.dS0 != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;

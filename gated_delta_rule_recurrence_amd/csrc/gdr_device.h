@@ -180,6 +180,27 @@ __device__ __forceinline__ uint4 tile_operand(const uint16_t* tile, int k0, int 
   return uint4{lo.x, lo.y, hi.x, hi.y};
 }
 
+// 4x4 transpose across the four lanes of each DPP quad: lane b holds
+// v[u] = M[u][b] before and M[b][u] after (two stages, each swapping the
+// elements whose lane and index differ in one bit with the partner lane).
+__device__ __forceinline__ f4 quad_transpose(f4 v, int lane) {
+  const int b = lane & 3;
+  f4 t;
+  t[0] = dpp<kDppQuadSwap1>(v[1]);
+  t[1] = dpp<kDppQuadSwap1>(v[0]);
+  t[2] = dpp<kDppQuadSwap1>(v[3]);
+  t[3] = dpp<kDppQuadSwap1>(v[2]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = ((b ^ u) & 1) ? t[u] : v[u];
+  t[0] = dpp<kDppQuadSwap2>(v[2]);
+  t[1] = dpp<kDppQuadSwap2>(v[3]);
+  t[2] = dpp<kDppQuadSwap2>(v[0]);
+  t[3] = dpp<kDppQuadSwap2>(v[1]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) v[u] = ((b ^ u) & 2) ? t[u] : v[u];
+  return v;
+}
+
 // DPP move with 1.0 in the lanes that get no source (the product identity).
 template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_or1(float x) {
