@@ -953,12 +953,28 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     if (t < n) {
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int j = 16 * jt + 4 * lq + v;
+        if constexpr (VEC) {
+          // columns 16 jt + 4 lq .. +3 of step t: one 4-element store each
+          const int j = 16 * jt + 4 * lq;
           if (j < Dk) {
-            st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[jt][v]);
-            st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[jt][v]);
+            if constexpr (std::is_same<TIn, bf16>::value) {
+              *reinterpret_cast<uint2*>(static_cast<bf16*>(a.dq) + qk_index(t, j)) =
+                  uint2{cvt_pk_bf16(dQ[jt][0], dQ[jt][1]), cvt_pk_bf16(dQ[jt][2], dQ[jt][3])};
+              *reinterpret_cast<uint2*>(static_cast<bf16*>(a.dk) + qk_index(t, j)) =
+                  uint2{cvt_pk_bf16(dK[jt][0], dK[jt][1]), cvt_pk_bf16(dK[jt][2], dK[jt][3])};
+            } else {
+              *reinterpret_cast<f4*>(static_cast<float*>(a.dq) + qk_index(t, j)) = dQ[jt];
+              *reinterpret_cast<f4*>(static_cast<float*>(a.dk) + qk_index(t, j)) = dK[jt];
+            }
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int j = 16 * jt + 4 * lq + v;
+            if (j < Dk) {
+              st(static_cast<TIn*>(a.dq), qk_index(t, j), dQ[jt][v]);
+              st(static_cast<TIn*>(a.dk), qk_index(t, j), dK[jt][v]);
+            }
           }
         }
       }

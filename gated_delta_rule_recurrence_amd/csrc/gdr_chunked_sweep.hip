@@ -1556,7 +1556,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     const bool iok = i0 + ti < Dv;
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
-    float* const sink = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink + l;
+    float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
     const int64_t vbase = v_base(c);
     deposit_rows<KRS>(kq, kr, qr);
     // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
@@ -1646,15 +1646,24 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     {
       const f4 Cv = mfma_pieces6(
           tp, [&](int ks, int p) { return step_piece(up, ks, p); }, zk, f4{0.f, 0.f, 0.f, 0.f});
-      f4 pc;
+      f4 pc, dvv;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int t = tw + 4 * lq + u;
         pc[u] = -(bet[u] * pre[u]) * Cv[u];
-        const bool ok = iok && t < n;
-        __builtin_nontemporal_store(Cv[u], ok ? a.C + vbase + t * vst + ti : sink);
-        *(ok ? dv + vbase + t * vst + ti : reinterpret_cast<bf16*>(sink)) =
-            from_f32<bf16>(bet[u] * Cv[u]);
+        dvv[u] = bet[u] * Cv[u];
+      }
+      // after a transpose across each lane quad, lane 4a + b holds step
+      // tw + 4 lq + b, rows 16 nt + 4a .. +3: one 16-byte C store (read once,
+      // by the chunk-parallel pass: non-temporal) and one 8-byte dv store
+      {
+        const f4 cr = quad_transpose(Cv, lr), dr4 = quad_transpose(dvv, lr);
+        const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
+        const bool ok = t < n && i0 + r4 < Dv;
+        const int64_t o = vbase + (int64_t)t * vst + r4;
+        __builtin_nontemporal_store(cr, reinterpret_cast<f4*>(ok ? a.C + o : sink16));
+        const uint2 dvb = {cvt_pk_bf16(dr4[0], dr4[1]), cvt_pk_bf16(dr4[2], dr4[3])};
+        *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(dv + o)
+                                     : reinterpret_cast<uint2*>(sink16)) = dvb;
       }
       put_steps(cpp, pc);
     }
@@ -1684,7 +1693,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
     }
     __syncthreads();  // stage reads done before it is rewritten
-    put_grad(c - 1, lr, lq, A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink);
+    put_grad(c - 1, lr, lq, sink16);
   }
   if (a.dS0 != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
