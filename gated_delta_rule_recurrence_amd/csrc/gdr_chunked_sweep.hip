@@ -975,16 +975,10 @@ struct SLB {
   static constexpr int EP = SP + 3 * DKP * kDS / 2;  // diag(ks) E pieces
   static constexpr int UP = EP + 3 * PS / 2;          // U pieces
   static constexpr int EQ = UP + 3 * PS / 2;          // E pieces
-  // output stages, copied out in 16-byte (y: 8-byte) row blocks after a
-  // later barrier: E fp32 [kN][OES], y bf16 [kN][OYS]
-  static constexpr int OES = kDS + 4, OYS = kDS + 8;
-  static constexpr int OE = EQ + 3 * PS / 2;
-  static constexpr int OY = OE + kN * OES;
-  static constexpr int SIZE = OY + kN * OYS / 2;
+  static constexpr int SIZE = EQ + 3 * PS / 2;
   static_assert((2 * KRS) % 256 == 128 && (2 * KTS) % 32 == 16, "row strides");
   static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
-  static_assert(QR % 4 == 0 && SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0 &&
-                    OE % 4 == 0 && OY % 4 == 0 && OES % 4 == 0,
+  static_assert(QR % 4 == 0 && SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0,
                 "16-byte aligned regions");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
@@ -1076,24 +1070,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     asm volatile("" : "+v"(tl));
     put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
   }
-  // 16-byte (y: 8-byte) row blocks of the E, y stages of a chunk to the
-  // tensors (lanes outside them store to the sink)
-  auto out_rows = [&](int64_t vbase, int n, float* sink) __attribute__((always_inline)) {
-    int tl = tid;
-    asm volatile("" : "+v"(tl));
-    const int t = tl >> 3, c4 = 4 * (tl & 7);  // step t, rows i0 + c4 .. +3
-    const bool ok = t < n && i0 + c4 < Dv;
-    const int64_t o = vbase + (int64_t)t * vst + c4;
-    if (SAVE) {
-      const f4 e = *reinterpret_cast<const f4*>(sm + L::OE + t * L::OES + c4);
-      __builtin_nontemporal_store(e, reinterpret_cast<f4*>(ok ? a.E + o : sink));
-    }
-    const uint2 yv = *reinterpret_cast<const uint2*>(
-        reinterpret_cast<const uint16_t*>(sm + L::OY) + t * L::OYS + c4);
-    *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(y + o) : reinterpret_cast<uint2*>(sink)) =
-        yv;
-  };
-
   for (int c = 0; c < a.nch; ++c) {
     int tl = tid;
     asm volatile("" : "+v"(tl));
@@ -1188,10 +1164,16 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
           tp, [&](int ks, int p) { return step_piece(up, ks, p); }, zk, f4{0.f, 0.f, 0.f, 0.f});
       f4 ke;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = tw + 4 * lq + u;
-        ke[u] = ksc[u] * E[u];
-        if (SAVE) sm[L::OE + t * L::OES + ti] = E[u];
+      for (int u = 0; u < 4; ++u) ke[u] = ksc[u] * E[u];
+      if (SAVE) {
+        // after a transpose across each lane quad, lane 4a + b holds step
+        // tw + 4 lq + b, rows 16 nt + 4a .. +3: one 16-byte store (read once,
+        // by the reverse pass: non-temporal)
+        const f4 er = quad_transpose(E, lr);
+        const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
+        const bool ok = t < n && i0 + r4 < Dv;
+        __builtin_nontemporal_store(
+            er, reinterpret_cast<f4*>(ok ? a.E + vbase + (int64_t)t * vst + r4 : sink16));
       }
       put_steps(eq, E);
       put_steps(ep, ke);
@@ -1204,10 +1186,14 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
       for (int u = 0; u < 4; ++u) Yv[u] = gam[u] * XQ[u];
       Yv = mfma_pieces6(mp, [&](int ks, int p) { return step_piece(eq, ks, p); }, zk, Yv);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = tw + 4 * lq + u;
-        reinterpret_cast<bf16*>(sm + L::OY)[t * L::OYS + ti] = from_f32<bf16>(Yv[u]);
+      {
+        // as E: one 8-byte store of four bf16 rows per lane
+        const f4 yr = quad_transpose(Yv, lr);
+        const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
+        const bool ok = t < n && i0 + r4 < Dv;
+        const uint2 yb = {cvt_pk_bf16(yr[0], yr[1]), cvt_pk_bf16(yr[2], yr[3])};
+        *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(y + vbase + (int64_t)t * vst + r4)
+                                     : reinterpret_cast<uint2*>(sink16)) = yb;
       }
     }
 
@@ -1230,7 +1216,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       }
     }
     __syncthreads();  // stage reads done before it is rewritten
-    out_rows(vbase, n, sink16);  // E, y of this chunk, staged before the barrier
     put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink16);
   }
   if (a.ST != nullptr) {
