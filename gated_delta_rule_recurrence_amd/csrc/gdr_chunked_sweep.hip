@@ -1076,7 +1076,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     kq.tid = tl;
     const int l = tl & 63, lr = l & 15, lq = l >> 4;
     const int ti = 16 * nt + lr;
-    const bool iok = i0 + ti < Dv;
     const int t0 = c * a.L;
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
@@ -1095,12 +1094,15 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       for (int u = 0; u < 4; ++u) gam[u] = g4[u], ksc[u] = k4[u];
     }
     const float gend = rec[kBrGend];
+    {
+      const bool iok = i0 + ti < Dv;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = tw + 4 * lq + u;
-      const bool ok = iok && t < n;
-      vr[u] = v[vbase + (ok ? t * vst + ti : 0)];
-      vm |= (uint32_t)ok << u;
+      for (int u = 0; u < 4; ++u) {
+        const int t = tw + 4 * lq + u;
+        const bool ok = iok && t < n;
+        vr[u] = v[vbase + (ok ? t * vst + ti : 0)];
+        vm |= (uint32_t)ok << u;
+      }
     }
     {
       const int cn = min(c + 1, a.nch - 1);
@@ -1468,21 +1470,18 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
 
   KQPrefetch<bf16, JT, true> kq;
   kq.init(tid);
-  // dy of this wave's tile (step tw + 4 lq + u, row i0 + ti), a chunk ahead
-  bf16 dr[4];
-  uint32_t dm = 0;
-  auto fetch_dy = [&](int c, int lq, int ti, bool iok) __attribute__((always_inline)) {
-    const int n = chunk_len(c);
-    const int64_t base = v_base(c);
-    uint32_t m = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = tw + 4 * lq + u;
-      const bool ok = iok && t < n;
-      dr[u] = dy[base + (ok ? t * vst + ti : 0)];
-      m |= (uint32_t)ok << u;
-    }
-    dm = m;
+  // dy of this wave's tile, a chunk ahead: four bf16 of step
+  // tw + 4 lq + (l % 4), rows 16 nt + 4 (lr / 4) .. (one 8-byte load; a quad
+  // transpose gives the lane its row ti at steps tw + 4 lq + u)
+  uint2 dq2;
+  bool dok = false;
+  auto fetch_dy = [&](int c, int lq, int lr) __attribute__((always_inline)) {
+    const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
+    const bool ok = t < chunk_len(c) && i0 + r4 < Dv;
+    int64_t o = ok ? v_base(c) + (int64_t)t * vst + r4 : 0;
+    asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
+    dq2 = *reinterpret_cast<const uint2*>(dy + o);
+    dok = ok;
   };
 
   f4 Hacc[JW];
@@ -1498,7 +1497,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         Hacc[nj][u] = ok ? a.dST[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
       }
     kq.fetch(k, q, kq_base(cl), chunk_len(cl), kst, Dk);
-    fetch_dy(cl, lq, 16 * nt + lr, i0 + 16 * nt + lr < Dv);
+    fetch_dy(cl, lq, lr);
   }
   // gradient tiles into the three j-major bf16 pieces and into checkpoint
   // slot `slot` (slot < 0: the sink; out-of-range lanes store to the sink too)
@@ -1538,7 +1537,6 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     kq.tid = tl;
     const int l = tl & 63, lr = l & 15, lq = l >> 4;
     const int ti = 16 * nt + lr;
-    const bool iok = i0 + ti < Dv;
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
     float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
@@ -1560,12 +1558,16 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     };
     float dyv[4];
     {
+      f4 d4 = {__uint_as_float(dq2.x << 16), __uint_as_float(dq2.x & 0xffff0000u),
+               __uint_as_float(dq2.y << 16), __uint_as_float(dq2.y & 0xffff0000u)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) d4[u] = dok ? d4[u] : 0.f;
+      d4 = quad_transpose(d4, lr);  // steps tw + 4 lq + u of row ti (exact moves)
       uint32_t db[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const bool ok = (dm >> u) & 1;
-        dyv[u] = ok ? to_f32(dr[u]) : 0.f;
-        db[u] = ok ? dr[u].bits : 0u;
+        dyv[u] = d4[u];
+        db[u] = __float_as_uint(d4[u]) >> 16;
       }
       *reinterpret_cast<uint2*>(dyt + so) = uint2{db[0] | (db[1] << 16), db[2] | (db[3] << 16)};
     }
@@ -1583,7 +1585,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     {
       const int cn = max(c - 1, 0);
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
-      fetch_dy(cn, lq, ti, iok);
+      fetch_dy(cn, lq, lr);
     }
     __syncthreads();
 
