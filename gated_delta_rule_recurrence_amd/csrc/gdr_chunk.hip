@@ -45,7 +45,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kN = 64;       // max chunk length
-constexpr int kNP = kN + 1;  // padded row stride of [kN][kN] LDS matrices
+constexpr int kNP = kN + 4;  // padded row stride of [kN][kN] LDS matrices
 constexpr int kKB = 32;      // Dv rows per staged block of the Dv pass
 constexpr int kSB = 16;      // chunk steps per staged block of the final products
 
@@ -74,10 +74,10 @@ struct CL {  // LDS layout, offsets in floats
                        BS_E = BS_C + 3 * kN * YS / 2;
   static constexpr int BSTAGE = BS_E + 3 * kN * YS / 2;
   static_assert((2 * YS) % 32 == 16, "dy, C, E row stride");
-  // per-head O(n^2) arrays, after the Dv pass (alias the stage)
-  static constexpr int PHI = 0, PSI = PHI + kN * kNP, GM = PSI + kN * kNP,
-                       MZ = GM + kN * kNP;
-  static constexpr int HEAD = MZ + kN * kNP;
+  // per-head M and the Phi', Psi' accumulators of every lane ([8][kThreads]
+  // f4, in lane order), after the Dv pass (alias the stage)
+  static constexpr int MZ = 0, GRD = (MZ + kN * kNP + 3) & ~3;
+  static constexpr int HEAD = GRD + 8 * kThreads * 4;
   // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns); with
   // bf16 products, q, k rows as bf16 [kN][KGS] (the row stride an odd
   // number of 16-byte units: the operand reads of 16 rows hit distinct banks)
@@ -104,12 +104,14 @@ struct CL {  // LDS layout, offsets in floats
                        V_PREX = VEC + 3 * kN, V_SUF = VEC + 4 * kN,
                        V_CHI = VEC + 5 * kN, V_PSI = VEC + 6 * kN,
                        V_A = VEC + 7 * kN, V_SCR = VEC + 8 * kN;  // kThreads
-  // persistent per workgroup: QK, KK and the head sums W1, -W2, Wq [kN][kNP]
+  // persistent per workgroup: QK, KK, the head sums W1 (lower triangle
+  // with the diagonal; Wq = W1^T) and -W2 (strict lower triangle; W2 is
+  // symmetric), and the decay products GM of the current value head
+  // [kN][kNP]
   static_assert(V_SCR % 4 == 0, "16-byte reads of the partials");
   static constexpr int QK = V_SCR + kThreads, KK = QK + kN * kNP,
-                       W1 = KK + kN * kNP, W2 = W1 + kN * kNP,
-                       WQ = W2 + kN * kNP;
-  static constexpr int SIZE = WQ + kN * kNP;
+                       W1 = KK + kN * kNP, W2 = W1 + kN * kNP, GM = W2 + kN * kNP;
+  static constexpr int SIZE = GM + kN * kNP;
   static constexpr bool BF_FINAL = BFINAL <= A_SZ && DKP % 64 == 0;
   static_assert(3 * kN * WS / 2 <= 2 * kN * kNP && (2 * WS) % 32 == 16, "W pieces");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS budget of one workgroup");
@@ -254,7 +256,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       const int o = (e >> 6) * kNP + (e & 63);
       sm[L::W1 + o] = 0.f;
       sm[L::W2 + o] = 0.f;
-      sm[L::WQ + o] = 0.f;
     }
   } else {
     f4 acc[8];  // QK tiles (w, 0..3), KK tiles (w, 0..3)
@@ -306,7 +307,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       const int o = (e >> 6) * kNP + (e & 63);
       sm[L::W1 + o] = 0.f;
       sm[L::W2 + o] = 0.f;
-      sm[L::WQ + o] = 0.f;
     }
   }
 
@@ -515,6 +515,16 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       const float sf = wave_prefix_product(gs);
       if (l < n) sm[L::V_SUF + n - 1 - l] = sf;
     }
+    // Gam(r, t] for r, t in the chunk: row r is read after the Dv passes
+    {  // rows r = 16 w .. 16 w + 15 of Gam(r, t] (lane l <-> t = l)
+      const float gl = l < n ? sm[L::V_G + l] : 1.f;
+#pragma unroll 4
+      for (int i = 0; i < 16; ++i) {
+        const int r = tw + i;
+        const float y = wave_prefix_product(l > r ? gl : 1.f);
+        sm[L::GM + r * kNP + l] = l == r ? 1.f : ((l > r && l < n) ? y : 0.f);
+      }
+    }
 
     // ---- passes over Dv: P1, P2', P3' (JPW column tiles per pass) and, in
     // the first pass, Phi', Psi' (MFMA) --------------------------------------
@@ -711,27 +721,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     __syncthreads();  // the stage is free: the O(n^2) arrays alias it
 
     // ---- per-head O(n^2) stage -------------------------------------------
-    float* sPhi = sm + L::PHI;  // Phi'[t][r]
-    float* sPsi = sm + L::PSI;  // Psi'[t][r]
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
-        sPhi[o] = GR[tb][v];
-        sPsi[o] = GR[4 + tb][v];
-      }
     sm[L::V_SCR + tid] = hs;
-    __syncthreads();
-    {  // rows r = 16 w .. 16 w + 15 of Gam(r, t] (lane l <-> t = l)
-      const float gl = l < n ? sm[L::V_G + l] : 1.f;
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const int r = tw + i;
-        const float y = wave_prefix_product(l > r ? gl : 1.f);
-        sm[L::GM + r * kNP + l] = l == r ? 1.f : ((l > r && l < n) ? y : 0.f);
-      }
-    }
+    f4* const grd = reinterpret_cast<f4*>(sm + L::GRD);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) grd[u * kThreads + tid] = GR[u];
     __syncthreads();
     if (w == 0) {  // phi0 = <H1, S0> from the 256 partials, in a fixed order
       const f4 x4 = *reinterpret_cast<const f4*>(sm + L::V_SCR + 4 * l);
@@ -742,47 +735,55 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
       if (l == 0) sm[L::V_SCR + 1] = (r0 + r1) + (r2 + r3);
     }
-    if (tid < n)  // g and beta do not enter an identity step
-      st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + tid) * Hv + h,
-         skipped(a.mask, b, T, t0 + tid) ? 0.f : sPsi[tid * kNP + tid]);
 
-    // running weight matrices and M.  The arrays are disjoint LDS regions:
-    // restrict-qualified pointers let the loads of later entries issue
-    // ahead of the stores of earlier ones.
+    // Running weight matrices, M and dbeta, from the Phi', Psi' accumulators
+    // as each lane left them: register v of tile tb holds entry (t, r),
+    // t = tw + 4 lq + v, r = 16 tb + lr.  The arrays are disjoint LDS regions:
+    // restrict-qualified pointers let the loads of later entries issue ahead
+    // of the stores of earlier ones.
     {
       const float* __restrict__ vB = sm + L::V_B;
-      const float* __restrict__ pPhi = sPhi;
-      const float* __restrict__ pPsi = sPsi;
       const float* __restrict__ pGM = sm + L::GM;
       const float* __restrict__ pQK = sm + L::QK;
       const float* __restrict__ pKK = sm + L::KK;
-      float* __restrict__ pWQ = sm + L::WQ;
       float* __restrict__ pW1 = sm + L::W1;
       float* __restrict__ pW2 = sm + L::W2;
       float* __restrict__ pMZ = sm + L::MZ;
-#pragma unroll 4
-      for (int x = 0; x < 16; ++x) {
-        const int e = tid + kThreads * x;
-        const int s = e >> 6, t = e & 63;  // entry (s, t)
-        const bool in = s < n && t < n;
-        const int o = s * kNP + t, ot = t * kNP + s;
-        const float bs = vB[s], bt = vB[t];
-        const float phi_st = pPhi[o], phi_ts = pPhi[ot];
-        const float psi_st = pPsi[o], psi_ts = pPsi[ot];
-        const float gam_st = pGM[o];   // Gam(s,t], s <= t
-        const float gam_ts = pGM[ot];  // Gam(t,s], t <= s
-        const float wq = pWQ[o], w1 = pW1[o], w2 = pW2[o];
-        const float qk = pQK[o], kk = pKK[o];
-        // Wq[s][t] = Gam(s,t] beta_s Phi'[t][s]            (s <= t)
-        if (in && s <= t) pWQ[o] = fmaf(gam_st * bs, phi_ts, wq);
-        // W1[s][t] = Gam(t,s] beta_t Phi'[s][t]            (s >= t)
-        if (in && s >= t) pW1[o] = fmaf(gam_ts * bt, phi_st, w1);
-        // -W2[s][t]: W2 = Gam(t,s] Psi[s][t] (s > t), Gam(s,t] Psi[t][s] (s < t)
-        if (in && s != t)
-          pW2[o] = fmaf(-(s > t ? gam_ts : gam_st) * (bs * bt), s > t ? psi_st : psi_ts, w2);
-        // M[s][r=t] = Phi[s][r] QK[s][r] - Psi[s][r] KK[s][r] (0 outside the
-        // chunk: M is multiplied over all 64 rows)
-        pMZ[o] = in ? (bt * phi_st) * qk - ((bs * bt) * psi_st) * kk : 0.f;
+      float bt[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) bt[v] = vB[tw + 4 * lq + v];
+#pragma unroll 1
+      for (int tb = 0; tb < 4; ++tb) {
+        const int r = 16 * tb + lr;
+        const float br = vB[r];
+        const f4 phi4 = grd[tb * kThreads + tid], psi4 = grd[(4 + tb) * kThreads + tid];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int t = tw + 4 * lq + v;
+          const bool in = t < n && r < n;
+          const int o = t * kNP + r;
+          const float phi = phi4[v], psi = psi4[v];
+          const float gam = pGM[r * kNP + t];  // Gam(r,t] (r <= t)
+          const float qk = pQK[o], kk = pKK[o], w1 = pW1[o], w2 = pW2[o];
+          // W1[t][r] = Gam(r,t] beta_r Phi'[t][r]            (t >= r)
+          // (Wq[s][t] = Gam(s,t] beta_s Phi'[t][s], s <= t, is W1[t][s])
+          if (in && t >= r) pW1[o] = fmaf(gam * br, phi, w1);
+          // -W2[t][r] = -Gam(r,t] beta_t beta_r Psi'[t][r]    (t > r)
+          if (in && t > r) pW2[o] = fmaf(-gam * (bt[v] * br), psi, w2);
+          // M[t][r] = Phi[t][r] QK[t][r] - Psi[t][r] KK[t][r] (0 outside the
+          // chunk: M is multiplied over all 64 rows)
+          pMZ[o] = in ? (br * phi) * qk - ((bt[v] * br) * psi) * kk : 0.f;
+        }
+      }
+      // dbeta_t = Psi'[t][t]: tile tb = w, lanes lr = 4 lq + v
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        if (tb != w) continue;
+        const int v = lr & 3, t = tw + lr;
+        const float d = sm[L::GRD + ((4 + tb) * kThreads + tid) * 4 + v];
+        if ((lr >> 2) == lq && t < n)  // g and beta do not enter an identity step
+          st(static_cast<TIn*>(a.dbeta), (int64_t)(b * (int64_t)T + t0 + t) * Hv + h,
+             skipped(a.mask, b, T, t0 + t) ? 0.f : d);
       }
     }
 
@@ -834,6 +835,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   }
 
   // ---- dq += K Wq;  dk += Q W1 - K W2 (MFMA over the chunk steps) --------
+  // Wq = W1^T; W1 is held on and below the diagonal, -W2 below it (W2 is
+  // symmetric with a zero diagonal, which reads back as the zero the array
+  // was cleared to)
+  auto wq_at = [&](int s, int t) __attribute__((always_inline)) {
+    return sm[L::W1 + t * kNP + s];
+  };
+  auto w1_at = [&](int s, int t) __attribute__((always_inline)) {
+    return sm[L::W1 + s * kNP + t];
+  };
+  auto w2_at = [&](int s, int t) __attribute__((always_inline)) {
+    return sm[L::W2 + (s > t ? s * kNP + t : t * kNP + s)];
+  };
   if constexpr (BFP && L::BF_FINAL) {
     // k, q (bf16) as swizzled tiles, read as A operands (A[j][s] = k_s[j])
     // through lds_read_tr16; each W as three bf16 pieces W^T [t][s]
@@ -877,15 +890,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         }
       }
     }
-    // acc[jt] += A^T W over the chunk steps, W from the LDS matrix at wo
-    auto wpass = [&](int wo, const uint16_t* at, f4(&acc)[JT]) __attribute__((always_inline)) {
+    // acc[jt] += A^T W over the chunk steps, W[s][t] = wget(s, t)
+    auto wpass = [&](auto wget, const uint16_t* at, f4(&acc)[JT]) __attribute__((always_inline)) {
 #pragma unroll
       for (int x = 0; x < 4; ++x) {  // W[s..s+3][t] -> pieces of row t
         const int e = tid + kThreads * x;
         const int t = e & 63, s = 4 * (e >> 6);
         f4 wv;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) wv[y] = sm[wo + (s + y) * kNP + t];
+        for (int y = 0; y < 4; ++y) wv[y] = wget(s + y, t);
         uint2 p0, p1, p2;
         split3_quad(wv, p0, p1, p2);
         const int o = t * WS + s;
@@ -910,9 +923,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       }
       __syncthreads();  // the pieces are rewritten by the next pass
     };
-    wpass(L::WQ, fk, dQ);
-    wpass(L::W1, fq, dK);
-    wpass(L::W2, fk, dK);  // W2 holds -W2
+    wpass(wq_at, fk, dQ);
+    wpass(w1_at, fq, dK);
+    wpass(w2_at, fk, dK);  // -W2
   } else
   for (int s0 = 0; s0 < n; s0 += kSB) {
     if (f_role) {
@@ -935,8 +948,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     __syncthreads();
 #pragma unroll 2
     for (int ks = 0; ks < kSB / 4; ++ks) {
-      const int wb = (s0 + 4 * ks + lq) * kNP + tw + lr;  // B: rows s, columns t
-      const float wq = sm[L::WQ + wb], w1 = sm[L::W1 + wb], w2 = sm[L::W2 + wb];
+      const int sb = s0 + 4 * ks + lq, tc = tw + lr;  // B: rows s, columns t
+      const float wq = wq_at(sb, tc), w1 = w1_at(sb, tc), w2 = w2_at(sb, tc);
 #pragma unroll
       for (int jt = 0; jt < JT; ++jt) {
         const int fa = ((ks * DKP + 16 * jt + lr) << 2) + lq;
