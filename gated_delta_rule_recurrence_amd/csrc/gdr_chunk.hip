@@ -65,13 +65,14 @@ struct CL {  // LDS layout, offsets in floats
                        ST_C = ST_Y + kKB * kN, ST_E = ST_C + kKB * kN;
   static constexpr int STAGE = ST_E + kKB * kN;
   // bf16-product stage (bf16 dy, PC = 64): S0, H1 as three bf16 pieces each
-  // [3][kKB][PC] (swizzled tiles, rows i, read through lds_read_tr16); dy
-  // [kN][YS] bf16 and C, E pieces [3][kN][YS] (rows t, columns i; the row
-  // stride of 80 bytes puts the 16-byte reads of 16 rows on distinct banks)
+  // [3][kKB][PC] (swizzled tiles, rows i, read through lds_read_tr16) and,
+  // in the first pass of a value head, the E pieces [3][kN][YS] (rows t,
+  // columns i; the row stride of 80 bytes puts the 16-byte accesses of 16
+  // rows on distinct banks).  dy and C, and E outside the Gram, go from
+  // global memory straight to the registers of the wave that owns the steps.
   static constexpr int YS = kKB + 8;
   static constexpr int BS_S = 0, BS_H = BS_S + 3 * kKB * PC / 2,
-                       BS_Y = BS_H + 3 * kKB * PC / 2, BS_C = BS_Y + kN * YS / 2,
-                       BS_E = BS_C + 3 * kN * YS / 2;
+                       BS_E = BS_H + 3 * kKB * PC / 2;
   static constexpr int BSTAGE = BS_E + 3 * kN * YS / 2;
   static_assert((2 * YS) % 32 == 16, "dy, C, E row stride");
   // per-head M and the Phi', Psi' accumulators of every lane ([8][kThreads]
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   struct SlotB {
     Quad<float, true> s[2], h[2], e[2], c[2];
     uint4 y;
-    uint32_t ms;  // validity: S0/H1 quads (bits 0, 1), e/c quads (2, 3), dy (4)
+    uint32_t ms;  // validity: S0/H1 quads (bits 0, 1), the e, c, dy row (2)
   };
   using RSlot = typename std::conditional<BFP, SlotB, Slot>::type;
   RSlot RA, RB;
@@ -374,23 +375,22 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         R.h[u].v = ld_nt(H1, o, ok);
         m |= (uint32_t)ok << u;
       }
+      // e, c, dy of step tw + lr (this wave's), Dv rows i0 + 8 lq .. +7
+      // (Dv is a multiple of 8: the eight are all inside or all outside)
+      const int i = i0 + 8 * lq;
+      const bool ok = tw + lr < n && i < Dv;
+      const int64_t o = rowbase + (tw + lr) * tstride + i;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int i = i0 + 4 * iq + 16 * u;
-        const bool ok = ts < n && i < Dv;
-        const int64_t o = rowbase + ts * tstride + i;
-        R.e[u].load(a.E, o, ok, 4);
-        R.c[u].load(a.C, o, ok, 4);
-        m |= (uint32_t)ok << (2 + u);
+        R.e[u].load(a.E, o + 4 * u, ok, 4);
+        R.c[u].load(a.C, o + 4 * u, ok, 4);
       }
       {
-        const int i = i0 + 8 * iq;
-        const bool ok = ts < n && i < Dv;
-        int64_t o = ok ? rowbase + ts * tstride + i : 0;
-        asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
-        R.y = *reinterpret_cast<const uint4*>(dy + o);
-        m |= (uint32_t)ok << 4;
+        int64_t oy = ok ? o : 0;
+        asm volatile("" : "+v"(oy));  // keeps the select (no branch around the load)
+        R.y = *reinterpret_cast<const uint4*>(dy + oy);
       }
+      m |= (uint32_t)ok << 2;
       R.ms = m;
     } else {
 #pragma unroll
@@ -416,12 +416,38 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     R.ms = m;
     }
   };
-  auto deposit = [&](const RSlot& R) __attribute__((always_inline)) {
+  // this wave's dy, C, E operands of one block (bf16 products): rows
+  // tw + lr, Dv rows 8 lq .. +7 of the block; C, E as three bf16 pieces
+  struct Ops {
+    uint4 fy, fc[3], fe[3];
+  };
+  auto pieces8 = [](const f4& x0, const f4& x1, uint4 (&f)[3]) __attribute__((always_inline)) {
+    uint2 a0, a1, a2, b0, b1, b2;
+    split3_quad(x0, a0, a1, a2);
+    split3_quad(x1, b0, b1, b2);
+    f[0] = uint4{a0.x, a0.y, b0.x, b0.y};
+    f[1] = uint4{a1.x, a1.y, b1.x, b1.y};
+    f[2] = uint4{a2.x, a2.y, b2.x, b2.y};
+  };
+  auto split_e = [&](const SlotB& R, Ops& op) __attribute__((always_inline)) {
+    const uint32_t mu = ((R.ms >> 2) & 1u) ? 15u : 0u;
+    pieces8(R.e[0].get(mu), R.e[1].get(mu), op.fe);
+  };
+  auto split_cy = [&](const SlotB& R, Ops& op) __attribute__((always_inline)) {
+    const bool ok = (R.ms >> 2) & 1u;
+    const uint32_t mu = ok ? 15u : 0u;
+    pieces8(R.c[0].get(mu), R.c[1].get(mu), op.fc);
+    op.fy.x = ok ? R.y.x : 0u;  // component selects (a vector select goes through memory)
+    op.fy.y = ok ? R.y.y : 0u;
+    op.fy.z = ok ? R.y.z : 0u;
+    op.fy.w = ok ? R.y.w : 0u;
+  };
+  // S0, H1 pieces of a block to LDS and, in the first pass of a value head
+  // (gram), this wave's E pieces (split into op.fe on the way)
+  auto deposit = [&](const RSlot& R, bool gram, Ops& op) __attribute__((always_inline)) {
     if constexpr (BFP) {
       uint16_t* const bs = reinterpret_cast<uint16_t*>(sm + L::BS_S);
       uint16_t* const bh = reinterpret_cast<uint16_t*>(sm + L::BS_H);
-      uint16_t* const by = reinterpret_cast<uint16_t*>(sm + L::BS_Y);
-      uint16_t* const bc = reinterpret_cast<uint16_t*>(sm + L::BS_C);
       uint16_t* const be = reinterpret_cast<uint16_t*>(sm + L::BS_E);
       constexpr int SP = kKB * PC, YP = kN * L::YS;  // piece strides (bf16)
       // three bf16 pieces of four fp32 values, stored as 8-byte blocks
@@ -444,21 +470,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         put3(bs, SP, o, sv);
         put3(bh, SP, o, hv);
       }
+      if (gram) {
+        split_e(R, op);
+        const int o = (tw + lr) * L::YS + 8 * lq;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const uint32_t mu = ((R.ms >> (2 + u)) & 1u) ? 15u : 0u;
-        const int o = ts * L::YS + 4 * iq + 16 * u;
-        put3(bc, YP, o, R.c[u].get(mu));
-        put3(be, YP, o, R.e[u].get(mu));
-      }
-      {
-        const bool ok = (R.ms >> 4) & 1u;
-        uint4 yv = R.y;
-        yv.x = ok ? yv.x : 0u;  // component selects (a vector select goes through memory)
-        yv.y = ok ? yv.y : 0u;
-        yv.z = ok ? yv.z : 0u;
-        yv.w = ok ? yv.w : 0u;
-        *reinterpret_cast<uint4*>(by + ts * L::YS + 8 * iq) = yv;
+        for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(be + p * YP + o) = op.fe[p];
       }
     } else {
 #pragma unroll
@@ -542,22 +558,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       // One staged block: kKB / 4 MFMA k-steps.  The operands of k-step
       // ks + 1 are read from LDS while the MFMAs of k-step ks issue.
       // bf16 products: the block is one k-step of 32 Dv rows
-      auto multiply_bf = [&]() __attribute__((always_inline)) {
+      auto multiply_bf = [&](const Ops& op) __attribute__((always_inline)) {
         const uint16_t* const bs = reinterpret_cast<const uint16_t*>(sm + L::BS_S);
         const uint16_t* const bh = reinterpret_cast<const uint16_t*>(sm + L::BS_H);
-        const uint16_t* const by = reinterpret_cast<const uint16_t*>(sm + L::BS_Y);
-        const uint16_t* const bc = reinterpret_cast<const uint16_t*>(sm + L::BS_C);
         const uint16_t* const be = reinterpret_cast<const uint16_t*>(sm + L::BS_E);
         constexpr int SP = kKB * PC, YP = kN * L::YS;
         // this wave's steps: dy, C, E rows tw + l % 16, Dv rows 8 (l / 16) ..
-        const int ro = (tw + lr) * L::YS + 8 * lq;
-        const uint4 fy = *reinterpret_cast<const uint4*>(by + ro);
-        uint4 fc[3], fe[3];
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          fc[p] = *reinterpret_cast<const uint4*>(bc + p * YP + ro);
-          fe[p] = *reinterpret_cast<const uint4*>(be + p * YP + ro);
-        }
+        const uint4 fy = op.fy;
+        const uint4(&fc)[3] = op.fc;
+        const uint4(&fe)[3] = op.fe;
 #pragma unroll
         for (int jt = 0; jt < JPW; ++jt) {
           uint4 fs[3], fh[3];
@@ -600,9 +609,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           }
         }
       };
-      auto multiply = [&]() __attribute__((always_inline)) {
+      auto multiply = [&](const Ops& op) __attribute__((always_inline)) {
         if constexpr (BFP) {
-          multiply_bf();
+          multiply_bf(op);
         } else {
         constexpr int KS = kKB / 4;
         const bool gram = jp == 0;  // Phi', Psi' ride along in the first pass
@@ -668,21 +677,32 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       const int gbase = (hh * NJP + jp) * nbk;
       // nbk >= 2: a do-while keeps the loads in flight identical on every
       // path out of the loop (the waits for qq/kq then skip the ring's loads)
+      // With bf16 products the wave's own dy, C (and, after the first pass,
+      // E) operands are split after the barrier, next to the MFMAs.
       int blk = 0;
       do {
         const int gb = gbase + blk;
+        Ops op;
         __syncthreads();  // the stage is no longer read
-        deposit(RA);
+        deposit(RA, jp == 0, op);
         __syncthreads();
+        if constexpr (BFP) {
+          if (jp != 0) split_e(RA, op);
+          split_cy(RA, op);
+        }
         // unconditional (clamped) refills: every path has the same loads in
         // flight, so the wait before a deposit covers only that slot
         fetch(RA, min(gb + 2, nblk_all - 1));
-        multiply();
+        multiply(op);
         __syncthreads();
-        deposit(RB);
+        deposit(RB, jp == 0, op);
         __syncthreads();
+        if constexpr (BFP) {
+          if (jp != 0) split_e(RB, op);
+          split_cy(RB, op);
+        }
         fetch(RB, min(gb + 3, nblk_all - 1));
-        multiply();
+        multiply(op);
         blk += 2;
       } while (blk < nbk);
 
