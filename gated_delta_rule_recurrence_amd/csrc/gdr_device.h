@@ -130,15 +130,32 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
 // bottom of the exponent range), and products of the pieces with a bf16
 // value are exact: three bf16 MFMAs give an fp32-accurate product.  Four
 // values at once, as three 8-byte blocks of packed bf16.
+// The residuals x - piece come from v_dot2_f32_bf16 against (-1, 0) or
+// (0, -1): one instruction instead of unpacking the piece and subtracting.
+// The residual is representable, so it is exact however the dot product
+// rounds (the pieces match the subtracting form bit for bit wherever the
+// leading piece does not overflow bf16).  The (-1, 0) pair is kept in a
+// register: folded, it becomes the inline constant -1.0, which the
+// instruction reads as the fp32 pattern, i.e. the pair (0, -1).
+__device__ __forceinline__ float minus_bf16_lo(uint32_t pk, float x) {  // x - low half
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  uint32_t m = 0x0000bf80u;
+  asm("" : "+v"(m));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pk),
+                                         __builtin_bit_cast(bf16x2v, m), x, false);
+}
+__device__ __forceinline__ float minus_bf16_hi(uint32_t pk, float x) {  // x - high half
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, pk),
+                                         __builtin_bit_cast(bf16x2v, 0xbf800000u), x, false);
+}
 __device__ __forceinline__ void split3_quad(f4 v, uint2& hi, uint2& mid, uint2& lo) {
   hi = uint2{cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3])};
-  const f4 r = {v[0] - __uint_as_float(hi.x << 16), v[1] - __uint_as_float(hi.x & 0xffff0000u),
-                v[2] - __uint_as_float(hi.y << 16), v[3] - __uint_as_float(hi.y & 0xffff0000u)};
+  const f4 r = {minus_bf16_lo(hi.x, v[0]), minus_bf16_hi(hi.x, v[1]),
+                minus_bf16_lo(hi.y, v[2]), minus_bf16_hi(hi.y, v[3])};
   mid = uint2{cvt_pk_bf16(r[0], r[1]), cvt_pk_bf16(r[2], r[3])};
-  lo = uint2{cvt_pk_bf16(r[0] - __uint_as_float(mid.x << 16),
-                         r[1] - __uint_as_float(mid.x & 0xffff0000u)),
-             cvt_pk_bf16(r[2] - __uint_as_float(mid.y << 16),
-                         r[3] - __uint_as_float(mid.y & 0xffff0000u))};
+  lo = uint2{cvt_pk_bf16(minus_bf16_lo(mid.x, r[0]), minus_bf16_hi(mid.x, r[1])),
+             cvt_pk_bf16(minus_bf16_lo(mid.y, r[2]), minus_bf16_hi(mid.y, r[3]))};
 }
 
 // ds_read_b64_tr_b16: each lane names an 8-byte block of four bf16; inside
