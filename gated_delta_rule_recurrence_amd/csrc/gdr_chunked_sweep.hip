@@ -1024,6 +1024,34 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   // k quads of a chunk (for the row-major k tile), a chunk ahead
   KQPrefetch<bf16, JT, true> kq;
   kq.init(tid);
+  // this wave's T pieces, the step factors and v of a chunk, a chunk ahead
+  struct ChunkIn {
+    uint4 tp[2][3];
+    f4 g4, k4;
+    float gend;
+    bf16 vr[4];
+    uint32_t vm;
+  };
+  auto fetch_in = [&](int c, int l, ChunkIn& x) __attribute__((always_inline)) {
+    const int lr = l & 15, lq = l >> 4, ti = 16 * nt + lr;
+    const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
+    pieces_from_record(rec + kBrT, tb, l, zk, x.tp);
+    x.g4 = *reinterpret_cast<const f4*>(rec + kBrGam + tw + 4 * lq);
+    x.k4 = *reinterpret_cast<const f4*>(rec + kBrKs + tw + 4 * lq);
+    x.gend = rec[kBrGend];
+    const int64_t vb = ((int64_t)b * T + c * a.L) * vst + (int64_t)h * Dv + i0;
+    const int n = chunk_len(c);
+    const bool iok = i0 + ti < Dv;
+    x.vm = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tw + 4 * lq + u;
+      const bool ok = iok && t < n;
+      x.vr[u] = v[vb + (ok ? t * vst + ti : 0)];
+      x.vm |= (uint32_t)ok << u;
+    }
+  };
+  ChunkIn nx;
   f4 Sacc[JW];
   {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1036,6 +1064,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         Sacc[nj][u] = ok ? a.S0[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
       }
     kq.fetch(k, q, kq_base(0), chunk_len(0), kst, Dk);
+    fetch_in(0, l, nx);
   }
   // the state tiles into the three j-major bf16 pieces (and checkpoint
   // `slot`, or the sink when slot < 0; out-of-range lanes store to the sink
@@ -1082,31 +1111,17 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
     const int64_t vbase = ((int64_t)b * T + t0) * vst + (int64_t)h * Dv + i0;
     deposit_rows<KRS>(kq, kr, qr);
-    uint4 tp[2][3], mp[2][3];  // T, M pieces of this wave's step tile
+    uint4 mp[2][3];  // M pieces of this wave's step tile
+    const ChunkIn cur = nx;
+    const uint4(&tp)[2][3] = cur.tp;  // T pieces
     float gam[4], ksc[4];
-    bf16 vr[4];
-    uint32_t vm = 0;
-    pieces_from_record(rec + kBrT, tb, l, zk, tp);
-    {
-      const f4 g4 = *reinterpret_cast<const f4*>(rec + kBrGam + tw + 4 * lq);
-      const f4 k4 = *reinterpret_cast<const f4*>(rec + kBrKs + tw + 4 * lq);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) gam[u] = g4[u], ksc[u] = k4[u];
-    }
-    const float gend = rec[kBrGend];
-    {
-      const bool iok = i0 + ti < Dv;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int t = tw + 4 * lq + u;
-        const bool ok = iok && t < n;
-        vr[u] = v[vbase + (ok ? t * vst + ti : 0)];
-        vm |= (uint32_t)ok << u;
-      }
-    }
+    for (int u = 0; u < 4; ++u) gam[u] = cur.g4[u], ksc[u] = cur.k4[u];
+    const float gend = cur.gend;
     {
       const int cn = min(c + 1, a.nch - 1);
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
+      fetch_in(cn, l, nx);
     }
     __syncthreads();
 
@@ -1153,7 +1168,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       f4 uv;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const float vu = ((vm >> u) & 1) ? to_f32(vr[u]) : 0.f;
+        const float vu = ((cur.vm >> u) & 1) ? to_f32(cur.vr[u]) : 0.f;
         uv[u] = vu - gam[u] * XK[u];
       }
       put_steps(up, uv);
@@ -1484,6 +1499,23 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     dok = ok;
   };
 
+  // this wave's Mq pieces and the step factors of a chunk, a chunk ahead
+  struct ChunkIn {
+    uint4 mp[2][3];
+    f4 s4, p4, b4;
+    float pend;
+  };
+  auto fetch_in = [&](int c, int l, ChunkIn& x) __attribute__((always_inline)) {
+    const int lq = l >> 4;
+    const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
+    pieces_from_record(rec + kBbM, tb, l, zk, x.mp);
+    x.s4 = *reinterpret_cast<const f4*>(rec + kBbSuf + tw + 4 * lq);
+    x.p4 = *reinterpret_cast<const f4*>(rec + kBbPre + tw + 4 * lq);
+    x.b4 = *reinterpret_cast<const f4*>(rec + kBbBeta + tw + 4 * lq);
+    x.pend = rec[kBbPre + chunk_len(c) - 1];
+  };
+  ChunkIn nx;
+
   f4 Hacc[JW];
   const int cl = a.nch - 1;
   {
@@ -1498,6 +1530,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
     kq.fetch(k, q, kq_base(cl), chunk_len(cl), kst, Dk);
     fetch_dy(cl, lq, lr);
+    fetch_in(cl, l, nx);
   }
   // gradient tiles into the three j-major bf16 pieces and into checkpoint
   // slot `slot` (slot < 0: the sink; out-of-range lanes store to the sink too)
@@ -1571,21 +1604,18 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
       *reinterpret_cast<uint2*>(dyt + so) = uint2{db[0] | (db[1] << 16), db[2] | (db[3] << 16)};
     }
-    uint4 tp[2][3], mp[2][3];  // Tb, Mq pieces of this wave's step tile
+    uint4 tp[2][3];  // Tb pieces of this wave's step tile
+    const ChunkIn cur = nx;
+    const uint4(&mp)[2][3] = cur.mp;  // Mq pieces
     float suf[4], pre[4], bet[4];
-    pieces_from_record(rec + kBbM, tb, l, zk, mp);
-    {
-      const f4 s4 = *reinterpret_cast<const f4*>(rec + kBbSuf + tw + 4 * lq);
-      const f4 p4 = *reinterpret_cast<const f4*>(rec + kBbPre + tw + 4 * lq);
-      const f4 b4 = *reinterpret_cast<const f4*>(rec + kBbBeta + tw + 4 * lq);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) suf[u] = s4[u], pre[u] = p4[u], bet[u] = b4[u];
-    }
-    const float pend = rec[kBbPre + n - 1];
+    for (int u = 0; u < 4; ++u) suf[u] = cur.s4[u], pre[u] = cur.p4[u], bet[u] = cur.b4[u];
+    const float pend = cur.pend;
     {
       const int cn = max(c - 1, 0);
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
       fetch_dy(cn, lq, lr);
+      fetch_in(cn, l, nx);
     }
     __syncthreads();
 
