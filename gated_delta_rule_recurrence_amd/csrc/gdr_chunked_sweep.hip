@@ -947,6 +947,66 @@ __device__ __forceinline__ void deposit_rows(const KQ& kq, uint16_t* kr, uint16_
   }
 }
 
+// bf16 k, q rows of a chunk in 8-element groups (Dk a multiple of 8), a
+// chunk ahead: one 16-byte load per group, and 16-byte LDS stores into the
+// row-major tiles
+template <int JT, int NTH = kSwThreads>
+struct KQPrefetch8 {
+  static constexpr int DKP = 16 * JT;
+  static constexpr int NGT = kN * DKP / 8;  // 8-column groups of one chunk
+  static constexpr int NG = NGT / NTH;
+  static_assert(NGT % NTH == 0 && NG <= 32, "groups per thread");
+  uint32_t pm = 0;
+  uint4 pk[NG], pq[NG];
+  int tid;
+  // group u of this thread: step qt(u), columns qj(u) .. qj(u) + 7
+  __device__ __forceinline__ int qt(int u) const { return (tid + NTH * u) / (DKP / 8); }
+  __device__ __forceinline__ int qj(int u) const { return 8 * ((tid + NTH * u) % (DKP / 8)); }
+  __device__ __forceinline__ void init(int t) { tid = t; }
+  // rows t0 .. t0 + n - 1; base = element (t0, kv head, 0); kst = row stride
+  __device__ __forceinline__ void fetch(const bf16* __restrict__ k, const bf16* __restrict__ q,
+                                        int64_t base, int n, int kst, int Dk) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const int t = qt(u), j = qj(u);
+      const bool ok = j < Dk && t < n;
+      int64_t o = ok ? base + (int64_t)t * kst + j : 0;
+      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+      pk[u] = *reinterpret_cast<const uint4*>(k + o);
+      pq[u] = *reinterpret_cast<const uint4*>(q + o);
+      m |= (uint32_t)ok << u;
+    }
+    pm = m;
+  }
+};
+
+template <int KRS, int JT>
+__device__ __forceinline__ void deposit_rows(const KQPrefetch8<JT>& kq, uint16_t* kr,
+                                             uint16_t* qr) {
+#pragma unroll
+  for (int u = 0; u < KQPrefetch8<JT>::NG; ++u) {
+    const bool ok = (kq.pm >> u) & 1u;
+    const int t = kq.qt(u), c = kq.qj(u) >> 3;
+    // 4-element blocks 2c, 2c + 1 stay adjacent under the swizzle
+    const int o = t * KRS + 4 * ((2 * c) ^ tile_swz(t));
+    uint4 rk = kq.pk[u];
+    rk.x = ok ? rk.x : 0u;  // component selects (a vector select goes through memory)
+    rk.y = ok ? rk.y : 0u;
+    rk.z = ok ? rk.z : 0u;
+    rk.w = ok ? rk.w : 0u;
+    *reinterpret_cast<uint4*>(kr + o) = rk;
+    if (qr != nullptr) {
+      uint4 rq = kq.pq[u];
+      rq.x = ok ? rq.x : 0u;
+      rq.y = ok ? rq.y : 0u;
+      rq.z = ok ? rq.z : 0u;
+      rq.w = ok ? rq.w : 0u;
+      *reinterpret_cast<uint4*>(qr + o) = rq;
+    }
+  }
+}
+
 // -------------------------------------------- forward sweep, bf16 inputs ----
 // The same sweep for bf16 k, q (Dk a multiple of 8), with the two products
 // that have k or q as an operand on bf16 MFMA (v_mfma_f32_16x16x32_bf16,
@@ -1021,35 +1081,33 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   auto kq_base = [&](int c) { return ((int64_t)b * T + c * a.L) * kst + (int64_t)hk * Dk; };
   auto chunk_len = [&](int c) { return min(a.L, T - c * a.L); };
 
-  // k quads of a chunk (for the row-major k tile), a chunk ahead
-  KQPrefetch<bf16, JT, true> kq;
+  // k, q rows of a chunk (for the row-major tiles), a chunk ahead
+  KQPrefetch8<JT> kq;
   kq.init(tid);
-  // this wave's T pieces, the step factors and v of a chunk, a chunk ahead
+  // this wave's T pieces, the step factors and v of a chunk, a chunk ahead;
+  // v as four bf16 of step tw + 4 lq + (l % 4), rows 16 nt + 4 (lr / 4) ..
+  // (one 8-byte load; a quad transpose gives the lane its row at steps
+  // tw + 4 lq + u)
   struct ChunkIn {
     uint4 tp[2][3];
     f4 g4, k4;
     float gend;
-    bf16 vr[4];
-    uint32_t vm;
+    uint2 v2;
+    bool vok;
   };
   auto fetch_in = [&](int c, int l, ChunkIn& x) __attribute__((always_inline)) {
-    const int lr = l & 15, lq = l >> 4, ti = 16 * nt + lr;
+    const int lr = l & 15, lq = l >> 4;
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
     pieces_from_record(rec + kBrT, tb, l, zk, x.tp);
     x.g4 = *reinterpret_cast<const f4*>(rec + kBrGam + tw + 4 * lq);
     x.k4 = *reinterpret_cast<const f4*>(rec + kBrKs + tw + 4 * lq);
     x.gend = rec[kBrGend];
-    const int64_t vb = ((int64_t)b * T + c * a.L) * vst + (int64_t)h * Dv + i0;
-    const int n = chunk_len(c);
-    const bool iok = i0 + ti < Dv;
-    x.vm = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int t = tw + 4 * lq + u;
-      const bool ok = iok && t < n;
-      x.vr[u] = v[vb + (ok ? t * vst + ti : 0)];
-      x.vm |= (uint32_t)ok << u;
-    }
+    const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
+    const bool ok = t < chunk_len(c) && i0 + r4 < Dv;
+    int64_t o = ok ? ((int64_t)b * T + c * a.L + t) * vst + (int64_t)h * Dv + i0 + r4 : 0;
+    asm volatile("" : "+v"(o));  // keeps the select (no branch around the load)
+    x.v2 = *reinterpret_cast<const uint2*>(v + o);
+    x.vok = ok;
   };
   ChunkIn nx;
   f4 Sacc[JW];
@@ -1165,12 +1223,14 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     };
     // U = V - diag(gam) X_K
     {
+      f4 v4 = {__uint_as_float(cur.v2.x << 16), __uint_as_float(cur.v2.x & 0xffff0000u),
+               __uint_as_float(cur.v2.y << 16), __uint_as_float(cur.v2.y & 0xffff0000u)};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v4[u] = cur.vok ? v4[u] : 0.f;
+      v4 = quad_transpose(v4, lr);  // steps tw + 4 lq + u of row ti (exact moves)
       f4 uv;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float vu = ((cur.vm >> u) & 1) ? to_f32(cur.vr[u]) : 0.f;
-        uv[u] = vu - gam[u] * XK[u];
-      }
+      for (int u = 0; u < 4; ++u) uv[u] = v4[u] - gam[u] * XK[u];
       put_steps(up, uv);
     }
     __syncthreads();
@@ -1483,7 +1543,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   auto v_base = [&](int c) { return ((int64_t)b * T + c * a.L) * vst + (int64_t)h * Dv + i0; };
   auto chunk_len = [&](int c) { return min(a.L, T - c * a.L); };
 
-  KQPrefetch<bf16, JT, true> kq;
+  KQPrefetch8<JT> kq;
   kq.init(tid);
   // dy of this wave's tile, a chunk ahead: four bf16 of step
   // tw + 4 lq + (l % 4), rows 16 nt + 4 (lr / 4) .. (one 8-byte load; a quad
