@@ -925,28 +925,6 @@ __device__ __forceinline__ uint4 piece_operand(const uint16_t* piece, int k0, in
   return uint4{lo.x, lo.y, hi.x, hi.y};
 }
 
-// The row-major k (and q) tile of a chunk from the quads fetched a chunk ago
-// (zero where the mask says so)
-template <int KRS, typename KQ>
-__device__ __forceinline__ void deposit_rows(const KQ& kq, uint16_t* kr, uint16_t* qr) {
-#pragma unroll
-  for (int u = 0; u < KQ::NQ; ++u) {
-    const uint32_t mu = (uint32_t)(kq.pm >> (4 * u)) & 15u;
-    const int t = kq.qt(u), cb = kq.qj(u) >> 2;
-    const int o = t * KRS + 4 * (cb ^ tile_swz(t));
-    uint2 rk = kq.pk[u].v;
-    rk.x = mu ? rk.x : 0u;  // component selects (a vector select goes through memory)
-    rk.y = mu ? rk.y : 0u;
-    *reinterpret_cast<uint2*>(kr + o) = rk;
-    if (qr != nullptr) {
-      uint2 rq = kq.pq[u].v;
-      rq.x = mu ? rq.x : 0u;
-      rq.y = mu ? rq.y : 0u;
-      *reinterpret_cast<uint2*>(qr + o) = rq;
-    }
-  }
-}
-
 // bf16 k, q rows of a chunk in 8-element groups (Dk a multiple of 8), a
 // chunk ahead: one 16-byte load per group, and 16-byte LDS stores into the
 // row-major tiles
@@ -981,6 +959,8 @@ struct KQPrefetch8 {
   }
 };
 
+// The row-major k (and q) tile of a chunk from the groups fetched a chunk
+// ago (zero where the mask says so)
 template <int KRS, int JT>
 __device__ __forceinline__ void deposit_rows(const KQPrefetch8<JT>& kq, uint16_t* kr,
                                              uint16_t* qr) {
