@@ -818,7 +818,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       f4 Bt[5];
 #pragma unroll
       for (int u = 0; u < 5; ++u) Bt[u] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         const int sk = 4 * ks + lq;
         const float ga = sm[L::GM + (tw + lr) * kNP + sk];  // A[t][s]
