@@ -1156,8 +1156,11 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
 #pragma unroll
     for (int u = 0; u < 4; ++u) gam[u] = cur.g4[u], ksc[u] = cur.k4[u];
     const float gend = cur.gend;
-    {
-      const int cn = min(c + 1, a.nch - 1);
+    // the next chunk's loads: waves 0-3 here, waves 4-7 (the other wave of
+    // each SIMD) after X, so that one wave's MFMAs run while the other
+    // issues
+    const int cn = min(c + 1, a.nch - 1);
+    if (w < 4) {
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
       fetch_in(cn, l, nx);
     }
@@ -1185,6 +1188,10 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       }
       XK = (xk[0] + xk[1]) + xk[2];
       XQ = (xq[0] + xq[1]) + xq[2];
+    }
+    if (w >= 4) {
+      kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
+      fetch_in(cn, l, nx);
     }
     pieces_from_record(rec + kBrM, tb, l, zk, mp);
     // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
@@ -1651,8 +1658,11 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
 #pragma unroll
     for (int u = 0; u < 4; ++u) suf[u] = cur.s4[u], pre[u] = cur.p4[u], bet[u] = cur.b4[u];
     const float pend = cur.pend;
-    {
-      const int cn = max(c - 1, 0);
+    // the next chunk's loads: waves 0-3 here, waves 4-7 (the other wave of
+    // each SIMD) after X, so that one wave's MFMAs run while the other
+    // issues
+    const int cn = max(c - 1, 0);
+    if (w < 4) {
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
       fetch_dy(cn, lq, lr);
       fetch_in(cn, l, nx);
@@ -1676,6 +1686,11 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
           x3[p] = mfma_bf16(ak, piece_operand(ht + p * DKP * kDS, 32 * ks, 16 * nt, lr, lq), x3[p]);
       }
       X = (x3[0] + x3[1]) + x3[2];
+    }
+    if (w >= 4) {
+      kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
+      fetch_dy(cn, lq, lr);
+      fetch_in(cn, l, nx);
     }
     pieces_from_record(rec + kBbT, tb, l, zk, tp);  // first used by C = Tb U
     // U = diag(suf) X + Mq DY; diag(pre) DY as three bf16 pieces [i][t]
