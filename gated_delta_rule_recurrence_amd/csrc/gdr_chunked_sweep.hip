@@ -1189,11 +1189,13 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       XK = (xk[0] + xk[1]) + xk[2];
       XQ = (xq[0] + xq[1]) + xq[2];
     }
+    // this chunk's M pieces before the next chunk's loads (loads complete in
+    // order: waiting for mp then waits for nothing issued after it)
+    pieces_from_record(rec + kBrM, tb, l, zk, mp);
     if (w >= 4) {
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
       fetch_in(cn, l, nx);
     }
-    pieces_from_record(rec + kBrM, tb, l, zk, mp);
     // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
     const int so = ti * KTS + tw + 4 * lq;
     auto put_steps = [&](uint16_t* dst, f4 v) __attribute__((always_inline)) {
@@ -1687,12 +1689,15 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
       X = (x3[0] + x3[1]) + x3[2];
     }
+    // this chunk's Tb pieces (first used by C = Tb U) before the next
+    // chunk's loads (loads complete in order: waiting for tp then waits for
+    // nothing issued after it)
+    pieces_from_record(rec + kBbT, tb, l, zk, tp);
     if (w >= 4) {
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
       fetch_dy(cn, lq, lr);
       fetch_in(cn, l, nx);
     }
-    pieces_from_record(rec + kBbT, tb, l, zk, tp);  // first used by C = Tb U
     // U = diag(suf) X + Mq DY; diag(pre) DY as three bf16 pieces [i][t]
     {
       f4 U;
