@@ -27,16 +27,17 @@
 // Hv/Hk value heads of the kv head in ascending order and accumulates dq, dk
 // in registers, so the GQA sum has a fixed order and needs no atomics.  Wave
 // w owns the chunk steps 16w .. 16w+15: the [Dk x 16] slices of P1, P2', P3',
-// dq, dk (all Dk tiles) and the rows 16w.. of Phi', Psi', QK, KK.  Every
-// contraction runs on fp32 MFMA (v_mfma_f32_16x16x4_f32) with the
-// accumulator layout "lane l, register v: row 16 i + 4 (l / 16) + v, column
-// 16 j + l % 16" of a 16 x 16 tile (i, j).  The Dv contractions P and the Gram
-// matrices share one pass over Dv: the dy/c fragments of a wave are at once
-// the B operands of P and the A operands of Phi', Psi'.  MFMA operands are
-// staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a fragment (lane
-// l <-> m = l % 16, k = l / 16) is 64 consecutive floats, 16 Dv rows per
-// block, with the next block fetched into registers while the current one is
-// multiplied.
+// dq, dk (all Dk tiles) and the rows 16w.. of Phi', Psi', QK, KK.  With
+// fp32 inputs every contraction runs on fp32 MFMA (v_mfma_f32_16x16x4_f32)
+// with the accumulator layout "lane l, register v: row 16 i + 4 (l / 16) + v,
+// column 16 j + l % 16" of a 16 x 16 tile (i, j).  The Dv contractions P and
+// the Gram matrices share one pass over Dv: the dy/c fragments of a wave are
+// at once the B operands of P and the A operands of Phi', Psi'.  MFMA
+// operands are staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a
+// fragment (lane l <-> m = l % 16, k = l / 16) is 64 consecutive floats, 16
+// Dv rows per block, with the next block fetched into registers while the
+// current one is multiplied.  With bf16 inputs (BFP below) the same passes
+// run on bf16 MFMA over exact three-piece splits of the fp32 operands.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -150,7 +151,10 @@ __device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
 // BFP (bf16 inputs, PC = 64, Dk and Dv multiples of 8): the Dv pass on bf16 MFMA,
 // the fp32 operands (S0, H1, C, E) split exactly into three bf16 pieces;
 // a product with bf16 dy takes the three pieces, a product of two fp32
-// operands the six piece products down to the order of fp32 rounding.
+// operands the six piece products down to the order of fp32 rounding.  S0,
+// H1 (and, for the Gram, E) are staged in LDS as pieces; each wave's own dy,
+// C, E rows go from global memory to its registers and are split there.
+// QK, KK, the final products and (fp32) dg keep the layouts above.
 template <typename TIn, int JT, bool VEC, bool BFP>
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   using L = CL<JT>;
