@@ -77,9 +77,14 @@ struct CL {  // LDS layout, offsets in floats
   static constexpr int BSTAGE = BS_E + 3 * kN * YS / 2;
   static_assert((2 * YS) % 32 == 16, "dy, C, E row stride");
   // per-head M and the Phi', Psi' accumulators of every lane ([8][kThreads]
-  // f4, in lane order), after the Dv pass (alias the stage)
-  static constexpr int MZ = 0, GRD = (MZ + kN * kNP + 3) & ~3;
+  // f4, in lane order), after the Dv pass (alias the stage).  M is fp32
+  // [kN][kNP] or, with bf16 products, M^T as three bf16 pieces [3][kN][MS]
+  // (rows r, columns s; the row stride an odd multiple of 16 bytes)
+  static constexpr int MS = kN + 8;
+  static constexpr int MZW = kN * kNP > 3 * kN * MS / 2 ? kN * kNP : 3 * kN * MS / 2;
+  static constexpr int MZ = 0, GRD = (MZ + MZW + 3) & ~3;
   static constexpr int HEAD = GRD + 8 * kThreads * 4;
+  static_assert((2 * MS) % 32 == 16, "M piece row stride");
   // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns); with
   // bf16 products, q, k rows as bf16 [kN][KGS] (the row stride an odd
   // number of 16-byte units: the operand reads of 16 rows hit distinct banks)
@@ -782,6 +787,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const int r = 16 * tb + lr;
         const float br = vB[r];
         const f4 phi4 = grd[tb * kThreads + tid], psi4 = grd[(4 + tb) * kThreads + tid];
+        f4 m4;  // M[t][r] of this lane's four steps t
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = tw + 4 * lq + v;
@@ -797,7 +803,17 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           if (in && t > r) pW2[o] = fmaf(-gam * (bt[v] * br), psi, w2);
           // M[t][r] = Phi[t][r] QK[t][r] - Psi[t][r] KK[t][r] (0 outside the
           // chunk: M is multiplied over all 64 rows)
-          pMZ[o] = in ? (br * phi) * qk - ((bt[v] * br) * psi) * kk : 0.f;
+          m4[v] = in ? (br * phi) * qk - ((bt[v] * br) * psi) * kk : 0.f;
+          if constexpr (!BFP) pMZ[o] = m4[v];
+        }
+        if constexpr (BFP) {  // M^T pieces: row r, steps tw + 4 lq .. +3
+          uint2 p0, p1, p2;
+          split3_quad(m4, p0, p1, p2);
+          uint16_t* const mt = reinterpret_cast<uint16_t*>(pMZ);
+          const int om = r * L::MS + tw + 4 * lq;
+          *reinterpret_cast<uint2*>(mt + om) = p0;
+          *reinterpret_cast<uint2*>(mt + kN * L::MS + om) = p1;
+          *reinterpret_cast<uint2*>(mt + 2 * kN * L::MS + om) = p2;
         }
       }
       // dbeta_t = Psi'[t][t]: tile tb = w, lanes lr = 4 lq + v
@@ -823,6 +839,42 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       f4 Bt[5];
 #pragma unroll
       for (int u = 0; u < 5; ++u) Bt[u] = f4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (BFP) {
+        // bf16 MFMA, both operands as three pieces (six piece products):
+        // A = GM rows tw + l % 16, s = 32 ks + 8 (l / 16) ..; B = M^T pieces
+        // (row r = 16 tb + l % 16) and chi in column 0 of the fifth tile
+        const uint16_t* const mt = reinterpret_cast<const uint16_t*>(sm + L::MZ);
+        auto six = [](const uint4 (&x)[3], const uint4 (&y)[3], f4 acc) __attribute__((always_inline)) {
+          acc = mfma_bf16(x[0], y[0], acc);
+          acc = mfma_bf16(x[0], y[1], acc);
+          acc = mfma_bf16(x[1], y[0], acc);
+          acc = mfma_bf16(x[0], y[2], acc);
+          acc = mfma_bf16(x[2], y[0], acc);
+          acc = mfma_bf16(x[1], y[1], acc);
+          return acc;
+        };
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int s0 = 32 * ks + 8 * lq;
+          const float* const gr = sm + L::GM + (tw + lr) * kNP + s0;
+          uint4 ga[3];
+          pieces8(*reinterpret_cast<const f4*>(gr), *reinterpret_cast<const f4*>(gr + 4), ga);
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            uint4 bm[3];
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+              bm[p] = *reinterpret_cast<const uint4*>(mt + p * kN * L::MS + (16 * tb + lr) * L::MS + s0);
+            Bt[tb] = six(ga, bm, Bt[tb]);
+          }
+          const float m0 = lr == 0 ? 1.f : 0.f;
+          const f4 c0 = *reinterpret_cast<const f4*>(sm + L::V_CHI + s0) * m0;
+          const f4 c1 = *reinterpret_cast<const f4*>(sm + L::V_CHI + s0 + 4) * m0;
+          uint4 bc[3];
+          pieces8(c0, c1, bc);
+          Bt[4] = six(ga, bc, Bt[4]);
+        }
+      } else {
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         const int sk = 4 * ks + lq;
@@ -832,6 +884,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           Bt[tb] = mfma(ga, sm[L::MZ + sk * kNP + 16 * tb + lr], Bt[tb]);
         const float cb = lr == 0 ? sm[L::V_CHI + sk] : 0.f;
         Bt[4] = mfma(ga, cb, Bt[4]);
+      }
       }
       const float phi0 = sm[L::V_SCR + 1];
 #pragma unroll
