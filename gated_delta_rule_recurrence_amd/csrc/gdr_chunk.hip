@@ -782,7 +782,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       float bt[4];
 #pragma unroll
       for (int v = 0; v < 4; ++v) bt[v] = vB[tw + 4 * lq + v];
-#pragma unroll 1
+#pragma unroll 2
       for (int tb = 0; tb < 4; ++tb) {
         const int r = 16 * tb + lr;
         const float br = vB[r];
