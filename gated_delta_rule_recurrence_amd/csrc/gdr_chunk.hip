@@ -542,12 +542,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       if (l < n) sm[L::V_SUF + n - 1 - l] = sf;
     }
     // Gam(r, t] for r, t in the chunk: row r is read after the Dv passes
-    {  // rows r = 16 w .. 16 w + 15 of Gam(r, t] (lane l <-> t = l)
+    {  // rows r = 16 w .. 16 w + 15 of Gam(r, t] (lane l <-> t = l): the
+       // wave's last row by a product scan, the others up from it as running
+       // products, Gam(r, t] = g_{r+1} Gam(r+1, t] (1 where t <= r)
       const float gl = l < n ? sm[L::V_G + l] : 1.f;
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
+      const int rl = tw + 15;
+      float y = wave_prefix_product(l > rl ? gl : 1.f);
+      sm[L::GM + rl * kNP + l] = l == rl ? 1.f : ((l > rl && l < n) ? y : 0.f);
+#pragma unroll 5
+      for (int i = 14; i >= 0; --i) {
         const int r = tw + i;
-        const float y = wave_prefix_product(l > r ? gl : 1.f);
+        const float gr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), r + 1));
+        y = l > r ? gr * y : 1.f;
         sm[L::GM + r * kNP + l] = l == r ? 1.f : ((l > r && l < n) ? y : 0.f);
       }
     }
