@@ -197,130 +197,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     return ((int64_t)(b * (int64_t)T + t0 + t) * Hk + hk) * Dk + j;
   };
 
-  // ---- QK and KK for the kv head (shared by all its value heads) ----------
-  if constexpr (BFP) {
-    // bf16 q, k rows staged as bf16, products on bf16 MFMA (exact products)
-    static_assert((2 * L::KGS) % 32 == 16, "q, k row stride");
-    constexpr int NCH = DKP / 8;  // 16-byte chunks per row
-    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
-    uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
-    uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
-    uint4 rq[NL], rk[NL];
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int ci = tid + kThreads * u;
-      const int s = ci / NCH, j = 8 * (ci % NCH);
-      const bool ok = ci < kN * NCH && s < n && j < Dk;
-      int64_t o = ok ? qk_index(s, j) : 0;
-      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
-      rq[u] = *reinterpret_cast<const uint4*>(q + o);
-      rk[u] = *reinterpret_cast<const uint4*>(k + o);
-    }
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int ci = tid + kThreads * u;
-      const int s = ci / NCH, j = 8 * (ci % NCH);
-      const bool ok = ci < kN * NCH && s < n && j < Dk;
-      if (ci < kN * NCH) {
-        uint4 xq = rq[u], xk = rk[u];
-        xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
-        xq.y = ok ? xq.y : 0u;
-        xq.z = ok ? xq.z : 0u;
-        xq.w = ok ? xq.w : 0u;
-        xk.x = ok ? xk.x : 0u;
-        xk.y = ok ? xk.y : 0u;
-        xk.z = ok ? xk.z : 0u;
-        xk.w = ok ? xk.w : 0u;
-        *reinterpret_cast<uint4*>(sq + s * L::KGS + j) = xq;
-        *reinterpret_cast<uint4*>(sk + s * L::KGS + j) = xk;
-      }
-    }
-    __syncthreads();
-    f4 acc[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DKP / 32; ++ks) {
-      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
-      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
-      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const uint4 bk =
-            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
-        acc[tb] = mfma_bf16(aq, bk, acc[tb]);
-        acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
-      }
-    }
-    __syncthreads();  // the stage is reused below
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
-        sm[L::QK + o] = acc[tb][v];
-        sm[L::KK + o] = acc[4 + tb][v];
-      }
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
-      const int e = tid + kThreads * x;
-      const int o = (e >> 6) * kNP + (e & 63);
-      sm[L::W1 + o] = 0.f;
-      sm[L::W2 + o] = 0.f;
-    }
-  } else {
-    f4 acc[8];  // QK tiles (w, 0..3), KK tiles (w, 0..3)
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < Dk; j0 += 64) {
-      // 64 steps x 64 columns of q and k: 4 quads of 4 columns per thread
-      f4 rq[4], rk[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int qi = tid + kThreads * u;
-        const int s = qi >> 4, j = j0 + 4 * (qi & 15);
-        const bool ok = s < n && j < Dk;
-        rq[u] = ld4<VEC>(q, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
-        rk[u] = ld4<VEC>(k, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int qi = tid + kThreads * u;
-        const int s = qi >> 4, jq = qi & 15;
-        *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq[u];
-        *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk[u];
-      }
-      __syncthreads();
-#pragma unroll 2
-      for (int ks = 0; ks < 16; ++ks) {
-        const int fw = ((ks * kN + tw + lr) << 2) + lq;
-        const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
-          acc[tb] = mfma(aq, bk, acc[tb]);
-          acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
-        }
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
-        sm[L::QK + o] = acc[tb][v];
-        sm[L::KK + o] = acc[4 + tb][v];
-      }
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
-      const int e = tid + kThreads * x;
-      const int o = (e >> 6) * kNP + (e & 63);
-      sm[L::W1 + o] = 0.f;
-      sm[L::W2 + o] = 0.f;
-    }
-  }
-
   f4 dQ[JT], dK[JT];
 #pragma unroll
   for (int u = 0; u < JT; ++u) dQ[u] = dK[u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -514,9 +390,139 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   auto gb_index = [&](int hh) {
     return (int64_t)(b * (int64_t)T + t0 + (gb_ok ? tid : 0)) * Hv + hk * rep + hh;
   };
+  // ---- QK and KK for the kv head (shared by all its value heads) ----------
+  if constexpr (BFP) {
+    // bf16 q, k rows staged as bf16, products on bf16 MFMA (exact products)
+    static_assert((2 * L::KGS) % 32 == 16, "q, k row stride");
+    constexpr int NCH = DKP / 8;  // 16-byte chunks per row
+    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
+    uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
+    uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
+    uint4 rq[NL], rk[NL];
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int ci = tid + kThreads * u;
+      const int s = ci / NCH, j = 8 * (ci % NCH);
+      const bool ok = ci < kN * NCH && s < n && j < Dk;
+      int64_t o = ok ? qk_index(s, j) : 0;
+      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+      rq[u] = *reinterpret_cast<const uint4*>(q + o);
+      rk[u] = *reinterpret_cast<const uint4*>(k + o);
+    }
+    // the first two blocks of the Dv passes, in flight during QK and KK
+    // (issued after the q, k loads: waiting for those never waits for these)
+    fetch(RA, 0);
+    fetch(RB, 1);
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int ci = tid + kThreads * u;
+      const int s = ci / NCH, j = 8 * (ci % NCH);
+      const bool ok = ci < kN * NCH && s < n && j < Dk;
+      if (ci < kN * NCH) {
+        uint4 xq = rq[u], xk = rk[u];
+        xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
+        xq.y = ok ? xq.y : 0u;
+        xq.z = ok ? xq.z : 0u;
+        xq.w = ok ? xq.w : 0u;
+        xk.x = ok ? xk.x : 0u;
+        xk.y = ok ? xk.y : 0u;
+        xk.z = ok ? xk.z : 0u;
+        xk.w = ok ? xk.w : 0u;
+        *reinterpret_cast<uint4*>(sq + s * L::KGS + j) = xq;
+        *reinterpret_cast<uint4*>(sk + s * L::KGS + j) = xk;
+      }
+    }
+    __syncthreads();
+    f4 acc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < DKP / 32; ++ks) {
+      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
+      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
+      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        const uint4 bk =
+            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
+        acc[tb] = mfma_bf16(aq, bk, acc[tb]);
+        acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
+      }
+    }
+    __syncthreads();  // the stage is reused below
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sm[L::QK + o] = acc[tb][v];
+        sm[L::KK + o] = acc[4 + tb][v];
+      }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
+      const int e = tid + kThreads * x;
+      const int o = (e >> 6) * kNP + (e & 63);
+      sm[L::W1 + o] = 0.f;
+      sm[L::W2 + o] = 0.f;
+    }
+  } else {
+    f4 acc[8];  // QK tiles (w, 0..3), KK tiles (w, 0..3)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < Dk; j0 += 64) {
+      // 64 steps x 64 columns of q and k: 4 quads of 4 columns per thread
+      f4 rq[4], rk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qi = tid + kThreads * u;
+        const int s = qi >> 4, j = j0 + 4 * (qi & 15);
+        const bool ok = s < n && j < Dk;
+        rq[u] = ld4<VEC>(q, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
+        rk[u] = ld4<VEC>(k, qk_index(ok ? s : 0, ok ? j : 0), ok, Dk - j);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qi = tid + kThreads * u;
+        const int s = qi >> 4, jq = qi & 15;
+        *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq[u];
+        *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk[u];
+      }
+      __syncthreads();
+#pragma unroll 2
+      for (int ks = 0; ks < 16; ++ks) {
+        const int fw = ((ks * kN + tw + lr) << 2) + lq;
+        const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
+          acc[tb] = mfma(aq, bk, acc[tb]);
+          acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
+        sm[L::QK + o] = acc[tb][v];
+        sm[L::KK + o] = acc[4 + tb][v];
+      }
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
+      const int e = tid + kThreads * x;
+      const int o = (e >> 6) * kNP + (e & 63);
+      sm[L::W1 + o] = 0.f;
+      sm[L::W2 + o] = 0.f;
+    }
+  }
+
   TIn g_nx = g[gb_index(0)], b_nx = beta[gb_index(0)];
-  fetch(RA, 0);
-  fetch(RB, 1);
+  if constexpr (!BFP) {
+    fetch(RA, 0);
+    fetch(RB, 1);
+  }
 
   for (int hh = 0; hh < rep; ++hh) {
     // per-head vectors: g, beta and the running decay products
