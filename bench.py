@@ -33,8 +33,8 @@ FLOPS_BWD = 15                 # per state element per step (reverse sweep)
 # by a plain-copy calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).
 # They describe the kernels built from sources with this digest and are not
 # reported otherwise.
-BWD_TRAFFIC = {"sources_sha256_16": "974ccefb9055cb45",
-               "read_bytes": 971.2e6, "write_bytes": 519.0e6}
+BWD_TRAFFIC = {"sources_sha256_16": "432195f4dce64c7d",
+               "read_bytes": 969.8e6, "write_bytes": 518.8e6}
 BWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
                "gdr_chunk.hip")
 
