@@ -104,6 +104,22 @@ def test_qwen_bf16_T256_full(cuda):
     compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["bf16"], "qwen T=256")
 
 
+@pytest.mark.parametrize("decay,seed,s0", [("weak", 31, None), ("strong", 32, None),
+                                             ("mix", 33, 0.05)])
+def test_bf16_state_outputs_fp32_accurate(cuda, decay, seed, s0):
+    """With bf16 inputs the state stays fp32 and the bf16-product kernels split
+    every fp32 operand exactly into three bf16 pieces, so the products keep
+    fp32 accuracy.  The bf16 outputs only show that to bf16 rounding; the
+    fp32 outputs S_T (forward sweep) and dS0 (reverse sweep) must meet the
+    fp32 bar against the oracle fed the same bf16-rounded inputs."""
+    p = inputs.draw(1, 256, 16, 64, 192, 128, seed=seed, normalised=True, decay=decay,
+                    S0_std=s0, dST_std=1.0, dtype="bf16")
+    log(f"bf16 Qwen shape T=256 decay={decay}: fp32 outputs at the fp32 bar")
+    errs = compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["bf16"], f"bf16 {decay}")
+    for name in ("S_T", "dS0"):
+        assert errs[name] <= TOL["f32"], f"bf16 {decay}: {name} rel L2 {errs[name]:.2e}"
+
+
 def test_qwen_f32_T256_sampled(cuda):
     p = inputs.qwen35_9b(256, dtype="f32")
     gpu = run_gpu(p, cuda, 64)
