@@ -120,6 +120,26 @@ def test_bf16_state_outputs_fp32_accurate(cuda, decay, seed, s0):
         assert errs[name] <= TOL["f32"], f"bf16 {decay}: {name} rel L2 {errs[name]:.2e}"
 
 
+def test_bf16_products_match_fp32_path(cuda):
+    """The bf16-product kernels against the fp32-operand kernels on the same
+    bf16-valued inputs (headline shape, T=256).  Both compute at fp32
+    accuracy, so after rounding the fp32 path's outputs to bf16 only a few in
+    10,000 elements differ (rounding-boundary flips: 1.4-4.9e-4 of them, rel
+    L2 of the difference 0.9-4.4e-5 when written).  A loss of precision in
+    the piece products would raise both several-fold; the bars leave a
+    fourfold margin."""
+    import dataclasses
+    p = inputs.qwen35_9b(256)
+    p32 = dataclasses.replace(p, dtype="f32")
+    gb, gf = run_gpu(p, cuda, 64), run_gpu(p32, cuda, 64)
+    for name in ("y", "dq", "dk", "dv", "dg", "dbeta"):
+        a, ref = gb[name], inputs.bf16_round(gf[name])
+        frac = float(np.mean(a != ref))
+        rel = float(np.linalg.norm(a - ref) / np.linalg.norm(ref))
+        log(f"  {name}: differing {frac:.2e}, rel L2 {rel:.2e}")
+        assert frac <= 2e-3 and rel <= 2e-4, f"{name}: differing {frac:.2e}, rel L2 {rel:.2e}"
+
+
 def test_qwen_f32_T256_sampled(cuda):
     p = inputs.qwen35_9b(256, dtype="f32")
     gpu = run_gpu(p, cuda, 64)
