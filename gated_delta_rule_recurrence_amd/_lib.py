@@ -43,6 +43,7 @@ _SIGNATURES = {
     "gdr_forward_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(GdrShape), ctypes.POINTER(ctypes.c_size_t)]),
     "gdr_forward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 11
                     + [ctypes.c_size_t, _vp]),
+    "gdr_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 11),
     "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 15
                      + [ctypes.c_size_t, _vp]),
     "gdr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
@@ -126,6 +127,17 @@ def forward_raw(shape, q, k, v, g, beta, S0, y, S_T, ckpt, workspace,
     return load().gdr_forward(ctypes.byref(shape), *ptrs,
                               ctypes.c_size_t(int(workspace_bytes)),
                               _vp(stream or None))
+
+
+def forward_noalloc_raw(shape, q, k, v, g, beta, S0, y, S_T, ckpt, stream, mask=0) -> int:
+    """gdr_forward_noalloc with integer device addresses (0 = NULL); returns
+    the status."""
+    ptrs = [_vp(x or None) for x in (q, k, v, g, beta, S0, mask, y, S_T, ckpt)]
+    return load().gdr_forward_noalloc(ctypes.byref(shape), *ptrs, _vp(stream or None))
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # GDR_NOALLOC_SCRATCH_BYTES
+GDR_ERR_SCRATCH_LIMIT = -12
 
 
 def backward_raw(shape, q, k, g, beta, ckpt, dy, dS_T, dq, dk, dv, dg, dbeta,

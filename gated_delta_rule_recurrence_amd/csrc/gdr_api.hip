@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/gdr.h"
 #include "gdr_internal.h"
@@ -92,6 +93,105 @@ bool aligned16(const void* p) {
 
 }  // namespace
 
+// ---- scratch of gdr_forward_noalloc ---------------------------------------
+// The chunked forward's per-chunk records live here for callers that cannot
+// allocate.  Each device that loads the library holds its own copy for the
+// life of the process.  In host code `scratch` is only a stand-in for the
+// symbol: its device address comes from hipGetSymbolAddress, once per
+// device, and only that address is handed to kernels.  Nothing in it has to
+// start at zero: the prep kernel writes every record the sweep then reads.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device, with that device current), or nullptr if HIP fails.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+// gdr_forward's pointer checks (required pointers, alignment)
+int forward_pointers_ok(const gdr_shape* shape, const void* q, const void* k, const void* v,
+                        const void* g, const void* beta, const float* S0, const void* y,
+                        const float* S_T, const void* ckpt, const void* workspace) {
+  const bool has_tokens = shape->B > 0 && shape->T > 0;
+  if (has_tokens && (!q || !k || !v || !g || !beta || !y))
+    return GDR_ERR_NULL_ARG;
+  const void* ptrs[] = {q, k, v, g, beta, S0, y, S_T, ckpt, workspace};
+  for (const void* p : ptrs)
+    if (p != nullptr && !aligned16(p)) return GDR_ERR_ALIGNMENT;
+  return GDR_OK;
+}
+
+// gdr_forward after check_shape: the caller's workspace, or the
+// no-allocation scratch array
+int forward_checked(const gdr_shape* shape, const Sizes& z, const void* q, const void* k,
+                    const void* v, const void* g, const void* beta, const float* S0,
+                    const uint8_t* mask, void* y, float* S_T, void* ckpt, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const bool has_tokens = shape->B > 0 && shape->T > 0;
+  const bool has_state = shape->B > 0;
+  const int pst = forward_pointers_ok(shape, q, k, v, g, beta, S0, y, S_T, ckpt, workspace);
+  if (pst != GDR_OK) return pst;
+  if (has_tokens && z.fws_bytes > 0 &&
+      (workspace == nullptr || workspace_bytes < static_cast<size_t>(z.fws_bytes)))
+    return GDR_ERR_WORKSPACE;
+  if (!has_state) return GDR_OK;
+
+  gdr::FwdSweepArgs a{};
+  a.B = (int)shape->B;
+  a.T = (int)shape->T;
+  a.Hk = (int)shape->Hk;
+  a.Hv = (int)shape->Hv;
+  a.Dk = (int)shape->Dk;
+  a.Dv = (int)shape->Dv;
+  a.L = (int)shape->chunk;
+  a.nch = (int)z.nch;
+  a.log_g = shape->decay == GDR_DECAY_LOG;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.S0 = S0;
+  a.mask = mask;
+  a.y = y;
+  a.ST = S_T;
+  if (ckpt != nullptr) {
+    a.Sck = static_cast<float*>(ckpt);
+    a.E = reinterpret_cast<float*>(static_cast<char*>(ckpt) + z.e_off);
+  }
+  if (!has_tokens && S_T == nullptr) return GDR_OK;
+  const bool bf16 = shape->dtype == GDR_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  if (has_tokens && gdr::decode_ok(shape->T)) {
+    err = gdr::launch_decode(a, bf16, s);
+  } else if (has_tokens && z.fws_bytes > 0) {
+    gdr::FwdChunkedArgs c{};
+    c.s = a;
+    c.prep = static_cast<float*>(workspace);
+    err = gdr::launch_fwd_chunked(c, bf16, s);
+  } else {
+    err = gdr::launch_fwd_sweep(a, bf16, s);
+  }
+  return err == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" {
 
 int gdr_num_chunks(const gdr_shape* shape, int64_t* out) {
@@ -138,56 +238,27 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
   Sizes z;
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
-  const bool has_tokens = shape->B > 0 && shape->T > 0;
-  const bool has_state = shape->B > 0;
-  if (has_tokens && (!q || !k || !v || !g || !beta || !y))
-    return GDR_ERR_NULL_ARG;
-  const void* ptrs[] = {q, k, v, g, beta, S0, y, S_T, ckpt, workspace};
-  for (const void* p : ptrs)
-    if (p != nullptr && !aligned16(p)) return GDR_ERR_ALIGNMENT;
-  if (has_tokens && z.fws_bytes > 0 &&
-      (workspace == nullptr || workspace_bytes < static_cast<size_t>(z.fws_bytes)))
-    return GDR_ERR_WORKSPACE;
-  if (!has_state) return GDR_OK;
+  return forward_checked(shape, z, q, k, v, g, beta, S0, mask, y, S_T, ckpt, workspace,
+                         workspace_bytes, stream);
+}
 
-  gdr::FwdSweepArgs a{};
-  a.B = (int)shape->B;
-  a.T = (int)shape->T;
-  a.Hk = (int)shape->Hk;
-  a.Hv = (int)shape->Hv;
-  a.Dk = (int)shape->Dk;
-  a.Dv = (int)shape->Dv;
-  a.L = (int)shape->chunk;
-  a.nch = (int)z.nch;
-  a.log_g = shape->decay == GDR_DECAY_LOG;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.g = g;
-  a.beta = beta;
-  a.S0 = S0;
-  a.mask = mask;
-  a.y = y;
-  a.ST = S_T;
-  if (ckpt != nullptr) {
-    a.Sck = static_cast<float*>(ckpt);
-    a.E = reinterpret_cast<float*>(static_cast<char*>(ckpt) + z.e_off);
+int gdr_forward_noalloc(const gdr_shape* shape, const void* q, const void* k,
+                        const void* v, const void* g, const void* beta,
+                        const float* S0, const uint8_t* mask, void* y, float* S_T,
+                        void* ckpt, void* stream) {
+  Sizes z;
+  const int st = check_shape(shape, &z);
+  if (st != GDR_OK) return st;
+  if (z.fws_bytes > static_cast<int64_t>(GDR_NOALLOC_SCRATCH_BYTES)) return GDR_ERR_SCRATCH_LIMIT;
+  const int pst = forward_pointers_ok(shape, q, k, v, g, beta, S0, y, S_T, ckpt, nullptr);
+  if (pst != GDR_OK) return pst;
+  void* ws = nullptr;
+  if (z.fws_bytes > 0 && shape->B > 0 && shape->T > 0) {
+    ws = scratch_address();
+    if (ws == nullptr) return GDR_ERR_HIP;
   }
-  if (!has_tokens && S_T == nullptr) return GDR_OK;
-  const bool bf16 = shape->dtype == GDR_BF16;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t err;
-  if (has_tokens && gdr::decode_ok(shape->T)) {
-    err = gdr::launch_decode(a, bf16, s);
-  } else if (has_tokens && z.fws_bytes > 0) {
-    gdr::FwdChunkedArgs c{};
-    c.s = a;
-    c.prep = static_cast<float*>(workspace);
-    err = gdr::launch_fwd_chunked(c, bf16, s);
-  } else {
-    err = gdr::launch_fwd_sweep(a, bf16, s);
-  }
-  return err == hipSuccess ? GDR_OK : GDR_ERR_HIP;
+  return forward_checked(shape, z, q, k, v, g, beta, S0, mask, y, S_T, ckpt, ws,
+                         ws != nullptr ? GDR_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
@@ -293,11 +364,13 @@ const char* gdr_strerror(int status) {
     case GDR_ERR_ALIGNMENT: return "a pointer is not 16-byte aligned";
     case GDR_ERR_HIP: return "the HIP runtime rejected a kernel launch";
     case GDR_ERR_BAD_DECAY: return "decay must be GDR_DECAY_G or GDR_DECAY_LOG";
+    case GDR_ERR_SCRATCH_LIMIT:
+      return "the forward workspace this shape needs exceeds the no-allocation scratch";
   }
   return "unknown gdr status";
 }
 
-const char* gdr_version(void) { return "0.4.0"; }
+const char* gdr_version(void) { return "0.5.0"; }
 
 }  // extern "C"
 

@@ -55,8 +55,15 @@ typedef enum {
   GDR_ERR_WORKSPACE = -8,       /* workspace smaller than the size query says  */
   GDR_ERR_ALIGNMENT = -9,       /* a pointer is not 16-byte aligned             */
   GDR_ERR_HIP = -10,            /* the HIP runtime rejected a launch            */
-  GDR_ERR_BAD_DECAY = -11       /* decay is not GDR_DECAY_G or GDR_DECAY_LOG    */
+  GDR_ERR_BAD_DECAY = -11,      /* decay is not GDR_DECAY_G or GDR_DECAY_LOG    */
+  GDR_ERR_SCRATCH_LIMIT = -12   /* gdr_forward_noalloc: the shape's forward
+                                   workspace exceeds GDR_NOALLOC_SCRATCH_BYTES */
 } gdr_status;
+
+/* Size of the device-side scratch array behind gdr_forward_noalloc (128 MiB;
+ * each device that loads the library holds one for the life of the
+ * process). */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
 
@@ -133,6 +140,26 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
                 const float* S0, const uint8_t* mask, void* y, float* S_T,
                 void* ckpt, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/* gdr_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as gdr_forward, without the workspace:
+ * the chunked forward's per-chunk records go to a scratch array inside the
+ * library (GDR_NOALLOC_SCRATCH_BYTES per device, located once per device on
+ * its first use).  The call allocates and frees nothing; the caller still
+ * passes every input and output buffer (ckpt included, when saving).
+ *   Limit: shapes whose gdr_forward_workspace_bytes exceeds
+ *   GDR_NOALLOC_SCRATCH_BYTES are rejected with GDR_ERR_SCRATCH_LIMIT before
+ *   anything is enqueued (at Hv = 64 and chunk 64 that is B * T up to about
+ *   2,600 steps; shapes with a 0-byte workspace always pass).
+ *   Concurrency: every call on one device shares that device's array, so
+ *   calls whose work overlaps on one device (different streams, or other
+ *   host threads) race on it and give undefined results; calls ordered on
+ *   one stream are safe. */
+int gdr_forward_noalloc(const gdr_shape* shape, const void* q, const void* k,
+                        const void* v, const void* g, const void* beta,
+                        const float* S0, const uint8_t* mask, void* y, float* S_T,
+                        void* ckpt, void* stream);
 
 /* Backward pass (VJP of gdr_forward for L = <dy, y> + <dS_T, S_T>).
  *   in : q, k, g, beta, dy (shape.dtype) - the same q, k, g, beta and mask

@@ -54,7 +54,7 @@ def test_binding_covers_header():
 
 def test_version_and_strerror(lib):
     assert re.fullmatch(r"\d+\.\d+\.\d+", lib.gdr_version().decode())
-    for code in range(0, -12, -1):
+    for code in range(0, -13, -1):
         assert "unknown" not in _lib.strerror(code)
     assert "unknown" in _lib.strerror(-999)
 
@@ -174,3 +174,40 @@ def test_empty_batch_is_a_no_op(lib):
     sh = S(T=0)
     assert _lib.forward_raw(sh, *([0] * 10), 0, 0) == 0
     assert _lib.backward_raw(sh, *([0] * 14), 0, 0) == 0
+
+
+# ---- gdr_forward_noalloc: the same host-side checks, plus the scratch limit
+def test_noalloc_shape_errors(lib):
+    for shape, code in [(S(Hk=3, Hv=4), -3), (S(chunk=0), -5), (S(dtype=2), -6),
+                        (S(Dk=257), -4)]:
+        assert _lib.forward_noalloc_raw(shape, *([0] * 9), 0) == code
+    assert lib.gdr_forward_noalloc(None, *([None] * 11)) == -1
+
+
+def test_noalloc_scratch_limit(lib):
+    """A shape whose forward workspace (the chunked forward's per-chunk
+    records) exceeds the scratch array is rejected before anything runs."""
+    big = S(1, 4096, 16, 64, 192, 128, 64, _lib.GDR_BF16)
+    assert _lib.forward_workspace_bytes(big) > _lib.NOALLOC_SCRATCH_BYTES
+    assert _lib.forward_noalloc_raw(big, *([FAKE] * 9), 0) == _lib.GDR_ERR_SCRATCH_LIMIT
+    fits = S(1, 2048, 16, 64, 192, 128, 64, _lib.GDR_BF16)
+    assert 0 < _lib.forward_workspace_bytes(fits) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert "scratch" in _lib.strerror(_lib.GDR_ERR_SCRATCH_LIMIT)
+
+
+def test_noalloc_pointer_errors(lib):
+    sh = S(T=64, Dk=64, Dv=32, chunk=32)  # takes the chunked forward (scratch)
+    assert _lib.forward_workspace_bytes(sh) > 0
+    for i in (0, 1, 2, 3, 4, 6):  # q, k, v, g, beta, y
+        ptrs = [FAKE] * 9
+        ptrs[i] = 0
+        assert _lib.forward_noalloc_raw(sh, *ptrs, 0) == -1
+    for i in range(9):
+        ptrs = [FAKE] * 9
+        ptrs[i] = FAKE + 4
+        assert _lib.forward_noalloc_raw(sh, *ptrs, 0) == -9
+
+
+def test_noalloc_empty_is_a_no_op(lib):
+    assert _lib.forward_noalloc_raw(S(B=0), *([0] * 9), 0) == 0
+    assert _lib.forward_noalloc_raw(S(T=0), *([0] * 9), 0) == 0
