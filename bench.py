@@ -7,11 +7,21 @@ fp32 state, weak decay, normalised q/k, S0=0 (synthetic, seeded).  A step is
 one gdr_forward (with save) plus one gdr_backward over that batch; inputs and
 every output/scratch buffer are resident in HBM before timing starts.
 
-Prints one JSON line (see README of the bench contract in the design doc).
+Default: prints one JSON line (the training step).  Other modes print one
+JSON line per case and exit:
+  --t-sweep       the same heads at T = 256, 512, 1024, 2048 (the Performance
+                  table's lengths): fwd/bwd ms, tokens/s, peak device memory;
+  --vjp-batch     the focused VJP shape of unsloth-zoo PR #776 (B = 1, 2, 4,
+                  8, T=64, Hk=Hv=2, Dk=Dv=64, fp32): backward alone and fwd+bwd;
+  --chunk-sweep   the long-context shape (B=4, T=8192) over checkpoint
+                  intervals C;
+  --decode B      single-step inference at batch B;
+  --copy-calibration MIB   a plain device copy (for the HBM byte counters).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,20 +37,32 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_PEAK_TF = 157.3           # MI355X FP32: dense MFMA and (packed) vector, TFLOP/s
 FLOPS_FWD = 7                  # per state element per step (S k, S q, decay+rank-1)
 FLOPS_BWD = 15                 # per state element per step (reverse sweep)
+PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value head, chunk)
 
-# HBM bytes per gdr_backward call at the default workload (the sum over its
-# three kernels), from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs scaled
-# by a plain-copy calibration (profiles/hbm_bytes_qwen35-9b_T2048_bf16.md).
-# They describe the kernels built from sources with this digest and are not
-# reported otherwise.
-BWD_TRAFFIC = {"sources_sha256_16": "432195f4dce64c7d",
-               "read_bytes": 969.8e6, "write_bytes": 518.8e6}
-BWD_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
-               "gdr_chunk.hip")
+# Counter figures for the default workload, from the rocprofv3 summaries
+# under profiles/ (HBM bytes: FETCH_SIZE and WRITE_SIZE scaled by a plain
+# copy; pipe utilisation: SQ counters).  They describe the kernels built from
+# the sources with this digest and are reported only while the sources still
+# hash to it (null otherwise).
+PROFILE = {
+    "sources_sha256_16": "12371b103bee4d16",
+    "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
+              "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
+    "bwd_read_bytes": 969.8e6, "bwd_write_bytes": 518.8e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 483.4e6,
+    "kernels": {
+        "prep_kernel<fwd>": {"mfma_busy_pct": 4.4, "valu_busy_pct": 16.9},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 49.0},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 4.6, "valu_busy_pct": 17.3},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.3, "valu_busy_pct": 47.4},
+        "chunk_kernel": {"mfma_busy_pct": 21.0, "valu_busy_pct": 33.0},
+    },
+}
+PROFILED_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
+                    "gdr_chunk.hip")
 
 
-def sources_digest(files):
-    import hashlib
+def sources_digest(files=PROFILED_SOURCES):
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_recurrence_amd", "csrc", f), "rb") as fh:
@@ -59,21 +81,151 @@ def parse():
     ap.add_argument("--dtype", default="bf16", choices=("bf16", "f32"))
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-T", type=int, default=2048)
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (default: the CPU affinity size, at most 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read + write), "
                          "the reference for scaling HBM byte counters, and exit")
     ap.add_argument("--chunk-sweep", action="store_true",
-                    help="instead of the training step, time fwd+bwd at the long-context "
-                         "shape (B=4, T=8192, Qwen3.5-9B heads, trainable S0) for the "
-                         "chunk sizes 8..64 the library takes, one JSON line each, and exit")
+                    help="time fwd+bwd at the long-context shape (B=4, T=8192, "
+                         "Qwen3.5-9B heads, trainable S0) for a range of checkpoint "
+                         "intervals, one JSON line each, and exit")
+    ap.add_argument("--chunks", default="16,32,64",
+                    help="checkpoint intervals of --chunk-sweep")
+    ap.add_argument("--t-sweep", action="store_true",
+                    help="time fwd+bwd at the Qwen3.5-9B heads for T = 256, 512, 1024, "
+                         "2048, one JSON line each, and exit")
+    ap.add_argument("--vjp-batch", action="store_true",
+                    help="time the backward alone (and fwd+bwd) at B = 1, 2, 4, 8, T=64, "
+                         "Hk=Hv=2, Dk=Dv=64, fp32, one JSON line each, and exit")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
-                    help="instead of the training step, time single-step inference "
-                         "(T=1, state updated in place, no save buffer) at batch B "
-                         "with the same heads, and exit")
+                    help="time single-step inference (T=1, state updated in place, no "
+                         "save buffer) at batch B with the same heads, and exit")
     return ap.parse_args()
 
 
+# ---------------------------------------------------------------- helpers --
+def algorithmic_bytes(B, T, Hk, Hv, Dk, Dv, esz, nch, s0=False, dst=False):
+    """The minimum HBM bytes of each call, every tensor touched once: the
+    forward reads q, k, v, g, beta (and S0) and writes y, the chunk
+    checkpoints and S_T; the backward reads q, k, v, g, beta, dy (and dS_T)
+    and the checkpoints and writes dq, dk, dv, dg, dbeta and dS0."""
+    tok = B * T
+    state = B * Hv * Dv * Dk * 4
+    fwd = tok * (2 * Hk * Dk + 2 * Hv * Dv + 2 * Hv) * esz + nch * state + state
+    bwd = tok * (4 * Hk * Dk + 3 * Hv * Dv + 4 * Hv) * esz + nch * state + state
+    return fwd + (state if s0 else 0), bwd + (state if dst else 0)
+
+
+def intermediate_bytes(B, T, Hv, Dv, Dk, nch, chunked):
+    """HBM round trips of the design's own intermediates (written by one
+    kernel, read by another): the fp32 residual e, the state-gradient
+    checkpoints, the per-step vectors c and the per-chunk records."""
+    rows32 = B * T * Hv * Dv * 4
+    state = B * Hv * Dv * Dk * 4
+    prep = B * Hv * nch * PREP_RECORD_BYTES if chunked else 0
+    fwd = rows32 + 2 * prep                  # e written; records written + read
+    bwd = rows32 + 2 * nch * state + 2 * rows32 + 2 * prep  # e read; H, c, records
+    return fwd, bwd
+
+
+class Step:
+    """Every buffer of one fwd+bwd step at one shape, allocated up front, and
+    the two library calls on the current stream."""
+
+    def __init__(self, d, chunk, with_dST=False):
+        import torch
+        from gated_delta_rule_recurrence_amd import _lib, ops
+        self.d = d
+        q, v = d["q"], d["v"]
+        dev = q.device
+        B, T, Hk, Dk = q.shape
+        Hv, Dv = v.shape[2], v.shape[3]
+        self.shape = ops.shape_of(q, v, chunk, q.dtype)
+        self.ckpt = torch.empty(_lib.checkpoint_bytes(self.shape), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(_lib.backward_workspace_bytes(self.shape), dtype=torch.uint8,
+                              device=dev)
+        self.fws = torch.empty(max(_lib.forward_workspace_bytes(self.shape), 1),
+                               dtype=torch.uint8, device=dev)
+        self.chunked = _lib.forward_workspace_bytes(self.shape) > 0
+        self.y = torch.empty_like(v)
+        self.S_T = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
+        self.outs = (torch.empty_like(q), torch.empty_like(d["k"]), torch.empty_like(v),
+                     torch.empty_like(d["g"]), torch.empty_like(d["beta"]),
+                     torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev))
+        self.dST = (torch.randn((B, Hv, Dv, Dk), device=dev) if with_dST else None)
+        self.saved = ops.Saved(self.ckpt, chunk)
+        self.chunk = chunk
+        self.nch = _lib.num_chunks(self.shape)
+        self.stream = torch.cuda.current_stream(dev)
+
+    def fwd(self):
+        from gated_delta_rule_recurrence_amd import ops
+        d = self.d
+        ops.gdr_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d.get("S0"),
+                        chunk=self.chunk, y=self.y, S_T=self.S_T, ckpt=self.ckpt,
+                        workspace=self.fws)
+
+    def bwd(self):
+        from gated_delta_rule_recurrence_amd import ops
+        d = self.d
+        ops.gdr_backward(d["q"], d["k"], d["g"], d["beta"], self.saved, d["dy"], self.dST,
+                         workspace=self.ws, out=self.outs)
+
+    def buffer_MB(self):
+        return {"checkpoint_MB": self.ckpt.numel() / 1e6,
+                "workspace_fwd_MB": (self.fws.numel() if self.chunked else 0) / 1e6,
+                "workspace_bwd_MB": self.ws.numel() / 1e6}
+
+    def time(self, n, warmup=3):
+        """Median and min fwd, bwd and step ms over n steps (HIP events on
+        the stream the library launches on)."""
+        import torch
+        for _ in range(warmup):
+            self.fwd()
+            self.bwd()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+        for e in ev:
+            e[0].record(self.stream)
+            self.fwd()
+            e[1].record(self.stream)
+            self.bwd()
+            e[2].record(self.stream)
+        torch.cuda.synchronize()
+        f = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        b = np.array([e[1].elapsed_time(e[2]) for e in ev])
+        return f, b
+
+
+def device_problem(B, T, Hk, Hv, Dk, Dv, dev, seed, dtype, decay="weak", S0_std=None):
+    from gated_delta_rule_recurrence_amd import inputs
+    return inputs.draw_device(B, T, Hk, Hv, Dk, Dv, device=dev, seed=seed, normalised=True,
+                              decay=decay, S0_std=S0_std, dtype=dtype)
+
+
+def copy_bandwidth(dev, mib=1024, reps=5):
+    """Attainable HBM bandwidth: a plain device copy of `mib` MiB (read +
+    write), best of `reps` by HIP events."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------ modes --
 def decode(args):
     """Inference decode: T=1 steps with the state in and out of one buffer.
     The steps are captured in a HIP graph (torch.cuda.CUDAGraph) so that the
@@ -131,69 +283,90 @@ def decode(args):
 def chunk_sweep(args):
     """Long-context training step (B=4, T=8192, Hk=16, Hv=64, Dk=192, Dv=128,
     S0 ~ N(0, 0.05), decay alternating weak/strong over value heads) for each
-    chunk size C: median fwd and bwd times by HIP events, save-buffer and
-    workspace sizes, algorithmic HBM bytes.  Inputs drawn on the device
-    (inputs.draw_device: the draw() distributions)."""
+    checkpoint interval C: median fwd and bwd times by HIP events, save
+    buffer and workspace sizes, algorithmic HBM bytes.  Inputs drawn on the
+    device (inputs.draw_device: the draw() distributions)."""
     import torch
-    from gated_delta_rule_recurrence_amd import _lib, inputs, ops
+    from gated_delta_rule_recurrence_amd import _lib
     dev = torch.device("cuda:0")
     _lib.load()
     B, T, Hk, Hv, Dk, Dv = 4, 8192, 16, 64, 192, 128
-    d = inputs.draw_device(B, T, Hk, Hv, Dk, Dv, device=dev, seed=args.seed, decay="mix",
-                           S0_std=0.05, dtype=args.dtype)
-    q, k, v, g, beta, dy, S0 = (d[n] for n in ("q", "k", "v", "g", "beta", "dy", "S0"))
+    d = device_problem(B, T, Hk, Hv, Dk, Dv, dev, args.seed, args.dtype, decay="mix",
+                       S0_std=0.05)
+    torch.cuda.synchronize()
     esz = 2 if args.dtype == "bf16" else 4
-    for C in (8, 16, 32, 64):  # the library's range: a chunk is one 64-step tile
-        shape = ops.shape_of(q, v, C, q.dtype)
-        ckpt = torch.empty(_lib.checkpoint_bytes(shape), dtype=torch.uint8, device=dev)
-        ws = torch.empty(_lib.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-        fws = torch.empty(max(_lib.forward_workspace_bytes(shape), 1), dtype=torch.uint8,
-                          device=dev)
-        y = torch.empty_like(v)
-        S_T = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
-        outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-                torch.empty_like(g), torch.empty_like(beta), torch.empty_like(S_T))
-        saved = ops.Saved(ckpt, C)
-
-        def fwd():
-            ops.gdr_forward(q, k, v, g, beta, S0, chunk=C, y=y, S_T=S_T, ckpt=ckpt,
-                            workspace=fws)
-
-        def bwd():
-            ops.gdr_backward(q, k, g, beta, saved, dy, None, workspace=ws, out=outs)
-
-        for _ in range(3):
-            fwd()
-            bwd()
-        torch.cuda.synchronize()
-        n = 10
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
-        for i in range(n):
-            ev[i][0].record()
-            fwd()
-            ev[i][1].record()
-            bwd()
-            ev[i][2].record()
-        torch.cuda.synchronize()
-        f = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
-        b = float(np.median([e[1].elapsed_time(e[2]) for e in ev]))
-        nch = -(-T // C)
-        tok_in = B * T * (2 * Hk * Dk + Hv * Dv + 2 * Hv) * esz
-        rows32 = B * T * Hv * Dv * 4
-        state = B * Hv * Dv * Dk * 4
-        nbytes = (2 * tok_in + B * T * Hv * Dv * esz + 2 * rows32 + (2 * nch + 3) * state
-                  + tok_in)
+    for C in (int(c) for c in args.chunks.split(",")):
+        torch.cuda.reset_peak_memory_stats(dev)
+        st = Step(d, C)
+        f, b = st.time(10)
+        f, b = float(np.median(f)), float(np.median(b))
+        fb, bb = algorithmic_bytes(B, T, Hk, Hv, Dk, Dv, esz, st.nch, s0=True)
         print(json.dumps({"chunk_sweep": {
             "C": C, "B": B, "T": T, "dtype": args.dtype,
-            "path": "chunked" if _lib.forward_workspace_bytes(shape) > 0 else "sweep",
+            "path": "chunked" if st.chunked else "per-step sweeps",
             "fwd_ms_median": f, "bwd_ms_median": b, "tokens_per_s": B * T / ((f + b) * 1e-3),
-            "checkpoint_MB": ckpt.numel() / 1e6, "workspace_fwd_MB": fws.numel() / 1e6,
-            "workspace_bwd_MB": ws.numel() / 1e6,
-            "algorithmic_bytes": nbytes,
-            "hbm_frac_algorithmic": nbytes / ((f + b) * 1e-3) / 1e9 / HBM_PEAK_GBS}}),
+            **st.buffer_MB(),
+            "peak_device_memory_MB": torch.cuda.max_memory_allocated(dev) / 1e6,
+            "algorithmic_bytes": fb + bb,
+            "hbm_frac_algorithmic": (fb + bb) / ((f + b) * 1e-3) / 1e9 / HBM_PEAK_GBS}}),
             flush=True)
-        del ckpt, ws, fws, y, S_T, outs, saved
+        del st
         torch.cuda.empty_cache()
+
+
+def t_sweep(args):
+    """The headline heads (B=1, Hk=16, Hv=64, Dk=192, Dv=128, bf16) at the
+    lengths of the mlx-lm PR #1217 Performance table: median fwd, bwd and
+    step ms (HIP events), tokens/s, save buffer and workspaces, and the peak
+    device memory of the step (inputs included)."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib
+    dev = torch.device("cuda:0")
+    _lib.load()
+    Hk, Hv, Dk, Dv = 16, 64, 192, 128
+    esz = 2 if args.dtype == "bf16" else 4
+    torch.zeros(1, device=dev)  # initialise the device before its memory statistics
+    for T in (256, 512, 1024, 2048):
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        d = device_problem(1, T, Hk, Hv, Dk, Dv, dev, args.seed, args.dtype)
+        st = Step(d, args.chunk)
+        f, b = st.time(50, warmup=10)
+        fm, bm = float(np.median(f)), float(np.median(b))
+        sm = float(np.median(f + b))
+        fb, bb = algorithmic_bytes(1, T, Hk, Hv, Dk, Dv, esz, st.nch)
+        elems = T * Hv * Dv * Dk
+        print(json.dumps({"t_sweep": {
+            "T": T, "B": 1, "chunk": args.chunk, "dtype": args.dtype,
+            "fwd_ms_median": fm, "bwd_ms_median": bm, "step_ms_median": sm,
+            "tokens_per_s": T / (sm * 1e-3),
+            "useful_tflops": (FLOPS_FWD + FLOPS_BWD) * elems / (sm * 1e-3) / 1e12,
+            "frac_fp32_peak": (FLOPS_FWD + FLOPS_BWD) * elems / (sm * 1e-3) / 1e12
+                              / FP32_PEAK_TF,
+            "hbm_frac_algorithmic": (fb + bb) / (sm * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            **st.buffer_MB(),
+            "peak_device_memory_MB": torch.cuda.max_memory_allocated(dev) / 1e6}}),
+            flush=True)
+        del st, d
+
+
+def vjp_batch(args):
+    """The focused VJP shape of unsloth-zoo PR #776 (T=64, Hk=Hv=2,
+    Dk=Dv=64, fp32, no mask) at B = 1, 2, 4, 8: median backward ms and
+    median fwd+bwd ms by HIP events over 200 steps."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib
+    dev = torch.device("cuda:0")
+    _lib.load()
+    for B in (1, 2, 4, 8):
+        d = device_problem(B, 64, 2, 2, 64, 64, dev, args.seed, "f32")
+        st = Step(d, 64)
+        f, b = st.time(200, warmup=20)
+        print(json.dumps({"vjp_batch": {
+            "B": B, "T": 64, "Hk": 2, "Hv": 2, "Dk": 64, "Dv": 64, "dtype": "f32",
+            "bwd_ms_median": float(np.median(b)), "bwd_ms_min": float(b.min()),
+            "fwd_bwd_ms_median": float(np.median(f + b))}}), flush=True)
+        del st, d
 
 
 def copy_calibration(mib):
@@ -211,39 +384,29 @@ def copy_calibration(mib):
                                            "dispatches": 2}}), flush=True)
 
 
-def cpu_baseline(T, seed, dtype, budget_s=25.0):
-    """Time the float64 oracle (as it stands, one BLAS thread) on the same
-    workload, one (batch row, kv group) at a time: forward + backward of the
-    group's value heads over the full T.  Groups run until all are done or
-    the time budget is spent; tokens are scaled by the share of groups run."""
-    from threadpoolctl import threadpool_limits
-    import oracle.gdr_oracle as O
+def cpu_baseline(T, seed, dtype, workers=0):
+    """The float64 oracle as it stands, on the host cores: every (batch row,
+    kv group) unit of the workload, forward + backward (oracle.backward runs
+    the forward recurrence and then the reverse sweep), one unit per worker
+    process at a time, one thread each.  Runs before the GPU is touched."""
+    from oracle import pool
     from gated_delta_rule_recurrence_amd import inputs
     p = inputs.qwen35_9b(T, seed=seed, dtype=dtype)
+    cpus, aff = pool.host_cores()
+    workers = workers or min(aff, 16)
+    units = [pool.unit_inputs(p, b, hk) for b in range(p.B) for hk in range(p.Hk)]
+    wall, per_unit = pool.time_units(units, workers)
     rep = p.Hv // p.Hk
-    groups = [(b, hk) for b in range(p.B) for hk in range(p.Hk)]
-    done = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        for b, hk in groups:
-            bs, ks, vs = slice(b, b + 1), slice(hk, hk + 1), slice(hk * rep, (hk + 1) * rep)
-            O.forward(p.q[bs, :, ks], p.k[bs, :, ks], p.v[bs, :, vs], p.g[bs, :, vs],
-                      p.beta[bs, :, vs])
-            O.backward(p.q[bs, :, ks], p.k[bs, :, ks], p.v[bs, :, vs], p.g[bs, :, vs],
-                       p.beta[bs, :, vs], p.dy[bs, :, vs])
-            done += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        dt = time.perf_counter() - t0
-    frac = done / len(groups)
-    return {"value": p.B * T * frac / dt, "unit": "tokens/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"{done} of {len(groups)} (batch row, kv group) units of the same "
-                      f"workload (B={p.B}, T={T}, {rep} value heads each), forward + "
-                      f"backward in {dt:.1f} s on 1 thread; tokens scaled by "
-                      f"{done}/{len(groups)}"}
+    return {"value": p.B * T / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"all {len(units)} (batch row, kv group) units of the workload (B={p.B}, "
+                      f"T={T}, {rep} value heads each), forward + backward, on {workers} "
+                      f"worker processes of one thread: {wall:.1f} s wall, "
+                      f"{sum(per_unit):.1f} s of CPU work",
+            "os_cpu_count": cpus, "affinity_cpus": aff, "workers": workers,
+            "single_core_tokens_per_s": p.B * T / sum(per_unit)}
 
 
+# ------------------------------------------------------------- main step --
 def main():
     args = parse()
     if args.gpus != 1:
@@ -260,41 +423,36 @@ def main():
     if args.chunk_sweep:
         chunk_sweep(args)
         return
-    import torch
-    from gated_delta_rule_recurrence_amd import _lib, inputs, ops
+    if args.t_sweep:
+        t_sweep(args)
+        return
+    if args.vjp_batch:
+        vjp_batch(args)
+        return
 
+    # the CPU baseline first: its worker processes start before this process
+    # touches the GPU
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args.T, args.seed, args.dtype, args.cpu_workers)
+
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
     _lib.load()  # fail loudly if the HIP library is missing
 
+    from gated_delta_rule_recurrence_amd import inputs
     p = inputs.qwen35_9b(args.T, seed=args.seed, dtype=args.dtype, B=args.B)
     dt = torch.bfloat16 if args.dtype == "bf16" else torch.float32
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev).to(dt)
-    q, k, v, g, beta, dy = (t(getattr(p, n)) for n in ("q", "k", "v", "g", "beta", "dy"))
+    d = {n: t(getattr(p, n)) for n in ("q", "k", "v", "g", "beta", "dy")}
     B, T, Hk, Hv, Dk, Dv = p.B, p.T, p.Hk, p.Hv, p.Dk, p.Dv
-
-    # every buffer allocated up front
-    shape = ops.shape_of(q, v, args.chunk, dt)
-    ckpt = torch.empty(_lib.checkpoint_bytes(shape), dtype=torch.uint8, device=dev)
-    ws = torch.empty(_lib.backward_workspace_bytes(shape), dtype=torch.uint8, device=dev)
-    fws = torch.empty(max(_lib.forward_workspace_bytes(shape), 1), dtype=torch.uint8,
-                      device=dev)
-    y = torch.empty_like(v)
-    S_T = torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev)
-    outs = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v),
-            torch.empty_like(g), torch.empty_like(beta),
-            torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev))
-    saved = ops.Saved(ckpt, args.chunk)
-    stream = torch.cuda.current_stream(dev)
-
-    def fwd():
-        ops.gdr_forward(q, k, v, g, beta, None, chunk=args.chunk, y=y, S_T=S_T,
-                        ckpt=ckpt, workspace=fws)
-
-    def bwd():
-        ops.gdr_backward(q, k, g, beta, saved, dy, None, workspace=ws, out=outs)
+    st = Step(d, args.chunk)   # every buffer allocated up front
+    stream = st.stream
+    fwd, bwd = st.fwd, st.bwd
 
     for _ in range(args.warmup):
         fwd()
@@ -332,6 +490,7 @@ def main():
     flushed_ms = np.array([e[0].elapsed_time(e[1]) for e in evf])
     del flush
     peak_mb = torch.cuda.max_memory_allocated(dev) / 1e6
+    copy_gbs = copy_bandwidth(dev)
     ms = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms / 1e3)
@@ -343,24 +502,20 @@ def main():
     # the bf16-product sweep kernels take bf16 inputs with Dk % 8 == 0 and Dv % 4 == 0
     sfx = "_bf16" if (args.dtype == "bf16" and Dk % 8 == 0 and Dv % 4 == 0) else ""
     all_tf = (FLOPS_FWD + FLOPS_BWD) * elems / (ms * 1e-3) / 1e12
-    # algorithmic HBM bytes, each tensor touched once: the forward reads q, k,
-    # v, g, beta and writes y, the residual rows e (fp32), the chunk
-    # checkpoints and S_T; the backward reads q, k, g, beta, dy, e and the
-    # checkpoints and writes dq, dk, dv, dg, dbeta and dS0
     esz = 2 if args.dtype == "bf16" else 4
-    nch = -(-T // args.chunk)
-    tok_in = B * T * (2 * Hk * Dk + Hv * Dv + 2 * Hv) * esz   # q, k, (v | dy), g, beta
-    rows32 = B * T * Hv * Dv * 4
-    state = B * Hv * Dv * Dk * 4
-    fwd_bytes = tok_in + B * T * Hv * Dv * esz + rows32 + (nch + 1) * state
-    bwd_bytes = tok_in + rows32 + nch * state + tok_in + state
-    traffic = None
-    default_workload = (args.T, args.B, args.chunk, args.dtype) == (2048, 1, 64, "bf16")
-    if default_workload and sources_digest(BWD_SOURCES) == BWD_TRAFFIC["sources_sha256_16"]:
-        traffic = BWD_TRAFFIC["read_bytes"] + BWD_TRAFFIC["write_bytes"]
+    fwd_bytes, bwd_bytes = algorithmic_bytes(B, T, Hk, Hv, Dk, Dv, esz, st.nch)
+    fwd_mid, bwd_mid = intermediate_bytes(B, T, Hv, Dv, Dk, st.nch, st.chunked)
 
-    ckpt_mb = ckpt.numel() / 1e6
-    ws_mb = ws.numel() / 1e6
+    default_workload = (args.T, args.B, args.chunk, args.dtype) == (2048, 1, 64, "bf16")
+    prof_ok = (default_workload and PROFILE["sources_sha256_16"] is not None
+               and sources_digest() == PROFILE["sources_sha256_16"])
+    traffic = fwd_traffic = None
+    counters = None
+    if prof_ok:
+        traffic = PROFILE["bwd_read_bytes"] + PROFILE["bwd_write_bytes"]
+        fwd_traffic = PROFILE["fwd_read_bytes"] + PROFILE["fwd_write_bytes"]
+        counters = PROFILE["kernels"]
+
     rec = {
         "metric": "fwd+bwd tokens/s, Qwen3.5-9B gated-delta shape T=2048",
         "value": value,
@@ -378,24 +533,35 @@ def main():
                                f"B={B} T={T} Hk={Hk} Hv={Hv} Dk={Dk} Dv={Dv}, "
                                f"{args.dtype} inputs, fp32 state, chunk={args.chunk}",
                    "global_batch": B, "seq_len": T, "parallelism": "none (1 GPU)"},
-        # the dominant call: gdr_backward (about 0.55 of 0.78 ms), timed with
-        # HIP events on the library's stream; its products deliver fp32
-        # accuracy (fp32 MFMA, or bf16 MFMA on three-piece splits), so the
-        # fp32 peak is the bar
+        # the dominant call, gdr_backward, timed with HIP events on the
+        # library's stream.  Its products deliver fp32 accuracy (fp32 MFMA,
+        # or bf16 MFMA on exact three-piece splits), so the work is priced as
+        # fp32: `achieved` counts the recurrence's useful fp32-equivalent
+        # flops (15 per state element per step), not the issued piece
+        # products.
         "roofline": {"bound": "mfma", "kernel": f"gdr_backward (prep_kernel<bwd>, "
                      f"bwd_chunked{sfx}_kernel, chunk_kernel)",
                      "achieved": bwd_tf, "peak": FP32_PEAK_TF,
                      "unit": "TFLOP/s", "frac": bwd_tf / FP32_PEAK_TF,
+                     "flops_basis": "useful fp32-equivalent, 15*B*T*Hv*Dv*Dk per call",
                      "traffic": traffic,
+                     "traffic_source": PROFILE["source"] if prof_ok else None,
                      "flops_per_launch": bwd_flops,
                      "algorithmic_bytes_per_launch": bwd_bytes,
+                     "intermediate_bytes_per_launch": bwd_mid,
                      "hbm_frac_algorithmic": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "hbm_frac_counters": (traffic / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+                                           if traffic else None),
                      "avg_launch_ms": bwd_ms},
         "forward": {"kernel": f"gdr_forward (prep_kernel<fwd>, fwd_chunked{sfx}_kernel)",
                     "achieved_tflops": fwd_tf, "frac": fwd_tf / FP32_PEAK_TF,
                     "flops_per_launch": fwd_flops, "algorithmic_bytes_per_launch": fwd_bytes,
+                    "intermediate_bytes_per_launch": fwd_mid,
+                    "traffic": fwd_traffic,
                     "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "avg_launch_ms": fwd_ms},
+        "counters": counters,
+        "achievable_hbm_GBps": copy_gbs,
         "timing": {"wall_ms_per_step": ms, "step_ms_median": float(np.median(step_ms)),
                    "step_ms_min": float(step_ms.min()),
                    "flushed_step_ms_median": float(np.median(flushed_ms)),
@@ -404,10 +570,10 @@ def main():
         "breakdown": {"fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
                       "useful_tflops_whole_step": all_tf,
                       "frac_whole_step_vs_fp32_peak": all_tf / FP32_PEAK_TF,
-                      "checkpoint_MB": ckpt_mb, "workspace_MB": ws_mb},
+                      **st.buffer_MB()},
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(min(args.cpu_sample_T, T), args.seed, args.dtype)
+    if cpu is not None:
+        rec["cpu_baseline"] = cpu
     print(json.dumps(rec), flush=True)
 
 
