@@ -90,7 +90,7 @@ def parse():
                     help="time fwd+bwd at the long-context shape (B=4, T=8192, "
                          "Qwen3.5-9B heads, trainable S0) for a range of checkpoint "
                          "intervals, one JSON line each, and exit")
-    ap.add_argument("--chunks", default="16,32,64",
+    ap.add_argument("--chunks", default="16,32,64,128,256,512",
                     help="checkpoint intervals of --chunk-sweep")
     ap.add_argument("--t-sweep", action="store_true",
                     help="time fwd+bwd at the Qwen3.5-9B heads for T = 256, 512, 1024, "
@@ -154,7 +154,7 @@ class Step:
                      torch.empty_like(d["g"]), torch.empty_like(d["beta"]),
                      torch.empty((B, Hv, Dv, Dk), dtype=torch.float32, device=dev))
         self.dST = (torch.randn((B, Hv, Dv, Dk), device=dev) if with_dST else None)
-        self.saved = ops.Saved(self.ckpt, chunk)
+        self.saved = ops.Saved(self.ckpt, chunk, v=v if chunk > 64 else None)
         self.chunk = chunk
         self.nch = _lib.num_chunks(self.shape)
         self.stream = torch.cuda.current_stream(dev)

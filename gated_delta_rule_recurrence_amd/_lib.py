@@ -44,7 +44,7 @@ _SIGNATURES = {
     "gdr_forward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 11
                     + [ctypes.c_size_t, _vp]),
     "gdr_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 11),
-    "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 15
+    "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 16
                      + [ctypes.c_size_t, _vp]),
     "gdr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gdr_version": (ctypes.c_char_p, []),
@@ -141,9 +141,10 @@ GDR_ERR_SCRATCH_LIMIT = -12
 
 
 def backward_raw(shape, q, k, g, beta, ckpt, dy, dS_T, dq, dk, dv, dg, dbeta,
-                 dS0, workspace, workspace_bytes, stream, mask=0) -> int:
-    """gdr_backward with integer device addresses (0 = NULL); returns the status."""
-    ptrs = [_vp(x or None) for x in (q, k, g, beta, mask, ckpt, dy, dS_T, dq, dk, dv,
+                 dS0, workspace, workspace_bytes, stream, mask=0, v=0) -> int:
+    """gdr_backward with integer device addresses (0 = NULL); returns the
+    status.  v is read only for chunk > 64."""
+    ptrs = [_vp(x or None) for x in (q, k, v, g, beta, mask, ckpt, dy, dS_T, dq, dk, dv,
                                      dg, dbeta, dS0, workspace)]
     return load().gdr_backward(ctypes.byref(shape), *ptrs,
                                ctypes.c_size_t(int(workspace_bytes)),

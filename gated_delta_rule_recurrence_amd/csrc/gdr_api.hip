@@ -13,7 +13,8 @@
 namespace {
 
 constexpr int64_t kMaxDim = 256;      // Dk, Dv
-constexpr int64_t kMaxChunk = 64;     // chunk length C
+constexpr int64_t kMaxTile = 64;      // steps of one tile of the kernels
+constexpr int64_t kMaxChunk = INT64_C(1) << 30;  // checkpoint interval C
 constexpr int64_t kMaxGrid = 65535;   // B and Hv index grid y/z
 constexpr int64_t kMaxIndex = INT64_C(1) << 62;
 
@@ -26,14 +27,40 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 
 int64_t round_up256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
+// a + b on byte counts already bounded by kMaxIndex
+bool add_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a > kMaxIndex - b) return false;
+  *out = a + b;
+  return true;
+}
+
+// The kernels' tile: C itself up to 64 steps, else the largest divisor of C
+// that is at most 64 (64 for a multiple of 64), so that tiles never straddle
+// a checkpoint.
+int64_t tile_of(int64_t C) {
+  if (C <= kMaxTile) return C;
+  for (int64_t d = kMaxTile; d > 1; --d)
+    if (C % d == 0) return d;
+  return 1;
+}
+
 struct Sizes {
-  int64_t nch;
-  int64_t state;     // elements of one [B][Hv][Dv][Dk] tensor
-  int64_t ckpt;      // elements of [B][Hv][nch][Dv][Dk]
-  int64_t rows;      // elements of one [B][T][Hv][Dv] tensor
+  int64_t L;       // tile length
+  int64_t m;       // tiles per checkpoint interval (C = m L)
+  int64_t ntiles;  // ceil(T / L)
+  int64_t nseg;    // saved states: ceil(T / C)
+  bool chunked;    // the chunked sweeps take tiles of L steps
+  bool replay;     // C > 64: the backward replays the tiles from the saved states
+  int64_t state;   // elements of one [B][Hv][Dv][Dk] tensor
+  int64_t rows;    // elements of one [B][T][Hv][Dv] tensor
   int64_t ckpt_bytes, ws_bytes, fws_bytes;
-  int64_t e_off, c_off;  // byte offsets of the per-step vectors
-  int64_t p_off;         // byte offset of the backward prep records (or 0)
+  int64_t e_off;   // save buffer: the residuals (C <= 64)
+  // backward workspace: state-gradient tiles at 0, then
+  int64_t c_off;   // the per-step vectors c
+  int64_t p_off;   // the reverse prep records (chunked; else 0)
+  int64_t rs_off;  // replay: the tile states
+  int64_t re_off;  // replay: the residuals
+  int64_t rp_off;  // replay: the forward prep records (chunked; else 0)
 };
 
 int check_shape(const gdr_shape* s, Sizes* z) {
@@ -51,33 +78,50 @@ int check_shape(const gdr_shape* s, Sizes* z) {
   if (s->T > INT32_MAX / 2) return GDR_ERR_OVERFLOW;
 
   Sizes r{};
-  r.nch = (s->T + s->chunk - 1) / s->chunk;
-  int64_t bh, mat, x;
+  r.L = tile_of(s->chunk);
+  r.m = s->chunk / r.L;
+  r.ntiles = (s->T + r.L - 1) / r.L;
+  r.nseg = (s->T + s->chunk - 1) / s->chunk;
+  r.replay = s->chunk > kMaxTile;
+  r.chunked = gdr::chunked_sweep_ok(s->Hk, s->Hv, s->Dk, s->Dv, r.L, s->T);
+  int64_t bh, mat, x, tiles, b_tiles, b_rows, b_seg;
   if (!mul_ok(s->B, s->Hv, &bh) || !mul_ok(s->Dv, s->Dk, &mat) ||
-      !mul_ok(bh, mat, &r.state) || !mul_ok(r.state, r.nch, &r.ckpt) ||
+      !mul_ok(bh, mat, &r.state) || !mul_ok(r.state, r.ntiles, &tiles) ||
       !mul_ok(s->B, s->T, &x) || !mul_ok(x, s->Hv, &x) ||
-      !mul_ok(x, s->Dv, &r.rows))
+      !mul_ok(x, s->Dv, &r.rows) || !mul_ok(tiles, 4, &b_tiles) ||
+      !mul_ok(r.rows, 4, &b_rows) || !mul_ok(r.state * 4, r.nseg, &b_seg))
     return GDR_ERR_OVERFLOW;
-  int64_t b1, b2;
-  if (!mul_ok(r.ckpt, 4, &b1) || !mul_ok(r.rows, 4, &b2)) return GDR_ERR_OVERFLOW;
-  r.e_off = round_up256(b1);
-  r.c_off = r.e_off;
-  if (r.e_off > kMaxIndex - b2) return GDR_ERR_OVERFLOW;
-  r.ckpt_bytes = r.e_off + b2;
-  r.ws_bytes = r.c_off + b2;
-  r.fws_bytes = 0;
-  r.p_off = 0;
-  if (gdr::chunked_sweep_ok(s->Hk, s->Hv, s->Dk, s->Dv, s->chunk, s->T)) {
-    // the chunked sweeps' prep records: the forward's whole workspace, and
-    // a region after the backward's per-step vectors
-    int64_t f;
-    if (!mul_ok(gdr::chunked_prep_floats(1, 1, r.nch), bh, &f) ||
-        !mul_ok(f, 4, &r.fws_bytes))
-      return GDR_ERR_OVERFLOW;
-    r.p_off = round_up256(r.ws_bytes);
-    if (r.p_off > kMaxIndex - r.fws_bytes) return GDR_ERR_OVERFLOW;
-    r.ws_bytes = r.p_off + r.fws_bytes;
+  int64_t prep = 0;
+  if (r.chunked && (!mul_ok(gdr::chunked_prep_floats(1, 1, r.ntiles), bh, &prep) ||
+                    !mul_ok(prep, 4, &prep)))
+    return GDR_ERR_OVERFLOW;
+  // save buffer: a state every C steps, and (C <= 64) the residuals
+  if (r.replay) {
+    r.ckpt_bytes = b_seg;
+  } else {
+    r.e_off = round_up256(b_tiles);
+    if (!add_ok(r.e_off, b_rows, &r.ckpt_bytes)) return GDR_ERR_OVERFLOW;
   }
+  r.fws_bytes = prep;
+  // backward workspace
+  int64_t end;
+  r.c_off = round_up256(b_tiles);
+  if (!add_ok(r.c_off, b_rows, &end)) return GDR_ERR_OVERFLOW;
+  if (r.chunked) {
+    r.p_off = round_up256(end);
+    if (!add_ok(r.p_off, prep, &end)) return GDR_ERR_OVERFLOW;
+  }
+  if (r.replay) {
+    r.rs_off = round_up256(end);
+    if (!add_ok(r.rs_off, b_tiles, &end)) return GDR_ERR_OVERFLOW;
+    r.re_off = round_up256(end);
+    if (!add_ok(r.re_off, b_rows, &end)) return GDR_ERR_OVERFLOW;
+    if (r.chunked) {
+      r.rp_off = round_up256(end);
+      if (!add_ok(r.rp_off, prep, &end)) return GDR_ERR_OVERFLOW;
+    }
+  }
+  r.ws_bytes = end;
   // element counts must also index as int64 inside the kernels
   int64_t qk;
   if (!mul_ok(s->B, s->T, &qk) || !mul_ok(qk, s->Hk, &qk) ||
@@ -157,8 +201,22 @@ int forward_checked(const gdr_shape* shape, const Sizes& z, const void* q, const
   a.Hv = (int)shape->Hv;
   a.Dk = (int)shape->Dk;
   a.Dv = (int)shape->Dv;
-  a.L = (int)shape->chunk;
-  a.nch = (int)z.nch;
+  const bool decode = has_tokens && gdr::decode_ok(shape->T);
+  const bool chunked = has_tokens && !decode && z.chunked;
+  if (chunked) {
+    // tiles of L steps, a saved state every m tiles
+    a.L = (int)z.L;
+    a.nch = (int)z.ntiles;
+    a.ck_every = (int)z.m;
+  } else {
+    // the per-step kernels save a state every C steps
+    a.L = (int)shape->chunk;
+    a.nch = (int)z.nseg;
+    a.ck_every = 1;
+  }
+  a.nslot = (int)z.nseg;
+  a.s0_stride = 1;
+  a.seg = 0;
   a.log_g = shape->decay == GDR_DECAY_LOG;
   a.q = q;
   a.k = k;
@@ -171,15 +229,16 @@ int forward_checked(const gdr_shape* shape, const Sizes& z, const void* q, const
   a.ST = S_T;
   if (ckpt != nullptr) {
     a.Sck = static_cast<float*>(ckpt);
-    a.E = reinterpret_cast<float*>(static_cast<char*>(ckpt) + z.e_off);
+    // C > 64 saves no residuals: the backward replays them
+    if (!z.replay) a.E = reinterpret_cast<float*>(static_cast<char*>(ckpt) + z.e_off);
   }
   if (!has_tokens && S_T == nullptr) return GDR_OK;
   const bool bf16 = shape->dtype == GDR_BF16;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err;
-  if (has_tokens && gdr::decode_ok(shape->T)) {
+  if (decode) {
     err = gdr::launch_decode(a, bf16, s);
-  } else if (has_tokens && z.fws_bytes > 0) {
+  } else if (chunked) {
     gdr::FwdChunkedArgs c{};
     c.s = a;
     c.prep = static_cast<float*>(workspace);
@@ -199,7 +258,7 @@ int gdr_num_chunks(const gdr_shape* shape, int64_t* out) {
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
   if (out == nullptr) return GDR_ERR_NULL_ARG;
-  *out = z.nch;
+  *out = z.nseg;
   return GDR_OK;
 }
 
@@ -262,7 +321,7 @@ int gdr_forward_noalloc(const gdr_shape* shape, const void* q, const void* k,
 }
 
 int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
-                 const void* g, const void* beta, const uint8_t* mask,
+                 const void* v, const void* g, const void* beta, const uint8_t* mask,
                  const void* ckpt,
                  const void* dy, const float* dS_T, void* dq, void* dk,
                  void* dv, void* dg, void* dbeta, float* dS0,
@@ -272,10 +331,10 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   if (st != GDR_OK) return st;
   const bool has_tokens = shape->B > 0 && shape->T > 0;
   if (has_tokens && (!q || !k || !g || !beta || !ckpt || !dy || !dq || !dk ||
-                     !dv || !dg || !dbeta || !workspace))
+                     !dv || !dg || !dbeta || !workspace || (z.replay && !v)))
     return GDR_ERR_NULL_ARG;
-  const void* ptrs[] = {q,  k,  g,  beta,  ckpt, dy,       dS_T, dq,
-                        dk, dv, dg, dbeta, dS0,  workspace};
+  const void* ptrs[] = {q,  k,  v,  g,     beta, ckpt, dy,       dS_T,
+                        dq, dk, dv, dg,    dbeta, dS0, workspace};
   for (const void* p : ptrs)
     if (p != nullptr && !aligned16(p)) return GDR_ERR_ALIGNMENT;
   if (has_tokens && workspace_bytes < static_cast<size_t>(z.ws_bytes))
@@ -285,6 +344,54 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
 
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = shape->dtype == GDR_BF16;
+  char* const ws = static_cast<char*>(workspace);
+  hipError_t err;
+
+  // the state before every tile and the residuals: saved by the forward
+  // (C <= 64), or replayed here from the states it saved every C steps
+  const float* Sck = static_cast<const float*>(ckpt);
+  const float* E =
+      reinterpret_cast<const float*>(static_cast<const char*>(ckpt) + z.e_off);
+  if (has_tokens && z.replay) {
+    gdr::FwdSweepArgs r{};
+    r.B = (int)shape->B;
+    r.T = (int)shape->T;
+    r.Hk = (int)shape->Hk;
+    r.Hv = (int)shape->Hv;
+    r.Dk = (int)shape->Dk;
+    r.Dv = (int)shape->Dv;
+    r.L = (int)z.L;
+    r.nch = (int)z.ntiles;
+    r.ck_every = 1;
+    r.nslot = (int)z.ntiles;
+    r.s0_stride = (int)z.nseg;  // slot s of each (batch row, value head)
+    r.log_g = shape->decay == GDR_DECAY_LOG;
+    r.mask = mask;
+    r.q = q;
+    r.k = k;
+    r.v = v;
+    r.g = g;
+    r.beta = beta;
+    r.S0 = static_cast<const float*>(ckpt);
+    r.y = nullptr;
+    r.ST = nullptr;
+    r.Sck = reinterpret_cast<float*>(ws + z.rs_off);
+    r.E = reinterpret_cast<float*>(ws + z.re_off);
+    if (z.chunked) {
+      // one workgroup row per saved state, when the grid takes them
+      r.seg = shape->B * z.nseg <= kMaxGrid ? (int)z.m : 0;
+      gdr::FwdChunkedArgs fc{};
+      fc.s = r;
+      fc.prep = reinterpret_cast<float*>(ws + z.rp_off);
+      err = gdr::launch_fwd_chunked(fc, bf16, s);
+    } else {
+      r.seg = 0;
+      err = gdr::launch_fwd_sweep(r, bf16, s);
+    }
+    if (err != hipSuccess) return GDR_ERR_HIP;
+    Sck = r.Sck;
+    E = r.E;
+  }
 
   gdr::BwdSweepArgs b{};
   b.B = (int)shape->B;
@@ -293,8 +400,8 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   b.Hv = (int)shape->Hv;
   b.Dk = (int)shape->Dk;
   b.Dv = (int)shape->Dv;
-  b.L = (int)shape->chunk;
-  b.nch = (int)z.nch;
+  b.L = (int)z.L;
+  b.nch = (int)z.ntiles;
   b.log_g = shape->decay == GDR_DECAY_LOG;
   b.q = q;
   b.k = k;
@@ -306,14 +413,13 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   b.dv = dv;
   b.dS0 = dS0;
   if (has_tokens) {
-    b.Hck = static_cast<float*>(workspace);
-    b.C = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.c_off);
+    b.Hck = reinterpret_cast<float*>(ws);
+    b.C = reinterpret_cast<float*>(ws + z.c_off);
   }
-  hipError_t err;
-  if (has_tokens && z.p_off > 0) {
+  if (has_tokens && z.chunked) {
     gdr::BwdChunkedArgs c{};
     c.s = b;
-    c.prep = reinterpret_cast<float*>(static_cast<char*>(workspace) + z.p_off);
+    c.prep = reinterpret_cast<float*>(ws + z.p_off);
     err = gdr::launch_bwd_chunked(c, bf16, s);
   } else {
     err = gdr::launch_bwd_sweep(b, bf16, s);
@@ -337,9 +443,8 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   c.beta = beta;
   c.dy = dy;
   c.mask = mask;
-  c.Sck = static_cast<const float*>(ckpt);
-  c.E = reinterpret_cast<const float*>(static_cast<const char*>(ckpt) +
-                                       z.e_off);
+  c.Sck = Sck;
+  c.E = E;
   c.Hck = b.Hck;
   c.C = b.C;
   c.dq = dq;
@@ -357,7 +462,7 @@ const char* gdr_strerror(int status) {
     case GDR_ERR_BAD_SHAPE: return "B and T must be >= 0 and Hk, Hv, Dk, Dv >= 1";
     case GDR_ERR_HEAD_RATIO: return "Hv must be a multiple of Hk";
     case GDR_ERR_UNSUPPORTED_DIM: return "Dk and Dv must be <= 256, B and Hv <= 65535";
-    case GDR_ERR_BAD_CHUNK: return "chunk must be in [1, 64]";
+    case GDR_ERR_BAD_CHUNK: return "chunk must be in [1, 2^30]";
     case GDR_ERR_BAD_DTYPE: return "dtype must be GDR_F32 or GDR_BF16";
     case GDR_ERR_OVERFLOW: return "a tensor size overflows 64-bit indexing";
     case GDR_ERR_WORKSPACE: return "workspace is smaller than the size query returns";
@@ -370,7 +475,7 @@ const char* gdr_strerror(int status) {
   return "unknown gdr status";
 }
 
-const char* gdr_version(void) { return "0.5.0"; }
+const char* gdr_version(void) { return "0.6.0"; }
 
 }  // extern "C"
 

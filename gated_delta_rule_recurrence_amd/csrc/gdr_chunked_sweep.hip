@@ -578,6 +578,33 @@ __device__ __forceinline__ SweepBlock sweep_block() {
   return SweepBlock{id % nx, (id / nx) % ny, id / (nx * ny)};
 }
 
+// The tiles a forward workgroup runs, from the batch index of its grid slot:
+// every tile from S0 normally; with a.seg > 0 (a replay from the save
+// buffer) segment s of batch row b, tiles s * seg .. from slot s.  s0 is the
+// (batch row, value head, slot) index of the starting state in units of one
+// [Dv][Dk] matrix, before the value head is added (see FwdSweepArgs).
+struct TileRange {
+  int b, c0, c1;
+  int64_t s0;
+};
+__device__ __forceinline__ TileRange tile_range(const FwdSweepArgs& a, int z, int h) {
+  TileRange r{z, 0, a.nch, 0};
+  int s = 0;
+  if (a.seg > 0) {
+    const int nseg = (a.nch + a.seg - 1) / a.seg;
+    r.b = z / nseg;
+    s = z - r.b * nseg;
+    r.c0 = s * a.seg;
+    r.c1 = min(r.c0 + a.seg, a.nch);
+  }
+  r.s0 = ((int64_t)r.b * a.Hv + h) * a.s0_stride + s;
+  return r;
+}
+// Save-buffer slot of the state before tile c, or -1 if it is not saved.
+__device__ __forceinline__ int ckpt_slot(const FwdSweepArgs& a, int c) {
+  return c % a.ck_every == 0 ? c / a.ck_every : -1;
+}
+
 // The k, q rows of a chunk: fetched into registers a chunk ahead (raw bits,
 // masked where deposited), then deposited into the natural-layout LDS stages
 // [kN][KLD] with zero padding columns.
@@ -754,7 +781,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
   TIn* __restrict__ y = static_cast<TIn*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
   const SweepBlock wb = sweep_block();
-  const int i0 = wb.x * kDS, h = wb.h, b = wb.b;
+  const TileRange tr = tile_range(a, wb.b, wb.h);
+  const int i0 = wb.x * kDS, h = wb.h, b = tr.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -781,13 +809,13 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
     for (int u = 0; u < 4; ++u) {
       const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
       const bool ok = a.S0 != nullptr && i0 + i < Dv && j < Dk;
-      Sacc[nj][u] = ok ? a.S0[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
+      Sacc[nj][u] = ok ? a.S0[ok ? tr.s0 * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
     }
   tiles_to_lds<JW>(sm + L::SK, Sacc, mt, jg, lq, lr);
-  kq.fetch(k, q, kq_base(0), min(a.L, T), kst, Dk);
+  kq.fetch(k, q, kq_base(tr.c0), min(a.L, T - tr.c0 * a.L), kst, Dk);
 
   // v, y of this wave's tile: step tw + 4 lq + u, row i0 + 16 nt + lr
-  for (int c = 0; c < a.nch; ++c) {
+  for (int c = tr.c0; c < tr.c1; ++c) {
     // lane indices re-derived in each chunk from an opaque copy of the
     // thread id: the compiler then recomputes the cheap per-lane addresses
     // instead of holding dozens of them in registers across the loop
@@ -823,13 +851,14 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
       vm |= (uint32_t)ok << u;
     }
     {  // unconditional (a branch around loads makes every later wait a full one)
-      const int cn = min(c + 1, a.nch - 1);
+      const int cn = min(c + 1, tr.c1 - 1);
       kq.fetch(k, q, kq_base(cn), min(a.L, T - cn * a.L), kst, Dk);
     }
     __syncthreads();
-    // checkpoint S_{c C}: the state before this chunk, from its LDS copy
-    if (a.Sck != nullptr)
-      lds_to_matrix<JT, VEC>(sm + L::SK, a.Sck + (bh * a.nch + c) * mat, i0, Dv, Dk, tid);
+    // checkpoint: the state before this chunk, from its LDS copy
+    const int slot = ckpt_slot(a, c);
+    if (a.Sck != nullptr && slot >= 0)
+      lds_to_matrix<JT, VEC>(sm + L::SK, a.Sck + (bh * a.nslot + slot) * mat, i0, Dv, Dk, tid);
 
     // X = [K; Q] S0^T on this wave's tile
     f4 X[2][1];
@@ -875,7 +904,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_kernel(FwdChunkedAr
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int t = tw + 4 * lq + u;
-        if (iok && t < n) st(y, vbase + t * vst + ti, Yv[u]);
+        if (y != nullptr && iok && t < n) st(y, vbase + t * vst + ti, Yv[u]);
       }
     }
 
@@ -1046,7 +1075,8 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   bf16* __restrict__ y = static_cast<bf16*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
   const SweepBlock wb = sweep_block();
-  const int i0 = wb.x * kDS, h = wb.h, b = wb.b;
+  const TileRange tr = tile_range(a, wb.b, wb.h);
+  const int i0 = wb.x * kDS, h = wb.h, b = tr.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1099,16 +1129,16 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       for (int u = 0; u < 4; ++u) {
         const int i = 16 * mt + 4 * lq + u, j = 16 * (jg + nj) + lr;
         const bool ok = a.S0 != nullptr && i0 + i < Dv && j < Dk;
-        Sacc[nj][u] = ok ? a.S0[ok ? bh * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
+        Sacc[nj][u] = ok ? a.S0[ok ? tr.s0 * mat + (int64_t)(i0 + i) * Dk + j : 0] : 0.f;
       }
-    kq.fetch(k, q, kq_base(0), chunk_len(0), kst, Dk);
-    fetch_in(0, l, nx);
+    kq.fetch(k, q, kq_base(tr.c0), chunk_len(tr.c0), kst, Dk);
+    fetch_in(tr.c0, l, nx);
   }
   // the state tiles into the three j-major bf16 pieces (and checkpoint
   // `slot`, or the sink when slot < 0; out-of-range lanes store to the sink
   // too)
   auto put_state = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
-    float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nch + (slot >= 0 ? slot : 0)) * mat : nullptr;
+    float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nslot + (slot >= 0 ? slot : 0)) * mat : nullptr;
     asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) {
@@ -1135,9 +1165,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_state(0, tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
+    put_state(ckpt_slot(a, tr.c0), tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
   }
-  for (int c = 0; c < a.nch; ++c) {
+  for (int c = tr.c0; c < tr.c1; ++c) {
     int tl = tid;
     asm volatile("" : "+v"(tl));
     kq.tid = tl;
@@ -1159,7 +1189,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
     // the next chunk's loads: waves 0-3 here, waves 4-7 (the other wave of
     // each SIMD) after X, so that one wave's MFMAs run while the other
     // issues
-    const int cn = min(c + 1, a.nch - 1);
+    const int cn = min(c + 1, tr.c1 - 1);
     if (w < 4) {
       kq.fetch(k, q, kq_base(cn), chunk_len(cn), kst, Dk);
       fetch_in(cn, l, nx);
@@ -1237,7 +1267,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         // by the reverse pass: non-temporal)
         const f4 er = quad_transpose(E, lr);
         const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
-        const bool ok = t < n && i0 + r4 < Dv;
+        const bool ok = a.E != nullptr && t < n && i0 + r4 < Dv;
         __builtin_nontemporal_store(
             er, reinterpret_cast<f4*>(ok ? a.E + vbase + (int64_t)t * vst + r4 : sink16));
       }
@@ -1256,7 +1286,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         // as E: one 8-byte store of four bf16 rows per lane
         const f4 yr = quad_transpose(Yv, lr);
         const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
-        const bool ok = t < n && i0 + r4 < Dv;
+        const bool ok = y != nullptr && t < n && i0 + r4 < Dv;
         const uint2 yb = {cvt_pk_bf16(yr[0], yr[1]), cvt_pk_bf16(yr[2], yr[3])};
         *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(y + vbase + (int64_t)t * vst + r4)
                                      : reinterpret_cast<uint2*>(sink16)) = yb;
@@ -1282,7 +1312,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       }
     }
     __syncthreads();  // stage reads done before it is rewritten
-    put_state(c + 1 < a.nch ? c + 1 : -1, lr, lq, sink16);
+    put_state(c + 1 < tr.c1 ? ckpt_slot(a, c + 1) : -1, lr, lq, sink16);
   }
   if (a.ST != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1869,7 +1899,9 @@ template <typename TIn>
 hipError_t fwd_go(const FwdChunkedArgs& A, hipStream_t s) {
   const hipError_t e = launch_prep<TIn, false>(shape_of(A.s), A.prep, s);
   if (e != hipSuccess) return e;
-  return launch_sweep<TIn, false>(A, A.s.Dk, A.s.Dv, A.s.Hv, A.s.B, s);
+  // a segment replay runs every (batch row, segment) pair side by side
+  const int zb = A.s.seg > 0 ? A.s.B * ((A.s.nch + A.s.seg - 1) / A.s.seg) : A.s.B;
+  return launch_sweep<TIn, false>(A, A.s.Dk, A.s.Dv, A.s.Hv, zb, s);
 }
 
 template <typename TIn>

@@ -7,8 +7,18 @@
 namespace gdr {
 
 // Forward sweep: state recurrence with save.
+//
+// Time runs in tiles of L steps (nch tiles).  The state before tile c is
+// saved to slot c / ck_every of Sck when c % ck_every == 0 (Sck holds nslot
+// slots per (batch row, value head)).  The state before the first tile is
+// S0 + (bh * s0_stride + s) * Dv * Dk: s0_stride = 1 for a [B][Hv][Dv][Dk]
+// S0, and the save buffer's slot count when the forward replays from it.
+// seg > 0 (chunked forward only) replays segment by segment: the grid's
+// batch dimension is B * ceil(nch / seg), and segment s runs tiles
+// s * seg .. from slot s of S0.
 struct FwdSweepArgs {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
+  int ck_every, nslot, s0_stride, seg;
   int log_g;  // g holds log of the decay
   const uint8_t* mask;  // [B][T], 0 = identity step; may be null
   const void* q;
@@ -17,10 +27,10 @@ struct FwdSweepArgs {
   const void* g;
   const void* beta;
   const float* S0;  // may be null (zeros)
-  void* y;
+  void* y;     // may be null (a replay writes no outputs)
   float* ST;   // may be null
-  float* Sck;  // [B][Hv][nch][Dv][Dk] or null (inference)
-  float* E;    // [B][T][Hv][Dv] or null (inference)
+  float* Sck;  // [B][Hv][nslot][Dv][Dk] or null (inference)
+  float* E;    // [B][T][Hv][Dv] or null (inference, or C > 64)
 };
 
 // Reverse sweep of the state gradient.

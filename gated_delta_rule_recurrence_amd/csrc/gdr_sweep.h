@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
   // S = sig * St
   float St[R][NC];
   float sig = 1.f;
-  tile_load<NC, R>(St, a.S0 ? a.S0 + bh * mat : nullptr, row0, p, Dk, Dv);
+  tile_load<NC, R>(St, a.S0 ? a.S0 + bh * a.s0_stride * mat : nullptr, row0, p, Dk, Dv);
 
   const int nblk = (T + kStage - 1) / kStage;
   St_ stg;
@@ -520,7 +520,7 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
     if (p < nsteps) {
       const int64_t o = rows0 + (int64_t)(tbase + p) * tstep;
       if (E != nullptr) st_rows<float, R>(E, o, ecap, nrow, rows_aligned);
-      if (tbase + p > 0) st_rows<TIn, R>(y, o - tstep, ycap, nrow, rows_aligned);
+      if (y != nullptr && tbase + p > 0) st_rows<TIn, R>(y, o - tstep, ycap, nrow, rows_aligned);
     }
     if (blk + 1 < nblk) stg.store(lds[(blk + 1) & 1]);
     __syncthreads();
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kThreads) void fwd_sweep_kernel(FwdSweepArgs a) {
       for (int c = 0; c < NC; ++c) aq = fmaf(St[r][c], qlast[c], aq);
       pq[r] = rowsum16(aq);
     }
-    if (writer) st(y, out0 + (int64_t)(T - 1) * tstep, sig * pick<R>(pq, p));
+    if (writer && y != nullptr) st(y, out0 + (int64_t)(T - 1) * tstep, sig * pick<R>(pq, p));
   }
   if (a.ST != nullptr)
     tile_store<NC, R>(St, sig, a.ST + bh * mat, row0, p, Dk, Dv);

@@ -47,6 +47,8 @@ class Saved:
     chunk: int
     log_decay: bool = False
     mask: Optional[torch.Tensor] = None
+    # the forward's v: the backward replays the tiles from it when chunk > 64
+    v: Optional[torch.Tensor] = None
 
 
 def shape_of(q, v, chunk, dtype, log_decay=False) -> _lib.GdrShape:
@@ -108,7 +110,7 @@ def gdr_forward(q, k, v, g, beta, S0=None, *, chunk=DEFAULT_CHUNK, save=True,
             ckpt = torch.empty((max(nbytes, 1),), dtype=torch.uint8, device=dev)
         if ckpt.numel() * ckpt.element_size() < nbytes:
             raise ValueError("ckpt buffer too small")
-        saved = Saved(ckpt, chunk, bool(log_decay), mask)
+        saved = Saved(ckpt, chunk, bool(log_decay), mask, v if chunk > 64 else None)
     wbytes = _lib.forward_workspace_bytes(shape)
     if wbytes > 0 and workspace is None:
         workspace = torch.empty((wbytes,), dtype=torch.uint8, device=dev)
@@ -156,7 +158,7 @@ def gdr_backward(q, k, g, beta, saved: Saved, dy, dS_T=None, *, want_dS0=True,
                            _ptr(saved.ckpt), _ptr(dy), _ptr(dS_T), _ptr(dq),
                            _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dS0),
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
-                           _stream(dev), mask=_ptr(saved.mask))
+                           _stream(dev), mask=_ptr(saved.mask), v=_ptr(saved.v))
     _lib.check(st, "gdr_backward")
     return dq, dk, dv, dg, dbeta, dS0
 

@@ -49,7 +49,7 @@ typedef enum {
   GDR_ERR_BAD_SHAPE = -2,       /* B or T < 0, or Hk, Hv, Dk, Dv < 1            */
   GDR_ERR_HEAD_RATIO = -3,      /* Hv is not a multiple of Hk                   */
   GDR_ERR_UNSUPPORTED_DIM = -4, /* Dk or Dv > 256, or B or Hv > 65535           */
-  GDR_ERR_BAD_CHUNK = -5,       /* chunk outside [1, 64]                        */
+  GDR_ERR_BAD_CHUNK = -5,       /* chunk outside [1, 2^30]                      */
   GDR_ERR_BAD_DTYPE = -6,       /* dtype is not GDR_F32 or GDR_BF16             */
   GDR_ERR_OVERFLOW = -7,        /* a byte size does not fit in 63 bits          */
   GDR_ERR_WORKSPACE = -8,       /* workspace smaller than the size query says  */
@@ -78,10 +78,19 @@ typedef enum { GDR_F32 = 0, GDR_BF16 = 1 } gdr_dtype;
  *                  uses its save buffer must use the same setting. */
 typedef enum { GDR_DECAY_G = 0, GDR_DECAY_LOG = 1 } gdr_decay;
 
-/* Problem description.  chunk = C, the checkpoint interval: the forward saves
- * the state every C steps and the backward processes time in chunks of C
- * steps (the "fixed-size chunks" of the pages' chunked VJP).  The last chunk
- * may be shorter.  Results do not depend on C beyond fp32 rounding. */
+/* Problem description.  chunk = C >= 1, the checkpoint interval: the forward
+ * saves the state every C steps (the "fixed-size chunks" of the pages'
+ * chunked VJP, mlx-lm PR #1217 "What this PR adds"); the last chunk may be
+ * shorter.  The kernels work in tiles of L steps: L = C for C <= 64, else
+ * the largest divisor of C that is at most 64 (64 for a multiple of 64).
+ *   C <= 64: the save buffer holds the state before every chunk and the
+ *            per-step residuals; the backward reads them.
+ *   C > 64:  the save buffer holds only the state before every chunk
+ *            (ceil(T / C) states: less memory held from the forward to the
+ *            backward); the backward first replays the forward tiles of each
+ *            chunk from its saved state into its workspace (recompute), then
+ *            runs as for C = L.
+ * Results do not depend on C beyond fp32 rounding. */
 typedef struct {
   int64_t B, T, Hk, Hv, Dk, Dv;
   int64_t chunk;
@@ -89,24 +98,27 @@ typedef struct {
   int32_t decay; /* gdr_decay: what g holds (0 = the decay itself) */
 } gdr_shape;
 
-/* Number of chunks, ceil(T / chunk) (0 when T == 0). */
+/* Number of saved states (chunks), ceil(T / chunk) (0 when T == 0). */
 int gdr_num_chunks(const gdr_shape* shape, int64_t* out);
 
 /* Bytes of the forward save buffer `ckpt`:
  *   state checkpoints  S_{jC} for j = 0..nchunks-1   [B][Hv][nchunks][Dv][Dk] fp32
  *   per-step residual  e_t = v_t - g_t S_{t-1} k_t    [B][T][Hv][Dv]           fp32
+ *                      (chunk <= 64 only)
  * each region starting on a 256-byte boundary. */
 int gdr_checkpoint_bytes(const gdr_shape* shape, size_t* out);
 
 /* Bytes of the scratch buffer gdr_backward needs: the state-gradient
- * checkpoints (one per chunk) and the per-step G_t k_t vectors, fp32. */
+ * checkpoints (one per tile) and the per-step G_t k_t vectors, fp32, the
+ * per-tile records of the chunked reverse sweep, and for chunk > 64 the
+ * replayed tile states, residuals and forward records. */
 int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out);
 
-/* Bytes of the scratch buffer gdr_forward needs.  Shapes with Dk <= 192,
- * chunk >= 16 and T >= chunk take the chunked forward (the products inside a
- * chunk on matrix cores), which keeps two 64 x 64 fp32 matrices and three
- * vectors per (batch row, value head, chunk) here; every other shape takes
- * the sequential sweep and needs 0 bytes. */
+/* Bytes of the scratch buffer gdr_forward needs.  Shapes with Dk <= 192, a
+ * tile of 16 to 64 steps and T at least one tile take the chunked forward
+ * (the products inside a tile on matrix cores), which keeps two 64 x 64 fp32
+ * matrices and three vectors per (batch row, value head, tile) here; every
+ * other shape takes the sequential sweep and needs 0 bytes. */
 int gdr_forward_workspace_bytes(const gdr_shape* shape, size_t* out);
 
 /* The step mask (optional, both passes): mask[B][T] uint8, NULL means every
@@ -162,17 +174,17 @@ int gdr_forward_noalloc(const gdr_shape* shape, const void* q, const void* k,
                         void* ckpt, void* stream);
 
 /* Backward pass (VJP of gdr_forward for L = <dy, y> + <dS_T, S_T>).
- *   in : q, k, g, beta, dy (shape.dtype) - the same q, k, g, beta and mask
- *        given to gdr_forward; ckpt as written by that gdr_forward call;
- *        dS_T (fp32, NULL means zeros).
+ *   in : q, k, v, g, beta, dy (shape.dtype) - the same q, k, v, g, beta and
+ *        mask given to gdr_forward; ckpt as written by that gdr_forward call;
+ *        dS_T (fp32, NULL means zeros).  v is read only when chunk > 64 (to
+ *        replay the tiles) and may be NULL otherwise.
  *   out: dq, dk (summed over the Hv/Hk value heads of each kv head, in
  *        ascending head order), dv, dg, dbeta (shape.dtype);
  *        dS0 (fp32, NULL means not written).
  *   workspace: at least gdr_backward_workspace_bytes bytes of device memory,
- *        contents ignored on entry and undefined on exit.
- * v is not needed: the forward saved the residual e_t in ckpt. */
+ *        contents ignored on entry and undefined on exit. */
 int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
-                 const void* g, const void* beta, const uint8_t* mask,
+                 const void* v, const void* g, const void* beta, const uint8_t* mask,
                  const void* ckpt,
                  const void* dy, const float* dS_T, void* dq, void* dk,
                  void* dv, void* dg, void* dbeta, float* dS0,

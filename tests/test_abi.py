@@ -66,7 +66,7 @@ def S(B=1, T=4, Hk=2, Hv=4, Dk=8, Dv=8, chunk=2, dtype=_lib.GDR_F32, decay=0):
 @pytest.mark.parametrize("shape,code", [
     (S(B=-1), -2), (S(T=-1), -2), (S(Hk=0), -2), (S(Hv=0), -2), (S(Dk=0), -2),
     (S(Dv=0), -2), (S(Hk=3, Hv=4), -3), (S(Dk=257), -4), (S(Dv=300), -4),
-    (S(B=70000), -4), (S(chunk=0), -5), (S(chunk=65), -5), (S(dtype=2), -6),
+    (S(B=70000), -4), (S(chunk=0), -5), (S(chunk=2**30 + 1), -5), (S(dtype=2), -6),
     (S(dtype=-1), -6), (S(T=2**40), -7), (S(decay=2), -11), (S(decay=-1), -11),
 ])
 def test_shape_errors(lib, shape, code):
@@ -81,7 +81,7 @@ def test_null_shape(lib):
     out = ctypes.c_size_t()
     assert lib.gdr_checkpoint_bytes(None, ctypes.byref(out)) == -1
     assert lib.gdr_forward(None, *([None] * 11), 0, None) == -1
-    assert lib.gdr_backward(None, *([None] * 15), 0, None) == -1
+    assert lib.gdr_backward(None, *([None] * 16), 0, None) == -1
 
 
 def test_null_out_pointer(lib):
@@ -94,27 +94,48 @@ def _round256(x):
     return (x + 255) // 256 * 256
 
 
+def _tile(C):
+    """The kernels' tile: C up to 64, else C's largest divisor up to 64."""
+    return C if C <= 64 else max(d for d in range(1, 65) if C % d == 0)
+
+
 @pytest.mark.parametrize("B,T,Hk,Hv,Dk,Dv,C", [
     (1, 4, 2, 4, 8, 8, 2), (1, 2048, 16, 64, 192, 128, 64),
     (4, 8192, 16, 64, 192, 128, 64), (2, 5, 1, 3, 7, 5, 64), (1, 0, 1, 1, 4, 4, 8),
+    (1, 2048, 16, 64, 192, 128, 512), (4, 8192, 16, 64, 192, 128, 256),
+    (1, 300, 2, 4, 64, 32, 256), (2, 230, 1, 2, 200, 40, 100), (1, 50, 1, 2, 8, 8, 97),
 ])
 def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
     sh = S(B, T, Hk, Hv, Dk, Dv, C)
-    nch = (T + C - 1) // C
-    assert _lib.num_chunks(sh) == nch
-    states = nch * B * Hv * Dv * Dk * 4
+    L = _tile(C)
+    ntiles = (T + L - 1) // L
+    nseg = (T + C - 1) // C
+    assert _lib.num_chunks(sh) == nseg
+    state = B * Hv * Dv * Dk * 4
     rows = B * T * Hv * Dv * 4
-    assert _lib.checkpoint_bytes(sh) == _round256(states) + rows
-    # the chunked sweeps (Dk <= 192, C >= 16, T >= C) keep two 64 x 64
-    # matrices (room for three bf16 pieces of each: 3 x 64 x 64 floats) and
-    # three 64-vectors per (batch row, value head, chunk), plus 64 floats: the
-    # whole forward workspace, and a region after the backward's per-step
-    # vectors
-    chunked = Dk <= 192 and C >= 16 and T >= C
-    prep = B * Hv * nch * (3 * 64 * 64 + 4 * 64) * 4 if chunked else 0
+    # C <= 64: a state per chunk and the per-step residuals; C > 64: only the
+    # state per chunk (the backward replays the rest)
+    if C <= 64:
+        assert _lib.checkpoint_bytes(sh) == _round256(ntiles * state) + rows
+    else:
+        assert _lib.checkpoint_bytes(sh) == nseg * state
+    # the chunked sweeps (Dk <= 192, a tile of 16..64 steps, T >= one tile)
+    # keep two 64 x 64 matrices (room for three bf16 pieces of each: 3 x 64 x
+    # 64 floats) and three 64-vectors per (batch row, value head, tile), plus
+    # 64 floats: the whole forward workspace, and a region after the
+    # backward's per-step vectors (and one more for a replay)
+    chunked = Dk <= 192 and 16 <= L <= 64 and T >= L
+    prep = B * Hv * ntiles * (3 * 64 * 64 + 4 * 64) * 4 if chunked else 0
     assert _lib.forward_workspace_bytes(sh) == prep
-    bwd = _round256(states) + rows
-    assert _lib.backward_workspace_bytes(sh) == (_round256(bwd) + prep if chunked else bwd)
+    end = _round256(ntiles * state) + rows
+    if chunked:
+        end = _round256(end) + prep
+    if C > 64:
+        end = _round256(end) + ntiles * state
+        end = _round256(end) + rows
+        if chunked:
+            end = _round256(end) + prep
+    assert _lib.backward_workspace_bytes(sh) == end
 
 
 FAKE = 1 << 20  # a 16-byte aligned address; never dereferenced in these tests
@@ -163,6 +184,19 @@ def test_backward_errors(lib):
     a = list(args)
     a[6] = FAKE + 8  # dS_T misaligned
     assert _lib.backward_raw(sh, *a, ws, 0) == -9
+
+
+def test_backward_needs_v_beyond_64(lib):
+    """chunk > 64: the backward replays the tiles, so v is required."""
+    sh = S(T=200, Dk=64, Dv=32, chunk=128)
+    ws = _lib.backward_workspace_bytes(sh)
+    args = [FAKE] * 14
+    assert _lib.backward_raw(sh, *args, ws, 0, v=0) == -1
+    assert _lib.backward_raw(sh, *args, ws, 0, v=FAKE + 4) == -9
+    # chunk <= 64 does not read v, but a non-NULL v must still be aligned
+    sh = S(T=200, Dk=64, Dv=32, chunk=64)
+    ws = _lib.backward_workspace_bytes(sh)
+    assert _lib.backward_raw(sh, *args, ws, 0, v=FAKE + 4) == -9
 
 
 def test_empty_batch_is_a_no_op(lib):

@@ -172,13 +172,16 @@ def test_qwen_bf16_B2_sampled(cuda):
 
 
 # ---------------------------------------------------------------- config 5
-def test_long_context_per_row(cuda):
+@pytest.mark.parametrize("C", [64, 512])
+def test_long_context_per_row(cuda, C):
     """Config 5 (B=4, T=8192, trainable S0, mixed decay): one kv group of
     every batch row against the oracle (a different group per row), the fp32
-    outputs S_T and dS0 at the fp32 bar."""
+    outputs S_T and dS0 at the fp32 bar; at C=64 (a state and the residuals
+    per 64 steps saved) and C=512 (a state per 512 steps, the tiles replayed
+    in the backward)."""
     p = inputs.long_context()
-    log("long context B=4 T=8192: one kv group per batch row")
-    gpu = run_gpu(p, cuda, 64)
+    log(f"long context B=4 T=8192 C={C}: one kv group per batch row")
+    gpu = run_gpu(p, cuda, C)
     compare_groups(gpu, p, TOL["bf16"], "long", units=[(0, 0), (1, 7), (2, 10), (3, 15)],
                    state_tol=TOL["f32"])
 
@@ -223,9 +226,76 @@ def test_chunk_invariance(cuda):
     p = inputs.draw(2, 150, 2, 6, 64, 64, seed=5, normalised=True, S0_std=0.1,
                     dST_std=1.0)
     ref = run_gpu(p, cuda, 64)
-    for C in (1, 7, 50):
+    for C in (1, 7, 50, 128, 256):
         got = run_gpu(p, cuda, C)
         compare(got, ref, 2e-6, f"C={C} vs C=64")
+
+
+def _masked(p, seed):
+    rng = np.random.default_rng(seed)
+    p.mask = (rng.random((p.B, p.T)) >= 0.2).astype(np.uint8)
+    return p
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("C,tile", [(256, 64), (128, 64), (96, 48), (192, 64)])
+def test_long_interval_replays_tiles_exactly(cuda, dtype, C, tile):
+    """C > 64 saves a state every C steps only; the backward replays the
+    tiles of each chunk from it with the same kernel, so every output equals
+    the run with C = the tile bit for bit (ragged T, two batch rows, a mask,
+    S0 and dS_T), and the oracle holds it to the bar."""
+    p = _masked(inputs.draw(2, 300, 2, 4, 64, 32, seed=67, normalised=True, decay="mix",
+                            S0_std=0.1, dST_std=1.0, dtype=dtype), 67)
+    log(f"C={C} vs C={tile} {dtype}")
+    a, b = run_gpu(p, cuda, C), run_gpu(p, cuda, tile)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"C={C} vs {tile}: {n}")
+    compare(a, run_oracle(p), TOL[dtype], f"C={C} {dtype}")
+
+
+def test_long_interval_replay_without_segments(cuda):
+    """More (batch row, saved state) pairs than one grid dimension holds: the
+    replay runs every tile of a row from its first saved state instead of
+    segment by segment; still bitwise the C=64 result."""
+    B = 32768
+    p = inputs.draw(B, 130, 1, 1, 16, 16, seed=71, normalised=True, S0_std=0.1)
+    log(f"C=128 replay, B={B}")
+    a, b = run_gpu(p, cuda, 128), run_gpu(p, cuda, 64)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=n)
+
+
+@pytest.mark.parametrize("C", [100, 128])
+def test_long_interval_per_step_path(cuda, C):
+    """Dk = 200 takes the per-step sweeps; C=100 runs 50-step tiles, C=128
+    64-step tiles, both replayed from states saved every C steps."""
+    p = _masked(inputs.draw(2, 230, 1, 2, 200, 40, seed=73, normalised=True, decay="mix",
+                            S0_std=0.1, dST_std=1.0), 73)
+    log(f"per-step path C={C}")
+    compare(run_gpu(p, cuda, C), run_oracle(p), TOL["f32"], f"per-step C={C}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_interval_decode(cuda, dtype):
+    """T <= 8 with C > 64: one saved state (S0), replayed by the per-step sweep."""
+    p = inputs.draw(3, 6, 2, 4, 192, 128, seed=79, normalised=True, S0_std=0.2,
+                    dST_std=1.0, dtype=dtype)
+    compare(run_gpu(p, cuda, 128), run_oracle(p), TOL[dtype], f"decode C=128 {dtype}")
+
+
+def test_long_interval_saved_states(cuda):
+    """At C = 128 the save buffer holds exactly the states S_{128 s}."""
+    import torch
+    import oracle.gdr_oracle as O
+    p = inputs.draw(1, 300, 2, 4, 64, 32, seed=83, normalised=True, S0_std=0.1)
+    res = run_gpu(p, cuda, 128, want_saved=True)
+    nseg = 3
+    ck = res["_saved"].ckpt.view(dtype=torch.float32)[: p.B * p.Hv * nseg * p.Dv * p.Dk]
+    ck = ck.reshape(p.B, p.Hv, nseg, p.Dv, p.Dk).double().cpu().numpy()
+    assert res["_saved"].ckpt.numel() == 4 * ck.size
+    _, _, states = O.forward(p.q, p.k, p.v, p.g, p.beta, p.S0, keep_states=True)
+    for j in range(nseg):
+        assert O.rel_l2(ck[:, :, j], states[128 * j]) <= TOL["f32"], j
 
 
 def test_gqa_matches_repeat_expanded(cuda):
@@ -474,13 +544,14 @@ def test_checkpoints_hold_states(cuda):
         assert O.rel_l2(ck[:, :, j], states[6 * j]) <= 1e-6
 
 
-def test_autograd_function(cuda):
+@pytest.mark.parametrize("chunk", [8, 128])
+def test_autograd_function(cuda, chunk):
     import torch
     from gated_delta_rule_recurrence_amd import ops
-    p = inputs.draw(1, 33, 2, 4, 32, 16, seed=31, normalised=True, S0_std=0.1)
+    p = inputs.draw(1, 133, 2, 4, 32, 16, seed=31, normalised=True, S0_std=0.1)
     d = device_inputs(p, cuda)
     leaves = [d[n].clone().requires_grad_(True) for n in ("q", "k", "v", "g", "beta", "S0")]
-    y, ST = ops.gated_delta_rule(*leaves, chunk=8)
+    y, ST = ops.gated_delta_rule(*leaves, chunk=chunk)
     (y * d["dy"]).sum().backward()
     ref = run_oracle(p)
     import oracle.gdr_oracle as O
