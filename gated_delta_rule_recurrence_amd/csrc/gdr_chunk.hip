@@ -159,8 +159,9 @@ __device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
 // operands the six piece products down to the order of fp32 rounding.  S0,
 // H1 (and, for the Gram, E) are staged in LDS as pieces; each wave's own dy,
 // C, E rows go from global memory to its registers and are split there.
-// QK, KK (bf16 rows) and the final products (each W as three pieces) run on
-// bf16 MFMA as well; the dg product stays on fp32 MFMA.
+// QK, KK (bf16 rows), the final products (each W as three pieces) and the dg
+// product Gam [M | chi] (Gam rows, M^T and chi as three pieces each, six
+// piece products) run on bf16 MFMA as well.
 template <typename TIn, int JT, bool VEC, bool BFP>
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   using L = CL<JT>;

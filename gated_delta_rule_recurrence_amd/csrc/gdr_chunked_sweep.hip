@@ -35,8 +35,12 @@
 //   * reverse: Tb = (I + Bm)^-1 (column-wise back substitution) and Mq.
 // Each substitution forms the same sums as the sequential recurrence.  The
 // sweep kernels then run a value head's chunks in order (reverse order for
-// the gradient), 32 state rows per workgroup.  Rows are independent.  Every
-// product runs on fp32 MFMA.
+// the gradient), 32 state rows per workgroup.  Rows are independent.  With
+// fp32 inputs every product runs on fp32 MFMA; with bf16 inputs (the
+// *_bf16_kernel sweeps) on bf16 MFMA over exact three-piece splits of the
+// fp32 operands.  A replay mode of the forward (FwdSweepArgs::seg) rebuilds
+// the tile states and residuals for the backward from states saved every
+// few tiles.
 //
 // Outputs match the sequential sweeps:
 //   * forward: y, S_T, the state checkpoint at every chunk start, and the
