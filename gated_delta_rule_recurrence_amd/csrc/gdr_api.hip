@@ -57,7 +57,8 @@ struct Sizes {
   int64_t e_off;   // save buffer: the residuals (C <= 64)
   // backward workspace: state-gradient tiles at 0, then
   int64_t c_off;   // the per-step vectors c
-  int64_t p_off;   // the reverse prep records (chunked; else 0)
+  int64_t k_off;   // the reverse sweep's store sinks (chunked)
+  int64_t p_off;   // the reverse records (chunked)
   int64_t rs_off;  // replay: the tile states
   int64_t re_off;  // replay: the residuals
   int64_t rp_off;  // replay: the forward prep records (chunked; else 0)
@@ -91,9 +92,9 @@ int check_shape(const gdr_shape* s, Sizes* z) {
       !mul_ok(x, s->Dv, &r.rows) || !mul_ok(tiles, 4, &b_tiles) ||
       !mul_ok(r.rows, 4, &b_rows) || !mul_ok(r.state * 4, r.nseg, &b_seg))
     return GDR_ERR_OVERFLOW;
-  int64_t prep = 0;
+  int64_t prep = 0, sinks = 0;
   if (r.chunked && (!mul_ok(gdr::chunked_prep_floats(1, 1, r.ntiles), bh, &prep) ||
-                    !mul_ok(prep, 4, &prep)))
+                    !mul_ok(prep, 4, &prep) || !mul_ok(bh * 256, r.ntiles, &sinks)))
     return GDR_ERR_OVERFLOW;
   // save buffer: a state every C steps, and (C <= 64) the residuals
   if (r.replay) {
@@ -108,6 +109,8 @@ int check_shape(const gdr_shape* s, Sizes* z) {
   r.c_off = round_up256(b_tiles);
   if (!add_ok(r.c_off, b_rows, &end)) return GDR_ERR_OVERFLOW;
   if (r.chunked) {
+    r.k_off = round_up256(end);
+    if (!add_ok(r.k_off, sinks, &end)) return GDR_ERR_OVERFLOW;
     r.p_off = round_up256(end);
     if (!add_ok(r.p_off, prep, &end)) return GDR_ERR_OVERFLOW;
   }
@@ -383,6 +386,7 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
       gdr::FwdChunkedArgs fc{};
       fc.s = r;
       fc.prep = reinterpret_cast<float*>(ws + z.rp_off);
+      fc.prep_b = reinterpret_cast<float*>(ws + z.p_off);  // and the reverse records
       err = gdr::launch_fwd_chunked(fc, bf16, s);
     } else {
       r.seg = 0;
@@ -419,7 +423,11 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   if (has_tokens && z.chunked) {
     gdr::BwdChunkedArgs c{};
     c.s = b;
-    c.prep = reinterpret_cast<float*>(ws + z.p_off);
+    // the reverse records: formed here, or (C > 64) by the replay's prep
+    // launch together with the forward records
+    c.prep = reinterpret_cast<const float*>(ws + z.p_off);
+    c.own_prep = z.replay ? 0 : 1;
+    c.sink = reinterpret_cast<float*>(ws + z.k_off);
     err = gdr::launch_bwd_chunked(c, bf16, s);
   } else {
     err = gdr::launch_bwd_sweep(b, bf16, s);

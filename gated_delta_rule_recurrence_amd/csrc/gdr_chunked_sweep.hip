@@ -267,16 +267,29 @@ __device__ __forceinline__ void invert_unit_triangular(float* G, int l) {
 }
 
 // ---------------------------------------------------------------- prep ----
-// grid (nch, Hk, B); wave w handles value heads w, w + 4, ... of the kv head.
+// grid (nch, Hk, B).  MODE kPrepFwd / kPrepBwd: four waves, wave w forms
+// the forward (reverse) records of value heads w, w + 4, ... of the kv head.
+// kPrepBoth: eight waves, two per SIMD, waves 0-3 the forward and waves 4-7
+// the reverse records of the same heads (the Gram matrices are formed once
+// for both, and the second wave of each SIMD hides the first one's
+// latencies); the backward's replay uses it.
+constexpr int kPrepFwd = 0, kPrepBwd = 1, kPrepBoth = 2;
+
+// QK (q_t . k_r) and KK (k_t . k_r) in one [kN][kNP] matrix: QK on and below
+// the diagonal, KK above it.  The records use QK[t][r] only for r <= t, and
+// KK (symmetric) only off the diagonal, read as KK[min][max].
+__device__ __forceinline__ int qk_at(int t, int r) { return t * kNP + r; }  // r <= t
+
+template <int NW>
 struct PL {
   static constexpr int QS = 0, KS = 64 * kN;          // q, k stage [16][kN][4]
-  static constexpr int GW = 0;                         // 4 x [kN][kGP] (alias)
-  static constexpr int VB = 4 * kN * kGP;              // 4 x beta[kN]
-  static constexpr int VS = VB + 4 * kN;               // 4 x g[kN]
-  static constexpr int QK = VS + 4 * kN, KK = QK + kN * kNP;
-  static constexpr int SIZE = KK + kN * kNP;
+  static constexpr int GW = 0;                         // NW x [kN][kGP] (alias)
+  static constexpr int VB = NW * kN * kGP;             // NW x beta[kN]
+  static constexpr int VS = VB + NW * kN;              // NW x g[kN]
+  static constexpr int QK = VS + NW * kN;              // QK / KK [kN][kNP]
+  static constexpr int SIZE = QK + kN * kNP;
   static_assert(2 * 64 * kN <= VB, "stage fits the per-wave arrays");
-  // bf16 inputs: q, k row-major bf16 [kN][KGS] (alias the per-wave arrays);
+  // bf16 inputs: q, k rows as bf16 [kN][KGS] (alias the per-wave arrays);
   // the row stride an odd number of 16-byte units, so the 16-byte operand
   // reads of 16 rows at one column group hit distinct banks
   static constexpr int KGS = 16 * kMaxJT + 8;
@@ -285,10 +298,12 @@ struct PL {
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
-template <typename TIn, bool BWD, bool VEC>
-__global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
-                                                           float* __restrict__ prep) {
-  using L = PL;
+template <typename TIn, int MODE, bool VEC>
+__global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) void prep_kernel(
+    ChunkedSweepShape a, float* __restrict__ prep_f, float* __restrict__ prep_b) {
+  constexpr int NW = MODE == kPrepBoth ? 8 : 4;
+  constexpr int NTH = 64 * NW;
+  using L = PL<NW>;
   extern __shared__ __align__(16) float sm[];
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -302,28 +317,32 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
-  const int tw = 16 * w;
+  const int tw = 16 * (w & 3);
+  // this wave's first value head, and which records it forms
+  const int wh = w & 3;
+  const bool bwd = MODE == kPrepBwd || (MODE == kPrepBoth && w >= 4);
 
   // g, beta of this wave's first value head, issued before the k, q loads
   // (index clamped into the tensors; masked where used)
   auto gb_index = [&](int hh) {
     return ((int64_t)b * T + t0 + (l < n ? l : 0)) * Hv + hk * rep + hh;
   };
-  TIn g_raw = g[gb_index(w < rep ? w : 0)], b_raw = beta[gb_index(w < rep ? w : 0)];
+  TIn g_raw = g[gb_index(wh < rep ? wh : 0)], b_raw = beta[gb_index(wh < rep ? wh : 0)];
 
   // ---- QK[t][r] = q_t . k_r, KK[t][r] = k_t . k_r (MFMA over Dk) ----------
+  // rows 16 w .. of both by waves 0-3 (the other waves only stage)
   constexpr bool kBf16 = std::is_same<TIn, bf16>::value && VEC;
   if (kBf16 && Dk % 8 == 0) {
     // bf16 k, q: the rows staged as bf16 and multiplied on bf16 MFMA (the
     // products of two bf16 values are exact in fp32, as in the fp32 path)
     constexpr int NCH = 2 * kMaxJT;                  // 16-byte chunks per row
-    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
+    constexpr int NL = (kN * NCH + NTH - 1) / NTH;
     uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
     uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
     uint4 rq[NL], rk[NL];
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int ci = tid + kThreads * u;
+      const int ci = tid + NTH * u;
       const int s = ci / NCH, j = 8 * (ci % NCH);
       const bool ok = ci < kN * NCH && s < n && j < Dk;
       int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j : 0;
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     }
 #pragma unroll
     for (int u = 0; u < NL; ++u) {
-      const int ci = tid + kThreads * u;
+      const int ci = tid + NTH * u;
       const int s = ci / NCH, j = 8 * (ci % NCH);
       const bool ok = ci < kN * NCH && s < n && j < Dk;
       if (ci < kN * NCH) {
@@ -354,37 +373,40 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     f4 acc[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; 32 * ks < Dk; ++ks) {
-      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
-      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
-      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
+    if (w < 4) {
+      for (int ks = 0; 32 * ks < Dk; ++ks) {
+        const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
+        const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
+        const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const uint4 bk =
-            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
-        acc[tb] = mfma_bf16(aq, bk, acc[tb]);
-        acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
+        for (int tb = 0; tb < 4; ++tb) {
+          const uint4 bk =
+              *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
+          acc[tb] = mfma_bf16(aq, bk, acc[tb]);
+          acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
+        }
       }
     }
     __syncthreads();  // the stage aliases the per-wave arrays
+    if (w < 4) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
-        sm[L::QK + o] = acc[tb][v];
-        sm[L::KK + o] = acc[4 + tb][v];
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int i = tw + 4 * lq + v, j = 16 * tb + lr;
+          sm[L::QK + i * kNP + j] = j <= i ? acc[tb][v] : acc[4 + tb][v];
+        }
+    }
     __syncthreads();
   } else   {
-    constexpr int NB = kMaxJT / 4, NU = 4;
+    constexpr int NB = kMaxJT / 4, NU = 4 * 256 / NTH;
     Quad<TIn, VEC> rq[NB][NU], rk[NB][NU];
     uint64_t msk = 0;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb)
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const int qi = tid + kThreads * u;
+        const int qi = tid + NTH * u;
         const int s = qi >> 4, j = 64 * jb + 4 * (qi & 15);
         const bool ok = s < n && j < Dk;
         const int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j : 0;
@@ -400,34 +422,37 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       if (64 * jb >= Dk) break;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
-        const int qi = tid + kThreads * u;
+        const int qi = tid + NTH * u;
         const int s = qi >> 4, jq = qi & 15;
         const uint32_t mu = (uint32_t)(msk >> (4 * (NU * jb + u))) & 15u;
         *reinterpret_cast<f4*>(sm + L::QS + (jq * kN + s) * 4) = rq[jb][u].get(mu);
         *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk[jb][u].get(mu);
       }
       __syncthreads();
+      if (w < 4) {
 #pragma unroll 2
-      for (int ks = 0; ks < 16; ++ks) {
-        const int fw = ((ks * kN + tw + lr) << 2) + lq;
-        const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
+        for (int ks = 0; ks < 16; ++ks) {
+          const int fw = ((ks * kN + tw + lr) << 2) + lq;
+          const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
-          acc[tb] = mfma(aq, bk, acc[tb]);
-          acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
+          for (int tb = 0; tb < 4; ++tb) {
+            const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
+            acc[tb] = mfma(aq, bk, acc[tb]);
+            acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
+          }
         }
       }
       __syncthreads();
     }
+    if (w < 4) {
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+      for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
-        sm[L::QK + o] = acc[tb][v];
-        sm[L::KK + o] = acc[4 + tb][v];
-      }
+        for (int v = 0; v < 4; ++v) {
+          const int i = tw + 4 * lq + v, j = 16 * tb + lr;
+          sm[L::QK + i * kNP + j] = j <= i ? acc[tb][v] : acc[4 + tb][v];
+        }
+    }
     __syncthreads();
   }
 
@@ -435,12 +460,12 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
   float* G = sm + L::GW + w * kN * kGP;  // [kN][kGP] per wave
   float* vb = sm + L::VB + w * kN;       // beta_t
   float* vg = sm + L::VS + w * kN;       // g_t
-  const float* QK = sm + L::QK;
-  const float* KK = sm + L::KK;
-  for (int hh = w; hh < rep; hh += 4) {
+  const float* QK = sm + L::QK;          // QK on and below the diagonal, KK above
+  for (int hh = wh; hh < rep; hh += 4) {
     const int h = hk * rep + hh;
-    float* __restrict__ rec = prep + (((int64_t)b * Hv + h) * a.nch + jc) * kChunkPrepStride;
-    if (hh != w) {
+    float* __restrict__ rec =
+        (bwd ? prep_b : prep_f) + (((int64_t)b * Hv + h) * a.nch + jc) * kChunkPrepStride;
+    if (hh != wh) {
       g_raw = g[gb_index(hh)];
       b_raw = beta[gb_index(hh)];
     }
@@ -467,11 +492,11 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
     // bf16 inputs in 8-element groups: the bf16-product sweeps read the
     // matrices as bf16 pieces
     const bool pieces = bf16_products(kBf16, Dk, a.Dv);
-    if constexpr (!BWD) {
+    if (!bwd) {
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
       if (pieces) {
         pieces_to_record(rec + kBrM, l, [&](int t, int s) {
-          return s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
+          return s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
         });
       } else
 #pragma unroll 2
@@ -481,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int s = rstep(4 * (bx & 3) + e, lq);
-          m4[e] = s <= t ? G[s * kGP + t] * QK[t * kNP + s] * vb[s] : 0.f;
+          m4[e] = s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
         }
         *reinterpret_cast<f4*>(rec + kPrM + (bx * 64 + l) * 4) = m4;
       }
@@ -490,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       {
         float av[kN];
 #pragma unroll
-        for (int t = 1; t < kN; ++t) av[t] = G[l * kGP + t] * KK[t * kNP + l] * bl;
+        for (int t = 1; t < kN; ++t) av[t] = G[l * kGP + t] * QK[l * kNP + t] * bl;  // KK[l][t], l < t
 #pragma unroll
         for (int t = 1; t < kN; ++t)
           if (l < t) G[t * kGP + l] = av[t];
@@ -512,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
       if (pieces) {
         pieces_to_record(rec + kBbM, l, [&](int t, int s) {
-          return s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
+          return s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
         });
       } else
 #pragma unroll 2
@@ -522,7 +547,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int s = rstep(4 * (bx & 3) + e, lq);
-          m4[e] = s >= t ? G[t * kGP + s] * QK[s * kNP + t] : 0.f;
+          m4[e] = s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
         }
         *reinterpret_cast<f4*>(rec + kPbM + (bx * 64 + l) * 4) = m4;
       }
@@ -531,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void prep_kernel(ChunkedSweepShape a,
       {
         float bv[kN];  // the lane's operands first, then the updates
 #pragma unroll
-        for (int t = 0; t < kN - 1; ++t) bv[t] = bl * KK[l * kNP + t] * G[t * kGP + l];
+        for (int t = 0; t < kN - 1; ++t) bv[t] = bl * QK[t * kNP + l] * G[t * kGP + l];  // KK[t][l], t < l
 #pragma unroll
         for (int t = 0; t < kN - 1; ++t)
           if (l > t) G[t * kGP + l] = bv[t];
@@ -1056,8 +1081,11 @@ struct SLB {
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
-// kDS = 32 state rows per workgroup, eight waves
-template <int JT, bool SAVE>
+// kDS = 32 state rows per workgroup, eight waves.  GEN: the general tile
+// range and save slots (a segment replay, a save every few tiles, a strided
+// S0, no y or residuals); without it every tile runs from S0 and saves its
+// state and residuals, which leaves the chunk loop fewer live scalars.
+template <int JT, bool SAVE, bool GEN>
 __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChunkedArgs A) {
   using L = SLB<JT>;
   constexpr int PS = L::PS;
@@ -1079,7 +1107,10 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   bf16* __restrict__ y = static_cast<bf16*>(a.y);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
   const SweepBlock wb = sweep_block();
-  const TileRange tr = tile_range(a, wb.b, wb.h);
+  const TileRange tr = GEN ? tile_range(a, wb.b, wb.h)
+                           : TileRange{wb.b, 0, a.nch, (int64_t)wb.b * a.Hv + wb.h};
+  const int nslot = GEN ? a.nslot : a.nch;
+  auto slot_of = [&](int c) { return GEN ? ckpt_slot(a, c) : c; };
   const int i0 = wb.x * kDS, h = wb.h, b = tr.b;
   const int hk = h / (Hv / Hk);
   const int tid = threadIdx.x;
@@ -1142,7 +1173,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   // `slot`, or the sink when slot < 0; out-of-range lanes store to the sink
   // too)
   auto put_state = [&](int slot, int lr, int lq, float* sink) __attribute__((always_inline)) {
-    float* __restrict__ ck = SAVE ? a.Sck + (bh * a.nslot + (slot >= 0 ? slot : 0)) * mat : nullptr;
+    float* __restrict__ ck = SAVE ? a.Sck + (bh * nslot + (slot >= 0 ? slot : 0)) * mat : nullptr;
     asm volatile("" : "+v"(slot));  // a per-lane select below, not a branch
 #pragma unroll
     for (int nj = 0; nj < JW; ++nj) {
@@ -1169,7 +1200,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_state(ckpt_slot(a, tr.c0), tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
+    put_state(slot_of(tr.c0), tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
   }
   for (int c = tr.c0; c < tr.c1; ++c) {
     int tl = tid;
@@ -1271,7 +1302,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         // by the reverse pass: non-temporal)
         const f4 er = quad_transpose(E, lr);
         const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
-        const bool ok = a.E != nullptr && t < n && i0 + r4 < Dv;
+        const bool ok = (!GEN || a.E != nullptr) && t < n && i0 + r4 < Dv;
         __builtin_nontemporal_store(
             er, reinterpret_cast<f4*>(ok ? a.E + vbase + (int64_t)t * vst + r4 : sink16));
       }
@@ -1290,7 +1321,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         // as E: one 8-byte store of four bf16 rows per lane
         const f4 yr = quad_transpose(Yv, lr);
         const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
-        const bool ok = y != nullptr && t < n && i0 + r4 < Dv;
+        const bool ok = (!GEN || y != nullptr) && t < n && i0 + r4 < Dv;
         const uint2 yb = {cvt_pk_bf16(yr[0], yr[1]), cvt_pk_bf16(yr[2], yr[3])};
         *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(y + vbase + (int64_t)t * vst + r4)
                                      : reinterpret_cast<uint2*>(sink16)) = yb;
@@ -1316,7 +1347,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
       }
     }
     __syncthreads();  // stage reads done before it is rewritten
-    put_state(c + 1 < tr.c1 ? ckpt_slot(a, c + 1) : -1, lr, lq, sink16);
+    put_state(c + 1 < tr.c1 ? slot_of(c + 1) : -1, lr, lq, sink16);
   }
   if (a.ST != nullptr) {
     const int l = tid & 63, lr = l & 15, lq = l >> 4;
@@ -1644,7 +1675,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
   {
     int tl = tid;
     asm volatile("" : "+v"(tl));
-    put_grad(cl, tl & 15, (tl & 63) >> 4, A.prep + kPrSink);
+    put_grad(cl, tl & 15, (tl & 63) >> 4, A.sink);
   }
 
   for (int c = cl; c >= 0; --c) {
@@ -1655,7 +1686,7 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
     const int ti = 16 * nt + lr;
     const int n = chunk_len(c);
     const float* __restrict__ rec = A.prep + (bh * a.nch + c) * kChunkPrepStride;
-    float* const sink16 = A.prep + (bh * a.nch + c) * kChunkPrepStride + kPrSink;  // 16-byte aligned
+    float* const sink16 = A.sink + (bh * a.nch + c) * 64;  // 16-byte aligned
     const int64_t vbase = v_base(c);
     deposit_rows<KRS>(kq, kr, qr);
     // step pieces [i][t]: this lane's rows t = tw + 4 lq .. +3 of column ti
@@ -1828,12 +1859,16 @@ hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
   return hipGetLastError();
 }
 
-template <typename TIn, bool BWD>
-hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep, hipStream_t s) {
+// The records of MODE (forward records to prep_f, reverse to prep_b).
+template <typename TIn, int MODE>
+hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep_f, float* prep_b,
+                       hipStream_t s) {
+  constexpr int NW = MODE == kPrepBoth ? 8 : 4;
   const dim3 grid(sh.nch, sh.Hk, sh.B);
-  const size_t lds = sizeof(float) * PL::SIZE;
-  if (sh.Dk % 4 == 0) return launch(prep_kernel<TIn, BWD, true>, grid, kThreads, lds, s, sh, prep);
-  return launch(prep_kernel<TIn, BWD, false>, grid, kThreads, lds, s, sh, prep);
+  const size_t lds = sizeof(float) * PL<NW>::SIZE;
+  if (sh.Dk % 4 == 0)
+    return launch(prep_kernel<TIn, MODE, true>, grid, 64 * NW, lds, s, sh, prep_f, prep_b);
+  return launch(prep_kernel<TIn, MODE, false>, grid, 64 * NW, lds, s, sh, prep_f, prep_b);
 }
 
 template <typename TIn, bool BWD, typename Args>
@@ -1857,10 +1892,15 @@ hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_
       if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
         if (bf16_products(true, Dk, Dv)) {
           const size_t lb = sizeof(float) * SLB<JT>::SIZE;
-          // the save buffer holds both the checkpoints and the residuals
-          if (A.s.Sck != nullptr)
-            return launch(fwd_chunked_bf16_kernel<JT, true>, grid, kSwThreads, lb, s, A);
-          return launch(fwd_chunked_bf16_kernel<JT, false>, grid, kSwThreads, lb, s, A);
+          const FwdSweepArgs& f = A.s;
+          const bool gen = f.seg > 0 || f.ck_every != 1 || f.s0_stride != 1 ||
+                           f.nslot != f.nch || f.y == nullptr ||
+                           (f.Sck != nullptr && f.E == nullptr);
+          if (f.Sck != nullptr)
+            return gen ? launch(fwd_chunked_bf16_kernel<JT, true, true>, grid, kSwThreads, lb, s, A)
+                       : launch(fwd_chunked_bf16_kernel<JT, true, false>, grid, kSwThreads, lb, s, A);
+          return gen ? launch(fwd_chunked_bf16_kernel<JT, false, true>, grid, kSwThreads, lb, s, A)
+                     : launch(fwd_chunked_bf16_kernel<JT, false, false>, grid, kSwThreads, lb, s, A);
         }
       return launch(fwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
     }
@@ -1901,7 +1941,10 @@ ChunkedSweepShape shape_of(const Args& a) {
 
 template <typename TIn>
 hipError_t fwd_go(const FwdChunkedArgs& A, hipStream_t s) {
-  const hipError_t e = launch_prep<TIn, false>(shape_of(A.s), A.prep, s);
+  const hipError_t e =
+      A.prep_b != nullptr
+          ? launch_prep<TIn, kPrepBoth>(shape_of(A.s), A.prep, A.prep_b, s)
+          : launch_prep<TIn, kPrepFwd>(shape_of(A.s), A.prep, nullptr, s);
   if (e != hipSuccess) return e;
   // a segment replay runs every (batch row, segment) pair side by side
   const int zb = A.s.seg > 0 ? A.s.B * ((A.s.nch + A.s.seg - 1) / A.s.seg) : A.s.B;
@@ -1910,8 +1953,11 @@ hipError_t fwd_go(const FwdChunkedArgs& A, hipStream_t s) {
 
 template <typename TIn>
 hipError_t bwd_go(const BwdChunkedArgs& A, hipStream_t s) {
-  const hipError_t e = launch_prep<TIn, true>(shape_of(A.s), A.prep, s);
-  if (e != hipSuccess) return e;
+  if (A.own_prep) {
+    const hipError_t e = launch_prep<TIn, kPrepBwd>(shape_of(A.s), nullptr,
+                                                    const_cast<float*>(A.prep), s);
+    if (e != hipSuccess) return e;
+  }
   return launch_sweep<TIn, true>(A, A.s.Dk, A.s.Dv, A.s.Hv, A.s.B, s);
 }
 

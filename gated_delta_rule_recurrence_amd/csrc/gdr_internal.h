@@ -75,11 +75,16 @@ struct ChunkArgs {
 // prep kernel.
 struct FwdChunkedArgs {
   FwdSweepArgs s;
-  float* prep;  // [B][Hv][nch][kChunkPrepStride]
+  float* prep;    // [B][Hv][nch][kChunkPrepStride]: the forward records
+  float* prep_b;  // may be null; else the reverse sweep's records are formed
+                  // here too, by the same prep launch
 };
 struct BwdChunkedArgs {
   BwdSweepArgs s;
-  float* prep;  // [B][Hv][nch][kChunkPrepStride]
+  const float* prep;  // [B][Hv][nch][kChunkPrepStride]: the reverse records
+  int own_prep;       // 1: form them here first (prep is then writable);
+                      // 0: a replay's prep launch formed them
+  float* sink;        // [B][Hv][nch][64]: store target of out-of-range lanes
 };
 // What the prep kernels read.
 struct ChunkedSweepShape {

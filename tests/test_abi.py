@@ -113,22 +113,25 @@ def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
     assert _lib.num_chunks(sh) == nseg
     state = B * Hv * Dv * Dk * 4
     rows = B * T * Hv * Dv * 4
+    # the chunked sweeps (Dk <= 192, a tile of 16..64 steps, T >= one tile)
+    # keep two 64 x 64 matrices (room for three bf16 pieces of each: 3 x 64 x
+    # 64 floats) and three 64-vectors per (batch row, value head, tile), plus
+    # 64 floats: the whole forward workspace
+    chunked = Dk <= 192 and 16 <= L <= 64 and T >= L
+    prep = B * Hv * ntiles * (3 * 64 * 64 + 4 * 64) * 4 if chunked else 0
+    assert _lib.forward_workspace_bytes(sh) == prep
     # C <= 64: a state per chunk and the per-step residuals; C > 64: only the
     # state per chunk (the backward replays the rest)
     if C <= 64:
         assert _lib.checkpoint_bytes(sh) == _round256(ntiles * state) + rows
     else:
         assert _lib.checkpoint_bytes(sh) == nseg * state
-    # the chunked sweeps (Dk <= 192, a tile of 16..64 steps, T >= one tile)
-    # keep two 64 x 64 matrices (room for three bf16 pieces of each: 3 x 64 x
-    # 64 floats) and three 64-vectors per (batch row, value head, tile), plus
-    # 64 floats: the whole forward workspace, and a region after the
-    # backward's per-step vectors (and one more for a replay)
-    chunked = Dk <= 192 and 16 <= L <= 64 and T >= L
-    prep = B * Hv * ntiles * (3 * 64 * 64 + 4 * 64) * 4 if chunked else 0
-    assert _lib.forward_workspace_bytes(sh) == prep
+    # backward: state-gradient tiles, c, (chunked) 256 bytes of store sinks
+    # per tile and the reverse records, and for a replay the tile states,
+    # residuals and (chunked) forward records
     end = _round256(ntiles * state) + rows
     if chunked:
+        end = _round256(end) + B * Hv * ntiles * 256
         end = _round256(end) + prep
     if C > 64:
         end = _round256(end) + ntiles * state
