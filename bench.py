@@ -45,17 +45,17 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "12371b103bee4d16",
+    "sources_sha256_16": "1c4dd4711cefdc62",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 969.8e6, "bwd_write_bytes": 518.8e6,
-    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 483.4e6,
+    "bwd_read_bytes": 968.1e6, "bwd_write_bytes": 519.0e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 485.0e6,
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 4.4, "valu_busy_pct": 16.9},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 49.0},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 4.6, "valu_busy_pct": 17.3},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.3, "valu_busy_pct": 47.4},
-        "chunk_kernel": {"mfma_busy_pct": 21.0, "valu_busy_pct": 33.0},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 4.4, "valu_busy_pct": 17.1},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.8, "valu_busy_pct": 48.2},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 4.7, "valu_busy_pct": 18.2},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.6, "valu_busy_pct": 48.0},
+        "chunk_kernel": {"mfma_busy_pct": 20.8, "valu_busy_pct": 32.8},
     },
 }
 PROFILED_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
