@@ -141,12 +141,34 @@ def test_bf16_products_match_fp32_path(cuda):
         assert frac <= 2e-3 and rel <= 2e-4, f"{name}: differing {frac:.2e}, rel L2 {rel:.2e}"
 
 
-def test_qwen_f32_T256_sampled(cuda):
+def test_qwen_f32_T256_all_groups(cuda):
+    """The headline heads with fp32 inputs (fp32-operand kernels): every kv
+    group at the fp32 bar."""
     p = inputs.qwen35_9b(256, dtype="f32")
     gpu = run_gpu(p, cuda, 64)
-    for hk in (0, 15):
-        compare(slice_group(gpu, p, 0, hk), run_oracle(p, 0, hk), TOL["f32"],
-                f"qwen f32 T=256 kv{hk}")
+    compare_groups(gpu, p, TOL["f32"], "qwen f32 T=256")
+
+
+def test_qwen_bf16_log_decay_mask_all_groups(cuda):
+    """The log-decay input and the step mask (rows f2, f4) at the headline
+    heads, bf16, T=512, with a trainable S0 and dS_T: every kv group."""
+    p = inputs.draw(1, 512, 16, 64, 192, 128, seed=89, normalised=True, decay="mix",
+                    S0_std=0.05, dST_std=1.0, dtype="bf16", log_decay=True)
+    rng = np.random.default_rng(89)
+    p.mask = (rng.random((1, 512)) >= 0.1).astype(np.uint8)
+    gpu = run_gpu(p, cuda, 64)
+    compare_groups(gpu, p, TOL["bf16"], "qwen log+mask T=512", state_tol=TOL["f32"])
+
+
+def test_qwen_bf16_T2048_long_interval_bitwise(cuda):
+    """The benchmark workload with C = 128 and 512 (tiles replayed in the
+    backward) equals C = 64 bit for bit."""
+    p = inputs.qwen35_9b(2048)
+    ref = run_gpu(p, cuda, 64)
+    for C in (128, 512):
+        got = run_gpu(p, cuda, C)
+        for n in ref:
+            np.testing.assert_array_equal(got[n], ref[n], err_msg=f"C={C}: {n}")
 
 
 @pytest.mark.parametrize("T", [512, 1024, 2048])
