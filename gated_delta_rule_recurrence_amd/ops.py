@@ -129,7 +129,9 @@ def gdr_backward(q, k, g, beta, saved: Saved, dy, dS_T=None, *, want_dS0=True,
                  workspace=None, out=None):
     """Backward pass.  Returns (dq, dk, dv, dg, dbeta, dS0 or None).
 
-    With a log-decay forward (saved.log_decay), dg is dL/d(log g)."""
+    With a log-decay forward (saved.log_decay), dg is dL/d(log g).  For
+    chunk > 64 the backward replays the forward tiles from saved.v, the
+    forward's v."""
     dev, dt = q.device, q.dtype
     B, T, Hk, Dk = q.shape
     Hv, Dv = dy.shape[2], dy.shape[3]
@@ -170,14 +172,20 @@ class GatedDeltaRule(torch.autograd.Function):
     def forward(ctx, q, k, v, g, beta, S0, chunk, log_decay=False, mask=None):
         y, S_T, saved = gdr_forward(q, k, v, g, beta, S0, chunk=chunk,
                                     log_decay=log_decay, mask=mask)
-        ctx.saved = saved
         ctx.has_S0 = S0 is not None
-        ctx.save_for_backward(q, k, g, beta)
+        # v is needed again only when the backward replays the tiles (chunk >
+        # 64); it then goes through save_for_backward like the other inputs
+        ctx.with_v = saved.v is not None
+        saved.v = None
+        ctx.saved = saved
+        ctx.save_for_backward(q, k, g, beta, *((v,) if ctx.with_v else ()))
         return y, S_T
 
     @staticmethod
     def backward(ctx, dy, dS_T):
-        q, k, g, beta = ctx.saved_tensors
+        q, k, g, beta, *rest = ctx.saved_tensors
+        if ctx.with_v:
+            ctx.saved.v = rest[0]
         # autograd materialises absent cotangents as zeros
         dy = dy.contiguous()
         dS_T = None if dS_T is None else dS_T.contiguous()
