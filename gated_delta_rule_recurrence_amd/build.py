@@ -23,6 +23,9 @@ CSRC = PKG / "csrc"
 BUILD = CSRC / "_build"
 LIB = PKG / "libgdr.so"
 INCLUDE = PKG.parent / "include"
+# test-only probes of the device helpers (not part of libgdr.so)
+PROBE_SRC = PKG.parent / "tests" / "probe" / "gdr_device_probe.hip"
+PROBE_LIB = PROBE_SRC.parent / "libgdr_probe.so"
 
 ARCH = "gfx950"
 CXXFLAGS = [
@@ -75,9 +78,22 @@ def build(jobs: int | None = None, verbose: bool = True) -> Path:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    if PROBE_SRC.exists():
+        build_probe()
     if verbose:
         print(f"built {LIB} from {len(sources)} sources")
     return LIB
+
+
+def build_probe() -> Path:
+    """The test-only probe library of the device helpers."""
+    tmp = PROBE_LIB.with_name(PROBE_LIB.name + ".tmp")
+    cmd = [hipcc(), *CXXFLAGS, "-shared", str(PROBE_SRC), "-o", str(tmp)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {PROBE_SRC.name}:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 def main() -> None:
