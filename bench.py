@@ -50,14 +50,27 @@ PROFILE = {
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
     "bwd_read_bytes": 968.1e6, "bwd_write_bytes": 519.0e6,
     "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 485.0e6,
+    # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 4.4, "valu_busy_pct": 17.1},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.8, "valu_busy_pct": 48.2},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 4.7, "valu_busy_pct": 18.2},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.6, "valu_busy_pct": 48.0},
-        "chunk_kernel": {"mfma_busy_pct": 20.8, "valu_busy_pct": 32.8},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 4.4, "valu_busy_pct": 17.1, "avg_us": 44.4},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.8, "valu_busy_pct": 48.2,
+                                    "avg_us": 163.8},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 4.7, "valu_busy_pct": 18.2, "avg_us": 43.4},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.6, "valu_busy_pct": 48.0,
+                                    "avg_us": 174.5},
+        "chunk_kernel": {"mfma_busy_pct": 20.8, "valu_busy_pct": 32.8, "avg_us": 257.9},
     },
 }
+BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_kernel")
+FWD_KERNELS = ("prep_kernel<fwd>", "fwd_chunked_bf16_kernel")
+
+
+def pipe_busy(names):
+    """Time-weighted MFMA and VALU busy percentages over a call's kernels."""
+    ks = [PROFILE["kernels"][n] for n in names]
+    t = sum(k["avg_us"] for k in ks)
+    return {"mfma_busy_pct": sum(k["mfma_busy_pct"] * k["avg_us"] for k in ks) / t,
+            "valu_busy_pct": sum(k["valu_busy_pct"] * k["avg_us"] for k in ks) / t}
 PROFILED_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
                     "gdr_chunk.hip")
 
@@ -510,11 +523,12 @@ def main():
     prof_ok = (default_workload and PROFILE["sources_sha256_16"] is not None
                and sources_digest() == PROFILE["sources_sha256_16"])
     traffic = fwd_traffic = None
-    counters = None
+    counters = bwd_pipes = fwd_pipes = None
     if prof_ok:
         traffic = PROFILE["bwd_read_bytes"] + PROFILE["bwd_write_bytes"]
         fwd_traffic = PROFILE["fwd_read_bytes"] + PROFILE["fwd_write_bytes"]
         counters = PROFILE["kernels"]
+        bwd_pipes, fwd_pipes = pipe_busy(BWD_KERNELS), pipe_busy(FWD_KERNELS)
 
     rec = {
         "metric": "fwd+bwd tokens/s, Qwen3.5-9B gated-delta shape T=2048",
@@ -552,12 +566,15 @@ def main():
                      "hbm_frac_algorithmic": bwd_bytes / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                      "hbm_frac_counters": (traffic / (bwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS
                                            if traffic else None),
+                     # SQ counters, weighted by kernel time over the call
+                     "pipes_counters": bwd_pipes,
                      "avg_launch_ms": bwd_ms},
         "forward": {"kernel": f"gdr_forward (prep_kernel<fwd>, fwd_chunked{sfx}_kernel)",
                     "achieved_tflops": fwd_tf, "frac": fwd_tf / FP32_PEAK_TF,
                     "flops_per_launch": fwd_flops, "algorithmic_bytes_per_launch": fwd_bytes,
                     "intermediate_bytes_per_launch": fwd_mid,
                     "traffic": fwd_traffic,
+                    "pipes_counters": fwd_pipes,
                     "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "avg_launch_ms": fwd_ms},
         "counters": counters,
