@@ -93,15 +93,18 @@ constexpr int kPrSink = 12480;
 static_assert(kPbBeta + kN <= kPrSink && kBbBeta + kN <= kPrSink &&
                   kPrSink + 64 <= kChunkPrepStride, "record");
 
-// A [64][64] matrix, given elementwise, to a record as three bf16 pieces in
-// 16x16x32 A-fragment order: block (tb, ks, piece) holds for lane l the 16
-// bytes of row 16 tb + l % 16, columns 32 ks + 8 (l / 16) .. +7; block b
-// starts at float (b * 64 + l) * 4, the blocks ordered (tb, ks, piece).
-template <typename Elem>
+// A [64][64] triangular matrix, given elementwise, to a record as three bf16
+// pieces in 16x16x32 A-fragment order: block (tb, ks, piece) holds for lane l
+// the 16 bytes of row 16 tb + l % 16, columns 32 ks + 8 (l / 16) .. +7; block
+// b = 2 tb + ks starts at float (3 b * 64 + l) * 4.  The two blocks past the
+// diagonal (lower triangle: tb < 2, ks = 1; UPPER: tb >= 2, ks = 0) are zero;
+// they are not written, and the readers skip them (pieces_from_record).
+template <bool UPPER, typename Elem>
 __device__ __forceinline__ void pieces_to_record(float* __restrict__ dst, int l, Elem elem) {
   const int lr = l & 15, lq = l >> 4;
 #pragma unroll 2
-  for (int b = 0; b < 8; ++b) {
+  for (int i = 0; i < 6; ++i) {
+    const int b = UPPER ? (i < 4 ? i : 2 * i - 3) : (i < 2 ? 2 * i : i + 2);
     const int t = 16 * (b >> 1) + lr, s0 = 32 * (b & 1) + 8 * lq;
     f4 x, y;
 #pragma unroll
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
     if (!bwd) {
       // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
       if (pieces) {
-        pieces_to_record(rec + kBrM, l, [&](int t, int s) {
+        pieces_to_record<false>(rec + kBrM, l, [&](int t, int s) {
           return s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
         });
       } else
@@ -523,7 +526,7 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
       // T = (I + A)^-1 in place of A
       invert_unit_triangular<false>(G, l);
       if (pieces) {
-        pieces_to_record(rec + kBrT, l, [&](int t, int s) { return G[t * kGP + s]; });
+        pieces_to_record<false>(rec + kBrT, l, [&](int t, int s) { return G[t * kGP + s]; });
         rec[kBrGam + l] = pre;
         rec[kBrKs + l] = bl * suf;
         if (l == n - 1) rec[kBrGend] = pre;
@@ -536,7 +539,7 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
     } else {
       // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
       if (pieces) {
-        pieces_to_record(rec + kBbM, l, [&](int t, int s) {
+        pieces_to_record<true>(rec + kBbM, l, [&](int t, int s) {
           return s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
         });
       } else
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
       // Tb = (I + Bm)^-1 in place of Bm
       invert_unit_triangular<true>(G, l);
       if (pieces) {
-        pieces_to_record(rec + kBbT, l, [&](int t, int s) { return G[t * kGP + s]; });
+        pieces_to_record<true>(rec + kBbT, l, [&](int t, int s) { return G[t * kGP + s]; });
         rec[kBbSuf + l] = suf;
         rec[kBbPre + l] = pre;
         rec[kBbBeta + l] = bl;
