@@ -45,23 +45,23 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "1c4dd4711cefdc62",
+    "sources_sha256_16": "66076bacab75bcf5",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 968.1e6, "bwd_write_bytes": 519.0e6,
-    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 485.0e6,
+    "bwd_read_bytes": 973.0e6, "bwd_write_bytes": 496.0e6,
+    "fwd_read_bytes": 162.4e6, "fwd_write_bytes": 457.4e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 4.4, "valu_busy_pct": 17.1, "avg_us": 44.4},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.8, "valu_busy_pct": 48.2,
-                                    "avg_us": 163.8},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 4.7, "valu_busy_pct": 18.2, "avg_us": 43.4},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.6, "valu_busy_pct": 48.0,
-                                    "avg_us": 174.5},
-        "chunk_kernel": {"mfma_busy_pct": 20.8, "valu_busy_pct": 32.8, "avg_us": 257.9},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 4.6, "valu_busy_pct": 18.3, "avg_us": 43.4},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 49.1,
+                                    "avg_us": 171.0},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 4.8, "valu_busy_pct": 18.9, "avg_us": 42.4},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.3,
+                                    "avg_us": 181.3},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 23.7, "valu_busy_pct": 39.6, "avg_us": 240.2},
     },
 }
-BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_kernel")
+BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
 FWD_KERNELS = ("prep_kernel<fwd>", "fwd_chunked_bf16_kernel")
 
 
@@ -72,7 +72,7 @@ def pipe_busy(names):
     return {"mfma_busy_pct": sum(k["mfma_busy_pct"] * k["avg_us"] for k in ks) / t,
             "valu_busy_pct": sum(k["valu_busy_pct"] * k["avg_us"] for k in ks) / t}
 PROFILED_SOURCES = ("gdr_api.hip", "gdr_device.h", "gdr_internal.h", "gdr_chunked_sweep.hip",
-                    "gdr_chunk.hip")
+                    "gdr_chunk.hip", "gdr_chunk_bf16.hip")
 
 
 def sources_digest(files=PROFILED_SOURCES):
@@ -514,6 +514,8 @@ def main():
     bwd_tf = bwd_flops / (bwd_ms * 1e-3) / 1e12
     # the bf16-product sweep kernels take bf16 inputs with Dk % 8 == 0 and Dv % 4 == 0
     sfx = "_bf16" if (args.dtype == "bf16" and Dk % 8 == 0 and Dv % 4 == 0) else ""
+    chunk_name = ("chunk_bf16_kernel" if (args.dtype == "bf16" and Dk % 8 == 0 and Dv % 8 == 0
+                                          and 48 < Dk <= 192) else "chunk_kernel")
     all_tf = (FLOPS_FWD + FLOPS_BWD) * elems / (ms * 1e-3) / 1e12
     esz = 2 if args.dtype == "bf16" else 4
     fwd_bytes, bwd_bytes = algorithmic_bytes(B, T, Hk, Hv, Dk, Dv, esz, st.nch)
@@ -554,7 +556,7 @@ def main():
         # flops (15 per state element per step), not the issued piece
         # products.
         "roofline": {"bound": "mfma", "kernel": f"gdr_backward (prep_kernel<bwd>, "
-                     f"bwd_chunked{sfx}_kernel, chunk_kernel)",
+                     f"bwd_chunked{sfx}_kernel, {chunk_name})",
                      "achieved": bwd_tf, "peak": FP32_PEAK_TF,
                      "unit": "TFLOP/s", "frac": bwd_tf / FP32_PEAK_TF,
                      "flops_basis": "useful fp32-equivalent, 15*B*T*Hv*Dv*Dk per call",

@@ -38,6 +38,11 @@
 // Dv rows per block, with the next block fetched into registers while the
 // current one is multiplied.  With bf16 inputs (BFP below) the same passes
 // run on bf16 MFMA over exact three-piece splits of the fp32 operands.
+//
+// bf16 inputs whose Dk and Dv are multiples of 8 with 48 < Dk <= 192 take the
+// eight-wave form of this computation instead (chunk_bf16_kernel,
+// gdr_chunk_bf16.hip); this file keeps fp32 inputs, the other bf16 shapes and
+// Dk above 192.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -1091,8 +1096,9 @@ hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
   const size_t lds = sizeof(float) * CL<JT>::SIZE;
   auto kern = chunk_kernel<TIn, JT, VEC, false>;
   // bf16 products: dy rows in 8-element blocks, k, q rows in 8-element
-  // groups (the 16-byte loads of the q, k stages)
-  if constexpr (std::is_same<TIn, gdr::bf16>::value && VEC && CL<JT>::PC == 64)
+  // groups (the 16-byte loads of the q, k stages); up to Dk = 192 such shapes
+  // go to chunk_bf16_kernel
+  if constexpr (std::is_same<TIn, gdr::bf16>::value && VEC && CL<JT>::PC == 64 && JT > 12)
     if (a.Dv % 8 == 0 && a.Dk % 8 == 0) kern = chunk_kernel<TIn, JT, VEC, true>;
   // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
   // launch error below.
@@ -1127,6 +1133,7 @@ hipError_t chunk_dispatch(const ChunkArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s) {
+  if (bf16 && chunk_bf16_ok(a)) return launch_chunk_bf16(a, s);
   return bf16 ? chunk_dispatch<gdr::bf16>(a, s) : chunk_dispatch<float>(a, s);
 }
 

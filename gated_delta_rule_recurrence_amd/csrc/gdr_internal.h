@@ -126,5 +126,9 @@ hipError_t launch_bwd_sweep_bf16(const BwdSweepArgs& a, int num_cu, hipStream_t 
 // Compute units of the current device (cached per device).
 int device_cu_count();
 hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s);
+// The eight-wave chunk kernel for bf16 inputs (gdr_chunk_bf16.hip): whether it
+// takes the shape (Dk, Dv multiples of 8, 48 < Dk <= 192), and its launch.
+bool chunk_bf16_ok(const ChunkArgs& a);
+hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s);
 
 }  // namespace gdr

@@ -384,7 +384,8 @@ def test_rows_per_lane_variants(cuda, B, dtype):
 
 
 @pytest.mark.parametrize("dims", [(72, 30), (68, 40), (136, 24), (192, 40), (64, 36),
-                                  (192, 20)])
+                                  (192, 20), (104, 48), (128, 64), (56, 16), (200, 40),
+                                  (256, 64)])
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_bf16_dims(cuda, dims, chunk):
     """bf16 inputs at the edges of the bf16-product kernels' shape conditions
@@ -392,7 +393,10 @@ def test_bf16_dims(cuda, dims, chunk):
     8-element blocks for the chunk-parallel part): Dk=72 with Dv=30 and Dk=68
     take the fp32-operand kernels, Dk=136 pads a 192-column tile, Dv=40 leaves
     a short last 32-row block, Dv=36 and Dv=20 pair the bf16-product sweeps
-    with the fp32-operand chunk kernel; T=70 leaves a short last chunk."""
+    with the fp32-operand chunk kernel; Dk=104 and 128 (128-column tiles) and
+    56 (a 64-column tile) cover the other widths of the eight-wave chunk
+    kernel, Dk=200 and 256 (per-step sweeps) the four-wave chunk kernel's
+    bf16 products; T=70 leaves a short last chunk."""
     Dk, Dv = dims
     p = inputs.draw(1, 70, 2, 4, Dk, Dv, seed=23, normalised=True, S0_std=0.2,
                     dST_std=1.0, dtype="bf16")
