@@ -506,14 +506,4 @@ int device_cu_count() {
   return n;
 }
 
-hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s) {
-  const int cu = device_cu_count();
-  return bf16 ? launch_fwd_sweep_bf16(a, cu, s) : launch_fwd_sweep_f32(a, cu, s);
-}
-
-hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s) {
-  const int cu = device_cu_count();
-  return bf16 ? launch_bwd_sweep_bf16(a, cu, s) : launch_bwd_sweep_f32(a, cu, s);
-}
-
 }  // namespace gdr

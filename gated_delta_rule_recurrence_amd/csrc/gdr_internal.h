@@ -117,12 +117,6 @@ hipError_t launch_decode(const FwdSweepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_fwd_sweep(const FwdSweepArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s);
 
-// per-dtype instantiations (gdr_sweep_{fwd,bwd}_{f32,bf16}.hip)
-hipError_t launch_fwd_sweep_f32(const FwdSweepArgs& a, int num_cu, hipStream_t s);
-hipError_t launch_fwd_sweep_bf16(const FwdSweepArgs& a, int num_cu, hipStream_t s);
-hipError_t launch_bwd_sweep_f32(const BwdSweepArgs& a, int num_cu, hipStream_t s);
-hipError_t launch_bwd_sweep_bf16(const BwdSweepArgs& a, int num_cu, hipStream_t s);
-
 // Compute units of the current device (cached per device).
 int device_cu_count();
 hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s);
