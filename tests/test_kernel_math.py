@@ -13,7 +13,9 @@ kernels' own definitions (gdr_device.h, gdr_chunked_sweep.hip):
   row) equals numpy's inverse;
 * the LDS layouts: the step permutation of the chunked sweeps is a
   permutation, and the swizzled bf16 tiles read by ds_read_b64_tr_b16 put
-  the 32 lanes of each half-wave on 64 distinct banks.
+  the 32 lanes of each half-wave on 64 distinct banks; the step planes of
+  the eight-wave chunk kernel (gdr_chunk_bf16.hip) are staged once per
+  element and written and read without bank conflicts.
 """
 import numpy as np
 import pytest
@@ -339,3 +341,51 @@ def test_state_piece_reads_conflict_free():
                     addr.append(j * 32 + 4 * (cb ^ p_swz(j)))
                 for banks in _half_wave_banks(addr):
                     assert len(set(banks)) == 64, (k0, n0, second)
+
+
+def step_of(x):
+    """Step staged by thread x of the eight-wave chunk kernel
+    (gdr_chunk_bf16.hip): half-wave h takes steps c, c + 4, c + 8, c + 12."""
+    grp = x >> 5
+    return 16 * (grp >> 2) + (grp & 3) + 4 * ((x >> 3) & 3)
+
+
+def test_step_plane_shares_cover_the_block():
+    """The 512 threads stage every (step, 4-row quad) of a 64-step x 32-row
+    block exactly once."""
+    cells = sorted((step_of(x), x & 7) for x in range(512))
+    assert cells == [(t, q) for t in range(64) for q in range(8)]
+
+
+def test_step_plane_writes_conflict_free():
+    """The 8-byte piece writes of the step planes ([64][40] bf16, element
+    (t, 4 q)) of each half-wave cover the 64 banks once; four consecutive
+    steps (the plain thread order) would not."""
+    ys = 40
+
+    def banks(steps_quads):
+        b = []
+        for t, q in steps_quads:
+            w = (2 * (t * ys + 4 * q)) // 4
+            b += [w % 64, (w + 1) % 64]
+        return b
+
+    for h in range(16):
+        xs = range(32 * h, 32 * h + 32)
+        assert len(set(banks([(step_of(x), x & 7) for x in xs]))) == 64, h
+    plain = banks([(x >> 3, x & 7) for x in range(32)])
+    assert len(set(plain)) < 64
+
+
+def test_step_plane_reads_conflict_free():
+    """The 16-byte operand reads of the step planes: lane l reads row
+    tw + l % 16, bf16 columns 8 (l / 16) ..; the 16 lanes of each quarter
+    (one column block) fall on 64 distinct banks."""
+    ys = 40
+    for tw in (0, 16, 32, 48):
+        for lq in range(4):
+            b = []
+            for lr in range(16):
+                w = (2 * ((tw + lr) * ys + 8 * lq)) // 4
+                b += [(w + i) % 64 for i in range(4)]
+            assert len(set(b)) == 64, (tw, lq)
