@@ -52,7 +52,6 @@
 namespace gdr {
 namespace {
 
-constexpr int kThreads = 256;    // prep workgroup
 constexpr int kSwThreads = 512;  // sweep workgroup: eight waves, two per SIMD
 constexpr int kN = 64;
 constexpr int kNP = kN + 1;   // row stride of the Gram matrices in the prep
@@ -98,12 +97,13 @@ static_assert(kPbBeta + kN <= kPrSink && kBbBeta + kN <= kPrSink &&
 // the 16 bytes of row 16 tb + l % 16, columns 32 ks + 8 (l / 16) .. +7; block
 // b = 2 tb + ks starts at float (3 b * 64 + l) * 4.  The two blocks past the
 // diagonal (lower triangle: tb < 2, ks = 1; UPPER: tb >= 2, ks = 0) are zero;
-// they are not written, and the readers skip them (pieces_from_record).
-template <bool UPPER, typename Elem>
+// they are not written, and the readers skip them (pieces_from_record).  The
+// other six are numbered 0..5 in record order; this writes blocks I0..I1-1.
+template <bool UPPER, int I0 = 0, int I1 = 6, typename Elem>
 __device__ __forceinline__ void pieces_to_record(float* __restrict__ dst, int l, Elem elem) {
   const int lr = l & 15, lq = l >> 4;
 #pragma unroll 2
-  for (int i = 0; i < 6; ++i) {
+  for (int i = I0; i < I1; ++i) {
     const int b = UPPER ? (i < 4 ? i : 2 * i - 3) : (i < 2 ? 2 * i : i + 2);
     const int t = 16 * (b >> 1) + lr, s0 = 32 * (b & 1) + 8 * lq;
     f4 x, y;
@@ -169,12 +169,13 @@ __device__ __forceinline__ void load_frags(const float* __restrict__ m, int tb, 
 }
 
 // Writes a matrix held in LDS (element (t, r) at src[t * ld + r]) to a record
-// in the order above; lane l writes block (tb, x) of itself.
+// in the order above; lane l writes block (tb, x) = bx of itself, for bx in
+// [bx0, bx1).
 __device__ __forceinline__ void store_frags(const float* src, int ld, float* __restrict__ m,
-                                            int l) {
+                                            int l, int bx0 = 0, int bx1 = 16) {
   const int lr = l & 15, lq = l >> 4;
 #pragma unroll 4
-  for (int bx = 0; bx < 16; ++bx) {
+  for (int bx = bx0; bx < bx1; ++bx) {
     const int tb = bx >> 2, x = bx & 3, t = 16 * tb + lr;
     f4 v;
 #pragma unroll
@@ -270,29 +271,35 @@ __device__ __forceinline__ void invert_unit_triangular(float* G, int l) {
 }
 
 // ---------------------------------------------------------------- prep ----
-// grid (nch, Hk, B).  MODE kPrepFwd / kPrepBwd: four waves, wave w forms
-// the forward (reverse) records of value heads w, w + 4, ... of the kv head.
-// kPrepBoth: eight waves, two per SIMD, waves 0-3 the forward and waves 4-7
-// the reverse records of the same heads (the Gram matrices are formed once
-// for both, and the second wave of each SIMD hides the first one's
-// latencies); the backward's replay uses it.
+// grid (nch, Hk, B), eight waves (two per SIMD).  MODE kPrepFwd / kPrepBwd:
+// the forward (reverse) records of value heads wh, wh + 4, ... of the kv head,
+// each formed by the two waves wh and wh + 4 together: they build Gam as two
+// running products (rows 63..32, rows 31..0), split the M (Mq) record, then
+// wave wh forms A (Bm) and its inverse, and they split the T (Tb) record
+// (three barriers per head).  kPrepBoth: waves 0-3 the forward and waves 4-7
+// the reverse records of the same heads, each wave every step of its head
+// alone (the Gram matrices formed once for both); the backward's replay uses
+// it.  Every record element takes the same operations in every mode, so the
+// records are bitwise the same whichever launch forms them.
 constexpr int kPrepFwd = 0, kPrepBwd = 1, kPrepBoth = 2;
+constexpr int kPrepThreads = 512;
 
 // QK (q_t . k_r) and KK (k_t . k_r) in one [kN][kNP] matrix: QK on and below
 // the diagonal, KK above it.  The records use QK[t][r] only for r <= t, and
 // KK (symmetric) only off the diagonal, read as KK[min][max].
 __device__ __forceinline__ int qk_at(int t, int r) { return t * kNP + r; }  // r <= t
 
-template <int NW>
+// LDS of the prep: NG per-head matrices [kN][kGP] and their beta vectors,
+// then the QK / KK matrix; the q, k stages alias the per-head arrays.
+template <int NG>
 struct PL {
   static constexpr int QS = 0, KS = 64 * kN;          // q, k stage [16][kN][4]
-  static constexpr int GW = 0;                         // NW x [kN][kGP] (alias)
-  static constexpr int VB = NW * kN * kGP;             // NW x beta[kN]
-  static constexpr int VS = VB + NW * kN;              // NW x g[kN]
-  static constexpr int QK = VS + NW * kN;              // QK / KK [kN][kNP]
+  static constexpr int GW = 0;                         // NG x [kN][kGP] (alias)
+  static constexpr int VB = NG * kN * kGP;             // NG x beta[kN]
+  static constexpr int QK = VB + NG * kN;              // QK / KK [kN][kNP]
   static constexpr int SIZE = QK + kN * kNP;
-  static_assert(2 * 64 * kN <= VB, "stage fits the per-wave arrays");
-  // bf16 inputs: q, k rows as bf16 [kN][KGS] (alias the per-wave arrays);
+  static_assert(2 * 64 * kN <= VB, "stage fits the per-head arrays");
+  // bf16 inputs: q, k rows as bf16 [kN][KGS] (alias the per-head arrays);
   // the row stride an odd number of 16-byte units, so the 16-byte operand
   // reads of 16 rows at one column group hit distinct banks
   static constexpr int KGS = 16 * kMaxJT + 8;
@@ -302,11 +309,11 @@ struct PL {
 };
 
 template <typename TIn, int MODE, bool VEC>
-__global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) void prep_kernel(
+__global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     ChunkedSweepShape a, float* __restrict__ prep_f, float* __restrict__ prep_b) {
-  constexpr int NW = MODE == kPrepBoth ? 8 : 4;
-  constexpr int NTH = 64 * NW;
-  using L = PL<NW>;
+  constexpr bool SPLIT = MODE != kPrepBoth;  // two waves per value head
+  constexpr int NTH = kPrepThreads;
+  using L = PL<SPLIT ? 4 : 8>;
   extern __shared__ __align__(16) float sm[];
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -321,9 +328,13 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const int tw = 16 * (w & 3);
-  // this wave's first value head, and which records it forms
+  const int half = w >> 2;  // this wave's Gram column tiles: 2 half, 2 half + 1
+  // this wave's first value head, which records it forms, and (SPLIT) its
+  // part of them: r0, the first wave of the pair, r1 the second (one wave
+  // does both in kPrepBoth)
   const int wh = w & 3;
   const bool bwd = MODE == kPrepBwd || (MODE == kPrepBoth && w >= 4);
+  const bool r0 = !SPLIT || w < 4, r1 = !SPLIT || w >= 4;
 
   // g, beta of this wave's first value head, issued before the k, q loads
   // (index clamped into the tensors; masked where used)
@@ -333,8 +344,11 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
   TIn g_raw = g[gb_index(wh < rep ? wh : 0)], b_raw = beta[gb_index(wh < rep ? wh : 0)];
 
   // ---- QK[t][r] = q_t . k_r, KK[t][r] = k_t . k_r (MFMA over Dk) ----------
-  // rows 16 w .. of both by waves 0-3 (the other waves only stage)
+  // wave w: rows 16 (w % 4) .., column tiles 2 half, 2 half + 1 of both
   constexpr bool kBf16 = std::is_same<TIn, bf16>::value && VEC;
+  f4 acc[4];  // QK tiles, then KK tiles
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
   if (kBf16 && Dk % 8 == 0) {
     // bf16 k, q: the rows staged as bf16 and multiplied on bf16 MFMA (the
     // products of two bf16 values are exact in fp32, as in the fp32 path)
@@ -373,35 +387,21 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
       }
     }
     __syncthreads();
-    f4 acc[8];
+    for (int ks = 0; 32 * ks < Dk; ++ks) {
+      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
+      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
+      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-    if (w < 4) {
-      for (int ks = 0; 32 * ks < Dk; ++ks) {
-        const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
-        const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
-        const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const uint4 bk =
-              *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
-          acc[tb] = mfma_bf16(aq, bk, acc[tb]);
-          acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
-        }
+      for (int x = 0; x < 2; ++x) {
+        const int tb = 2 * half + x;
+        const uint4 bk =
+            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
+        acc[x] = mfma_bf16(aq, bk, acc[x]);
+        acc[2 + x] = mfma_bf16(ak, bk, acc[2 + x]);
       }
     }
-    __syncthreads();  // the stage aliases the per-wave arrays
-    if (w < 4) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = tw + 4 * lq + v, j = 16 * tb + lr;
-          sm[L::QK + i * kNP + j] = j <= i ? acc[tb][v] : acc[4 + tb][v];
-        }
-    }
-    __syncthreads();
-  } else   {
+    __syncthreads();  // the stage aliases the per-head arrays
+  } else {
     constexpr int NB = kMaxJT / 4, NU = 4 * 256 / NTH;
     Quad<TIn, VEC> rq[NB][NU], rk[NB][NU];
     uint64_t msk = 0;
@@ -417,9 +417,6 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
         rk[jb][u].load(k, o, ok, Dk - j);
         msk |= (uint64_t)Quad<TIn, VEC>::mask(ok, Dk - j) << (4 * (NU * jb + u));
       }
-    f4 acc[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
       if (64 * jb >= Dk) break;
@@ -432,152 +429,193 @@ __global__ __launch_bounds__(MODE == kPrepBoth ? 2 * kThreads : kThreads, 1) voi
         *reinterpret_cast<f4*>(sm + L::KS + (jq * kN + s) * 4) = rk[jb][u].get(mu);
       }
       __syncthreads();
-      if (w < 4) {
 #pragma unroll 2
-        for (int ks = 0; ks < 16; ++ks) {
-          const int fw = ((ks * kN + tw + lr) << 2) + lq;
-          const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
+      for (int ks = 0; ks < 16; ++ks) {
+        const int fw = ((ks * kN + tw + lr) << 2) + lq;
+        const float aq = sm[L::QS + fw], ak = sm[L::KS + fw];
 #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
-            acc[tb] = mfma(aq, bk, acc[tb]);
-            acc[4 + tb] = mfma(ak, bk, acc[4 + tb]);
-          }
+        for (int x = 0; x < 2; ++x) {
+          const int tb = 2 * half + x;
+          const float bk = sm[L::KS + ((ks * kN + 16 * tb + lr) << 2) + lq];
+          acc[x] = mfma(aq, bk, acc[x]);
+          acc[2 + x] = mfma(ak, bk, acc[2 + x]);
         }
       }
       __syncthreads();
     }
-    if (w < 4) {
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = tw + 4 * lq + v, j = 16 * tb + lr;
-          sm[L::QK + i * kNP + j] = j <= i ? acc[tb][v] : acc[4 + tb][v];
-        }
-    }
-    __syncthreads();
   }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = tw + 4 * lq + v, j = 16 * (2 * half + x) + lr;
+      sm[L::QK + i * kNP + j] = j <= i ? acc[x][v] : acc[2 + x][v];
+    }
+  __syncthreads();
 
-  // ---- per value head (one wave each; no barriers below) ------------------
-  float* G = sm + L::GW + w * kN * kGP;  // [kN][kGP] per wave
-  float* vb = sm + L::VB + w * kN;       // beta_t
-  float* vg = sm + L::VS + w * kN;       // g_t
-  const float* QK = sm + L::QK;          // QK on and below the diagonal, KK above
-  for (int hh = wh; hh < rep; hh += 4) {
-    const int h = hk * rep + hh;
+  // ---- per value head ------------------------------------------------------
+  // (SPLIT: the two waves of a head share its matrix G, and every wave runs
+  // the same number of passes, so that the barriers below match up)
+  float* G = sm + L::GW + (SPLIT ? wh : w) * kN * kGP;  // [kN][kGP] per head
+  float* vb = sm + L::VB + (SPLIT ? wh : w) * kN;        // beta_t
+  const float* QK = sm + L::QK;  // QK on and below the diagonal, KK above
+  // bf16 inputs in 8-element groups: the bf16-product sweeps read the
+  // matrices as bf16 pieces
+  const bool pieces = bf16_products(kBf16, Dk, a.Dv);
+  for (int h0 = 0; h0 < rep; h0 += 4) {
+    // the lane indices again, from an opaque copy of the thread id: otherwise
+    // the compiler evaluates the per-row lane masks of the loops below ahead
+    // of the Gram phase and spills them (a lane read back per use)
+    int lane = tid & 63;
+    asm volatile("" : "+v"(lane));
+    const int l = lane, lr = l & 15, lq = l >> 4;
+    const int hh = h0 + wh;
+    const bool act = hh < rep;
+    const int h = hk * rep + (act ? hh : 0);
     float* __restrict__ rec =
         (bwd ? prep_b : prep_f) + (((int64_t)b * Hv + h) * a.nch + jc) * kChunkPrepStride;
-    if (hh != wh) {
-      g_raw = g[gb_index(hh)];
-      b_raw = beta[gb_index(hh)];
+    if (h0 > 0) {
+      g_raw = g[gb_index(act ? hh : 0)];
+      b_raw = beta[gb_index(act ? hh : 0)];
     }
     // an identity step (mask byte 0) has g = 1, beta = 0
     const bool skip = l < n && skipped(a.mask, b, T, t0 + l);
     const float gl = l < n && !skip ? decay_of(to_f32(g_raw), a.log_g) : 1.f;
     const float bl = l < n && !skip ? to_f32(b_raw) : 0.f;
-    vb[l] = bl;
-    vg[l] = gl;
-    // Gam(r,t] (lane l <-> t = l) as a running product down the rows:
-    // Gam(t-1,t] = g_t, Gam(r,t] = g_{r+1} Gam(r+1,t]; 1 on the diagonal and
-    // 0 below it (rows r > t).  G[r][t] holds it.
-    // (g_{r+1} read from lane r + 1, so the loop holds only LDS stores)
-    float p = 1.f;
+    // Gam(r,t] (lane l <-> t = l), held in G[r][t]: 1 on the diagonal, 0
+    // below it (rows r > t), and above it two running products down the rows,
+    // Gam(r,t] = g_{r+1} Gam(r+1,t]: rows 63..32 from 1, rows 31..0 from
+    // Gam(32,t] (a product scan over the lanes).  g_{r+1} is read from lane
+    // r + 1, so the loops hold only LDS stores.
+    auto gam_rows = [&](int r_hi, int r_lo, float p) __attribute__((always_inline)) {
 #pragma unroll 8
-    for (int r = kN - 1; r >= 0; --r) {
-      const float gr =
-          r + 1 < kN ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), r + 1)) : 1.f;
-      p = r < l ? p * gr : p;
-      G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
-    }
-    const float pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * p;  // Gam(-1, l] = g_0 Gam(0, l]
-    const float suf = l < n ? G[l * kGP + n - 1] : 0.f;  // Gam(l, n-1]
-    // bf16 inputs in 8-element groups: the bf16-product sweeps read the
-    // matrices as bf16 pieces
-    const bool pieces = bf16_products(kBf16, Dk, a.Dv);
-    if (!bwd) {
-      // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
-      if (pieces) {
-        pieces_to_record<false>(rec + kBrM, l, [&](int t, int s) {
-          return s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
-        });
-      } else
-#pragma unroll 2
-      for (int bx = 0; bx < 16; ++bx) {
-        const int t = 16 * (bx >> 2) + lr;
-        f4 m4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = rstep(4 * (bx & 3) + e, lq);
-          m4[e] = s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
-        }
-        *reinterpret_cast<f4*>(rec + kPrM + (bx * 64 + l) * 4) = m4;
+      for (int r = r_hi; r >= r_lo; --r) {
+        const float gr =
+            r + 1 < kN ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), r + 1)) : 1.f;
+        p = r < l ? p * gr : p;
+        G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
       }
-      // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r):
-      // all of the lane's operands loaded first, then the stores
-      {
+      return p;
+    };
+    float pre = 0.f;  // Gam(-1, l] = g_0 Gam(0, l]
+    if (act && r1) (void)gam_rows(kN - 1, 32, 1.f);
+    if (act && r0) {
+      const float p = gam_rows(31, 0, wave_prefix_product(l > 32 ? gl : 1.f));
+      pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * p;
+      vb[l] = bl;
+    }
+    if (SPLIT) __syncthreads();
+
+    // the M (Mq) record, its blocks split between the two waves; suf is read
+    // before Bm replaces Gam above the diagonal
+    float suf = 0.f;  // Gam(l, n-1]
+    if (act && r0) suf = l < n ? G[l * kGP + n - 1] : 0.f;
+    if (act) {
+      if (!bwd) {
+        // M[t][s] = Gam(s,t] QK[t][s] beta_s, s <= t, in fragment order
+        auto m_el = [&](int t, int s) __attribute__((always_inline)) {
+          return s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
+        };
+        if (pieces) {
+          if (!SPLIT) pieces_to_record<false>(rec + kBrM, l, m_el);
+          else if (r0) pieces_to_record<false, 0, 3>(rec + kBrM, l, m_el);
+          else pieces_to_record<false, 3, 6>(rec + kBrM, l, m_el);
+        } else {
+#pragma unroll 2
+          for (int bx = SPLIT && r1 ? 8 : 0; bx < (SPLIT && r0 ? 8 : 16); ++bx) {
+            const int t = 16 * (bx >> 2) + lr;
+            f4 m4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m4[e] = m_el(t, rstep(4 * (bx & 3) + e, lq));
+            *reinterpret_cast<f4*>(rec + kPrM + (bx * 64 + l) * 4) = m4;
+          }
+        }
+      } else {
+        // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
+        auto m_el = [&](int t, int s) __attribute__((always_inline)) {
+          return s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
+        };
+        if (pieces) {
+          if (!SPLIT) pieces_to_record<true>(rec + kBbM, l, m_el);
+          else if (r0) pieces_to_record<true, 0, 3>(rec + kBbM, l, m_el);
+          else pieces_to_record<true, 3, 6>(rec + kBbM, l, m_el);
+        } else {
+#pragma unroll 2
+          for (int bx = SPLIT && r1 ? 8 : 0; bx < (SPLIT && r0 ? 8 : 16); ++bx) {
+            const int t = 16 * (bx >> 2) + lr;
+            f4 m4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) m4[e] = m_el(t, rstep(4 * (bx & 3) + e, lq));
+            *reinterpret_cast<f4*>(rec + kPbM + (bx * 64 + l) * 4) = m4;
+          }
+        }
+      }
+    }
+    if (SPLIT) __syncthreads();
+
+    // A (Bm) in place and its inverse, by the first wave
+    if (act && r0) {
+      if (!bwd) {
+        // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r):
+        // all of the lane's operands loaded first, then the stores
         float av[kN];
 #pragma unroll
         for (int t = 1; t < kN; ++t) av[t] = G[l * kGP + t] * QK[l * kNP + t] * bl;  // KK[l][t], l < t
 #pragma unroll
         for (int t = 1; t < kN; ++t)
           if (l < t) G[t * kGP + l] = av[t];
-      }
-      // T = (I + A)^-1 in place of A
-      invert_unit_triangular<false>(G, l);
-      if (pieces) {
-        pieces_to_record<false>(rec + kBrT, l, [&](int t, int s) { return G[t * kGP + s]; });
-        rec[kBrGam + l] = pre;
-        rec[kBrKs + l] = bl * suf;
-        if (l == n - 1) rec[kBrGend] = pre;
+        // T = (I + A)^-1 in place of A
+        invert_unit_triangular<false>(G, l);
       } else {
-        store_frags(G, kGP, rec + kPrT, l);
-        rec[kPrGam + l] = pre;
-        rec[kPrKs + l] = bl * suf;
-        if (l == n - 1) rec[kPrGend] = pre;
-      }
-    } else {
-      // Mq[t][s] = Gam(t,s] QK[s][t], s >= t, in fragment order
-      if (pieces) {
-        pieces_to_record<true>(rec + kBbM, l, [&](int t, int s) {
-          return s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
-        });
-      } else
-#pragma unroll 2
-      for (int bx = 0; bx < 16; ++bx) {
-        const int t = 16 * (bx >> 2) + lr;
-        f4 m4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int s = rstep(4 * (bx & 3) + e, lq);
-          m4[e] = s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
-        }
-        *reinterpret_cast<f4*>(rec + kPbM + (bx * 64 + l) * 4) = m4;
-      }
-      // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
-      // diagonal (lane l <-> s)
-      {
+        // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
+        // diagonal (lane l <-> s)
         float bv[kN];  // the lane's operands first, then the updates
 #pragma unroll
         for (int t = 0; t < kN - 1; ++t) bv[t] = bl * QK[t * kNP + l] * G[t * kGP + l];  // KK[t][l], t < l
 #pragma unroll
         for (int t = 0; t < kN - 1; ++t)
           if (l > t) G[t * kGP + l] = bv[t];
-      }
-      // Tb = (I + Bm)^-1 in place of Bm
-      invert_unit_triangular<true>(G, l);
-      if (pieces) {
-        pieces_to_record<true>(rec + kBbT, l, [&](int t, int s) { return G[t * kGP + s]; });
-        rec[kBbSuf + l] = suf;
-        rec[kBbPre + l] = pre;
-        rec[kBbBeta + l] = bl;
-      } else {
-        store_frags(G, kGP, rec + kPbT, l);
-        rec[kPbSuf + l] = suf;
-        rec[kPbPre + l] = pre;
-        rec[kPbBeta + l] = bl;
+        // Tb = (I + Bm)^-1 in place of Bm
+        invert_unit_triangular<true>(G, l);
       }
     }
+    if (SPLIT) __syncthreads();
+
+    // the T (Tb) record, its blocks split between the two waves, and the
+    // step vectors by the first
+    if (act) {
+      auto t_el = [&](int t, int s) __attribute__((always_inline)) { return G[t * kGP + s]; };
+      if (!bwd) {
+        if (pieces) {
+          if (!SPLIT) pieces_to_record<false>(rec + kBrT, l, t_el);
+          else if (r0) pieces_to_record<false, 0, 3>(rec + kBrT, l, t_el);
+          else pieces_to_record<false, 3, 6>(rec + kBrT, l, t_el);
+        } else {
+          store_frags(G, kGP, rec + kPrT, l, SPLIT && r1 ? 8 : 0, SPLIT && r0 ? 8 : 16);
+        }
+        if (r0) {
+          rec[(pieces ? kBrGam : kPrGam) + l] = pre;
+          rec[(pieces ? kBrKs : kPrKs) + l] = bl * suf;
+          if (l == n - 1) rec[pieces ? kBrGend : kPrGend] = pre;
+        }
+      } else {
+        if (pieces) {
+          if (!SPLIT) pieces_to_record<true>(rec + kBbT, l, t_el);
+          else if (r0) pieces_to_record<true, 0, 3>(rec + kBbT, l, t_el);
+          else pieces_to_record<true, 3, 6>(rec + kBbT, l, t_el);
+        } else {
+          store_frags(G, kGP, rec + kPbT, l, SPLIT && r1 ? 8 : 0, SPLIT && r0 ? 8 : 16);
+        }
+        if (r0) {
+          rec[(pieces ? kBbSuf : kPbSuf) + l] = suf;
+          rec[(pieces ? kBbPre : kPbPre) + l] = pre;
+          rec[(pieces ? kBbBeta : kPbBeta) + l] = bl;
+        }
+      }
+    }
+    // (the next head's Gam is written only after every wave has passed the
+    // barrier that follows its own Gam rows, which comes after these reads)
+    if (SPLIT) __syncthreads();
   }
 }
 
@@ -1866,12 +1904,14 @@ hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
 template <typename TIn, int MODE>
 hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep_f, float* prep_b,
                        hipStream_t s) {
-  constexpr int NW = MODE == kPrepBoth ? 8 : 4;
+  // per-head matrices: one per value head of a pass (two waves share it), or
+  // one per wave with both record sets
+  constexpr int NG = MODE == kPrepBoth ? 8 : 4;
   const dim3 grid(sh.nch, sh.Hk, sh.B);
-  const size_t lds = sizeof(float) * PL<NW>::SIZE;
+  const size_t lds = sizeof(float) * PL<NG>::SIZE;
   if (sh.Dk % 4 == 0)
-    return launch(prep_kernel<TIn, MODE, true>, grid, 64 * NW, lds, s, sh, prep_f, prep_b);
-  return launch(prep_kernel<TIn, MODE, false>, grid, 64 * NW, lds, s, sh, prep_f, prep_b);
+    return launch(prep_kernel<TIn, MODE, true>, grid, kPrepThreads, lds, s, sh, prep_f, prep_b);
+  return launch(prep_kernel<TIn, MODE, false>, grid, kPrepThreads, lds, s, sh, prep_f, prep_b);
 }
 
 template <typename TIn, bool BWD, typename Args>
