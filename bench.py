@@ -45,20 +45,20 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "2b7723702795e301",
+    "sources_sha256_16": "dc0f4bbfd31c5106",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 973.0e6, "bwd_write_bytes": 496.0e6,
-    "fwd_read_bytes": 162.4e6, "fwd_write_bytes": 457.4e6,
+    "bwd_read_bytes": 972.5e6, "bwd_write_bytes": 496.5e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 458.5e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 4.6, "valu_busy_pct": 18.3, "avg_us": 43.4},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 49.1,
-                                    "avg_us": 171.0},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 4.8, "valu_busy_pct": 18.9, "avg_us": 42.4},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.3,
-                                    "avg_us": 181.3},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 23.7, "valu_busy_pct": 39.6, "avg_us": 240.2},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.0, "valu_busy_pct": 18.7, "avg_us": 38.7},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.9, "valu_busy_pct": 48.4,
+                                    "avg_us": 172.6},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.8, "avg_us": 37.2},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.7, "valu_busy_pct": 48.4,
+                                    "avg_us": 182.7},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 23.6, "valu_busy_pct": 39.4, "avg_us": 240.8},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
