@@ -62,6 +62,8 @@ struct Sizes {
   int64_t rs_off;  // replay: the tile states
   int64_t re_off;  // replay: the residuals
   int64_t rp_off;  // replay: the forward prep records (chunked; else 0)
+  bool hsplit;     // the chunk kernel runs one workgroup per value head
+  int64_t hp_off;  // hsplit: the value heads' dq, dk terms
 };
 
 int check_shape(const gdr_shape* s, Sizes* z) {
@@ -124,12 +126,20 @@ int check_shape(const gdr_shape* s, Sizes* z) {
       if (!add_ok(r.rp_off, prep, &end)) return GDR_ERR_OVERFLOW;
     }
   }
-  r.ws_bytes = end;
   // element counts must also index as int64 inside the kernels
   int64_t qk;
   if (!mul_ok(s->B, s->T, &qk) || !mul_ok(qk, s->Hk, &qk) ||
       !mul_ok(qk, s->Dk, &qk))
     return GDR_ERR_OVERFLOW;
+  r.hsplit = gdr::chunk_head_split(s->B, s->Hk, s->Hv, s->Dk, s->Dv, r.L, r.ntiles,
+                                   s->dtype == GDR_BF16);
+  if (r.hsplit) {
+    int64_t pb;  // [2][Hv/Hk] x qk floats
+    if (!mul_ok(qk, 8 * (s->Hv / s->Hk), &pb)) return GDR_ERR_OVERFLOW;
+    r.hp_off = round_up256(end);
+    if (!add_ok(r.hp_off, pb, &end)) return GDR_ERR_OVERFLOW;
+  }
+  r.ws_bytes = end;
   if (z) *z = r;
   return GDR_OK;
 }
@@ -459,6 +469,7 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   c.dk = dk;
   c.dg = dg;
   c.dbeta = dbeta;
+  c.part = z.hsplit ? reinterpret_cast<float*>(ws + z.hp_off) : nullptr;
   err = gdr::launch_bwd_chunk(c, bf16, s);
   return err == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -125,8 +125,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
   const bf16* __restrict__ dy = static_cast<const bf16*>(a.dy);
 
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
-  const int jc = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int rep = Hv / Hk;
+  // all the value heads of kv head blockIdx.y, or (a.part) value head
+  // blockIdx.y alone, its dq, dk terms to a.part
+  const bool one_head = a.part != nullptr;
+  const int jc = blockIdx.x, b = blockIdx.z;
+  const int hk = one_head ? (int)blockIdx.y / rep : (int)blockIdx.y;
+  const int h_lo = one_head ? (int)blockIdx.y - hk * rep : 0;  // first value head (of the kv head)
+  const int nh = one_head ? 1 : rep;                          // value heads
   const int t0 = jc * a.L;
   const int n = min(a.L, T - t0);
   const int tid = threadIdx.x;
@@ -170,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
   // land, and the first blocks of the next pass or value head are in flight
   // while the current one finishes.
   const int nbk = (((Dv + kKB - 1) / kKB) + 1) & ~1;
-  const int nblk_all = rep * NJP * nbk;
+  const int nblk_all = nh * NJP * nbk;
   const int64_t tstride = (int64_t)Hv * Dv;
   struct Slot {
     Quad<float, true> s, h, c, e;
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
     const int rem = gbi - hb * (NJP * nbk);
     const int jp = rem / nbk;
     const int i0 = (rem - jp * nbk) * kKB;
-    const int hv = hk * rep + hb;
+    const int hv = hk * rep + h_lo + hb;
     const int64_t bh = (int64_t)b * Hv + hv;
     uint32_t m;
     {
@@ -328,9 +334,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
     }
   }
 
-  bf16 g_nx = g[gb_index(0)], b_nx = beta[gb_index(0)];
+  bf16 g_nx = g[gb_index(h_lo)], b_nx = beta[gb_index(h_lo)];
 
-  for (int hh = 0; hh < rep; ++hh) {
+  for (int hh = h_lo; hh < h_lo + nh; ++hh) {
     {  // lane indices re-derived per head from an opaque copy of the thread
        // id, so that the compiler does not hoist per-lane addresses out of
        // the loop (and spill them)
@@ -350,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
       sm[L::V_B + tid] = gb_ok && !gb_skip ? to_f32(b_nx) : 0.f;
     }
     {
-      const int hn = hh + 1 < rep ? hh + 1 : hh;  // (unconditional: clamped)
+      const int hn = hh + 1 < h_lo + nh ? hh + 1 : hh;  // (unconditional: clamped)
       g_nx = g[gb_index(hn)];
       b_nx = beta[gb_index(hn)];
     }
@@ -453,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
         kq[x].load(k, o, ok, 4);
         qkm |= Quad<bf16, true>::mask(ok, 4) << (4 * x);
       }
-      const int gbase = (hh * NJP + jp) * nbk;
+      const int gbase = ((hh - h_lo) * NJP + jp) * nbk;
       // nbk >= 2: a do-while keeps the loads in flight identical on every
       // path out of the loop (the waits for qq/kq then skip the ring's loads)
       int blk = 0;
@@ -757,21 +763,48 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
     wpass(w2_at, fk, dK);  // -W2
   }
   {
-    // columns 16 J + 4 lq .. +3 of step t: one 4-element store each
+    // columns 16 J + 4 lq .. +3 of step t: one 4-element store each (bf16,
+    // or the head's fp32 terms)
     const int t = tw + lr;
+    const int64_t nqk = (int64_t)a.B * T * Hk * Dk;
+    float* const pq = one_head ? a.part + (int64_t)h_lo * nqk : nullptr;
+    float* const pk = one_head ? a.part + (int64_t)(rep + h_lo) * nqk : nullptr;
     if (t < n) {
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
         const int j = 16 * jtile(u) + 4 * lq;
         if (j < Dk) {
-          *reinterpret_cast<uint2*>(static_cast<bf16*>(a.dq) + qk_index(t, j)) =
-              uint2{cvt_pk_bf16(dQ[u][0], dQ[u][1]), cvt_pk_bf16(dQ[u][2], dQ[u][3])};
-          *reinterpret_cast<uint2*>(static_cast<bf16*>(a.dk) + qk_index(t, j)) =
-              uint2{cvt_pk_bf16(dK[u][0], dK[u][1]), cvt_pk_bf16(dK[u][2], dK[u][3])};
+          const int64_t o = qk_index(t, j);
+          if (one_head) {
+            *reinterpret_cast<f4*>(pq + o) = dQ[u];
+            *reinterpret_cast<f4*>(pk + o) = dK[u];
+          } else {
+            *reinterpret_cast<uint2*>(static_cast<bf16*>(a.dq) + o) =
+                uint2{cvt_pk_bf16(dQ[u][0], dQ[u][1]), cvt_pk_bf16(dQ[u][2], dQ[u][3])};
+            *reinterpret_cast<uint2*>(static_cast<bf16*>(a.dk) + o) =
+                uint2{cvt_pk_bf16(dK[u][0], dK[u][1]), cvt_pk_bf16(dK[u][2], dK[u][3])};
+          }
         }
       }
     }
   }
+}
+
+// dq, dk = the sum of the value heads' terms (a.part), in ascending head
+// order, to bf16: thread i takes four consecutive elements of dq (i < n4) or
+// of dk.
+__global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__ part, int rep,
+                                                       int64_t n4, bf16* __restrict__ dq,
+                                                       bf16* __restrict__ dk) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= 2 * n4) return;
+  const bool second = i >= n4;
+  const int64_t e = 4 * (second ? i - n4 : i);
+  const float* __restrict__ p = part + (second ? (int64_t)rep * 4 * n4 : 0) + e;
+  f4 acc = *reinterpret_cast<const f4*>(p);
+  for (int r = 1; r < rep; ++r) acc += *reinterpret_cast<const f4*>(p + (int64_t)r * 4 * n4);
+  *reinterpret_cast<uint2*>((second ? dk : dq) + e) =
+      uint2{cvt_pk_bf16(acc[0], acc[1]), cvt_pk_bf16(acc[2], acc[3])};
 }
 
 template <int JT>
@@ -782,7 +815,14 @@ hipError_t launch_jt(const ChunkArgs& a, hipStream_t s) {
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  hipLaunchKernelGGL(kern, dim3(a.nch, a.Hk, a.B), dim3(kThreads), lds, s, a);
+  const int gy = a.part != nullptr ? a.Hv : a.Hk;
+  hipLaunchKernelGGL(kern, dim3(a.nch, gy, a.B), dim3(kThreads), lds, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.part == nullptr) return e;
+  const int64_t n4 = (int64_t)a.B * a.T * a.Hk * a.Dk / 4;  // Dk is a multiple of 8
+  const int64_t blocks = (2 * n4 + 255) / 256;
+  hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.part,
+                     a.Hv / a.Hk, n4, static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk));
   return hipGetLastError();
 }
 
@@ -790,6 +830,16 @@ hipError_t launch_jt(const ChunkArgs& a, hipStream_t s) {
 
 bool chunk_bf16_ok(const ChunkArgs& a) {
   return a.Dk % 8 == 0 && a.Dv % 8 == 0 && a.Dk > 48 && a.Dk <= 192 && a.L >= 1 && a.L <= kN;
+}
+
+// One workgroup per value head when the (chunk, kv head, batch row) grid has
+// at most 128 workgroups (half a 256-CU device or less) and 2 to 16 value
+// heads share a kv head.
+bool chunk_head_split(int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L,
+                      int64_t nch, bool bf16) {
+  const int64_t rep = Hv / Hk;
+  return bf16 && Dk % 8 == 0 && Dv % 8 == 0 && Dk > 48 && Dk <= 192 && L >= 1 && L <= kN &&
+         rep >= 2 && rep <= 16 && nch * Hk * B <= 128;
 }
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s) {
