@@ -45,20 +45,20 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "dc0f4bbfd31c5106",
+    "sources_sha256_16": "9a18ffa976b3a065",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 972.5e6, "bwd_write_bytes": 496.5e6,
-    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 458.5e6,
+    "bwd_read_bytes": 974.9e6, "bwd_write_bytes": 497.4e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 457.5e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.0, "valu_busy_pct": 18.7, "avg_us": 38.7},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.9, "valu_busy_pct": 48.4,
-                                    "avg_us": 172.6},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.8, "avg_us": 37.2},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.7, "valu_busy_pct": 48.4,
-                                    "avg_us": 182.7},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 23.6, "valu_busy_pct": 39.4, "avg_us": 240.8},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.1, "valu_busy_pct": 19.0, "avg_us": 38.3},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.2, "valu_busy_pct": 49.1,
+                                    "avg_us": 166.5},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.8, "avg_us": 36.6},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.3,
+                                    "avg_us": 178.7},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 22.1, "valu_busy_pct": 36.7, "avg_us": 235.5},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
