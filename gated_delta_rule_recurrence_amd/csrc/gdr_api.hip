@@ -62,8 +62,8 @@ struct Sizes {
   int64_t rs_off;  // replay: the tile states
   int64_t re_off;  // replay: the residuals
   int64_t rp_off;  // replay: the forward prep records (chunked; else 0)
-  bool hsplit;     // the chunk kernel runs one workgroup per value head
-  int64_t hp_off;  // hsplit: the value heads' dq, dk terms
+  int hpw;         // > 0: the chunk kernel gives a workgroup hpw value heads
+  int64_t hp_off;  // hpw > 0: the head groups' dq, dk terms
 };
 
 int check_shape(const gdr_shape* s, Sizes* z) {
@@ -131,11 +131,11 @@ int check_shape(const gdr_shape* s, Sizes* z) {
   if (!mul_ok(s->B, s->T, &qk) || !mul_ok(qk, s->Hk, &qk) ||
       !mul_ok(qk, s->Dk, &qk))
     return GDR_ERR_OVERFLOW;
-  r.hsplit = gdr::chunk_head_split(s->B, s->Hk, s->Hv, s->Dk, s->Dv, r.L, r.ntiles,
-                                   s->dtype == GDR_BF16);
-  if (r.hsplit) {
-    int64_t pb;  // [2][Hv/Hk] x qk floats
-    if (!mul_ok(qk, 8 * (s->Hv / s->Hk), &pb)) return GDR_ERR_OVERFLOW;
+  r.hpw = gdr::chunk_head_split(s->B, s->Hk, s->Hv, s->Dk, s->Dv, r.L, r.ntiles,
+                                s->dtype == GDR_BF16);
+  if (r.hpw > 0) {
+    int64_t pb;  // [2][Hv/Hk/hpw] x qk floats
+    if (!mul_ok(qk, 8 * (s->Hv / s->Hk / r.hpw), &pb)) return GDR_ERR_OVERFLOW;
     r.hp_off = round_up256(end);
     if (!add_ok(r.hp_off, pb, &end)) return GDR_ERR_OVERFLOW;
   }
@@ -469,7 +469,8 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   c.dk = dk;
   c.dg = dg;
   c.dbeta = dbeta;
-  c.part = z.hsplit ? reinterpret_cast<float*>(ws + z.hp_off) : nullptr;
+  c.part = z.hpw > 0 ? reinterpret_cast<float*>(ws + z.hp_off) : nullptr;
+  c.hpw = z.hpw;
   err = gdr::launch_bwd_chunk(c, bf16, s);
   return err == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }

@@ -126,13 +126,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
 
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk, Dv = a.Dv;
   const int rep = Hv / Hk;
-  // all the value heads of kv head blockIdx.y, or (a.part) value head
-  // blockIdx.y alone, its dq, dk terms to a.part
-  const bool one_head = a.part != nullptr;
+  // all the value heads of kv head blockIdx.y, or (a.part) the group
+  // blockIdx.y % ng of a.hpw of them, their dq, dk terms to a.part
+  const bool split = a.part != nullptr;
+  const int ng = split ? rep / a.hpw : 1;  // head groups per kv head
   const int jc = blockIdx.x, b = blockIdx.z;
-  const int hk = one_head ? (int)blockIdx.y / rep : (int)blockIdx.y;
-  const int h_lo = one_head ? (int)blockIdx.y - hk * rep : 0;  // first value head (of the kv head)
-  const int nh = one_head ? 1 : rep;                          // value heads
+  const int hk = (int)blockIdx.y / ng;
+  const int grp = (int)blockIdx.y - hk * ng;
+  const int nh = rep / ng;      // value heads of this workgroup
+  const int h_lo = grp * nh;    // the first (of the kv head)
   const int t0 = jc * a.L;
   const int n = min(a.L, T - t0);
   const int tid = threadIdx.x;
@@ -162,8 +164,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
   // the 80-byte row stride of the step planes their 8-byte writes then cover
   // the 64 banks once (four consecutive steps would overlap on 12 banks).
   auto step_of = [](int x) __attribute__((always_inline)) {
-    const int grp = x >> 5;
-    return 16 * (grp >> 2) + (grp & 3) + 4 * ((x >> 3) & 3);
+    const int q = x >> 5;
+    return 16 * (q >> 2) + (q & 3) + 4 * ((x >> 3) & 3);
   };
   int sr = tid >> 4, sc = tid & 15;
   int ys = step_of(tid), yq = tid & 7;
@@ -767,15 +769,15 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
     // or the head's fp32 terms)
     const int t = tw + lr;
     const int64_t nqk = (int64_t)a.B * T * Hk * Dk;
-    float* const pq = one_head ? a.part + (int64_t)h_lo * nqk : nullptr;
-    float* const pk = one_head ? a.part + (int64_t)(rep + h_lo) * nqk : nullptr;
+    float* const pq = split ? a.part + (int64_t)grp * nqk : nullptr;
+    float* const pk = split ? a.part + (int64_t)(ng + grp) * nqk : nullptr;
     if (t < n) {
 #pragma unroll
       for (int u = 0; u < NT; ++u) {
         const int j = 16 * jtile(u) + 4 * lq;
         if (j < Dk) {
           const int64_t o = qk_index(t, j);
-          if (one_head) {
+          if (split) {
             *reinterpret_cast<f4*>(pq + o) = dQ[u];
             *reinterpret_cast<f4*>(pk + o) = dK[u];
           } else {
@@ -790,19 +792,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_bf16_kernel(ChunkArgs a) {
   }
 }
 
-// dq, dk = the sum of the value heads' terms (a.part), in ascending head
+// dq, dk = the sum of the ng head groups' terms (a.part), in ascending group
 // order, to bf16: thread i takes four consecutive elements of dq (i < n4) or
 // of dk.
-__global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__ part, int rep,
+__global__ __launch_bounds__(256) void head_sum_kernel(const float* __restrict__ part, int ng,
                                                        int64_t n4, bf16* __restrict__ dq,
                                                        bf16* __restrict__ dk) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= 2 * n4) return;
   const bool second = i >= n4;
   const int64_t e = 4 * (second ? i - n4 : i);
-  const float* __restrict__ p = part + (second ? (int64_t)rep * 4 * n4 : 0) + e;
+  const float* __restrict__ p = part + (second ? (int64_t)ng * 4 * n4 : 0) + e;
   f4 acc = *reinterpret_cast<const f4*>(p);
-  for (int r = 1; r < rep; ++r) acc += *reinterpret_cast<const f4*>(p + (int64_t)r * 4 * n4);
+  for (int r = 1; r < ng; ++r) acc += *reinterpret_cast<const f4*>(p + (int64_t)r * 4 * n4);
   *reinterpret_cast<uint2*>((second ? dk : dq) + e) =
       uint2{cvt_pk_bf16(acc[0], acc[1]), cvt_pk_bf16(acc[2], acc[3])};
 }
@@ -815,14 +817,14 @@ hipError_t launch_jt(const ChunkArgs& a, hipStream_t s) {
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-  const int gy = a.part != nullptr ? a.Hv : a.Hk;
-  hipLaunchKernelGGL(kern, dim3(a.nch, gy, a.B), dim3(kThreads), lds, s, a);
+  const int ng = a.part != nullptr ? a.Hv / a.Hk / a.hpw : 1;  // head groups per kv head
+  hipLaunchKernelGGL(kern, dim3(a.nch, a.Hk * ng, a.B), dim3(kThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.part == nullptr) return e;
   const int64_t n4 = (int64_t)a.B * a.T * a.Hk * a.Dk / 4;  // Dk is a multiple of 8
   const int64_t blocks = (2 * n4 + 255) / 256;
-  hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.part,
-                     a.Hv / a.Hk, n4, static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk));
+  hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.part, ng, n4,
+                     static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk));
   return hipGetLastError();
 }
 
@@ -832,14 +834,21 @@ bool chunk_bf16_ok(const ChunkArgs& a) {
   return a.Dk % 8 == 0 && a.Dv % 8 == 0 && a.Dk > 48 && a.Dk <= 192 && a.L >= 1 && a.L <= kN;
 }
 
-// One workgroup per value head when the (chunk, kv head, batch row) grid has
-// at most 128 workgroups (half a 256-CU device or less) and 2 to 16 value
-// heads share a kv head.
-bool chunk_head_split(int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L,
-                      int64_t nch, bool bf16) {
-  const int64_t rep = Hv / Hk;
-  return bf16 && Dk % 8 == 0 && Dv % 8 == 0 && Dk > 48 && Dk <= 192 && L >= 1 && L <= kN &&
-         rep >= 2 && rep <= 16 && nch * Hk * B <= 128;
+// When the (chunk, kv head, batch row) grid has fewer than 256 workgroups
+// (one round of a 256-CU device) and 2 to 16 value heads share a kv head,
+// the value heads of a kv head go to ng groups, ng the smallest divisor of
+// their count that gives at least 256 workgroups (or all of them): each
+// workgroup forms fewer heads, and the per-workgroup set-up (QK, KK, the final
+// products) repeats as little as it can.
+int chunk_head_split(int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L,
+                     int64_t nch, bool bf16) {
+  const int64_t rep = Hv / Hk, wg = nch * Hk * B;
+  if (!(bf16 && Dk % 8 == 0 && Dv % 8 == 0 && Dk > 48 && Dk <= 192 && L >= 1 && L <= kN &&
+        rep >= 2 && rep <= 16 && wg < 256))
+    return 0;
+  int64_t ng = 2;
+  while (ng < rep && (rep % ng != 0 || wg * ng < 256)) ++ng;
+  return static_cast<int>(rep / ng);
 }
 
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s) {

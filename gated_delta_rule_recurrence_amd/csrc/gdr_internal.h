@@ -68,10 +68,12 @@ struct ChunkArgs {
   void* dk;
   void* dg;
   void* dbeta;
-  // may be null; else (chunk_head_split) one workgroup per value head writes
-  // its dq, dk terms here, [2][Hv/Hk][B][T][Hk][Dk] fp32 (dq, then dk), and a
-  // second kernel sums them over the value heads in ascending order
+  // may be null; else (chunk_head_split) each workgroup takes hpw of the
+  // Hv/Hk value heads of a kv head and writes their dq, dk terms here,
+  // [2][Hv/Hk/hpw][B][T][Hk][Dk] fp32 (dq, then dk), and a second kernel sums
+  // them over the head groups in ascending order
   float* part;
+  int hpw;
 };
 
 // Chunked sweeps (per-chunk matrices on MFMA): the sequential sweeps'
@@ -128,10 +130,11 @@ hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s);
 // takes the shape (Dk, Dv multiples of 8, 48 < Dk <= 192), and its launch.
 bool chunk_bf16_ok(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s);
-// Whether that kernel runs one workgroup per value head (a.part, then the sum
-// over the value heads): short sequences, whose (chunk, kv head) grid would
-// leave most of the device idle.
-bool chunk_head_split(int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L,
-                      int64_t nch, bool bf16);
+// How many value heads that kernel gives a workgroup when it splits a kv
+// head's value heads over several (a.part, then the sum over the groups):
+// short sequences, whose (chunk, kv head) grid would leave much of the device
+// idle; 0 when it does not split.
+int chunk_head_split(int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L,
+                     int64_t nch, bool bf16);
 
 }  // namespace gdr

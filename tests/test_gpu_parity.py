@@ -404,6 +404,20 @@ def test_bf16_dims(cuda, dims, chunk):
     compare(run_gpu(p, cuda, chunk), run_oracle(p), TOL["bf16"], f"bf16 Dk={Dk} Dv={Dv}")
 
 
+@pytest.mark.parametrize("shape", [(4, 12, 72, 70), (2, 16, 64, 200), (1, 2, 32, 70)])
+def test_bf16_head_groups(cuda, shape):
+    """Short sequences whose (chunk, kv head, batch row) grid is under 256
+    workgroups split each kv head's value heads over head groups, the dq, dk
+    terms summed over the groups afterwards: 6 value heads per kv head in 3
+    groups of 2 (96 workgroups before the split), 4 in 2 groups of 2 (128),
+    and 16 in 16 groups of 1 (4)."""
+    B, Hk, Hv, T = shape
+    p = inputs.draw(B, T, Hk, Hv, 64, 32, seed=41, normalised=True, S0_std=0.2,
+                    dST_std=1.0, dtype="bf16")
+    log(f"bf16 head groups B={B} Hk={Hk} Hv={Hv} T={T}")
+    compare(run_gpu(p, cuda, 64), run_oracle(p), TOL["bf16"], f"head groups {shape}")
+
+
 def test_bf16_small(cuda):
     p = inputs.draw(2, 70, 2, 4, 64, 32, seed=19, normalised=True, S0_std=0.1,
                     dST_std=1.0, dtype="bf16")
