@@ -45,20 +45,20 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "9a18ffa976b3a065",
+    "sources_sha256_16": "d94673b0cc3a6e3e",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 974.9e6, "bwd_write_bytes": 497.4e6,
+    "bwd_read_bytes": 974.4e6, "bwd_write_bytes": 498.2e6,
     "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 457.5e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.1, "valu_busy_pct": 19.0, "avg_us": 38.3},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.2, "valu_busy_pct": 49.1,
-                                    "avg_us": 166.5},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.8, "avg_us": 36.6},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.3,
-                                    "avg_us": 178.7},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 22.1, "valu_busy_pct": 36.7, "avg_us": 235.5},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.0, "valu_busy_pct": 18.6, "avg_us": 38.6},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 48.9,
+                                    "avg_us": 168.0},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.8, "avg_us": 36.9},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.7, "valu_busy_pct": 48.3,
+                                    "avg_us": 179.5},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 21.9, "valu_busy_pct": 36.4, "avg_us": 237.2},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
