@@ -45,7 +45,7 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "d94673b0cc3a6e3e",
+    "sources_sha256_16": "c508c4f8734a64fa",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
     "bwd_read_bytes": 974.4e6, "bwd_write_bytes": 498.2e6,

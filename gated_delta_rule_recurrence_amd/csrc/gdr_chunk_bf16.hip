@@ -11,7 +11,8 @@
 // one wave's MFMAs run while the other waits for LDS or memory; at most 256
 // registers each) per (batch row, kv head, chunk), looping over the value
 // heads of the kv head in ascending order (the GQA sum in a fixed order, no
-// atomics).  Wave w owns the chunk steps 16 (w % 4) .. +15 and the half
+// atomics); on short sequences, per (batch row, group of the kv head's value
+// heads, chunk), the groups' dq, dk terms summed afterwards (chunk_head_split).  Wave w owns the chunk steps 16 (w % 4) .. +15 and the half
 // h = w / 4 of every 64-column group of Dk: its Dk tiles are 4 p + 2 h + {0, 1}
 // (p = 0 .. Dk/64 - 1).  The two waves of a step tile split the Dv-pass
 // products, the Gram matrices (by column tile), the weight-matrix update and
