@@ -424,7 +424,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path "
-              "shards by (batch row, kv head) with no communication, see DESIGN.md",
+              "shards by (batch row, kv head) with no communication between GPUs",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
