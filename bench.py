@@ -45,20 +45,18 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "c508c4f8734a64fa",
+    "sources_sha256_16": "ec236a38f42765f3",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 974.4e6, "bwd_write_bytes": 498.2e6,
-    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 457.5e6,
+    "bwd_read_bytes": 973.2e6, "bwd_write_bytes": 490.1e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 459.7e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.0, "valu_busy_pct": 18.6, "avg_us": 38.6},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 48.9,
-                                    "avg_us": 168.0},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.8, "avg_us": 36.9},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.7, "valu_busy_pct": 48.3,
-                                    "avg_us": 179.5},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 21.9, "valu_busy_pct": 36.4, "avg_us": 237.2},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.0, "valu_busy_pct": 18.7, "avg_us": 38.8},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.9, "valu_busy_pct": 48.4, "avg_us": 172.8},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.6, "avg_us": 37.1},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.4, "valu_busy_pct": 50.2, "avg_us": 174.2},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 22.0, "valu_busy_pct": 36.5, "avg_us": 242.0},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")

@@ -1850,31 +1850,31 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
       }
       put_steps(cpp, pc);
     }
-    __syncthreads();
-
-    // H_start = pre_{n-1} Hend + (diag(pre) DY)^T Q + (-diag(beta pre) C)^T K
+    // H_start = pre_{n-1} Hend + (diag(pre) DY)^T Q + (-diag(beta pre) C)^T K.
+    // The first two terms do not depend on C: formed here, beside the C
+    // phase (the diag(pre) DY pieces are in place since the last barrier).
+    auto h_update = [&](const uint16_t* steps, const uint16_t* rows)
+                        __attribute__((always_inline)) {
 #pragma unroll
-    for (int nj = 0; nj < JW; ++nj) Hacc[nj] *= pend;
+      for (int ks = 0; ks < 2; ++ks) {
+        uint4 as[3];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      uint4 ad[3], ac[3];
+        for (int p = 0; p < 3; ++p)
+          as[p] = *reinterpret_cast<const uint4*>(steps + (p * kDS + 16 * mt + lr) * KTS +
+                                                  32 * ks + 8 * lq);
 #pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        const int o = (p * kDS + 16 * mt + lr) * KTS + 32 * ks + 8 * lq;
-        ad[p] = *reinterpret_cast<const uint4*>(dpp + o);
-        ac[p] = *reinterpret_cast<const uint4*>(cpp + o);
-      }
+        for (int nj = 0; nj < JW; ++nj) {
+          const uint4 br = tile_operand<KRS>(rows, 32 * ks, 16 * (jg + nj), lr, lq);
 #pragma unroll
-      for (int nj = 0; nj < JW; ++nj) {
-        const uint4 bq = tile_operand<KRS>(qr, 32 * ks, 16 * (jg + nj), lr, lq);
-        const uint4 bk = tile_operand<KRS>(kr, 32 * ks, 16 * (jg + nj), lr, lq);
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-          Hacc[nj] = mfma_bf16(ad[p], bq, Hacc[nj]);
-          Hacc[nj] = mfma_bf16(ac[p], bk, Hacc[nj]);
+          for (int p = 0; p < 3; ++p) Hacc[nj] = mfma_bf16(as[p], br, Hacc[nj]);
         }
       }
-    }
+    };
+#pragma unroll
+    for (int nj = 0; nj < JW; ++nj) Hacc[nj] *= pend;
+    h_update(dpp, qr);
+    __syncthreads();
+    h_update(cpp, kr);
     __syncthreads();  // stage reads done before it is rewritten
     put_grad(c - 1, lr, lq, sink16);
   }
