@@ -110,8 +110,11 @@ int gdr_checkpoint_bytes(const gdr_shape* shape, size_t* out);
 
 /* Bytes of the scratch buffer gdr_backward needs: the state-gradient
  * checkpoints (one per tile) and the per-step G_t k_t vectors, fp32, the
- * per-tile records of the chunked reverse sweep, and for chunk > 64 the
- * replayed tile states, residuals and forward records. */
+ * per-tile records of the chunked reverse sweep, for chunk > 64 the
+ * replayed tile states, residuals and forward records, and, for bf16 inputs
+ * whose (tile, kv head, batch row) grid is under 256 with 2 to 16 value
+ * heads per kv head, the fp32 dq, dk terms of each group of value heads
+ * (summed over the groups into dq, dk). */
 int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out);
 
 /* Bytes of the scratch buffer gdr_forward needs.  Shapes with Dk <= 192, a
