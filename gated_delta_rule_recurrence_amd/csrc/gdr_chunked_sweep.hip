@@ -553,31 +553,42 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     }
     if (SPLIT) __syncthreads();
 
-    // A (Bm) in place and its inverse, by the first wave
-    if (act && r0) {
+    // A (Bm) in place, its rows t split between the two waves of the head
+    // (SPLIT: rows 0..31 by the first, 32..63 by the second), then its
+    // inverse by the first wave
+    auto build_a = [&](int ta, int tb) __attribute__((always_inline)) {
       if (!bwd) {
         // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r):
         // all of the lane's operands loaded first, then the stores
         float av[kN];
 #pragma unroll
-        for (int t = 1; t < kN; ++t) av[t] = G[l * kGP + t] * QK[l * kNP + t] * bl;  // KK[l][t], l < t
+        for (int t = ta; t < tb; ++t)
+          av[t] = t > 0 ? G[l * kGP + t] * QK[l * kNP + t] * bl : 0.f;  // KK[l][t], l < t
 #pragma unroll
-        for (int t = 1; t < kN; ++t)
+        for (int t = ta; t < tb; ++t)
           if (l < t) G[t * kGP + l] = av[t];
-        // T = (I + A)^-1 in place of A
-        invert_unit_triangular<false>(G, l);
       } else {
         // Bm[t][s] = Gam(t,s] beta_s KK[s][t], s > t, in place of Gam above the
         // diagonal (lane l <-> s)
         float bv[kN];  // the lane's operands first, then the updates
 #pragma unroll
-        for (int t = 0; t < kN - 1; ++t) bv[t] = bl * QK[t * kNP + l] * G[t * kGP + l];  // KK[t][l], t < l
+        for (int t = ta; t < tb; ++t)
+          bv[t] = t < kN - 1 ? bl * QK[t * kNP + l] * G[t * kGP + l] : 0.f;  // KK[t][l], t < l
 #pragma unroll
-        for (int t = 0; t < kN - 1; ++t)
+        for (int t = ta; t < tb; ++t)
           if (l > t) G[t * kGP + l] = bv[t];
-        // Tb = (I + Bm)^-1 in place of Bm
-        invert_unit_triangular<true>(G, l);
       }
+    };
+    if (act) {
+      if (!SPLIT) build_a(0, kN);
+      else if (r0) build_a(0, kN / 2);
+      else build_a(kN / 2, kN);
+    }
+    if (SPLIT) __syncthreads();
+    if (act && r0) {
+      // T = (I + A)^-1 (Tb = (I + Bm)^-1) in place of A (Bm)
+      if (!bwd) invert_unit_triangular<false>(G, l);
+      else invert_unit_triangular<true>(G, l);
     }
     if (SPLIT) __syncthreads();
 
