@@ -272,15 +272,18 @@ __device__ __forceinline__ void invert_unit_triangular(float* G, int l) {
 
 // ---------------------------------------------------------------- prep ----
 // grid (nch, Hk, B), eight waves (two per SIMD).  MODE kPrepFwd / kPrepBwd:
-// the forward (reverse) records of value heads wh, wh + 4, ... of the kv head,
-// each formed by the two waves wh and wh + 4 together: they build Gam as two
-// running products (rows 63..32, rows 31..0), split the M (Mq) record, then
-// wave wh forms A (Bm) and its inverse, and they split the T (Tb) record
-// (three barriers per head).  kPrepBoth: waves 0-3 the forward and waves 4-7
-// the reverse records of the same heads, each wave every step of its head
-// alone (the Gram matrices formed once for both); the backward's replay uses
-// it.  Every record element takes the same operations in every mode, so the
-// records are bitwise the same whichever launch forms them.
+// the forward (reverse) records of the kv head's value heads, two at a time,
+// each formed by four waves (waves 4 s .. 4 s + 3 for head slot s): they
+// build Gam as running products down the rows (rows 63..32 from 1, rows
+// 31..0 from a product scan, each wave storing a quarter of the rows), split
+// the M (Mq) record and the rows of A (Bm), then the first forms the inverse,
+// and they split the T (Tb) record (five barriers per round).  The workgroup
+// then holds two per-head matrices, 51 KB of LDS, and three workgroups share a
+// CU.  kPrepBoth: waves 0-3 the forward and waves 4-7 the reverse records of
+// the same heads, each wave every step of its head alone (the Gram matrices
+// formed once for both); the backward's replay uses it.  Every record element
+// takes the same operations in every mode, so the records are bitwise the
+// same whichever launch forms them.
 constexpr int kPrepFwd = 0, kPrepBwd = 1, kPrepBoth = 2;
 constexpr int kPrepThreads = 512;
 
@@ -290,7 +293,8 @@ constexpr int kPrepThreads = 512;
 __device__ __forceinline__ int qk_at(int t, int r) { return t * kNP + r; }  // r <= t
 
 // LDS of the prep: NG per-head matrices [kN][kGP] and their beta vectors,
-// then the QK / KK matrix; the q, k stages alias the per-head arrays.
+// then the QK / KK matrix; the q, k stages alias all of it (the QK / KK
+// matrix is written once the stages are no longer read).
 template <int NG>
 struct PL {
   static constexpr int QS = 0, KS = 64 * kN;          // q, k stage [16][kN][4]
@@ -298,22 +302,22 @@ struct PL {
   static constexpr int VB = NG * kN * kGP;             // NG x beta[kN]
   static constexpr int QK = VB + NG * kN;              // QK / KK [kN][kNP]
   static constexpr int SIZE = QK + kN * kNP;
-  static_assert(2 * 64 * kN <= VB, "stage fits the per-head arrays");
+  static_assert(2 * 64 * kN <= QK + kN * kNP, "stage fits the workgroup's LDS");
   // bf16 inputs: q, k rows as bf16 [kN][KGS] (alias the per-head arrays);
   // the row stride an odd number of 16-byte units, so the 16-byte operand
   // reads of 16 rows at one column group hit distinct banks
   static constexpr int KGS = 16 * kMaxJT + 8;
   static constexpr int BQ = 0, BK = kN * KGS / 2;
-  static_assert((2 * KGS) % 32 == 16 && 2 * kN * KGS / 2 <= VB, "bf16 stage");
+  static_assert((2 * KGS) % 32 == 16 && 2 * kN * KGS / 2 <= QK + kN * kNP, "bf16 stage");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
 template <typename TIn, int MODE, bool VEC>
 __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     ChunkedSweepShape a, float* __restrict__ prep_f, float* __restrict__ prep_b) {
-  constexpr bool SPLIT = MODE != kPrepBoth;  // two waves per value head
+  constexpr bool SPLIT = MODE != kPrepBoth;  // four waves per value head
   constexpr int NTH = kPrepThreads;
-  using L = PL<SPLIT ? 4 : 8>;
+  using L = PL<SPLIT ? 2 : 8>;
   extern __shared__ __align__(16) float sm[];
   const TIn* __restrict__ q = static_cast<const TIn*>(a.q);
   const TIn* __restrict__ k = static_cast<const TIn*>(a.k);
@@ -330,11 +334,13 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
   const int tw = 16 * (w & 3);
   const int half = w >> 2;  // this wave's Gram column tiles: 2 half, 2 half + 1
   // this wave's first value head, which records it forms, and (SPLIT) its
-  // part of them: r0, the first wave of the pair, r1 the second (one wave
-  // does both in kPrepBoth)
-  const int wh = w & 3;
+  // part of them: quarter q of the head's four waves (one wave does all of
+  // it in kPrepBoth); r0: the wave that forms the inverse and the vectors
+  const int wh = SPLIT ? w >> 2 : w & 3;
+  const int qw = SPLIT ? w & 3 : 0;
+  constexpr int HSTEP = SPLIT ? 2 : 4;  // value heads per round
   const bool bwd = MODE == kPrepBwd || (MODE == kPrepBoth && w >= 4);
-  const bool r0 = !SPLIT || w < 4, r1 = !SPLIT || w >= 4;
+  const bool r0 = qw == 0;
 
   // g, beta of this wave's first value head, issued before the k, q loads
   // (index clamped into the tensors; masked where used)
@@ -454,15 +460,26 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
   __syncthreads();
 
   // ---- per value head ------------------------------------------------------
-  // (SPLIT: the two waves of a head share its matrix G, and every wave runs
-  // the same number of passes, so that the barriers below match up)
+  // (SPLIT: the four waves of a head share its matrix G, and every wave runs
+  // the same number of rounds, so that the barriers below match up)
   float* G = sm + L::GW + (SPLIT ? wh : w) * kN * kGP;  // [kN][kGP] per head
   float* vb = sm + L::VB + (SPLIT ? wh : w) * kN;        // beta_t
   const float* QK = sm + L::QK;  // QK on and below the diagonal, KK above
   // bf16 inputs in 8-element groups: the bf16-product sweeps read the
   // matrices as bf16 pieces
   const bool pieces = bf16_products(kBf16, Dk, a.Dv);
-  for (int h0 = 0; h0 < rep; h0 += 4) {
+  // a record's six piece blocks: all of them (one wave per head), or this
+  // wave's share of the four (blocks 0-1, 2-3, 4, 5)
+  auto pieces_quarter = [&](float* dst, int ll, auto elem, auto upper)
+                            __attribute__((always_inline)) {
+    constexpr bool U = decltype(upper)::value;
+    if (!SPLIT) pieces_to_record<U>(dst, ll, elem);
+    else if (qw == 0) pieces_to_record<U, 0, 2>(dst, ll, elem);
+    else if (qw == 1) pieces_to_record<U, 2, 4>(dst, ll, elem);
+    else if (qw == 2) pieces_to_record<U, 4, 5>(dst, ll, elem);
+    else pieces_to_record<U, 5, 6>(dst, ll, elem);
+  };
+  for (int h0 = 0; h0 < rep; h0 += HSTEP) {
     // the lane indices again, from an opaque copy of the thread id: otherwise
     // the compiler evaluates the per-row lane masks of the loops below ahead
     // of the Gram phase and spills them (a lane read back per use)
@@ -486,28 +503,34 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     // below it (rows r > t), and above it two running products down the rows,
     // Gam(r,t] = g_{r+1} Gam(r+1,t]: rows 63..32 from 1, rows 31..0 from
     // Gam(32,t] (a product scan over the lanes).  g_{r+1} is read from lane
-    // r + 1, so the loops hold only LDS stores.
-    auto gam_rows = [&](int r_hi, int r_lo, float p) __attribute__((always_inline)) {
+    // r + 1, so the loops hold only LDS stores.  A wave runs its chain from
+    // the top of its half and stores rows r_st .. r_lo: every row takes the
+    // same products in every mode.
+    auto gam_rows = [&](int r_hi, int r_st, int r_lo, float p) __attribute__((always_inline)) {
 #pragma unroll 8
       for (int r = r_hi; r >= r_lo; --r) {
         const float gr =
             r + 1 < kN ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), r + 1)) : 1.f;
         p = r < l ? p * gr : p;
-        G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
+        if (r <= r_st) G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
       }
       return p;
     };
     float pre = 0.f;  // Gam(-1, l] = g_0 Gam(0, l]
-    if (act && r1) (void)gam_rows(kN - 1, 32, 1.f);
-    if (act && r0) {
-      const float p = gam_rows(31, 0, wave_prefix_product(l > 32 ? gl : 1.f));
-      pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * p;
-      vb[l] = bl;
+    if (act) {
+      if (!SPLIT || qw == 3) (void)gam_rows(kN - 1, kN - 1, SPLIT ? 48 : 32, 1.f);
+      if (SPLIT && qw == 2) (void)gam_rows(kN - 1, 47, 32, 1.f);
+      if (SPLIT && qw == 1) (void)gam_rows(31, 31, 16, wave_prefix_product(l > 32 ? gl : 1.f));
+      if (r0) {
+        const float p = gam_rows(31, SPLIT ? 15 : 31, 0, wave_prefix_product(l > 32 ? gl : 1.f));
+        pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * p;
+        vb[l] = bl;
+      }
     }
     if (SPLIT) __syncthreads();
 
-    // the M (Mq) record, its blocks split between the two waves; suf is read
-    // before Bm replaces Gam above the diagonal
+    // the M (Mq) record, its blocks split between the four waves; suf is
+    // read before Bm replaces Gam above the diagonal
     float suf = 0.f;  // Gam(l, n-1]
     if (act && r0) suf = l < n ? G[l * kGP + n - 1] : 0.f;
     if (act) {
@@ -517,12 +540,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
           return s <= t ? G[s * kGP + t] * QK[qk_at(t, s)] * vb[s] : 0.f;
         };
         if (pieces) {
-          if (!SPLIT) pieces_to_record<false>(rec + kBrM, l, m_el);
-          else if (r0) pieces_to_record<false, 0, 3>(rec + kBrM, l, m_el);
-          else pieces_to_record<false, 3, 6>(rec + kBrM, l, m_el);
+          pieces_quarter(rec + kBrM, l, m_el, std::false_type{});
         } else {
 #pragma unroll 2
-          for (int bx = SPLIT && r1 ? 8 : 0; bx < (SPLIT && r0 ? 8 : 16); ++bx) {
+          for (int bx = SPLIT ? 4 * qw : 0; bx < (SPLIT ? 4 * qw + 4 : 16); ++bx) {
             const int t = 16 * (bx >> 2) + lr;
             f4 m4;
 #pragma unroll
@@ -536,12 +557,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
           return s >= t ? G[t * kGP + s] * QK[qk_at(s, t)] : 0.f;
         };
         if (pieces) {
-          if (!SPLIT) pieces_to_record<true>(rec + kBbM, l, m_el);
-          else if (r0) pieces_to_record<true, 0, 3>(rec + kBbM, l, m_el);
-          else pieces_to_record<true, 3, 6>(rec + kBbM, l, m_el);
+          pieces_quarter(rec + kBbM, l, m_el, std::true_type{});
         } else {
 #pragma unroll 2
-          for (int bx = SPLIT && r1 ? 8 : 0; bx < (SPLIT && r0 ? 8 : 16); ++bx) {
+          for (int bx = SPLIT ? 4 * qw : 0; bx < (SPLIT ? 4 * qw + 4 : 16); ++bx) {
             const int t = 16 * (bx >> 2) + lr;
             f4 m4;
 #pragma unroll
@@ -553,9 +572,9 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     }
     if (SPLIT) __syncthreads();
 
-    // A (Bm) in place, its rows t split between the two waves of the head
-    // (SPLIT: rows 0..31 by the first, 32..63 by the second), then its
-    // inverse by the first wave
+    // A (Bm) in place, its rows t split between the four waves of the head
+    // (SPLIT: rows 16 q .. 16 q + 15 by quarter q), then its inverse by the
+    // first wave
     auto build_a = [&](int ta, int tb) __attribute__((always_inline)) {
       if (!bwd) {
         // A[t][r] = Gam(r,t] KK[t][r] beta_r below the diagonal (lane l <-> r):
@@ -581,8 +600,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     };
     if (act) {
       if (!SPLIT) build_a(0, kN);
-      else if (r0) build_a(0, kN / 2);
-      else build_a(kN / 2, kN);
+      else if (qw == 0) build_a(0, 16);
+      else if (qw == 1) build_a(16, 32);
+      else if (qw == 2) build_a(32, 48);
+      else build_a(48, kN);
     }
     if (SPLIT) __syncthreads();
     if (act && r0) {
@@ -592,17 +613,15 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     }
     if (SPLIT) __syncthreads();
 
-    // the T (Tb) record, its blocks split between the two waves, and the
+    // the T (Tb) record, its blocks split between the four waves, and the
     // step vectors by the first
     if (act) {
       auto t_el = [&](int t, int s) __attribute__((always_inline)) { return G[t * kGP + s]; };
       if (!bwd) {
         if (pieces) {
-          if (!SPLIT) pieces_to_record<false>(rec + kBrT, l, t_el);
-          else if (r0) pieces_to_record<false, 0, 3>(rec + kBrT, l, t_el);
-          else pieces_to_record<false, 3, 6>(rec + kBrT, l, t_el);
+          pieces_quarter(rec + kBrT, l, t_el, std::false_type{});
         } else {
-          store_frags(G, kGP, rec + kPrT, l, SPLIT && r1 ? 8 : 0, SPLIT && r0 ? 8 : 16);
+          store_frags(G, kGP, rec + kPrT, l, SPLIT ? 4 * qw : 0, SPLIT ? 4 * qw + 4 : 16);
         }
         if (r0) {
           rec[(pieces ? kBrGam : kPrGam) + l] = pre;
@@ -611,11 +630,9 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
         }
       } else {
         if (pieces) {
-          if (!SPLIT) pieces_to_record<true>(rec + kBbT, l, t_el);
-          else if (r0) pieces_to_record<true, 0, 3>(rec + kBbT, l, t_el);
-          else pieces_to_record<true, 3, 6>(rec + kBbT, l, t_el);
+          pieces_quarter(rec + kBbT, l, t_el, std::true_type{});
         } else {
-          store_frags(G, kGP, rec + kPbT, l, SPLIT && r1 ? 8 : 0, SPLIT && r0 ? 8 : 16);
+          store_frags(G, kGP, rec + kPbT, l, SPLIT ? 4 * qw : 0, SPLIT ? 4 * qw + 4 : 16);
         }
         if (r0) {
           rec[(pieces ? kBbSuf : kPbSuf) + l] = suf;
@@ -1915,9 +1932,9 @@ hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
 template <typename TIn, int MODE>
 hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep_f, float* prep_b,
                        hipStream_t s) {
-  // per-head matrices: one per value head of a pass (two waves share it), or
-  // one per wave with both record sets
-  constexpr int NG = MODE == kPrepBoth ? 8 : 4;
+  // per-head matrices: one per value head of a round (four waves share it),
+  // or one per wave with both record sets
+  constexpr int NG = MODE == kPrepBoth ? 8 : 2;
   const dim3 grid(sh.nch, sh.Hk, sh.B);
   const size_t lds = sizeof(float) * PL<NG>::SIZE;
   if (sh.Dk % 4 == 0)
