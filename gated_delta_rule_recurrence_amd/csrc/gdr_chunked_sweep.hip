@@ -324,8 +324,15 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
   const TIn* __restrict__ g = static_cast<const TIn*>(a.g);
   const TIn* __restrict__ beta = static_cast<const TIn*>(a.beta);
   const int T = a.T, Hk = a.Hk, Hv = a.Hv, Dk = a.Dk;
-  const int jc = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
   const int rep = Hv / Hk;
+  // SPLIT with a.pair_grid: grid y runs over (kv head, pair of its value
+  // heads), one round per workgroup; else over the kv heads
+  const int npair = (rep + 1) / 2;
+  const bool pg = SPLIT && a.pair_grid;
+  const int jc = blockIdx.x, b = blockIdx.z;
+  const int hk = pg ? (int)blockIdx.y / npair : (int)blockIdx.y;
+  const int hbase = pg ? 2 * ((int)blockIdx.y - hk * npair) : 0;  // first value head
+  const int hend = pg ? min(rep, hbase + 2) : rep;
   const int t0 = jc * a.L;
   const int n = min(a.L, T - t0);
   const int tid = threadIdx.x;
@@ -347,7 +354,8 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
   auto gb_index = [&](int hh) {
     return ((int64_t)b * T + t0 + (l < n ? l : 0)) * Hv + hk * rep + hh;
   };
-  TIn g_raw = g[gb_index(wh < rep ? wh : 0)], b_raw = beta[gb_index(wh < rep ? wh : 0)];
+  const int hw0 = hbase + wh < rep ? hbase + wh : 0;
+  TIn g_raw = g[gb_index(hw0)], b_raw = beta[gb_index(hw0)];
 
   // ---- QK[t][r] = q_t . k_r, KK[t][r] = k_t . k_r (MFMA over Dk) ----------
   // wave w: rows 16 (w % 4) .., column tiles 2 half, 2 half + 1 of both
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     else if (qw == 2) pieces_to_record<U, 4, 5>(dst, ll, elem);
     else pieces_to_record<U, 5, 6>(dst, ll, elem);
   };
-  for (int h0 = 0; h0 < rep; h0 += HSTEP) {
+  for (int h0 = hbase; h0 < hend; h0 += HSTEP) {
     // the lane indices again, from an opaque copy of the thread id: otherwise
     // the compiler evaluates the per-row lane masks of the loops below ahead
     // of the Gram phase and spills them (a lane read back per use)
@@ -491,7 +499,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     const int h = hk * rep + (act ? hh : 0);
     float* __restrict__ rec =
         (bwd ? prep_b : prep_f) + (((int64_t)b * Hv + h) * a.nch + jc) * kChunkPrepStride;
-    if (h0 > 0) {
+    if (h0 > hbase) {
       g_raw = g[gb_index(act ? hh : 0)];
       b_raw = beta[gb_index(act ? hh : 0)];
     }
@@ -1930,12 +1938,17 @@ hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
 
 // The records of MODE (forward records to prep_f, reverse to prep_b).
 template <typename TIn, int MODE>
-hipError_t launch_prep(const ChunkedSweepShape& sh, float* prep_f, float* prep_b,
-                       hipStream_t s) {
+hipError_t launch_prep(ChunkedSweepShape sh, float* prep_f, float* prep_b, hipStream_t s) {
   // per-head matrices: one per value head of a round (four waves share it),
   // or one per wave with both record sets
   constexpr int NG = MODE == kPrepBoth ? 8 : 2;
-  const dim3 grid(sh.nch, sh.Hk, sh.B);
+  // one workgroup per pair of a kv head's value heads (each one round, the
+  // Gram matrices formed per pair) when all of them fit on the device at
+  // once (three per CU), else one per kv head (the rounds one after another)
+  const int npair = (sh.Hv / sh.Hk + 1) / 2;
+  const int64_t pairs = (int64_t)sh.nch * sh.Hk * npair * sh.B;
+  sh.pair_grid = MODE != kPrepBoth && npair > 1 && pairs <= 3 * device_cu_count();
+  const dim3 grid(sh.nch, sh.pair_grid ? sh.Hk * npair : sh.Hk, sh.B);
   const size_t lds = sizeof(float) * PL<NG>::SIZE;
   if (sh.Dk % 4 == 0)
     return launch(prep_kernel<TIn, MODE, true>, grid, kPrepThreads, lds, s, sh, prep_f, prep_b);

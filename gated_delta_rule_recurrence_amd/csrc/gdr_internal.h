@@ -96,6 +96,7 @@ struct BwdChunkedArgs {
 struct ChunkedSweepShape {
   int B, T, Hk, Hv, Dk, Dv, L, nch;
   int log_g;
+  int pair_grid;  // set by the launch: one prep workgroup per pair of value heads
   const uint8_t* mask;
   const void* q;
   const void* k;
