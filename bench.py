@@ -45,18 +45,18 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "ec236a38f42765f3",
+    "sources_sha256_16": "9c54e7c876632a9e",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 973.2e6, "bwd_write_bytes": 490.1e6,
-    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 459.7e6,
+    "bwd_read_bytes": 973.0e6, "bwd_write_bytes": 494.1e6,
+    "fwd_read_bytes": 162.4e6, "fwd_write_bytes": 457.5e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.0, "valu_busy_pct": 18.7, "avg_us": 38.8},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 18.9, "valu_busy_pct": 48.4, "avg_us": 172.8},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 5.4, "valu_busy_pct": 19.6, "avg_us": 37.1},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.4, "valu_busy_pct": 50.2, "avg_us": 174.2},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 22.0, "valu_busy_pct": 36.5, "avg_us": 242.0},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.5, "valu_busy_pct": 24.1, "avg_us": 35.6},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.2, "valu_busy_pct": 49.3, "avg_us": 173.0},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 5.8, "valu_busy_pct": 24.8, "avg_us": 34.5},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.1, "avg_us": 179.7},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 21.9, "valu_busy_pct": 36.5, "avg_us": 244.9},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
