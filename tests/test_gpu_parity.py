@@ -275,6 +275,21 @@ def test_long_interval_replays_tiles_exactly(cuda, dtype, C, tile):
     compare(a, run_oracle(p), TOL[dtype], f"C={C} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_long_interval_replay_pair_grid(cuda, dtype):
+    """Four value heads per kv head on a short sequence: the forward's prep
+    runs one workgroup per pair of value heads, the backward's replay forms
+    both record sets in one launch of eight one-wave heads; the records are
+    the same element by element, so C = 128 still equals C = 64 bit for bit."""
+    p = _masked(inputs.draw(2, 300, 2, 8, 64, 32, seed=73, normalised=True, decay="mix",
+                            S0_std=0.1, dST_std=1.0, dtype=dtype), 73)
+    log(f"C=128 vs C=64, Hv/Hk=4, {dtype}")
+    a, b = run_gpu(p, cuda, 128), run_gpu(p, cuda, 64)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"C=128 vs 64: {n}")
+    compare(a, run_oracle(p), TOL[dtype], f"C=128 Hv/Hk=4 {dtype}")
+
+
 def test_long_interval_replay_without_segments(cuda):
     """More (batch row, saved state) pairs than one grid dimension holds: the
     replay runs every tile of a row from its first saved state instead of
