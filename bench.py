@@ -236,6 +236,48 @@ def copy_bandwidth(dev, mib=1024, reps=5):
     return 2 * n * 4 / (best * 1e-3) / 1e9
 
 
+PROBE_LIB = os.path.join(ROOT, "tests", "probe", "libgdr_probe.so")
+
+
+def compute_peaks(dev, reps=3):
+    """Attainable compute rates: loops of one instruction kind from the
+    test-only probe library (fp32 FMA on the vector ALU, non-packed as this
+    build's vector code is; bf16 and fp32 MFMA), 2048 workgroups of 256
+    threads, best of `reps` launches by HIP events on torch's stream.  None
+    when the probe library is not built."""
+    import ctypes
+    import torch
+    if not os.path.exists(PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.gdr_probe_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    blocks = 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    # kind, iterations, flops per launch
+    kinds = {"fp32_fma_vector": (0, 1000, 256 * 256 * blocks),
+             "bf16_mfma": (1, 5000, blocks * 4 * 4 * 16384),
+             "fp32_mfma": (2, 4000, blocks * 4 * 4 * 2048)}
+    res = {}
+    for name, (kind, iters, per_iter) in kinds.items():
+        if lib.gdr_probe_peak(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                              ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError(f"peak probe {name} failed to launch")
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.gdr_probe_peak(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()),
+                               ctypes.c_void_p(stream))
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        res[name + "_TFLOPs"] = per_iter * iters / (best * 1e-3) / 1e12
+    del out
+    return res
+
+
 # ------------------------------------------------------------------ modes --
 def decode(args):
     """Inference decode: T=1 steps with the state in and out of one buffer.
@@ -502,6 +544,7 @@ def main():
     del flush
     peak_mb = torch.cuda.max_memory_allocated(dev) / 1e6
     copy_gbs = copy_bandwidth(dev)
+    peaks = compute_peaks(dev)
     ms = wall * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms / 1e3)
@@ -579,6 +622,7 @@ def main():
                     "avg_launch_ms": fwd_ms},
         "counters": counters,
         "achievable_hbm_GBps": copy_gbs,
+        "achievable_compute": peaks,
         "timing": {"wall_ms_per_step": ms, "step_ms_median": float(np.median(step_ms)),
                    "step_ms_min": float(step_ms.min()),
                    "flushed_step_ms_median": float(np.median(flushed_ms)),

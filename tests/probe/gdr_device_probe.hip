@@ -2,7 +2,12 @@
 // into a test-only library (libgdr_probe.so, not part of libgdr.so):
 //   * split3_quad: the exact three-piece bf16 split of fp32 values;
 //   * lds_read_tr16 (ds_read_b64_tr_b16): which elements each lane receives;
-//   * tile_operand: the MFMA operand it gathers from a swizzled bf16 tile.
+//   * tile_operand: the MFMA operand it gathers from a swizzled bf16 tile;
+//   * compute peaks: loops of one instruction kind (fp32 FMA on the vector
+//     ALU, bf16 and fp32 MFMA) whose launch the host times, so that the
+//     benchmark can report what this build reaches on the device next to
+//     the published peaks (fp32 vector code here is built without packed
+//     FP32 instructions, so its peak is the non-packed rate).
 // The tests compare the outputs with CPU models of the same definitions.
 // Every kernel indexes only within the buffers the host sizes below, and
 // each entry point checks its sizes before launching.
@@ -59,6 +64,63 @@ __global__ void tile_operand_probe(int k0, int n0, uint16_t* __restrict__ out) {
   for (int e = 0; e < 8; ++e) out[8 * l + e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
 }
 
+// Compute peaks.  Every thread (fma) or wave (mfma) runs independent chains
+// of one instruction for `iters` iterations and writes the sum of its
+// accumulators, one float per thread.  The values converge or count
+// exactly, so the tests can check them:
+//   fma:  a <- a * 0.5 + 1 from a = k (k = 0..7), eight chains, 128 FMAs per
+//         iteration: every chain reaches 2 exactly, the sum is 16;
+//   mfma: operands of ones (x, y: the bf16 / fp32 one from the host), four
+//         accumulators from zero: each bf16 MFMA adds 32 to every element,
+//         each fp32 one 4; a thread's sum is 4 * 4 * that * iters.
+__global__ __launch_bounds__(256) void fma_peak(float* __restrict__ out, int iters, float m,
+                                                float c) {
+  float a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a[k] = (float)k;
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) a[k] = fmaf(a[k], m, c);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) s += a[k];
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void mfma_bf16_peak(float* __restrict__ out, int iters,
+                                                      uint32_t one2) {
+  const uint4 x = {one2, one2, one2, one2};
+  gdr::f4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = gdr::f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = gdr::mfma_bf16(x, x, acc[u]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s += (acc[u][0] + acc[u][1]) + (acc[u][2] + acc[u][3]);
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void mfma_f32_peak(float* __restrict__ out, int iters,
+                                                     float one) {
+  gdr::f4 acc[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) acc[u] = gdr::f4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = gdr::mfma(one, one, acc[u]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s += (acc[u][0] + acc[u][1]) + (acc[u][2] + acc[u][3]);
+  out[blockIdx.x * 256 + threadIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -86,6 +148,25 @@ int gdr_probe_tile_operand(int k0, int n0, uint16_t* out, void* stream) {
     return -1;
   hipLaunchKernelGGL(tile_operand_probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
                      k0, n0, out);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+// kind 0: fp32 FMA, 1: bf16 MFMA (16x16x32), 2: fp32 MFMA (16x16x4); blocks
+// workgroups of 256 threads, out: 256 * blocks floats (device).  Flops per
+// launch: kind 0: 256 * blocks * iters * 256; kinds 1, 2: blocks * 4 waves *
+// iters * 4 * (16384 or 2048).  0 or -1.
+int gdr_probe_peak(int kind, int blocks, int iters, float* out, void* stream) {
+  if (out == nullptr || blocks < 1 || blocks > 65535 || iters < 1 || iters > (1 << 20) ||
+      kind < 0 || kind > 2)
+    return -1;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (kind == 0)
+    hipLaunchKernelGGL(fma_peak, dim3(blocks), dim3(256), 0, s, out, iters, 0.5f, 1.0f);
+  else if (kind == 1)
+    hipLaunchKernelGGL(mfma_bf16_peak, dim3(blocks), dim3(256), 0, s, out, iters,
+                       0x3f803f80u);  // two bf16 ones
+  else
+    hipLaunchKernelGGL(mfma_f32_peak, dim3(blocks), dim3(256), 0, s, out, iters, 1.0f);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -9,7 +9,8 @@ models (in-bounds probe kernels in tests/probe, a test-only library):
   receives element i % 4 of the 8-byte blocks named by lanes i / 4,
   4 + i / 4, 8 + i / 4 and 12 + i / 4, in that order;
 * tile_operand: from a swizzled row-major bf16 tile, lane l gathers rows
-  k0 + 8 (l / 16) + 0..7 of column n0 + l % 16, element e in bits 16e...
+  k0 + 8 (l / 16) + 0..7 of column n0 + l % 16, element e in bits 16e...;
+* the compute-peak loops that bench.py times count exactly.
 """
 import ctypes
 import os
@@ -34,6 +35,7 @@ def probe():
     lib.gdr_probe_split3.argtypes = [vp, vp, ctypes.c_int, vp]
     lib.gdr_probe_tr16.argtypes = [vp, vp, vp]
     lib.gdr_probe_tile_operand.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.gdr_probe_peak.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
     return lib
 
 
@@ -88,8 +90,27 @@ def test_tile_operand_gathers_columns(cuda, probe, k0, n0):
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("kind,per_iter", [(0, None), (1, 512.0), (2, 64.0)])
+def test_peak_loops_count_exactly(cuda, probe, kind, per_iter):
+    """The compute-peak loops the benchmark times do the work they claim:
+    the FMA chains a <- a/2 + 1 from a = 0..7 all reach 2 (sum 16); each
+    bf16 MFMA of ones adds 32 to each of a wave's 4 x 4 accumulator values
+    per lane (512 per iteration), each fp32 16x16x4 MFMA adds 4 (64)."""
+    import torch
+    iters, blocks = 3, 8
+    out = torch.full((blocks * 256,), -1.0, dtype=torch.float32, device=cuda)
+    assert probe.gdr_probe_peak(kind, blocks, iters, out.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    want = 16.0 if per_iter is None else per_iter * iters
+    np.testing.assert_array_equal(out.cpu().numpy(), np.full(blocks * 256, want, np.float32))
+
+
 def test_probe_rejects_bad_arguments(probe):
     """Host-side checks (no launch)."""
     assert probe.gdr_probe_tile_operand(5, 0, 16, None) == -1
     assert probe.gdr_probe_tile_operand(0, 184, 16, None) == -1
     assert probe.gdr_probe_split3(None, None, 4, None) == -1
+    assert probe.gdr_probe_peak(3, 8, 1, 16, None) == -1
+    assert probe.gdr_probe_peak(0, 0, 1, 16, None) == -1
+    assert probe.gdr_probe_peak(0, 8, 0, 16, None) == -1
+    assert probe.gdr_probe_peak(0, 8, 1, None, None) == -1
