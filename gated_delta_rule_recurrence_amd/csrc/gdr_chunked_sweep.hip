@@ -508,30 +508,35 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
     const float gl = l < n && !skip ? decay_of(to_f32(g_raw), a.log_g) : 1.f;
     const float bl = l < n && !skip ? to_f32(b_raw) : 0.f;
     // Gam(r,t] (lane l <-> t = l), held in G[r][t]: 1 on the diagonal, 0
-    // below it (rows r > t), and above it two running products down the rows,
-    // Gam(r,t] = g_{r+1} Gam(r+1,t]: rows 63..32 from 1, rows 31..0 from
-    // Gam(32,t] (a product scan over the lanes).  g_{r+1} is read from lane
-    // r + 1, so the loops hold only LDS stores.  A wave runs its chain from
-    // the top of its half and stores rows r_st .. r_lo: every row takes the
-    // same products in every mode.
-    auto gam_rows = [&](int r_hi, int r_st, int r_lo, float p) __attribute__((always_inline)) {
+    // below it (rows r > t), and above it running products down the rows,
+    // Gam(r,t] = g_{r+1} Gam(r+1,t], in four quarters of 16 rows: rows
+    // 63..48 from 1, each lower quarter from Gam(16 (z + 1), t] (a product
+    // scan over the lanes) for its rows 16 z + 15 .. 16 z.  g_{r+1} is read
+    // from lane r + 1, so the loops hold only LDS stores.  Every row takes the
+    // same products in every mode (one quarter per wave of a head, or all
+    // four by one wave).
+    auto gam_rows = [&](int z) __attribute__((always_inline)) {
+      float p = z == 3 ? 1.f : wave_prefix_product(l > 16 * (z + 1) ? gl : 1.f);
 #pragma unroll 8
-      for (int r = r_hi; r >= r_lo; --r) {
+      for (int r = 16 * z + 15; r >= 16 * z; --r) {
         const float gr =
             r + 1 < kN ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), r + 1)) : 1.f;
         p = r < l ? p * gr : p;
-        if (r <= r_st) G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
+        G[r * kGP + l] = r < l ? p : (r == l ? 1.f : 0.f);
       }
       return p;
     };
     float pre = 0.f;  // Gam(-1, l] = g_0 Gam(0, l]
     if (act) {
-      if (!SPLIT || qw == 3) (void)gam_rows(kN - 1, kN - 1, SPLIT ? 48 : 32, 1.f);
-      if (SPLIT && qw == 2) (void)gam_rows(kN - 1, 47, 32, 1.f);
-      if (SPLIT && qw == 1) (void)gam_rows(31, 31, 16, wave_prefix_product(l > 32 ? gl : 1.f));
+      if (!SPLIT) {
+        (void)gam_rows(3);
+        (void)gam_rows(2);
+        (void)gam_rows(1);
+      } else if (qw > 0) {
+        (void)gam_rows(qw);
+      }
       if (r0) {
-        const float p = gam_rows(31, SPLIT ? 15 : 31, 0, wave_prefix_product(l > 32 ? gl : 1.f));
-        pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * p;
+        pre = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gl), 0)) * gam_rows(0);
         vb[l] = bl;
       }
     }
