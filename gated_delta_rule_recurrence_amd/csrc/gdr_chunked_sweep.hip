@@ -192,11 +192,15 @@ __device__ __forceinline__ void store_frags(const float* src, int ld, float* __r
 //   L_ik = -T_ii A_ik for the off-diagonal blocks of the triangle (MFMA);
 //   T_ij = sum_k L_ik T_kj, k from j to i - 1 (UPPER: i + 1 to j), block
 //   row by block row (MFMA), from the block-row equations of (I + A) T = I.
-// T replaces A in G (all of it: the other triangle is zeroed).
-template <bool UPPER>
-__device__ __forceinline__ void invert_unit_triangular(float* G, int l) {
+// T replaces A in G (all of it: the other triangle is zeroed).  Stage
+// STG 0 does all of it; with several waves on the matrix, stage 1 forms the
+// diagonal blocks, stage 2 (every wave, its share nw of the six products,
+// from wave iw) the L blocks, and stage 3 the rest, a barrier between the
+// stages: each block takes the same operations either way.
+template <bool UPPER, int STG = 0>
+__device__ __forceinline__ void invert_unit_triangular(float* G, int l, int iw = 0, int nw = 1) {
   const int lr = l & 15, lq = l >> 4;
-  {
+  if (STG == 0 || STG == 1) {
     const int base = 16 * lq, c = lr;
     float x[16];
 #pragma unroll
@@ -230,14 +234,20 @@ __device__ __forceinline__ void invert_unit_triangular(float* G, int l) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) G[(16 * rb + 4 * lq + e) * kGP + 16 * cb + lr] = v[e];
   };
-  // L_ik = -T_ii A_ik in place of A_ik
+  if (STG == 1) return;
+  // L_ik = -T_ii A_ik in place of A_ik (product x of the six: this wave's
+  // when x % nw == iw)
+  if (STG == 0 || STG == 2) {
+    int x = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (UPPER ? k <= i : k >= i) continue;
-      put(i, k, -prod(i, i, i, k, f4{0.f, 0.f, 0.f, 0.f}));
-    }
+      for (int k = 0; k < 4; ++k) {
+        if (UPPER ? k <= i : k >= i) continue;
+        if (x++ % nw == iw) put(i, k, -prod(i, i, i, k, f4{0.f, 0.f, 0.f, 0.f}));
+      }
+  }
+  if (STG == 2) return;
   // T_ij, a block row at a time (its products read L of the same row, so
   // the row is written once all of it is formed)
 #pragma unroll
@@ -619,10 +629,29 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
       else build_a(48, kN);
     }
     if (SPLIT) __syncthreads();
-    if (act && r0) {
-      // T = (I + A)^-1 (Tb = (I + Bm)^-1) in place of A (Bm)
-      if (!bwd) invert_unit_triangular<false>(G, l);
-      else invert_unit_triangular<true>(G, l);
+    // T = (I + A)^-1 (Tb = (I + Bm)^-1) in place of A (Bm): the diagonal
+    // blocks and the block rows by the first wave, the six L blocks (SPLIT)
+    // over the head's four waves
+    if (!SPLIT) {
+      if (act) {
+        if (!bwd) invert_unit_triangular<false>(G, l);
+        else invert_unit_triangular<true>(G, l);
+      }
+    } else {
+      if (act && r0) {
+        if (!bwd) invert_unit_triangular<false, 1>(G, l);
+        else invert_unit_triangular<true, 1>(G, l);
+      }
+      __syncthreads();
+      if (act) {
+        if (!bwd) invert_unit_triangular<false, 2>(G, l, qw, 4);
+        else invert_unit_triangular<true, 2>(G, l, qw, 4);
+      }
+      __syncthreads();
+      if (act && r0) {
+        if (!bwd) invert_unit_triangular<false, 3>(G, l);
+        else invert_unit_triangular<true, 3>(G, l);
+      }
     }
     if (SPLIT) __syncthreads();
 
