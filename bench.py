@@ -45,18 +45,18 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "9c54e7c876632a9e",
+    "sources_sha256_16": "38e9a9c4177f4747",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 973.0e6, "bwd_write_bytes": 494.1e6,
-    "fwd_read_bytes": 162.4e6, "fwd_write_bytes": 457.5e6,
+    "bwd_read_bytes": 974.6e6, "bwd_write_bytes": 492.1e6,
+    "fwd_read_bytes": 162.4e6, "fwd_write_bytes": 458.3e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.5, "valu_busy_pct": 24.1, "avg_us": 35.6},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.2, "valu_busy_pct": 49.3, "avg_us": 173.0},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 5.8, "valu_busy_pct": 24.8, "avg_us": 34.5},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.1, "avg_us": 179.7},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 21.9, "valu_busy_pct": 36.5, "avg_us": 244.9},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.7, "valu_busy_pct": 24.8, "avg_us": 32.7},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.0, "valu_busy_pct": 48.7, "avg_us": 173.3},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 6.4, "valu_busy_pct": 26.6, "avg_us": 31.4},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.2, "valu_busy_pct": 49.6, "avg_us": 180.4},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 21.9, "valu_busy_pct": 36.4, "avg_us": 245.4},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
