@@ -282,14 +282,14 @@ __device__ __forceinline__ void invert_unit_triangular(float* G, int l, int iw =
 
 // ---------------------------------------------------------------- prep ----
 // grid (nch, Hk, B), eight waves (two per SIMD).  MODE kPrepFwd / kPrepBwd:
-// the forward (reverse) records of the kv head's value heads, two at a time,
-// each formed by four waves (waves 4 s .. 4 s + 3 for head slot s): they
-// build Gam as running products down the rows (rows 63..32 from 1, rows
-// 31..0 from a product scan, each wave storing a quarter of the rows), split
-// the M (Mq) record and the rows of A (Bm), then the first forms the inverse,
-// and they split the T (Tb) record (five barriers per round).  The workgroup
-// then holds two per-head matrices, 51 KB of LDS, and three workgroups share a
-// CU.  kPrepBoth: waves 0-3 the forward and waves 4-7 the reverse records of
+// the forward (reverse) records of the kv head's value heads (or of a pair
+// of them: a.pair_grid), two at a time, each formed by four waves (waves
+// 4 s .. 4 s + 3 for head slot s): they build Gam as running products down
+// the rows, a quarter of the rows each, split the M (Mq) record and the rows
+// of A (Bm), the first forms the diagonal blocks of the inverse, all four its
+// L blocks, the first its block rows, and they split the T (Tb) record (seven
+// barriers per round).  The workgroup holds two per-head matrices, 51 KB of
+// LDS, and three workgroups share a CU.  kPrepBoth: waves 0-3 the forward and waves 4-7 the reverse records of
 // the same heads, each wave every step of its head alone (the Gram matrices
 // formed once for both); the backward's replay uses it.  Every record element
 // takes the same operations in every mode, so the records are bitwise the
