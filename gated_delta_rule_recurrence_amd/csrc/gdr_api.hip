@@ -86,7 +86,8 @@ int check_shape(const gdr_shape* s, Sizes* z) {
   r.ntiles = (s->T + r.L - 1) / r.L;
   r.nseg = (s->T + s->chunk - 1) / s->chunk;
   r.replay = s->chunk > kMaxTile;
-  r.chunked = gdr::chunked_sweep_ok(s->Hk, s->Hv, s->Dk, s->Dv, r.L, s->T);
+  r.chunked = gdr::chunked_sweep_ok(s->Hk, s->Hv, s->Dk, s->Dv, r.L, s->T,
+                                    s->dtype == GDR_BF16);
   int64_t bh, mat, x, tiles, b_tiles, b_rows, b_seg;
   if (!mul_ok(s->B, s->Hv, &bh) || !mul_ok(s->Dv, s->Dk, &mat) ||
       !mul_ok(bh, mat, &r.state) || !mul_ok(r.state, r.ntiles, &tiles) ||

@@ -36,9 +36,9 @@
 // Each substitution forms the same sums as the sequential recurrence.  The
 // sweep kernels then run a value head's chunks in order (reverse order for
 // the gradient), 32 state rows per workgroup.  Rows are independent.  With
-// fp32 inputs every product runs on fp32 MFMA; with bf16 inputs (the
-// *_bf16_kernel sweeps) on bf16 MFMA over exact three-piece splits of the
-// fp32 operands.  A replay mode of the forward (FwdSweepArgs::seg) rebuilds
+// fp32 inputs every product runs on fp32 MFMA (Dk <= 192); with bf16 inputs
+// (the *_bf16_kernel sweeps, Dk <= 256) on bf16 MFMA over exact three-piece
+// splits of the fp32 operands.  A replay mode of the forward (FwdSweepArgs::seg) rebuilds
 // the tile states and residuals for the backward from states saved every
 // few tiles.
 //
@@ -58,7 +58,9 @@ constexpr int kNP = kN + 1;   // row stride of the Gram matrices in the prep
 constexpr int kGP = kN + 4;   // row stride of the per-head matrix (16-byte rows)
 constexpr int kDS = 32;       // state rows per sweep workgroup
 constexpr int kUBS = 36;      // row stride of the [kN][kDS] step-by-row stages
-constexpr int kMaxJT = 12;    // Dk <= 192 (LDS of the sweep kernels)
+constexpr int kMaxJT = 12;    // Dk <= 192: the fp32-operand sweeps (their LDS); the
+                              // prep's bf16 Gram stage takes Dk in passes of this width
+constexpr int kMaxJTB = 16;   // Dk <= 256: the bf16-product sweeps
 
 // The products over the steps of a chunk (E = T U, Y = M E, C = Tb U,
 // U += Mq DY and the state updates) use step rstep(ks, lq) as the k index
@@ -375,56 +377,61 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_kernel(
   for (int u = 0; u < 4; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
   if (kBf16 && Dk % 8 == 0) {
     // bf16 k, q: the rows staged as bf16 and multiplied on bf16 MFMA (the
-    // products of two bf16 values are exact in fp32, as in the fp32 path)
-    constexpr int NCH = 2 * kMaxJT;                  // 16-byte chunks per row
+    // products of two bf16 values are exact in fp32, as in the fp32 path).
+    // The stage holds 192 columns: a wider Dk takes a second pass, the
+    // accumulators carried over (the same k-steps in the same order).
+    constexpr int PW = 16 * kMaxJT;                  // columns per pass
+    constexpr int NCH = PW / 8;                      // 16-byte chunks per row
     constexpr int NL = (kN * NCH + NTH - 1) / NTH;
     uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
     uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
-    uint4 rq[NL], rk[NL];
+    for (int j0 = 0; j0 < Dk; j0 += PW) {
+      uint4 rq[NL], rk[NL];
 #pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int ci = tid + NTH * u;
-      const int s = ci / NCH, j = 8 * (ci % NCH);
-      const bool ok = ci < kN * NCH && s < n && j < Dk;
-      int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j : 0;
-      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
-      rq[u] = *reinterpret_cast<const uint4*>(q + o);
-      rk[u] = *reinterpret_cast<const uint4*>(k + o);
-    }
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int ci = tid + NTH * u;
-      const int s = ci / NCH, j = 8 * (ci % NCH);
-      const bool ok = ci < kN * NCH && s < n && j < Dk;
-      if (ci < kN * NCH) {
-        uint4 xq = rq[u], xk = rk[u];
-        xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
-        xq.y = ok ? xq.y : 0u;
-        xq.z = ok ? xq.z : 0u;
-        xq.w = ok ? xq.w : 0u;
-        xk.x = ok ? xk.x : 0u;
-        xk.y = ok ? xk.y : 0u;
-        xk.z = ok ? xk.z : 0u;
-        xk.w = ok ? xk.w : 0u;
-        *reinterpret_cast<uint4*>(sq + s * L::KGS + j) = xq;
-        *reinterpret_cast<uint4*>(sk + s * L::KGS + j) = xk;
+      for (int u = 0; u < NL; ++u) {
+        const int ci = tid + NTH * u;
+        const int s = ci / NCH, j = j0 + 8 * (ci % NCH);
+        const bool ok = ci < kN * NCH && s < n && j < Dk;
+        int64_t o = ok ? ((int64_t)(b * (int64_t)T + t0 + s) * Hk + hk) * Dk + j : 0;
+        asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
+        rq[u] = *reinterpret_cast<const uint4*>(q + o);
+        rk[u] = *reinterpret_cast<const uint4*>(k + o);
       }
-    }
-    __syncthreads();
-    for (int ks = 0; 32 * ks < Dk; ++ks) {
-      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
-      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
-      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        const int tb = 2 * half + x;
-        const uint4 bk =
-            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
-        acc[x] = mfma_bf16(aq, bk, acc[x]);
-        acc[2 + x] = mfma_bf16(ak, bk, acc[2 + x]);
+      for (int u = 0; u < NL; ++u) {
+        const int ci = tid + NTH * u;
+        const int s = ci / NCH, jl = 8 * (ci % NCH);
+        const bool ok = ci < kN * NCH && s < n && j0 + jl < Dk;
+        if (ci < kN * NCH) {
+          uint4 xq = rq[u], xk = rk[u];
+          xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
+          xq.y = ok ? xq.y : 0u;
+          xq.z = ok ? xq.z : 0u;
+          xq.w = ok ? xq.w : 0u;
+          xk.x = ok ? xk.x : 0u;
+          xk.y = ok ? xk.y : 0u;
+          xk.z = ok ? xk.z : 0u;
+          xk.w = ok ? xk.w : 0u;
+          *reinterpret_cast<uint4*>(sq + s * L::KGS + jl) = xq;
+          *reinterpret_cast<uint4*>(sk + s * L::KGS + jl) = xk;
+        }
       }
+      __syncthreads();
+      for (int ks = 0; ks < PW / 32 && j0 + 32 * ks < Dk; ++ks) {
+        const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
+        const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
+        const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int tb = 2 * half + x;
+          const uint4 bk =
+              *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
+          acc[x] = mfma_bf16(aq, bk, acc[x]);
+          acc[2 + x] = mfma_bf16(ak, bk, acc[2 + x]);
+        }
+      }
+      __syncthreads();  // the stage aliases the per-head arrays (and the next pass's)
     }
-    __syncthreads();  // the stage aliases the per-head arrays
   } else {
     constexpr int NB = kMaxJT / 4, NU = 4 * 256 / NTH;
     Quad<TIn, VEC> rq[NB][NU], rk[NB][NU];
@@ -1181,14 +1188,20 @@ struct SLB {
   static constexpr int KR = 0;                    // float offsets below
   static constexpr int QR = KR + kN * KRS / 2;
   static constexpr int SP = QR + kN * KRS / 2;
-  static constexpr int EP = SP + 3 * DKP * kDS / 2;  // diag(ks) E pieces
-  static constexpr int UP = EP + 3 * PS / 2;          // U pieces
-  static constexpr int EQ = UP + 3 * PS / 2;          // E pieces
-  static constexpr int SIZE = EQ + 3 * PS / 2;
+  // Dk above 192: the E and diag(ks) E pieces overlay the q tile, which X =
+  // [K; Q] S^T reads before the barrier after which they are written, and
+  // which the next chunk's deposit rewrites only after the barrier that
+  // follows their last reads
+  static constexpr bool QALIAS = JT > kMaxJT;
+  static constexpr int EP = QALIAS ? QR : SP + 3 * DKP * kDS / 2;  // diag(ks) E pieces
+  static constexpr int UP = QALIAS ? SP + 3 * DKP * kDS / 2 : EP + 3 * PS / 2;  // U pieces
+  static constexpr int EQ = QALIAS ? EP + 3 * PS / 2 : UP + 3 * PS / 2;          // E pieces
+  static constexpr int SIZE = QALIAS ? UP + 3 * PS / 2 : EQ + 3 * PS / 2;
   static_assert((2 * KRS) % 256 == 128 && (2 * KTS) % 32 == 16, "row strides");
   static_assert(DKP % 64 == 0, "16 blocks per swizzle group");
   static_assert(QR % 4 == 0 && SP % 4 == 0 && EP % 4 == 0 && UP % 4 == 0 && EQ % 4 == 0,
                 "16-byte aligned regions");
+  static_assert(!QALIAS || EQ + 3 * PS / 2 <= SP, "E pieces inside the q tile");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
@@ -1657,8 +1670,13 @@ struct SLR {
   static constexpr int QR = KR + kN * KRS / 2;
   static constexpr int HT = QR + kN * KRS / 2;        // gradient pieces [3][DKP][kDS]
   static constexpr int DPP = HT + 3 * DKP * kDS / 2;  // diag(pre) DY pieces [3][kDS][KTS]
-  static constexpr int CPP = DPP + 3 * PS / 2;        // -diag(beta pre) C pieces
-  static constexpr int DYT = CPP + 3 * PS / 2;        // dy bf16 [kDS][KTS]
+  // Dk above 192: the -diag(beta pre) C pieces overlay the gradient pieces,
+  // which X = K Hend^T reads before the barrier after which they are
+  // written, and which are rewritten only after the barrier that follows
+  // their last reads
+  static constexpr bool HALIAS = JT > kMaxJT;
+  static constexpr int CPP = HALIAS ? HT : DPP + 3 * PS / 2;  // -diag(beta pre) C pieces
+  static constexpr int DYT = HALIAS ? DPP + 3 * PS / 2 : CPP + 3 * PS / 2;  // dy bf16 [kDS][KTS]
   static constexpr int UP = DYT + PS / 2;             // U pieces [3][kDS][KTS]
   static constexpr int SIZE = UP + 3 * PS / 2;
   static_assert((2 * KRS) % 256 == 128, "k, q row stride");
@@ -1667,6 +1685,7 @@ struct SLR {
   static_assert(QR % 4 == 0 && HT % 4 == 0 && DPP % 4 == 0 && CPP % 4 == 0 && DYT % 4 == 0 &&
                     UP % 4 == 0,
                 "alignment");
+  static_assert(!HALIAS || 3 * PS <= 3 * DKP * kDS, "C pieces inside the gradient pieces");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS");
 };
 
@@ -1989,44 +2008,53 @@ hipError_t launch_prep(ChunkedSweepShape sh, float* prep_f, float* prep_b, hipSt
   return launch(prep_kernel<TIn, MODE, false>, grid, kPrepThreads, lds, s, sh, prep_f, prep_b);
 }
 
+// The bf16-product sweep of JT 16-column Dk tiles.
+template <int JT, bool BWD, typename Args>
+hipError_t launch_bf16_sweep(const Args& A, dim3 grid, hipStream_t s) {
+  if constexpr (BWD) {
+    return launch(bwd_chunked_bf16_kernel<JT>, grid, kSwThreads, sizeof(float) * SLR<JT>::SIZE,
+                  s, A);
+  } else {
+    const size_t lb = sizeof(float) * SLB<JT>::SIZE;
+    const FwdSweepArgs& f = A.s;
+    const bool gen = f.seg > 0 || f.ck_every != 1 || f.s0_stride != 1 || f.nslot != f.nch ||
+                     f.y == nullptr || (f.Sck != nullptr && f.E == nullptr);
+    if (f.Sck != nullptr)
+      return gen ? launch(fwd_chunked_bf16_kernel<JT, true, true>, grid, kSwThreads, lb, s, A)
+                 : launch(fwd_chunked_bf16_kernel<JT, true, false>, grid, kSwThreads, lb, s, A);
+    return gen ? launch(fwd_chunked_bf16_kernel<JT, false, true>, grid, kSwThreads, lb, s, A)
+               : launch(fwd_chunked_bf16_kernel<JT, false, false>, grid, kSwThreads, lb, s, A);
+  }
+}
+
 template <typename TIn, bool BWD, typename Args>
 hipError_t launch_sweep(const Args& A, int Dk, int Dv, int Hv, int B, hipStream_t s) {
   const dim3 grid((Dv + kDS - 1) / kDS, Hv, B);
   const int jt = (Dk + 15) / 16;
   const bool vec = Dk % 4 == 0;  // 4-element groups of a row start on a 4-element boundary
+  // bf16 k, q in 8-element groups (and 4-element row blocks of the value
+  // rows): the bf16-product kernels
+  constexpr bool kBf16 = std::is_same<TIn, gdr::bf16>::value;
+  const bool pieces = kBf16 && vec && bf16_products(true, Dk, Dv);
   auto go = [&](auto jtc, auto vc) {
     constexpr int JT = decltype(jtc)::value;
     constexpr bool V = decltype(vc)::value;
+    if constexpr (kBf16 && V)
+      if (pieces) return launch_bf16_sweep<JT, BWD>(A, grid, s);
     const size_t lds = sizeof(float) * SL<JT>::SIZE;
-    if constexpr (BWD) {
-      if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
-        if (bf16_products(true, Dk, Dv))
-          return launch(bwd_chunked_bf16_kernel<JT>, grid, kSwThreads,
-                        sizeof(float) * SLR<JT>::SIZE, s, A);
+    if constexpr (BWD)
       return launch(bwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
-    } else {
-      // bf16 k, q in 8-element groups (and 4-element row blocks of the value
-      // outputs): the bf16-product kernel
-      if constexpr (std::is_same<TIn, gdr::bf16>::value && V)
-        if (bf16_products(true, Dk, Dv)) {
-          const size_t lb = sizeof(float) * SLB<JT>::SIZE;
-          const FwdSweepArgs& f = A.s;
-          const bool gen = f.seg > 0 || f.ck_every != 1 || f.s0_stride != 1 ||
-                           f.nslot != f.nch || f.y == nullptr ||
-                           (f.Sck != nullptr && f.E == nullptr);
-          if (f.Sck != nullptr)
-            return gen ? launch(fwd_chunked_bf16_kernel<JT, true, true>, grid, kSwThreads, lb, s, A)
-                       : launch(fwd_chunked_bf16_kernel<JT, true, false>, grid, kSwThreads, lb, s, A);
-          return gen ? launch(fwd_chunked_bf16_kernel<JT, false, true>, grid, kSwThreads, lb, s, A)
-                     : launch(fwd_chunked_bf16_kernel<JT, false, false>, grid, kSwThreads, lb, s, A);
-        }
+    else
       return launch(fwd_chunked_kernel<TIn, JT, V>, grid, kSwThreads, lds, s, A);
-    }
   };
   using I4 = std::integral_constant<int, 4>;
   using I8 = std::integral_constant<int, 8>;
   using I12 = std::integral_constant<int, 12>;
-  if (jt > kMaxJT) return hipErrorInvalidValue;
+  if (jt > kMaxJT) {
+    // Dk above 192: the bf16-product kernels alone
+    if (pieces && jt <= kMaxJTB) return launch_bf16_sweep<kMaxJTB, BWD>(A, grid, s);
+    return hipErrorInvalidValue;
+  }
   if (vec) {
     if (jt <= 4) return go(I4{}, std::true_type{});
     if (jt <= 8) return go(I8{}, std::true_type{});
@@ -2081,11 +2109,14 @@ hipError_t bwd_go(const BwdChunkedArgs& A, hipStream_t s) {
 
 }  // namespace
 
-bool chunked_sweep_ok(int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L, int64_t T) {
+bool chunked_sweep_ok(int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L, int64_t T,
+                      bool bf16) {
   // the sweep kernels index 64 steps of k, q, v, y with int offsets
   const int64_t lim = int64_t(1) << 31;
-  return Dk <= 16 * kMaxJT && L >= 16 && L <= kN && T >= L && kN * Hk * Dk < lim &&
-         kN * Hv * Dv < lim;
+  // Dk up to 192 on every form, up to 256 on the bf16-product sweeps
+  const bool dk_ok = Dk <= 16 * kMaxJT ||
+                     (Dk <= 16 * kMaxJTB && bf16_products(bf16, (int)Dk, (int)Dv));
+  return dk_ok && L >= 16 && L <= kN && T >= L && kN * Hk * Dk < lim && kN * Hv * Dv < lim;
 }
 
 int64_t chunked_prep_floats(int64_t B, int64_t Hv, int64_t nch) {

@@ -112,7 +112,8 @@ constexpr int kChunkPrepStride = 3 * 64 * 64 + 4 * 64;
 
 // Whether the chunked sweeps take this shape, and the floats of their prep
 // records.
-bool chunked_sweep_ok(int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L, int64_t T);
+bool chunked_sweep_ok(int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L, int64_t T,
+                      bool bf16);
 int64_t chunked_prep_floats(int64_t B, int64_t Hv, int64_t nch);
 hipError_t launch_fwd_chunked(const FwdChunkedArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_bwd_chunked(const BwdChunkedArgs& a, bool bf16, hipStream_t s);

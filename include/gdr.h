@@ -117,8 +117,9 @@ int gdr_checkpoint_bytes(const gdr_shape* shape, size_t* out);
  * (summed over the groups into dq, dk). */
 int gdr_backward_workspace_bytes(const gdr_shape* shape, size_t* out);
 
-/* Bytes of the scratch buffer gdr_forward needs.  Shapes with Dk <= 192, a
- * tile of 16 to 64 steps and T at least one tile take the chunked forward
+/* Bytes of the scratch buffer gdr_forward needs.  Shapes with Dk <= 192 (or
+ * Dk <= 256 for bf16 inputs with Dk a multiple of 8 and Dv of 4), a tile of
+ * 16 to 64 steps and T at least one tile take the chunked forward
  * (the products inside a tile on matrix cores), which keeps two 64 x 64 fp32
  * matrices and three vectors per (batch row, value head, tile) here; every
  * other shape takes the sequential sweep and needs 0 bytes. */

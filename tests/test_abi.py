@@ -99,25 +99,31 @@ def _tile(C):
     return C if C <= 64 else max(d for d in range(1, 65) if C % d == 0)
 
 
-@pytest.mark.parametrize("B,T,Hk,Hv,Dk,Dv,C", [
-    (1, 4, 2, 4, 8, 8, 2), (1, 2048, 16, 64, 192, 128, 64),
-    (4, 8192, 16, 64, 192, 128, 64), (2, 5, 1, 3, 7, 5, 64), (1, 0, 1, 1, 4, 4, 8),
-    (1, 2048, 16, 64, 192, 128, 512), (4, 8192, 16, 64, 192, 128, 256),
-    (1, 300, 2, 4, 64, 32, 256), (2, 230, 1, 2, 200, 40, 100), (1, 50, 1, 2, 8, 8, 97),
+@pytest.mark.parametrize("B,T,Hk,Hv,Dk,Dv,C,bf16", [
+    (1, 4, 2, 4, 8, 8, 2, 0), (1, 2048, 16, 64, 192, 128, 64, 0),
+    (4, 8192, 16, 64, 192, 128, 64, 0), (2, 5, 1, 3, 7, 5, 64, 0), (1, 0, 1, 1, 4, 4, 8, 0),
+    (1, 2048, 16, 64, 192, 128, 512, 0), (4, 8192, 16, 64, 192, 128, 256, 0),
+    (1, 300, 2, 4, 64, 32, 256, 0), (2, 230, 1, 2, 200, 40, 100, 0), (1, 50, 1, 2, 8, 8, 97, 0),
+    (1, 2048, 16, 64, 256, 128, 64, 1), (2, 230, 1, 2, 200, 40, 100, 1),
+    (1, 300, 2, 4, 256, 64, 128, 1), (1, 300, 2, 4, 252, 64, 64, 1),
+    (1, 300, 2, 4, 256, 66, 64, 1), (1, 300, 2, 4, 256, 64, 64, 0),
 ])
-def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C):
-    sh = S(B, T, Hk, Hv, Dk, Dv, C)
+def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C, bf16):
+    sh = S(B, T, Hk, Hv, Dk, Dv, C, dtype=_lib.GDR_BF16 if bf16 else _lib.GDR_F32)
     L = _tile(C)
     ntiles = (T + L - 1) // L
     nseg = (T + C - 1) // C
     assert _lib.num_chunks(sh) == nseg
     state = B * Hv * Dv * Dk * 4
     rows = B * T * Hv * Dv * 4
-    # the chunked sweeps (Dk <= 192, a tile of 16..64 steps, T >= one tile)
-    # keep two 64 x 64 matrices (room for three bf16 pieces of each: 3 x 64 x
-    # 64 floats) and three 64-vectors per (batch row, value head, tile), plus
-    # 64 floats: the whole forward workspace
-    chunked = Dk <= 192 and 16 <= L <= 64 and T >= L
+    # the chunked sweeps (Dk <= 192, or Dk <= 256 with bf16 inputs whose k
+    # rows come in 8-element groups and value rows in 4-element blocks; a
+    # tile of 16..64 steps, T >= one tile) keep two 64 x 64 matrices (room
+    # for three bf16 pieces of each: 3 x 64 x 64 floats) and three 64-vectors
+    # per (batch row, value head, tile), plus 64 floats: the whole forward
+    # workspace
+    wide = bf16 and Dk <= 256 and Dk % 8 == 0 and Dv % 4 == 0
+    chunked = (Dk <= 192 or wide) and 16 <= L <= 64 and T >= L
     prep = B * Hv * ntiles * (3 * 64 * 64 + 4 * 64) * 4 if chunked else 0
     assert _lib.forward_workspace_bytes(sh) == prep
     # C <= 64: a state per chunk and the per-step residuals; C > 64: only the

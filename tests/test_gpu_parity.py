@@ -398,6 +398,38 @@ def test_rows_per_lane_variants(cuda, B, dtype):
     compare(run_gpu(p, cuda, 16), run_oracle(p), TOL[dtype], f"wide B={B} {dtype}")
 
 
+@pytest.mark.parametrize("Dk,chunk", [(256, 64), (232, 48), (248, 16)])
+def test_bf16_wide_keys_chunked(cuda, Dk, chunk):
+    """Dk above 192 with bf16 inputs runs the chunked sweeps with 256-column
+    tiles (the E and C pieces overlaid on the q tile and on the gradient
+    pieces, the prep's Gram products over Dk in two column passes): three
+    32-row blocks, a ragged last tile, two batch rows, S0 and dS_T, mixed
+    decay.  The bf16 outputs meet the bf16 bar and the fp32 outputs S_T, dS0
+    the fp32 bar."""
+    from gated_delta_rule_recurrence_amd import _lib
+    p = inputs.draw(2, 150, 2, 4, Dk, 96, seed=79 + Dk, normalised=True, decay="mix",
+                    S0_std=0.1, dST_std=1.0, dtype="bf16")
+    sh = _lib.make_shape(2, 150, 2, 4, Dk, 96, chunk, _lib.GDR_BF16, 0)
+    assert _lib.forward_workspace_bytes(sh) > 0, "not the chunked sweeps"
+    log(f"bf16 wide keys Dk={Dk} chunk={chunk}")
+    errs = compare(run_gpu(p, cuda, chunk), run_oracle(p), TOL["bf16"], f"bf16 Dk={Dk}")
+    for name in ("S_T", "dS0"):
+        assert errs[name] <= TOL["f32"], f"bf16 Dk={Dk}: {name} rel L2 {errs[name]:.2e}"
+
+
+def test_bf16_wide_keys_replay(cuda):
+    """C = 128 at Dk = 256: the backward's replay (the prep forming both
+    record sets in one launch, the forward sweep in its general form) gives
+    every output bit for bit as C = 64."""
+    p = _masked(inputs.draw(2, 300, 2, 4, 256, 64, seed=83, normalised=True, decay="mix",
+                            S0_std=0.1, dST_std=1.0, dtype="bf16"), 83)
+    log("C=128 vs C=64, Dk=256 bf16")
+    a, b = run_gpu(p, cuda, 128), run_gpu(p, cuda, 64)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"Dk=256 C=128 vs 64: {n}")
+    compare(a, run_oracle(p), TOL["bf16"], "Dk=256 C=128")
+
+
 @pytest.mark.parametrize("dims", [(72, 30), (68, 40), (136, 24), (192, 40), (64, 36),
                                   (192, 20), (104, 48), (128, 64), (56, 16), (200, 40),
                                   (256, 64)])
@@ -410,8 +442,8 @@ def test_bf16_dims(cuda, dims, chunk):
     a short last 32-row block, Dv=36 and Dv=20 pair the bf16-product sweeps
     with the fp32-operand chunk kernel; Dk=104 and 128 (128-column tiles) and
     56 (a 64-column tile) cover the other widths of the eight-wave chunk
-    kernel, Dk=200 and 256 (per-step sweeps) the four-wave chunk kernel's
-    bf16 products; T=70 leaves a short last chunk."""
+    kernel, Dk=200 and 256 (chunked sweeps with 256-column tiles) the
+    four-wave chunk kernel's bf16 products; T=70 leaves a short last chunk."""
     Dk, Dv = dims
     p = inputs.draw(1, 70, 2, 4, Dk, Dv, seed=23, normalised=True, S0_std=0.2,
                     dST_std=1.0, dtype="bf16")
