@@ -36,13 +36,12 @@
 // operands are staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a
 // fragment (lane l <-> m = l % 16, k = l / 16) is 64 consecutive floats, 16
 // Dv rows per block, with the next block fetched into registers while the
-// current one is multiplied.  With bf16 inputs (BFP below) the same passes
-// run on bf16 MFMA over exact three-piece splits of the fp32 operands.
+// current one is multiplied.
 //
-// bf16 inputs whose Dk and Dv are multiples of 8 with 48 < Dk <= 192 take the
-// eight-wave form of this computation instead (chunk_bf16_kernel,
-// gdr_chunk_bf16.hip); this file keeps fp32 inputs, the other bf16 shapes and
-// Dk above 192.
+// bf16 inputs whose Dk and Dv are multiples of 8 with 48 < Dk <= 256 take the
+// eight-wave form of this computation instead, with every contraction on bf16
+// MFMA (chunk_bf16_kernel, gdr_chunk_bf16.hip); this file keeps fp32 inputs
+// and the other bf16 shapes.
 #include "gdr_device.h"
 #include "gdr_internal.h"
 
@@ -70,44 +69,15 @@ struct CL {  // LDS layout, offsets in floats
   static constexpr int ST_S = 0, ST_H = kKB * PCP, ST_Y = 2 * kKB * PCP,
                        ST_C = ST_Y + kKB * kN, ST_E = ST_C + kKB * kN;
   static constexpr int STAGE = ST_E + kKB * kN;
-  // bf16-product stage (bf16 dy, PC = 64): S0, H1 as three bf16 pieces each
-  // [3][kKB][PC] (swizzled tiles, rows i, read through lds_read_tr16) and,
-  // in the first pass of a value head, the E pieces [3][kN][YS] (rows t,
-  // columns i; the row stride of 80 bytes puts the 16-byte accesses of 16
-  // rows on distinct banks).  dy and C, and E outside the Gram, go from
-  // global memory straight to the registers of the wave that owns the steps.
-  static constexpr int YS = kKB + 8;
-  static constexpr int BS_S = 0, BS_H = BS_S + 3 * kKB * PC / 2,
-                       BS_E = BS_H + 3 * kKB * PC / 2;
-  static constexpr int BSTAGE = BS_E + 3 * kN * YS / 2;
-  static_assert((2 * YS) % 32 == 16, "dy, C, E row stride");
-  // per-head M and the Phi', Psi' accumulators of every lane ([8][kThreads]
-  // f4, in lane order), after the Dv pass (alias the stage).  M is fp32
-  // [kN][kNP] or, with bf16 products, M^T as three bf16 pieces [3][kN][MS]
-  // (rows r, columns s; the row stride an odd multiple of 16 bytes)
-  static constexpr int MS = kN + 8;
-  static constexpr int MZW = kN * kNP > 3 * kN * MS / 2 ? kN * kNP : 3 * kN * MS / 2;
-  static constexpr int MZ = 0, GRD = (MZ + MZW + 3) & ~3;
+  // per-head M [kN][kNP] and the Phi', Psi' accumulators of every lane
+  // ([8][kThreads] f4, in lane order), after the Dv pass (alias the stage)
+  static constexpr int MZ = 0, GRD = (MZ + kN * kNP + 3) & ~3;
   static constexpr int HEAD = GRD + 8 * kThreads * 4;
-  static_assert((2 * MS) % 32 == 16, "M piece row stride");
-  // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns); with
-  // bf16 products, q, k rows as bf16 [kN][KGS] (the row stride an odd
-  // number of 16-byte units: the operand reads of 16 rows hit distinct banks)
-  static constexpr int QS = 0, KS = 64 * kN, QKST0 = 2 * 64 * kN;
-  static constexpr int KGS = DKP + 8;
-  static constexpr int BQ = 0, BK = kN * KGS / 2, QKSTB = kN * KGS;
-  static constexpr int QKST = QKST0 > QKSTB ? QKST0 : QKSTB;
+  // q, k stage of the QK/KK pass: [16][kN][4] each (64 Dk columns)
+  static constexpr int QS = 0, KS = 64 * kN, QKST = 2 * 64 * kN;
   // k, q stage of the final products: [kSB/4][DKP][4] each
   static constexpr int FK = 0, FQ = kSB * DKP, FINAL = 2 * kSB * DKP;
-  // with bf16 products: k, q rows as swizzled bf16 tiles [kN][KFS] (the row
-  // stride an odd multiple of 128 bytes), in the aliased region when they
-  // fit; a weight matrix W[s][t] as three bf16 pieces [3][kN][WS] (rows t),
-  // in the QK, KK region (free after the value heads)
-  static constexpr int KFS = DKP % 128 == 0 ? DKP + 64 : DKP;
-  static constexpr int BFK = 0, BFQ = kN * KFS / 2, BFINAL = kN * KFS;
-  static constexpr int WS = kN + 8;
-  static constexpr int A_SZB = STAGE > BSTAGE ? STAGE : BSTAGE;
-  static constexpr int A_SZ0 = A_SZB > HEAD ? A_SZB : HEAD;
+  static constexpr int A_SZ0 = STAGE > HEAD ? STAGE : HEAD;
   static constexpr int A_SZ1 = A_SZ0 > QKST ? A_SZ0 : QKST;
   static constexpr int A_SZ = A_SZ1 > FINAL ? A_SZ1 : FINAL;
   // per-head vectors
@@ -124,8 +94,6 @@ struct CL {  // LDS layout, offsets in floats
   static constexpr int QK = V_SCR + kThreads, KK = QK + kN * kNP,
                        W1 = KK + kN * kNP, W2 = W1 + kN * kNP, GM = W2 + kN * kNP;
   static constexpr int SIZE = GM + kN * kNP;
-  static constexpr bool BF_FINAL = BFINAL <= A_SZ && DKP % 64 == 0;
-  static_assert(3 * kN * WS / 2 <= 2 * kN * kNP && (2 * WS) % 32 == 16, "W pieces");
   static_assert(SIZE * 4 <= 160 * 1024, "LDS budget of one workgroup");
   static_assert(JT % JPW == 0, "whole passes");
 };
@@ -158,20 +126,9 @@ __device__ __forceinline__ f4 ld4(const T* __restrict__ p, int64_t o, bool ok,
   return r;
 }
 
-// BFP (bf16 inputs, PC = 64, Dk and Dv multiples of 8): the Dv pass on bf16 MFMA,
-// the fp32 operands (S0, H1, C, E) split exactly into three bf16 pieces;
-// a product with bf16 dy takes the three pieces, a product of two fp32
-// operands the six piece products down to the order of fp32 rounding.  S0,
-// H1 (and, for the Gram, E) are staged in LDS as pieces; each wave's own dy,
-// C, E rows go from global memory to its registers and are split there.
-// QK, KK (bf16 rows), the final products (each W as three pieces) and the dg
-// product Gam [M | chi] (Gam rows, M^T and chi as three pieces each, six
-// piece products) run on bf16 MFMA as well.
-template <typename TIn, int JT, bool VEC, bool BFP>
+template <typename TIn, int JT, bool VEC>
 __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   using L = CL<JT>;
-  static_assert(!BFP || (std::is_same<TIn, bf16>::value && VEC && L::PC == 64),
-                "bf16 products: bf16 inputs in 64-column passes");
   constexpr int DKP = L::DKP;
   constexpr int JPW = L::JPW, NJP = L::NJP, PC = L::PC;
   constexpr int PCP = L::PCP;
@@ -231,22 +188,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     Quad<TIn, VEC> y[2];
     uint32_t ms;  // validity: 4 bits per S0/H1 quad, then 4 per dy/e/c quad
   };
-  // S0, H1 slices are read once (each pass its own columns): non-temporal
-  // loads keep them from displacing the dy, C, E rows that every pass of a
-  // value head reads again
-  auto ld_nt = [](const float* p, int64_t o, bool ok) __attribute__((always_inline)) {
-    const f4 x = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p + (ok ? o : 0)));
-    return float4{x[0], x[1], x[2], x[3]};
-  };
-  struct SlotB {
-    Quad<float, true> s[2], h[2], e[2], c[2];
-    uint4 y;
-    uint32_t ms;  // validity: S0/H1 quads (bits 0, 1), the e, c, dy row (2)
-  };
-  using RSlot = typename std::conditional<BFP, SlotB, Slot>::type;
-  RSlot RA, RB;
+  Slot RA, RB;
   float hs = 0.f;  // partial <H1, S0> of the current value head
-  auto fetch = [&](RSlot& R, int gbi) __attribute__((always_inline)) {
+  auto fetch = [&](Slot& R, int gbi) __attribute__((always_inline)) {
     const int hb = gbi / (NJP * nbk);
     const int rem = gbi - hb * (NJP * nbk);
     const int jp = rem / nbk;
@@ -256,35 +200,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     const float* __restrict__ H1 = a.Hck + (bh * a.nch + jc) * mat;
     const int64_t rowbase = ((int64_t)b * T + t0) * tstride + (bh - (int64_t)b * Hv) * Dv;
     uint32_t m = 0;
-    if constexpr (BFP) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qd = tid + kThreads * u;  // row qd / 16, columns 4 (qd % 16) ..
-        const int i = i0 + qd / 16, j = 64 * jp + 4 * (qd % 16);
-        const bool ok = i < Dv && j < Dk;
-        const int64_t o = (int64_t)i * Dk + j;
-        R.s[u].v = ld_nt(S0, o, ok);
-        R.h[u].v = ld_nt(H1, o, ok);
-        m |= (uint32_t)ok << u;
-      }
-      // e, c, dy of step tw + lr (this wave's), Dv rows i0 + 8 lq .. +7
-      // (Dv is a multiple of 8: the eight are all inside or all outside)
-      const int i = i0 + 8 * lq;
-      const bool ok = tw + lr < n && i < Dv;
-      const int64_t o = rowbase + (tw + lr) * tstride + i;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        R.e[u].load(a.E, o + 4 * u, ok, 4);
-        R.c[u].load(a.C, o + 4 * u, ok, 4);
-      }
-      {
-        int64_t oy = ok ? o : 0;
-        asm volatile("" : "+v"(oy));  // keeps the select (no branch around the load)
-        R.y = *reinterpret_cast<const uint4*>(dy + oy);
-      }
-      m |= (uint32_t)ok << 2;
-      R.ms = m;
-    } else {
 #pragma unroll
     for (int u = 0; u < SQT; ++u) {
       const int qd = tid + kThreads * u;
@@ -306,69 +221,9 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       m |= Quad<float, VEC>::mask(ok, Dv - i) << (16 + 4 * u);
     }
     R.ms = m;
-    }
   };
-  // this wave's dy, C, E operands of one block (bf16 products): rows
-  // tw + lr, Dv rows 8 lq .. +7 of the block; C, E as three bf16 pieces
-  struct Ops {
-    uint4 fy, fc[3], fe[3];
-  };
-  auto pieces8 = [](const f4& x0, const f4& x1, uint4 (&f)[3]) __attribute__((always_inline)) {
-    uint2 a0, a1, a2, b0, b1, b2;
-    split3_quad(x0, a0, a1, a2);
-    split3_quad(x1, b0, b1, b2);
-    f[0] = uint4{a0.x, a0.y, b0.x, b0.y};
-    f[1] = uint4{a1.x, a1.y, b1.x, b1.y};
-    f[2] = uint4{a2.x, a2.y, b2.x, b2.y};
-  };
-  auto split_e = [&](const SlotB& R, Ops& op) __attribute__((always_inline)) {
-    const uint32_t mu = ((R.ms >> 2) & 1u) ? 15u : 0u;
-    pieces8(R.e[0].get(mu), R.e[1].get(mu), op.fe);
-  };
-  auto split_cy = [&](const SlotB& R, Ops& op) __attribute__((always_inline)) {
-    const bool ok = (R.ms >> 2) & 1u;
-    const uint32_t mu = ok ? 15u : 0u;
-    pieces8(R.c[0].get(mu), R.c[1].get(mu), op.fc);
-    op.fy.x = ok ? R.y.x : 0u;  // component selects (a vector select goes through memory)
-    op.fy.y = ok ? R.y.y : 0u;
-    op.fy.z = ok ? R.y.z : 0u;
-    op.fy.w = ok ? R.y.w : 0u;
-  };
-  // S0, H1 pieces of a block to LDS and, in the first pass of a value head
-  // (gram), this wave's E pieces (split into op.fe on the way)
-  auto deposit = [&](const RSlot& R, bool gram, Ops& op) __attribute__((always_inline)) {
-    if constexpr (BFP) {
-      uint16_t* const bs = reinterpret_cast<uint16_t*>(sm + L::BS_S);
-      uint16_t* const bh = reinterpret_cast<uint16_t*>(sm + L::BS_H);
-      uint16_t* const be = reinterpret_cast<uint16_t*>(sm + L::BS_E);
-      constexpr int SP = kKB * PC, YP = kN * L::YS;  // piece strides (bf16)
-      // three bf16 pieces of four fp32 values, stored as 8-byte blocks
-      auto put3 = [&](uint16_t* dst, int stride, int o, f4 v) __attribute__((always_inline)) {
-        uint2 p0, p1, p2;
-        split3_quad(v, p0, p1, p2);
-        *reinterpret_cast<uint2*>(dst + o) = p0;
-        *reinterpret_cast<uint2*>(dst + stride + o) = p1;
-        *reinterpret_cast<uint2*>(dst + 2 * stride + o) = p2;
-      };
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qd = tid + kThreads * u;
-        const int r = qd / 16, o = r * PC + 4 * ((qd % 16) ^ tile_swz(r));
-        const uint32_t mu = ((R.ms >> u) & 1u) ? 15u : 0u;
-        const f4 sv = R.s[u].get(mu), hv = R.h[u].get(mu);
-        // every element of the slice passes one thread once: <H1, S0>
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hs = fmaf(sv[e], hv[e], hs);
-        put3(bs, SP, o, sv);
-        put3(bh, SP, o, hv);
-      }
-      if (gram) {
-        split_e(R, op);
-        const int o = (tw + lr) * L::YS + 8 * lq;
-#pragma unroll
-        for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(be + p * YP + o) = op.fe[p];
-      }
-    } else {
+  // a block's S0, H1 slices and dy, E, C rows to the stage
+  auto deposit = [&](const Slot& R) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < SQT; ++u) {
       const int qd = tid + kThreads * u;
@@ -387,7 +242,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       *reinterpret_cast<f4*>(sm + L::ST_E + o) = R.e[u].get(mu);
       *reinterpret_cast<f4*>(sm + L::ST_C + o) = R.c[u].get(mu);
     }
-    }
   };
   // g, beta of step tid (threads tid < kN), a value head ahead; an identity
   // step (mask byte 0) has g = 1, beta = 0
@@ -397,81 +251,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
     return (int64_t)(b * (int64_t)T + t0 + (gb_ok ? tid : 0)) * Hv + hk * rep + hh;
   };
   // ---- QK and KK for the kv head (shared by all its value heads) ----------
-  if constexpr (BFP) {
-    // bf16 q, k rows staged as bf16, products on bf16 MFMA (exact products)
-    static_assert((2 * L::KGS) % 32 == 16, "q, k row stride");
-    constexpr int NCH = DKP / 8;  // 16-byte chunks per row
-    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
-    uint16_t* const sq = reinterpret_cast<uint16_t*>(sm + L::BQ);
-    uint16_t* const sk = reinterpret_cast<uint16_t*>(sm + L::BK);
-    uint4 rq[NL], rk[NL];
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int ci = tid + kThreads * u;
-      const int s = ci / NCH, j = 8 * (ci % NCH);
-      const bool ok = ci < kN * NCH && s < n && j < Dk;
-      int64_t o = ok ? qk_index(s, j) : 0;
-      asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
-      rq[u] = *reinterpret_cast<const uint4*>(q + o);
-      rk[u] = *reinterpret_cast<const uint4*>(k + o);
-    }
-    // the first two blocks of the Dv passes, in flight during QK and KK
-    // (issued after the q, k loads: waiting for those never waits for these)
-    fetch(RA, 0);
-    fetch(RB, 1);
-#pragma unroll
-    for (int u = 0; u < NL; ++u) {
-      const int ci = tid + kThreads * u;
-      const int s = ci / NCH, j = 8 * (ci % NCH);
-      const bool ok = ci < kN * NCH && s < n && j < Dk;
-      if (ci < kN * NCH) {
-        uint4 xq = rq[u], xk = rk[u];
-        xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
-        xq.y = ok ? xq.y : 0u;
-        xq.z = ok ? xq.z : 0u;
-        xq.w = ok ? xq.w : 0u;
-        xk.x = ok ? xk.x : 0u;
-        xk.y = ok ? xk.y : 0u;
-        xk.z = ok ? xk.z : 0u;
-        xk.w = ok ? xk.w : 0u;
-        *reinterpret_cast<uint4*>(sq + s * L::KGS + j) = xq;
-        *reinterpret_cast<uint4*>(sk + s * L::KGS + j) = xk;
-      }
-    }
-    __syncthreads();
-    f4 acc[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DKP / 32; ++ks) {
-      const int o = (tw + lr) * L::KGS + 32 * ks + 8 * lq;
-      const uint4 aq = *reinterpret_cast<const uint4*>(sq + o);
-      const uint4 ak = *reinterpret_cast<const uint4*>(sk + o);
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-        const uint4 bk =
-            *reinterpret_cast<const uint4*>(sk + (16 * tb + lr) * L::KGS + 32 * ks + 8 * lq);
-        acc[tb] = mfma_bf16(aq, bk, acc[tb]);
-        acc[4 + tb] = mfma_bf16(ak, bk, acc[4 + tb]);
-      }
-    }
-    __syncthreads();  // the stage is reused below
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int o = (tw + 4 * lq + v) * kNP + 16 * tb + lr;
-        sm[L::QK + o] = acc[tb][v];
-        sm[L::KK + o] = acc[4 + tb][v];
-      }
-#pragma unroll
-    for (int x = 0; x < 16; ++x) {  // running sums over the value heads
-      const int e = tid + kThreads * x;
-      const int o = (e >> 6) * kNP + (e & 63);
-      sm[L::W1 + o] = 0.f;
-      sm[L::W2 + o] = 0.f;
-    }
-  } else {
+  {
     f4 acc[8];  // QK tiles (w, 0..3), KK tiles (w, 0..3)
 #pragma unroll
     for (int u = 0; u < 8; ++u) acc[u] = f4{0.f, 0.f, 0.f, 0.f};
@@ -525,10 +305,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   }
 
   TIn g_nx = g[gb_index(0)], b_nx = beta[gb_index(0)];
-  if constexpr (!BFP) {
-    fetch(RA, 0);
-    fetch(RB, 1);
-  }
+  fetch(RA, 0);
+  fetch(RB, 1);
 
   for (int hh = 0; hh < rep; ++hh) {
     // per-head vectors: g, beta and the running decay products
@@ -585,62 +363,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       for (int u = 0; u < JPW; ++u) P1[u] = P2[u] = P3[u] = f4{0.f, 0.f, 0.f, 0.f};
       // One staged block: kKB / 4 MFMA k-steps.  The operands of k-step
       // ks + 1 are read from LDS while the MFMAs of k-step ks issue.
-      // bf16 products: the block is one k-step of 32 Dv rows
-      auto multiply_bf = [&](const Ops& op) __attribute__((always_inline)) {
-        const uint16_t* const bs = reinterpret_cast<const uint16_t*>(sm + L::BS_S);
-        const uint16_t* const bh = reinterpret_cast<const uint16_t*>(sm + L::BS_H);
-        const uint16_t* const be = reinterpret_cast<const uint16_t*>(sm + L::BS_E);
-        constexpr int SP = kKB * PC, YP = kN * L::YS;
-        // this wave's steps: dy, C, E rows tw + l % 16, Dv rows 8 (l / 16) ..
-        const uint4 fy = op.fy;
-        const uint4(&fc)[3] = op.fc;
-        const uint4(&fe)[3] = op.fe;
-#pragma unroll
-        for (int jt = 0; jt < JPW; ++jt) {
-          uint4 fs[3], fh[3];
-#pragma unroll
-          for (int p = 0; p < 3; ++p) {
-            fs[p] = tile_operand<PC>(bs + p * SP, 0, 16 * jt, lr, lq);
-            fh[p] = tile_operand<PC>(bh + p * SP, 0, 16 * jt, lr, lq);
-          }
-          // P1 = S0^T DY; P2' = S0^T C; P3' = H1^T E
-#pragma unroll
-          for (int p = 0; p < 3; ++p) P1[jt] = mfma_bf16(fs[p], fy, P1[jt]);
-          P2[jt] = mfma_bf16(fs[0], fc[0], P2[jt]);
-          P2[jt] = mfma_bf16(fs[0], fc[1], P2[jt]);
-          P2[jt] = mfma_bf16(fs[1], fc[0], P2[jt]);
-          P2[jt] = mfma_bf16(fs[0], fc[2], P2[jt]);
-          P2[jt] = mfma_bf16(fs[2], fc[0], P2[jt]);
-          P2[jt] = mfma_bf16(fs[1], fc[1], P2[jt]);
-          P3[jt] = mfma_bf16(fh[0], fe[0], P3[jt]);
-          P3[jt] = mfma_bf16(fh[0], fe[1], P3[jt]);
-          P3[jt] = mfma_bf16(fh[1], fe[0], P3[jt]);
-          P3[jt] = mfma_bf16(fh[0], fe[2], P3[jt]);
-          P3[jt] = mfma_bf16(fh[2], fe[0], P3[jt]);
-          P3[jt] = mfma_bf16(fh[1], fe[1], P3[jt]);
-        }
-        if (jp == 0) {  // Phi'[t][r] = dy_t . e_r, Psi'[t][r] = c_t . e_r
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            const int rr = (16 * tb + lr) * L::YS + 8 * lq;
-            uint4 ge[3];
-#pragma unroll
-            for (int p = 0; p < 3; ++p) ge[p] = *reinterpret_cast<const uint4*>(be + p * YP + rr);
-#pragma unroll
-            for (int p = 0; p < 3; ++p) GR[tb] = mfma_bf16(fy, ge[p], GR[tb]);
-            GR[4 + tb] = mfma_bf16(fc[0], ge[0], GR[4 + tb]);
-            GR[4 + tb] = mfma_bf16(fc[0], ge[1], GR[4 + tb]);
-            GR[4 + tb] = mfma_bf16(fc[1], ge[0], GR[4 + tb]);
-            GR[4 + tb] = mfma_bf16(fc[0], ge[2], GR[4 + tb]);
-            GR[4 + tb] = mfma_bf16(fc[2], ge[0], GR[4 + tb]);
-            GR[4 + tb] = mfma_bf16(fc[1], ge[1], GR[4 + tb]);
-          }
-        }
-      };
-      auto multiply = [&](const Ops& op) __attribute__((always_inline)) {
-        if constexpr (BFP) {
-          multiply_bf(op);
-        } else {
+      auto multiply = [&]() __attribute__((always_inline)) {
         constexpr int KS = kKB / 4;
         const bool gram = jp == 0;  // Phi', Psi' ride along in the first pass
         float by[2], bc[2], bw[2], be[2][4], as[2][JPW], ah[2][JPW];
@@ -687,7 +410,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           if (ks + 2 < KS) rd(ks + 2, 0);
           mm(1);
         }
-        }
       };
       // q, k of this lane's step for the pass's chi/psi, loaded before the
       // pass's block loads so that waiting for them never waits for those
@@ -705,32 +427,21 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       const int gbase = (hh * NJP + jp) * nbk;
       // nbk >= 2: a do-while keeps the loads in flight identical on every
       // path out of the loop (the waits for qq/kq then skip the ring's loads)
-      // With bf16 products the wave's own dy, C (and, after the first pass,
-      // E) operands are split after the barrier, next to the MFMAs.
       int blk = 0;
       do {
         const int gb = gbase + blk;
-        Ops op;
         __syncthreads();  // the stage is no longer read
-        deposit(RA, jp == 0, op);
+        deposit(RA);
         __syncthreads();
-        if constexpr (BFP) {
-          if (jp != 0) split_e(RA, op);
-          split_cy(RA, op);
-        }
         // unconditional (clamped) refills: every path has the same loads in
         // flight, so the wait before a deposit covers only that slot
         fetch(RA, min(gb + 2, nblk_all - 1));
-        multiply(op);
+        multiply();
         __syncthreads();
-        deposit(RB, jp == 0, op);
+        deposit(RB);
         __syncthreads();
-        if constexpr (BFP) {
-          if (jp != 0) split_e(RB, op);
-          split_cy(RB, op);
-        }
         fetch(RB, min(gb + 3, nblk_all - 1));
-        multiply(op);
+        multiply();
         blk += 2;
       } while (blk < nbk);
 
@@ -805,7 +516,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
         const int r = 16 * tb + lr;
         const float br = vB[r];
         const f4 phi4 = grd[tb * kThreads + tid], psi4 = grd[(4 + tb) * kThreads + tid];
-        f4 m4;  // M[t][r] of this lane's four steps t
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int t = tw + 4 * lq + v;
@@ -821,17 +531,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           if (in && t > r) pW2[o] = fmaf(-gam * (bt[v] * br), psi, w2);
           // M[t][r] = Phi[t][r] QK[t][r] - Psi[t][r] KK[t][r] (0 outside the
           // chunk: M is multiplied over all 64 rows)
-          m4[v] = in ? (br * phi) * qk - ((bt[v] * br) * psi) * kk : 0.f;
-          if constexpr (!BFP) pMZ[o] = m4[v];
-        }
-        if constexpr (BFP) {  // M^T pieces: row r, steps tw + 4 lq .. +3
-          uint2 p0, p1, p2;
-          split3_quad(m4, p0, p1, p2);
-          uint16_t* const mt = reinterpret_cast<uint16_t*>(pMZ);
-          const int om = r * L::MS + tw + 4 * lq;
-          *reinterpret_cast<uint2*>(mt + om) = p0;
-          *reinterpret_cast<uint2*>(mt + kN * L::MS + om) = p1;
-          *reinterpret_cast<uint2*>(mt + 2 * kN * L::MS + om) = p2;
+          pMZ[o] = in ? (br * phi) * qk - ((bt[v] * br) * psi) * kk : 0.f;
         }
       }
       // dbeta_t = Psi'[t][t]: tile tb = w, lanes lr = 4 lq + v
@@ -857,42 +557,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
       f4 Bt[5];
 #pragma unroll
       for (int u = 0; u < 5; ++u) Bt[u] = f4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (BFP) {
-        // bf16 MFMA, both operands as three pieces (six piece products):
-        // A = GM rows tw + l % 16, s = 32 ks + 8 (l / 16) ..; B = M^T pieces
-        // (row r = 16 tb + l % 16) and chi in column 0 of the fifth tile
-        const uint16_t* const mt = reinterpret_cast<const uint16_t*>(sm + L::MZ);
-        auto six = [](const uint4 (&x)[3], const uint4 (&y)[3], f4 acc) __attribute__((always_inline)) {
-          acc = mfma_bf16(x[0], y[0], acc);
-          acc = mfma_bf16(x[0], y[1], acc);
-          acc = mfma_bf16(x[1], y[0], acc);
-          acc = mfma_bf16(x[0], y[2], acc);
-          acc = mfma_bf16(x[2], y[0], acc);
-          acc = mfma_bf16(x[1], y[1], acc);
-          return acc;
-        };
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int s0 = 32 * ks + 8 * lq;
-          const float* const gr = sm + L::GM + (tw + lr) * kNP + s0;
-          uint4 ga[3];
-          pieces8(*reinterpret_cast<const f4*>(gr), *reinterpret_cast<const f4*>(gr + 4), ga);
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            uint4 bm[3];
-#pragma unroll
-            for (int p = 0; p < 3; ++p)
-              bm[p] = *reinterpret_cast<const uint4*>(mt + p * kN * L::MS + (16 * tb + lr) * L::MS + s0);
-            Bt[tb] = six(ga, bm, Bt[tb]);
-          }
-          const float m0 = lr == 0 ? 1.f : 0.f;
-          const f4 c0 = *reinterpret_cast<const f4*>(sm + L::V_CHI + s0) * m0;
-          const f4 c1 = *reinterpret_cast<const f4*>(sm + L::V_CHI + s0 + 4) * m0;
-          uint4 bc[3];
-          pieces8(c0, c1, bc);
-          Bt[4] = six(ga, bc, Bt[4]);
-        }
-      } else {
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         const int sk = 4 * ks + lq;
@@ -902,7 +566,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
           Bt[tb] = mfma(ga, sm[L::MZ + sk * kNP + 16 * tb + lr], Bt[tb]);
         const float cb = lr == 0 ? sm[L::V_CHI + sk] : 0.f;
         Bt[4] = mfma(ga, cb, Bt[4]);
-      }
       }
       const float phi0 = sm[L::V_SCR + 1];
 #pragma unroll
@@ -943,86 +606,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
   auto w2_at = [&](int s, int t) __attribute__((always_inline)) {
     return sm[L::W2 + (s > t ? s * kNP + t : t * kNP + s)];
   };
-  if constexpr (BFP && L::BF_FINAL) {
-    // k, q (bf16) as swizzled tiles, read as A operands (A[j][s] = k_s[j])
-    // through lds_read_tr16; each W as three bf16 pieces W^T [t][s]
-    constexpr int KFS = L::KFS, WS = L::WS;
-    constexpr int NCH = DKP / 8;
-    constexpr int NL = (kN * NCH + kThreads - 1) / kThreads;
-    uint16_t* const fk = reinterpret_cast<uint16_t*>(sm + L::BFK);
-    uint16_t* const fq = reinterpret_cast<uint16_t*>(sm + L::BFQ);
-    uint16_t* const wp = reinterpret_cast<uint16_t*>(sm + L::QK);
-    {
-      uint4 rq[NL], rk[NL];
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const int ci = tid + kThreads * u;
-        const int s = ci / NCH, j = 8 * (ci % NCH);
-        const bool ok = ci < kN * NCH && s < n && j < Dk;
-        int64_t o = ok ? qk_index(s, j) : 0;
-        asm volatile("" : "+v"(o));  // keeps the select (no branch around the loads)
-        rq[u] = *reinterpret_cast<const uint4*>(q + o);
-        rk[u] = *reinterpret_cast<const uint4*>(k + o);
-      }
-#pragma unroll
-      for (int u = 0; u < NL; ++u) {
-        const int ci = tid + kThreads * u;
-        const int s = ci / NCH, c = ci % NCH;
-        const bool ok = ci < kN * NCH && s < n && 8 * c < Dk;
-        if (ci < kN * NCH) {
-          uint4 xq = rq[u], xk = rk[u];
-          xq.x = ok ? xq.x : 0u;  // component selects (a vector select goes through memory)
-          xq.y = ok ? xq.y : 0u;
-          xq.z = ok ? xq.z : 0u;
-          xq.w = ok ? xq.w : 0u;
-          xk.x = ok ? xk.x : 0u;
-          xk.y = ok ? xk.y : 0u;
-          xk.z = ok ? xk.z : 0u;
-          xk.w = ok ? xk.w : 0u;
-          // 4-element blocks 2c, 2c + 1 stay adjacent under the swizzle
-          const int o = s * KFS + 4 * ((2 * c) ^ tile_swz(s));
-          *reinterpret_cast<uint4*>(fk + o) = xk;
-          *reinterpret_cast<uint4*>(fq + o) = xq;
-        }
-      }
-    }
-    // acc[jt] += A^T W over the chunk steps, W[s][t] = wget(s, t)
-    auto wpass = [&](auto wget, const uint16_t* at, f4(&acc)[JT]) __attribute__((always_inline)) {
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {  // W[s..s+3][t] -> pieces of row t
-        const int e = tid + kThreads * x;
-        const int t = e & 63, s = 4 * (e >> 6);
-        f4 wv;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) wv[y] = wget(s + y, t);
-        uint2 p0, p1, p2;
-        split3_quad(wv, p0, p1, p2);
-        const int o = t * WS + s;
-        *reinterpret_cast<uint2*>(wp + o) = p0;
-        *reinterpret_cast<uint2*>(wp + kN * WS + o) = p1;
-        *reinterpret_cast<uint2*>(wp + 2 * kN * WS + o) = p2;
-      }
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        uint4 bw[3];
-#pragma unroll
-        for (int pc = 0; pc < 3; ++pc)
-          bw[pc] = *reinterpret_cast<const uint4*>(wp + pc * kN * WS + (tw + lr) * WS + 32 * ks +
-                                                   8 * lq);
-#pragma unroll
-        for (int jt = 0; jt < JT; ++jt) {
-          const uint4 af = tile_operand<KFS>(at, 32 * ks, 16 * jt, lr, lq);
-#pragma unroll
-          for (int pc = 0; pc < 3; ++pc) acc[jt] = mfma_bf16(af, bw[pc], acc[jt]);
-        }
-      }
-      __syncthreads();  // the pieces are rewritten by the next pass
-    };
-    wpass(wq_at, fk, dQ);
-    wpass(w1_at, fq, dK);
-    wpass(w2_at, fk, dK);  // -W2
-  } else
   for (int s0 = 0; s0 < n; s0 += kSB) {
     if (f_role) {
       f4 rk[4], rq[4];
@@ -1094,12 +677,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_kernel(ChunkArgs a) {
 template <typename TIn, int JT, bool VEC>
 hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
   const size_t lds = sizeof(float) * CL<JT>::SIZE;
-  auto kern = chunk_kernel<TIn, JT, VEC, false>;
-  // bf16 products: dy rows in 8-element blocks, k, q rows in 8-element
-  // groups (the 16-byte loads of the q, k stages); up to Dk = 192 such shapes
-  // go to chunk_bf16_kernel
-  if constexpr (std::is_same<TIn, gdr::bf16>::value && VEC && CL<JT>::PC == 64 && JT > 12)
-    if (a.Dv % 8 == 0 && a.Dk % 8 == 0) kern = chunk_kernel<TIn, JT, VEC, true>;
+  auto kern = chunk_kernel<TIn, JT, VEC>;
   // Opt in to more than 64 KiB of dynamic LDS; a failure here surfaces as a
   // launch error below.
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

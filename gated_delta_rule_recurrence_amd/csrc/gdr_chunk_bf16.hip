@@ -62,19 +62,27 @@ struct BL {  // LDS layout, offsets in floats
   static constexpr int KFS = DKP % 128 == 0 ? DKP + 64 : DKP;
   static constexpr int BFK = 0, BFQ = kN * KFS / 2, BFINAL = kN * KFS;
   static constexpr int WS = kN + 8;
-  static constexpr int A_SZ = cmax(cmax(BSTAGE, HEAD), cmax(QKST, BFINAL));
+  // Dk above 192 (WIDE): the QK/KK stage and the final k, q tiles overlay the
+  // per-head vectors and GM too, which the first value head writes only after
+  // the stage is released and the last one reads before the final products
+  static constexpr bool WIDE = JT > 12;
+  static constexpr int A_SZ = WIDE ? cmax(BSTAGE, HEAD)
+                                   : cmax(cmax(BSTAGE, HEAD), cmax(QKST, BFINAL));
   // per-head vectors; chi, psi and the dg partials of the two column halves
   static constexpr int VEC = A_SZ;
   static constexpr int V_G = VEC, V_B = VEC + kN, V_PRE = VEC + 2 * kN,
                        V_PREX = VEC + 3 * kN, V_SUF = VEC + 4 * kN, V_CHI = VEC + 5 * kN,
                        V_PSI = VEC + 7 * kN, V_DG = VEC + 9 * kN, V_SCR = VEC + 11 * kN;
   // persistent: QK, KK, the head sums W1 (lower triangle with the diagonal;
-  // Wq = W1^T) and -W2 (strict lower triangle; W2 is symmetric), and the
-  // decay products GM of the current value head [kN][kNP]
-  static constexpr int QK = V_SCR + kThreads, KK = QK + kN * kNP, W1 = KK + kN * kNP,
-                       W2 = W1 + kN * kNP, GM = W2 + kN * kNP;
-  static constexpr int SIZE = GM + kN * kNP;
-  static_assert(JT % 4 == 0 && JT <= 12, "64-column passes, Dk <= 192");
+  // Wq = W1^T) and -W2 (strict lower triangle; W2 is symmetric); and the
+  // decay products GM of the current value head [kN][kNP] (after the
+  // vectors when WIDE, else last)
+  static constexpr int GM0 = V_SCR + kThreads;
+  static constexpr int QK = WIDE ? GM0 + kN * kNP : GM0, KK = QK + kN * kNP, W1 = KK + kN * kNP,
+                       W2 = W1 + kN * kNP, GM = WIDE ? GM0 : W2 + kN * kNP;
+  static constexpr int SIZE = (WIDE ? W2 : GM) + kN * kNP;
+  static_assert(JT % 4 == 0 && JT <= 16, "64-column passes, Dk <= 256");
+  static_assert(!WIDE || (QKST <= QK && BFINAL <= QK), "overlays end before QK");
   static_assert((2 * YS) % 32 == 16 && (2 * MS) % 32 == 16 && (2 * KGS) % 32 == 16 &&
                     (2 * WS) % 32 == 16,
                 "row strides: odd multiples of 16 bytes");
@@ -832,7 +840,7 @@ hipError_t launch_jt(const ChunkArgs& a, hipStream_t s) {
 }  // namespace
 
 bool chunk_bf16_ok(const ChunkArgs& a) {
-  return a.Dk % 8 == 0 && a.Dv % 8 == 0 && a.Dk > 48 && a.Dk <= 192 && a.L >= 1 && a.L <= kN;
+  return a.Dk % 8 == 0 && a.Dv % 8 == 0 && a.Dk > 48 && a.Dk <= 256 && a.L >= 1 && a.L <= kN;
 }
 
 // When the (chunk, kv head, batch row) grid has fewer than 256 workgroups
@@ -844,7 +852,7 @@ bool chunk_bf16_ok(const ChunkArgs& a) {
 int chunk_head_split(int64_t B, int64_t Hk, int64_t Hv, int64_t Dk, int64_t Dv, int64_t L,
                      int64_t nch, bool bf16) {
   const int64_t rep = Hv / Hk, wg = nch * Hk * B;
-  if (!(bf16 && Dk % 8 == 0 && Dv % 8 == 0 && Dk > 48 && Dk <= 192 && L >= 1 && L <= kN &&
+  if (!(bf16 && Dk % 8 == 0 && Dv % 8 == 0 && Dk > 48 && Dk <= 256 && L >= 1 && L <= kN &&
         rep >= 2 && rep <= 16 && wg < 256))
     return 0;
   int64_t ng = 2;
@@ -857,7 +865,8 @@ hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s) {
   const int jt = (a.Dk + 15) / 16;
   if (jt <= 4) return launch_jt<4>(a, s);
   if (jt <= 8) return launch_jt<8>(a, s);
-  return launch_jt<12>(a, s);
+  if (jt <= 12) return launch_jt<12>(a, s);
+  return launch_jt<16>(a, s);
 }
 
 }  // namespace gdr

@@ -129,7 +129,7 @@ hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s);
 int device_cu_count();
 hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s);
 // The eight-wave chunk kernel for bf16 inputs (gdr_chunk_bf16.hip): whether it
-// takes the shape (Dk, Dv multiples of 8, 48 < Dk <= 192), and its launch.
+// takes the shape (Dk, Dv multiples of 8, 48 < Dk <= 256), and its launch.
 bool chunk_bf16_ok(const ChunkArgs& a);
 hipError_t launch_chunk_bf16(const ChunkArgs& a, hipStream_t s);
 // How many value heads that kernel gives a workgroup when it splits a kv

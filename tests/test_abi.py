@@ -107,6 +107,8 @@ def _tile(C):
     (1, 2048, 16, 64, 256, 128, 64, 1), (2, 230, 1, 2, 200, 40, 100, 1),
     (1, 300, 2, 4, 256, 64, 128, 1), (1, 300, 2, 4, 252, 64, 64, 1),
     (1, 300, 2, 4, 256, 66, 64, 1), (1, 300, 2, 4, 256, 64, 64, 0),
+    (1, 256, 16, 64, 192, 128, 64, 1), (1, 512, 16, 64, 192, 128, 64, 1),
+    (2, 150, 2, 4, 232, 96, 48, 1), (2, 2048, 4, 8, 256, 64, 64, 1),
 ])
 def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C, bf16):
     sh = S(B, T, Hk, Hv, Dk, Dv, C, dtype=_lib.GDR_BF16 if bf16 else _lib.GDR_F32)
@@ -144,6 +146,18 @@ def test_sizes(lib, B, T, Hk, Hv, Dk, Dv, C, bf16):
         end = _round256(end) + rows
         if chunked:
             end = _round256(end) + prep
+    # bf16 inputs on the eight-wave chunk kernel (Dk, Dv multiples of 8,
+    # 48 < Dk <= 256) with a (tile, kv head, batch row) grid under 256 and 2
+    # to 16 value heads per kv head: the value heads go to ng groups (the
+    # smallest divisor of their count that brings the grid to 256, else one
+    # head each), whose fp32 dq, dk terms [2][ng][B][T][Hk][Dk] follow
+    rep, wg = Hv // Hk, ntiles * Hk * B
+    if (bf16 and Dk % 8 == 0 and Dv % 8 == 0 and 48 < Dk <= 256 and L <= 64
+            and 2 <= rep <= 16 and wg < 256):
+        ng = 2
+        while ng < rep and (rep % ng or wg * ng < 256):
+            ng += 1
+        end = _round256(end) + B * T * Hk * Dk * 4 * 2 * ng
     assert _lib.backward_workspace_bytes(sh) == end
 
 

@@ -417,6 +417,22 @@ def test_bf16_wide_keys_chunked(cuda, Dk, chunk):
         assert errs[name] <= TOL["f32"], f"bf16 Dk={Dk}: {name} rel L2 {errs[name]:.2e}"
 
 
+def test_bf16_wide_keys_full_grid(cuda):
+    """Dk = 256 on a grid of 256 (tile, kv head, batch row) workgroups, so
+    the chunk kernel runs one workgroup per kv head without head groups
+    (T = 2048, 32 tiles); units of both batch rows against the oracle, the
+    fp32 outputs at the fp32 bar."""
+    from gated_delta_rule_recurrence_amd import _lib
+    p = inputs.draw(2, 2048, 4, 8, 256, 64, seed=89, normalised=True, decay="mix",
+                    S0_std=0.05, dST_std=1.0, dtype="bf16")
+    sh = _lib.make_shape(2, 2048, 4, 8, 256, 64, 64, _lib.GDR_BF16, 0)
+    assert _lib.forward_workspace_bytes(sh) > 0, "not the chunked sweeps"
+    log("bf16 Dk=256 T=2048, 256 chunk workgroups")
+    gpu = run_gpu(p, cuda, 64)
+    compare_groups(gpu, p, TOL["bf16"], "Dk=256 T=2048", units=[(0, 0), (1, 3)],
+                   state_tol=TOL["f32"])
+
+
 def test_bf16_wide_keys_replay(cuda):
     """C = 128 at Dk = 256: the backward's replay (the prep forming both
     record sets in one launch, the forward sweep in its general form) gives
@@ -442,8 +458,8 @@ def test_bf16_dims(cuda, dims, chunk):
     a short last 32-row block, Dv=36 and Dv=20 pair the bf16-product sweeps
     with the fp32-operand chunk kernel; Dk=104 and 128 (128-column tiles) and
     56 (a 64-column tile) cover the other widths of the eight-wave chunk
-    kernel, Dk=200 and 256 (chunked sweeps with 256-column tiles) the
-    four-wave chunk kernel's bf16 products; T=70 leaves a short last chunk."""
+    kernel, Dk=200 and 256 the 256-column tiles of the chunked sweeps and
+    of the eight-wave chunk kernel; T=70 leaves a short last chunk."""
     Dk, Dv = dims
     p = inputs.draw(1, 70, 2, 4, Dk, Dv, seed=23, normalised=True, S0_std=0.2,
                     dST_std=1.0, dtype="bf16")
