@@ -448,7 +448,7 @@ def test_bf16_wide_keys_replay(cuda):
 
 @pytest.mark.parametrize("dims", [(72, 30), (68, 40), (136, 24), (192, 40), (64, 36),
                                   (192, 20), (104, 48), (128, 64), (56, 16), (200, 40),
-                                  (256, 64)])
+                                  (256, 64), (252, 40), (250, 24)])
 @pytest.mark.parametrize("chunk", [32, 64])
 def test_bf16_dims(cuda, dims, chunk):
     """bf16 inputs at the edges of the bf16-product kernels' shape conditions
@@ -459,7 +459,9 @@ def test_bf16_dims(cuda, dims, chunk):
     with the fp32-operand chunk kernel; Dk=104 and 128 (128-column tiles) and
     56 (a 64-column tile) cover the other widths of the eight-wave chunk
     kernel, Dk=200 and 256 the 256-column tiles of the chunked sweeps and
-    of the eight-wave chunk kernel; T=70 leaves a short last chunk."""
+    of the eight-wave chunk kernel; Dk=252 (4-element groups) and 250 take
+    the per-step sweeps and the four-wave chunk kernel with bf16 inputs;
+    T=70 leaves a short last chunk."""
     Dk, Dv = dims
     p = inputs.draw(1, 70, 2, 4, Dk, Dv, seed=23, normalised=True, S0_std=0.2,
                     dST_std=1.0, dtype="bf16")
