@@ -59,3 +59,18 @@ def test_noalloc_matches_forward_twice(cuda):
                               mask=small.mask)
     assert O.rel_l2(a["y"], y_ref) <= TOL["f32"]
     assert O.rel_l2(a["S_T"], ST_ref) <= TOL["f32"]
+
+
+def test_noalloc_wide_keys(cuda):
+    """Dk = 256 with bf16 inputs takes the chunked forward with 256-column
+    tiles, whose records also go to the scratch array: bitwise gdr_forward's
+    y, S_T and save buffer (a ragged last tile, S0 given)."""
+    p = inputs.draw(1, 300, 4, 16, 256, 128, seed=91, normalised=True, S0_std=0.1,
+                    decay="mix", dtype="bf16")
+    shape = _lib.make_shape(1, 300, 4, 16, 256, 128, 64, _lib.GDR_BF16, 0)
+    assert 0 < _lib.forward_workspace_bytes(shape) <= _lib.NOALLOC_SCRATCH_BYTES
+    log("noalloc vs gdr_forward: Dk=256 bf16")
+    a = _run(p, cuda, 64, noalloc=True)
+    b = _run(p, cuda, 64, noalloc=False)
+    for n in a:
+        np.testing.assert_array_equal(a[n], b[n], err_msg=f"Dk=256: {n}")
