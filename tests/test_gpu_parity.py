@@ -433,6 +433,17 @@ def test_bf16_wide_keys_full_grid(cuda):
                    state_tol=TOL["f32"])
 
 
+def test_bf16_wide_keys_long(cuda):
+    """Dk = 256 over 64 tiles (T = 4096, S0 and dS_T given, mixed decay):
+    one unit against the oracle, the fp32 outputs at the fp32 bar."""
+    p = inputs.draw(1, 4096, 2, 8, 256, 128, seed=97, normalised=True, decay="mix",
+                    S0_std=0.05, dST_std=1.0, dtype="bf16")
+    log("bf16 Dk=256 T=4096")
+    gpu = run_gpu(p, cuda, 64)
+    compare_groups(gpu, p, TOL["bf16"], "Dk=256 T=4096", units=[(0, 1)],
+                   state_tol=TOL["f32"])
+
+
 def test_bf16_wide_keys_replay(cuda):
     """C = 128 at Dk = 256: the backward's replay (the prep forming both
     record sets in one launch, the forward sweep in its general form) gives
