@@ -109,6 +109,11 @@ def parse():
     ap.add_argument("--vjp-batch", action="store_true",
                     help="time the backward alone (and fwd+bwd) at B = 1, 2, 4, 8, T=64, "
                          "Hk=Hv=2, Dk=Dv=64, fp32, one JSON line each, and exit")
+    ap.add_argument("--dk-sweep", action="store_true",
+                    help="time fwd+bwd at B=1, T=2048, Hk=16, Hv=64, Dv=128 for each key "
+                         "width of --dks, one JSON line each, and exit")
+    ap.add_argument("--dks", default="128,192,200,256,252",
+                    help="key widths of --dk-sweep")
     ap.add_argument("--decode", type=int, default=0, metavar="B",
                     help="time single-step inference (T=1, state updated in place, no "
                          "save buffer) at batch B with the same heads, and exit")
@@ -422,6 +427,29 @@ def vjp_batch(args):
         del st, d
 
 
+def dk_sweep(args):
+    """Key widths at the headline's other dims (B=1, T=2048, Hk=16, Hv=64,
+    Dv=128, chunk 64): median fwd, bwd and step ms by HIP events over 50
+    steps, and which forward path the shape takes (the chunked sweeps, or
+    the per-step sweeps when the forward needs no workspace)."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib
+    dev = torch.device("cuda:0")
+    _lib.load()
+    for Dk in (int(x) for x in args.dks.split(",")):
+        d = device_problem(1, 2048, 16, 64, Dk, 128, dev, args.seed, args.dtype)
+        st = Step(d, 64)
+        f, b = st.time(50, warmup=10)
+        sm = float(np.median(f + b))
+        print(json.dumps({"dk_sweep": {
+            "Dk": Dk, "B": 1, "T": 2048, "Hk": 16, "Hv": 64, "Dv": 128, "dtype": args.dtype,
+            "path": "chunked" if st.chunked else "per-step sweeps",
+            "fwd_ms_median": float(np.median(f)), "bwd_ms_median": float(np.median(b)),
+            "step_ms_median": sm, "tokens_per_s": 2048 / (sm * 1e-3)}}), flush=True)
+        del st, d
+        torch.cuda.empty_cache()
+
+
 def copy_calibration(mib):
     """One warm-up and one measured dispatch of a plain contiguous fp32 copy
     (mib MiB read, mib MiB written): the HBM byte counters of the second
@@ -481,6 +509,9 @@ def main():
         return
     if args.vjp_batch:
         vjp_batch(args)
+        return
+    if args.dk_sweep:
+        dk_sweep(args)
         return
 
     # the CPU baseline first: its worker processes start before this process
