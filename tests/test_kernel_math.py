@@ -287,7 +287,7 @@ def _half_wave_banks(addr_bf16):
     return out
 
 
-@pytest.mark.parametrize("dkp", [64, 128, 192])
+@pytest.mark.parametrize("dkp", [64, 128, 192, 256])
 def test_swizzled_tile_reads_conflict_free(dkp):
     """tile_operand: lane l reads the 8-byte block of row k0 + 8 (l / 16) +
     (l % 16) / 4 (+ 4 for the second read), block (n0 / 4 + l % 4) ^
@@ -307,7 +307,7 @@ def test_swizzled_tile_reads_conflict_free(dkp):
                     assert len(set(banks)) == 64, (dkp, k0, n0, second)
 
 
-@pytest.mark.parametrize("dkp", [64, 128, 192])
+@pytest.mark.parametrize("dkp", [64, 128, 192, 256])
 def test_swizzled_tile_row_writes_conflict_free(dkp):
     """deposit_rows: 16-byte groups (blocks 2c, 2c+1, adjacent under the
     swizzle) of the rows of a chunk; the lanes of a half-wave write
