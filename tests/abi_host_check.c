@@ -50,7 +50,14 @@ int main(void) {
         EXPECT(gdr_num_chunks(&s, &nc) == GDR_OK);
         EXPECT(nc == (Ts[j] + Cs[i] - 1) / Cs[i]);
         s.Dk = 256;
+        EXPECT(gdr_checkpoint_bytes(&s, &n) == GDR_OK);
+        EXPECT(gdr_forward_workspace_bytes(&s, &n) == GDR_OK);
         EXPECT(gdr_backward_workspace_bytes(&s, &n) == GDR_OK);
+        /* a small grid: the chunk kernel's head groups at Dk = 256 (bf16) */
+        gdr_shape w = shape(1, Ts[j], 2, 4, 256, 128, Cs[i], dt);
+        EXPECT(gdr_checkpoint_bytes(&w, &n) == GDR_OK);
+        EXPECT(gdr_forward_workspace_bytes(&w, &n) == GDR_OK);
+        EXPECT(gdr_backward_workspace_bytes(&w, &n) == GDR_OK);
       }
 
   /* shape errors */
