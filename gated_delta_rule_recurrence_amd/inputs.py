@@ -130,7 +130,7 @@ def draw(B, T, Hk, Hv, Dk, Dv, *, seed=0, normalised=False, decay="weak",
     p = Problem(B, T, Hk, Hv, Dk, Dv, q, k, v, log_g if log_decay else g, beta, dy,
                 S0, dST, dtype,
                 meta=dict(seed=seed, normalised=normalised, decay=decay,
-                          mean_log_g=float(log_g.mean())),
+                          mean_log_g=float(log_g.mean()) if log_g.size else float("nan")),
                 log_decay=log_decay)
     if dtype == "bf16":
         for name in ("q", "k", "v", "g", "beta", "dy"):
