@@ -53,3 +53,40 @@ def test_random_shape(cuda, i):
         p.mask = (rng.random((c["B"], c["T"])) >= 0.25).astype(np.uint8)
     log(f"random case {i}: {c}")
     compare(run_gpu(p, cuda, c["chunk"]), run_oracle(p), TOL[c["dtype"]], f"case {i}")
+
+
+def _medium_cases(n=8, seed=2027):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        Hk = int(rng.choice([2, 4, 8, 16]))
+        out.append(dict(B=int(rng.integers(1, 3)), T=int(rng.choice([256, 512, 1000, 1500])),
+                        Hk=Hk, Hv=Hk * int(rng.choice([1, 2, 4, 8])),
+                        Dk=int(rng.choice([64, 128, 192, 200, 256])),
+                        Dv=int(rng.choice([64, 96, 128])),
+                        dtype=str(rng.choice(["bf16", "bf16", "f32"])),
+                        chunk=int(rng.choice([32, 64, 128])),
+                        decay=str(rng.choice(["weak", "strong", "mix"])),
+                        seed=int(rng.integers(1 << 30))))
+    return out
+
+
+MEDIUM = _medium_cases()
+
+
+@pytest.mark.parametrize("i", range(len(MEDIUM)))
+def test_random_medium_shape(cuda, i):
+    """Medium shapes (T up to 1500, up to 8 value heads per kv head): the
+    prep's pair grid and the chunk kernel's head groups at realistic sizes;
+    one (batch row, kv group) unit, drawn from the case's seed, against the
+    oracle, the fp32 outputs S_T and dS0 at the fp32 bar."""
+    from parity import compare_groups
+    c = MEDIUM[i]
+    p = inputs.draw(c["B"], c["T"], c["Hk"], c["Hv"], c["Dk"], c["Dv"], seed=c["seed"],
+                    normalised=True, decay=c["decay"], S0_std=0.05, dST_std=1.0,
+                    dtype=c["dtype"])
+    rng = np.random.default_rng(c["seed"] + 2)
+    unit = (int(rng.integers(c["B"])), int(rng.integers(c["Hk"])))
+    log(f"medium case {i}: {c}, unit {unit}")
+    compare_groups(run_gpu(p, cuda, c["chunk"]), p, TOL[c["dtype"]], f"medium {i}",
+                   units=[unit], state_tol=TOL["f32"])
