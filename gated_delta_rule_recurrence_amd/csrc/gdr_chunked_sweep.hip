@@ -1,5 +1,5 @@
-// Chunked sweeps of the gated delta rule on gfx950 (fp32 MFMA): the forward
-// state recurrence and the reverse recurrence of its state gradient.
+// Chunked sweeps of the gated delta rule on gfx950 (matrix cores): the
+// forward state recurrence and the reverse recurrence of its state gradient.
 //
 // Notation: a chunk has n <= 64 steps, local t = 0..n-1, and Gam(a,b] is the
 // product of g over the steps a+1..b.  It is always formed as a running
