@@ -214,6 +214,42 @@ class Step:
         return f, b
 
 
+def live_kernel_ms(st, names_f, names_b, n=20):
+    """Per-kernel durations of the two calls, by HIP events that the library
+    records right after each of its kernel launches (gdr_set_launch_events:
+    one event per kernel named plus one more, those past a call's last
+    launch recorded at its end), over n steps run after the timed region:
+    the median ms of each kernel, in launch order, for each call.  The extra
+    event closes an interval with no kernel in it, whose median is the cost
+    of the event records themselves (each kernel's figure includes it)."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib
+    nf, nb = len(names_f) + 1, len(names_b) + 1
+    rows = [[torch.cuda.Event(enable_timing=True) for _ in range(2 + nf + nb)]
+            for _ in range(n)]
+    for row in rows:
+        for e in row:
+            e.record(st.stream)  # creates the underlying events
+    torch.cuda.synchronize()
+    try:
+        for row in rows:
+            _lib.check(_lib.set_launch_events([e.cuda_event for e in row[1:1 + nf]]),
+                       "gdr_set_launch_events")
+            row[0].record(st.stream)
+            st.fwd()
+            _lib.check(_lib.set_launch_events([e.cuda_event for e in row[2 + nf:]]),
+                       "gdr_set_launch_events")
+            row[1 + nf].record(st.stream)
+            st.bwd()
+    finally:
+        _lib.set_launch_events([])
+    torch.cuda.synchronize()
+    med = lambda i: float(np.median([r[i].elapsed_time(r[i + 1]) for r in rows]))
+    return {"gdr_forward": {names_f[i]: med(i) for i in range(nf - 1)},
+            "gdr_backward": {names_b[i]: med(1 + nf + i) for i in range(nb - 1)},
+            "event_gap_ms": med(nf - 1), "steps": n}
+
+
 def device_problem(B, T, Hk, Hv, Dk, Dv, dev, seed, dtype, decay="weak", S0_std=None):
     from gated_delta_rule_recurrence_amd import inputs
     return inputs.draw_device(B, T, Hk, Hv, Dk, Dv, device=dev, seed=seed, normalised=True,
@@ -587,13 +623,21 @@ def main():
     # the bf16-product sweep kernels take bf16 inputs with Dk % 8 == 0 and Dv % 4 == 0
     sfx = "_bf16" if (args.dtype == "bf16" and Dk % 8 == 0 and Dv % 4 == 0) else ""
     chunk_name = ("chunk_bf16_kernel" if (args.dtype == "bf16" and Dk % 8 == 0 and Dv % 8 == 0
-                                          and 48 < Dk <= 192) else "chunk_kernel")
+                                          and 48 < Dk <= 256) else "chunk_kernel")
     all_tf = (FLOPS_FWD + FLOPS_BWD) * elems / (ms * 1e-3) / 1e12
     esz = 2 if args.dtype == "bf16" else 4
     fwd_bytes, bwd_bytes = algorithmic_bytes(B, T, Hk, Hv, Dk, Dv, esz, st.nch)
     fwd_mid, bwd_mid = intermediate_bytes(B, T, Hv, Dv, Dk, st.nch, st.chunked)
 
     default_workload = (args.T, args.B, args.chunk, args.dtype) == (2048, 1, 64, "bf16")
+    # the kernels of each call one by one (the chunked path at chunk <= 64;
+    # a fourth backward interval is the head-group sum when the chunk kernel
+    # splits the value heads, else empty)
+    live = None
+    if st.chunked and args.chunk <= 64:
+        live = live_kernel_ms(st, ["prep_kernel<fwd>", f"fwd_chunked{sfx}_kernel"],
+                              ["prep_kernel<bwd>", f"bwd_chunked{sfx}_kernel", chunk_name,
+                               "head_sum_kernel"])
     prof_ok = (default_workload and PROFILE["sources_sha256_16"] is not None
                and sources_digest() == PROFILE["sources_sha256_16"])
     traffic = fwd_traffic = None
@@ -652,6 +696,7 @@ def main():
                     "hbm_frac_algorithmic": fwd_bytes / (fwd_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "avg_launch_ms": fwd_ms},
         "counters": counters,
+        "kernels_live_ms": live,
         "achievable_hbm_GBps": copy_gbs,
         "achievable_compute": peaks,
         "timing": {"wall_ms_per_step": ms, "step_ms_median": float(np.median(step_ms)),

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "gdr_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 11),
     "gdr_backward": (ctypes.c_int, [ctypes.POINTER(GdrShape)] + [_vp] * 16
                      + [ctypes.c_size_t, _vp]),
+    "gdr_set_launch_events": (ctypes.c_int, [ctypes.POINTER(_vp), ctypes.c_int]),
     "gdr_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gdr_version": (ctypes.c_char_p, []),
 }
@@ -138,6 +139,17 @@ def forward_noalloc_raw(shape, q, k, v, g, beta, S0, y, S_T, ckpt, stream, mask=
 
 NOALLOC_SCRATCH_BYTES = 128 << 20  # GDR_NOALLOC_SCRATCH_BYTES
 GDR_ERR_SCRATCH_LIMIT = -12
+GDR_ERR_BAD_COUNT = -13
+MAX_LAUNCH_EVENTS = 8  # GDR_MAX_LAUNCH_EVENTS
+
+
+def set_launch_events(handles) -> int:
+    """gdr_set_launch_events: the raw hipEvent_t handles (ints) that the
+    following calls record after their kernel launches, in order; an empty
+    sequence clears the hook.  Returns the status."""
+    handles = list(handles)
+    arr = (_vp * max(len(handles), 1))(*[_vp(h) for h in handles])
+    return load().gdr_set_launch_events(arr, len(handles))
 
 
 def backward_raw(shape, q, k, g, beta, ckpt, dy, dS_T, dq, dk, dv, dg, dbeta,

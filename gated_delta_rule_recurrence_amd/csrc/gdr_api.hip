@@ -180,6 +180,22 @@ void* scratch_address() {
   return scratch_ptr[dev];
 }
 
+// ---- gdr_set_launch_events -------------------------------------------------
+// The caller's events and how many kernels the current call has launched
+// (process-wide: the hook is for single-threaded measurement).
+hipEvent_t launch_events[GDR_MAX_LAUNCH_EVENTS];
+int n_launch_events = 0;
+int launch_count = 0;
+
+// A call's end (on success): the events past its last launch, so that every
+// set event is recorded once per call.
+int end_call(int status, void* stream) {
+  if (status == GDR_OK)
+    for (int i = launch_count; i < n_launch_events; ++i)
+      (void)hipEventRecord(launch_events[i], static_cast<hipStream_t>(stream));
+  return status;
+}
+
 // gdr_forward's pointer checks (required pointers, alignment)
 int forward_pointers_ok(const gdr_shape* shape, const void* q, const void* k, const void* v,
                         const void* g, const void* beta, const float* S0, const void* y,
@@ -308,17 +324,20 @@ int gdr_forward(const gdr_shape* shape, const void* q, const void* k,
                 const float* S0, const uint8_t* mask, void* y, float* S_T,
                 void* ckpt, void* workspace, size_t workspace_bytes,
                 void* stream) {
+  launch_count = 0;
   Sizes z;
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
-  return forward_checked(shape, z, q, k, v, g, beta, S0, mask, y, S_T, ckpt, workspace,
-                         workspace_bytes, stream);
+  return end_call(forward_checked(shape, z, q, k, v, g, beta, S0, mask, y, S_T, ckpt,
+                                  workspace, workspace_bytes, stream),
+                  stream);
 }
 
 int gdr_forward_noalloc(const gdr_shape* shape, const void* q, const void* k,
                         const void* v, const void* g, const void* beta,
                         const float* S0, const uint8_t* mask, void* y, float* S_T,
                         void* ckpt, void* stream) {
+  launch_count = 0;
   Sizes z;
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
@@ -330,16 +349,18 @@ int gdr_forward_noalloc(const gdr_shape* shape, const void* q, const void* k,
     ws = scratch_address();
     if (ws == nullptr) return GDR_ERR_HIP;
   }
-  return forward_checked(shape, z, q, k, v, g, beta, S0, mask, y, S_T, ckpt, ws,
-                         ws != nullptr ? GDR_NOALLOC_SCRATCH_BYTES : 0, stream);
+  return end_call(forward_checked(shape, z, q, k, v, g, beta, S0, mask, y, S_T, ckpt, ws,
+                                  ws != nullptr ? GDR_NOALLOC_SCRATCH_BYTES : 0, stream),
+                  stream);
 }
 
-int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
-                 const void* v, const void* g, const void* beta, const uint8_t* mask,
-                 const void* ckpt,
-                 const void* dy, const float* dS_T, void* dq, void* dk,
-                 void* dv, void* dg, void* dbeta, float* dS0,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+// gdr_backward's work (the entry point below adds the launch-event hook's
+// bookkeeping)
+static int backward_call(const gdr_shape* shape, const void* q, const void* k,
+                         const void* v, const void* g, const void* beta, const uint8_t* mask,
+                         const void* ckpt, const void* dy, const float* dS_T, void* dq,
+                         void* dk, void* dv, void* dg, void* dbeta, float* dS0,
+                         void* workspace, size_t workspace_bytes, void* stream) {
   Sizes z;
   const int st = check_shape(shape, &z);
   if (st != GDR_OK) return st;
@@ -476,6 +497,28 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
   return err == hipSuccess ? GDR_OK : GDR_ERR_HIP;
 }
 
+int gdr_set_launch_events(void* const* events, int n) {
+  if (n < 0 || n > GDR_MAX_LAUNCH_EVENTS) return GDR_ERR_BAD_COUNT;
+  if (n > 0 && events == nullptr) return GDR_ERR_NULL_ARG;
+  for (int i = 0; i < n; ++i)
+    if (events[i] == nullptr) return GDR_ERR_NULL_ARG;
+  for (int i = 0; i < n; ++i) launch_events[i] = static_cast<hipEvent_t>(events[i]);
+  n_launch_events = n;
+  return GDR_OK;
+}
+
+int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
+                 const void* v, const void* g, const void* beta, const uint8_t* mask,
+                 const void* ckpt,
+                 const void* dy, const float* dS_T, void* dq, void* dk,
+                 void* dv, void* dg, void* dbeta, float* dS0,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  launch_count = 0;
+  return end_call(backward_call(shape, q, k, v, g, beta, mask, ckpt, dy, dS_T, dq, dk, dv,
+                                dg, dbeta, dS0, workspace, workspace_bytes, stream),
+                  stream);
+}
+
 const char* gdr_strerror(int status) {
   switch (status) {
     case GDR_OK: return "ok";
@@ -492,15 +535,22 @@ const char* gdr_strerror(int status) {
     case GDR_ERR_BAD_DECAY: return "decay must be GDR_DECAY_G or GDR_DECAY_LOG";
     case GDR_ERR_SCRATCH_LIMIT:
       return "the forward workspace this shape needs exceeds the no-allocation scratch";
+    case GDR_ERR_BAD_COUNT:
+      return "the launch-event count must be in [0, GDR_MAX_LAUNCH_EVENTS]";
   }
   return "unknown gdr status";
 }
 
-const char* gdr_version(void) { return "0.6.0"; }
+const char* gdr_version(void) { return "0.7.0"; }
 
 }  // extern "C"
 
 namespace gdr {
+
+void note_launch(hipStream_t s) {
+  const int i = launch_count++;
+  if (i < n_launch_events) (void)hipEventRecord(launch_events[i], s);
+}
 
 int device_cu_count() {
   static std::atomic<int> cache[64];

@@ -685,7 +685,9 @@ hipError_t chunk_launch(const ChunkArgs& a, hipStream_t s) {
                             static_cast<int>(lds));
   dim3 grid(a.nch, a.Hk, a.B);
   hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  note_launch(s);
+  return e;
 }
 
 template <typename TIn, bool VEC>

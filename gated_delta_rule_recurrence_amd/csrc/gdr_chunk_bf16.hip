@@ -829,12 +829,15 @@ hipError_t launch_jt(const ChunkArgs& a, hipStream_t s) {
   const int ng = a.part != nullptr ? a.Hv / a.Hk / a.hpw : 1;  // head groups per kv head
   hipLaunchKernelGGL(kern, dim3(a.nch, a.Hk * ng, a.B), dim3(kThreads), lds, s, a);
   hipError_t e = hipGetLastError();
+  note_launch(s);
   if (e != hipSuccess || a.part == nullptr) return e;
   const int64_t n4 = (int64_t)a.B * a.T * a.Hk * a.Dk / 4;  // Dk is a multiple of 8
   const int64_t blocks = (2 * n4 + 255) / 256;
   hipLaunchKernelGGL(head_sum_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a.part, ng, n4,
                      static_cast<bf16*>(a.dq), static_cast<bf16*>(a.dk));
-  return hipGetLastError();
+  e = hipGetLastError();
+  note_launch(s);
+  return e;
 }
 
 }  // namespace

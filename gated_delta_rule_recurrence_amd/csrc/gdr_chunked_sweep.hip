@@ -1986,7 +1986,9 @@ hipError_t launch(Kern kern, dim3 grid, int threads, size_t lds, hipStream_t s,
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
   hipLaunchKernelGGL(kern, grid, dim3(threads), lds, s, args...);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  note_launch(s);
+  return e;
 }
 
 // The records of MODE (forward records to prep_f, reverse to prep_b).

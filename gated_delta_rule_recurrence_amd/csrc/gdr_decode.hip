@@ -140,7 +140,9 @@ hipError_t launch_nc(const FwdSweepArgs& a, hipStream_t s) {
     case 16: hipLaunchKernelGGL((decode_kernel<TIn, 16, VEC>), grid, dim3(kThreads), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  note_launch(s);
+  return e;
 }
 
 template <typename TIn>

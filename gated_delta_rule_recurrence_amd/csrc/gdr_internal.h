@@ -127,6 +127,9 @@ hipError_t launch_bwd_sweep(const BwdSweepArgs& a, bool bf16, hipStream_t s);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
+// After each kernel launch: records the caller's next measurement event on s,
+// if gdr_set_launch_events has set one for this launch (include/gdr.h).
+void note_launch(hipStream_t s);
 hipError_t launch_bwd_chunk(const ChunkArgs& a, bool bf16, hipStream_t s);
 // The eight-wave chunk kernel for bf16 inputs (gdr_chunk_bf16.hip): whether it
 // takes the shape (Dk, Dv multiples of 8, 48 < Dk <= 256), and its launch.

@@ -729,7 +729,9 @@ hipError_t fwd_launch(const FwdSweepArgs& a, hipStream_t s) {
   dim3 grid((a.Dv + Lo::RW - 1) / Lo::RW, a.Hv, a.B);
   hipLaunchKernelGGL((fwd_sweep_kernel<TIn, NC, R, FAST>), grid,
                      dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  note_launch(s);
+  return e;
 }
 
 template <typename TIn, int NC, int R, bool FAST>
@@ -738,7 +740,9 @@ hipError_t bwd_launch(const BwdSweepArgs& a, hipStream_t s) {
   dim3 grid((a.Dv + Lo::RW - 1) / Lo::RW, a.Hv, a.B);
   hipLaunchKernelGGL((bwd_sweep_kernel<TIn, NC, R, FAST>), grid,
                      dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  note_launch(s);
+  return e;
 }
 
 // Columns per lane: the smallest multiple of 4 with 16 * NC >= Dk.

@@ -56,8 +56,10 @@ typedef enum {
   GDR_ERR_ALIGNMENT = -9,       /* a pointer is not 16-byte aligned             */
   GDR_ERR_HIP = -10,            /* the HIP runtime rejected a launch            */
   GDR_ERR_BAD_DECAY = -11,      /* decay is not GDR_DECAY_G or GDR_DECAY_LOG    */
-  GDR_ERR_SCRATCH_LIMIT = -12   /* gdr_forward_noalloc: the shape's forward
+  GDR_ERR_SCRATCH_LIMIT = -12,  /* gdr_forward_noalloc: the shape's forward
                                    workspace exceeds GDR_NOALLOC_SCRATCH_BYTES */
+  GDR_ERR_BAD_COUNT = -13       /* gdr_set_launch_events: n outside
+                                   0 .. GDR_MAX_LAUNCH_EVENTS               */
 } gdr_status;
 
 /* Size of the device-side scratch array behind gdr_forward_noalloc (128 MiB;
@@ -193,6 +195,26 @@ int gdr_backward(const gdr_shape* shape, const void* q, const void* k,
                  const void* dy, const float* dS_T, void* dq, void* dk,
                  void* dv, void* dg, void* dbeta, float* dS0,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement hook, for callers that time the library's kernels one by one
+ * (a profiler-free per-kernel breakdown; not needed to compute anything).
+ * While n > 0, every gdr_forward, gdr_forward_noalloc and gdr_backward call
+ * records events[i] on its stream right after launching its i-th kernel
+ * (counted from 0 in each call; launches past the n-th record nothing) and,
+ * when it succeeds, the events past its last launch at its end, so that each
+ * event is recorded once per call.  The time between two consecutive events,
+ * or between an event the caller records before the call and events[0], is
+ * then one kernel's (zero past the call's last kernel).  events holds n
+ * hipEvent_t handles that the caller created and owns (with timing for
+ * elapsed times); n = 0 clears the hook.  The setting is process-wide: set
+ * it only while no other host thread calls into the library.  A chunked call
+ * launches, in order: forward - the prep, the sweep; backward (chunk <= 64) -
+ * the prep, the reverse sweep, the chunk kernel and, when it splits the
+ * value heads (see gdr_backward_workspace_bytes), the sum of their dq, dk
+ * terms.  Errors: GDR_ERR_BAD_COUNT (n outside 0 .. GDR_MAX_LAUNCH_EVENTS),
+ * GDR_ERR_NULL_ARG (events, or one of its first n entries, is NULL, n > 0). */
+#define GDR_MAX_LAUNCH_EVENTS 8
+int gdr_set_launch_events(void* const* events, int n);
 
 /* Static, human-readable text for a gdr_status value. */
 const char* gdr_strerror(int status);

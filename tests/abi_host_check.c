@@ -114,7 +114,19 @@ int main(void) {
                       NULL, NULL, NULL, NULL, 0, NULL) == GDR_OK);
 
   /* every status has a message */
-  for (int st = 0; st >= -12; --st) EXPECT(strstr(gdr_strerror(st), "unknown") == NULL);
+  for (int st = 0; st >= -13; --st) EXPECT(strstr(gdr_strerror(st), "unknown") == NULL);
+  /* the launch-event hook: argument checks (set, then cleared before any launch) */
+  {
+    void* evs[GDR_MAX_LAUNCH_EVENTS + 1];
+    for (int i = 0; i <= GDR_MAX_LAUNCH_EVENTS; ++i) evs[i] = F;
+    EXPECT(gdr_set_launch_events(evs, GDR_MAX_LAUNCH_EVENTS + 1) == GDR_ERR_BAD_COUNT);
+    EXPECT(gdr_set_launch_events(evs, -1) == GDR_ERR_BAD_COUNT);
+    EXPECT(gdr_set_launch_events(NULL, 2) == GDR_ERR_NULL_ARG);
+    evs[1] = NULL;
+    EXPECT(gdr_set_launch_events(evs, 2) == GDR_ERR_NULL_ARG);
+    EXPECT(gdr_set_launch_events(evs, 1) == GDR_OK);
+    EXPECT(gdr_set_launch_events(NULL, 0) == GDR_OK);
+  }
   EXPECT(strstr(gdr_strerror(-99), "unknown") != NULL);
   EXPECT(strlen(gdr_version()) >= 5);
 

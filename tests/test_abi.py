@@ -54,7 +54,7 @@ def test_binding_covers_header():
 
 def test_version_and_strerror(lib):
     assert re.fullmatch(r"\d+\.\d+\.\d+", lib.gdr_version().decode())
-    for code in range(0, -13, -1):
+    for code in range(0, -14, -1):
         assert "unknown" not in _lib.strerror(code)
     assert "unknown" in _lib.strerror(-999)
 
@@ -268,3 +268,17 @@ def test_noalloc_pointer_errors(lib):
 def test_noalloc_empty_is_a_no_op(lib):
     assert _lib.forward_noalloc_raw(S(B=0), *([0] * 9), 0) == 0
     assert _lib.forward_noalloc_raw(S(T=0), *([0] * 9), 0) == 0
+
+
+# ---- gdr_set_launch_events: argument checks (no GPU: nothing is recorded
+# until a call launches a kernel, and the hook is cleared again)
+def test_launch_events_arguments(lib):
+    FAKE_EVENT = 0x1000  # never recorded: no launch happens while it is set
+    assert _lib.set_launch_events([FAKE_EVENT] * 9) == _lib.GDR_ERR_BAD_COUNT
+    assert lib.gdr_set_launch_events(None, -1) == _lib.GDR_ERR_BAD_COUNT
+    assert lib.gdr_set_launch_events(None, 1) == -1  # GDR_ERR_NULL_ARG
+    assert _lib.set_launch_events([FAKE_EVENT, 0]) == -1
+    assert _lib.set_launch_events([FAKE_EVENT] * _lib.MAX_LAUNCH_EVENTS) == 0
+    assert _lib.set_launch_events([]) == 0
+    assert lib.gdr_set_launch_events(None, 0) == 0
+    assert "launch-event" in _lib.strerror(_lib.GDR_ERR_BAD_COUNT)

@@ -244,6 +244,52 @@ def test_deterministic(cuda):
         np.testing.assert_array_equal(a[n], b[n], err_msg=n)
 
 
+def test_launch_events(cuda):
+    """gdr_set_launch_events: a call records the caller's events right after
+    its kernel launches, in order (forward: prep, sweep; backward on a grid
+    small enough for head groups: prep, reverse sweep, chunk kernel, the sum
+    of the groups' dq, dk terms); an event past a call's last launch is
+    recorded at its end.  Every kernel's interval is positive, the extra one
+    empty, the last event falls before an event recorded after the call, and
+    the outputs are bit for bit those of a run without the hook."""
+    import torch
+    from gated_delta_rule_recurrence_amd import _lib, ops
+    p = inputs.draw(1, 256, 2, 8, 128, 64, seed=101, normalised=True, S0_std=0.1,
+                    dST_std=1.0, dtype="bf16")
+    d = device_inputs(p, cuda)
+    ref = run_gpu(p, cuda, 64, d)
+    stream = torch.cuda.current_stream(cuda)
+    ef = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    end = torch.cuda.Event(enable_timing=True)
+    for e in ef + eb + [end]:
+        e.record(stream)  # creates the underlying events
+    torch.cuda.synchronize()
+    try:
+        assert _lib.set_launch_events([e.cuda_event for e in ef[1:]]) == 0
+        ef[0].record(stream)
+        y, S_T, saved = ops.gdr_forward(d["q"], d["k"], d["v"], d["g"], d["beta"], d["S0"],
+                                        chunk=64)
+        assert _lib.set_launch_events([e.cuda_event for e in eb[1:]]) == 0
+        eb[0].record(stream)
+        outs = ops.gdr_backward(d["q"], d["k"], d["g"], d["beta"], saved, d["dy"], d["dST"])
+        end.record(stream)
+    finally:
+        assert _lib.set_launch_events([]) == 0
+    torch.cuda.synchronize()
+    tf = [ef[i].elapsed_time(ef[i + 1]) for i in range(3)]
+    tb = [eb[i].elapsed_time(eb[i + 1]) for i in range(4)]
+    log(f"launch intervals ms: forward {tf}, backward {tb}")
+    assert all(t > 0 for t in tf[:2] + tb), (tf, tb)
+    assert 0 <= tf[2] < min(tf[:2]), tf  # past the forward's two launches
+    assert eb[4].elapsed_time(end) >= 0
+    got = dict(y=y, S_T=S_T, dq=outs[0], dk=outs[1], dv=outs[2], dg=outs[3], dbeta=outs[4],
+               dS0=outs[5])
+    for n, t in got.items():
+        np.testing.assert_array_equal(t.float().cpu().numpy().astype(np.float64), ref[n],
+                                      err_msg=f"with the hook: {n}")
+
+
 def test_chunk_invariance(cuda):
     p = inputs.draw(2, 150, 2, 6, 64, 64, seed=5, normalised=True, S0_std=0.1,
                     dST_std=1.0)
