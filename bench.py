@@ -45,18 +45,18 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "092fafc206533d2a",
+    "sources_sha256_16": "b34b6ea74e2fb2a2",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 974.4e6, "bwd_write_bytes": 492.0e6,
-    "fwd_read_bytes": 162.4e6, "fwd_write_bytes": 459.4e6,
+    "bwd_read_bytes": 974.6e6, "bwd_write_bytes": 492.6e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 458.4e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.7, "valu_busy_pct": 24.9, "avg_us": 32.5},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.1, "valu_busy_pct": 48.9, "avg_us": 169.9},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 6.3, "valu_busy_pct": 26.3, "avg_us": 30.9},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.0, "valu_busy_pct": 49.0, "avg_us": 176.6},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 21.9, "valu_busy_pct": 36.4, "avg_us": 239.3},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.9, "valu_busy_pct": 25.9, "avg_us": 32.8},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.0, "valu_busy_pct": 48.8, "avg_us": 173.6},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 6.3, "valu_busy_pct": 26.2, "avg_us": 31.3},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.9, "valu_busy_pct": 48.8, "avg_us": 181.0},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 23.1, "valu_busy_pct": 38.4, "avg_us": 244.8},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
