@@ -181,11 +181,11 @@ void* scratch_address() {
 }
 
 // ---- gdr_set_launch_events -------------------------------------------------
-// The caller's events and how many kernels the current call has launched
-// (process-wide: the hook is for single-threaded measurement).
+// The caller's events (process-wide: set while no other thread calls in), and
+// how many kernels the current call of this host thread has launched.
 hipEvent_t launch_events[GDR_MAX_LAUNCH_EVENTS];
 int n_launch_events = 0;
-int launch_count = 0;
+thread_local int launch_count = 0;
 
 // A call's end (on success): the events past its last launch, so that every
 // set event is recorded once per call.
