@@ -1447,8 +1447,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void fwd_chunked_bf16_kernel(FwdChun
         const int t = tw + 4 * lq + (lr & 3), r4 = 16 * nt + 4 * (lr >> 2);
         const bool ok = (!GEN || y != nullptr) && t < n && i0 + r4 < Dv;
         const uint2 yb = {cvt_pk_bf16(yr[0], yr[1]), cvt_pk_bf16(yr[2], yr[3])};
-        *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(y + vbase + (int64_t)t * vst + r4)
-                                     : reinterpret_cast<uint2*>(sink16)) = yb;
+        __builtin_nontemporal_store((uint64_t)yb.x | ((uint64_t)yb.y << 32),
+                                    ok ? reinterpret_cast<uint64_t*>(y + vbase + (int64_t)t * vst + r4)
+                                       : reinterpret_cast<uint64_t*>(sink16));
       }
     }
 
@@ -1934,8 +1935,9 @@ __global__ __launch_bounds__(kSwThreads, 1) void bwd_chunked_bf16_kernel(BwdChun
         const int64_t o = vbase + (int64_t)t * vst + r4;
         __builtin_nontemporal_store(cr, reinterpret_cast<f4*>(ok ? a.C + o : sink16));
         const uint2 dvb = {cvt_pk_bf16(dr4[0], dr4[1]), cvt_pk_bf16(dr4[2], dr4[3])};
-        *reinterpret_cast<uint2*>(ok ? reinterpret_cast<uint2*>(dv + o)
-                                     : reinterpret_cast<uint2*>(sink16)) = dvb;
+        __builtin_nontemporal_store((uint64_t)dvb.x | ((uint64_t)dvb.y << 32),
+                                    ok ? reinterpret_cast<uint64_t*>(dv + o)
+                                       : reinterpret_cast<uint64_t*>(sink16));
       }
       put_steps(cpp, pc);
     }
