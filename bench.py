@@ -45,18 +45,18 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "fa9104285cbac083",
+    "sources_sha256_16": "bbc82f42f5720800",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
-    "bwd_read_bytes": 974.6e6, "bwd_write_bytes": 492.6e6,
-    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 458.4e6,
+    "bwd_read_bytes": 974.4e6, "bwd_write_bytes": 507.9e6,
+    "fwd_read_bytes": 162.3e6, "fwd_write_bytes": 472.9e6,
     # per kernel: SQ-counter pipe utilisation and the trace's average duration
     "kernels": {
-        "prep_kernel<fwd>": {"mfma_busy_pct": 5.9, "valu_busy_pct": 25.9, "avg_us": 32.8},
-        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.0, "valu_busy_pct": 48.8, "avg_us": 173.6},
-        "prep_kernel<bwd>": {"mfma_busy_pct": 6.3, "valu_busy_pct": 26.2, "avg_us": 31.3},
-        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 16.9, "valu_busy_pct": 48.8, "avg_us": 181.0},
-        "chunk_bf16_kernel": {"mfma_busy_pct": 23.1, "valu_busy_pct": 38.4, "avg_us": 244.8},
+        "prep_kernel<fwd>": {"mfma_busy_pct": 5.9, "valu_busy_pct": 25.8, "avg_us": 33.3},
+        "fwd_chunked_bf16_kernel": {"mfma_busy_pct": 19.3, "valu_busy_pct": 49.4, "avg_us": 176.7},
+        "prep_kernel<bwd>": {"mfma_busy_pct": 6.3, "valu_busy_pct": 26.1, "avg_us": 31.8},
+        "bwd_chunked_bf16_kernel": {"mfma_busy_pct": 17.5, "valu_busy_pct": 50.4, "avg_us": 182.5},
+        "chunk_bf16_kernel": {"mfma_busy_pct": 22.7, "valu_busy_pct": 37.8, "avg_us": 251.8},
     },
 }
 BWD_KERNELS = ("prep_kernel<bwd>", "bwd_chunked_bf16_kernel", "chunk_bf16_kernel")
