@@ -23,8 +23,10 @@
  *   GDR_DECAY_LOG (see gdr_decay).
  *
  * Ownership: every buffer is allocated and freed by the caller; all data
- * pointers are device pointers.  The library allocates nothing, keeps no
- * state between calls and is reentrant.  Work is enqueued on `stream`
+ * pointers are device pointers.  The library allocates nothing and is
+ * reentrant; the only state it keeps between calls is the scratch array of
+ * gdr_forward_noalloc and the event list of gdr_set_launch_events, each
+ * with the concurrency rule stated there.  Work is enqueued on `stream`
  * (hipStream_t, NULL = the default stream) without any host synchronisation;
  * results are ready when the stream reaches that point.
  *
