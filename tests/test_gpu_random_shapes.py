@@ -90,3 +90,42 @@ def test_random_medium_shape(cuda, i):
     log(f"medium case {i}: {c}, unit {unit}")
     compare_groups(run_gpu(p, cuda, c["chunk"]), p, TOL[c["dtype"]], f"medium {i}",
                    units=[unit], state_tol=TOL["f32"])
+
+
+def _wide_cases(n=24, seed=2028):
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        B, T, Hk = int(rng.integers(1, 4)), int(rng.choice([16, 63, 64, 65, 100, 200, 300])), \
+            int(rng.integers(1, 3))
+        Hv = Hk * int(rng.integers(1, 5))
+        Dk = int(rng.choice([200, 208, 224, 232, 240, 248, 256]))
+        Dv = int(rng.choice([8, 16, 24, 40, 64, 96, 128, 136, 200, 256]))
+        if B * T * Hv * Dk * Dv > 6e7:
+            continue
+        out.append(dict(B=B, T=T, Hk=Hk, Hv=Hv, Dk=Dk, Dv=Dv, dtype="bf16",
+                        chunk=int(rng.choice([16, 32, 48, 64, 96, 128, 256])),
+                        mask=bool(rng.random() < 0.3), log_decay=bool(rng.random() < 0.3),
+                        decay=str(rng.choice(["weak", "strong", "mix"])),
+                        states=bool(rng.random() < 0.5), seed=int(rng.integers(1 << 30))))
+    return out
+
+
+WIDE = _wide_cases()
+
+
+@pytest.mark.parametrize("i", range(len(WIDE)))
+def test_random_wide_key_shape(cuda, i):
+    """bf16 inputs with Dk from 200 to 256: the chunked sweeps' and the
+    eight-wave chunk kernel's 256-column layouts (and their head groups)
+    over ragged Dv, tiles of 16 to 64 steps and intervals up to 256."""
+    c = WIDE[i]
+    p = inputs.draw(c["B"], c["T"], c["Hk"], c["Hv"], c["Dk"], c["Dv"], seed=c["seed"],
+                    normalised=True, decay=c["decay"], S0_std=0.1 if c["states"] else None,
+                    dST_std=1.0 if c["states"] else None, dtype="bf16",
+                    log_decay=c["log_decay"])
+    if c["mask"]:
+        rng = np.random.default_rng(c["seed"] + 1)
+        p.mask = (rng.random((c["B"], c["T"])) >= 0.25).astype(np.uint8)
+    log(f"wide case {i}: {c}")
+    compare(run_gpu(p, cuda, c["chunk"]), run_oracle(p), TOL["bf16"], f"wide {i}")
