@@ -45,7 +45,7 @@ PREP_RECORD_BYTES = (3 * 64 * 64 + 4 * 64) * 4   # one per (batch row, value hea
 # the sources with this digest and are reported only while the sources still
 # hash to it (null otherwise).
 PROFILE = {
-    "sources_sha256_16": "bbc82f42f5720800",
+    "sources_sha256_16": "5fc284b1d2f7f323",
     "source": "profiles/hbm_bytes_qwen35-9b_T2048_bf16.md and "
               "profiles/sq_counters_qwen35-9b_T2048_bf16.md (rocprofv3 --pmc)",
     "bwd_read_bytes": 974.4e6, "bwd_write_bytes": 507.9e6,

@@ -27,16 +27,17 @@
 // Hv/Hk value heads of the kv head in ascending order and accumulates dq, dk
 // in registers, so the GQA sum has a fixed order and needs no atomics.  Wave
 // w owns the chunk steps 16w .. 16w+15: the [Dk x 16] slices of P1, P2', P3',
-// dq, dk (all Dk tiles) and the rows 16w.. of Phi', Psi', QK, KK.  With
-// fp32 inputs every contraction runs on fp32 MFMA (v_mfma_f32_16x16x4_f32)
-// with the accumulator layout "lane l, register v: row 16 i + 4 (l / 16) + v,
+// dq, dk (all Dk tiles) and the rows 16w.. of Phi', Psi', QK, KK.  Every
+// contraction runs on fp32 MFMA (v_mfma_f32_16x16x4_f32; bf16 inputs are
+// widened as they are staged) with the accumulator layout "lane l, register
+// v: row 16 i + 4 (l / 16) + v,
 // column 16 j + l % 16" of a 16 x 16 tile (i, j).  The Dv contractions P and
 // the Gram matrices share one pass over Dv: the dy/c fragments of a wave are
 // at once the B operands of P and the A operands of Phi', Psi'.  MFMA
 // operands are staged in LDS "k-interleaved" ([k / 4][m][k % 4]) so that a
-// fragment (lane l <-> m = l % 16, k = l / 16) is 64 consecutive floats, 16
-// Dv rows per block, with the next block fetched into registers while the
-// current one is multiplied.
+// fragment (lane l <-> m = l % 16, k = l / 16) is 64 consecutive floats,
+// kKB = 32 Dv rows (eight k-steps) per block, with the next block fetched
+// into registers while the current one is multiplied.
 //
 // bf16 inputs whose Dk and Dv are multiples of 8 with 48 < Dk <= 256 take the
 // eight-wave form of this computation instead, with every contraction on bf16
